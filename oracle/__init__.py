@@ -1,0 +1,365 @@
+"""CPU oracle of the tile-based 3D Gaussian Splatting rasterizer.
+
+TEST INFRASTRUCTURE ONLY: a plain, slow, obviously-correct reference that the
+HIP path is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the product package
+never does.  It shares no code with the HIP path: ``liboracle.so`` is built
+from ``oracle.cpp`` alone by ``g++`` (see :func:`build`).
+
+Inputs use the natural per-Gaussian layout: means [N,3], scales [N,3]
+(activated, > 0), quats [N,4] (w,x,y,z, any non-zero norm), opacities [N]
+(activated, in [0,1]), sh [N,K,3] with K = (degree+1)^2.  ``cam`` is any
+object with attributes R [3,3] (world-to-camera), t [3], fx, fy, cx, cy,
+width, height, near, far.
+
+Passages followed (the pages print no formulas; see oracle.cpp for the
+step-by-step reading): gsplat guide (lmnt.cn/news/262699) §2.1 three-stage
+pipeline, §2.2 separate backward, §3.3 quaternion order and activations;
+Moore Threads MUSA article (qwbw.cn/news/278220) §3.3 covariance from scale
+and rotation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.cpp")
+
+MODE_F32KEY = 0
+MODE_F64 = 1
+LOSS_L2 = 0
+LOSS_L1 = 1
+
+# fp32 constants of the method (the pages give none; textbook 3DGS values)
+DEFAULT_SETTINGS = dict(eps2d=0.3, alpha_min=1.0 / 255.0, alpha_max=0.99,
+                        T_min=1e-4, fov_clamp=1.3, sh_offset=0.5)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with g++ (IEEE fp32, no contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Camera(C.Structure):
+    _fields_ = [("R", C.c_double * 9), ("t", C.c_double * 3),
+                ("fx", C.c_double), ("fy", C.c_double), ("cx", C.c_double), ("cy", C.c_double),
+                ("width", C.c_int32), ("height", C.c_int32),
+                ("near_plane", C.c_double), ("far_plane", C.c_double)]
+
+
+class _Settings(C.Structure):
+    _fields_ = [(k, C.c_float) for k in
+                ("eps2d", "alpha_min", "alpha_max", "T_min", "fov_clamp", "sh_offset")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = C.CDLL(_LIB_PATH)
+        P = C.c_void_p
+        lib.orc_project.argtypes = [C.c_int, C.c_int64, C.c_int] + [P] * 15
+        lib.orc_project.restype = C.c_int
+        lib.orc_bin_f32.argtypes = [C.c_int64, P, P, P, C.c_int32, C.c_int32, C.c_int64, P, P, P, P]
+        lib.orc_bin_f32.restype = C.c_int64
+        lib.orc_bin_f64.argtypes = [C.c_int64, P, P, P, C.c_int32, C.c_int32, C.c_int64, P, P]
+        lib.orc_bin_f64.restype = C.c_int64
+        lib.orc_composite.argtypes = [C.c_int32, C.c_int32] + [P] * 15
+        lib.orc_composite.restype = C.c_int
+        lib.orc_composite_bwd.argtypes = [C.c_int32, C.c_int32, C.c_int64] + [P] * 14
+        lib.orc_composite_bwd.restype = C.c_int
+        lib.orc_project_bwd.argtypes = [C.c_int64, C.c_int] + [P] * 14
+        lib.orc_project_bwd.restype = C.c_int
+        lib.orc_loss_jvp.argtypes = [C.c_int64, C.c_int] + [P] * 13 + [C.c_int] + [P] * 5
+        lib.orc_loss_jvp.restype = C.c_int64
+        for name in ("orc_rotation",):
+            getattr(lib, name).argtypes = [P, P]
+        lib.orc_cov3d.argtypes = [P, P, P]
+        lib.orc_sh_basis.argtypes = [C.c_int, P, P]
+        lib.orc_sh_basis_grad.argtypes = [C.c_int, P, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f64(a, shape=None):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None:
+        a = a.reshape(shape)
+    return a
+
+
+def camera_struct(cam) -> _Camera:
+    c = _Camera()
+    R = np.asarray(cam.R, dtype=np.float64).reshape(9)
+    t = np.asarray(cam.t, dtype=np.float64).reshape(3)
+    for i in range(9):
+        c.R[i] = R[i]
+    for i in range(3):
+        c.t[i] = t[i]
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.near_plane, c.far_plane = float(cam.near), float(cam.far)
+    return c
+
+
+def settings_struct(settings=None) -> _Settings:
+    d = dict(DEFAULT_SETTINGS)
+    if settings:
+        d.update(settings)
+    s = _Settings()
+    for k, v in d.items():
+        setattr(s, k, float(v))
+    return s
+
+
+def num_tiles(width: int, height: int) -> int:
+    return ((width + 15) // 16) * ((height + 15) // 16)
+
+
+def project(means, scales, quats, sh, sh_degree, cam, settings=None, mode=MODE_F32KEY):
+    """Steps 1-8 for every Gaussian. Returns a dict of arrays (see oracle.h)."""
+    lib = _load()
+    means, scales, quats = _f64(means), _f64(scales), _f64(quats)
+    N = means.shape[0]
+    K = (sh_degree + 1) ** 2
+    sh = _f64(sh, (N, K, 3))
+    out = dict(means2d=np.zeros((N, 2)), conics=np.zeros((N, 3)), cov2d=np.zeros((N, 3)),
+               depths=np.zeros(N), radii=np.zeros(N, np.int32), tiles=np.zeros(N, np.uint32),
+               rect=np.zeros((N, 4), np.int32), colors=np.zeros((N, 3)),
+               clamped=np.zeros((N, 3), np.uint8))
+    cs, ss = camera_struct(cam), settings_struct(settings)
+    lib.orc_project(mode, N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
+                    C.addressof(cs), C.addressof(ss),
+                    *[_ptr(out[k]) for k in ("means2d", "conics", "cov2d", "depths", "radii",
+                                             "tiles", "rect", "colors", "clamped")])
+    return out
+
+
+def bin_f32(means2d, radii, depths, width, height):
+    """Steps 9-11 on the fp32 key path. Returns dict(M, offsets, keys, ids, ranges)."""
+    lib = _load()
+    m2 = np.ascontiguousarray(np.asarray(means2d, dtype=np.float32).reshape(-1, 2))
+    rad = np.ascontiguousarray(np.asarray(radii, dtype=np.int32))
+    dep = np.ascontiguousarray(np.asarray(depths, dtype=np.float32))
+    N = rad.shape[0]
+    T = num_tiles(width, height)
+    offsets = np.zeros(N, np.uint32)
+    M = lib.orc_bin_f32(N, _ptr(m2), _ptr(rad), _ptr(dep), width, height, 0,
+                        _ptr(offsets), None, None, None)
+    keys = np.zeros(M, np.uint64)
+    ids = np.zeros(M, np.uint32)
+    ranges = np.zeros((T, 2), np.uint32)
+    M2 = lib.orc_bin_f32(N, _ptr(m2), _ptr(rad), _ptr(dep), width, height, M,
+                         _ptr(offsets), _ptr(keys), _ptr(ids), _ptr(ranges))
+    assert M2 == M
+    return dict(M=int(M), offsets=offsets, keys=keys, ids=ids, ranges=ranges)
+
+
+def bin_f64(means2d, radii, depths, width, height):
+    lib = _load()
+    m2, dep = _f64(means2d, (-1, 2)), _f64(depths)
+    rad = np.ascontiguousarray(np.asarray(radii, dtype=np.int32))
+    N = rad.shape[0]
+    T = num_tiles(width, height)
+    M = lib.orc_bin_f64(N, _ptr(m2), _ptr(rad), _ptr(dep), width, height, 0, None, None)
+    ids = np.zeros(M, np.uint32)
+    ranges = np.zeros((T, 2), np.uint32)
+    lib.orc_bin_f64(N, _ptr(m2), _ptr(rad), _ptr(dep), width, height, M, _ptr(ids), _ptr(ranges))
+    return dict(M=int(M), ids=ids, ranges=ranges)
+
+
+def composite(width, height, ranges, ids, means2d, conics, opacities, colors, depths,
+              background=(0.0, 0.0, 0.0), settings=None, with_margin=False):
+    """Step 12. Returns dict(image [H,W,3], final_T, last, depth, alpha[, margin])."""
+    lib = _load()
+    ranges = np.ascontiguousarray(np.asarray(ranges, dtype=np.uint32))
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.uint32))
+    m2, con, op, col, dep = (_f64(means2d, (-1, 2)), _f64(conics, (-1, 3)), _f64(opacities),
+                             _f64(colors, (-1, 3)), _f64(depths))
+    bg = _f64(background, (3,))
+    H, W = height, width
+    out = dict(image=np.zeros((H, W, 3)), final_T=np.zeros((H, W)),
+               last=np.zeros((H, W), np.uint32), depth=np.zeros((H, W)),
+               alpha=np.zeros((H, W)))
+    margin = np.zeros((H, W)) if with_margin else None
+    ss = settings_struct(settings)
+    lib.orc_composite(W, H, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(con), _ptr(op), _ptr(col),
+                      _ptr(dep), _ptr(bg), C.addressof(ss), _ptr(out["image"]),
+                      _ptr(out["final_T"]), _ptr(out["last"]), _ptr(out["depth"]),
+                      _ptr(out["alpha"]), _ptr(margin))
+    if with_margin:
+        out["margin"] = margin
+    return out
+
+
+def composite_bwd(width, height, ranges, ids, means2d, conics, opacities, colors,
+                  dL_dimage, background=(0.0, 0.0, 0.0), settings=None, with_abs=False):
+    """Step 13a. Returns dict(means2d [N,2], conics [N,3], opacities [N], colors [N,3][, abs_sum])."""
+    lib = _load()
+    ranges = np.ascontiguousarray(np.asarray(ranges, dtype=np.uint32))
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.uint32))
+    m2, con, op, col = (_f64(means2d, (-1, 2)), _f64(conics, (-1, 3)), _f64(opacities),
+                        _f64(colors, (-1, 3)))
+    N = op.shape[0]
+    g = _f64(dL_dimage, (height, width, 3))
+    bg = _f64(background, (3,))
+    out = dict(means2d=np.zeros((N, 2)), conics=np.zeros((N, 3)), opacities=np.zeros(N),
+               colors=np.zeros((N, 3)))
+    abs_sum = np.zeros((N, 9)) if with_abs else None
+    ss = settings_struct(settings)
+    lib.orc_composite_bwd(width, height, N, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(con),
+                          _ptr(op), _ptr(col), _ptr(bg), C.addressof(ss), _ptr(g),
+                          _ptr(out["means2d"]), _ptr(out["conics"]), _ptr(out["opacities"]),
+                          _ptr(out["colors"]), _ptr(abs_sum))
+    if with_abs:
+        out["abs_sum"] = abs_sum
+    return out
+
+
+def project_bwd(means, scales, quats, sh, sh_degree, cam, radii, g_means2d, g_conics,
+                g_colors, settings=None):
+    """Step 13b. Returns dict(means [N,3], scales [N,3], quats [N,4], sh [N,K,3])."""
+    lib = _load()
+    means, scales, quats = _f64(means), _f64(scales), _f64(quats)
+    N = means.shape[0]
+    K = (sh_degree + 1) ** 2
+    sh = _f64(sh, (N, K, 3))
+    rad = np.ascontiguousarray(np.asarray(radii, dtype=np.int32))
+    gm2, gc, gcol = _f64(g_means2d, (N, 2)), _f64(g_conics, (N, 3)), _f64(g_colors, (N, 3))
+    out = dict(means=np.zeros((N, 3)), scales=np.zeros((N, 3)), quats=np.zeros((N, 4)),
+               sh=np.zeros((N, K, 3)))
+    cs, ss = camera_struct(cam), settings_struct(settings)
+    lib.orc_project_bwd(N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
+                        C.addressof(cs), C.addressof(ss), _ptr(rad), _ptr(gm2), _ptr(gc),
+                        _ptr(gcol), _ptr(out["means"]), _ptr(out["scales"]), _ptr(out["quats"]),
+                        _ptr(out["sh"]))
+    return out
+
+
+def loss_jvp(means, scales, quats, opacities, sh, sh_degree, cam, target, loss_kind=LOSS_L2,
+             background=(0.0, 0.0, 0.0), settings=None, direction=None, return_image=False):
+    """Whole fp64 forward + loss; with ``direction`` (dict of tangents keyed like the
+    parameters) also the exact directional derivative via dual numbers.
+    Returns (loss, dloss, signature, M) and, if ``return_image``, the image."""
+    lib = _load()
+    means, scales, quats, op = _f64(means), _f64(scales), _f64(quats), _f64(opacities)
+    N = means.shape[0]
+    K = (sh_degree + 1) ** 2
+    sh = _f64(sh, (N, K, 3))
+    tgt = _f64(target, (cam.height, cam.width, 3))
+    bg = _f64(background, (3,))
+    d = direction or {}
+    dm = _f64(d["means"], (N, 3)) if "means" in d else None
+    ds = _f64(d["scales"], (N, 3)) if "scales" in d else None
+    dq = _f64(d["quats"], (N, 4)) if "quats" in d else None
+    do = _f64(d["opacities"], (N,)) if "opacities" in d else None
+    dsh = _f64(d["sh"], (N, K, 3)) if "sh" in d else None
+    loss = C.c_double()
+    dloss = C.c_double()
+    sig = C.c_uint64()
+    cs, ss = camera_struct(cam), settings_struct(settings)
+    img = np.zeros((cam.height, cam.width, 3)) if return_image else None
+    M = lib.orc_loss_jvp(N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(op), _ptr(sh),
+                         _ptr(dm), _ptr(ds), _ptr(dq), _ptr(do), _ptr(dsh), C.addressof(cs),
+                         C.addressof(ss), _ptr(bg), loss_kind, _ptr(tgt), C.byref(loss),
+                         C.byref(dloss), C.byref(sig), _ptr(img))
+    if return_image:
+        return loss.value, dloss.value, sig.value, int(M), img
+    return loss.value, dloss.value, sig.value, int(M)
+
+
+def rotation(quat):
+    lib = _load()
+    q = _f64(quat, (4,))
+    R = np.zeros(9)
+    lib.orc_rotation(_ptr(q), _ptr(R))
+    return R.reshape(3, 3)
+
+
+def cov3d(quat, scale):
+    lib = _load()
+    q, s = _f64(quat, (4,)), _f64(scale, (3,))
+    S = np.zeros(9)
+    lib.orc_cov3d(_ptr(q), _ptr(s), _ptr(S))
+    return S.reshape(3, 3)
+
+
+def sh_basis(sh_degree, direction):
+    lib = _load()
+    d = _f64(direction, (3,))
+    Y = np.zeros((sh_degree + 1) ** 2)
+    lib.orc_sh_basis(sh_degree, _ptr(d), _ptr(Y))
+    return Y
+
+
+def sh_basis_grad(sh_degree, direction):
+    lib = _load()
+    d = _f64(direction, (3,))
+    dY = np.zeros(((sh_degree + 1) ** 2, 3))
+    lib.orc_sh_basis_grad(sh_degree, _ptr(d), _ptr(dY))
+    return dY
+
+
+# --------------------------------------------------------------------------
+# Whole-frame helpers composed from the stages above (parity mode: fp32 key
+# path, fp64 values).
+# --------------------------------------------------------------------------
+def render(scene, cam, settings=None, background=(0.0, 0.0, 0.0), with_margin=False):
+    """Forward of one frame in parity mode. ``scene`` has means, scales, quats,
+    opacities, sh, sh_degree. Returns dict with 'proj', 'bins', 'raster'."""
+    proj = project(scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree, cam,
+                   settings, MODE_F32KEY)
+    bins = bin_f32(proj["means2d"].astype(np.float32), proj["radii"],
+                   proj["depths"].astype(np.float32), cam.width, cam.height)
+    raster = composite(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
+                       proj["conics"], scene.opacities, proj["colors"], proj["depths"],
+                       background, settings, with_margin)
+    return dict(proj=proj, bins=bins, raster=raster)
+
+
+def loss_grad_image(image, target, loss_kind):
+    """dL/dimage of the sum-reduced loss: L2 -> 2 (C - T); L1 -> sign(C - T), sign(0) = 0."""
+    r = np.asarray(image, np.float64) - np.asarray(target, np.float64)
+    return 2.0 * r if loss_kind == LOSS_L2 else np.sign(r)
+
+
+def backward(scene, cam, fwd, dL_dimage, settings=None, background=(0.0, 0.0, 0.0),
+             with_abs=False):
+    """Step 13 for a forward produced by :func:`render` (or the fp64 path)."""
+    proj, bins = fwd["proj"], fwd["bins"]
+    g2 = composite_bwd(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
+                       proj["conics"], scene.opacities, proj["colors"], dL_dimage, background,
+                       settings, with_abs)
+    g3 = project_bwd(scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree, cam,
+                     proj["radii"], g2["means2d"], g2["conics"], g2["colors"], settings)
+    return dict(g2=g2, g3=g3)
+
+
+def render_f64(scene, cam, settings=None, background=(0.0, 0.0, 0.0)):
+    """Forward of one frame with every step in fp64 (for the gradient pins)."""
+    proj = project(scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree, cam,
+                   settings, MODE_F64)
+    bins = bin_f64(proj["means2d"], proj["radii"], proj["depths"], cam.width, cam.height)
+    raster = composite(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
+                       proj["conics"], scene.opacities, proj["colors"], proj["depths"],
+                       background, settings)
+    return dict(proj=proj, bins=bins, raster=raster)
