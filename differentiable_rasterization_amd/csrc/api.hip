@@ -1,0 +1,286 @@
+// api.hip — host side of the C ABI declared in include/gsraster.h: argument
+// validation, status codes and kernel launches.  Holds no state between
+// calls except a thread-local error message.
+#include <stdio.h>
+#include <string.h>
+
+#include "gs_common.h"
+
+extern "C" {
+hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
+                                 const float* scales, const float* quats, const float* sh,
+                                 const gs::Cam& cam, const gs::Settings& st, float* means2d,
+                                 float* conics, float* depths, int32_t* radii, float* colors,
+                                 uint32_t* tiles, hipStream_t stream);
+hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, const float* means,
+                                 const float* scales, const float* quats, const float* sh,
+                                 const gs::Cam& cam, const gs::Settings& st, const int32_t* radii,
+                                 const float* g_m2, const float* g_con, const float* g_col,
+                                 float* o_means, float* o_scales, float* o_quats, float* o_sh,
+                                 int accumulate, hipStream_t stream);
+size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
+hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, void* workspace,
+                          uint64_t capacity, int32_t T, uint64_t* total_host, hipStream_t s);
+hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
+                                     const int32_t* radii, const float* depths,
+                                     const uint32_t* tiles, const uint32_t* offsets, int32_t W,
+                                     int32_t H, uint64_t M, uint64_t* keys, uint32_t* ids,
+                                     uint32_t* ranges, void* workspace, uint64_t capacity,
+                                     hipStream_t s);
+hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges, const uint32_t* ids,
+                                int64_t ld, const float* means2d, const float* conics,
+                                const float* opac, const float* colors, const float* depths,
+                                const float* bg, const gs::Settings& st, float* image,
+                                float* final_T, uint32_t* last_idx, float* out_depth,
+                                float* out_alpha, hipStream_t s);
+hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
+                                const uint32_t* ids, int64_t ld, const float* means2d,
+                                const float* conics, const float* opac, const float* colors,
+                                const float* bg, const gs::Settings& st, const float* final_T,
+                                const uint32_t* last_idx, const float* dL_dimage, float* g_m2,
+                                float* g_con, float* g_op, float* g_col, int accumulate,
+                                hipStream_t s);
+hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
+                               float* loss, hipStream_t s);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gs_status fail(gs_status s, const char* fmt, const char* what) {
+  snprintf(g_err, sizeof(g_err), fmt, what);
+  return s;
+}
+
+gs_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return GS_OK;
+  }
+  snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+  return GS_ERR_HIP;
+}
+
+#define GS_REQUIRE(cond, msg)                                        \
+  do {                                                               \
+    if (!(cond)) return fail(GS_ERR_INVALID_ARGUMENT, "%s", msg);    \
+  } while (0)
+
+gs_status check_sizes(int64_t N, int64_t ld) {
+  GS_REQUIRE(N >= 0, "N must be >= 0");
+  GS_REQUIRE(ld >= N, "ld must be >= N");
+  GS_REQUIRE(N < (int64_t)1 << 31, "N must be < 2^31");
+  GS_REQUIRE(ld <= ((int64_t)1 << 40), "ld too large");
+  return GS_OK;
+}
+
+gs_status check_image(int32_t W, int32_t H) {
+  GS_REQUIRE(W > 0 && H > 0, "width and height must be > 0");
+  GS_REQUIRE((int64_t)W * H < ((int64_t)1 << 31), "image too large");
+  return GS_OK;
+}
+
+gs_status check_camera(const gs_camera* cam) {
+  GS_REQUIRE(cam != nullptr, "camera is NULL");
+  gs_status s = check_image(cam->width, cam->height);
+  if (s != GS_OK) return s;
+  GS_REQUIRE(cam->fx > 0.0f && cam->fy > 0.0f, "fx and fy must be > 0");
+  GS_REQUIRE(cam->near_plane > 0.0f && cam->far_plane > cam->near_plane,
+             "need 0 < near_plane < far_plane");
+  return GS_OK;
+}
+
+gs_status check_settings(const gs_settings* st) {
+  GS_REQUIRE(st != nullptr, "settings is NULL");
+  GS_REQUIRE(st->eps2d >= 0.0f, "eps2d must be >= 0");
+  GS_REQUIRE(st->alpha_min > 0.0f && st->alpha_max < 1.0f && st->alpha_min <= st->alpha_max,
+             "need 0 < alpha_min <= alpha_max < 1");
+  GS_REQUIRE(st->T_min > 0.0f && st->T_min < 1.0f, "need 0 < T_min < 1");
+  GS_REQUIRE(st->fov_clamp > 0.0f, "fov_clamp must be > 0");
+  return GS_OK;
+}
+
+#define GS_CHECK(expr)               \
+  do {                               \
+    gs_status _s = (expr);           \
+    if (_s != GS_OK) return _s;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+gs_settings gs_default_settings(void) {
+  gs_settings s;
+  s.eps2d = 0.3f;
+  s.alpha_min = 1.0f / 255.0f;
+  s.alpha_max = 0.99f;
+  s.T_min = 1e-4f;
+  s.fov_clamp = 1.3f;
+  s.sh_offset = 0.5f;
+  return s;
+}
+
+const char* gs_status_string(gs_status s) {
+  switch (s) {
+    case GS_OK: return "GS_OK";
+    case GS_ERR_INVALID_ARGUMENT: return "GS_ERR_INVALID_ARGUMENT";
+    case GS_ERR_CAPACITY: return "GS_ERR_CAPACITY";
+    case GS_ERR_HIP: return "GS_ERR_HIP";
+  }
+  return "GS_ERR_UNKNOWN";
+}
+
+const char* gs_last_error(void) { return g_err; }
+
+int32_t gs_num_tiles(int32_t width, int32_t height) {
+  if (width <= 0 || height <= 0) return 0;
+  return gs::grid_dim(width) * gs::grid_dim(height);
+}
+
+gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
+                         const float* scales, const float* quats, const float* sh,
+                         const gs_camera* cam, const gs_settings* settings, float* means2d,
+                         float* conics, float* depths, int32_t* radii, float* colors,
+                         uint32_t* tiles_touched, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_CHECK(check_camera(cam));
+  GS_CHECK(check_settings(settings));
+  if (N > 0)
+    GS_REQUIRE(means && scales && quats && sh && means2d && conics && depths && radii && colors &&
+                   tiles_touched,
+               "NULL array pointer");
+  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, sh,
+                                          gs::make_cam(*cam), gs::make_settings(*settings),
+                                          means2d, conics, depths, radii, colors, tiles_touched,
+                                          (hipStream_t)stream),
+                    "gs_project_fwd");
+}
+
+size_t gs_bin_and_sort_workspace_size(int64_t N, uint64_t capacity, int32_t width,
+                                      int32_t height) {
+  if (N < 0 || width <= 0 || height <= 0) return 0;
+  return gs_binsort_workspace_bytes(N, capacity, gs_num_tiles(width, height));
+}
+
+gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int32_t* radii,
+                          const float* depths, const uint32_t* tiles_touched, int32_t width,
+                          int32_t height, uint32_t* offsets, uint64_t capacity,
+                          uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                          uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(num_instances != nullptr, "num_instances is NULL");
+  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+  GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
+  if (N > 0)
+    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets, "NULL array pointer");
+  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
+  const int32_t T = gs_num_tiles(width, height);
+  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
+             "workspace smaller than gs_bin_and_sort_workspace_size()");
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t M = 0;
+  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, offsets, workspace, capacity, T, &M, s),
+                            "gs_bin_and_sort(scan)");
+  if (st != GS_OK) return st;
+  *num_instances = M;
+  if (M >= ((uint64_t)1 << 30))
+    return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
+  if (M > capacity) {
+    snprintf(g_err, sizeof(g_err), "gs_bin_and_sort: %llu instances exceed capacity %llu",
+             (unsigned long long)M, (unsigned long long)capacity);
+    return GS_ERR_CAPACITY;
+  }
+  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
+                                              offsets, width, height, M, keys, ids, tile_ranges,
+                                              workspace, capacity, s),
+                    "gs_bin_and_sort");
+}
+
+gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
+                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const float* means2d, const float* conics, const float* opacities,
+                           const float* colors, const float* depths, const float* background,
+                           const gs_settings* settings, float* image, float* final_T,
+                           uint32_t* last_idx, float* out_depth, float* out_alpha,
+                           void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
+  GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
+  if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  return hip_status(gs_launch_raster_fwd(width, height, tile_ranges, ids, ld, means2d, conics,
+                                         opacities, colors, depths, background,
+                                         gs::make_settings(*settings), image, final_T, last_idx,
+                                         out_depth, out_alpha, (hipStream_t)stream),
+                    "gs_rasterize_fwd");
+}
+
+gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
+                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const float* means2d, const float* conics, const float* opacities,
+                           const float* colors, const float* background,
+                           const gs_settings* settings, const float* final_T,
+                           const uint32_t* last_idx, const float* dL_dimage,
+                           float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
+                           float* dL_dcolors, int32_t accumulate, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
+  GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
+  GS_REQUIRE(dL_dmeans2d && dL_dconics && dL_dopacities && dL_dcolors, "NULL gradient pointer");
+  GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, ld, means2d, conics,
+                                         opacities, colors, background,
+                                         gs::make_settings(*settings), final_T, last_idx,
+                                         dL_dimage, dL_dmeans2d, dL_dconics, dL_dopacities,
+                                         dL_dcolors, accumulate, (hipStream_t)stream),
+                    "gs_rasterize_bwd");
+}
+
+gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
+                         const float* scales, const float* quats, const float* sh,
+                         const gs_camera* cam, const gs_settings* settings,
+                         const int32_t* radii, const float* dL_dmeans2d,
+                         const float* dL_dconics, const float* dL_dcolors, float* dL_dmeans,
+                         float* dL_dscales, float* dL_dquats, float* dL_dsh,
+                         int32_t accumulate, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_CHECK(check_camera(cam));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+  if (N > 0)
+    GS_REQUIRE(means && scales && quats && sh && radii && dL_dmeans2d && dL_dconics &&
+                   dL_dcolors && dL_dmeans && dL_dscales && dL_dquats && dL_dsh,
+               "NULL array pointer");
+  return hip_status(gs_launch_project_bwd(N, ld, sh_degree, means, scales, quats, sh,
+                                          gs::make_cam(*cam), gs::make_settings(*settings), radii,
+                                          dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans,
+                                          dL_dscales, dL_dquats, dL_dsh, accumulate,
+                                          (hipStream_t)stream),
+                    "gs_project_bwd");
+}
+
+gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* image,
+                             const float* target, float* dL_dimage, float* loss,
+                             void* stream) {
+  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
+  GS_REQUIRE(count >= 0, "count must be >= 0");
+  if (count > 0) GS_REQUIRE(image && target && dL_dimage, "NULL array pointer");
+  return hip_status(gs_launch_loss_grad(kind, count, image, target, dL_dimage, loss,
+                                        (hipStream_t)stream),
+                    "gs_image_loss_grad");
+}
+
+}  // extern "C"

@@ -1,0 +1,480 @@
+// binsort.hip — stages 2-3: scan of tiles touched, key duplication, onesweep
+// LSD radix sort of the (tile_id << 32 | depth bits, Gaussian id) pairs, and
+// per-tile ranges.
+//
+// All of it is data movement, bound by HBM bandwidth (or by latency at small
+// instance counts):
+//   - the scan is reduce-then-scan over 2048-element blocks;
+//   - duplication is balanced by output slot: a workgroup owns 256 Gaussians
+//     and writes all of their instances with consecutive, coalesced stores,
+//     so one Gaussian touching thousands of tiles does not serialise a lane;
+//   - the sort is a onesweep LSD radix sort with 8-bit digits: one pass
+//     computes every digit's global histogram, then each digit pass reads and
+//     writes the keys once.  A workgroup takes its partition from an atomic
+//     ticket (so it only ever waits on partitions already running), ranks
+//     its 4096 keys stably with wave64 ballots into LDS histograms, publishes
+//     per-digit counts and resolves its global offsets by decoupled
+//     look-back, then scatters through LDS so that global writes come out
+//     in digit runs.  Only the low 32 + ceil(log2 T) key bits are sorted.
+#include "gs_common.h"
+
+namespace gs {
+
+// ---------------------------------------------------------------------------
+// Fill
+// ---------------------------------------------------------------------------
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+static hipError_t fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide scans (256 threads = 4 wave64)
+// ---------------------------------------------------------------------------
+__device__ inline uint64_t wave_incl_scan_u64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of one value per thread; returns the block total.
+__device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
+  __shared__ uint64_t s_w[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t inc = wave_incl_scan_u64(x);
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  uint64_t off = 0, tot = 0;
+  for (int k = 0; k < 4; ++k) {
+    if (k < w) off += s_w[k];
+    tot += s_w[k];
+  }
+  excl = off + inc - x;
+  __syncthreads();
+  return tot;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: exclusive scan of tiles_touched -> offsets, total M
+// ---------------------------------------------------------------------------
+constexpr int kScanItems = 8;
+constexpr int kScanBlock = 256 * kScanItems;
+
+__global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __restrict__ in,
+                                                          int64_t N,
+                                                          uint64_t* __restrict__ block_sums) {
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock;
+  uint64_t s = 0;
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + (int64_t)k * 256 + threadIdx.x;
+    if (i < N) s += in[i];
+  }
+  uint64_t excl;
+  const uint64_t tot = block_excl_scan_u64(s, excl);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict__ sums,
+                                                            int64_t nb,
+                                                            uint64_t* __restrict__ total) {
+  uint64_t carry = 0;
+  for (int64_t b = 0; b < nb; b += 256) {
+    const int64_t i = b + threadIdx.x;
+    const uint64_t x = i < nb ? sums[i] : 0;
+    uint64_t excl;
+    const uint64_t tot = block_excl_scan_u64(x, excl);
+    if (i < nb) sums[i] = carry + excl;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) *total = carry;
+}
+
+__global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restrict__ in, int64_t N,
+                                                        const uint64_t* __restrict__ sums,
+                                                        uint32_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanItems;
+  uint32_t v[kScanItems];
+  uint64_t s = 0;
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    v[k] = i < N ? in[i] : 0u;
+    s += v[k];
+  }
+  uint64_t excl;
+  block_excl_scan_u64(s, excl);
+  uint64_t run = sums[blockIdx.x] + excl;
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    if (i < N) out[i] = (uint32_t)run;
+    run += v[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3a: duplicate each visible Gaussian once per touched tile
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void duplicate_kernel(
+    int64_t N, const float* __restrict__ means2d, int64_t ld, const int32_t* __restrict__ radii,
+    const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
+    const uint32_t* __restrict__ offsets, int gx, int gy, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ ids) {
+  __shared__ uint32_t s_off[257];
+  __shared__ int32_t s_x0[256], s_w[256], s_y0[256];
+  __shared__ uint32_t s_db[256];
+  const int t = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * 256;
+  const int64_t i = g0 + t;
+  const int64_t nloc = (N - g0) < 256 ? (N - g0) : 256;
+  if (i < N) {
+    const uint32_t off = offsets[i];
+    const uint32_t cnt = tiles_touched[i];
+    s_off[t] = off;
+    int x0 = 0, x1 = 0, y0 = 0, y1 = 0;
+    if (cnt > 0) tile_rect(means2d[i], means2d[ld + i], radii[i], gx, gy, x0, x1, y0, y1);
+    s_x0[t] = x0;
+    s_w[t] = (x1 > x0) ? (x1 - x0) : 1;
+    s_y0[t] = y0;
+    s_db[t] = __float_as_uint(depths[i]);
+    if (i == N - 1 || t == 255) s_off[t + 1] = off + cnt;
+  }
+  __syncthreads();
+  const uint32_t begin = s_off[0], end = s_off[nloc];
+  for (uint32_t slot = begin + t; slot < end; slot += 256) {
+    // last j with s_off[j] <= slot (zero-count Gaussians share offsets)
+    int lo = 0, hi = (int)nloc;  // invariant: s_off[lo] <= slot < s_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= slot) lo = mid; else hi = mid;
+    }
+    const uint32_t k = slot - s_off[lo];
+    const uint32_t w = (uint32_t)s_w[lo];
+    const uint32_t ty = (uint32_t)s_y0[lo] + k / w;
+    const uint32_t tx = (uint32_t)s_x0[lo] + k % w;
+    const uint32_t tile = ty * (uint32_t)gx + tx;
+    keys[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
+    ids[slot] = (uint32_t)(g0 + lo);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3b: onesweep radix sort
+// ---------------------------------------------------------------------------
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortItems = 16;
+constexpr int kPart = 256 * kSortItems;  // keys per partition
+constexpr int kMaxPasses = 8;
+constexpr uint32_t kFlagAgg = 1u << 30;
+constexpr uint32_t kFlagPrefix = 2u << 30;
+constexpr uint32_t kCountMask = (1u << 30) - 1u;
+
+// Global histogram of every pass's digit (one LDS histogram per pass).
+__global__ __launch_bounds__(256) void sort_histogram_kernel(const uint64_t* __restrict__ keys,
+                                                             uint32_t M, int passes,
+                                                             uint32_t* __restrict__ hist) {
+  __shared__ uint32_t s_h[kMaxPasses][kRadix];
+  for (int k = threadIdx.x; k < kMaxPasses * kRadix; k += 256) (&s_h[0][0])[k] = 0;
+  __syncthreads();
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < M; i += gridDim.x * 256u) {
+    const uint64_t key = keys[i];
+    for (int p = 0; p < passes; ++p)
+      atomicAdd(&s_h[p][(key >> (p * kRadixBits)) & (kRadix - 1)], 1u);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < passes * kRadix; k += 256) {
+    const uint32_t v = (&s_h[0][0])[k];
+    if (v) atomicAdd(&hist[k], v);
+  }
+}
+
+// hist[p][d] -> exclusive offsets, one workgroup per pass.
+__global__ __launch_bounds__(256) void sort_hist_scan_kernel(uint32_t* __restrict__ hist) {
+  uint32_t* h = hist + blockIdx.x * kRadix;
+  const uint64_t x = h[threadIdx.x];
+  uint64_t excl;
+  block_excl_scan_u64(x, excl);
+  h[threadIdx.x] = (uint32_t)excl;
+}
+
+__device__ inline uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__global__ __launch_bounds__(256) void sort_pass_kernel(
+    const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
+    uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, uint32_t M, int shift,
+    const uint32_t* __restrict__ digit_offsets, uint32_t* __restrict__ status,
+    uint32_t* __restrict__ ticket) {
+  __shared__ uint64_t s_keys[kPart];
+  __shared__ uint32_t s_vals[kPart];
+  __shared__ uint32_t s_wh[4][kRadix];  // per-wave digit counts, later wave offsets
+  __shared__ uint32_t s_start[kRadix];  // block-local exclusive digit start
+  __shared__ uint32_t s_gbase[kRadix];  // global base minus local start
+  __shared__ uint32_t s_part;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_part = atomicAdd(ticket, 1u);
+  for (int k = tid; k < 4 * kRadix; k += 256) (&s_wh[0][0])[k] = 0;
+  __syncthreads();
+  const uint32_t part = s_part;
+  const uint32_t base = part * (uint32_t)kPart;
+  const uint32_t nvalid = (M - base) < (uint32_t)kPart ? (M - base) : (uint32_t)kPart;
+
+  uint64_t k[kSortItems];
+  uint32_t v[kSortItems];
+  uint32_t rank[kSortItems];
+  const uint32_t wbase = base + (uint32_t)wave * 64u * kSortItems;
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it) {
+    const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
+    const bool valid = idx < M;
+    k[it] = valid ? kin[idx] : ~0ull;  // padding ranks last in digit 255
+    v[it] = valid ? vin[idx] : 0u;
+  }
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it) {
+    const uint32_t d = (uint32_t)(k[it] >> shift) & (kRadix - 1);
+    uint64_t match = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+      const uint64_t bal = __ballot((d >> b) & 1u);
+      match &= ((d >> b) & 1u) ? bal : ~bal;
+    }
+    const uint32_t before = s_wh[wave][d];
+    rank[it] = before + (uint32_t)__popcll(match & lt);
+    const int leader = __ffsll((long long)match) - 1;
+    __builtin_amdgcn_wave_barrier();
+    if (lane == leader) s_wh[wave][d] = before + (uint32_t)__popcll(match);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // per digit (thread = digit): wave offsets, block count, block-local start
+  const uint32_t d = (uint32_t)tid;
+  uint32_t cnt = 0;
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t c = s_wh[w][d];
+    s_wh[w][d] = cnt;
+    cnt += c;
+  }
+  uint64_t excl64;
+  block_excl_scan_u64(cnt, excl64);
+  s_start[d] = (uint32_t)excl64;
+  const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in digit 255
+  const uint32_t mine = (d == kRadix - 1) ? cnt - pad : cnt;
+
+  // decoupled look-back over earlier partitions, one lane per digit
+  uint32_t* st = status + (size_t)part * kRadix;
+  uint32_t prefix = 0;
+  if (part == 0) {
+    __hip_atomic_store(&st[d], kFlagPrefix | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __hip_atomic_store(&st[d], kFlagAgg | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int64_t p = (int64_t)part - 1;
+    while (p >= 0) {
+      const uint32_t s = __hip_atomic_load(&status[(size_t)p * kRadix + d], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t flag = s & ~kCountMask;
+      if (flag == 0u) {
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      prefix += s & kCountMask;
+      if (flag == kFlagPrefix) break;
+      --p;
+    }
+    __hip_atomic_store(&st[d], kFlagPrefix | (prefix + mine), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  s_gbase[d] = digit_offsets[d] + prefix - s_start[d];
+  __syncthreads();
+
+  // scatter into LDS in local sorted order
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it) {
+    const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
+    if (idx < M) {
+      const uint32_t dd = (uint32_t)(k[it] >> shift) & (kRadix - 1);
+      const uint32_t pos = s_start[dd] + s_wh[wave][dd] + rank[it];
+      s_keys[pos] = k[it];
+      s_vals[pos] = v[it];
+    }
+  }
+  __syncthreads();
+  // write out in local order: consecutive lanes hit consecutive slots of a digit run
+  for (uint32_t j = (uint32_t)tid; j < nvalid; j += 256u) {
+    const uint64_t key = s_keys[j];
+    const uint32_t dd = (uint32_t)(key >> shift) & (kRadix - 1);
+    const uint32_t out = s_gbase[dd] + j;
+    kout[out] = key;
+    vout[out] = s_vals[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3c: per-tile [start, end) ranges of the sorted keys
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ranges_kernel(const uint64_t* __restrict__ keys, uint32_t M,
+                                                     uint32_t T, uint32_t* __restrict__ ranges) {
+  const uint32_t m = blockIdx.x * 256u + threadIdx.x;
+  if (m >= M) return;
+  const uint32_t tile = (uint32_t)(keys[m] >> 32);
+  if (tile >= T) return;
+  if (m == 0 || (uint32_t)(keys[m - 1] >> 32) != tile) ranges[2 * tile] = m;
+  if (m == M - 1 || (uint32_t)(keys[m + 1] >> 32) != tile) ranges[2 * tile + 1] = m + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout
+// ---------------------------------------------------------------------------
+struct SortPlan {
+  int passes;
+  uint32_t parts;
+};
+
+static inline int ceil_log2(uint32_t x) {
+  int b = 0;
+  while ((1ull << b) < x) ++b;
+  return b;
+}
+
+static inline SortPlan sort_plan(uint64_t M, int32_t T) {
+  const int bits = 32 + ceil_log2((uint32_t)T);
+  SortPlan p;
+  p.passes = (bits + kRadixBits - 1) / kRadixBits;
+  p.parts = (uint32_t)((M + kPart - 1) / kPart);
+  return p;
+}
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  uint64_t* keys_alt;
+  uint32_t* ids_alt;
+  uint64_t* scan_sums;
+  uint64_t* total;
+  uint32_t* hist;    // [passes][256]
+  uint32_t* ticket;  // [passes]
+  uint32_t* status;  // [passes][parts][256]
+  size_t bytes;
+};
+
+static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
+  const SortPlan sp = sort_plan(capacity, T);
+  const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
+  Workspace w;
+  char* p = (char*)base;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.keys_alt = (uint64_t*)take(sizeof(uint64_t) * (capacity ? capacity : 1));
+  w.ids_alt = (uint32_t*)take(sizeof(uint32_t) * (capacity ? capacity : 1));
+  w.scan_sums = (uint64_t*)take(sizeof(uint64_t) * (nb ? nb : 1));
+  w.total = (uint64_t*)take(sizeof(uint64_t));
+  w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
+  w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace gs
+
+extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T) {
+  return gs::carve(nullptr, N, capacity, T).bytes;
+}
+
+// Scan; writes offsets and the total to *total_host (one synchronising read).
+extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets,
+                                     void* workspace, uint64_t capacity, int32_t T,
+                                     uint64_t* total_host, hipStream_t s) {
+  using namespace gs;
+  Workspace w = carve(workspace, N, capacity, T);
+  hipError_t e;
+  if (N == 0) {
+    *total_host = 0;
+    return hipSuccess;
+  }
+  const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, s, tiles, N, w.scan_sums);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, w.scan_sums, nb, w.total);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, s, tiles, N, w.scan_sums,
+                     offsets);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint64_t tot = 0;
+  if ((e = hipMemcpyAsync(&tot, w.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  *total_host = tot;
+  return hipSuccess;
+}
+
+// Duplicate, sort and extract ranges for M instances (M <= capacity).
+extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
+                                                const int32_t* radii, const float* depths,
+                                                const uint32_t* tiles, const uint32_t* offsets,
+                                                int32_t W, int32_t H, uint64_t M,
+                                                uint64_t* keys, uint32_t* ids, uint32_t* ranges,
+                                                void* workspace, uint64_t capacity, hipStream_t s) {
+  using namespace gs;
+  const int gx = grid_dim(W), gy = grid_dim(H);
+  const int32_t T = gx * gy;
+  Workspace w = carve(workspace, N, capacity, T);
+  hipError_t e;
+  if ((e = fill_u32(ranges, 2 * (int64_t)T, 0u, s)) != hipSuccess) return e;
+  if (M == 0) return hipSuccess;
+  const SortPlan sp = sort_plan(M, T);
+  // land the final pass in (keys, ids): start from the alternate buffer when
+  // the pass count is odd
+  uint64_t* ka = (sp.passes & 1) ? w.keys_alt : keys;
+  uint32_t* ia = (sp.passes & 1) ? w.ids_alt : ids;
+  uint64_t* kb = (sp.passes & 1) ? keys : w.keys_alt;
+  uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
+  const int64_t nblk = (N + 255) / 256;
+  hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
+                     depths, tiles, offsets, gx, gy, ka, ia);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  const uint32_t M32 = (uint32_t)M;
+  if ((e = fill_u32(w.hist, (int64_t)kMaxPasses * kRadix, 0u, s)) != hipSuccess) return e;
+  if ((e = fill_u32(w.ticket, kMaxPasses, 0u, s)) != hipSuccess) return e;
+  if ((e = fill_u32(w.status, (int64_t)sp.passes * sp.parts * kRadix, 0u, s)) != hipSuccess) return e;
+  unsigned hblocks = (unsigned)((M + 256 * 16 - 1) / (256 * 16));
+  if (hblocks > 1024) hblocks = 1024;
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, M32, sp.passes,
+                     w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(256), 0, s, w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int p = 0; p < sp.passes; ++p) {
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(256), 0, s, ka, ia, kb, ib, M32,
+                       p * kRadixBits, w.hist + p * kRadix,
+                       w.status + (size_t)p * sp.parts * kRadix, w.ticket + p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint64_t* tk = ka; ka = kb; kb = tk;
+    uint32_t* ti = ia; ia = ib; ib = ti;
+  }
+  const unsigned rblocks = (unsigned)((M + 255) / 256);
+  hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, M32, (uint32_t)T, ranges);
+  return hipGetLastError();
+}

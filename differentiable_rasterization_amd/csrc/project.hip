@@ -1,0 +1,449 @@
+// project.hip — stage 1 (projection) and its backward.
+//
+// Gaussian-parallel and HBM-bound: one lane per Gaussian, every parameter
+// plane read once with coalesced 4-byte loads (the planes are structure-of-
+// arrays with leading dimension ld), outputs written the same way.
+//
+// The geometric key path (camera transform, covariance, EWA Jacobian, 2D
+// covariance, conic, radius, pixel mean, tile rect) follows the pipeline of
+// the gsplat guide (lmnt.cn/news/262699) §2.1 and the scale/rotation
+// covariance of the Moore Threads MUSA article (qwbw.cn/news/278220) §3.3.
+// It is evaluated in IEEE fp32 in one fixed operation order with no
+// contraction, with correctly rounded division and square root, so its
+// outputs (and the tile keys derived from them) are reproducible bit for bit.
+#include "gs_common.h"
+
+namespace gs {
+
+struct Geom {
+  float u, v, depth, a, b, c, A, B, C;
+  int32_t radius;
+  int x0, x1, y0, y1;
+  bool clampx, clampy;
+};
+
+// Rotation of the unit quaternion (w,x,y,z), row-major.
+__device__ inline void quat_to_rot(float w, float x, float y, float z, float R[9]) {
+  R[0] = 1.0f - 2.0f * (y * y + z * z);
+  R[1] = 2.0f * (x * y - w * z);
+  R[2] = 2.0f * (x * z + w * y);
+  R[3] = 2.0f * (x * y + w * z);
+  R[4] = 1.0f - 2.0f * (x * x + z * z);
+  R[5] = 2.0f * (y * z - w * x);
+  R[6] = 2.0f * (x * z - w * y);
+  R[7] = 2.0f * (y * z + w * x);
+  R[8] = 1.0f - 2.0f * (x * x + y * y);
+}
+
+__device__ inline float sel_min(float a, float b) { return (b < a) ? b : a; }
+__device__ inline float sel_max(float a, float b) { return (a < b) ? b : a; }
+
+// Returns false when the Gaussian is culled.  qn receives the unit
+// quaternion and its norm, Sig the 3D covariance, Tm = J W (2x3).
+__device__ inline bool project_geom(const float m[3], const float s[3], const float q[4],
+                                    const Cam& cam, const Settings& st, Geom& g, float qn[5],
+                                    float Rq[9], float Sig[6], float Tm[6], float tcam[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (!__builtin_isfinite(m[i]) || !__builtin_isfinite(s[i])) return false;
+  for (int i = 0; i < 4; ++i)
+    if (!__builtin_isfinite(q[i])) return false;
+  const float* W = cam.R;
+  const float tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + cam.t[0];
+  const float ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + cam.t[1];
+  const float tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + cam.t[2];
+  if (!(tz > cam.near_p && tz < cam.far_p)) return false;
+  if (!__builtin_isfinite(tx) || !__builtin_isfinite(ty)) return false;
+  tcam[0] = tx; tcam[1] = ty; tcam[2] = tz;
+
+  const float n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
+  if (!(n2 > 0.0f) || !__builtin_isfinite(n2)) return false;
+  const float nr = sqrtf(n2);
+  qn[0] = q[0] / nr; qn[1] = q[1] / nr; qn[2] = q[2] / nr; qn[3] = q[3] / nr; qn[4] = nr;
+  quat_to_rot(qn[0], qn[1], qn[2], qn[3], Rq);
+  float M[9];
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) M[i * 3 + j] = Rq[i * 3 + j] * s[j];
+  // Sigma = M M^T (upper triangle: 00 01 02 11 12 22)
+  {
+    int k = 0;
+    for (int i = 0; i < 3; ++i)
+      for (int j = i; j < 3; ++j)
+        Sig[k++] = (M[i * 3 + 0] * M[j * 3 + 0] + M[i * 3 + 1] * M[j * 3 + 1]) +
+                   M[i * 3 + 2] * M[j * 3 + 2];
+  }
+  const float S00 = Sig[0], S01 = Sig[1], S02 = Sig[2], S11 = Sig[3], S12 = Sig[4], S22 = Sig[5];
+  const float Sf[9] = {S00, S01, S02, S01, S11, S12, S02, S12, S22};
+
+  const float txz = tx / tz, tyz = ty / tz;
+  const float tanx = (0.5f * (float)cam.W) / cam.fx;
+  const float tany = (0.5f * (float)cam.H) / cam.fy;
+  const float limx = st.fov_clamp * tanx;
+  const float limy = st.fov_clamp * tany;
+  const float cxz = sel_min(limx, sel_max(-limx, txz));
+  const float cyz = sel_min(limy, sel_max(-limy, tyz));
+  g.clampx = (txz > limx) || (txz < -limx);
+  g.clampy = (tyz > limy) || (tyz < -limy);
+  const float xc = cxz * tz, yc = cyz * tz;
+  const float tz2 = tz * tz;
+  const float J00 = cam.fx / tz;
+  const float J02 = -((cam.fx * xc) / tz2);
+  const float J11 = cam.fy / tz;
+  const float J12 = -((cam.fy * yc) / tz2);
+  for (int j = 0; j < 3; ++j) {
+    Tm[0 * 3 + j] = J00 * W[0 * 3 + j] + J02 * W[2 * 3 + j];
+    Tm[1 * 3 + j] = J11 * W[1 * 3 + j] + J12 * W[2 * 3 + j];
+  }
+  float U[6];
+  for (int a = 0; a < 2; ++a)
+    for (int j = 0; j < 3; ++j)
+      U[a * 3 + j] = (Tm[a * 3 + 0] * Sf[0 * 3 + j] + Tm[a * 3 + 1] * Sf[1 * 3 + j]) +
+                     Tm[a * 3 + 2] * Sf[2 * 3 + j];
+  const float c00 = (U[0] * Tm[0] + U[1] * Tm[1]) + U[2] * Tm[2];
+  const float c01 = (U[0] * Tm[3] + U[1] * Tm[4]) + U[2] * Tm[5];
+  const float c11 = (U[3] * Tm[3] + U[4] * Tm[4]) + U[5] * Tm[5];
+  const float a = c00 + st.eps2d;
+  const float b = c01;
+  const float c = c11 + st.eps2d;
+
+  const float det = a * c - b * b;
+  if (!(det > 0.0f) || !__builtin_isfinite(det)) return false;
+  const float A = c / det;
+  const float B = -(b / det);
+  const float C = a / det;
+
+  const float mid = 0.5f * (a + c);
+  const float disc = mid * mid - det;
+  const float lam = mid + sqrtf(sel_max(disc, 0.0f));
+  if (!__builtin_isfinite(lam)) return false;
+  float rf = ceilf(3.0f * sqrtf(lam));
+  if (rf > 16777216.0f) rf = 16777216.0f;
+  const int32_t radius = (int32_t)rf;
+  if (radius <= 0) return false;
+
+  const float u = cam.fx * txz + cam.cx;
+  const float v = cam.fy * tyz + cam.cy;
+  if (!__builtin_isfinite(u) || !__builtin_isfinite(v)) return false;
+
+  const int gx = grid_dim(cam.W), gy = grid_dim(cam.H);
+  tile_rect(u, v, radius, gx, gy, g.x0, g.x1, g.y0, g.y1);
+  if (g.x1 <= g.x0 || g.y1 <= g.y0) return false;
+
+  g.u = u; g.v = v; g.depth = tz;
+  g.a = a; g.b = b; g.c = c;
+  g.A = A; g.B = B; g.C = C;
+  g.radius = radius;
+  return true;
+}
+
+// Real spherical harmonics up to degree 3 at the unit direction (x,y,z),
+// ordered (l, m=-l..l), Condon-Shortley phase.  Each constant is
+// N_lm = sqrt((2l+1)/(4 pi) (l-|m|)!/(l+|m|)!) (times sqrt 2 for m != 0)
+// times the integer factor of the Cartesian polynomial of P_l^|m|.
+namespace shc {
+constexpr float C0 = 0.28209479177387814f;
+constexpr float C1 = 0.4886025119029199f;
+constexpr float C2a = 1.0925484305920792f;   // xy, yz, xz
+constexpr float C2b = 0.31539156525252005f;  // 3z^2 - 1
+constexpr float C2c = 0.5462742152960396f;   // x^2 - y^2
+constexpr float C3a = 0.5900435899266435f;   // y(3x^2-y^2), x(x^2-3y^2)
+constexpr float C3b = 2.890611442640554f;    // xyz
+constexpr float C3c = 0.4570457994644658f;   // y(5z^2-1), x(5z^2-1)
+constexpr float C3d = 0.3731763325901154f;   // z(5z^2-3)
+constexpr float C3e = 1.445305721320277f;    // z(x^2-y^2)
+}  // namespace shc
+
+__device__ inline void sh_basis(int deg, float x, float y, float z, float Y[16]) {
+  using namespace shc;
+  Y[0] = C0;
+  if (deg < 1) return;
+  Y[1] = -C1 * y;
+  Y[2] = C1 * z;
+  Y[3] = -C1 * x;
+  if (deg < 2) return;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  Y[4] = C2a * (x * y);
+  Y[5] = -C2a * (y * z);
+  Y[6] = C2b * (3.0f * zz - 1.0f);
+  Y[7] = -C2a * (x * z);
+  Y[8] = C2c * (xx - yy);
+  if (deg < 3) return;
+  Y[9] = -C3a * (y * (3.0f * xx - yy));
+  Y[10] = C3b * (x * y * z);
+  Y[11] = -C3c * (y * (5.0f * zz - 1.0f));
+  Y[12] = C3d * (z * (5.0f * zz - 3.0f));
+  Y[13] = -C3c * (x * (5.0f * zz - 1.0f));
+  Y[14] = C3e * (z * (xx - yy));
+  Y[15] = -C3a * (x * (xx - 3.0f * yy));
+}
+
+// g[0..2] += w * grad Y_j(x,y,z) for the Cartesian polynomials above.
+__device__ inline void sh_basis_grad_acc(int j, float w, float x, float y, float z, float g[3]) {
+  using namespace shc;
+  const float xx = x * x, yy = y * y, zz = z * z;
+  float dx = 0.0f, dy = 0.0f, dz = 0.0f;
+  switch (j) {
+    case 1: dy = -C1; break;
+    case 2: dz = C1; break;
+    case 3: dx = -C1; break;
+    case 4: dx = C2a * y; dy = C2a * x; break;
+    case 5: dy = -C2a * z; dz = -C2a * y; break;
+    case 6: dz = 6.0f * C2b * z; break;
+    case 7: dx = -C2a * z; dz = -C2a * x; break;
+    case 8: dx = 2.0f * C2c * x; dy = -2.0f * C2c * y; break;
+    case 9: dx = -C3a * 6.0f * x * y; dy = -C3a * (3.0f * xx - 3.0f * yy); break;
+    case 10: dx = C3b * y * z; dy = C3b * x * z; dz = C3b * x * y; break;
+    case 11: dy = -C3c * (5.0f * zz - 1.0f); dz = -C3c * 10.0f * y * z; break;
+    case 12: dz = C3d * (15.0f * zz - 3.0f); break;
+    case 13: dx = -C3c * (5.0f * zz - 1.0f); dz = -C3c * 10.0f * x * z; break;
+    case 14: dx = 2.0f * C3e * x * z; dy = -2.0f * C3e * y * z; dz = C3e * (xx - yy); break;
+    case 15: dx = -C3a * (3.0f * xx - 3.0f * yy); dy = C3a * 6.0f * x * y; break;
+    default: break;
+  }
+  g[0] = fmaf(w, dx, g[0]);
+  g[1] = fmaf(w, dy, g[1]);
+  g[2] = fmaf(w, dz, g[2]);
+}
+
+__device__ inline void camera_centre(const Cam& cam, float c[3]) {
+  for (int j = 0; j < 3; ++j)
+    c[j] = -(cam.R[0 * 3 + j] * cam.t[0] + cam.R[1 * 3 + j] * cam.t[1] +
+             cam.R[2 * 3 + j] * cam.t[2]);
+}
+
+// colour = max(0, offset + sum_j Y_j(d) c_j) per channel; raw values kept
+// for the clamp mask of the backward.
+__device__ inline void sh_colour(int deg, int K, const float* __restrict__ sh, int64_t ld,
+                                 int64_t i, const float d[3], float off, float raw[3],
+                                 float Y[16]) {
+  sh_basis(deg, d[0], d[1], d[2], Y);
+  raw[0] = raw[1] = raw[2] = off;
+  for (int j = 0; j < K; ++j)
+    for (int ch = 0; ch < 3; ++ch)
+      raw[ch] = fmaf(Y[j], sh[(int64_t)(j * 3 + ch) * ld + i], raw[ch]);
+}
+
+__global__ __launch_bounds__(256) void project_fwd_kernel(
+    int64_t N, int64_t ld, int deg, const float* __restrict__ means,
+    const float* __restrict__ scales, const float* __restrict__ quats,
+    const float* __restrict__ sh, Cam cam, Settings st, float* __restrict__ means2d,
+    float* __restrict__ conics, float* __restrict__ depths, int32_t* __restrict__ radii,
+    float* __restrict__ colors, uint32_t* __restrict__ tiles) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
+  const float s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
+  const float q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
+  Geom g;
+  float qn[5], Rq[9], Sig[6], Tm[6], tc[3];
+  const bool vis = project_geom(m, s, q, cam, st, g, qn, Rq, Sig, Tm, tc);
+  if (!vis) {
+    means2d[i] = 0.0f; means2d[ld + i] = 0.0f;
+    conics[i] = 0.0f; conics[ld + i] = 0.0f; conics[2 * ld + i] = 0.0f;
+    depths[i] = 0.0f; radii[i] = 0; tiles[i] = 0u;
+    colors[i] = 0.0f; colors[ld + i] = 0.0f; colors[2 * ld + i] = 0.0f;
+    return;
+  }
+  means2d[i] = g.u; means2d[ld + i] = g.v;
+  conics[i] = g.A; conics[ld + i] = g.B; conics[2 * ld + i] = g.C;
+  depths[i] = g.depth;
+  radii[i] = g.radius;
+  tiles[i] = (uint32_t)(g.x1 - g.x0) * (uint32_t)(g.y1 - g.y0);
+
+  float cc[3];
+  camera_centre(cam, cc);
+  float dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
+  const float L = sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+  const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
+  const int K = (deg + 1) * (deg + 1);
+  float raw[3], Y[16];
+  sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
+  for (int ch = 0; ch < 3; ++ch) colors[(int64_t)ch * ld + i] = raw[ch] < 0.0f ? 0.0f : raw[ch];
+}
+
+// Backward of the projection, chain rule in fp32.  The forward's geometry is
+// recomputed with the same code, so every decision (cull, fov clamp, colour
+// clamp) is the forward's.
+__global__ __launch_bounds__(256) void project_bwd_kernel(
+    int64_t N, int64_t ld, int deg, const float* __restrict__ means,
+    const float* __restrict__ scales, const float* __restrict__ quats,
+    const float* __restrict__ sh, Cam cam, Settings st, const int32_t* __restrict__ radii,
+    const float* __restrict__ g_m2, const float* __restrict__ g_con,
+    const float* __restrict__ g_col, float* __restrict__ o_means, float* __restrict__ o_scales,
+    float* __restrict__ o_quats, float* __restrict__ o_sh, int accumulate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const int K = (deg + 1) * (deg + 1);
+  float gm[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0};
+  const bool vis = radii[i] > 0;
+  Geom g;
+  float qn[5], Rq[9], Sig[6], Tm[6], tc[3];
+  const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
+  const float s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
+  bool ok = false;
+  if (vis) {
+    const float q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
+    ok = project_geom(m, s, q, cam, st, g, qn, Rq, Sig, Tm, tc);
+  }
+  if (!ok) {
+    if (!accumulate) {
+      for (int k = 0; k < 3; ++k) { o_means[(int64_t)k * ld + i] = 0.0f; o_scales[(int64_t)k * ld + i] = 0.0f; }
+      for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + i] = 0.0f;
+      for (int k = 0; k < 3 * K; ++k) o_sh[(int64_t)k * ld + i] = 0.0f;
+    }
+    return;
+  }
+  const float* W = cam.R;
+  const float tx = tc[0], ty = tc[1], tz = tc[2];
+  const float fx = cam.fx, fy = cam.fy;
+
+  // conic (A,B,C) = (c, -b, a) / det  ->  gradients on (a, b, c)
+  const float a = g.a, b = g.b, c = g.c;
+  const float det = a * c - b * b;
+  const float id = 1.0f / det, id2 = id * id;
+  const float gA = g_con[i], gB = g_con[ld + i], gC = g_con[2 * ld + i];
+  const float ga = gA * (-c * c * id2) + gB * (b * c * id2) + gC * (id - a * c * id2);
+  const float gb = gA * (2.0f * b * c * id2) + gB * (-id - 2.0f * b * b * id2) + gC * (2.0f * a * b * id2);
+  const float gc = gA * (id - a * c * id2) + gB * (a * b * id2) + gC * (-a * a * id2);
+
+  const float Sf[9] = {Sig[0], Sig[1], Sig[2], Sig[1], Sig[3], Sig[4], Sig[2], Sig[4], Sig[5]};
+  float ST0[3], ST1[3];
+  for (int r = 0; r < 3; ++r) {
+    ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
+    ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
+  }
+  // dL/dSigma (general 3x3) = ga T0^T T0 + gb T0^T T1 + gc T1^T T1
+  float gSig[9];
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k)
+      gSig[r * 3 + k] = ga * Tm[r] * Tm[k] + gb * Tm[r] * Tm[3 + k] + gc * Tm[3 + r] * Tm[3 + k];
+  float gT0[3], gT1[3];
+  for (int r = 0; r < 3; ++r) {
+    gT0[r] = 2.0f * ga * ST0[r] + gb * ST1[r];
+    gT1[r] = gb * ST0[r] + 2.0f * gc * ST1[r];
+  }
+  float gJ00 = 0.0f, gJ02 = 0.0f, gJ11 = 0.0f, gJ12 = 0.0f;
+  for (int j = 0; j < 3; ++j) {
+    gJ00 += gT0[j] * W[j];
+    gJ02 += gT0[j] * W[6 + j];
+    gJ11 += gT1[j] * W[3 + j];
+    gJ12 += gT1[j] * W[6 + j];
+  }
+  const float itz = 1.0f / tz, itz2 = itz * itz, itz3 = itz2 * itz;
+  float gt[3] = {0.0f, 0.0f, 0.0f};
+  gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
+  const float limx = st.fov_clamp * ((0.5f * (float)cam.W) / fx);
+  const float limy = st.fov_clamp * ((0.5f * (float)cam.H) / fy);
+  if (g.clampx) {
+    const float cl = tx / tz > 0.0f ? limx : -limx;
+    gt[2] += gJ02 * (fx * cl * itz2);
+  } else {
+    gt[0] += gJ02 * (-fx * itz2);
+    gt[2] += gJ02 * (2.0f * fx * tx * itz3);
+  }
+  if (g.clampy) {
+    const float cl = ty / tz > 0.0f ? limy : -limy;
+    gt[2] += gJ12 * (fy * cl * itz2);
+  } else {
+    gt[1] += gJ12 * (-fy * itz2);
+    gt[2] += gJ12 * (2.0f * fy * ty * itz3);
+  }
+  const float gu = g_m2[i], gv = g_m2[ld + i];
+  gt[0] += gu * fx * itz;
+  gt[2] += gu * (-fx * tx * itz2);
+  gt[1] += gv * fy * itz;
+  gt[2] += gv * (-fy * ty * itz2);
+  for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
+
+  // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M
+  float M[9];
+  for (int r = 0; r < 3; ++r)
+    for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
+  float gR[9];
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k) {
+      float acc = 0.0f;
+      for (int j = 0; j < 3; ++j) acc += (gSig[r * 3 + j] + gSig[j * 3 + r]) * M[j * 3 + k];
+      gs[k] += acc * Rq[r * 3 + k];
+      gR[r * 3 + k] = acc * s[k];
+    }
+  const float w = qn[0], x = qn[1], y = qn[2], z = qn[3];
+  float gqn[4];
+  gqn[0] = 2.0f * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
+  gqn[1] = 2.0f * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
+           4.0f * x * (gR[4] + gR[8]);
+  gqn[2] = 2.0f * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
+           4.0f * y * (gR[0] + gR[8]);
+  gqn[3] = 2.0f * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
+           4.0f * z * (gR[0] + gR[4]);
+  const float dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
+  const float inr = 1.0f / qn[4];
+  for (int k = 0; k < 4; ++k) gq[k] = (gqn[k] - qn[k] * dot) * inr;
+
+  // colour -> SH coefficients and the view direction
+  float cc[3];
+  camera_centre(cam, cc);
+  const float dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
+  const float L = sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+  const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
+  float raw[3], Y[16];
+  sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
+  float gcol[3];
+  for (int ch = 0; ch < 3; ++ch)
+    gcol[ch] = raw[ch] < 0.0f ? 0.0f : g_col[(int64_t)ch * ld + i];
+  float gd[3] = {0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < K; ++j) {
+    float wj = 0.0f;
+    for (int ch = 0; ch < 3; ++ch) {
+      const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
+      const float gval = Y[j] * gcol[ch];
+      o_sh[p] = accumulate ? o_sh[p] + gval : gval;
+      wj = fmaf(gcol[ch], sh[p], wj);
+    }
+    if (j > 0) sh_basis_grad_acc(j, wj, d[0], d[1], d[2], gd);
+  }
+  const float dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+  const float iL = 1.0f / L;
+  for (int e = 0; e < 3; ++e) gm[e] += (gd[e] - d[e] * dd) * iL;
+
+  for (int k = 0; k < 3; ++k) {
+    const int64_t p = (int64_t)k * ld + i;
+    o_means[p] = accumulate ? o_means[p] + gm[k] : gm[k];
+    o_scales[p] = accumulate ? o_scales[p] + gs[k] : gs[k];
+  }
+  for (int k = 0; k < 4; ++k) {
+    const int64_t p = (int64_t)k * ld + i;
+    o_quats[p] = accumulate ? o_quats[p] + gq[k] : gq[k];
+  }
+}
+
+}  // namespace gs
+
+extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
+                                            const float* scales, const float* quats,
+                                            const float* sh, const gs::Cam& cam,
+                                            const gs::Settings& st, float* means2d,
+                                            float* conics, float* depths, int32_t* radii,
+                                            float* colors, uint32_t* tiles, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t blocks = (N + 255) / 256;
+  hipLaunchKernelGGL(gs::project_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
+                     deg, means, scales, quats, sh, cam, st, means2d, conics, depths, radii,
+                     colors, tiles);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, const float* means,
+                                            const float* scales, const float* quats,
+                                            const float* sh, const gs::Cam& cam,
+                                            const gs::Settings& st, const int32_t* radii,
+                                            const float* g_m2, const float* g_con,
+                                            const float* g_col, float* o_means, float* o_scales,
+                                            float* o_quats, float* o_sh, int accumulate,
+                                            hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t blocks = (N + 255) / 256;
+  hipLaunchKernelGGL(gs::project_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
+                     deg, means, scales, quats, sh, cam, st, radii, g_m2, g_con, g_col, o_means,
+                     o_scales, o_quats, o_sh, accumulate);
+  return hipGetLastError();
+}

@@ -1,0 +1,335 @@
+"""Thin ctypes binding of libgsraster.so.
+
+The functions below carry the names of the C entry points declared in
+``include/gsraster.h`` and do argument marshalling only: every stage runs in
+the library's HIP kernels.  PyTorch supplies device memory and the stream
+(``torch.cuda.current_stream()``); no compute happens in torch.  There is no
+fallback: if the library is missing or the device is not a GPU, calls raise.
+
+Array layout is the library's: per-Gaussian structure-of-arrays planes
+``[P, ld]`` (float32/int32/uint32, contiguous), images ``[H, W, 3]`` and
+``[H, W]``.  :class:`Frame` strings the five calls together with caller-owned
+buffers (growing the instance capacity when ``gs_bin_and_sort`` asks for it).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgsraster.so")
+
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
+EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_tiles",
+            "gs_project_fwd", "gs_bin_and_sort_workspace_size", "gs_bin_and_sort",
+            "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd", "gs_image_loss_grad")
+
+
+class GsError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (status, msg))
+        self.status = status
+
+
+class gs_camera(C.Structure):
+    _fields_ = [("R", C.c_float * 9), ("t", C.c_float * 3), ("fx", C.c_float),
+                ("fy", C.c_float), ("cx", C.c_float), ("cy", C.c_float),
+                ("width", C.c_int32), ("height", C.c_int32),
+                ("near_plane", C.c_float), ("far_plane", C.c_float)]
+
+
+class gs_settings(C.Structure):
+    _fields_ = [(k, C.c_float) for k in
+                ("eps2d", "alpha_min", "alpha_max", "T_min", "fov_clamp", "sh_offset")]
+
+
+_lib = None
+
+
+def load():
+    """Load libgsraster.so (built in-tree by ``build.py``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgsraster.so is not built: run differentiable_rasterization_amd/build.py")
+    lib = C.CDLL(LIB_PATH)
+    P, i64, i32, u64 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint64
+    lib.gs_default_settings.restype = gs_settings
+    lib.gs_default_settings.argtypes = []
+    lib.gs_status_string.restype = C.c_char_p
+    lib.gs_status_string.argtypes = [C.c_int]
+    lib.gs_last_error.restype = C.c_char_p
+    lib.gs_last_error.argtypes = []
+    lib.gs_num_tiles.restype = i32
+    lib.gs_num_tiles.argtypes = [i32, i32]
+    lib.gs_project_fwd.restype = C.c_int
+    lib.gs_project_fwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 6 + [P]
+    lib.gs_bin_and_sort_workspace_size.restype = C.c_size_t
+    lib.gs_bin_and_sort_workspace_size.argtypes = [i64, u64, i32, i32]
+    lib.gs_bin_and_sort.restype = C.c_int
+    lib.gs_bin_and_sort.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
+                                    C.c_size_t, P]
+    lib.gs_rasterize_fwd.restype = C.c_int
+    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 8 + [P, P] + [P] * 4 + [P]
+    lib.gs_rasterize_bwd.restype = C.c_int
+    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 7 + [P] + [P] * 3 + [P] * 4 + \
+        [i32, P]
+    lib.gs_project_bwd.restype = C.c_int
+    lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 4 + [P] * 4 + \
+        [i32, P]
+    lib.gs_image_loss_grad.restype = C.c_int
+    lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != GS_OK:
+        lib = load()
+        raise GsError(lib.gs_status_string(status).decode(), lib.gs_last_error().decode())
+
+
+def _p(t):
+    """Device (or host) pointer of a tensor/array, None for None."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data_as(C.c_void_p)
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def make_camera(cam) -> gs_camera:
+    """gs_camera from any object with R, t, fx, fy, cx, cy, width, height, near, far."""
+    c = gs_camera()
+    R = np.asarray(cam.R, np.float32).reshape(9)
+    t = np.asarray(cam.t, np.float32).reshape(3)
+    for i in range(9):
+        c.R[i] = float(R[i])
+    for i in range(3):
+        c.t[i] = float(t[i])
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.near_plane = float(getattr(cam, "near", 0.01))
+    c.far_plane = float(getattr(cam, "far", 1e10))
+    return c
+
+
+def default_settings(**overrides) -> gs_settings:
+    s = load().gs_default_settings()
+    for k, v in overrides.items():
+        setattr(s, k, float(v))
+    return s
+
+
+def num_tiles(width, height) -> int:
+    return int(load().gs_num_tiles(int(width), int(height)))
+
+
+# ---------------------------------------------------------------------------
+# The entry points
+# ---------------------------------------------------------------------------
+def gs_project_fwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, means2d, conics,
+                   depths, radii, colors, tiles_touched, stream=None):
+    lib = load()
+    _check(lib.gs_project_fwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
+                              C.byref(cam), C.byref(settings), _p(means2d), _p(conics),
+                              _p(depths), _p(radii), _p(colors), _p(tiles_touched),
+                              _stream(stream)))
+
+
+def gs_bin_and_sort_workspace_size(N, capacity, width, height) -> int:
+    return int(load().gs_bin_and_sort_workspace_size(N, capacity, width, height))
+
+
+def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                    capacity, keys, ids, tile_ranges, workspace, workspace_bytes, stream=None):
+    """Returns (status, M); GS_ERR_CAPACITY is returned, not raised."""
+    lib = load()
+    M = C.c_uint64(0)
+    st = lib.gs_bin_and_sort(N, ld, _p(means2d), _p(radii), _p(depths), _p(tiles_touched),
+                             width, height, _p(offsets), capacity, C.byref(M), _p(keys), _p(ids),
+                             _p(tile_ranges), _p(workspace), workspace_bytes, _stream(stream))
+    if st not in (GS_OK, GS_ERR_CAPACITY):
+        _check(st)
+    return st, int(M.value)
+
+
+def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
+                     depths, background, settings, image, final_T, last_idx, out_depth=None,
+                     out_alpha=None, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
+                                _p(conics), _p(opacities), _p(colors), _p(depths), bg,
+                                C.byref(settings), _p(image), _p(final_T), _p(last_idx),
+                                _p(out_depth), _p(out_alpha), _stream(stream)))
+
+
+def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
+                     background, settings, final_T, last_idx, dL_dimage, dL_dmeans2d,
+                     dL_dconics, dL_dopacities, dL_dcolors, accumulate=0, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
+                                _p(conics), _p(opacities), _p(colors), bg, C.byref(settings),
+                                _p(final_T), _p(last_idx), _p(dL_dimage), _p(dL_dmeans2d),
+                                _p(dL_dconics), _p(dL_dopacities), _p(dL_dcolors),
+                                int(accumulate), _stream(stream)))
+
+
+def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii,
+                   dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans, dL_dscales, dL_dquats,
+                   dL_dsh, accumulate=0, stream=None):
+    lib = load()
+    _check(lib.gs_project_bwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
+                              C.byref(cam), C.byref(settings), _p(radii), _p(dL_dmeans2d),
+                              _p(dL_dconics), _p(dL_dcolors), _p(dL_dmeans), _p(dL_dscales),
+                              _p(dL_dquats), _p(dL_dsh), int(accumulate), _stream(stream)))
+
+
+def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
+    lib = load()
+    _check(lib.gs_image_loss_grad(int(kind), int(count), _p(image), _p(target), _p(dL_dimage),
+                                  _p(loss), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Device-resident Gaussians and a frame orchestrator
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class Gaussians:
+    """Parameters as SoA planes [P, ld] on the GPU (first N columns used)."""
+    means: "object"
+    scales: "object"
+    quats: "object"
+    opacities: "object"
+    sh: "object"
+    sh_degree: int
+    N: int
+
+    @property
+    def ld(self) -> int:
+        return int(self.means.shape[1])
+
+    @staticmethod
+    def from_scene(scene, device="cuda", ld=None) -> "Gaussians":
+        """Upload a scene with [N, ...] arrays as [P, ld] planes."""
+        import torch
+        N = scene.means.shape[0]
+        ld = N if ld is None else ld
+        K = (scene.sh_degree + 1) ** 2
+
+        def planes(a, P):
+            out = torch.zeros((P, ld), dtype=torch.float32, device=device)
+            if N:
+                out[:, :N] = torch.from_numpy(np.ascontiguousarray(
+                    np.asarray(a, np.float32).reshape(N, P).T)).to(device)
+            return out
+        return Gaussians(planes(scene.means, 3), planes(scene.scales, 3), planes(scene.quats, 4),
+                         planes(scene.opacities, 1), planes(scene.sh, 3 * K), scene.sh_degree, N)
+
+
+class Frame:
+    """Buffers and calls for one camera: projection, binning + sort,
+    compositing, and the two backward stages.  All buffers are torch tensors
+    on the current device; only ``gs_bin_and_sort`` synchronises (to read
+    the instance count)."""
+
+    def __init__(self, ld, sh_degree, width, height, capacity=None, settings=None,
+                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda"):
+        import torch
+        self.torch = torch
+        self.device = device
+        self.ld, self.sh_degree, self.W, self.H = int(ld), int(sh_degree), int(width), int(height)
+        self.K = (sh_degree + 1) ** 2
+        self.settings = settings if settings is not None else default_settings()
+        self.background = tuple(float(x) for x in background)
+        self.T = num_tiles(width, height)
+        # index buffers use signed torch dtypes of the same width: the library
+        # reads them as uint32/uint64 and torch only supplies the storage
+        f32, i32, u32 = torch.float32, torch.int32, torch.int32
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.means2d, self.conics = z((2, ld), f32), z((3, ld), f32)
+        self.depths, self.radii = z((ld,), f32), z((ld,), i32)
+        self.colors, self.tiles = z((3, ld), f32), z((ld,), u32)
+        self.offsets = z((max(ld, 1),), u32)
+        self.ranges = z((self.T, 2), u32)
+        self.image = z((height, width, 3), f32)
+        self.final_T = z((height, width), f32)
+        self.last_idx = z((height, width), u32)
+        self.out_depth = z((height, width), f32) if with_depth_alpha else None
+        self.out_alpha = z((height, width), f32) if with_depth_alpha else None
+        self.g_means2d, self.g_conics = z((2, ld), f32), z((3, ld), f32)
+        self.g_opacities, self.g_colors = z((ld,), f32), z((3, ld), f32)
+        self.g_means, self.g_scales = z((3, ld), f32), z((3, ld), f32)
+        self.g_quats, self.g_sh = z((4, ld), f32), z((3 * self.K, ld), f32)
+        self.dL_dimage = z((height, width, 3), f32)
+        self.loss = z((1,), f32)
+        self.M = 0
+        self._alloc_sort(capacity if capacity else max(1024, 4 * ld))
+
+    def _alloc_sort(self, capacity):
+        torch = self.torch
+        self.capacity = int(capacity)
+        self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
+        self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
+        self.ws_bytes = gs_bin_and_sort_workspace_size(self.ld, self.capacity, self.W, self.H)
+        self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8, device=self.device)
+        # 256-byte alignment of the workspace start
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws = self.workspace[off:off + self.ws_bytes]
+
+    def project(self, g: Gaussians, cam):
+        self.cam = make_camera(cam)
+        gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
+                       self.settings, self.means2d, self.conics, self.depths, self.radii,
+                       self.colors, self.tiles)
+
+    def bin_and_sort(self, g: Gaussians):
+        st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
+                                self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
+                                self.ranges, self.ws, self.ws_bytes)
+        if st == GS_ERR_CAPACITY:
+            self._alloc_sort(int(M * 1.25) + 1024)
+            st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
+                                    self.W, self.H, self.offsets, self.capacity, self.keys,
+                                    self.ids, self.ranges, self.ws, self.ws_bytes)
+            _check(st)
+        self.M = M
+        return M
+
+    def rasterize(self, g: Gaussians):
+        gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.means2d,
+                         self.conics, g.opacities, self.colors, self.depths, self.background,
+                         self.settings, self.image, self.final_T, self.last_idx, self.out_depth,
+                         self.out_alpha)
+
+    def forward(self, g: Gaussians, cam):
+        self.project(g, cam)
+        self.bin_and_sort(g)
+        self.rasterize(g)
+        return self.image
+
+    def loss_grad(self, target, kind):
+        gs_image_loss_grad(kind, self.W * self.H * 3, self.image, target, self.dL_dimage,
+                           self.loss)
+
+    def backward(self, g: Gaussians, dL_dimage=None, accumulate=0):
+        dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.means2d,
+                         self.conics, g.opacities, self.colors, self.background, self.settings,
+                         self.final_T, self.last_idx, dl, self.g_means2d, self.g_conics,
+                         self.g_opacities, self.g_colors, accumulate)
+        gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
+                       self.settings, self.radii, self.g_means2d, self.g_conics, self.g_colors,
+                       self.g_means, self.g_scales, self.g_quats, self.g_sh, accumulate)

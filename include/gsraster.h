@@ -1,0 +1,199 @@
+/*
+ * gsraster.h — C ABI of libgsraster.so, the MI355X (gfx950) differentiable
+ * tile rasterizer of 3D Gaussian Splatting.
+ *
+ * The five stages follow the pipeline the gsplat guide (lmnt.cn/news/262699)
+ * describes in §2.1 — transform each Gaussian by (R, t, scale, rotation),
+ * project it to depth and screen space, then alpha-blend it differentiably —
+ * with the blending backward callable on its own (gsplat guide §2.2) and
+ * accumulating per-Gaussian gradients with atomics (3DGS deployment guide
+ * (hmyw.cn/news/140031) §2.1; Moore Threads MUSA article
+ * (qwbw.cn/news/278220) §2.1).  The primitive is a position, a covariance
+ * built from scale and rotation (MUSA article §3.3), an opacity and SH colour
+ * coefficients (deployment guide §1).  Formulas below the stage level are the
+ * textbook EWA-splatting reading; the pages print none.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers unless marked HOST.  Every buffer is owned by the
+ *     caller; the library allocates nothing and keeps no state between calls
+ *     (calls on different streams may run concurrently on distinct buffers).
+ *   - Per-Gaussian arrays are fp32/int32 structure-of-arrays planes with a
+ *     leading dimension ld >= N: plane p of array X starts at X + p*ld.
+ *       means [3][ld] (world x,y,z)   scales [3][ld] (activated, > 0)
+ *       quats [4][ld] (w,x,y,z, any non-zero norm; normalised inside)
+ *       opacities [ld] (activated, in [0,1])
+ *       sh [K*3][ld], K = (sh_degree+1)^2, plane k*3+c = coefficient k of
+ *       colour channel c, coefficients ordered (l, m=-l..l), real SH with the
+ *       Condon-Shortley phase; colour = max(0, sh_offset + sum_k Y_k(d) c_k)
+ *       with d the unit vector from the camera centre to the mean.
+ *     (Opacity = sigmoid(logit), scale = exp(log-scale) and the quaternion's
+ *     w-first order are those of the gsplat guide §3.3; the activations stay
+ *     with the caller, so gradients are with respect to activated values.)
+ *   - Images are row-major [H][W] (colour [H][W][3]); pixel (px,py) has its
+ *     centre at (px+0.5, py+0.5); tiles are 16x16, T = ceil(W/16)*ceil(H/16),
+ *     tile id = ty*ceil(W/16) + tx.
+ *   - stream is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on it except gs_bin_and_sort, which reads the instance
+ *     count back to the host once.
+ *   - Errors: invalid arguments are rejected on the host before anything is
+ *     launched (GS_ERR_INVALID_ARGUMENT); a failed launch returns GS_ERR_HIP.
+ *     gs_last_error() gives a thread-local message.  Non-finite or degenerate
+ *     Gaussians are not errors: they are culled (radius 0, no tiles, zero
+ *     gradients).  N = 0 and zero instances are valid (background image).
+ */
+#ifndef GSRASTER_H
+#define GSRASTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GS_API __attribute__((visibility("default")))
+#else
+#define GS_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARGUMENT = 1,
+  GS_ERR_CAPACITY = 2,
+  GS_ERR_HIP = 3
+} gs_status;
+
+/* Pinhole camera (HOST struct, passed by pointer).  R, t map world to camera
+ * coordinates, t_cam = R x + t, with OpenCV axes (+x right, +y down, +z
+ * forward) as in the world-to-camera view matrix and [fx, fy, cx, cy]
+ * intrinsics of the gsplat guide §3.3. */
+typedef struct {
+  float R[9]; /* row-major */
+  float t[3];
+  float fx, fy, cx, cy;
+  int32_t width, height;
+  float near_plane, far_plane; /* Gaussians with depth outside (near, far) are culled */
+} gs_camera;
+
+/* Constants of the method (HOST struct).  gs_default_settings() returns
+ * eps2d 0.3 (screen-space dilation added to the 2D covariance diagonal),
+ * alpha_min 1/255 (pairs below are skipped), alpha_max 0.99 (alpha clamp),
+ * T_min 1e-4 (a pixel stops before the Gaussian that would take its
+ * transmittance below this), fov_clamp 1.3 (the EWA Jacobian is evaluated
+ * with x/z, y/z clamped to 1.3 times the half field of view), sh_offset 0.5. */
+typedef struct {
+  float eps2d, alpha_min, alpha_max, T_min, fov_clamp, sh_offset;
+} gs_settings;
+
+GS_API gs_settings gs_default_settings(void);
+GS_API const char* gs_status_string(gs_status s);
+GS_API const char* gs_last_error(void);
+GS_API int32_t gs_num_tiles(int32_t width, int32_t height);
+
+/* Stage 1 — projection (gsplat guide §2.1, steps "3D transform" and "depth
+ * and screen projection"; covariance from scale and rotation, MUSA article
+ * §3.3).  Per Gaussian: t = R mean + t; cull outside (near, far) or
+ * non-finite; Sigma = R(q) S S^T R(q)^T; 2D covariance J W Sigma W^T J^T
+ * plus eps2d on the diagonal, with J the pinhole Jacobian; conic = its
+ * inverse; radius = ceil(3 sqrt(lambda_max)); pixel mean; number of 16x16
+ * tiles the square [u-r,u+r]x[v-r,v+r] touches; SH colour.
+ * Outputs ([p][ld] planes): means2d [2][ld] (u,v), conics [3][ld] (A,B,C of
+ * q = A dx^2 + 2B dx dy + C dy^2), depths [ld] (camera z), radii [ld],
+ * colors [3][ld], tiles_touched [ld].  Culled Gaussians get radius 0,
+ * tiles 0 and zeros elsewhere.  The geometric outputs are computed in IEEE
+ * fp32 in a fixed operation order without contraction, so they are
+ * reproducible bit for bit. */
+GS_API gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree,
+                         const float* means, const float* scales, const float* quats,
+                         const float* sh, const gs_camera* cam, const gs_settings* settings,
+                         float* means2d, float* conics, float* depths, int32_t* radii,
+                         float* colors, uint32_t* tiles_touched, void* stream);
+
+/* Workspace needed by gs_bin_and_sort for N Gaussians and up to `capacity`
+ * tile instances on a width x height image. */
+GS_API size_t gs_bin_and_sort_workspace_size(int64_t N, uint64_t capacity, int32_t width,
+                                      int32_t height);
+
+/* Stages 2-3 — binning and sort.  offsets = exclusive scan of tiles_touched
+ * (Gaussian order); M = total.  *num_instances (HOST) receives M; this is the
+ * one device-to-host read of a frame.  If M > capacity the call returns
+ * GS_ERR_CAPACITY with offsets valid and keys untouched: grow the buffers and
+ * call again.  Otherwise every visible Gaussian i is duplicated once per
+ * touched tile (row-major within its rect) at slot offsets[i] + k with key
+ * (tile_id << 32) | bits(depth_i) and value i; the (key, value) pairs are
+ * radix-sorted stably by key (equal keys keep ascending Gaussian index) into
+ * keys [capacity] / ids [capacity]; tile_ranges [T][2] receives each tile's
+ * [start, end) in the sorted list ((0,0) for empty tiles).  M must be below
+ * 2^30.  workspace: device memory of at least
+ * gs_bin_and_sort_workspace_size() bytes, 256-byte aligned. */
+GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int32_t* radii,
+                          const float* depths, const uint32_t* tiles_touched, int32_t width,
+                          int32_t height, uint32_t* offsets, uint64_t capacity,
+                          uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                          uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Stage 4 — front-to-back alpha compositing per 16x16 tile (gsplat guide
+ * §2.1, "differentiable alpha-blending rasterisation").  Per pixel, over its
+ * tile's sorted list: q from the conic at (px+0.5-u, py+0.5-v); skip q < 0;
+ * alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop (without
+ * blending) when T (1-alpha) < T_min; else C += colour alpha T, T *= 1-alpha.
+ * Outputs: image [H][W][3] = C + T bg; final_T [H][W]; last_idx [H][W] =
+ * number of the tile's list entries up to and including the last blended one
+ * (0 if none); out_depth [H][W] = sum alpha T depth and out_alpha [H][W] =
+ * 1 - T when non-NULL.  background: HOST float[3]. */
+GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
+                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const float* means2d, const float* conics, const float* opacities,
+                           const float* colors, const float* depths, const float* background,
+                           const gs_settings* settings, float* image, float* final_T,
+                           uint32_t* last_idx, float* out_depth, float* out_alpha,
+                           void* stream);
+
+/* Stage 5a — compositing backward (gsplat guide §2.2).  Walks each pixel's
+ * blended list back to front from last_idx, recovering T by division and
+ * accumulating the colour behind, and adds per-Gaussian gradients of the
+ * loss with respect to means2d [2][ld], conics [3][ld] (A, B, C as scalars of
+ * q), opacities [ld] and colors [3][ld], given dL_dimage [H][W][3].  Pairs
+ * whose alpha was clamped at alpha_max carry no opacity/conic/mean gradient.
+ * accumulate = 0 zero-fills the N entries of each output first;
+ * accumulate = 1 adds to their contents.  Additions use fp32 atomics, so the
+ * low bits vary between runs. */
+GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
+                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const float* means2d, const float* conics, const float* opacities,
+                           const float* colors, const float* background,
+                           const gs_settings* settings, const float* final_T,
+                           const uint32_t* last_idx, const float* dL_dimage,
+                           float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
+                           float* dL_dcolors, int32_t accumulate, void* stream);
+
+/* Stage 5b — projection backward: chain rule from (u, v), the conic and the
+ * colour to means [3][ld], scales [3][ld], quats [4][ld] (through the
+ * normalisation) and sh [K*3][ld].  Visibility comes from radii (the forward's
+ * decisions are kept: the fov clamp and the colour clamp are re-evaluated
+ * from the same fp32 inputs).  accumulate = 0 overwrites (zeros for culled
+ * Gaussians); 1 adds. */
+GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
+                         const float* scales, const float* quats, const float* sh,
+                         const gs_camera* cam, const gs_settings* settings,
+                         const int32_t* radii, const float* dL_dmeans2d,
+                         const float* dL_dconics, const float* dL_dcolors, float* dL_dmeans,
+                         float* dL_dscales, float* dL_dquats, float* dL_dsh,
+                         int32_t accumulate, void* stream);
+
+/* Loss gradient of a rendered image against a target, both [count] floats:
+ * kind 0 = L2 (sum (x-y)^2, gradient 2(x-y)), kind 1 = L1 (sum |x-y|,
+ * gradient sign(x-y), sign(0) = 0).  Writes dL_dimage [count]; if loss (a
+ * device float) is non-NULL it is overwritten with the loss value.  Sum
+ * reduction, as the L2 loss of the 1,024-Gaussian case and the L1 loss of the
+ * clustered cases are defined. */
+GS_API gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* image,
+                             const float* target, float* dL_dimage, float* loss,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GSRASTER_H */

@@ -1,0 +1,145 @@
+"""Helpers shared by the GPU parity tests: run a frame through the HIP
+library and through the CPU oracle on the same seeded inputs, and compare.
+
+Tolerances (fp32 GPU against the oracle's fp32 key path + fp64 values):
+  * integer outputs and the fp32 key path (means2d, conics, depths, radii,
+    tiles touched, offsets, keys, ids, ranges): bit-exact;
+  * pixels (image, final_T): max |diff| <= 1e-4;
+  * gradients: |g_gpu - g_oracle| <= max(1e-3 |g_oracle|, 1e-5).
+Mismatches are never hidden by widening these; they are classified:
+  * threshold flip: the oracle's pixel has a threshold decision (alpha vs
+    alpha_min or alpha_max, T' vs T_min) within FLIP_REL relative distance,
+    where fp32 exp/rounding on the GPU may legitimately decide the other way;
+    gradients of Gaussians listed in a tile holding such a pixel inherit it;
+  * cancellation: a gradient that is a sum of per-pixel terms of mixed sign,
+    whose error stays within COND_K * eps32 * sum|terms| (the fp32 summation
+    bound) although it exceeds the relative tolerance.
+Counts of both are reported and bounded by the tests; anything else fails.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+PIX_TOL = 1e-4
+G_REL, G_ABS = 1e-3, 1e-5
+FLIP_REL = 2e-4
+EPS32 = 2.0 ** -24
+COND_K = 256
+
+
+def torch_cuda():
+    import torch
+    return torch
+
+
+def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
+              loss_kind=None, target=None, backward=True, depth_alpha=False, capacity=None,
+              dL_dimage=None):
+    """Run the five stages on the GPU; returns numpy arrays in the natural
+    [N, ...] layout plus the raw Frame."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    g = raster.Gaussians.from_scene(scene, ld=ld)
+    st = raster.default_settings(**(settings or {}))
+    fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=capacity,
+                      settings=st, background=background, with_depth_alpha=depth_alpha)
+    fr.forward(g, cam)
+    out = {}
+    if backward:
+        if dL_dimage is not None:
+            dl = torch.from_numpy(np.ascontiguousarray(dL_dimage, np.float32)).cuda()
+            fr.backward(g, dl)
+        else:
+            tgt = torch.from_numpy(np.ascontiguousarray(target, np.float32)).cuda()
+            fr.loss_grad(tgt, 0 if loss_kind == "l2" else 1)
+            fr.backward(g)
+    torch.cuda.synchronize()
+    N = scene.n
+    T = lambda t, P=None: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
+    M = fr.M
+    out.update(
+        means2d=T(fr.means2d), conics=T(fr.conics), depths=T(fr.depths), radii=T(fr.radii),
+        colors=T(fr.colors), tiles=T(fr.tiles).view(np.uint32),
+        offsets=fr.offsets[:N].cpu().numpy().view(np.uint32), M=M,
+        keys=fr.keys[:M].cpu().numpy().view(np.uint64), ids=fr.ids[:M].cpu().numpy().view(np.uint32),
+        ranges=fr.ranges.cpu().numpy().view(np.uint32), image=fr.image.cpu().numpy(),
+        final_T=fr.final_T.cpu().numpy(), last=fr.last_idx.cpu().numpy().view(np.uint32))
+    if depth_alpha:
+        out.update(depth=fr.out_depth.cpu().numpy(), alpha=fr.out_alpha.cpu().numpy())
+    if backward:
+        K = (scene.sh_degree + 1) ** 2
+        out.update(dL_dimage=fr.dL_dimage.cpu().numpy() if dL_dimage is None else dL_dimage,
+                   loss=float(fr.loss.cpu().numpy()[0]),
+                   g_means2d=T(fr.g_means2d), g_conics=T(fr.g_conics),
+                   g_opacities=T(fr.g_opacities), g_colors=T(fr.g_colors),
+                   g_means=T(fr.g_means), g_scales=T(fr.g_scales), g_quats=T(fr.g_quats),
+                   g_sh=T(fr.g_sh).reshape(N, K, 3))
+    out["frame"] = fr
+    return out
+
+
+def assert_bits_equal(a, b, what):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    if a.dtype.kind == "f":
+        a = a.astype(np.float32).view(np.uint32)
+        b = b.astype(np.float32).view(np.uint32)
+    bad = np.nonzero(a != b)
+    assert bad[0].size == 0, "%s: %d mismatches, first at %s" % (what, bad[0].size,
+                                                                 tuple(x[0] for x in bad))
+
+
+def flip_tiles(margin, width, height, extra_pixels=None):
+    """Tiles containing a pixel whose oracle margin is below FLIP_REL."""
+    near = margin < FLIP_REL
+    if extra_pixels is not None:
+        near = near | extra_pixels
+    gx = (width + 15) // 16
+    ys, xs = np.nonzero(near)
+    return set(((ys // 16) * gx + (xs // 16)).tolist()), near
+
+
+def compare_pixels(gpu_img, or_img, margin, name="image"):
+    """Returns (n_fail_unexplained, n_flip_exempt, max_abs_diff_nonexempt)."""
+    d = np.abs(np.asarray(gpu_img, np.float64) - or_img)
+    if d.ndim == 3:
+        d = d.max(axis=2)
+    fail = d > PIX_TOL
+    flip = fail & (margin < FLIP_REL)
+    unexplained = fail & ~flip
+    md = float(d[~flip].max()) if (~flip).any() else 0.0
+    return int(unexplained.sum()), int(flip.sum()), md, np.argwhere(unexplained)[:5]
+
+
+def gaussians_in_tiles(ranges, ids, tiles):
+    s = set()
+    for t in tiles:
+        a, b = ranges[t]
+        s.update(ids[a:b].tolist())
+    return s
+
+
+def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
+    """Per-element |diff| <= max(G_REL |g|, G_ABS); classify the rest.
+    Returns dict(fail, flip, cond, checked, worst)."""
+    g_gpu = np.asarray(g_gpu, np.float64).reshape(g_or.shape[0], -1)
+    g_or = np.asarray(g_or, np.float64).reshape(g_or.shape[0], -1)
+    err = np.abs(g_gpu - g_or)
+    tol = np.maximum(G_REL * np.abs(g_or), G_ABS)
+    bad = err > tol
+    flip = np.zeros_like(bad)
+    if exempt_rows is not None and len(exempt_rows):
+        rows = np.fromiter(exempt_rows, dtype=np.int64)
+        flip[rows] = bad[rows]
+    cond = np.zeros_like(bad)
+    if abs_sum is not None:
+        a = np.asarray(abs_sum, np.float64).reshape(bad.shape)
+        cond = bad & ~flip & (err <= COND_K * EPS32 * a)
+    fail = bad & ~flip & ~cond
+    worst = float((err / tol)[~flip & ~cond].max()) if (~flip & ~cond).any() else 0.0
+    where = np.argwhere(fail)[:5]
+    return dict(fail=int(fail.sum()), flip=int(flip.sum()), cond=int(cond.sum()),
+                checked=int(bad.size), worst=worst, where=where.tolist(), name=name)
