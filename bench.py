@@ -1,0 +1,215 @@
+"""Benchmark: forward+backward frames per second of the tile rasterizer on one
+MI355X, with per-stage times, the dominant kernel's roofline fraction and the
+CPU oracle timed on the host for context.
+
+A step is one whole pass of the hot path for one camera: projection, binning
++ radix sort, compositing, loss gradient, compositing backward and
+projection backward.  Inputs (Gaussians, targets, cameras) are resident in
+HBM before the timed region; each step renders the next of the workload's
+seeded poses.
+
+  python bench.py [--steps K] [--warmup W] [--config cluster_1m_1080p]
+                  [--no-cpu-baseline] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd frames/sec at 1M Gaussians 1920×1080 SH3; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+# Plain fp32 VALU issue: 256 CUs x 64 lanes x 2.4 GHz (one non-packed VALU
+# instruction per lane per clock).
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
+    """Algorithmic HBM bytes of each stage (what the method must move with the
+    intermediates the ABI materialises)."""
+    return {
+        "project_fwd": 20 * N + (64 + 12 * K) * V,
+        "bin_and_sort": 8 * N + 20 * V + (28 + 24 * P) * M + 8 * T,
+        "rasterize_fwd": 40 * M + 20 * Px,
+        "loss_grad": 24 * Px,
+        "rasterize_bwd": 36 * N + 36 * V + 40 * M_bwd + 20 * Px,
+        "project_bwd": 4 * N + (72 + 12 * K) * V + (40 + 12 * K) * N,
+    }
+
+
+def cpu_baseline(scene, cams, targets, loss_kind, frames):
+    """The oracle as it stands, fwd+bwd on `frames` poses of the same workload."""
+    import oracle
+    kind = oracle.LOSS_L2 if loss_kind == "l2" else oracle.LOSS_L1
+    t0 = time.perf_counter()
+    for i in range(frames):
+        cam = cams[i % len(cams)]
+        f = oracle.render(scene, cam)
+        dl = oracle.loss_grad_image(f["raster"]["image"], targets[i % len(cams)], kind)
+        oracle.backward(scene, cam, f, dl)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": frames / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": "%d fwd+bwd frame(s) of the same workload (poses 0..%d), %.1f s" %
+                      (frames, frames - 1, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="cluster_1m_1080p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frames", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from differentiable_rasterization_amd import raster, scenes
+
+    torch.cuda.set_device(0)
+    scene, cams, loss_kind = scenes.make_config(args.config)
+    loss_kind = loss_kind or "l1"
+    W, H = cams[0].width, cams[0].height
+    N, K = scene.n, (scene.sh_degree + 1) ** 2
+    targets_np = [scenes.target_image(c, i) for i, c in enumerate(cams)]
+    targets = [torch.from_numpy(t).cuda() for t in targets_np]
+    g = raster.Gaussians.from_scene(scene)
+    fr = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=4 * N)
+    gcams = [raster.make_camera(c) for c in cams]
+    kind = 0 if loss_kind == "l2" else 1
+    P = len(cams)
+    T = fr.T
+    Px = W * H
+    sort_passes = (32 + int(np.ceil(np.log2(max(T, 2)))) + 7) // 8
+    names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "loss_grad", "rasterize_bwd",
+             "project_bwd"]
+
+    def step(i, ev=None):
+        c = gcams[i % P]
+        fr.cam = c
+        if ev is not None:
+            ev[0].record()
+        raster.gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, c,
+                              fr.settings, fr.means2d, fr.conics, fr.depths, fr.radii, fr.colors,
+                              fr.tiles)
+        if ev is not None:
+            ev[1].record()
+        fr.bin_and_sort(g)
+        if ev is not None:
+            ev[2].record()
+        fr.rasterize(g)
+        if ev is not None:
+            ev[3].record()
+        fr.loss_grad(targets[i % P], kind)
+        if ev is not None:
+            ev[4].record()
+        raster.gs_rasterize_bwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
+                                g.opacities, fr.colors, fr.background, fr.settings, fr.final_T,
+                                fr.last_idx, fr.dL_dimage, fr.g_means2d, fr.g_conics,
+                                fr.g_opacities, fr.g_colors, 0)
+        if ev is not None:
+            ev[5].record()
+        raster.gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, c,
+                              fr.settings, fr.radii, fr.g_means2d, fr.g_conics, fr.g_colors,
+                              fr.g_means, fr.g_scales, fr.g_quats, fr.g_sh, 0)
+        if ev is not None:
+            ev[6].record()
+        return fr.M
+
+    # workload statistics per pose (one untimed pass)
+    stats = []
+    for i in range(P):
+        step(i)
+        torch.cuda.synchronize()
+        V = int((fr.radii[:N] > 0).sum().item())
+        rng = fr.ranges.cpu().numpy().view(np.uint32).astype(np.int64)
+        lens = rng[:, 1] - rng[:, 0]
+        last = fr.last_idx.cpu().numpy().view(np.uint32).astype(np.int64)
+        gx = (W + 15) // 16
+        tile_of = (np.arange(H)[:, None] // 16) * gx + (np.arange(W)[None, :] // 16)
+        maxlast = np.zeros(T, np.int64)
+        np.maximum.at(maxlast, tile_of.ravel(), last.ravel())
+        inside = np.bincount(tile_of.ravel(), minlength=T)
+        stats.append(dict(V=V, M=fr.M, M_bwd=int(maxlast.sum()),
+                          pairs=int((inside * lens).sum())))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    stage_ms = {n: 0.0 for n in names}
+    for ev in evs:
+        for k, n in enumerate(names):
+            stage_ms[n] += ev[k].elapsed_time(ev[k + 1])
+    stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
+    # average workload over the poses the timed steps visited
+    visited = [stats[i % P] for i in range(args.steps)]
+    avg = {k: float(np.mean([s[k] for s in visited])) for k in visited[0]}
+    byts = stage_bytes(None, N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes)
+    stages = {}
+    for n in names:
+        ms = stage_ms[n]
+        gbs = byts[n] / (ms * 1e-3) / 1e9
+        stages[n] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    fps = args.steps / dt
+    fwd_ms = stage_ms["project_fwd"] + stage_ms["bin_and_sort"] + stage_ms["rasterize_fwd"]
+    dominant = max(names, key=lambda n: stage_ms[n])
+    # the compositing kernels are bound by VALU issue: algorithmic work =
+    # pixel-splat pairs x VALU instructions per pair in the kernel's loop
+    valu_per_pair = {"rasterize_fwd": 17, "rasterize_bwd": 62}
+    if dominant in valu_per_pair:
+        ops = avg["pairs"] * valu_per_pair[dominant]
+        ach = ops / (stage_ms[dominant] * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
+                "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None,
+                "work_per_launch": {"pairs": int(avg["pairs"]),
+                                    "valu_per_pair": valu_per_pair[dominant]}}
+    else:
+        ach = byts[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": None}
+    c = cams[0]
+    out = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * dt / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "gaussians": N, "width": W, "height": H,
+                   "sh_degree": scene.sh_degree, "poses": P, "loss": loss_kind,
+                   "visible": int(avg["V"]), "instances": int(avg["M"])},
+        "fwd_fps": round(1e3 / fwd_ms, 2),
+        "sort_keys_per_s": round(avg["M"] / (stage_ms["bin_and_sort"] * 1e-3), 1),
+        "stages": stages,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -64,9 +64,36 @@ inline bool operator>(Dual a, Dual b) { return a.v > b.v; }
 inline bool operator<=(Dual a, Dual b) { return a.v <= b.v; }
 inline bool operator>=(Dual a, Dual b) { return a.v >= b.v; }
 
+/* Value with a first-order rounding-error scale m (>= |v|): sums add the
+ * scales, products and quotients propagate them to first order, so that an
+ * fp32 evaluation of the same expression errs by at most about u * m. */
+struct ErrScale {
+  double v, m;
+  ErrScale() : v(0), m(0) {}
+  ErrScale(double x) : v(x), m(std::fabs(x)) {}
+  ErrScale(double x, double mm) : v(x), m(mm) {}
+};
+inline ErrScale operator+(ErrScale a, ErrScale b) { return ErrScale(a.v + b.v, a.m + b.m); }
+inline ErrScale operator-(ErrScale a, ErrScale b) { return ErrScale(a.v - b.v, a.m + b.m); }
+inline ErrScale operator-(ErrScale a) { return ErrScale(-a.v, a.m); }
+inline ErrScale operator*(ErrScale a, ErrScale b) {
+  return ErrScale(a.v * b.v, a.m * std::fabs(b.v) + std::fabs(a.v) * b.m);
+}
+inline ErrScale operator/(ErrScale a, ErrScale b) {
+  return ErrScale(a.v / b.v, a.m / std::fabs(b.v) + std::fabs(a.v) * b.m / (b.v * b.v));
+}
+inline ErrScale& operator+=(ErrScale& a, ErrScale b) { return a = a + b; }
+inline bool operator<(ErrScale a, ErrScale b) { return a.v < b.v; }
+inline bool operator>(ErrScale a, ErrScale b) { return a.v > b.v; }
+inline ErrScale s_sqrt(ErrScale a) {
+  double r = std::sqrt(a.v);
+  return ErrScale(r, r > 0 ? a.m / r : a.m);
+}
+
 inline double val(float x) { return x; }
 inline double val(double x) { return x; }
 inline double val(Dual x) { return x.v; }
+inline double val(ErrScale x) { return x.v; }
 
 inline float s_sqrt(float x) { return std::sqrt(x); }
 inline double s_sqrt(double x) { return std::sqrt(x); }
@@ -239,35 +266,35 @@ template <class T> void sh_basis(int deg, T x, T y, T z, T* Y) {
     }
   }
 }
-/* dY[K][3]: gradient of the Cartesian polynomial of each Y (double only) */
-void sh_basis_grad(int deg, double x, double y, double z, double* dY) {
+/* dY[K][3]: gradient of the Cartesian polynomial of each Y */
+template <class T> void sh_basis_grad(int deg, T x, T y, T z, T* dY) {
   const double sqrt2 = std::sqrt(2.0);
   int j = 0;
   for (int l = 0; l <= deg; ++l) {
     for (int m = -l; m <= l; ++m, ++j) {
       int am = m < 0 ? -m : m;
       double sign = (am % 2) ? -1.0 : 1.0;
-      double dz = poly_z(l, am, z);
-      double dz1 = poly_z(l, am + 1, z);
+      T dz = poly_z(l, am, z);
+      T dz1 = poly_z(l, am + 1, z);
       if (m == 0) {
-        double c = sh_norm(l, 0);
-        dY[j * 3 + 0] = 0.0;
-        dY[j * 3 + 1] = 0.0;
+        T c = T(sh_norm(l, 0));
+        dY[j * 3 + 0] = T(0.0);
+        dY[j * 3 + 1] = T(0.0);
         dY[j * 3 + 2] = c * dz1;
       } else {
-        double c = sqrt2 * sh_norm(l, am) * sign;
-        double re, im, re1, im1;
+        T c = T(sqrt2 * sh_norm(l, am) * sign);
+        T re, im, re1, im1;
         cpow(x, y, am, re, im);
         cpow(x, y, am - 1, re1, im1);
-        double ang, dang_dx, dang_dy;
+        T ang, dang_dx, dang_dy;
         if (m > 0) { /* Re((x+iy)^m) */
           ang = re;
-          dang_dx = am * re1;
-          dang_dy = -am * im1;
+          dang_dx = T(am) * re1;
+          dang_dy = T(-am) * im1;
         } else { /* Im((x+iy)^m) */
           ang = im;
-          dang_dx = am * im1;
-          dang_dy = am * re1;
+          dang_dx = T(am) * im1;
+          dang_dy = T(am) * re1;
         }
         dY[j * 3 + 0] = c * dz * dang_dx;
         dY[j * 3 + 1] = c * dz * dang_dy;
@@ -679,86 +706,90 @@ void composite_bwd_impl(int W, int H, int64_t N, const uint32_t* ranges,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Step 13b: projection backward (fp64), chain rule from (u, v), the conic   */
-/* and the colour to mean, scale, quaternion and SH coefficients.            */
+/* Step 13b: projection backward, chain rule from (u, v), the conic and the  */
+/* colour to mean, scale, quaternion and SH coefficients.  S = S is the */
+/* reference; S = ErrScale carries, next to each value, a first-order bound  */
+/* on the rounding error an fp32 evaluation of the same expressions can      */
+/* accumulate (in units of the unit roundoff), used only to classify fp32    */
+/* cancellation in the parity tests.                                         */
 /* ------------------------------------------------------------------------ */
-void project_bwd_one(int deg, const double* mean, const double* scale, const double* quat,
-                     const double* sh, const Cam<double>& cam, const orc_settings& st,
-                     const double* gm2, const double* gcon, const double* gcol,
-                     double* g_mean, double* g_scale, double* g_quat, double* g_sh) {
+template <class S>
+void project_bwd_one(int deg, const S* mean, const S* scale, const S* quat, const S* sh,
+                     const Cam<S>& cam, const orc_settings& st, const S* gm2, const S* gcon,
+                     const S* gcol, S* g_mean, S* g_scale, S* g_quat, S* g_sh) {
   const int K = (deg + 1) * (deg + 1);
-  const double* W = cam.R;
-  double t[3];
+  const S* W = cam.R;
+  S t[3];
   for (int r = 0; r < 3; ++r)
     t[r] = W[r * 3 + 0] * mean[0] + W[r * 3 + 1] * mean[1] + W[r * 3 + 2] * mean[2] + cam.t[r];
-  const double tx = t[0], ty = t[1], tz = t[2];
-  double n2 = quat[0] * quat[0] + quat[1] * quat[1] + quat[2] * quat[2] + quat[3] * quat[3];
-  double nr = std::sqrt(n2);
-  double qn[4] = {quat[0] / nr, quat[1] / nr, quat[2] / nr, quat[3] / nr};
-  double Rq[9], Sig[9];
+  const S tx = t[0], ty = t[1], tz = t[2];
+  S n2 = quat[0] * quat[0] + quat[1] * quat[1] + quat[2] * quat[2] + quat[3] * quat[3];
+  S nr = s_sqrt(n2);
+  S qn[4] = {quat[0] / nr, quat[1] / nr, quat[2] / nr, quat[3] / nr};
+  S Rq[9], Sig[9];
   rotation_from_unit_quat(qn[0], qn[1], qn[2], qn[3], Rq);
   cov3d_from(Rq, scale, Sig);
 
-  const double fx = cam.fx, fy = cam.fy;
-  const double limx = (double)st.fov_clamp * (0.5 * cam.W / fx);
-  const double limy = (double)st.fov_clamp * (0.5 * cam.H / fy);
-  const double txz = tx / tz, tyz = ty / tz;
+  const S fx = cam.fx, fy = cam.fy;
+  const S limx = S((double)st.fov_clamp) * (S(0.5 * cam.W) / fx);
+  const S limy = S((double)st.fov_clamp) * (S(0.5 * cam.H) / fy);
+  const S txz = tx / tz, tyz = ty / tz;
   const bool clx = txz > limx || txz < -limx;
   const bool cly = tyz > limy || tyz < -limy;
-  const double xc = clx ? (txz > 0 ? limx : -limx) * tz : tx;
-  const double yc = cly ? (tyz > 0 ? limy : -limy) * tz : ty;
-  const double J00 = fx / tz, J02 = -fx * xc / (tz * tz);
-  const double J11 = fy / tz, J12 = -fy * yc / (tz * tz);
-  double Tm[6];
+  const S xc = clx ? (txz > S(0) ? limx : -limx) * tz : tx;
+  const S yc = cly ? (tyz > S(0) ? limy : -limy) * tz : ty;
+  const S J00 = fx / tz, J02 = -fx * xc / (tz * tz);
+  const S J11 = fy / tz, J12 = -fy * yc / (tz * tz);
+  S Tm[6];
   for (int j = 0; j < 3; ++j) {
     Tm[j] = J00 * W[j] + J02 * W[6 + j];
     Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
   }
-  double ST0[3], ST1[3]; /* Sigma T0^T, Sigma T1^T */
+  S ST0[3], ST1[3]; /* Sigma T0^T, Sigma T1^T */
   for (int i = 0; i < 3; ++i) {
     ST0[i] = Sig[i * 3] * Tm[0] + Sig[i * 3 + 1] * Tm[1] + Sig[i * 3 + 2] * Tm[2];
     ST1[i] = Sig[i * 3] * Tm[3] + Sig[i * 3 + 1] * Tm[4] + Sig[i * 3 + 2] * Tm[5];
   }
-  double a = Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2] + st.eps2d;
-  double b = Tm[3] * ST0[0] + Tm[4] * ST0[1] + Tm[5] * ST0[2];
-  double c = Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2] + st.eps2d;
-  double det = a * c - b * b, det2 = det * det;
+  S a = Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2] + S((double)st.eps2d);
+  S b = Tm[3] * ST0[0] + Tm[4] * ST0[1] + Tm[5] * ST0[2];
+  S c = Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2] + S((double)st.eps2d);
+  S det = a * c - b * b, det2 = det * det;
 
   /* conic (A,B,C) = (c, -b, a)/det -> (a, b, c) */
-  const double gA = gcon[0], gB = gcon[1], gC = gcon[2];
-  double ga = gA * (-c * c / det2) + gB * (b * c / det2) + gC * (1.0 / det - a * c / det2);
-  double gb = gA * (2.0 * b * c / det2) + gB * (-1.0 / det - 2.0 * b * b / det2) +
+  const S gA = gcon[0], gB = gcon[1], gC = gcon[2];
+  S ga = gA * (-c * c / det2) + gB * (b * c / det2) + gC * (1.0 / det - a * c / det2);
+  S gb = gA * (2.0 * b * c / det2) + gB * (-1.0 / det - 2.0 * b * b / det2) +
               gC * (2.0 * a * b / det2);
-  double gc = gA * (1.0 / det - a * c / det2) + gB * (a * b / det2) + gC * (-a * a / det2);
+  S gc = gA * (1.0 / det - a * c / det2) + gB * (a * b / det2) + gC * (-a * a / det2);
 
   /* Sigma2D entries: cov00 = T0 S T0^T, cov01 = T0 S T1^T, cov11 = T1 S T1^T */
-  double gSig[9];
+  S gSig[9];
   for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 3; ++j)
       gSig[i * 3 + j] = ga * Tm[i] * Tm[j] + gb * Tm[i] * Tm[3 + j] + gc * Tm[3 + i] * Tm[3 + j];
-  double gT0[3], gT1[3];
+  S gT0[3], gT1[3];
   for (int i = 0; i < 3; ++i) {
     gT0[i] = 2.0 * ga * ST0[i] + gb * ST1[i];
     gT1[i] = gb * ST0[i] + 2.0 * gc * ST1[i];
   }
-  double gJ00 = 0, gJ02 = 0, gJ11 = 0, gJ12 = 0;
+  S gJ00 = S(0), gJ02 = S(0), gJ11 = S(0), gJ12 = S(0);
   for (int j = 0; j < 3; ++j) {
     gJ00 += gT0[j] * W[j];
     gJ02 += gT0[j] * W[6 + j];
     gJ11 += gT1[j] * W[3 + j];
     gJ12 += gT1[j] * W[6 + j];
   }
-  double gt[3] = {0, 0, 0};
+  S gt[3] = {S(0), S(0), S(0)};
   gt[2] += gJ00 * (-fx / (tz * tz)) + gJ11 * (-fy / (tz * tz));
   if (clx) {
-    double cx_ = txz > 0 ? limx : -limx;
+    S cx_ = txz > S(0) ? limx : -limx;
     gt[2] += gJ02 * (fx * cx_ / (tz * tz));
   } else {
     gt[0] += gJ02 * (-fx / (tz * tz));
     gt[2] += gJ02 * (2.0 * fx * tx / (tz * tz * tz));
   }
   if (cly) {
-    double cy_ = tyz > 0 ? limy : -limy;
+    S cy_ = tyz > S(0) ? limy : -limy;
     gt[2] += gJ12 * (fy * cy_ / (tz * tz));
   } else {
     gt[1] += gJ12 * (-fy / (tz * tz));
@@ -773,60 +804,60 @@ void project_bwd_one(int deg, const double* mean, const double* scale, const dou
     g_mean[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
 
   /* Sigma = M M^T, M = R diag(s) */
-  double M[9];
+  S M[9];
   for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 3; ++j) M[i * 3 + j] = Rq[i * 3 + j] * scale[j];
-  double gM[9];
+  S gM[9];
   for (int i = 0; i < 3; ++i)
     for (int k = 0; k < 3; ++k) {
-      double s = 0.0;
+      S s = S(0.0);
       for (int j = 0; j < 3; ++j) s += (gSig[i * 3 + j] + gSig[j * 3 + i]) * M[j * 3 + k];
       gM[i * 3 + k] = s;
     }
-  double gR[9];
+  S gR[9];
   for (int j = 0; j < 3; ++j) {
-    double s = 0.0;
+    S s = S(0.0);
     for (int i = 0; i < 3; ++i) {
       s += gM[i * 3 + j] * Rq[i * 3 + j];
       gR[i * 3 + j] = gM[i * 3 + j] * scale[j];
     }
     g_scale[j] = s;
   }
-  const double w = qn[0], x = qn[1], y = qn[2], z = qn[3];
-  double gq[4] = {0, 0, 0, 0};
+  const S w = qn[0], x = qn[1], y = qn[2], z = qn[3];
+  S gq[4] = {S(0), S(0), S(0), S(0)};
   /* partial derivatives of each rotation entry wrt (w, x, y, z) */
-  const double dR[9][4] = {
-      {0, 0, -4 * y, -4 * z},          {-2 * z, 2 * y, 2 * x, -2 * w},
+  const S dR[9][4] = {
+      {S(0), S(0), -4 * y, -4 * z},          {-2 * z, 2 * y, 2 * x, -2 * w},
       {2 * y, 2 * z, 2 * w, 2 * x},    {2 * z, 2 * y, 2 * x, 2 * w},
-      {0, -4 * x, 0, -4 * z},          {-2 * x, -2 * w, 2 * z, 2 * y},
+      {S(0), -4 * x, S(0), -4 * z},          {-2 * x, -2 * w, 2 * z, 2 * y},
       {-2 * y, 2 * z, -2 * w, 2 * x},  {2 * x, 2 * w, 2 * z, 2 * y},
-      {0, -4 * x, -4 * y, 0}};
+      {S(0), -4 * x, -4 * y, S(0)}};
   for (int e = 0; e < 9; ++e)
     for (int k = 0; k < 4; ++k) gq[k] += gR[e] * dR[e][k];
-  double dot = qn[0] * gq[0] + qn[1] * gq[1] + qn[2] * gq[2] + qn[3] * gq[3];
+  S dot = qn[0] * gq[0] + qn[1] * gq[1] + qn[2] * gq[2] + qn[3] * gq[3];
   for (int k = 0; k < 4; ++k) g_quat[k] = (gq[k] - qn[k] * dot) / nr;
 
   /* colour -> SH coefficients and view direction */
-  double campos[3];
+  S campos[3];
   camera_center(cam, campos);
-  double dir[3] = {mean[0] - campos[0], mean[1] - campos[1], mean[2] - campos[2]};
-  double L = std::sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-  double d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
-  double Y[16], dY[48];
+  S dir[3] = {mean[0] - campos[0], mean[1] - campos[1], mean[2] - campos[2]};
+  S L = s_sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+  S d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
+  S Y[16], dY[48];
   sh_basis(deg, d[0], d[1], d[2], Y);
   sh_basis_grad(deg, d[0], d[1], d[2], dY);
-  double gd[3] = {0, 0, 0};
+  S gd[3] = {S(0), S(0), S(0)};
   for (int ch = 0; ch < 3; ++ch) {
-    double raw = st.sh_offset;
+    S raw = S((double)st.sh_offset);
     for (int j = 0; j < K; ++j) raw += Y[j] * sh[j * 3 + ch];
-    bool pass = !(raw < 0.0);
+    bool pass = !(raw < S(0.0));
     for (int j = 0; j < K; ++j) {
-      g_sh[j * 3 + ch] = pass ? Y[j] * gcol[ch] : 0.0;
+      g_sh[j * 3 + ch] = pass ? Y[j] * gcol[ch] : S(0.0);
       if (pass)
         for (int e = 0; e < 3; ++e) gd[e] += gcol[ch] * sh[j * 3 + ch] * dY[j * 3 + e];
     }
   }
-  double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+  S dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
   for (int e = 0; e < 3; ++e) g_mean[e] += (gd[e] - d[e] * dd) / L;
 }
 
@@ -1061,6 +1092,46 @@ int orc_project_bwd(int64_t N, int deg, const double* means, const double* scale
     project_bwd_one(deg, &means[3 * i], &scales[3 * i], &quats[4 * i], &sh[(size_t)K * 3 * i],
                     cam, *st, &g_means2d[2 * i], &g_conics[3 * i], &g_colors[3 * i], gm, gs, gq,
                     gsh);
+  }
+  return 0;
+}
+
+int orc_project_bwd_errscale(int64_t N, int deg, const double* means, const double* scales,
+                             const double* quats, const double* sh, const orc_camera* camd,
+                             const orc_settings* st, const int32_t* radii,
+                             const double* g_means2d, const double* g_conics,
+                             const double* g_colors, const double* s_means2d,
+                             const double* s_conics, const double* s_colors, double* e_means,
+                             double* e_scales, double* e_quats, double* e_sh) {
+  const int K = (deg + 1) * (deg + 1);
+  Cam<ErrScale> cam = cam_as<ErrScale>(*camd);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) {
+    double* em = &e_means[3 * i];
+    double* es = &e_scales[3 * i];
+    double* eq = &e_quats[4 * i];
+    double* esh = &e_sh[(size_t)K * 3 * i];
+    if (radii[i] <= 0) {
+      std::fill(em, em + 3, 0.0);
+      std::fill(es, es + 3, 0.0);
+      std::fill(eq, eq + 4, 0.0);
+      std::fill(esh, esh + 3 * K, 0.0);
+      continue;
+    }
+    ErrScale m[3], sc[3], q[4], shv[48], gm2[2], gc[3], gcol[3];
+    ErrScale om[3], os[3], oq[4], osh[48];
+    for (int k = 0; k < 3; ++k) { m[k] = ErrScale(means[3 * i + k]); sc[k] = ErrScale(scales[3 * i + k]); }
+    for (int k = 0; k < 4; ++k) q[k] = ErrScale(quats[4 * i + k]);
+    for (int k = 0; k < 3 * K; ++k) shv[k] = ErrScale(sh[(size_t)K * 3 * i + k]);
+    for (int k = 0; k < 2; ++k) gm2[k] = ErrScale(g_means2d[2 * i + k], s_means2d[2 * i + k]);
+    for (int k = 0; k < 3; ++k) {
+      gc[k] = ErrScale(g_conics[3 * i + k], s_conics[3 * i + k]);
+      gcol[k] = ErrScale(g_colors[3 * i + k], s_colors[3 * i + k]);
+    }
+    project_bwd_one(deg, m, sc, q, shv, cam, *st, gm2, gc, gcol, om, os, oq, osh);
+    for (int k = 0; k < 3; ++k) { em[k] = om[k].m; es[k] = os[k].m; }
+    for (int k = 0; k < 4; ++k) eq[k] = oq[k].m;
+    for (int k = 0; k < 3 * K; ++k) esh[k] = osh[k].m;
   }
   return 0;
 }

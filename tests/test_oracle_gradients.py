@@ -179,3 +179,25 @@ def test_central_finite_differences(case):
     print("FD worst err/tol %.3g, checked %d, flipped %d" % (worst, checked, flipped))
     assert checked > 300
     assert flipped <= 0.05 * (checked + flipped)
+
+
+def test_errscale_bounds_the_values_and_scales_linearly():
+    """The rounding-error scale of the projection backward dominates the
+    gradient it accompanies and is linear in the inputs' scales."""
+    scene, cam = coverage_scene()
+    scene = _scene64(scene)
+    f = oracle.render_f64(scene, cam)
+    rng = np.random.default_rng(3)
+    N = scene.n
+    g2 = rng.normal(size=(N, 2)), rng.normal(size=(N, 3)), rng.normal(size=(N, 3))
+    out = oracle.project_bwd(scene.means, scene.scales, scene.quats, scene.sh, 3, cam,
+                             f["proj"]["radii"], *g2)
+    e1 = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh, 3, cam,
+                                     f["proj"]["radii"], *g2)
+    for k in ("means", "scales", "quats", "sh"):
+        assert np.all(e1[k] >= np.abs(out[k]) * (1 - 1e-12)), k
+    big = [10 * np.abs(x) for x in g2]
+    e2 = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh, 3, cam,
+                                     f["proj"]["radii"], *g2, *big)
+    for k in ("means", "scales", "quats", "sh"):
+        assert np.all(e2[k] >= e1[k] * (1 - 1e-12)), k

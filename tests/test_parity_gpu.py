@@ -15,8 +15,9 @@ import pytest
 import oracle
 from differentiable_rasterization_amd import scenes
 
-from parity_util import (FLIP_REL, G_ABS, G_REL, PIX_TOL, assert_bits_equal, compare_grad,
-                         compare_pixels, flip_tiles, gaussians_in_tiles, gpu_frame)
+from parity_util import (COND_K, EPS32, ERR_C, FLIP_REL, G_ABS, G_REL, PIX_TOL,
+                         assert_bits_equal, compare_grad, compare_pixels, flip_tiles,
+                         gaussians_in_tiles, gpu_frame)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +46,7 @@ CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "box_100k_1080p
          "cluster_1m_1080p"]
 
 
-@functools.lru_cache(maxsize=1)
+@functools.lru_cache(maxsize=None)
 def run_case(name):
     t0 = time.time()
     print("\n[parity] case %s" % name, flush=True)
@@ -141,34 +142,38 @@ def test_rasterize_bwd(name):
 
 @pytest.mark.parametrize("name", CASES)
 def test_project_bwd(name):
+    """Stage-isolated: the oracle gets the GPU's 2D gradients.  Elements outside
+    max(1e-3 |g|, 1e-5) must lie within ERR_C * u * e, e the first-order fp32
+    rounding scale of the same chain rule (cancellation, counted)."""
     r = run_case(name)
-    g, o = r["gpu"], r["iso_pbwd"]
+    g, o, scene, cam = r["gpu"], r["iso_pbwd"], r["scene"], r["cam"]
     vis = g["radii"] > 0
     for k in ("means", "scales", "quats", "sh"):
-        gg = g["g_" + k]
-        assert np.all(gg[~vis] == 0), k
-    # fp32 chain rule against fp64: each output is a short sum of products of
-    # the 2D gradients; scale the absolute floor by the input magnitude
-    mag = (np.abs(g["g_means2d"]).sum(1) + np.abs(g["g_conics"]).sum(1) +
-           np.abs(g["g_colors"]).sum(1))
+        assert np.all(g["g_" + k][~vis] == 0), k
+    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
+                                    scene.sh_degree, cam, g["radii"], g["g_means2d"],
+                                    g["g_conics"], g["g_colors"])
     for k in ("means", "scales", "quats", "sh"):
         gg = np.asarray(g["g_" + k], np.float64).reshape(len(vis), -1)[vis]
         oo = o[k].reshape(len(vis), -1)[vis]
+        ee = e[k].reshape(len(vis), -1)[vis]
         err = np.abs(gg - oo)
-        tol = np.maximum(G_REL * np.abs(oo), G_ABS)
-        bad = err > tol
-        # conditioning: terms of magnitude |2D grads| x |Jacobian| cancelling
-        scale = np.abs(oo).max(axis=1, keepdims=True) + mag[vis, None] * 1e-3
-        cond = bad & (err <= 1e-4 * scale)
-        print("[parity] %s project_bwd %s: bad %d, cancellation %d of %d" %
-              (name, k, bad.sum(), cond.sum(), bad.size))
+        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
+        cond = bad & (err <= ERR_C * EPS32 * ee)
+        print("[parity] %s project_bwd %s: outside tol %d, within fp32 cancellation bound %d, "
+              "of %d" % (name, k, bad.sum(), cond.sum(), bad.size))
         assert (bad & ~cond).sum() == 0, (k, np.argwhere(bad & ~cond)[:5])
-        assert cond.sum() <= 1e-3 * bad.size + 2
+        assert cond.sum() <= 1e-4 * bad.size + 4
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_end_to_end_gradients(name):
-    """Whole path: GPU gradients against the oracle's own forward + backward."""
+    """Whole path: GPU gradients against the oracle's own forward + backward.
+    2D gradients: as in the stage test.  3D gradients: outside max(1e-3 |g|,
+    1e-5) they must lie within the first-order bound that propagates the 2D
+    allowance (max(1e-3|g|, 1e-5, COND_K u sum|terms|)) through the projection
+    backward plus its own fp32 rounding.  Gaussians listed in a tile with a
+    threshold-flip pixel are exempt (counted)."""
     r = run_case(name)
     g, scene, cam, bg = r["gpu"], r["scene"], r["cam"], r["bg"]
     orc = r["orc"]
@@ -180,27 +185,32 @@ def test_end_to_end_gradients(name):
                           (np.sign(g["dL_dimage"]) != np.sign(dl)).any(axis=2))
     ex = gaussians_in_tiles(g["ranges"], g["ids"], flips)
     a = bw["g2"]["abs_sum"]
-    rep = compare_grad(g["g_opacities"], bw["g2"]["opacities"], a[:, 5], ex, "opacities")
-    print("[parity] %s e2e %s" % (name, rep))
-    assert rep["fail"] == 0, rep
-    vis = g["radii"] > 0
+    reps = [compare_grad(g["g_means2d"], bw["g2"]["means2d"], a[:, 0:2], ex, "means2d"),
+            compare_grad(g["g_conics"], bw["g2"]["conics"], a[:, 2:5], ex, "conics"),
+            compare_grad(g["g_opacities"], bw["g2"]["opacities"], a[:, 5], ex, "opacities"),
+            compare_grad(g["g_colors"], bw["g2"]["colors"], a[:, 6:9], ex, "colors")]
+    for rep in reps:
+        print("[parity] %s e2e %s" % (name, rep))
+        assert rep["fail"] == 0, rep
+    allow = lambda go, ab: np.maximum(np.maximum(G_REL * np.abs(go), G_ABS), COND_K * EPS32 * ab)
+    s_m2 = np.abs(bw["g2"]["means2d"]) + allow(bw["g2"]["means2d"], a[:, 0:2]) / (ERR_C * EPS32)
+    s_con = np.abs(bw["g2"]["conics"]) + allow(bw["g2"]["conics"], a[:, 2:5]) / (ERR_C * EPS32)
+    s_col = np.abs(bw["g2"]["colors"]) + allow(bw["g2"]["colors"], a[:, 6:9]) / (ERR_C * EPS32)
+    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
+                                    scene.sh_degree, cam, orc["proj"]["radii"],
+                                    bw["g2"]["means2d"], bw["g2"]["conics"], bw["g2"]["colors"],
+                                    s_m2, s_con, s_col)
+    rows = np.zeros(scene.n, bool)
+    if ex:
+        rows[np.fromiter(ex, np.int64)] = True
     for k in ("means", "scales", "quats", "sh"):
         gg = np.asarray(g["g_" + k], np.float64).reshape(scene.n, -1)
         oo = bw["g3"][k].reshape(scene.n, -1)
+        ee = e[k].reshape(scene.n, -1)
         err = np.abs(gg - oo)
-        tol = np.maximum(G_REL * np.abs(oo), G_ABS)
-        bad = err > tol
-        rows = np.zeros(scene.n, bool)
-        if ex:
-            rows[np.fromiter(ex, np.int64)] = True
-        # a 3D gradient inherits the cancellation of its 2D inputs
-        amag = a.sum(axis=1)
-        cond = bad & (err <= COND3 * amag[:, None] * 1e-3 + 1e-4 * np.abs(oo).max(axis=1, keepdims=True))
+        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
+        cond = bad & ~rows[:, None] & (err <= ERR_C * EPS32 * ee)
         unexplained = bad & ~rows[:, None] & ~cond
-        print("[parity] %s e2e %s: bad %d (flip rows %d, cancellation %d) of %d" %
-              (name, k, bad.sum(), (bad & rows[:, None]).sum(), (bad & cond & ~rows[:, None]).sum(),
-               bad[vis].size))
+        print("[parity] %s e2e %s: outside tol %d (flip rows %d, within propagated bound %d) "
+              "of %d" % (name, k, bad.sum(), (bad & rows[:, None]).sum(), cond.sum(), bad.size))
         assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])
-
-
-COND3 = 2e-3
