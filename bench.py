@@ -27,9 +27,17 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd frames/sec at 1M Gaussians 1920×1080 SH3; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
-# Plain fp32 VALU issue: 256 CUs x 64 lanes x 2.4 GHz (one non-packed VALU
-# instruction per lane per clock).
+# Plain fp32 VALU issue: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane
+# slots/s (one non-packed VALU instruction per lane per slot; transcendental
+# exp2/rcp take four slots).
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# VALU slots per pixel-splat pair of the compositing inner loops, counted in
+# the gfx950 assembly of raster.hip: forward 57 VALU per two unrolled pairs
+# plus 3 extra slots for v_exp_f32; backward 60 VALU per pair plus 6 extra for
+# v_exp_f32 and v_rcp_f32, and 28 VALU per executed 9-field wave reduction.
+FWD_SLOTS_PER_PAIR = 31.5
+BWD_SLOTS_PER_PAIR = 66.0
+BWD_SLOTS_PER_REDUCTION = 28.0
 
 
 def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
@@ -70,6 +78,9 @@ def main():
     ap.add_argument("--config", default="cluster_1m_1080p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=4)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a reference "
+                         "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -80,6 +91,12 @@ def main():
     from differentiable_rasterization_amd import raster, scenes
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     scene, cams, loss_kind = scenes.make_config(args.config)
     loss_kind = loss_kind or "l1"
     W, H = cams[0].width, cams[0].height
@@ -113,7 +130,7 @@ def main():
         fr.rasterize(g)
         if ev is not None:
             ev[3].record()
-        fr.loss_grad(targets[i % P], kind)
+        raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i % P], fr.dL_dimage, None)
         if ev is not None:
             ev[4].record()
         raster.gs_rasterize_bwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
@@ -129,11 +146,21 @@ def main():
             ev[6].record()
         return fr.M
 
-    # workload statistics per pose (one untimed pass)
+    # workload statistics per pose (one untimed pass with the counting variants)
+    cnt = torch.zeros(8, dtype=torch.int64, device="cuda")
     stats = []
     for i in range(P):
         step(i)
+        cnt.zero_()
+        raster.gs_rasterize_fwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
+                                g.opacities, fr.colors, fr.depths, fr.background, fr.settings,
+                                fr.image, fr.final_T, fr.last_idx, None, None, cnt[0:4])
+        raster.gs_rasterize_bwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
+                                g.opacities, fr.colors, fr.background, fr.settings, fr.final_T,
+                                fr.last_idx, fr.dL_dimage, fr.g_means2d, fr.g_conics,
+                                fr.g_opacities, fr.g_colors, 0, cnt[4:8])
         torch.cuda.synchronize()
+        c = cnt.cpu().numpy()
         V = int((fr.radii[:N] > 0).sum().item())
         rng = fr.ranges.cpu().numpy().view(np.uint32).astype(np.int64)
         lens = rng[:, 1] - rng[:, 0]
@@ -144,7 +171,9 @@ def main():
         np.maximum.at(maxlast, tile_of.ravel(), last.ravel())
         inside = np.bincount(tile_of.ravel(), minlength=T)
         stats.append(dict(V=V, M=fr.M, M_bwd=int(maxlast.sum()),
-                          pairs=int((inside * lens).sum())))
+                          pairs_tile=int((inside * lens).sum()), fwd_eval=int(c[0]),
+                          blended=int(c[1]), plain_pairs=int(c[2]), bwd_eval=int(c[4]),
+                          bwd_hit=int(c[5]), bwd_reductions=int(c[7])))
 
     for i in range(args.warmup):
         step(i)
@@ -176,17 +205,32 @@ def main():
     fps = args.steps / dt
     fwd_ms = stage_ms["project_fwd"] + stage_ms["bin_and_sort"] + stage_ms["rasterize_fwd"]
     dominant = max(names, key=lambda n: stage_ms[n])
-    # the compositing kernels are bound by VALU issue: algorithmic work =
-    # pixel-splat pairs x VALU instructions per pair in the kernel's loop
-    valu_per_pair = {"rasterize_fwd": 17, "rasterize_bwd": 62}
-    if dominant in valu_per_pair:
-        ops = avg["pairs"] * valu_per_pair[dominant]
-        ach = ops / (stage_ms[dominant] * 1e-3) / 1e12
+    # The compositing kernels are bound by VALU issue.  Algorithmic work = the
+    # pixel-splat pairs that blend (the pairs whose result the method uses)
+    # x VALU slots per pair of the kernel's loop; "issued" adds the pairs the
+    # kernel evaluated but that did not blend, and the wave reductions.
+    alu = {
+        "rasterize_fwd": (avg["blended"] * FWD_SLOTS_PER_PAIR,
+                          avg["fwd_eval"] * FWD_SLOTS_PER_PAIR),
+        "rasterize_bwd": (avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
+                          avg["bwd_eval"] * BWD_SLOTS_PER_PAIR +
+                          avg["bwd_reductions"] * 64 * BWD_SLOTS_PER_REDUCTION),
+    }
+    work = {"pairs_blended": int(avg["blended"]), "pairs_evaluated_fwd": int(avg["fwd_eval"]),
+            "pairs_evaluated_bwd": int(avg["bwd_eval"]),
+            "pairs_plain_method": int(avg["plain_pairs"]),
+            "pairs_all_tile_pixels": int(avg["pairs_tile"]),
+            "wave_reductions_bwd": int(avg["bwd_reductions"])}
+    if dominant in alu:
+        useful, issued = alu[dominant]
+        t = stage_ms[dominant] * 1e-3
+        ach = useful / t / 1e12
         roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
                 "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
                 "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None,
-                "work_per_launch": {"pairs": int(avg["pairs"]),
-                                    "valu_per_pair": valu_per_pair[dominant]}}
+                "issued_frac": round(issued / t / 1e12 / VALU_PEAK_TOPS, 4),
+                "slots_per_pair": BWD_SLOTS_PER_PAIR if dominant == "rasterize_bwd"
+                else FWD_SLOTS_PER_PAIR, "work_per_launch": work}
     else:
         ach = byts[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),

@@ -32,14 +32,14 @@ hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges, co
                                 const float* opac, const float* colors, const float* depths,
                                 const float* bg, const gs::Settings& st, float* image,
                                 float* final_T, uint32_t* last_idx, float* out_depth,
-                                float* out_alpha, hipStream_t s);
+                                float* out_alpha, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
                                 const uint32_t* ids, int64_t ld, const float* means2d,
                                 const float* conics, const float* opac, const float* colors,
                                 const float* bg, const gs::Settings& st, const float* final_T,
                                 const uint32_t* last_idx, const float* dL_dimage, float* g_m2,
                                 float* g_con, float* g_op, float* g_col, int accumulate,
-                                hipStream_t s);
+                                uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
 }
@@ -209,18 +209,20 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const float* colors, const float* depths, const float* background,
                            const gs_settings* settings, float* image, float* final_T,
                            uint32_t* last_idx, float* out_depth, float* out_alpha,
-                           void* stream) {
+                           uint64_t* counters, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_image(width, height));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(background != nullptr, "background is NULL");
   GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
-  GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
-  if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  if (N > 0) {
+    GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
+    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  }
   return hip_status(gs_launch_raster_fwd(width, height, tile_ranges, ids, ld, means2d, conics,
                                          opacities, colors, depths, background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
-                                         out_depth, out_alpha, (hipStream_t)stream),
+                                         out_depth, out_alpha, counters, (hipStream_t)stream),
                     "gs_rasterize_fwd");
 }
 
@@ -231,20 +233,24 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const gs_settings* settings, const float* final_T,
                            const uint32_t* last_idx, const float* dL_dimage,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
-                           float* dL_dcolors, int32_t accumulate, void* stream) {
+                           float* dL_dcolors, int32_t accumulate, uint64_t* counters,
+                           void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_image(width, height));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(background != nullptr, "background is NULL");
   GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
-  GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
-  GS_REQUIRE(dL_dmeans2d && dL_dconics && dL_dopacities && dL_dcolors, "NULL gradient pointer");
+  if (N > 0) {
+    GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
+    GS_REQUIRE(dL_dmeans2d && dL_dconics && dL_dopacities && dL_dcolors,
+               "NULL gradient pointer");
+  }
   GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
   return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, ld, means2d, conics,
                                          opacities, colors, background,
                                          gs::make_settings(*settings), final_T, last_idx,
                                          dL_dimage, dL_dmeans2d, dL_dconics, dL_dopacities,
-                                         dL_dcolors, accumulate, (hipStream_t)stream),
+                                         dL_dcolors, accumulate, counters, (hipStream_t)stream),
                     "gs_rasterize_bwd");
 }
 

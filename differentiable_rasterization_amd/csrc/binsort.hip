@@ -29,6 +29,18 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
     p[i] = v;
 }
 
+// Zero up to four u32 segments in one launch.
+struct Segs {
+  uint32_t* p[4];
+  int64_t n[4];
+};
+__global__ void zero_segs_kernel(Segs sg) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int k = 0; k < 4; ++k)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < sg.n[k]; i += stride)
+      sg.p[k][i] = 0u;
+}
+
 static hipError_t fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -441,9 +453,18 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   const int32_t T = gx * gy;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
-  if ((e = fill_u32(ranges, 2 * (int64_t)T, 0u, s)) != hipSuccess) return e;
-  if (M == 0) return hipSuccess;
+  if (M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   const SortPlan sp = sort_plan(M, T);
+  {
+    Segs sg = {{ranges, w.hist, w.ticket, w.status},
+               {2 * (int64_t)T, (int64_t)kMaxPasses * kRadix, kMaxPasses,
+                (int64_t)sp.passes * sp.parts * kRadix}};
+    int64_t big = sg.n[0] > sg.n[3] ? sg.n[0] : sg.n[3];
+    int64_t blocks = (big + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // land the final pass in (keys, ids): start from the alternate buffer when
   // the pass count is odd
   uint64_t* ka = (sp.passes & 1) ? w.keys_alt : keys;
@@ -456,9 +477,6 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const uint32_t M32 = (uint32_t)M;
-  if ((e = fill_u32(w.hist, (int64_t)kMaxPasses * kRadix, 0u, s)) != hipSuccess) return e;
-  if ((e = fill_u32(w.ticket, kMaxPasses, 0u, s)) != hipSuccess) return e;
-  if ((e = fill_u32(w.status, (int64_t)sp.passes * sp.parts * kRadix, 0u, s)) != hipSuccess) return e;
   unsigned hblocks = (unsigned)((M + 256 * 16 - 1) / (256 * 16));
   if (hblocks > 1024) hblocks = 1024;
   hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, M32, sp.passes,

@@ -74,10 +74,10 @@ def load():
     lib.gs_bin_and_sort.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                     C.c_size_t, P]
     lib.gs_rasterize_fwd.restype = C.c_int
-    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 8 + [P, P] + [P] * 4 + [P]
+    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 8 + [P, P] + [P] * 5 + [P]
     lib.gs_rasterize_bwd.restype = C.c_int
     lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 7 + [P] + [P] * 3 + [P] * 4 + \
-        [i32, P]
+        [i32, P, P]
     lib.gs_project_bwd.restype = C.c_int
     lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 4 + [P] * 4 + \
         [i32, P]
@@ -166,25 +166,26 @@ def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height,
 
 def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
                      depths, background, settings, image, final_T, last_idx, out_depth=None,
-                     out_alpha=None, stream=None):
+                     out_alpha=None, counters=None, stream=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
                                 _p(conics), _p(opacities), _p(colors), _p(depths), bg,
                                 C.byref(settings), _p(image), _p(final_T), _p(last_idx),
-                                _p(out_depth), _p(out_alpha), _stream(stream)))
+                                _p(out_depth), _p(out_alpha), _p(counters), _stream(stream)))
 
 
 def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
                      background, settings, final_T, last_idx, dL_dimage, dL_dmeans2d,
-                     dL_dconics, dL_dopacities, dL_dcolors, accumulate=0, stream=None):
+                     dL_dconics, dL_dopacities, dL_dcolors, accumulate=0, counters=None,
+                     stream=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
                                 _p(conics), _p(opacities), _p(colors), bg, C.byref(settings),
                                 _p(final_T), _p(last_idx), _p(dL_dimage), _p(dL_dmeans2d),
                                 _p(dL_dconics), _p(dL_dopacities), _p(dL_dcolors),
-                                int(accumulate), _stream(stream)))
+                                int(accumulate), _p(counters), _stream(stream)))
 
 
 def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii,

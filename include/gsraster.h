@@ -37,7 +37,9 @@
  *     count back to the host once.
  *   - Errors: invalid arguments are rejected on the host before anything is
  *     launched (GS_ERR_INVALID_ARGUMENT); a failed launch returns GS_ERR_HIP.
- *     gs_last_error() gives a thread-local message.  Non-finite or degenerate
+ *     gs_last_error() gives a thread-local message.  Per-Gaussian pointers
+ *     may be NULL when N = 0; tile_ranges and ids must come from
+ *     gs_bin_and_sort for the same Gaussians and image.  Non-finite or degenerate
  *     Gaussians are not errors: they are culled (radius 0, no tiles, zero
  *     gradients).  N = 0 and zero instances are valid (background image).
  */
@@ -142,14 +144,18 @@ GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, co
  * Outputs: image [H][W][3] = C + T bg; final_T [H][W]; last_idx [H][W] =
  * number of the tile's list entries up to and including the last blended one
  * (0 if none); out_depth [H][W] = sum alpha T depth and out_alpha [H][W] =
- * 1 - T when non-NULL.  background: HOST float[3]. */
+ * 1 - T when non-NULL.  background: HOST float[3].
+ * counters: NULL, or device uint64[4] that the call adds work counts to:
+ * [0] pixel-splat pairs evaluated by the kernel, [1] pairs blended, [2] pairs
+ * the plain method evaluates (per pixel, its tile's entries up to the one
+ * that stops it), [3] unused.  Counting uses a separate kernel variant. */
 GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
                            const float* means2d, const float* conics, const float* opacities,
                            const float* colors, const float* depths, const float* background,
                            const gs_settings* settings, float* image, float* final_T,
                            uint32_t* last_idx, float* out_depth, float* out_alpha,
-                           void* stream);
+                           uint64_t* counters, void* stream);
 
 /* Stage 5a — compositing backward (gsplat guide §2.2).  Walks each pixel's
  * blended list back to front from last_idx, recovering T by division and
@@ -157,9 +163,12 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
  * loss with respect to means2d [2][ld], conics [3][ld] (A, B, C as scalars of
  * q), opacities [ld] and colors [3][ld], given dL_dimage [H][W][3].  Pairs
  * whose alpha was clamped at alpha_max carry no opacity/conic/mean gradient.
- * accumulate = 0 zero-fills the N entries of each output first;
- * accumulate = 1 adds to their contents.  Additions use fp32 atomics, so the
- * low bits vary between runs. */
+ * The 2D gradients (means2d, conics, colors) belong to this camera and are
+ * always recomputed (zero-filled, then added to); dL_dopacities is a
+ * parameter gradient: accumulate = 0 zero-fills it first, accumulate = 1 adds
+ * to its contents (summing cameras; pair with gs_project_bwd(accumulate = 1)).
+ * Additions use fp32 atomics, so the low bits vary between runs.  counters: NULL, or device uint64[4]: [0] pairs
+ * evaluated, [1] pairs with a gradient, [3] wavefront reductions executed. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
                            const float* means2d, const float* conics, const float* opacities,
@@ -167,14 +176,15 @@ GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t 
                            const gs_settings* settings, const float* final_T,
                            const uint32_t* last_idx, const float* dL_dimage,
                            float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
-                           float* dL_dcolors, int32_t accumulate, void* stream);
+                           float* dL_dcolors, int32_t accumulate, uint64_t* counters,
+                           void* stream);
 
 /* Stage 5b — projection backward: chain rule from (u, v), the conic and the
  * colour to means [3][ld], scales [3][ld], quats [4][ld] (through the
  * normalisation) and sh [K*3][ld].  Visibility comes from radii (the forward's
  * decisions are kept: the fov clamp and the colour clamp are re-evaluated
  * from the same fp32 inputs).  accumulate = 0 overwrites (zeros for culled
- * Gaussians); 1 adds. */
+ * Gaussians); 1 adds (summing cameras). */
 GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
                          const float* scales, const float* quats, const float* sh,
                          const gs_camera* cam, const gs_settings* settings,

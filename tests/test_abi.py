@@ -123,13 +123,17 @@ def test_raster_and_loss_reject_bad_arguments(lib):
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
     r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, dummy, dummy, dummy, dummy, dummy, dummy, bg,
-                             C.byref(st), dummy, dummy, dummy, None, None, None)
+                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT
     r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, dummy, None, bg,
-                             C.byref(st), dummy, dummy, dummy, dummy, None, None)
+                             C.byref(st), dummy, dummy, dummy, dummy, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # depth output without depths
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, dummy, dummy, dummy, dummy, bg,
+                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # splat arrays needed when N > 0
     r = lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, dummy, bg,
-                             C.byref(st), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None)
+                             C.byref(st), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None,
+                             None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # accumulate must be 0/1
     assert lib.gs_image_loss_grad(2, 10, dummy, dummy, dummy, None, None) == \
         raster.GS_ERR_INVALID_ARGUMENT

@@ -1,0 +1,174 @@
+"""Edge cases of the HIP path through the C ABI, checked against the oracle
+or against properties that hold exactly."""
+import numpy as np
+import pytest
+
+import oracle
+from differentiable_rasterization_amd import scenes
+
+from parity_util import PIX_TOL, assert_bits_equal, gpu_frame
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def test_counting_variant_matches_and_counts_consistently():
+    """The counting kernels produce the same outputs; the backward's gradient
+    pairs are exactly the forward's blended pairs; evaluated pairs bound them."""
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    scene, cam = scenes.box_scene(n=20000, seed=12, width=500, height=270, fx=290.0)
+    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 7))
+    fr, g = out["frame"], raster.Gaussians.from_scene(scene)
+    cnt = torch.zeros(8, dtype=torch.int64, device="cuda")
+    img = torch.zeros_like(fr.image)
+    fT = torch.zeros_like(fr.final_T)
+    last = torch.zeros_like(fr.last_idx)
+    raster.gs_rasterize_fwd(g.N, g.ld, cam.width, cam.height, fr.ranges, fr.ids, fr.means2d,
+                            fr.conics, g.opacities, fr.colors, fr.depths, fr.background,
+                            fr.settings, img, fT, last, None, None, cnt[0:4])
+    gm2 = torch.zeros_like(fr.g_means2d)
+    gc = torch.zeros_like(fr.g_conics)
+    go = torch.zeros_like(fr.g_opacities)
+    gcol = torch.zeros_like(fr.g_colors)
+    raster.gs_rasterize_bwd(g.N, g.ld, cam.width, cam.height, fr.ranges, fr.ids, fr.means2d,
+                            fr.conics, g.opacities, fr.colors, fr.background, fr.settings, fT,
+                            last, fr.dL_dimage, gm2, gc, go, gcol, 0, cnt[4:8])
+    torch.cuda.synchronize()
+    assert torch.equal(img, fr.image) and torch.equal(fT, fr.final_T)
+    assert torch.equal(last, fr.last_idx)
+    c = cnt.cpu().numpy()
+    print("counters fwd", c[:4], "bwd", c[4:])
+    assert c[5] == c[1] > 0            # gradient pairs == blended pairs
+    assert c[1] <= c[0] and c[1] <= c[2]
+    assert c[0] <= out["M"] * 256       # culling never adds work
+    assert c[7] > 0
+
+
+def test_zero_gaussians_and_all_culled():
+    torch = _torch()
+    cam = scenes.identity_camera(40, 24, 30.0)
+    bg = (0.25, 0.5, 0.75)
+    empty = scenes.Scene(np.zeros((0, 3), np.float32), np.zeros((0, 3), np.float32),
+                         np.zeros((0, 4), np.float32), np.zeros(0, np.float32),
+                         np.zeros((0, 1, 3), np.float32), 0)
+    behind, _ = scenes.tiny_scene(n=50)
+    behind.means[:, 2] = -behind.means[:, 2]
+    for sc in (empty, behind):
+        out = gpu_frame(sc, cam, background=bg, loss_kind="l2",
+                        target=scenes.target_image(cam, 1))
+        assert out["M"] == 0
+        np.testing.assert_array_equal(out["image"], np.broadcast_to(np.float32(bg), (24, 40, 3)))
+        assert np.all(out["final_T"] == 1.0) and np.all(out["last"] == 0)
+        assert np.all(out["ranges"] == 0)
+        for k in ("g_means", "g_scales", "g_quats", "g_sh", "g_opacities"):
+            assert np.all(out[k] == 0), k
+
+
+def test_capacity_retry_and_leading_dimension():
+    scene, cam = scenes.tiny_scene()
+    ref = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 2))
+    small = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 2), capacity=16)
+    assert small["frame"].capacity >= small["M"] == ref["M"]
+    for k in ("keys", "ids", "ranges", "image", "final_T", "last"):
+        assert_bits_equal(small[k], ref[k], k)
+    wide = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 2),
+                     ld=scene.n + 37)
+    for k in ("means2d", "conics", "depths", "radii", "tiles", "keys", "ids", "ranges", "image",
+              "final_T", "last"):
+        assert_bits_equal(wide[k], ref[k], k)
+    # gradients are summed with fp32 atomics, so their low bits vary run to run
+    for k in ("g_means", "g_scales", "g_quats", "g_sh", "g_opacities"):
+        np.testing.assert_allclose(wide[k], ref[k], rtol=1e-3, atol=1e-5, err_msg=k)
+
+
+def test_accumulate_adds_into_outputs():
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    scene, cam = scenes.tiny_scene()
+    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 3))
+    fr, g = out["frame"], raster.Gaussians.from_scene(scene)
+    fr.backward(g, accumulate=1)  # second pass on top of the first
+    torch.cuda.synchronize()
+    N = scene.n
+    twice = lambda t: t[:, :N].T.cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
+    # atomics make each pass's low bits differ: the documented gradient tolerance
+    np.testing.assert_allclose(twice(fr.g_opacities), 2 * out["g_opacities"], rtol=1e-3, atol=1e-5)
+    np.testing.assert_allclose(twice(fr.g_means), 2 * out["g_means"], rtol=1e-3, atol=1e-5)
+    np.testing.assert_allclose(twice(fr.g_sh).reshape(N, 1, 3), 2 * out["g_sh"], rtol=1e-3,
+                               atol=1e-5)
+
+
+def test_non_finite_and_degenerate_gaussians_are_culled():
+    scene, cam = scenes.tiny_scene(n=200)
+    scene.means[0, 0] = np.nan
+    scene.scales[1, 1] = np.inf
+    scene.quats[2] = 0.0
+    scene.quats[3, 0] = np.nan
+    scene.scales[4] = 0.0           # a point: dilation keeps it visible
+    scene.opacities[5] = 0.0        # invisible but projected
+    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 4))
+    o = oracle.render(scene, cam)
+    assert_bits_equal(out["radii"], o["proj"]["radii"], "radii")
+    assert np.all(out["radii"][:4] == 0)
+    for k in ("image", "final_T", "g_means", "g_scales", "g_quats", "g_sh", "g_opacities"):
+        assert np.all(np.isfinite(out[k])), k
+    assert np.abs(out["image"] - o["raster"]["image"]).max() <= PIX_TOL
+
+
+def test_depth_and_alpha_outputs():
+    scene, cam = scenes.box_scene(n=5000, seed=3, width=200, height=120, fx=110.0)
+    out = gpu_frame(scene, cam, backward=False, depth_alpha=True)
+    o = oracle.render(scene, cam, with_margin=True)
+    r = o["raster"]
+    ok = r["margin"] >= 2e-4
+    np.testing.assert_allclose(out["alpha"], 1 - out["final_T"], rtol=0, atol=0)
+    np.testing.assert_allclose(out["alpha"][ok], r["alpha"][ok], atol=PIX_TOL)
+    # depth accumulates alpha T z with z of a few units
+    np.testing.assert_allclose(out["depth"][ok], r["depth"][ok], atol=1e-4 * 12)
+
+
+def test_forward_and_sort_are_deterministic():
+    scene, cam = scenes.box_scene(n=20000, seed=5, width=320, height=200, fx=180.0)
+    a = gpu_frame(scene, cam, backward=False)
+    b = gpu_frame(scene, cam, backward=False)
+    for k in ("means2d", "conics", "colors", "keys", "ids", "ranges", "image", "final_T", "last"):
+        assert_bits_equal(a[k], b[k], k)
+
+
+def test_exact_depth_ties_keep_index_order():
+    """Clones share keys exactly; the stable sort keeps ascending index, as the
+    oracle's stable sort does."""
+    base, cam = scenes.tiny_scene(n=300, seed=9)
+    idx = np.concatenate([np.arange(300), np.arange(0, 300, 3), np.arange(0, 300, 7)])
+    scene = base.subset(idx)
+    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 5))
+    o = oracle.render(scene, cam)
+    assert_bits_equal(out["keys"], o["bins"]["keys"], "keys")
+    assert_bits_equal(out["ids"], o["bins"]["ids"], "ids")
+    assert np.abs(out["image"] - o["raster"]["image"]).max() <= PIX_TOL
+
+
+def test_loss_value_and_gradient():
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    rng = np.random.default_rng(0)
+    n = 1_000_003
+    img = rng.uniform(size=n).astype(np.float32)
+    tgt = rng.uniform(size=n).astype(np.float32)
+    tgt[:100] = img[:100]  # exact ties: sign(0) = 0
+    ti, tt = torch.from_numpy(img).cuda(), torch.from_numpy(tgt).cuda()
+    g = torch.empty_like(ti)
+    loss = torch.zeros(1, device="cuda")
+    for kind in (0, 1):
+        raster.gs_image_loss_grad(kind, n, ti, tt, g, loss)
+        torch.cuda.synchronize()
+        r = img.astype(np.float64) - tgt
+        ref_g = 2 * r if kind == 0 else np.sign(r)
+        ref_l = np.sum(r * r) if kind == 0 else np.sum(np.abs(r))
+        np.testing.assert_allclose(g.cpu().numpy(), ref_g, rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(float(loss.item()), ref_l, rtol=1e-5)
