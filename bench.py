@@ -44,12 +44,22 @@ def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
     """Algorithmic HBM bytes of each stage (what the method must move with the
     intermediates the ABI materialises)."""
     return {
-        "project_fwd": 20 * N + (64 + 12 * K) * V,
+        # means + radius/tiles for all; scales, quats, opacity, SH in and
+        # means2d, conic, depth, colour planes plus the 64-byte splat record out
+        "project_fwd": 20 * N + (132 + 12 * K) * V,
         "bin_and_sort": 8 * N + 20 * V + (28 + 24 * P) * M + 8 * T,
-        "rasterize_fwd": 40 * M + 20 * Px,
+        # id + the 48 used bytes of the splat record per instance; image out
+        "rasterize_fwd": 52 * M + 20 * Px,
         "loss_grad": 24 * Px,
-        "rasterize_bwd": 36 * N + 36 * V + 40 * M_bwd + 20 * Px,
-        "project_bwd": 4 * N + (72 + 12 * K) * V + (40 + 12 * K) * N,
+        # per instance walked: id, offset, 64-byte record, 48-byte partial
+        # store; per instance past the tile's last blend: id, offset, 32
+        # record bytes, zero store; final T, last index, dL/dimage in; then the
+        # reduction: tiles + offsets, every partial read, the visible records
+        "rasterize_bwd": 120 * M_bwd + 88 * (M - M_bwd) + 20 * Px
+                         + 8 * N + 48 * M + 48 * V,
+        # radii; parameters, SH and the 2D gradient record in for the visible;
+        # mean, scale, quaternion, opacity and SH gradients out for all
+        "project_bwd": 4 * N + (76 + 12 * K) * V + (44 + 12 * K) * N,
     }
 
 
@@ -116,12 +126,9 @@ def main():
 
     def step(i, ev=None):
         c = gcams[i % P]
-        fr.cam = c
         if ev is not None:
             ev[0].record()
-        raster.gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, c,
-                              fr.settings, fr.means2d, fr.conics, fr.depths, fr.radii, fr.colors,
-                              fr.tiles)
+        fr.project(g, c)
         if ev is not None:
             ev[1].record()
         fr.bin_and_sort(g)
@@ -133,15 +140,10 @@ def main():
         raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i % P], fr.dL_dimage, None)
         if ev is not None:
             ev[4].record()
-        raster.gs_rasterize_bwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
-                                g.opacities, fr.colors, fr.background, fr.settings, fr.final_T,
-                                fr.last_idx, fr.dL_dimage, fr.g_means2d, fr.g_conics,
-                                fr.g_opacities, fr.g_colors, 0)
+        fr.rasterize_backward(g)
         if ev is not None:
             ev[5].record()
-        raster.gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, c,
-                              fr.settings, fr.radii, fr.g_means2d, fr.g_conics, fr.g_colors,
-                              fr.g_means, fr.g_scales, fr.g_quats, fr.g_sh, 0)
+        fr.project_backward(g)
         if ev is not None:
             ev[6].record()
         return fr.M
@@ -152,13 +154,8 @@ def main():
     for i in range(P):
         step(i)
         cnt.zero_()
-        raster.gs_rasterize_fwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
-                                g.opacities, fr.colors, fr.depths, fr.background, fr.settings,
-                                fr.image, fr.final_T, fr.last_idx, None, None, cnt[0:4])
-        raster.gs_rasterize_bwd(g.N, g.ld, W, H, fr.ranges, fr.ids, fr.means2d, fr.conics,
-                                g.opacities, fr.colors, fr.background, fr.settings, fr.final_T,
-                                fr.last_idx, fr.dL_dimage, fr.g_means2d, fr.g_conics,
-                                fr.g_opacities, fr.g_colors, 0, cnt[4:8])
+        fr.rasterize(g, counters=cnt[0:4])
+        fr.rasterize_backward(g, counters=cnt[4:8])
         torch.cuda.synchronize()
         c = cnt.cpu().numpy()
         V = int((fr.radii[:N] > 0).sum().item())

@@ -8,16 +8,17 @@
 
 extern "C" {
 hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
-                                 const float* scales, const float* quats, const float* sh,
-                                 const gs::Cam& cam, const gs::Settings& st, float* means2d,
-                                 float* conics, float* depths, int32_t* radii, float* colors,
-                                 uint32_t* tiles, hipStream_t stream);
+                                 const float* scales, const float* quats, const float* opac,
+                                 const float* sh, const gs::Cam& cam, const gs::Settings& st,
+                                 float* means2d, float* conics, float* depths, int32_t* radii,
+                                 float* colors, uint32_t* tiles, float* splats,
+                                 hipStream_t stream);
 hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, const float* means,
                                  const float* scales, const float* quats, const float* sh,
                                  const gs::Cam& cam, const gs::Settings& st, const int32_t* radii,
-                                 const float* g_m2, const float* g_con, const float* g_col,
-                                 float* o_means, float* o_scales, float* o_quats, float* o_sh,
-                                 int accumulate, hipStream_t stream);
+                                 const float* grads2d, float* o_means, float* o_scales,
+                                 float* o_quats, float* o_opac, float* o_sh, int accumulate,
+                                 hipStream_t stream);
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
 hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, void* workspace,
                           uint64_t capacity, int32_t T, uint64_t* total_host, hipStream_t s);
@@ -28,18 +29,17 @@ hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
 hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges, const uint32_t* ids,
-                                int64_t ld, const float* means2d, const float* conics,
-                                const float* opac, const float* colors, const float* depths,
-                                const float* bg, const gs::Settings& st, float* image,
-                                float* final_T, uint32_t* last_idx, float* out_depth,
-                                float* out_alpha, uint64_t* counters, hipStream_t s);
+                                const float* splats, const float* depths, const float* bg,
+                                const gs::Settings& st,
+                                float* image, float* final_T, uint32_t* last_idx,
+                                float* out_depth, float* out_alpha, uint64_t* counters,
+                                hipStream_t s);
 hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
-                                const uint32_t* ids, int64_t ld, const float* means2d,
-                                const float* conics, const float* opac, const float* colors,
-                                const float* bg, const gs::Settings& st, const float* final_T,
-                                const uint32_t* last_idx, const float* dL_dimage, float* g_m2,
-                                float* g_con, float* g_op, float* g_col, int accumulate,
-                                uint64_t* counters, hipStream_t s);
+                                const uint32_t* ids, const float* splats, const uint32_t* offsets,
+                                const uint32_t* tiles, const float* bg, const gs::Settings& st,
+                                const float* final_T, const uint32_t* last_idx,
+                                const float* dL_dimage, float* partials, uint64_t capacity,
+                                float* grads2d, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
 }
@@ -101,6 +101,8 @@ gs_status check_settings(const gs_settings* st) {
   return GS_OK;
 }
 
+bool aligned64(const void* p) { return ((uintptr_t)p & 63u) == 0; }
+
 #define GS_CHECK(expr)               \
   do {                               \
     gs_status _s = (expr);           \
@@ -140,22 +142,24 @@ int32_t gs_num_tiles(int32_t width, int32_t height) {
 }
 
 gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
-                         const float* scales, const float* quats, const float* sh,
-                         const gs_camera* cam, const gs_settings* settings, float* means2d,
-                         float* conics, float* depths, int32_t* radii, float* colors,
-                         uint32_t* tiles_touched, void* stream) {
+                         const float* scales, const float* quats, const float* opacities,
+                         const float* sh, const gs_camera* cam, const gs_settings* settings,
+                         float* means2d, float* conics, float* depths, int32_t* radii,
+                         float* colors, uint32_t* tiles_touched, float* splats, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
   GS_CHECK(check_camera(cam));
   GS_CHECK(check_settings(settings));
-  if (N > 0)
-    GS_REQUIRE(means && scales && quats && sh && means2d && conics && depths && radii && colors &&
-                   tiles_touched,
+  if (N > 0) {
+    GS_REQUIRE(means && scales && quats && opacities && sh && means2d && conics && depths &&
+                   radii && colors && tiles_touched && splats,
                "NULL array pointer");
-  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, sh,
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
+  }
+  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh,
                                           gs::make_cam(*cam), gs::make_settings(*settings),
                                           means2d, conics, depths, radii, colors, tiles_touched,
-                                          (hipStream_t)stream),
+                                          splats, (hipStream_t)stream),
                     "gs_project_fwd");
 }
 
@@ -204,11 +208,10 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
 }
 
 gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids,
-                           const float* means2d, const float* conics, const float* opacities,
-                           const float* colors, const float* depths, const float* background,
-                           const gs_settings* settings, float* image, float* final_T,
-                           uint32_t* last_idx, float* out_depth, float* out_alpha,
+                           const uint32_t* tile_ranges, const uint32_t* ids, const float* splats,
+                           const float* depths, const float* background,
+                           const gs_settings* settings, float* image,
+                           float* final_T, uint32_t* last_idx, float* out_depth, float* out_alpha,
                            uint64_t* counters, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_image(width, height));
@@ -216,65 +219,68 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
   GS_REQUIRE(background != nullptr, "background is NULL");
   GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
   if (N > 0) {
-    GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
+    GS_REQUIRE(ids && splats, "NULL splat pointer");
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
     if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
   }
-  return hip_status(gs_launch_raster_fwd(width, height, tile_ranges, ids, ld, means2d, conics,
-                                         opacities, colors, depths, background,
+  return hip_status(gs_launch_raster_fwd(width, height, tile_ranges, ids, splats, depths,
+                                         background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
                                          out_depth, out_alpha, counters, (hipStream_t)stream),
                     "gs_rasterize_fwd");
 }
 
 gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids,
-                           const float* means2d, const float* conics, const float* opacities,
-                           const float* colors, const float* background,
+                           const uint32_t* tile_ranges, const uint32_t* ids, const float* splats,
+                           const uint32_t* offsets, const uint32_t* tiles_touched,
+                           uint64_t num_instances, const float* background,
                            const gs_settings* settings, const float* final_T,
-                           const uint32_t* last_idx, const float* dL_dimage,
-                           float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
-                           float* dL_dcolors, int32_t accumulate, uint64_t* counters,
+                           const uint32_t* last_idx, const float* dL_dimage, float* partials,
+                           uint64_t partials_capacity, float* grads2d, uint64_t* counters,
                            void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_image(width, height));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(background != nullptr, "background is NULL");
   GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
+  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
   if (N > 0) {
-    GS_REQUIRE(ids && means2d && conics && opacities && colors, "NULL splat pointer");
-    GS_REQUIRE(dL_dmeans2d && dL_dconics && dL_dopacities && dL_dcolors,
-               "NULL gradient pointer");
+    GS_REQUIRE(ids && splats && offsets && tiles_touched && grads2d,
+               "NULL splat, offset or gradient pointer");
+    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
   }
-  GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
-  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, ld, means2d, conics,
-                                         opacities, colors, background,
-                                         gs::make_settings(*settings), final_T, last_idx,
-                                         dL_dimage, dL_dmeans2d, dL_dconics, dL_dopacities,
-                                         dL_dcolors, accumulate, counters, (hipStream_t)stream),
+  if (num_instances > 0) {
+    GS_REQUIRE(partials != nullptr, "partials is NULL");
+    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
+  }
+  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
+                                         tiles_touched, background, gs::make_settings(*settings),
+                                         final_T, last_idx, dL_dimage, partials, num_instances,
+                                         grads2d, counters, (hipStream_t)stream),
                     "gs_rasterize_bwd");
 }
 
 gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
                          const float* scales, const float* quats, const float* sh,
                          const gs_camera* cam, const gs_settings* settings,
-                         const int32_t* radii, const float* dL_dmeans2d,
-                         const float* dL_dconics, const float* dL_dcolors, float* dL_dmeans,
-                         float* dL_dscales, float* dL_dquats, float* dL_dsh,
-                         int32_t accumulate, void* stream) {
+                         const int32_t* radii, const float* grads2d, float* dL_dmeans,
+                         float* dL_dscales, float* dL_dquats, float* dL_dopacities,
+                         float* dL_dsh, int32_t accumulate, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
   GS_CHECK(check_camera(cam));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
-  if (N > 0)
-    GS_REQUIRE(means && scales && quats && sh && radii && dL_dmeans2d && dL_dconics &&
-                   dL_dcolors && dL_dmeans && dL_dscales && dL_dquats && dL_dsh,
+  if (N > 0) {
+    GS_REQUIRE(means && scales && quats && sh && radii && grads2d && dL_dmeans && dL_dscales &&
+                   dL_dquats && dL_dopacities && dL_dsh,
                "NULL array pointer");
+    GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
+  }
   return hip_status(gs_launch_project_bwd(N, ld, sh_degree, means, scales, quats, sh,
                                           gs::make_cam(*cam), gs::make_settings(*settings), radii,
-                                          dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans,
-                                          dL_dscales, dL_dquats, dL_dsh, accumulate,
-                                          (hipStream_t)stream),
+                                          grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities,
+                                          dL_dsh, accumulate, (hipStream_t)stream),
                     "gs_project_bwd");
 }
 

@@ -222,12 +222,36 @@ __device__ inline void sh_colour(int deg, int K, const float* __restrict__ sh, i
       raw[ch] = fmaf(Y[j], sh[(int64_t)(j * 3 + ch) * ld + i], raw[ch]);
 }
 
+// Padded half-extents of the footprint where alpha = o exp(-q/2) can reach
+// alpha_min: q <= Q = 2 ln(o / alpha_min), whose ellipse lies inside
+// |dx| <= sqrt(Q a), |dy| <= sqrt(Q c) for the dilated 2D covariance
+// (a, b, c) = conic^-1.  Q and the extents are padded (2% + constants) so
+// that the compositing kernels' fp32 pixel test can never reach alpha_min
+// outside the box; nearly singular covariances (kappa > ~1e4) are left
+// unbounded.  Negative: the Gaussian never reaches alpha_min (o < alpha_min).
+__device__ inline void footprint(float a, float b, float c, float o, float alpha_min, float& ex,
+                                 float& ey) {
+  if (!(o >= alpha_min)) {
+    ex = ey = -1.0f;
+    return;
+  }
+  const float tr = a + c;
+  if (!(a * c - b * b > 1e-4f * tr * tr)) {
+    ex = ey = __builtin_inff();
+    return;
+  }
+  const float Q = fmaf(2.0f * (__logf(o) - __logf(alpha_min)), 1.02f, 0.05f);
+  ex = sqrtf(Q * a) + 0.02f;
+  ey = sqrtf(Q * c) + 0.02f;
+}
+
 __global__ __launch_bounds__(256) void project_fwd_kernel(
     int64_t N, int64_t ld, int deg, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ sh, Cam cam, Settings st, float* __restrict__ means2d,
-    float* __restrict__ conics, float* __restrict__ depths, int32_t* __restrict__ radii,
-    float* __restrict__ colors, uint32_t* __restrict__ tiles) {
+    const float* __restrict__ opac, const float* __restrict__ sh, Cam cam, Settings st,
+    float* __restrict__ means2d, float* __restrict__ conics, float* __restrict__ depths,
+    int32_t* __restrict__ radii, float* __restrict__ colors, uint32_t* __restrict__ tiles,
+    float4* __restrict__ splats) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
   const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
@@ -257,7 +281,19 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
   const int K = (deg + 1) * (deg + 1);
   float raw[3], Y[16];
   sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
-  for (int ch = 0; ch < 3; ++ch) colors[(int64_t)ch * ld + i] = raw[ch] < 0.0f ? 0.0f : raw[ch];
+  float col[3];
+  for (int ch = 0; ch < 3; ++ch) {
+    col[ch] = raw[ch] < 0.0f ? 0.0f : raw[ch];
+    colors[(int64_t)ch * ld + i] = col[ch];
+  }
+  const float o = opac[i];
+  float ex, ey;
+  footprint(g.a, g.b, g.c, o, st.alpha_min, ex, ey);
+  float4* rec = splats + 4 * i;
+  rec[0] = make_float4(g.u, g.v, (-0.5f * kLog2e) * g.A, (-kLog2e) * g.B);
+  rec[1] = make_float4((-0.5f * kLog2e) * g.C, o, col[0], col[1]);
+  rec[2] = make_float4(col[2], __int_as_float(g.radius), ex, ey);
+  rec[3] = make_float4(g.A, g.B, g.C, 0.0f);
 }
 
 // Backward of the projection, chain rule in fp32.  The forward's geometry is
@@ -267,9 +303,9 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     int64_t N, int64_t ld, int deg, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ sh, Cam cam, Settings st, const int32_t* __restrict__ radii,
-    const float* __restrict__ g_m2, const float* __restrict__ g_con,
-    const float* __restrict__ g_col, float* __restrict__ o_means, float* __restrict__ o_scales,
-    float* __restrict__ o_quats, float* __restrict__ o_sh, int accumulate) {
+    const float4* __restrict__ grads2d, float* __restrict__ o_means,
+    float* __restrict__ o_scales, float* __restrict__ o_quats, float* __restrict__ o_opac,
+    float* __restrict__ o_sh, int accumulate) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
   const int K = (deg + 1) * (deg + 1);
@@ -289,9 +325,13 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
       for (int k = 0; k < 3; ++k) { o_means[(int64_t)k * ld + i] = 0.0f; o_scales[(int64_t)k * ld + i] = 0.0f; }
       for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + i] = 0.0f;
       for (int k = 0; k < 3 * K; ++k) o_sh[(int64_t)k * ld + i] = 0.0f;
+      o_opac[i] = 0.0f;
     }
     return;
   }
+  const float4 r0 = grads2d[4 * i + 0], r1 = grads2d[4 * i + 1], r2 = grads2d[4 * i + 2];
+  // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
+  o_opac[i] = accumulate ? o_opac[i] + r1.y : r1.y;
   const float* W = cam.R;
   const float tx = tc[0], ty = tc[1], tz = tc[2];
   const float fx = cam.fx, fy = cam.fy;
@@ -300,7 +340,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   const float a = g.a, b = g.b, c = g.c;
   const float det = a * c - b * b;
   const float id = 1.0f / det, id2 = id * id;
-  const float gA = g_con[i], gB = g_con[ld + i], gC = g_con[2 * ld + i];
+  const float gA = r0.z, gB = r0.w, gC = r1.x;
   const float ga = gA * (-c * c * id2) + gB * (b * c * id2) + gC * (id - a * c * id2);
   const float gb = gA * (2.0f * b * c * id2) + gB * (-id - 2.0f * b * b * id2) + gC * (2.0f * a * b * id2);
   const float gc = gA * (id - a * c * id2) + gB * (a * b * id2) + gC * (-a * a * id2);
@@ -347,7 +387,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     gt[1] += gJ12 * (-fy * itz2);
     gt[2] += gJ12 * (2.0f * fy * ty * itz3);
   }
-  const float gu = g_m2[i], gv = g_m2[ld + i];
+  const float gu = r0.x, gv = r0.y;
   gt[0] += gu * fx * itz;
   gt[2] += gu * (-fx * tx * itz2);
   gt[1] += gv * fy * itz;
@@ -387,9 +427,9 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
   float raw[3], Y[16];
   sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
+  const float gin[3] = {r1.z, r1.w, r2.x};
   float gcol[3];
-  for (int ch = 0; ch < 3; ++ch)
-    gcol[ch] = raw[ch] < 0.0f ? 0.0f : g_col[(int64_t)ch * ld + i];
+  for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0f ? 0.0f : gin[ch];
   float gd[3] = {0.0f, 0.0f, 0.0f};
   for (int j = 0; j < K; ++j) {
     float wj = 0.0f;
@@ -420,15 +460,16 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
 
 extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
                                             const float* scales, const float* quats,
-                                            const float* sh, const gs::Cam& cam,
-                                            const gs::Settings& st, float* means2d,
-                                            float* conics, float* depths, int32_t* radii,
-                                            float* colors, uint32_t* tiles, hipStream_t stream) {
+                                            const float* opac, const float* sh,
+                                            const gs::Cam& cam, const gs::Settings& st,
+                                            float* means2d, float* conics, float* depths,
+                                            int32_t* radii, float* colors, uint32_t* tiles,
+                                            float* splats, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
   hipLaunchKernelGGL(gs::project_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
-                     deg, means, scales, quats, sh, cam, st, means2d, conics, depths, radii,
-                     colors, tiles);
+                     deg, means, scales, quats, opac, sh, cam, st, means2d, conics, depths, radii,
+                     colors, tiles, (float4*)splats);
   return hipGetLastError();
 }
 
@@ -436,14 +477,13 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, cons
                                             const float* scales, const float* quats,
                                             const float* sh, const gs::Cam& cam,
                                             const gs::Settings& st, const int32_t* radii,
-                                            const float* g_m2, const float* g_con,
-                                            const float* g_col, float* o_means, float* o_scales,
-                                            float* o_quats, float* o_sh, int accumulate,
-                                            hipStream_t stream) {
+                                            const float* grads2d, float* o_means,
+                                            float* o_scales, float* o_quats, float* o_opac,
+                                            float* o_sh, int accumulate, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
   hipLaunchKernelGGL(gs::project_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
-                     deg, means, scales, quats, sh, cam, st, radii, g_m2, g_con, g_col, o_means,
-                     o_scales, o_quats, o_sh, accumulate);
+                     deg, means, scales, quats, sh, cam, st, radii, (const float4*)grads2d,
+                     o_means, o_scales, o_quats, o_opac, o_sh, accumulate);
   return hipGetLastError();
 }

@@ -19,8 +19,11 @@
 // blended entry.  Per splat each wave reduces its 64 pixels' nine gradient
 // terms with two gfx950 lane-swap transpose steps and a DPP row scan
 // (skipped with a ballot when no lane of the wave touched the splat); the
-// wave partials meet in LDS and one lane per splat issues at most nine fp32
-// atomics per tile, instead of one per pixel.
+// wave partials meet in LDS and the tile stores its sums for the splat, with
+// a plain 48-byte store, into the instance's own slot (the Gaussian's offset
+// plus the tile's index in its rect).  A second kernel adds each Gaussian's
+// slots in a fixed order.  No global atomics: device-scope float atomics go
+// to memory on this part, and a fixed order makes gradients reproducible.
 //
 // Decisions (q < 0, alpha < alpha_min, alpha clamp, stop at T < T_min) are
 // taken by the same inline code in both kernels, compiled without
@@ -36,44 +39,24 @@ struct SplatLds {
   float u, v, qa, qb, qc, o, r, g, b, z;
 };
 
-__device__ inline void stage_splat(SplatLds& s, uint32_t id, int64_t ld,
-                                   const float* __restrict__ means2d,
-                                   const float* __restrict__ conics,
-                                   const float* __restrict__ opac,
-                                   const float* __restrict__ colors,
-                                   const float* __restrict__ depths, float& A, float& B,
-                                   float& C) {
-  s.u = means2d[id];
-  s.v = means2d[ld + id];
-  A = conics[id];
-  B = conics[ld + id];
-  C = conics[2 * ld + id];
-  s.qa = (-0.5f * kLog2e) * A;
-  s.qb = (-kLog2e) * B;
-  s.qc = (-0.5f * kLog2e) * C;
-  s.o = opac[id];
-  s.r = colors[id];
-  s.g = colors[ld + id];
-  s.b = colors[2 * ld + id];
-  s.z = depths ? depths[id] : 0.0f;
+// Stage one splat record (three 16-byte loads of one 64-byte line) into LDS
+// and return the record's radius and footprint half-extents.
+__device__ inline void stage_splat(SplatLds& s, const float4* __restrict__ rec, int32_t& radius,
+                                   float& ex, float& ey) {
+  const float4 a = rec[0], b = rec[1], c = rec[2];
+  s.u = a.x; s.v = a.y; s.qa = a.z; s.qb = a.w;
+  s.qc = b.x; s.o = b.y; s.r = b.z; s.g = b.w;
+  s.b = c.x; s.z = 0.0f;
+  radius = __float_as_int(c.y);
+  ex = c.z;
+  ey = c.w;
 }
 
 // Which of the tile's four 4-row bands (one wavefront each) can hold a pixel
-// centre where the splat reaches alpha_min.  alpha >= alpha_min needs
-// q <= Q = 2 ln(o / alpha_min); the ellipse {q <= Q} lies inside
-// |dx| <= sqrt(Q Sxx), |dy| <= sqrt(Q Syy) with S = conic^-1.  Q and the
-// extents are padded (2% + constants) so that fp32 rounding of the pixel test
-// can never reach alpha_min outside the box: a skipped pair is one the
-// forward would have skipped too.  Ill-conditioned conics keep every band.
-__device__ inline uint32_t band_mask(const SplatLds& s, float A, float B, float C,
-                                     float alpha_min, int tx0, int ty0) {
-  if (!(s.o >= alpha_min)) return 0u;  // alpha <= o everywhere
-  const float tr = A + C;
-  const float det = A * C - B * B;
-  if (!(det > 1e-4f * tr * tr)) return 0xFu;
-  const float Q = fmaf(2.0f * (__logf(s.o) - __logf(alpha_min)), 1.02f, 0.05f);
-  const float ex = sqrtf(Q * (C / det)) + 0.02f;
-  const float ey = sqrtf(Q * (A / det)) + 0.02f;
+// centre where the splat reaches alpha_min, from the record's padded
+// footprint half-extents (a skipped pair is one the forward skips too).
+__device__ inline uint32_t band_mask(const SplatLds& s, float ex, float ey, int tx0, int ty0) {
+  if (!(ex >= 0.0f)) return 0u;  // opacity below alpha_min
   const float x0 = (float)tx0 + 0.5f, x1 = (float)tx0 + 15.5f;
   if (!(s.u + ex >= x0 && s.u - ex <= x1)) return 0u;
   uint32_t m = 0u;
@@ -145,11 +128,10 @@ __device__ inline void add_counters(uint64_t* cnt, uint64_t a, uint64_t b, uint6
 template <bool kDepth, bool kStats>
 __global__ __launch_bounds__(256) void raster_fwd_kernel(
     int W, int H, int gx, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids,
-    int64_t ld, const float* __restrict__ means2d, const float* __restrict__ conics,
-    const float* __restrict__ opac, const float* __restrict__ colors,
-    const float* __restrict__ depths, float bg0, float bg1, float bg2, Settings st,
-    float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ last_idx,
-    float* __restrict__ out_depth, float* __restrict__ out_alpha, uint64_t* __restrict__ cnt) {
+    const float4* __restrict__ splats, const float* __restrict__ depths, float bg0, float bg1,
+    float bg2, Settings st, float* __restrict__ image, float* __restrict__ final_T,
+    uint32_t* __restrict__ last_idx, float* __restrict__ out_depth,
+    float* __restrict__ out_alpha, uint64_t* __restrict__ cnt) {
   __shared__ SplatLds s_sp[256];
   __shared__ uint8_t s_list[4][256];
   __shared__ uint32_t s_cnt[4];
@@ -172,10 +154,12 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     const uint32_t j = b + (uint32_t)tid;
     uint32_t mask = 0u;
     if (j < end) {
-      float A, B, C;
-      stage_splat(s_sp[tid], ids[j], ld, means2d, conics, opac, colors,
-                  kDepth ? depths : nullptr, A, B, C);
-      mask = band_mask(s_sp[tid], A, B, C, amin, tx * kTile, ty * kTile);
+      const uint32_t id = ids[j];
+      float ex, ey;
+      int32_t rad;
+      stage_splat(s_sp[tid], splats + 4 * (size_t)id, rad, ex, ey);
+      if (kDepth) s_sp[tid].z = depths[id];
+      mask = band_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
     compact_bands(mask, s_list, s_cnt, s_wc);
     const int cnt = (int)s_cnt[wave];
@@ -253,8 +237,11 @@ __device__ inline float row_total_lane15(float v) {
 }
 #undef GS_ROW_ADD
 
-// Sums f[0..8] over the wavefront and stores field q at dst[q * stride].
-__device__ inline void reduce9_store(const float f[9], float* dst, int stride) {
+// Sums f[0..8] over the wavefront and adds field q to dst[q * stride] (LDS,
+// atomically).  Callers give each pair of wavefronts its own slots: from a
+// zero start, two float additions give the same bits in either order, so the
+// result does not depend on which wavefront of the pair came first.
+__device__ inline void reduce9_add(const float f[9], float* dst, int stride) {
   const float s01 = swap_add32(f[0], f[1]);
   const float s23 = swap_add32(f[2], f[3]);
   const float s45 = swap_add32(f[4], f[5]);
@@ -271,9 +258,9 @@ __device__ inline void reduce9_store(const float f[9], float* dst, int stride) {
   if ((lane & 15) == 15) {
     const int row = lane >> 4;
     const int q = (row == 1) ? 2 : (row == 2 ? 1 : row);
-    dst[q * stride] = t0;
-    dst[(4 + q) * stride] = t1;
-    if (row == 0) dst[8 * stride] = t2;
+    atomicAdd(&dst[q * stride], t0);
+    atomicAdd(&dst[(4 + q) * stride], t1);
+    if (row == 0) atomicAdd(&dst[8 * stride], t2);
   }
 }
 
@@ -284,22 +271,28 @@ __device__ inline void reduce9_store(const float f[9], float* dst, int stride) {
 //   dL/dA = Sxx, dL/dB = 2 Sxy, dL/dC = Syy.
 constexpr int kFields = 9;
 
+// Slot of Gaussian `id`'s instance for tile (tx, ty): its offset plus the
+// tile's row-major index inside the Gaussian's rect.
+__device__ inline uint64_t instance_slot(float u, float v, int32_t radius, uint32_t offset, int tx,
+                                         int ty, int gx, int gy) {
+  int x0, x1, y0, y1;
+  tile_rect(u, v, radius, gx, gy, x0, x1, y0, y1);
+  const int w = (x1 > x0) ? x1 - x0 : 1;
+  return (uint64_t)offset + (uint64_t)((ty - y0) * w + (tx - x0));
+}
+
 template <bool kStats>
 __global__ __launch_bounds__(256) void raster_bwd_kernel(
     int W, int H, int gx, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids,
-    int64_t ld, const float* __restrict__ means2d, const float* __restrict__ conics,
-    const float* __restrict__ opac, const float* __restrict__ colors, float bg0, float bg1,
-    float bg2, Settings st, const float* __restrict__ final_T,
+    const float4* __restrict__ splats, const uint32_t* __restrict__ offsets, float bg0,
+    float bg1, float bg2, Settings st, const float* __restrict__ final_T,
     const uint32_t* __restrict__ last_idx, const float* __restrict__ dL_dimage,
-    float* __restrict__ g_m2, float* __restrict__ g_con, float* __restrict__ g_op,
-    float* __restrict__ g_col, uint64_t* __restrict__ cnt) {
+    float4* __restrict__ partials, uint64_t capacity, uint64_t* __restrict__ cnt) {
   __shared__ SplatLds s_sp[256];
-  __shared__ uint32_t s_id[256];
-  __shared__ uint8_t s_mask[256];
   __shared__ uint8_t s_list[4][256];
   __shared__ uint32_t s_cnt[4];
   __shared__ uint32_t s_wc[4][4];
-  __shared__ float s_part[4][kFields][256];
+  __shared__ float s_acc[2][kFields][256];  // one set per pair of wavefronts
   __shared__ uint32_t s_maxlast;
   const int tile = blockIdx.x;
   const int tx = tile % gx, ty = tile / gx;
@@ -326,27 +319,52 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   __syncthreads();
   if (last) atomicMax(&s_maxlast, last);
   __syncthreads();
-  const uint32_t stop = start + s_maxlast;  // nothing at or after this is blended
-  if (stop > end) return;  // inconsistent inputs: leave gradients untouched
+  // nothing at or after `stop` is blended; last indices beyond the tile's
+  // list (inputs that do not belong together) give the tile zero gradients
+  const uint32_t stop = (s_maxlast > end - start) ? start : start + s_maxlast;
+  const int gy = grid_dim(H);
   uint32_t n_eval = 0, n_hit = 0, n_red = 0;  // counters (kStats only)
+
+  // entries no pixel of the tile blends: their instance slots get zeros
+  for (uint32_t j = stop + (uint32_t)tid; j < end; j += 256u) {
+    const uint32_t id = ids[j];
+    const float4 a = splats[4 * (size_t)id], c = splats[4 * (size_t)id + 2];
+    const uint64_t slot =
+        instance_slot(a.x, a.y, __float_as_int(c.y), offsets[id], tx, ty, gx, gy);
+    if (slot < capacity) {
+      const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      partials[4 * slot + 0] = z;
+      partials[4 * slot + 1] = z;
+      partials[4 * slot + 2] = z;
+    }
+  }
 
   for (uint32_t b_end = stop; b_end > start;) {
     const uint32_t b_begin = (b_end - start) > 256u ? b_end - 256u : start;
     const int n = (int)(b_end - b_begin);
     __syncthreads();
-    uint32_t mask = 0u;
+    uint32_t mask = 0u, my_off = 0u;
+    int32_t my_rad = 0;
+    float cA = 0.0f, cB = 0.0f, cC = 0.0f;  // raw conic of the splat this thread stages
     if (tid < n) {
-      const uint32_t id = ids[b_end - 1u - (uint32_t)tid];  // slot k = tid: back to front
-      float A, B, C;
-      s_id[tid] = id;
-      stage_splat(s_sp[tid], id, ld, means2d, conics, opac, colors, nullptr, A, B, C);
-      mask = band_mask(s_sp[tid], A, B, C, amin, tx * kTile, ty * kTile);
-      s_mask[tid] = (uint8_t)mask;
+      const uint32_t my_id = ids[b_end - 1u - (uint32_t)tid];  // slot k = tid: back to front
+      const float4* rec = splats + 4 * (size_t)my_id;
+      my_off = offsets[my_id];
+      float ex, ey;
+      stage_splat(s_sp[tid], rec, my_rad, ex, ey);
+      const float4 d = rec[3];
+      cA = d.x; cB = d.y; cC = d.z;
+      mask = band_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
+    }
+#pragma unroll
+    for (int q = 0; q < kFields; ++q) {
+      s_acc[0][q][tid] = 0.0f;
+      s_acc[1][q][tid] = 0.0f;
     }
     compact_bands(mask, s_list, s_cnt, s_wc);
-    const int cnt = (int)s_cnt[wave];
+    const int cnt_w = (int)s_cnt[wave];
     const uint32_t relbase = b_end - 1u - start;
-    for (int i = 0; i < cnt; ++i) {
+    for (int i = 0; i < cnt_w; ++i) {
       const int k = s_list[wave][i];
       const SplatLds& s = s_sp[k];
       const uint32_t rel = relbase - (uint32_t)k;  // list position in the tile
@@ -381,60 +399,102 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       f[2] = mx * dx;
       f[3] = mx * dy;
       f[4] = my * dy;
-      float* dst = &s_part[wave][0][k];
       if (kStats) {
         n_eval += inside ? 1u : 0u;
         n_hit += hit ? 1u : 0u;
       }
       if (__ballot(hit) != 0ull) {
         if (kStats) n_red += (lane == 0) ? 1u : 0u;
-        reduce9_store(f, dst, 256);
-      } else if (lane == 0) {
-#pragma unroll
-        for (int q = 0; q < kFields; ++q) dst[q * 256] = 0.0f;
+        reduce9_add(f, &s_acc[wave >> 1][0][k], 256);
       }
     }
     __syncthreads();
     if (tid < n) {
-      const uint32_t id = s_id[tid];
-      const uint32_t msk = s_mask[tid];
       float acc[kFields];
 #pragma unroll
-      for (int q = 0; q < kFields; ++q) acc[q] = 0.0f;
-      for (int w = 0; w < 4; ++w)
-        if ((msk >> w) & 1u)
-#pragma unroll
-          for (int q = 0; q < kFields; ++q) acc[q] += s_part[w][q][tid];
-      const SplatLds& s = s_sp[tid];
-      const float A = s.qa * (-2.0f / kLog2e), B = s.qb * (-1.0f / kLog2e),
-                  C = s.qc * (-2.0f / kLog2e);
-      const float gu = -2.0f * fmaf(A, acc[0], B * acc[1]);
-      const float gv = -2.0f * fmaf(B, acc[0], C * acc[1]);
-      const float gA = acc[2], gB = 2.0f * acc[3], gC = acc[4];
-      if (gu != 0.0f) atomicAdd(&g_m2[id], gu);
-      if (gv != 0.0f) atomicAdd(&g_m2[ld + id], gv);
-      if (gA != 0.0f) atomicAdd(&g_con[id], gA);
-      if (gB != 0.0f) atomicAdd(&g_con[ld + id], gB);
-      if (gC != 0.0f) atomicAdd(&g_con[2 * ld + id], gC);
-      if (acc[5] != 0.0f) atomicAdd(&g_op[id], acc[5]);
-      if (acc[6] != 0.0f) atomicAdd(&g_col[id], acc[6]);
-      if (acc[7] != 0.0f) atomicAdd(&g_col[ld + id], acc[7]);
-      if (acc[8] != 0.0f) atomicAdd(&g_col[2 * ld + id], acc[8]);
+      for (int q = 0; q < kFields; ++q) acc[q] = s_acc[0][q][tid] + s_acc[1][q][tid];
+      // moments -> gradients of u, v and the conic
+      const float gu = -2.0f * fmaf(cA, acc[0], cB * acc[1]);
+      const float gv = -2.0f * fmaf(cB, acc[0], cC * acc[1]);
+      const uint64_t slot =
+          instance_slot(s_sp[tid].u, s_sp[tid].v, my_rad, my_off, tx, ty, gx, gy);
+      if (slot < capacity) {
+        partials[4 * slot + 0] = make_float4(gu, gv, acc[2], 2.0f * acc[3]);
+        partials[4 * slot + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        partials[4 * slot + 2] = make_float4(acc[8], 0.0f, 0.0f, 0.0f);
+      }
     }
     b_end = b_begin;
   }
   if (kStats) add_counters(cnt, n_eval, n_hit, 0u, n_red);
 }
 
-// Zero the first n entries of nine gradient planes in one launch.
-struct ZeroPlanes {
-  float* p[9];
-};
-__global__ void zero_planes_kernel(ZeroPlanes z, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
+// Sum each visible Gaussian's instance slots [offsets[i], offsets[i] +
+// tiles[i]) of partials into its 2D gradient record, in slot order, so the
+// result does not depend on scheduling.  A lane sums a Gaussian touching at
+// most kSmallSeg tiles on its own; larger ones are summed by the whole
+// workgroup with a fixed-shape tree.
+constexpr uint32_t kSmallSeg = 32;
+
+__device__ inline void add_rec(float a[kFields], const float4* __restrict__ p) {
+  const float4 x = p[0], y = p[1], z = p[2];
+  a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
+  a[4] += y.x; a[5] += y.y; a[6] += y.z; a[7] += y.w;
+  a[8] += z.x;
+}
+
+__device__ inline void store_rec(float4* __restrict__ r, const float a[kFields]) {
+  r[0] = make_float4(a[0], a[1], a[2], a[3]);
+  r[1] = make_float4(a[4], a[5], a[6], a[7]);
+  r[2] = make_float4(a[8], 0.0f, 0.0f, 0.0f);
+}
+
+__global__ __launch_bounds__(256) void reduce_partials_kernel(
+    int64_t N, const uint32_t* __restrict__ offsets, const uint32_t* __restrict__ tiles,
+    const float4* __restrict__ partials, float4* __restrict__ grads2d) {
+  __shared__ uint32_t s_big[256];
+  __shared__ uint32_t s_nbig;
+  __shared__ float s_red[kFields][256];
+  const int t = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + t;
+  if (t == 0) s_nbig = 0;
+  __syncthreads();
+  if (i < N) {
+    const uint32_t cnt = tiles[i];
+    if (cnt > kSmallSeg) {
+      s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)t;
+    } else if (cnt > 0) {
+      float a[kFields] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+      const uint64_t base = offsets[i];
+      for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
+      store_rec(grads2d + 4 * i, a);
+    }
+  }
+  __syncthreads();
+  const uint32_t nbig = s_nbig;
+  for (uint32_t b = 0; b < nbig; ++b) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + s_big[b];
+    const uint32_t cnt = tiles[gi];
+    const uint64_t base = offsets[gi];
+    float a[kFields] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    for (uint32_t k = (uint32_t)t; k < cnt; k += 256u) add_rec(a, partials + 4 * (base + k));
 #pragma unroll
-    for (int k = 0; k < 9; ++k) z.p[k][i] = 0.0f;
+    for (int q = 0; q < kFields; ++q) s_red[q][t] = a[q];
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+      if (t < h)
+#pragma unroll
+        for (int q = 0; q < kFields; ++q) s_red[q][t] += s_red[q][t + h];
+      __syncthreads();
+    }
+    if (t == 0) {
+      float r[kFields];
+#pragma unroll
+      for (int q = 0; q < kFields; ++q) r[q] = s_red[q][0];
+      store_rec(grads2d + 4 * gi, r);
+    }
+    __syncthreads();
+  }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p) { *p = 0.0f; }
@@ -474,65 +534,60 @@ __global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n,
 }  // namespace gs
 
 extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges,
-                                           const uint32_t* ids, int64_t ld, const float* means2d,
-                                           const float* conics, const float* opac,
-                                           const float* colors, const float* depths,
-                                           const float* bg, const gs::Settings& st, float* image,
+                                           const uint32_t* ids, const float* splats,
+                                           const float* depths, const float* bg,
+                                           const gs::Settings& st, float* image,
                                            float* final_T, uint32_t* last_idx, float* out_depth,
                                            float* out_alpha, uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid((unsigned)(gx * gy)), block(256);
+  const float4* sp = (const float4*)splats;
   if (counters) {
     if (out_depth)
       hipLaunchKernelGGL((gs::raster_fwd_kernel<true, true>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, ld, means2d, conics, opac, colors, depths, bg[0], bg[1], bg[2], st,
-                         image, final_T, last_idx, out_depth, out_alpha, counters);
+                         ids, sp, depths, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
+                         out_depth, out_alpha, counters);
     else
       hipLaunchKernelGGL((gs::raster_fwd_kernel<false, true>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, ld, means2d, conics, opac, colors, nullptr, bg[0], bg[1], bg[2], st,
-                         image, final_T, last_idx, nullptr, out_alpha, counters);
+                         ids, sp, nullptr, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
+                         nullptr, out_alpha, counters);
   } else {
     if (out_depth)
       hipLaunchKernelGGL((gs::raster_fwd_kernel<true, false>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, ld, means2d, conics, opac, colors, depths, bg[0], bg[1], bg[2], st,
-                         image, final_T, last_idx, out_depth, out_alpha, nullptr);
+                         ids, sp, depths, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
+                         out_depth, out_alpha, nullptr);
     else
       hipLaunchKernelGGL((gs::raster_fwd_kernel<false, false>), grid, block, 0, s, W, H, gx,
-                         ranges, ids, ld, means2d, conics, opac, colors, nullptr, bg[0], bg[1],
-                         bg[2], st, image, final_T, last_idx, nullptr, out_alpha, nullptr);
+                         ranges, ids, sp, nullptr, bg[0], bg[1], bg[2], st, image, final_T,
+                         last_idx, nullptr, out_alpha, nullptr);
   }
   return hipGetLastError();
 }
 
 extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
-                                           const uint32_t* ids, int64_t ld, const float* means2d,
-                                           const float* conics, const float* opac,
-                                           const float* colors, const float* bg,
-                                           const gs::Settings& st, const float* final_T,
-                                           const uint32_t* last_idx, const float* dL_dimage,
-                                           float* g_m2, float* g_con, float* g_op, float* g_col,
-                                           int accumulate, uint64_t* counters, hipStream_t s) {
-  if (N > 0) {
-    // the 2D gradients are per call; the opacity gradient is a parameter
-    // gradient and keeps its contents when accumulating
-    gs::ZeroPlanes z = {{g_m2, g_m2 + ld, g_con, g_con + ld, g_con + 2 * ld, g_col, g_col + ld,
-                         g_col + 2 * ld, accumulate ? g_col : g_op}};
-    int64_t blocks = (N + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(gs::zero_planes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, z, N);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+                                           const uint32_t* ids, const float* splats,
+                                           const uint32_t* offsets, const uint32_t* tiles,
+                                           const float* bg, const gs::Settings& st,
+                                           const float* final_T, const uint32_t* last_idx,
+                                           const float* dL_dimage, float* partials,
+                                           uint64_t capacity, float* grads2d, uint64_t* counters,
+                                           hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid((unsigned)(gx * gy)), block(256);
+  const float4* sp = (const float4*)splats;
+  float4* part = (float4*)partials;
   if (counters)
-    hipLaunchKernelGGL(gs::raster_bwd_kernel<true>, grid, block, 0, s, W, H, gx, ranges, ids, ld,
-                       means2d, conics, opac, colors, bg[0], bg[1], bg[2], st, final_T, last_idx,
-                       dL_dimage, g_m2, g_con, g_op, g_col, counters);
+    hipLaunchKernelGGL(gs::raster_bwd_kernel<true>, grid, block, 0, s, W, H, gx, ranges, ids, sp,
+                       offsets, bg[0], bg[1], bg[2], st, final_T, last_idx, dL_dimage, part,
+                       capacity, counters);
   else
-    hipLaunchKernelGGL(gs::raster_bwd_kernel<false>, grid, block, 0, s, W, H, gx, ranges, ids, ld,
-                       means2d, conics, opac, colors, bg[0], bg[1], bg[2], st, final_T, last_idx,
-                       dL_dimage, g_m2, g_con, g_op, g_col, nullptr);
+    hipLaunchKernelGGL(gs::raster_bwd_kernel<false>, grid, block, 0, s, W, H, gx, ranges, ids, sp,
+                       offsets, bg[0], bg[1], bg[2], st, final_T, last_idx, dL_dimage, part,
+                       capacity, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || N == 0) return e;
+  hipLaunchKernelGGL(gs::reduce_partials_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                     N, offsets, tiles, part, (float4*)grads2d);
   return hipGetLastError();
 }
 

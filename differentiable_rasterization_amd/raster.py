@@ -67,19 +67,19 @@ def load():
     lib.gs_num_tiles.restype = i32
     lib.gs_num_tiles.argtypes = [i32, i32]
     lib.gs_project_fwd.restype = C.c_int
-    lib.gs_project_fwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 6 + [P]
+    lib.gs_project_fwd.argtypes = [i64, i64, i32] + [P] * 5 + [P, P] + [P] * 7 + [P]
     lib.gs_bin_and_sort_workspace_size.restype = C.c_size_t
     lib.gs_bin_and_sort_workspace_size.argtypes = [i64, u64, i32, i32]
     lib.gs_bin_and_sort.restype = C.c_int
     lib.gs_bin_and_sort.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                     C.c_size_t, P]
     lib.gs_rasterize_fwd.restype = C.c_int
-    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 8 + [P, P] + [P] * 5 + [P]
+    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 13
     lib.gs_rasterize_bwd.restype = C.c_int
-    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 7 + [P] + [P] * 3 + [P] * 4 + \
-        [i32, P, P]
+    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 5 + [u64] + [P] * 6 + \
+        [u64, P, P, P]
     lib.gs_project_bwd.restype = C.c_int
-    lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 4 + [P] * 4 + \
+    lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 2 + [P] * 5 + \
         [i32, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
@@ -138,12 +138,12 @@ def num_tiles(width, height) -> int:
 # ---------------------------------------------------------------------------
 # The entry points
 # ---------------------------------------------------------------------------
-def gs_project_fwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, means2d, conics,
-                   depths, radii, colors, tiles_touched, stream=None):
+def gs_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh, cam, settings,
+                   means2d, conics, depths, radii, colors, tiles_touched, splats, stream=None):
     lib = load()
-    _check(lib.gs_project_fwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
-                              C.byref(cam), C.byref(settings), _p(means2d), _p(conics),
-                              _p(depths), _p(radii), _p(colors), _p(tiles_touched),
+    _check(lib.gs_project_fwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(opacities),
+                              _p(sh), C.byref(cam), C.byref(settings), _p(means2d), _p(conics),
+                              _p(depths), _p(radii), _p(colors), _p(tiles_touched), _p(splats),
                               _stream(stream)))
 
 
@@ -164,38 +164,37 @@ def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height,
     return st, int(M.value)
 
 
-def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
-                     depths, background, settings, image, final_T, last_idx, out_depth=None,
-                     out_alpha=None, counters=None, stream=None):
+def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, background,
+                     settings, image, final_T, last_idx, out_depth=None, out_alpha=None,
+                     counters=None, stream=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
-                                _p(conics), _p(opacities), _p(colors), _p(depths), bg,
-                                C.byref(settings), _p(image), _p(final_T), _p(last_idx),
-                                _p(out_depth), _p(out_alpha), _p(counters), _stream(stream)))
+    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+                                _p(depths), bg, C.byref(settings), _p(image), _p(final_T),
+                                _p(last_idx), _p(out_depth), _p(out_alpha), _p(counters),
+                                _stream(stream)))
 
 
-def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, means2d, conics, opacities, colors,
-                     background, settings, final_T, last_idx, dL_dimage, dL_dmeans2d,
-                     dL_dconics, dL_dopacities, dL_dcolors, accumulate=0, counters=None,
-                     stream=None):
+def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, splats, offsets, tiles_touched,
+                     num_instances, background, settings, final_T, last_idx, dL_dimage, partials,
+                     partials_capacity, grads2d, counters=None, stream=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(means2d),
-                                _p(conics), _p(opacities), _p(colors), bg, C.byref(settings),
-                                _p(final_T), _p(last_idx), _p(dL_dimage), _p(dL_dmeans2d),
-                                _p(dL_dconics), _p(dL_dopacities), _p(dL_dcolors),
-                                int(accumulate), _p(counters), _stream(stream)))
+    _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+                                _p(offsets), _p(tiles_touched), int(num_instances), bg,
+                                C.byref(settings), _p(final_T), _p(last_idx), _p(dL_dimage),
+                                _p(partials), int(partials_capacity), _p(grads2d), _p(counters),
+                                _stream(stream)))
 
 
-def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii,
-                   dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans, dL_dscales, dL_dquats,
-                   dL_dsh, accumulate=0, stream=None):
+def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii, grads2d,
+                   dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, accumulate=0,
+                   stream=None):
     lib = load()
     _check(lib.gs_project_bwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
-                              C.byref(cam), C.byref(settings), _p(radii), _p(dL_dmeans2d),
-                              _p(dL_dconics), _p(dL_dcolors), _p(dL_dmeans), _p(dL_dscales),
-                              _p(dL_dquats), _p(dL_dsh), int(accumulate), _stream(stream)))
+                              C.byref(cam), C.byref(settings), _p(radii), _p(grads2d),
+                              _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
+                              _p(dL_dsh), int(accumulate), _stream(stream)))
 
 
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
@@ -270,8 +269,10 @@ class Frame:
         self.last_idx = z((height, width), u32)
         self.out_depth = z((height, width), f32) if with_depth_alpha else None
         self.out_alpha = z((height, width), f32) if with_depth_alpha else None
-        self.g_means2d, self.g_conics = z((2, ld), f32), z((3, ld), f32)
-        self.g_opacities, self.g_colors = z((ld,), f32), z((3, ld), f32)
+        # 64-byte records (torch allocations are 256-byte aligned)
+        self.splats = z((max(ld, 1), 16), f32)
+        self.grads2d = z((max(ld, 1), 16), f32)
+        self.g_opacities = z((ld,), f32)
         self.g_means, self.g_scales = z((3, ld), f32), z((3, ld), f32)
         self.g_quats, self.g_sh = z((4, ld), f32), z((3 * self.K, ld), f32)
         self.dL_dimage = z((height, width, 3), f32)
@@ -284,6 +285,8 @@ class Frame:
         self.capacity = int(capacity)
         self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
         self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
+        # per-instance 64-byte gradient slots of the compositing backward
+        self.partials = torch.empty((self.capacity, 16), dtype=torch.float32, device=self.device)
         self.ws_bytes = gs_bin_and_sort_workspace_size(self.ld, self.capacity, self.W, self.H)
         self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8, device=self.device)
         # 256-byte alignment of the workspace start
@@ -291,10 +294,10 @@ class Frame:
         self.ws = self.workspace[off:off + self.ws_bytes]
 
     def project(self, g: Gaussians, cam):
-        self.cam = make_camera(cam)
-        gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
-                       self.settings, self.means2d, self.conics, self.depths, self.radii,
-                       self.colors, self.tiles)
+        self.cam = cam if isinstance(cam, gs_camera) else make_camera(cam)
+        gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.opacities, g.sh,
+                       self.cam, self.settings, self.means2d, self.conics, self.depths,
+                       self.radii, self.colors, self.tiles, self.splats)
 
     def bin_and_sort(self, g: Gaussians):
         st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
@@ -309,11 +312,10 @@ class Frame:
         self.M = M
         return M
 
-    def rasterize(self, g: Gaussians):
-        gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.means2d,
-                         self.conics, g.opacities, self.colors, self.depths, self.background,
-                         self.settings, self.image, self.final_T, self.last_idx, self.out_depth,
-                         self.out_alpha)
+    def rasterize(self, g: Gaussians, counters=None):
+        gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
+                         self.depths, self.background, self.settings, self.image, self.final_T,
+                         self.last_idx, self.out_depth, self.out_alpha, counters)
 
     def forward(self, g: Gaussians, cam):
         self.project(g, cam)
@@ -321,16 +323,22 @@ class Frame:
         self.rasterize(g)
         return self.image
 
-    def loss_grad(self, target, kind):
+    def loss_grad(self, target, kind, with_loss=True):
         gs_image_loss_grad(kind, self.W * self.H * 3, self.image, target, self.dL_dimage,
-                           self.loss)
+                           self.loss if with_loss else None)
+
+    def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None):
+        dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
+                         self.offsets, self.tiles, self.M, self.background, self.settings,
+                         self.final_T, self.last_idx, dl, self.partials, self.capacity,
+                         self.grads2d, counters)
+
+    def project_backward(self, g: Gaussians, accumulate=0):
+        gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
+                       self.settings, self.radii, self.grads2d, self.g_means, self.g_scales,
+                       self.g_quats, self.g_opacities, self.g_sh, accumulate)
 
     def backward(self, g: Gaussians, dL_dimage=None, accumulate=0):
-        dl = self.dL_dimage if dL_dimage is None else dL_dimage
-        gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.means2d,
-                         self.conics, g.opacities, self.colors, self.background, self.settings,
-                         self.final_T, self.last_idx, dl, self.g_means2d, self.g_conics,
-                         self.g_opacities, self.g_colors, accumulate)
-        gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
-                       self.settings, self.radii, self.g_means2d, self.g_conics, self.g_colors,
-                       self.g_means, self.g_scales, self.g_quats, self.g_sh, accumulate)
+        self.rasterize_backward(g, dL_dimage)
+        self.project_backward(g, accumulate)

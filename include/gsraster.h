@@ -29,6 +29,22 @@
  *     (Opacity = sigmoid(logit), scale = exp(log-scale) and the quaternion's
  *     w-first order are those of the gsplat guide §3.3; the activations stay
  *     with the caller, so gradients are with respect to activated values.)
+ *   - Between stages, projected Gaussians and their 2D gradients travel as
+ *     64-byte records, one per Gaussian ([ld][16] floats, record i at
+ *     X + 16*i, 64-byte aligned): a tile instance then costs one cache line
+ *     to stage and one line of atomics in the backward.
+ *       splat record (gs_project_fwd -> compositing), visible Gaussians only:
+ *         [0] u  [1] v  [2..4] qa, qb, qc  [5] opacity  [6..8] colour r,g,b
+ *         [9] radius (int32 bits)  [10] ex  [11] ey  [12..14] conic A, B, C
+ *         [15] 0
+ *       with (qa, qb, qc) = (-A/2, -B, -C/2) * log2(e), so that the Gaussian
+ *       at pixel offset (dx, dy) is exp2(qa dx^2 + qb dx dy + qc dy^2), and
+ *       (ex, ey) padded half-extents of the footprint where alpha can reach
+ *       alpha_min (negative: never; +inf: not bounded);
+ *       2D gradient record (gs_rasterize_bwd -> gs_project_bwd), and the
+ *       same layout per tile instance in its workspace:
+ *         [0] dL/du [1] dL/dv [2..4] dL/dA, dL/dB, dL/dC [5] dL/dopacity
+ *         [6..8] dL/dcolour r,g,b  [9..11] 0.
  *   - Images are row-major [H][W] (colour [H][W][3]); pixel (px,py) has its
  *     centre at (px+0.5, py+0.5); tiles are 16x16, T = ceil(W/16)*ceil(H/16),
  *     tile id = ty*ceil(W/16) + tx.
@@ -102,15 +118,18 @@ GS_API int32_t gs_num_tiles(int32_t width, int32_t height);
  * tiles the square [u-r,u+r]x[v-r,v+r] touches; SH colour.
  * Outputs ([p][ld] planes): means2d [2][ld] (u,v), conics [3][ld] (A,B,C of
  * q = A dx^2 + 2B dx dy + C dy^2), depths [ld] (camera z), radii [ld],
- * colors [3][ld], tiles_touched [ld].  Culled Gaussians get radius 0,
- * tiles 0 and zeros elsewhere.  The geometric outputs are computed in IEEE
- * fp32 in a fixed operation order without contraction, so they are
- * reproducible bit for bit. */
+ * colors [3][ld], tiles_touched [ld], and the splat record [ld][16] of
+ * every visible Gaussian (opacities [ld] is read for it).  Culled Gaussians
+ * get radius 0, tiles 0 and zeros in the planes; their records are not
+ * written.  The geometric outputs are computed in IEEE fp32 in a fixed
+ * operation order without contraction, so they are reproducible bit for
+ * bit. */
 GS_API gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree,
                          const float* means, const float* scales, const float* quats,
-                         const float* sh, const gs_camera* cam, const gs_settings* settings,
-                         float* means2d, float* conics, float* depths, int32_t* radii,
-                         float* colors, uint32_t* tiles_touched, void* stream);
+                         const float* opacities, const float* sh, const gs_camera* cam,
+                         const gs_settings* settings, float* means2d, float* conics,
+                         float* depths, int32_t* radii, float* colors,
+                         uint32_t* tiles_touched, float* splats, void* stream);
 
 /* Workspace needed by gs_bin_and_sort for N Gaussians and up to `capacity`
  * tile instances on a width x height image. */
@@ -144,54 +163,55 @@ GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, co
  * Outputs: image [H][W][3] = C + T bg; final_T [H][W]; last_idx [H][W] =
  * number of the tile's list entries up to and including the last blended one
  * (0 if none); out_depth [H][W] = sum alpha T depth and out_alpha [H][W] =
- * 1 - T when non-NULL.  background: HOST float[3].
+ * 1 - T when non-NULL (out_depth needs depths [ld]; otherwise depths may be
+ * NULL).  background: HOST float[3].
  * counters: NULL, or device uint64[4] that the call adds work counts to:
  * [0] pixel-splat pairs evaluated by the kernel, [1] pairs blended, [2] pairs
  * the plain method evaluates (per pixel, its tile's entries up to the one
  * that stops it), [3] unused.  Counting uses a separate kernel variant. */
 GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
-                           const float* means2d, const float* conics, const float* opacities,
-                           const float* colors, const float* depths, const float* background,
+                           const float* splats, const float* depths, const float* background,
                            const gs_settings* settings, float* image, float* final_T,
                            uint32_t* last_idx, float* out_depth, float* out_alpha,
                            uint64_t* counters, void* stream);
 
 /* Stage 5a — compositing backward (gsplat guide §2.2).  Walks each pixel's
  * blended list back to front from last_idx, recovering T by division and
- * accumulating the colour behind, and adds per-Gaussian gradients of the
- * loss with respect to means2d [2][ld], conics [3][ld] (A, B, C as scalars of
- * q), opacities [ld] and colors [3][ld], given dL_dimage [H][W][3].  Pairs
- * whose alpha was clamped at alpha_max carry no opacity/conic/mean gradient.
- * The 2D gradients (means2d, conics, colors) belong to this camera and are
- * always recomputed (zero-filled, then added to); dL_dopacities is a
- * parameter gradient: accumulate = 0 zero-fills it first, accumulate = 1 adds
- * to its contents (summing cameras; pair with gs_project_bwd(accumulate = 1)).
- * Additions use fp32 atomics, so the low bits vary between runs.  counters: NULL, or device uint64[4]: [0] pairs
- * evaluated, [1] pairs with a gradient, [3] wavefront reductions executed. */
+ * accumulating the colour behind, and sums per Gaussian the gradients of the
+ * loss with respect to u, v, the conic (A, B, C as scalars of
+ * q = A dx^2 + 2B dx dy + C dy^2), opacity and colour, given dL_dimage
+ * [H][W][3].  Each tile writes its nine sums for each of its Gaussians with a
+ * plain store into that instance's slot of partials (offsets[i] + k for the
+ * k-th tile, row-major, of Gaussian i's rect; partials [capacity][16],
+ * capacity >= num_instances of gs_bin_and_sort); a segmented reduction then
+ * adds each Gaussian's slots, in slot order, into its record of grads2d
+ * [ld][16] (visible Gaussians only).  There are no atomics, so the result is
+ * bit-for-bit reproducible.  Pairs whose alpha was clamped at alpha_max carry
+ * no opacity/conic/mean gradient.  counters: NULL, or device uint64[4]:
+ * [0] pairs evaluated, [1] pairs with a gradient, [3] wavefront reductions. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
-                           const float* means2d, const float* conics, const float* opacities,
-                           const float* colors, const float* background,
-                           const gs_settings* settings, const float* final_T,
-                           const uint32_t* last_idx, const float* dL_dimage,
-                           float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
-                           float* dL_dcolors, int32_t accumulate, uint64_t* counters,
+                           const float* splats, const uint32_t* offsets,
+                           const uint32_t* tiles_touched, uint64_t num_instances,
+                           const float* background, const gs_settings* settings,
+                           const float* final_T, const uint32_t* last_idx,
+                           const float* dL_dimage, float* partials,
+                           uint64_t partials_capacity, float* grads2d, uint64_t* counters,
                            void* stream);
 
-/* Stage 5b — projection backward: chain rule from (u, v), the conic and the
- * colour to means [3][ld], scales [3][ld], quats [4][ld] (through the
- * normalisation) and sh [K*3][ld].  Visibility comes from radii (the forward's
- * decisions are kept: the fov clamp and the colour clamp are re-evaluated
- * from the same fp32 inputs).  accumulate = 0 overwrites (zeros for culled
- * Gaussians); 1 adds (summing cameras). */
+/* Stage 5b — projection backward: chain rule from the 2D gradient records
+ * grads2d [ld][16] to means [3][ld], scales [3][ld], quats [4][ld] (through
+ * the normalisation), opacities [ld] and sh [K*3][ld].  Visibility comes from
+ * radii (the forward's decisions are kept: the fov clamp and the colour clamp
+ * are re-evaluated from the same fp32 inputs).  accumulate = 0 overwrites
+ * (zeros for culled Gaussians); 1 adds, which sums cameras. */
 GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
                          const float* scales, const float* quats, const float* sh,
                          const gs_camera* cam, const gs_settings* settings,
-                         const int32_t* radii, const float* dL_dmeans2d,
-                         const float* dL_dconics, const float* dL_dcolors, float* dL_dmeans,
-                         float* dL_dscales, float* dL_dquats, float* dL_dsh,
-                         int32_t accumulate, void* stream);
+                         const int32_t* radii, const float* grads2d, float* dL_dmeans,
+                         float* dL_dscales, float* dL_dquats, float* dL_dopacities,
+                         float* dL_dsh, int32_t accumulate, void* stream);
 
 /* Loss gradient of a rendered image against a target, both [count] floats:
  * kind 0 = L2 (sum (x-y)^2, gradient 2(x-y)), kind 1 = L1 (sum |x-y|,

@@ -75,10 +75,14 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
         out.update(depth=fr.out_depth.cpu().numpy(), alpha=fr.out_alpha.cpu().numpy())
     if backward:
         K = (scene.sh_degree + 1) ** 2
+        rec = fr.grads2d[:N].cpu().numpy()
+        vis = out["radii"] > 0
+        rec[~vis] = 0.0  # records of culled Gaussians are not written
         out.update(dL_dimage=fr.dL_dimage.cpu().numpy() if dL_dimage is None else dL_dimage,
                    loss=float(fr.loss.cpu().numpy()[0]),
-                   g_means2d=T(fr.g_means2d), g_conics=T(fr.g_conics),
-                   g_opacities=T(fr.g_opacities), g_colors=T(fr.g_colors),
+                   g_means2d=rec[:, 0:2].copy(), g_conics=rec[:, 2:5].copy(),
+                   g_opac2d=rec[:, 5].copy(), g_colors=rec[:, 6:9].copy(),
+                   g_opacities=T(fr.g_opacities),
                    g_means=T(fr.g_means), g_scales=T(fr.g_scales), g_quats=T(fr.g_quats),
                    g_sh=T(fr.g_sh).reshape(N, K, 3))
     out["frame"] = fr

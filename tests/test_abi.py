@@ -77,8 +77,8 @@ def _call_project(lib, N=4, ld=4, deg=0, cam=None, st=None, null_means=False):
     cam = cam if cam is not None else _cam()
     st = st if st is not None else raster.default_settings()
     return lib.gs_project_fwd(N, ld, deg, None if null_means else dummy, dummy, dummy, dummy,
-                              C.byref(cam), C.byref(st), dummy, dummy, dummy, dummy, dummy,
-                              dummy, None)
+                              dummy, C.byref(cam), C.byref(st), dummy, dummy, dummy, dummy, dummy,
+                              dummy, C.c_void_p(64), None)
 
 
 @pytest.mark.parametrize("kw", [dict(N=-1), dict(N=5, ld=4), dict(deg=4), dict(deg=-1),
@@ -119,21 +119,33 @@ def test_bin_and_sort_rejects_bad_arguments(lib):
 
 
 def test_raster_and_loss_reject_bad_arguments(lib):
-    dummy = C.c_void_p(16)
+    dummy = C.c_void_p(64)
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, dummy, dummy, dummy, dummy, dummy, dummy, bg,
-                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, dummy, None, bg,
-                             C.byref(st), dummy, dummy, dummy, dummy, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # depth output without depths
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, dummy, dummy, dummy, dummy, bg,
-                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # splat arrays needed when N > 0
-    r = lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, dummy, bg,
-                             C.byref(st), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None,
-                             None)
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, dummy, dummy, None, bg, C.byref(st), dummy,
+                             dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # no tile ranges
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, C.c_void_p(68), None, bg, C.byref(st),
+                             dummy, dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # misaligned records
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, None, bg, C.byref(st), dummy,
+                             dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # ids needed when N > 0
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, dummy, None, bg, C.byref(st), dummy,
+                             dummy, dummy, dummy, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # the depth output needs depths
+
+    def bwd(offsets=dummy, M=10, cap=10, partials=dummy, grads=dummy):
+        return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, dummy, dummy, offsets, dummy, M, bg,
+                                    C.byref(st), dummy, dummy, dummy, partials, cap, grads, None,
+                                    None)
+    assert bwd(offsets=None) == raster.GS_ERR_INVALID_ARGUMENT     # offsets needed
+    assert bwd(cap=9) == raster.GS_ERR_INVALID_ARGUMENT            # slots < instances
+    assert bwd(partials=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(partials=C.c_void_p(80)) == raster.GS_ERR_INVALID_ARGUMENT  # misaligned
+    assert bwd(grads=C.c_void_p(72)) == raster.GS_ERR_INVALID_ARGUMENT
+    r = lib.gs_project_bwd(4, 4, 0, dummy, dummy, dummy, dummy, C.byref(_cam()), C.byref(st),
+                           dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # accumulate must be 0/1
     assert lib.gs_image_loss_grad(2, 10, dummy, dummy, dummy, None, None) == \
         raster.GS_ERR_INVALID_ARGUMENT

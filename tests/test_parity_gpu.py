@@ -131,7 +131,7 @@ def test_rasterize_bwd(name):
     abs_sum = ob["abs_sum"]
     reps = [compare_grad(g["g_means2d"], ob["means2d"], abs_sum[:, 0:2], ex, "means2d"),
             compare_grad(g["g_conics"], ob["conics"], abs_sum[:, 2:5], ex, "conics"),
-            compare_grad(g["g_opacities"], ob["opacities"], abs_sum[:, 5], ex, "opacities"),
+            compare_grad(g["g_opac2d"], ob["opacities"], abs_sum[:, 5], ex, "opacities"),
             compare_grad(g["g_colors"], ob["colors"], abs_sum[:, 6:9], ex, "colors")]
     for rep in reps:
         print("[parity] %s raster_bwd %s" % (name, rep))
@@ -148,8 +148,10 @@ def test_project_bwd(name):
     r = run_case(name)
     g, o, scene, cam = r["gpu"], r["iso_pbwd"], r["scene"], r["cam"]
     vis = g["radii"] > 0
-    for k in ("means", "scales", "quats", "sh"):
+    for k in ("means", "scales", "quats", "sh", "opacities"):
         assert np.all(g["g_" + k][~vis] == 0), k
+    # the opacity gradient passes through the projection backward unchanged
+    assert_bits_equal(g["g_opacities"][vis], g["g_opac2d"][vis], "opacities")
     e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
                                     scene.sh_degree, cam, g["radii"], g["g_means2d"],
                                     g["g_conics"], g["g_colors"])
@@ -187,7 +189,7 @@ def test_end_to_end_gradients(name):
     a = bw["g2"]["abs_sum"]
     reps = [compare_grad(g["g_means2d"], bw["g2"]["means2d"], a[:, 0:2], ex, "means2d"),
             compare_grad(g["g_conics"], bw["g2"]["conics"], a[:, 2:5], ex, "conics"),
-            compare_grad(g["g_opacities"], bw["g2"]["opacities"], a[:, 5], ex, "opacities"),
+            compare_grad(g["g_opac2d"], bw["g2"]["opacities"], a[:, 5], ex, "opacities"),
             compare_grad(g["g_colors"], bw["g2"]["colors"], a[:, 6:9], ex, "colors")]
     for rep in reps:
         print("[parity] %s e2e %s" % (name, rep))
