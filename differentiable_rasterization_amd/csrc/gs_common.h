@@ -16,6 +16,9 @@ namespace gs {
 constexpr int kTile = 16;
 constexpr int kTilePixels = kTile * kTile;  // 256 = one workgroup per tile
 constexpr float kLog2e = 1.4426950408889634f;
+// sqrt(log2(e) / 2): factors of the conic scaled by it give the Gaussian as
+// exp2(-(e1^2 + e2^2)).
+constexpr float kSqrtHalfLog2e = 0.8493218002880191f;
 
 // Camera and settings travel to the kernels by value.
 struct Cam {

@@ -17,6 +17,7 @@ namespace gs {
 
 struct Geom {
   float u, v, depth, a, b, c, A, B, C;
+  float L11, L21, L22;  // conic = L L^T, L lower triangular
   int32_t radius;
   int x0, x1, y0, y1;
   bool clampx, clampy;
@@ -105,11 +106,19 @@ __device__ inline bool project_geom(const float m[3], const float s[3], const fl
   const float b = c01;
   const float c = c11 + st.eps2d;
 
+  // conic = inverse of the (positive definite) dilated 2D covariance, and
+  // its Cholesky factor, with which the quadratic form is the completed
+  // square q = (L11 dx + L21 dy)^2 + (L22 dy)^2: no cancellation for
+  // needle-like splats, where the expanded form loses about u (|A| dx^2 +
+  // 2|B dx dy| + |C| dy^2) with those terms 1e4-1e5 times q
   const float det = a * c - b * b;
-  if (!(det > 0.0f) || !__builtin_isfinite(det)) return false;
+  if (!(det > 0.0f) || !__builtin_isfinite(det) || !(a > 0.0f)) return false;
   const float A = c / det;
   const float B = -(b / det);
   const float C = a / det;
+  const float L11 = sqrtf(A);
+  const float L21 = B / L11;
+  const float L22 = 1.0f / sqrtf(c);
 
   const float mid = 0.5f * (a + c);
   const float disc = mid * mid - det;
@@ -131,6 +140,7 @@ __device__ inline bool project_geom(const float m[3], const float s[3], const fl
   g.u = u; g.v = v; g.depth = tz;
   g.a = a; g.b = b; g.c = c;
   g.A = A; g.B = B; g.C = C;
+  g.L11 = L11; g.L21 = L21; g.L22 = L22;
   g.radius = radius;
   return true;
 }
@@ -290,15 +300,78 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
   float ex, ey;
   footprint(g.a, g.b, g.c, o, st.alpha_min, ex, ey);
   float4* rec = splats + 4 * i;
-  rec[0] = make_float4(g.u, g.v, (-0.5f * kLog2e) * g.A, (-kLog2e) * g.B);
-  rec[1] = make_float4((-0.5f * kLog2e) * g.C, o, col[0], col[1]);
+  rec[0] = make_float4(g.u, g.v, kSqrtHalfLog2e * g.L11, kSqrtHalfLog2e * g.L21);
+  rec[1] = make_float4(kSqrtHalfLog2e * g.L22, o, col[0], col[1]);
   rec[2] = make_float4(col[2], __int_as_float(g.radius), ex, ey);
   rec[3] = make_float4(g.A, g.B, g.C, 0.0f);
 }
 
-// Backward of the projection, chain rule in fp32.  The forward's geometry is
-// recomputed with the same code, so every decision (cull, fov clamp, colour
-// clamp) is the forward's.
+// Real SH basis and its gradient in fp64, for the backward (the same
+// polynomials and constants as the fp32 forward above).
+__device__ inline void sh_basis64(int deg, double x, double y, double z, double Y[16]) {
+  using namespace shc;
+  Y[0] = (double)C0;
+  if (deg < 1) return;
+  Y[1] = -(double)C1 * y;
+  Y[2] = (double)C1 * z;
+  Y[3] = -(double)C1 * x;
+  if (deg < 2) return;
+  const double xx = x * x, yy = y * y, zz = z * z;
+  Y[4] = (double)C2a * (x * y);
+  Y[5] = -(double)C2a * (y * z);
+  Y[6] = (double)C2b * (3.0 * zz - 1.0);
+  Y[7] = -(double)C2a * (x * z);
+  Y[8] = (double)C2c * (xx - yy);
+  if (deg < 3) return;
+  Y[9] = -(double)C3a * (y * (3.0 * xx - yy));
+  Y[10] = (double)C3b * (x * y * z);
+  Y[11] = -(double)C3c * (y * (5.0 * zz - 1.0));
+  Y[12] = (double)C3d * (z * (5.0 * zz - 3.0));
+  Y[13] = -(double)C3c * (x * (5.0 * zz - 1.0));
+  Y[14] = (double)C3e * (z * (xx - yy));
+  Y[15] = -(double)C3a * (x * (xx - 3.0 * yy));
+}
+
+__device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, double z,
+                                           double g[3]) {
+  using namespace shc;
+  const double xx = x * x, yy = y * y, zz = z * z;
+  double dx = 0.0, dy = 0.0, dz = 0.0;
+  switch (j) {
+    case 1: dy = -(double)C1; break;
+    case 2: dz = (double)C1; break;
+    case 3: dx = -(double)C1; break;
+    case 4: dx = (double)C2a * y; dy = (double)C2a * x; break;
+    case 5: dy = -(double)C2a * z; dz = -(double)C2a * y; break;
+    case 6: dz = 6.0 * (double)C2b * z; break;
+    case 7: dx = -(double)C2a * z; dz = -(double)C2a * x; break;
+    case 8: dx = 2.0 * (double)C2c * x; dy = -2.0 * (double)C2c * y; break;
+    case 9: dx = -(double)C3a * 6.0 * x * y; dy = -(double)C3a * (3.0 * xx - 3.0 * yy); break;
+    case 10: dx = (double)C3b * y * z; dy = (double)C3b * x * z; dz = (double)C3b * x * y; break;
+    case 11: dy = -(double)C3c * (5.0 * zz - 1.0); dz = -(double)C3c * 10.0 * y * z; break;
+    case 12: dz = (double)C3d * (15.0 * zz - 3.0); break;
+    case 13: dx = -(double)C3c * (5.0 * zz - 1.0); dz = -(double)C3c * 10.0 * x * z; break;
+    case 14:
+      dx = 2.0 * (double)C3e * x * z; dy = -2.0 * (double)C3e * y * z;
+      dz = (double)C3e * (xx - yy);
+      break;
+    case 15: dx = -(double)C3a * (3.0 * xx - 3.0 * yy); dy = (double)C3a * 6.0 * x * y; break;
+    default: break;
+  }
+  g[0] = fma(w, dx, g[0]);
+  g[1] = fma(w, dy, g[1]);
+  g[2] = fma(w, dz, g[2]);
+}
+
+// Backward of the projection: the chain rule from the 2D gradient record to
+// the mean, scale, quaternion and SH coefficients, evaluated in fp64 (inputs
+// converted exactly, each output rounded once to fp32).  The geometry is
+// recomputed in fp64 from the parameters; visibility is the forward's
+// (radius > 0), the fov and colour clamps are re-decided in fp64.  fp64
+// because the chain through a nearly singular 2D covariance (needle-like
+// splats, condition numbers 1e4-1e5) loses about u times the condition
+// number in fp32; the kernel moves ~300 bytes per Gaussian against a few
+// hundred fp64 operations, so it stays memory-bound.
 __global__ __launch_bounds__(256) void project_bwd_kernel(
     int64_t N, int64_t ld, int deg, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
@@ -309,18 +382,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
   const int K = (deg + 1) * (deg + 1);
-  float gm[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0};
-  const bool vis = radii[i] > 0;
-  Geom g;
-  float qn[5], Rq[9], Sig[6], Tm[6], tc[3];
-  const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
-  const float s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
-  bool ok = false;
-  if (vis) {
-    const float q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
-    ok = project_geom(m, s, q, cam, st, g, qn, Rq, Sig, Tm, tc);
-  }
-  if (!ok) {
+  if (!(radii[i] > 0)) {
     if (!accumulate) {
       for (int k = 0; k < 3; ++k) { o_means[(int64_t)k * ld + i] = 0.0f; o_scales[(int64_t)k * ld + i] = 0.0f; }
       for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + i] = 0.0f;
@@ -332,127 +394,177 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   const float4 r0 = grads2d[4 * i + 0], r1 = grads2d[4 * i + 1], r2 = grads2d[4 * i + 2];
   // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
   o_opac[i] = accumulate ? o_opac[i] + r1.y : r1.y;
-  const float* W = cam.R;
-  const float tx = tc[0], ty = tc[1], tz = tc[2];
-  const float fx = cam.fx, fy = cam.fy;
 
-  // conic (A,B,C) = (c, -b, a) / det  ->  gradients on (a, b, c)
-  const float a = g.a, b = g.b, c = g.c;
-  const float det = a * c - b * b;
-  const float id = 1.0f / det, id2 = id * id;
-  const float gA = r0.z, gB = r0.w, gC = r1.x;
-  const float ga = gA * (-c * c * id2) + gB * (b * c * id2) + gC * (id - a * c * id2);
-  const float gb = gA * (2.0f * b * c * id2) + gB * (-id - 2.0f * b * b * id2) + gC * (2.0f * a * b * id2);
-  const float gc = gA * (id - a * c * id2) + gB * (a * b * id2) + gC * (-a * a * id2);
+  const double m[3] = {means[i], means[ld + i], means[2 * ld + i]};
+  const double s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
+  const double q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
+  double W[9];
+  for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
+  const double fx = cam.fx, fy = cam.fy;
+  const double tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + (double)cam.t[0];
+  const double ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + (double)cam.t[1];
+  const double tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + (double)cam.t[2];
 
-  const float Sf[9] = {Sig[0], Sig[1], Sig[2], Sig[1], Sig[3], Sig[4], Sig[2], Sig[4], Sig[5]};
-  float ST0[3], ST1[3];
+  // unit quaternion, rotation, M = R diag(s), Sigma = M M^T
+  const double n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
+  const double nr = sqrt(n2);
+  const double w = q[0] / nr, x = q[1] / nr, y = q[2] / nr, z = q[3] / nr;
+  double Rq[9];
+  Rq[0] = 1.0 - 2.0 * (y * y + z * z);
+  Rq[1] = 2.0 * (x * y - w * z);
+  Rq[2] = 2.0 * (x * z + w * y);
+  Rq[3] = 2.0 * (x * y + w * z);
+  Rq[4] = 1.0 - 2.0 * (x * x + z * z);
+  Rq[5] = 2.0 * (y * z - w * x);
+  Rq[6] = 2.0 * (x * z - w * y);
+  Rq[7] = 2.0 * (y * z + w * x);
+  Rq[8] = 1.0 - 2.0 * (x * x + y * y);
+  double M[9];
+  for (int r = 0; r < 3; ++r)
+    for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
+  double Sf[9];
+  for (int r = 0; r < 3; ++r)
+    for (int j = r; j < 3; ++j) {
+      const double v = (M[r * 3] * M[j * 3] + M[r * 3 + 1] * M[j * 3 + 1]) + M[r * 3 + 2] * M[j * 3 + 2];
+      Sf[r * 3 + j] = v;
+      Sf[j * 3 + r] = v;
+    }
+
+  // EWA Jacobian with the fov clamp, T = J W, 2D covariance and conic
+  const double txz = tx / tz, tyz = ty / tz;
+  const double limx = (double)st.fov_clamp * ((0.5 * (double)cam.W) / fx);
+  const double limy = (double)st.fov_clamp * ((0.5 * (double)cam.H) / fy);
+  const bool clampx = (txz > limx) || (txz < -limx);
+  const bool clampy = (tyz > limy) || (tyz < -limy);
+  const double xc = (clampx ? (txz > 0.0 ? limx : -limx) : txz) * tz;
+  const double yc = (clampy ? (tyz > 0.0 ? limy : -limy) : tyz) * tz;
+  const double tz2 = tz * tz;
+  const double J00 = fx / tz, J02 = -((fx * xc) / tz2);
+  const double J11 = fy / tz, J12 = -((fy * yc) / tz2);
+  double Tm[6];
+  for (int j = 0; j < 3; ++j) {
+    Tm[j] = J00 * W[j] + J02 * W[6 + j];
+    Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
+  }
+  double ST0[3], ST1[3];
   for (int r = 0; r < 3; ++r) {
     ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
     ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
   }
-  // dL/dSigma (general 3x3) = ga T0^T T0 + gb T0^T T1 + gc T1^T T1
-  float gSig[9];
+  const double a = (Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2]) + (double)st.eps2d;
+  const double b = Tm[0] * ST1[0] + Tm[1] * ST1[1] + Tm[2] * ST1[2];
+  const double c = (Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2]) + (double)st.eps2d;
+  const double det = a * c - b * b;
+  const double A = c / det, B = -(b / det), C = a / det;
+
+  // conic = Sigma2D^-1: dL/dSigma2D = -conic G conic, G = [[gA, gB/2], [gB/2, gC]]
+  const double gA = r0.z, gB = r0.w, gC = r1.x;
+  const double ga = -(gA * A * A + gB * A * B + gC * B * B);
+  const double gb = -(2.0 * gA * A * B + gB * (A * C + B * B) + 2.0 * gC * B * C);
+  const double gc = -(gA * B * B + gB * B * C + gC * C * C);
+
+  // Sigma2D = T Sigma T^T: dL/dSigma = T^T G2 T, dL/dT = 2 G2 T Sigma
+  double gSig[9];
   for (int r = 0; r < 3; ++r)
     for (int k = 0; k < 3; ++k)
       gSig[r * 3 + k] = ga * Tm[r] * Tm[k] + gb * Tm[r] * Tm[3 + k] + gc * Tm[3 + r] * Tm[3 + k];
-  float gT0[3], gT1[3];
+  double gT0[3], gT1[3];
   for (int r = 0; r < 3; ++r) {
-    gT0[r] = 2.0f * ga * ST0[r] + gb * ST1[r];
-    gT1[r] = gb * ST0[r] + 2.0f * gc * ST1[r];
+    gT0[r] = 2.0 * ga * ST0[r] + gb * ST1[r];
+    gT1[r] = gb * ST0[r] + 2.0 * gc * ST1[r];
   }
-  float gJ00 = 0.0f, gJ02 = 0.0f, gJ11 = 0.0f, gJ12 = 0.0f;
+  double gJ00 = 0.0, gJ02 = 0.0, gJ11 = 0.0, gJ12 = 0.0;
   for (int j = 0; j < 3; ++j) {
     gJ00 += gT0[j] * W[j];
     gJ02 += gT0[j] * W[6 + j];
     gJ11 += gT1[j] * W[3 + j];
     gJ12 += gT1[j] * W[6 + j];
   }
-  const float itz = 1.0f / tz, itz2 = itz * itz, itz3 = itz2 * itz;
-  float gt[3] = {0.0f, 0.0f, 0.0f};
+  const double itz = 1.0 / tz, itz2 = itz * itz, itz3 = itz2 * itz;
+  double gt[3] = {0.0, 0.0, 0.0};
   gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
-  const float limx = st.fov_clamp * ((0.5f * (float)cam.W) / fx);
-  const float limy = st.fov_clamp * ((0.5f * (float)cam.H) / fy);
-  if (g.clampx) {
-    const float cl = tx / tz > 0.0f ? limx : -limx;
-    gt[2] += gJ02 * (fx * cl * itz2);
+  if (clampx) {
+    gt[2] += gJ02 * (fx * (txz > 0.0 ? limx : -limx) * itz2);
   } else {
     gt[0] += gJ02 * (-fx * itz2);
-    gt[2] += gJ02 * (2.0f * fx * tx * itz3);
+    gt[2] += gJ02 * (2.0 * fx * tx * itz3);
   }
-  if (g.clampy) {
-    const float cl = ty / tz > 0.0f ? limy : -limy;
-    gt[2] += gJ12 * (fy * cl * itz2);
+  if (clampy) {
+    gt[2] += gJ12 * (fy * (tyz > 0.0 ? limy : -limy) * itz2);
   } else {
     gt[1] += gJ12 * (-fy * itz2);
-    gt[2] += gJ12 * (2.0f * fy * ty * itz3);
+    gt[2] += gJ12 * (2.0 * fy * ty * itz3);
   }
-  const float gu = r0.x, gv = r0.y;
+  const double gu = r0.x, gv = r0.y;
   gt[0] += gu * fx * itz;
   gt[2] += gu * (-fx * tx * itz2);
   gt[1] += gv * fy * itz;
   gt[2] += gv * (-fy * ty * itz2);
+  double gm[3];
   for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
 
   // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M
-  float M[9];
-  for (int r = 0; r < 3; ++r)
-    for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
-  float gR[9];
+  double gs[3] = {0.0, 0.0, 0.0}, gR[9];
   for (int r = 0; r < 3; ++r)
     for (int k = 0; k < 3; ++k) {
-      float acc = 0.0f;
+      double acc = 0.0;
       for (int j = 0; j < 3; ++j) acc += (gSig[r * 3 + j] + gSig[j * 3 + r]) * M[j * 3 + k];
       gs[k] += acc * Rq[r * 3 + k];
       gR[r * 3 + k] = acc * s[k];
     }
-  const float w = qn[0], x = qn[1], y = qn[2], z = qn[3];
-  float gqn[4];
-  gqn[0] = 2.0f * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
-  gqn[1] = 2.0f * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
-           4.0f * x * (gR[4] + gR[8]);
-  gqn[2] = 2.0f * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
-           4.0f * y * (gR[0] + gR[8]);
-  gqn[3] = 2.0f * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
-           4.0f * z * (gR[0] + gR[4]);
-  const float dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
-  const float inr = 1.0f / qn[4];
-  for (int k = 0; k < 4; ++k) gq[k] = (gqn[k] - qn[k] * dot) * inr;
+  double gqn[4];
+  gqn[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
+  gqn[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
+           4.0 * x * (gR[4] + gR[8]);
+  gqn[2] = 2.0 * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
+           4.0 * y * (gR[0] + gR[8]);
+  gqn[3] = 2.0 * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
+           4.0 * z * (gR[0] + gR[4]);
+  const double dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
+  double gq[4];
+  gq[0] = (gqn[0] - w * dot) / nr;
+  gq[1] = (gqn[1] - x * dot) / nr;
+  gq[2] = (gqn[2] - y * dot) / nr;
+  gq[3] = (gqn[3] - z * dot) / nr;
 
   // colour -> SH coefficients and the view direction
-  float cc[3];
-  camera_centre(cam, cc);
-  const float dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
-  const float L = sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-  const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
-  float raw[3], Y[16];
-  sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
-  const float gin[3] = {r1.z, r1.w, r2.x};
-  float gcol[3];
-  for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0f ? 0.0f : gin[ch];
-  float gd[3] = {0.0f, 0.0f, 0.0f};
+  double cc[3];
+  for (int j = 0; j < 3; ++j)
+    cc[j] = -((W[j] * (double)cam.t[0] + W[3 + j] * (double)cam.t[1]) + W[6 + j] * (double)cam.t[2]);
+  const double dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
+  const double L = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+  const double d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
+  double Y[16];
+  sh_basis64(deg, d[0], d[1], d[2], Y);
+  double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
+  for (int j = 0; j < K; ++j)
+    for (int ch = 0; ch < 3; ++ch)
+      raw[ch] = fma(Y[j], (double)sh[(int64_t)(j * 3 + ch) * ld + i], raw[ch]);
+  const double gin[3] = {r1.z, r1.w, r2.x};
+  double gcol[3];
+  for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0 : gin[ch];
+  double gd[3] = {0.0, 0.0, 0.0};
   for (int j = 0; j < K; ++j) {
-    float wj = 0.0f;
+    double wj = 0.0;
     for (int ch = 0; ch < 3; ++ch) {
       const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
-      const float gval = Y[j] * gcol[ch];
+      const float gval = (float)(Y[j] * gcol[ch]);
       o_sh[p] = accumulate ? o_sh[p] + gval : gval;
-      wj = fmaf(gcol[ch], sh[p], wj);
+      wj = fma(gcol[ch], (double)sh[p], wj);
     }
-    if (j > 0) sh_basis_grad_acc(j, wj, d[0], d[1], d[2], gd);
+    if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
   }
-  const float dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
-  const float iL = 1.0f / L;
-  for (int e = 0; e < 3; ++e) gm[e] += (gd[e] - d[e] * dd) * iL;
+  const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+  for (int e = 0; e < 3; ++e) gm[e] += (gd[e] - d[e] * dd) / L;
 
   for (int k = 0; k < 3; ++k) {
     const int64_t p = (int64_t)k * ld + i;
-    o_means[p] = accumulate ? o_means[p] + gm[k] : gm[k];
-    o_scales[p] = accumulate ? o_scales[p] + gs[k] : gs[k];
+    o_means[p] = accumulate ? o_means[p] + (float)gm[k] : (float)gm[k];
+    o_scales[p] = accumulate ? o_scales[p] + (float)gs[k] : (float)gs[k];
   }
   for (int k = 0; k < 4; ++k) {
     const int64_t p = (int64_t)k * ld + i;
-    o_quats[p] = accumulate ? o_quats[p] + gq[k] : gq[k];
+    o_quats[p] = accumulate ? o_quats[p] + (float)gq[k] : (float)gq[k];
   }
 }
 

@@ -25,18 +25,18 @@
 // slots in a fixed order.  No global atomics: device-scope float atomics go
 // to memory on this part, and a fixed order makes gradients reproducible.
 //
-// Decisions (q < 0, alpha < alpha_min, alpha clamp, stop at T < T_min) are
+// Decisions (alpha < alpha_min, alpha clamp, stop at T < T_min) are
 // taken by the same inline code in both kernels, compiled without
 // contraction, so the backward replays exactly the forward's choices.
 #include "gs_common.h"
 
 namespace gs {
 
-// Splat staged in LDS: mean, conic pre-scaled so that exp2 of the quadratic
-// form is the Gaussian (qa = -log2e/2 A, qb = -log2e B, qc = -log2e/2 C),
-// opacity, colour, depth.
+// Splat staged in LDS: mean, the conic's Cholesky factor scaled by
+// sqrt(log2(e)/2) (l11, l21, l22: the Gaussian is exp2(-(e1^2 + e2^2)) with
+// e1 = l11 dx + l21 dy, e2 = l22 dy), opacity, colour, depth.
 struct SplatLds {
-  float u, v, qa, qb, qc, o, r, g, b, z;
+  float u, v, l11, l21, l22, o, r, g, b, z;
 };
 
 // Stage one splat record (three 16-byte loads of one 64-byte line) into LDS
@@ -44,8 +44,8 @@ struct SplatLds {
 __device__ inline void stage_splat(SplatLds& s, const float4* __restrict__ rec, int32_t& radius,
                                    float& ex, float& ey) {
   const float4 a = rec[0], b = rec[1], c = rec[2];
-  s.u = a.x; s.v = a.y; s.qa = a.z; s.qb = a.w;
-  s.qc = b.x; s.o = b.y; s.r = b.z; s.g = b.w;
+  s.u = a.x; s.v = a.y; s.l11 = a.z; s.l21 = a.w;
+  s.l22 = b.x; s.o = b.y; s.r = b.z; s.g = b.w;
   s.b = c.x; s.z = 0.0f;
   radius = __float_as_int(c.y);
   ex = c.z;
@@ -100,9 +100,12 @@ __device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[256], uint
   __syncthreads();
 }
 
-// log2 of the Gaussian at pixel offset (dx, dy): -log2e * q / 2.
+// log2 of the Gaussian at pixel offset (dx, dy): -log2e * q / 2, from the
+// completed square (never positive).
 __device__ inline float splat_power2(const SplatLds& s, float dx, float dy) {
-  return fmaf(s.qa * dx, dx, fmaf(s.qc * dy, dy, s.qb * (dx * dy)));
+  const float e1 = fmaf(s.l11, dx, s.l21 * dy);
+  const float e2 = s.l22 * dy;
+  return -fmaf(e1, e1, e2 * e2);
 }
 
 // Work counters (optional diagnostics, one atomic per workgroup):
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
       const float p2 = splat_power2(s, dx, dy);
       const float oG = s.o * __builtin_amdgcn_exp2f(p2);
       const float alpha = oG > amax ? amax : oG;
-      const bool ok = !done & !(p2 > 0.0f) & !(alpha < amin);
+      const bool ok = !done & !(alpha < amin);
       const float Tn = T * (1.0f - alpha);
       const bool low = Tn < Tmin;
       const bool blend = ok & !low;
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const float oG = s.o * G;
       const bool clamped = oG > amax;
       const float alpha = clamped ? amax : oG;
-      const bool hit = (rel < last) & !(p2 > 0.0f) & !(alpha < amin);
+      const bool hit = (rel < last) & !(alpha < amin);
       const float rom = __builtin_amdgcn_rcpf(1.0f - alpha);
       T = hit ? T * rom : T;  // transmittance in front of this splat
       const float wgt = hit ? alpha * T : 0.0f;

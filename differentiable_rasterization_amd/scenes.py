@@ -88,8 +88,9 @@ def _finish(rng, means, log_scales, degree):
 
 def identity_camera(width, height, fx, fy=None) -> Camera:
     fy = fx if fy is None else fy
-    return Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), float(fx), float(fy),
-                  width / 2.0, height / 2.0, int(width), int(height))
+    f32 = lambda x: float(np.float32(x))
+    return Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), f32(fx), f32(fy),
+                  f32(width / 2.0), f32(height / 2.0), int(width), int(height))
 
 
 def look_at_camera(eye, width, height, fx, fy=None, target=(0.0, 0.0, 0.0)) -> Camera:
@@ -104,7 +105,9 @@ def look_at_camera(eye, width, height, fx, fy=None, target=(0.0, 0.0, 0.0)) -> C
     d = np.cross(f, r)
     R = np.stack([r, d, f], axis=0)
     t = -R @ eye
-    return Camera(_f32(R), _f32(t), float(fx), float(fy), width / 2.0, height / 2.0,
+    # the library's camera is fp32: every value handed to either side is one
+    return Camera(_f32(R), _f32(t), float(np.float32(fx)), float(np.float32(fy)),
+                  float(np.float32(width / 2.0)), float(np.float32(height / 2.0)),
                   int(width), int(height))
 
 
@@ -182,6 +185,21 @@ def heavy_tail_scene(n=6_000_000, seed=5, sh_degree=3, n_clusters=512, box=24.0)
     means = clustered_means(rng, n, n_clusters, box)
     log_s = np.minimum(-3.5 + 0.5 * rng.standard_t(3, size=(n, 3)), 1.0)
     return _finish(rng, means, log_s, sh_degree)
+
+
+def densify_prune(scene, grad_norm, clone_frac=0.02, min_opacity=0.005):
+    """The count-changing step between iterations of the 6M-Gaussian workload
+    (a harness operation, not part of the rasterizer): exact copies of the
+    ``clone_frac`` Gaussians with the largest ``grad_norm`` (ties by lower
+    index) are appended in index order, then every Gaussian with opacity
+    below ``min_opacity`` is removed.  The criterion follows the densify /
+    prune of the gsplat guide (lmnt.cn/news/262699) §4.1 (gradient threshold,
+    minimum opacity 0.005)."""
+    n_clone = int(round(clone_frac * scene.n))
+    order = np.argsort(-np.asarray(grad_norm, np.float64), kind="stable")
+    idx = np.concatenate([np.arange(scene.n), np.sort(order[:n_clone])])
+    keep = scene.opacities[idx] >= np.float32(min_opacity)
+    return scene.subset(idx[keep])
 
 
 def focal_for(width):

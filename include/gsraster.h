@@ -5,10 +5,12 @@
  * The five stages follow the pipeline the gsplat guide (lmnt.cn/news/262699)
  * describes in §2.1 — transform each Gaussian by (R, t, scale, rotation),
  * project it to depth and screen space, then alpha-blend it differentiably —
- * with the blending backward callable on its own (gsplat guide §2.2) and
- * accumulating per-Gaussian gradients with atomics (3DGS deployment guide
+ * with the blending backward callable on its own (gsplat guide §2.2).  The
+ * pages sum per-Gaussian gradients with atomics (3DGS deployment guide
  * (hmyw.cn/news/140031) §2.1; Moore Threads MUSA article
- * (qwbw.cn/news/278220) §2.1).  The primitive is a position, a covariance
+ * (qwbw.cn/news/278220) §2.1); here every tile instance gets its own
+ * gradient slot instead, added up in a fixed order, so the backward is
+ * deterministic.  The primitive is a position, a covariance
  * built from scale and rotation (MUSA article §3.3), an opacity and SH colour
  * coefficients (deployment guide §1).  Formulas below the stage level are the
  * textbook EWA-splatting reading; the pages print none.
@@ -32,17 +34,21 @@
  *   - Between stages, projected Gaussians and their 2D gradients travel as
  *     64-byte records, one per Gaussian ([ld][16] floats, record i at
  *     X + 16*i, 64-byte aligned): a tile instance then costs one cache line
- *     to stage and one line of atomics in the backward.
+ *     to stage and one 48-byte gradient store in the backward.
  *       splat record (gs_project_fwd -> compositing), visible Gaussians only:
- *         [0] u  [1] v  [2..4] qa, qb, qc  [5] opacity  [6..8] colour r,g,b
- *         [9] radius (int32 bits)  [10] ex  [11] ey  [12..14] conic A, B, C
- *         [15] 0
- *       with (qa, qb, qc) = (-A/2, -B, -C/2) * log2(e), so that the Gaussian
- *       at pixel offset (dx, dy) is exp2(qa dx^2 + qb dx dy + qc dy^2), and
- *       (ex, ey) padded half-extents of the footprint where alpha can reach
+ *         [0] u  [1] v  [2..4] l11, l21, l22  [5] opacity  [6..8] colour
+ *         r,g,b  [9] radius (int32 bits)  [10] ex  [11] ey  [12..14] conic
+ *         A, B, C  [15] 0
+ *       with (l11, l21, l22) = sqrt(log2(e)/2) (L11, L21, L22), L the
+ *       Cholesky factor of the conic (L11 = sqrt(A), L21 = B / L11,
+ *       L22 = 1 / sqrt(c), c the dilated 2D covariance's yy entry), so that
+ *       the Gaussian at pixel offset (dx, dy) is exp2(-(e1^2 + e2^2)) with
+ *       e1 = l11 dx + l21 dy, e2 = l22 dy (the quadratic form as a completed
+ *       square, free of cancellation for needle-like splats), and (ex, ey)
+ *       padded half-extents of the footprint where alpha can reach
  *       alpha_min (negative: never; +inf: not bounded);
  *       2D gradient record (gs_rasterize_bwd -> gs_project_bwd), and the
- *       same layout per tile instance in its workspace:
+ *       same layout per tile instance in its partials buffer:
  *         [0] dL/du [1] dL/dv [2..4] dL/dA, dL/dB, dL/dC [5] dL/dopacity
  *         [6..8] dL/dcolour r,g,b  [9..11] 0.
  *   - Images are row-major [H][W] (colour [H][W][3]); pixel (px,py) has its
@@ -109,11 +115,12 @@ GS_API const char* gs_status_string(gs_status s);
 GS_API const char* gs_last_error(void);
 GS_API int32_t gs_num_tiles(int32_t width, int32_t height);
 
-/* Stage 1 — projection (gsplat guide §2.1, steps "3D transform" and "depth
- * and screen projection"; covariance from scale and rotation, MUSA article
- * §3.3).  Per Gaussian: t = R mean + t; cull outside (near, far) or
- * non-finite; Sigma = R(q) S S^T R(q)^T; 2D covariance J W Sigma W^T J^T
- * plus eps2d on the diagonal, with J the pinhole Jacobian; conic = its
+/* Stage 1 — projection (gsplat guide §2.1, its first two steps: the 3D
+ * transform, then depth and screen-space projection; covariance from scale
+ * and rotation, MUSA article §3.3).  Per Gaussian: t = R mean + t; cull
+ * outside (near, far) or non-finite; Sigma = R(q) S S^T R(q)^T; 2D covariance
+ * J W Sigma W^T J^T plus eps2d on the diagonal, with J the pinhole Jacobian
+ * (culled unless positive definite); conic = its
  * inverse; radius = ceil(3 sqrt(lambda_max)); pixel mean; number of 16x16
  * tiles the square [u-r,u+r]x[v-r,v+r] touches; SH colour.
  * Outputs ([p][ld] planes): means2d [2][ld] (u,v), conics [3][ld] (A,B,C of
@@ -156,8 +163,9 @@ GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, co
                           void* stream);
 
 /* Stage 4 — front-to-back alpha compositing per 16x16 tile (gsplat guide
- * §2.1, "differentiable alpha-blending rasterisation").  Per pixel, over its
- * tile's sorted list: q from the conic at (px+0.5-u, py+0.5-v); skip q < 0;
+ * §2.1, its third, differentiable blending step).  Per pixel, over its
+ * tile's sorted list: q, the conic's quadratic form at (px+0.5-u, py+0.5-v),
+ * evaluated as the completed square of the splat record;
  * alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop (without
  * blending) when T (1-alpha) < T_min; else C += colour alpha T, T *= 1-alpha.
  * Outputs: image [H][W][3] = C + T bg; final_T [H][W]; last_idx [H][W] =

@@ -73,7 +73,7 @@ def _load():
             build(force=False)
         lib = C.CDLL(_LIB_PATH)
         P = C.c_void_p
-        lib.orc_project.argtypes = [C.c_int, C.c_int64, C.c_int] + [P] * 15
+        lib.orc_project.argtypes = [C.c_int, C.c_int64, C.c_int] + [P] * 16
         lib.orc_project.restype = C.c_int
         lib.orc_bin_f32.argtypes = [C.c_int64, P, P, P, C.c_int32, C.c_int32, C.c_int64, P, P, P, P]
         lib.orc_bin_f32.restype = C.c_int64
@@ -81,7 +81,7 @@ def _load():
         lib.orc_bin_f64.restype = C.c_int64
         lib.orc_composite.argtypes = [C.c_int32, C.c_int32] + [P] * 15
         lib.orc_composite.restype = C.c_int
-        lib.orc_composite_bwd.argtypes = [C.c_int32, C.c_int32, C.c_int64] + [P] * 14
+        lib.orc_composite_bwd.argtypes = [C.c_int32, C.c_int32, C.c_int64] + [P] * 15
         lib.orc_composite_bwd.restype = C.c_int
         lib.orc_project_bwd.argtypes = [C.c_int64, C.c_int] + [P] * 14
         lib.orc_project_bwd.restype = C.c_int
@@ -144,15 +144,16 @@ def project(means, scales, quats, sh, sh_degree, cam, settings=None, mode=MODE_F
     N = means.shape[0]
     K = (sh_degree + 1) ** 2
     sh = _f64(sh, (N, K, 3))
-    out = dict(means2d=np.zeros((N, 2)), conics=np.zeros((N, 3)), cov2d=np.zeros((N, 3)),
+    out = dict(means2d=np.zeros((N, 2)), conics=np.zeros((N, 3)), chol=np.zeros((N, 3)),
+               cov2d=np.zeros((N, 3)),
                depths=np.zeros(N), radii=np.zeros(N, np.int32), tiles=np.zeros(N, np.uint32),
                rect=np.zeros((N, 4), np.int32), colors=np.zeros((N, 3)),
                clamped=np.zeros((N, 3), np.uint8))
     cs, ss = camera_struct(cam), settings_struct(settings)
     lib.orc_project(mode, N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
                     C.addressof(cs), C.addressof(ss),
-                    *[_ptr(out[k]) for k in ("means2d", "conics", "cov2d", "depths", "radii",
-                                             "tiles", "rect", "colors", "clamped")])
+                    *[_ptr(out[k]) for k in ("means2d", "conics", "chol", "cov2d", "depths",
+                                             "radii", "tiles", "rect", "colors", "clamped")])
     return out
 
 
@@ -189,14 +190,16 @@ def bin_f64(means2d, radii, depths, width, height):
     return dict(M=int(M), ids=ids, ranges=ranges)
 
 
-def composite(width, height, ranges, ids, means2d, conics, opacities, colors, depths,
+def composite(width, height, ranges, ids, means2d, chol, opacities, colors, depths,
               background=(0.0, 0.0, 0.0), settings=None, with_margin=False):
-    """Step 12. Returns dict(image [H,W,3], final_T, last, depth, alpha[, margin])."""
+    """Step 12, with q from the conic's Cholesky factor ``chol`` [N,3] =
+    (L11, L21, L22): q = (L11 dx + L21 dy)^2 + (L22 dy)^2.
+    Returns dict(image [H,W,3], final_T, last, depth, alpha[, margin])."""
     lib = _load()
     ranges = np.ascontiguousarray(np.asarray(ranges, dtype=np.uint32))
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.uint32))
-    m2, con, op, col, dep = (_f64(means2d, (-1, 2)), _f64(conics, (-1, 3)), _f64(opacities),
-                             _f64(colors, (-1, 3)), _f64(depths))
+    m2, ch, op, col, dep = (_f64(means2d, (-1, 2)), _f64(chol, (-1, 3)), _f64(opacities),
+                            _f64(colors, (-1, 3)), _f64(depths))
     bg = _f64(background, (3,))
     H, W = height, width
     out = dict(image=np.zeros((H, W, 3)), final_T=np.zeros((H, W)),
@@ -204,7 +207,7 @@ def composite(width, height, ranges, ids, means2d, conics, opacities, colors, de
                alpha=np.zeros((H, W)))
     margin = np.zeros((H, W)) if with_margin else None
     ss = settings_struct(settings)
-    lib.orc_composite(W, H, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(con), _ptr(op), _ptr(col),
+    lib.orc_composite(W, H, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(ch), _ptr(op), _ptr(col),
                       _ptr(dep), _ptr(bg), C.addressof(ss), _ptr(out["image"]),
                       _ptr(out["final_T"]), _ptr(out["last"]), _ptr(out["depth"]),
                       _ptr(out["alpha"]), _ptr(margin))
@@ -213,14 +216,14 @@ def composite(width, height, ranges, ids, means2d, conics, opacities, colors, de
     return out
 
 
-def composite_bwd(width, height, ranges, ids, means2d, conics, opacities, colors,
+def composite_bwd(width, height, ranges, ids, means2d, chol, conics, opacities, colors,
                   dL_dimage, background=(0.0, 0.0, 0.0), settings=None, with_abs=False):
     """Step 13a. Returns dict(means2d [N,2], conics [N,3], opacities [N], colors [N,3][, abs_sum])."""
     lib = _load()
     ranges = np.ascontiguousarray(np.asarray(ranges, dtype=np.uint32))
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.uint32))
-    m2, con, op, col = (_f64(means2d, (-1, 2)), _f64(conics, (-1, 3)), _f64(opacities),
-                        _f64(colors, (-1, 3)))
+    m2, ch, con, op, col = (_f64(means2d, (-1, 2)), _f64(chol, (-1, 3)), _f64(conics, (-1, 3)),
+                            _f64(opacities), _f64(colors, (-1, 3)))
     N = op.shape[0]
     g = _f64(dL_dimage, (height, width, 3))
     bg = _f64(background, (3,))
@@ -228,7 +231,7 @@ def composite_bwd(width, height, ranges, ids, means2d, conics, opacities, colors
                colors=np.zeros((N, 3)))
     abs_sum = np.zeros((N, 9)) if with_abs else None
     ss = settings_struct(settings)
-    lib.orc_composite_bwd(width, height, N, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(con),
+    lib.orc_composite_bwd(width, height, N, _ptr(ranges), _ptr(ids), _ptr(m2), _ptr(ch), _ptr(con),
                           _ptr(op), _ptr(col), _ptr(bg), C.addressof(ss), _ptr(g),
                           _ptr(out["means2d"]), _ptr(out["conics"]), _ptr(out["opacities"]),
                           _ptr(out["colors"]), _ptr(abs_sum))
@@ -357,7 +360,7 @@ def render(scene, cam, settings=None, background=(0.0, 0.0, 0.0), with_margin=Fa
     bins = bin_f32(proj["means2d"].astype(np.float32), proj["radii"],
                    proj["depths"].astype(np.float32), cam.width, cam.height)
     raster = composite(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
-                       proj["conics"], scene.opacities, proj["colors"], proj["depths"],
+                       proj["chol"], scene.opacities, proj["colors"], proj["depths"],
                        background, settings, with_margin)
     return dict(proj=proj, bins=bins, raster=raster)
 
@@ -373,8 +376,8 @@ def backward(scene, cam, fwd, dL_dimage, settings=None, background=(0.0, 0.0, 0.
     """Step 13 for a forward produced by :func:`render` (or the fp64 path)."""
     proj, bins = fwd["proj"], fwd["bins"]
     g2 = composite_bwd(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
-                       proj["conics"], scene.opacities, proj["colors"], dL_dimage, background,
-                       settings, with_abs)
+                       proj["chol"], proj["conics"], scene.opacities, proj["colors"], dL_dimage,
+                       background, settings, with_abs)
     g3 = project_bwd(scene.means, scene.scales, scene.quats, scene.sh, scene.sh_degree, cam,
                      proj["radii"], g2["means2d"], g2["conics"], g2["colors"], settings)
     return dict(g2=g2, g3=g3)
@@ -386,6 +389,6 @@ def render_f64(scene, cam, settings=None, background=(0.0, 0.0, 0.0)):
                    settings, MODE_F64)
     bins = bin_f64(proj["means2d"], proj["radii"], proj["depths"], cam.width, cam.height)
     raster = composite(cam.width, cam.height, bins["ranges"], bins["ids"], proj["means2d"],
-                       proj["conics"], scene.opacities, proj["colors"], proj["depths"],
+                       proj["chol"], scene.opacities, proj["colors"], proj["depths"],
                        background, settings)
     return dict(proj=proj, bins=bins, raster=raster)

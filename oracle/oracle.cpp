@@ -315,6 +315,7 @@ template <class T> struct Geom {
   T u = T(0), v = T(0), depth = T(0);
   T a = T(0), b = T(0), c = T(0);     /* dilated 2D covariance */
   T A = T(0), B = T(0), C = T(0);     /* conic */
+  T L11 = T(0), L21 = T(0), L22 = T(0); /* conic = L L^T, L lower triangular */
   int32_t radius = 0;
   int32_t rect[4] = {0, 0, 0, 0};     /* x0, x1, y0, y1 (exclusive ends) */
   uint32_t ntiles = 0;
@@ -382,12 +383,19 @@ Geom<T> project_geom(const T mean[3], const T scale[3], const T quat[4],
   T b = c01;
   T c = c11 + T(st.eps2d);
 
-  /* 4. conic = inverse of the dilated 2D covariance */
+  /* 4. conic = inverse of the dilated 2D covariance (which must be positive
+   *    definite), and its Cholesky factor L (conic = L L^T), with which the
+   *    quadratic form is the completed square
+   *      q = (L11 dx + L21 dy)^2 + (L22 dy)^2,
+   *    L11 = sqrt(A), L21 = B / L11, L22 = 1 / sqrt(c). */
   T det = a * c - b * b;
-  if (!(det > T(0)) || !s_finite(det)) return g;
+  if (!(det > T(0)) || !s_finite(det) || !(a > T(0))) return g;
   T A = c / det;
   T B = -(b / det);
   T C = a / det;
+  T L11 = s_sqrt(A);
+  T L21 = B / L11;
+  T L22 = T(1) / s_sqrt(c);
 
   /* 5. radius = ceil(3 sqrt(lambda_max)) */
   T mid = T(0.5f) * (a + c);
@@ -422,6 +430,7 @@ Geom<T> project_geom(const T mean[3], const T scale[3], const T quat[4],
   g.u = u; g.v = v; g.depth = tz;
   g.a = a; g.b = b; g.c = c;
   g.A = A; g.B = B; g.C = C;
+  g.L11 = L11; g.L21 = L21; g.L22 = L22;
   g.radius = radius;
   g.rect[0] = x0; g.rect[1] = x1; g.rect[2] = y0; g.rect[3] = y1;
   g.ntiles = (uint32_t)(x1 - x0) * (uint32_t)(y1 - y0);
@@ -501,7 +510,7 @@ void fill_ranges(const std::vector<Inst>& inst, int T, uint32_t* ranges) {
 /* ------------------------------------------------------------------------ */
 /* Step 12: per-pixel front-to-back compositing.                            */
 /* ------------------------------------------------------------------------ */
-enum PairOutcome : uint8_t { SKIP_Q = 1, SKIP_ALPHA = 2, STOP = 3, BLEND = 4, BLEND_CLAMPED = 5 };
+enum PairOutcome : uint8_t { SKIP_ALPHA = 2, STOP = 3, BLEND = 4, BLEND_CLAMPED = 5 };
 
 struct Layer { /* one blended entry of a pixel (fp64 backward) */
   uint32_t pos; /* position in the sorted list */
@@ -529,7 +538,7 @@ inline double rel_dist(double x, double th) { return std::fabs(x - th) / std::fa
  * layers (for the backward). */
 template <class T>
 PixelOut<T> composite_pixel(int px, int py, uint32_t start, uint32_t end,
-                            const uint32_t* ids, const T* means2d, const T* conics,
+                            const uint32_t* ids, const T* means2d, const T* chol,
                             const T* opac, const T* colors, const T* depths,
                             const double* bg, const orc_settings& st,
                             std::vector<Layer>* layers) {
@@ -546,12 +555,10 @@ PixelOut<T> composite_pixel(int px, int py, uint32_t start, uint32_t end,
     uint32_t i = ids[j];
     T dx = T(pcx) - means2d[2 * i + 0];
     T dy = T(pcy) - means2d[2 * i + 1];
-    T q = conics[3 * i + 0] * dx * dx + T(2) * conics[3 * i + 1] * dx * dy +
-          conics[3 * i + 2] * dy * dy;
-    if (q < T(0)) {
-      sig = mix(sig, (uint64_t)(j - start) * 8 + SKIP_Q);
-      continue;
-    }
+    /* q = [dx dy] conic [dx dy]^T as the completed square (never negative) */
+    T e1 = chol[3 * i + 0] * dx + chol[3 * i + 1] * dy;
+    T e2 = chol[3 * i + 2] * dy;
+    T q = e1 * e1 + e2 * e2;
     T G = s_exp(T(-0.5) * q);
     T oG = opac[i] * G;
     bool clamped = oG > T(a_max);
@@ -587,7 +594,7 @@ PixelOut<T> composite_pixel(int px, int py, uint32_t start, uint32_t end,
 
 template <class T>
 uint64_t composite_image(int W, int H, const uint32_t* ranges, const uint32_t* ids,
-                         const T* means2d, const T* conics, const T* opac,
+                         const T* means2d, const T* chol, const T* opac,
                          const T* colors, const T* depths, const double* bg,
                          const orc_settings& st, T* image, T* finalT, uint32_t* last,
                          T* out_depth, T* out_alpha, double* margin) {
@@ -600,7 +607,7 @@ uint64_t composite_image(int W, int H, const uint32_t* ranges, const uint32_t* i
     for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
       for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
         PixelOut<T> o = composite_pixel<T>(px, py, ranges[2 * t], ranges[2 * t + 1], ids,
-                                           means2d, conics, opac, colors, depths, bg, st,
+                                           means2d, chol, opac, colors, depths, bg, st,
                                            nullptr);
         size_t p = (size_t)py * W + px;
         if (image)
@@ -626,7 +633,7 @@ uint64_t composite_image(int W, int H, const uint32_t* ranges, const uint32_t* i
 /* with R_{k+1} = sum_{j>k} c_j a_j T_j + T_{n+1} bg.                        */
 /* ------------------------------------------------------------------------ */
 void composite_bwd_impl(int W, int H, int64_t N, const uint32_t* ranges,
-                        const uint32_t* ids, const double* means2d,
+                        const uint32_t* ids, const double* means2d, const double* chol,
                         const double* conics, const double* opac,
                         const double* colors, const double* bg,
                         const orc_settings& st, const double* dLdI,
@@ -647,7 +654,7 @@ void composite_bwd_impl(int W, int H, int64_t N, const uint32_t* ranges,
     for (int py = ty * kTile; py < std::min(H, (ty + 1) * kTile); ++py)
       for (int px = tx * kTile; px < std::min(W, (tx + 1) * kTile); ++px) {
         layers.clear();
-        PixelOut<double> o = composite_pixel<double>(px, py, start, end, ids, means2d, conics,
+        PixelOut<double> o = composite_pixel<double>(px, py, start, end, ids, means2d, chol,
                                                      opac, colors, colors /*unused*/, bg, st,
                                                      &layers);
         size_t p = (size_t)py * W + px;
@@ -874,7 +881,7 @@ int64_t full_loss(int64_t N, int deg, const std::vector<T>& means, const std::ve
   Cam<T> cam = cam_as<T>(camd);
   T campos[3];
   camera_center(cam, campos);
-  std::vector<T> m2(2 * N), con(3 * N), col(3 * N), dep(N);
+  std::vector<T> m2(2 * N), chol(3 * N), col(3 * N), dep(N);
   std::vector<int32_t> rects(4 * N);
   std::vector<uint8_t> vis(N);
   std::vector<double> depd(N);
@@ -887,7 +894,7 @@ int64_t full_loss(int64_t N, int deg, const std::vector<T>& means, const std::ve
                          : 0);
     for (int q = 0; q < 4; ++q) rects[4 * i + q] = g.rect[q];
     m2[2 * i] = g.u; m2[2 * i + 1] = g.v;
-    con[3 * i] = g.A; con[3 * i + 1] = g.B; con[3 * i + 2] = g.C;
+    chol[3 * i] = g.L11; chol[3 * i + 1] = g.L21; chol[3 * i + 2] = g.L22;
     dep[i] = g.depth;
     depd[i] = val(g.depth);
     if (g.vis) {
@@ -904,7 +911,7 @@ int64_t full_loss(int64_t N, int deg, const std::vector<T>& means, const std::ve
   fill_ranges(inst, NT, ranges.data());
   for (size_t m = 0; m < inst.size(); ++m) sig = mix(sig, inst[m].id);
   std::vector<T> img(3 * (size_t)W * H);
-  uint64_t csig = composite_image<T>(W, H, ranges.data(), ids.data(), m2.data(), con.data(),
+  uint64_t csig = composite_image<T>(W, H, ranges.data(), ids.data(), m2.data(), chol.data(),
                                      opac.data(), col.data(), dep.data(), bg, st, img.data(),
                                      nullptr, nullptr, nullptr, nullptr, nullptr);
   sig = mix(sig, csig);
@@ -932,9 +939,9 @@ extern "C" {
 
 int orc_project(int mode, int64_t N, int deg, const double* means, const double* scales,
                 const double* quats, const double* sh, const orc_camera* camd,
-                const orc_settings* st, double* means2d, double* conics, double* cov2d,
-                double* depths, int32_t* radii, uint32_t* tiles, int32_t* rect,
-                double* colors, uint8_t* clamped) {
+                const orc_settings* st, double* means2d, double* conics, double* chol,
+                double* cov2d, double* depths, int32_t* radii, uint32_t* tiles,
+                int32_t* rect, double* colors, uint8_t* clamped) {
   const int K = (deg + 1) * (deg + 1);
   Cam<double> camD = cam_as<double>(*camd);
   Cam<float> camF = cam_as<float>(*camd);
@@ -943,7 +950,7 @@ int orc_project(int mode, int64_t N, int deg, const double* means, const double*
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < N; ++i) {
     bool vis;
-    double u, v, dep, a, b, c, A, B, C;
+    double u, v, dep, a, b, c, A, B, C, L11, L21, L22;
     int32_t rad, rc[4];
     uint32_t nt;
     if (mode == ORC_MODE_F32KEY) {
@@ -953,11 +960,13 @@ int orc_project(int mode, int64_t N, int deg, const double* means, const double*
       Geom<float> g = project_geom<float>(mf, sf, qf, camF, *st);
       vis = g.vis; u = g.u; v = g.v; dep = g.depth; a = g.a; b = g.b; c = g.c;
       A = g.A; B = g.B; C = g.C; rad = g.radius; nt = g.ntiles;
+      L11 = g.L11; L21 = g.L21; L22 = g.L22;
       for (int k = 0; k < 4; ++k) rc[k] = g.rect[k];
     } else {
       Geom<double> g = project_geom<double>(&means[3 * i], &scales[3 * i], &quats[4 * i], camD, *st);
       vis = g.vis; u = g.u; v = g.v; dep = g.depth; a = g.a; b = g.b; c = g.c;
       A = g.A; B = g.B; C = g.C; rad = g.radius; nt = g.ntiles;
+      L11 = g.L11; L21 = g.L21; L22 = g.L22;
       for (int k = 0; k < 4; ++k) rc[k] = g.rect[k];
     }
     double col[3] = {0, 0, 0};
@@ -972,6 +981,7 @@ int orc_project(int mode, int64_t N, int deg, const double* means, const double*
     }
     if (means2d) { means2d[2 * i] = u; means2d[2 * i + 1] = v; }
     if (conics) { conics[3 * i] = A; conics[3 * i + 1] = B; conics[3 * i + 2] = C; }
+    if (chol) { chol[3 * i] = L11; chol[3 * i + 1] = L21; chol[3 * i + 2] = L22; }
     if (cov2d) { cov2d[3 * i] = a; cov2d[3 * i + 1] = b; cov2d[3 * i + 2] = c; }
     if (depths) depths[i] = dep;
     if (radii) radii[i] = rad;
@@ -1049,22 +1059,22 @@ int64_t orc_bin_f64(int64_t N, const double* means2d, const int32_t* radii, cons
 }
 
 int orc_composite(int32_t W, int32_t H, const uint32_t* ranges, const uint32_t* ids,
-                  const double* means2d, const double* conics, const double* opacities,
+                  const double* means2d, const double* chol, const double* opacities,
                   const double* colors, const double* depths, const double* bg,
                   const orc_settings* st, double* image, double* final_T, uint32_t* last,
                   double* out_depth, double* out_alpha, double* margin) {
-  composite_image<double>(W, H, ranges, ids, means2d, conics, opacities, colors, depths, bg, *st,
+  composite_image<double>(W, H, ranges, ids, means2d, chol, opacities, colors, depths, bg, *st,
                           image, final_T, last, out_depth, out_alpha, margin);
   return 0;
 }
 
 int orc_composite_bwd(int32_t W, int32_t H, int64_t N, const uint32_t* ranges,
-                      const uint32_t* ids, const double* means2d, const double* conics,
-                      const double* opacities, const double* colors, const double* bg,
-                      const orc_settings* st, const double* dL_dimage, double* g_means2d,
-                      double* g_conics, double* g_opacities, double* g_colors,
-                      double* abs_sum) {
-  composite_bwd_impl(W, H, N, ranges, ids, means2d, conics, opacities, colors, bg, *st,
+                      const uint32_t* ids, const double* means2d, const double* chol,
+                      const double* conics, const double* opacities, const double* colors,
+                      const double* bg, const orc_settings* st, const double* dL_dimage,
+                      double* g_means2d, double* g_conics, double* g_opacities,
+                      double* g_colors, double* abs_sum) {
+  composite_bwd_impl(W, H, N, ranges, ids, means2d, chol, conics, opacities, colors, bg, *st,
                      dL_dimage, g_means2d, g_conics, g_opacities, g_colors, abs_sum);
   return 0;
 }

@@ -46,6 +46,8 @@ enum { ORC_LOSS_L2 = 0, ORC_LOSS_L1 = 1 };
 
 /* Projection (steps 1-8).  Outputs (all [N,...]):
  *   means2d [N,2], conics [N,3] (A,B,C of q = A dx^2 + 2B dx dy + C dy^2),
+ *   chol [N,3] (L11, L21, L22 with conic = L L^T, so that
+ *   q = (L11 dx + L21 dy)^2 + (L22 dy)^2),
  *   cov2d [N,3] (a,b,c after the eps2d dilation), depths [N], radii [N],
  *   tiles [N] (tiles touched), rect [N,4] (x0,x1,y0,y1), colors [N,3],
  *   clamped [N,3] (1 where the colour's max(0,.) clamp was active).
@@ -54,9 +56,9 @@ enum { ORC_LOSS_L2 = 0, ORC_LOSS_L1 = 1 };
 int orc_project(int mode, int64_t N, int sh_degree,
                 const double* means, const double* scales, const double* quats,
                 const double* sh, const orc_camera* cam, const orc_settings* st,
-                double* means2d, double* conics, double* cov2d, double* depths,
-                int32_t* radii, uint32_t* tiles, int32_t* rect, double* colors,
-                uint8_t* clamped);
+                double* means2d, double* conics, double* chol, double* cov2d,
+                double* depths, int32_t* radii, uint32_t* tiles, int32_t* rect,
+                double* colors, uint8_t* clamped);
 
 /* Binning + stable sort + tile ranges (steps 9-11) on the fp32 key path.
  * means2d [N,2] and depths [N] are fp32.  Writes offsets [N] (exclusive scan
@@ -74,27 +76,29 @@ int64_t orc_bin_f64(int64_t N, const double* means2d, const int32_t* radii,
                     const double* depths, int32_t width, int32_t height,
                     int64_t capacity, uint32_t* ids, uint32_t* ranges);
 
-/* Front-to-back compositing (step 12), fp64.  image [H,W,3], final_T [H,W],
+/* Front-to-back compositing (step 12), fp64, with q evaluated from chol
+ * [N,3] as the completed square.  image [H,W,3], final_T [H,W],
  * last [H,W] (number of the tile's list entries up to and including the
  * last blended one; 0 if none), depth/alpha/margin [H,W] optional (NULL).
  * margin = smallest relative distance of a threshold decision taken for the
  * pixel (alpha vs alpha_min, o*G vs alpha_max, T' vs T_min). */
 int orc_composite(int32_t width, int32_t height, const uint32_t* ranges,
                   const uint32_t* ids, const double* means2d,
-                  const double* conics, const double* opacities,
+                  const double* chol, const double* opacities,
                   const double* colors, const double* depths,
                   const double* background, const orc_settings* st,
                   double* image, double* final_T, uint32_t* last,
                   double* out_depth, double* out_alpha, double* margin);
 
 /* Compositing backward (step 13, first half), fp64, recomputing the forward
- * per pixel and keeping every layer's transmittance.  Writes (overwrites)
+ * per pixel (q from chol) and keeping every layer's transmittance; the
+ * derivatives of q with respect to u, v and the conic use conics.  Writes (overwrites)
  * g_means2d [N,2], g_conics [N,3], g_opacities [N], g_colors [N,3], and if
  * non-NULL abs_sum [N,9] = sum of |per-pixel contribution| for each of those
  * nine fields (u,v,A,B,C,o,r,g,b), a conditioning measure. */
 int orc_composite_bwd(int32_t width, int32_t height, int64_t N,
                       const uint32_t* ranges, const uint32_t* ids,
-                      const double* means2d, const double* conics,
+                      const double* means2d, const double* chol, const double* conics,
                       const double* opacities, const double* colors,
                       const double* background, const orc_settings* st,
                       const double* dL_dimage, double* g_means2d,

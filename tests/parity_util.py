@@ -89,6 +89,31 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
     return out
 
 
+def gpu_project_bwd(scene, cam, g2, ld=None):
+    """GPU projection backward fed the given 2D gradients (dict with means2d
+    [N,2], conics [N,3], opacities [N], colors [N,3]), packed into the 2D
+    gradient records; returns the 3D gradients in [N, ...] layout."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    N = scene.n
+    g = raster.Gaussians.from_scene(scene, ld=ld)
+    fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=1024)
+    fr.project(g, cam)
+    rec = np.zeros(tuple(fr.grads2d.shape), np.float32)
+    rec[:N, 0:2] = g2["means2d"]
+    rec[:N, 2:5] = g2["conics"]
+    rec[:N, 5] = g2["opacities"]
+    rec[:N, 6:9] = g2["colors"]
+    fr.grads2d.copy_(torch.from_numpy(rec))
+    fr.project_backward(g)
+    torch.cuda.synchronize()
+    K = (scene.sh_degree + 1) ** 2
+    T = lambda t: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
+    return dict(radii=fr.radii[:N].cpu().numpy(), g_means=T(fr.g_means), g_scales=T(fr.g_scales),
+                g_quats=T(fr.g_quats), g_sh=T(fr.g_sh).reshape(N, K, 3),
+                g_opacities=T(fr.g_opacities))
+
+
 def assert_bits_equal(a, b, what):
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)
@@ -124,11 +149,12 @@ def compare_pixels(gpu_img, or_img, margin, name="image"):
 
 
 def gaussians_in_tiles(ranges, ids, tiles):
-    s = set()
-    for t in tiles:
-        a, b = ranges[t]
-        s.update(ids[a:b].tolist())
-    return s
+    """Unique ids listed in the given tiles (int64 array)."""
+    tiles = sorted(tiles)
+    if not tiles:
+        return np.zeros(0, np.int64)
+    parts = [ids[ranges[t][0]:ranges[t][1]] for t in tiles]
+    return np.unique(np.concatenate(parts).astype(np.int64))
 
 
 def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
@@ -141,7 +167,7 @@ def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
     bad = err > tol
     flip = np.zeros_like(bad)
     if exempt_rows is not None and len(exempt_rows):
-        rows = np.fromiter(exempt_rows, dtype=np.int64)
+        rows = np.asarray(exempt_rows, dtype=np.int64)
         flip[rows] = bad[rows]
     cond = np.zeros_like(bad)
     if abs_sum is not None:
@@ -152,3 +178,172 @@ def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
     where = np.argwhere(fail)[:5]
     return dict(fail=int(fail.sum()), flip=int(flip.sum()), cond=int(cond.sum()),
                 checked=int(bad.size), worst=worst, where=where.tolist(), name=name)
+
+
+# ---------------------------------------------------------------------------
+# One parity case: both sides run the same seeded scene and camera; the
+# oracle's own loss gradient and 2D gradients also drive the GPU's backward
+# stages in isolation (data flows from the oracle to the GPU only).
+# ---------------------------------------------------------------------------
+def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alpha=False,
+                    ld=None):
+    import time
+    t0 = time.time()
+    print("\n[parity] case %s" % name, flush=True)
+    gpu = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=target,
+                    backward=backward, depth_alpha=depth_alpha, ld=ld)
+    t1 = time.time()
+    orc = oracle.render(scene, cam, None, bg, with_margin=True)
+    r = dict(name=name, scene=scene, cam=cam, loss=loss, bg=bg, target=target, gpu=gpu, orc=orc)
+    if backward:
+        kind = oracle.LOSS_L2 if loss == "l2" else oracle.LOSS_L1
+        dl = oracle.loss_grad_image(orc["raster"]["image"], target, kind).astype(np.float32)
+        bw = oracle.backward(scene, cam, orc, dl.astype(np.float64), None, bg, with_abs=True)
+        r.update(dl=dl, bw=bw)
+    t2 = time.time()
+    if backward:
+        r["gpu_iso"] = gpu_frame(scene, cam, background=bg, dL_dimage=r["dl"], ld=ld)
+        r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld)
+    print("[parity] %s: N=%d M=%d gpu %.1fs oracle %.1fs" % (
+        name, scene.n, gpu["M"], t1 - t0 + time.time() - t2, t2 - t1), flush=True)
+    return r
+
+
+def check_project_fwd(r):
+    g, p = r["gpu"], r["orc"]["proj"]
+    for k in ("means2d", "conics", "depths"):
+        assert_bits_equal(g[k], p[k].astype(np.float32), k)
+    assert_bits_equal(g["radii"], p["radii"], "radii")
+    assert_bits_equal(g["tiles"], p["tiles"], "tiles")
+    vis = p["radii"] > 0
+    assert vis.sum() > 0
+    err = np.abs(g["colors"][vis] - p["colors"][vis])
+    assert err.max() <= 2e-6 + 1e-5 * np.abs(p["colors"][vis]).max(), err.max()
+    assert np.all(g["colors"][~vis] == 0)
+
+
+def check_bins(r):
+    g, b = r["gpu"], r["orc"]["bins"]
+    assert g["M"] == b["M"]
+    assert_bits_equal(g["offsets"], b["offsets"], "offsets")
+    assert_bits_equal(g["keys"], b["keys"], "keys")
+    assert_bits_equal(g["ids"], b["ids"], "ids")
+    assert_bits_equal(g["ranges"], b["ranges"], "ranges")
+
+
+def check_raster_fwd(r):
+    g, cam, o = r["gpu"], r["cam"], r["orc"]["raster"]
+    npx = cam.width * cam.height
+    for k in ("image", "final_T"):
+        nf, nflip, md, where = compare_pixels(g[k], o[k], o["margin"], k)
+        print("[parity] %s %s: max|d| %.3g (non-exempt), flips %d, unexplained %d" %
+              (r["name"], k, md, nflip, nf))
+        assert nf == 0, (k, where)
+        assert nflip <= max(2, 2e-5 * npx)
+    last_bad = (g["last"] != o["last"]) & (o["margin"] >= FLIP_REL)
+    assert last_bad.sum() == 0, np.argwhere(last_bad)[:5]
+    if "depth" in g:
+        ok = o["margin"] >= FLIP_REL
+        assert np.array_equal(g["alpha"], (1.0 - g["final_T"]).astype(np.float32))
+        assert np.abs(g["alpha"][ok] - o["alpha"][ok]).max() <= PIX_TOL
+        # depth sums alpha T z with z up to the far side of the scene
+        zmax = float(np.abs(r["orc"]["proj"]["depths"]).max())
+        assert np.abs(g["depth"][ok] - o["depth"][ok]).max() <= PIX_TOL * max(1.0, zmax)
+
+
+def check_raster_bwd(r):
+    """Compositing backward given the oracle's dL/dimage on both sides."""
+    g, cam, ob, o = r["gpu_iso"], r["cam"], r["bw"]["g2"], r["orc"]
+    flips, _ = flip_tiles(o["raster"]["margin"], cam.width, cam.height,
+                          extra_pixels=(g["last"] != o["raster"]["last"]))
+    ex = gaussians_in_tiles(o["bins"]["ranges"], o["bins"]["ids"], flips)
+    a = ob["abs_sum"]
+    reps = [compare_grad(g["g_means2d"], ob["means2d"], a[:, 0:2], ex, "means2d"),
+            compare_grad(g["g_conics"], ob["conics"], a[:, 2:5], ex, "conics"),
+            compare_grad(g["g_opac2d"], ob["opacities"], a[:, 5], ex, "opacities"),
+            compare_grad(g["g_colors"], ob["colors"], a[:, 6:9], ex, "colors")]
+    for rep in reps:
+        print("[parity] %s raster_bwd %s" % (r["name"], rep))
+    for rep in reps:
+        assert rep["fail"] == 0, rep
+        assert rep["cond"] <= 1e-3 * rep["checked"] + 2, rep
+
+
+def check_project_bwd(r):
+    """Projection backward given the oracle's 2D gradients on both sides.
+    Elements outside max(1e-3 |g|, 1e-5) must lie within ERR_C * u * e, e the
+    first-order fp32 rounding scale of the same chain rule including the
+    rounding of its fp32 inputs (cancellation, counted)."""
+    g, scene, cam = r["gpu_pbwd"], r["scene"], r["cam"]
+    g2, o = r["bw"]["g2"], r["bw"]["g3"]
+    radii = r["orc"]["proj"]["radii"]
+    assert_bits_equal(g["radii"], radii, "radii")
+    vis = radii > 0
+    for k in ("means", "scales", "quats", "sh", "opacities"):
+        assert np.all(g["g_" + k][~vis] == 0), k
+    # the opacity gradient passes through the projection backward unchanged
+    assert_bits_equal(g["g_opacities"][vis], g2["opacities"][vis].astype(np.float32),
+                      "opacities")
+    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
+                                    scene.sh_degree, cam, radii, g2["means2d"], g2["conics"],
+                                    g2["colors"])
+    for k in ("means", "scales", "quats", "sh"):
+        gg = np.asarray(g["g_" + k], np.float64).reshape(len(vis), -1)[vis]
+        oo = o[k].reshape(len(vis), -1)[vis]
+        ee = e[k].reshape(len(vis), -1)[vis]
+        err = np.abs(gg - oo)
+        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
+        cond = bad & (err <= ERR_C * EPS32 * ee)
+        print("[parity] %s project_bwd %s: outside tol %d, within fp32 cancellation bound %d, "
+              "of %d" % (r["name"], k, bad.sum(), cond.sum(), bad.size))
+        assert (bad & ~cond).sum() == 0, (k, np.argwhere(bad & ~cond)[:5])
+        # the 2D gradients arrive rounded to fp32 (the record is fp32), and
+        # the chain through a nearly singular 2D covariance multiplies that
+        # rounding by its condition number; heavy-tailed scenes hold a few
+        # such Gaussians in ten thousand
+        assert cond.sum() <= 1e-3 * bad.size + 4
+
+
+def check_e2e_grads(r):
+    """Whole path: GPU gradients against the oracle's own forward + backward.
+    2D gradients: as in the stage check.  3D gradients: outside max(1e-3 |g|,
+    1e-5) they must lie within the first-order bound that propagates the 2D
+    allowance (max(1e-3|g|, 1e-5, COND_K u sum|terms|)) through the projection
+    backward plus its own fp32 rounding.  Gaussians listed in a tile with a
+    threshold-flip pixel are exempt (counted)."""
+    g, scene, cam = r["gpu"], r["scene"], r["cam"]
+    orc, bw, dl = r["orc"], r["bw"], r["dl"]
+    flips, _ = flip_tiles(orc["raster"]["margin"], cam.width, cam.height,
+                          extra_pixels=(g["last"] != orc["raster"]["last"]) |
+                          (np.sign(g["dL_dimage"]) != np.sign(dl)).any(axis=2))
+    ex = gaussians_in_tiles(orc["bins"]["ranges"], orc["bins"]["ids"], flips)
+    a = bw["g2"]["abs_sum"]
+    reps = [compare_grad(g["g_means2d"], bw["g2"]["means2d"], a[:, 0:2], ex, "means2d"),
+            compare_grad(g["g_conics"], bw["g2"]["conics"], a[:, 2:5], ex, "conics"),
+            compare_grad(g["g_opac2d"], bw["g2"]["opacities"], a[:, 5], ex, "opacities"),
+            compare_grad(g["g_colors"], bw["g2"]["colors"], a[:, 6:9], ex, "colors")]
+    for rep in reps:
+        print("[parity] %s e2e %s" % (r["name"], rep))
+        assert rep["fail"] == 0, rep
+    allow = lambda go, ab: np.maximum(np.maximum(G_REL * np.abs(go), G_ABS), COND_K * EPS32 * ab)
+    s_m2 = np.abs(bw["g2"]["means2d"]) + allow(bw["g2"]["means2d"], a[:, 0:2]) / (ERR_C * EPS32)
+    s_con = np.abs(bw["g2"]["conics"]) + allow(bw["g2"]["conics"], a[:, 2:5]) / (ERR_C * EPS32)
+    s_col = np.abs(bw["g2"]["colors"]) + allow(bw["g2"]["colors"], a[:, 6:9]) / (ERR_C * EPS32)
+    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
+                                    scene.sh_degree, cam, orc["proj"]["radii"],
+                                    bw["g2"]["means2d"], bw["g2"]["conics"], bw["g2"]["colors"],
+                                    s_m2, s_con, s_col)
+    rows = np.zeros(scene.n, bool)
+    rows[ex] = True
+    for k in ("means", "scales", "quats", "sh"):
+        gg = np.asarray(g["g_" + k], np.float64).reshape(scene.n, -1)
+        oo = bw["g3"][k].reshape(scene.n, -1)
+        ee = e[k].reshape(scene.n, -1)
+        err = np.abs(gg - oo)
+        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
+        cond = bad & ~rows[:, None] & (err <= ERR_C * EPS32 * ee)
+        unexplained = bad & ~rows[:, None] & ~cond
+        print("[parity] %s e2e %s: outside tol %d (flip rows %d, within propagated bound %d) "
+              "of %d" % (r["name"], k, bad.sum(), (bad & rows[:, None]).sum(), cond.sum(),
+                         bad.size))
+        assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])

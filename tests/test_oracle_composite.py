@@ -117,7 +117,7 @@ def test_invariants_on_tiny_scene():
     np.testing.assert_allclose(r["alpha"], 1 - r["final_T"], rtol=0, atol=0)
     # unit colours, black background: image = sum a_k T_k = 1 - T_final
     ones = np.ones_like(p["colors"])
-    r1 = oracle.composite(64, 64, b["ranges"], b["ids"], p["means2d"], p["conics"],
+    r1 = oracle.composite(64, 64, b["ranges"], b["ids"], p["means2d"], p["chol"],
                           scene.opacities, ones, np.full(scene.n, 2.5))
     np.testing.assert_allclose(r1["image"][..., 0] + r1["final_T"], 1.0, atol=1e-12)
     # constant depth z0: depth output = z0 (1 - T_final)
@@ -134,7 +134,7 @@ def test_transmittance_monotone_along_lists():
     for k in list(range(0, maxlen + 1, 7)) + [maxlen]:
         rg = b["ranges"].copy()
         rg[:, 1] = np.minimum(rg[:, 1], rg[:, 0] + k)
-        r = oracle.composite(64, 64, rg, b["ids"], p["means2d"], p["conics"], scene.opacities,
+        r = oracle.composite(64, 64, rg, b["ids"], p["means2d"], p["chol"], scene.opacities,
                              p["colors"], p["depths"])
         assert np.all(r["final_T"] <= prevT)
         prevT = r["final_T"]
@@ -163,11 +163,9 @@ def _brute_force_pixel_render(p, opac, width, height, bg):
             T, C = 1.0, np.zeros(3)
             for _, i in cand:
                 u, v = p["means2d"][i]
-                A, B, Cc = p["conics"][i]
+                l11, l21, l22 = p["chol"][i]
                 dx, dy = px + 0.5 - u, py + 0.5 - v
-                q = A * dx * dx + 2.0 * B * dx * dy + Cc * dy * dy
-                if q < 0:
-                    continue
+                q = (l11 * dx + l21 * dy) ** 2 + (l22 * dy) ** 2
                 a = min(A_MAX, opac[i] * math.exp(-0.5 * q))
                 if a < A_MIN:
                     continue

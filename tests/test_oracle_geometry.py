@@ -124,6 +124,11 @@ def test_ewa_off_axis_against_numerical_jacobian():
                 A, B, Cc = p["conics"][0]
                 np.testing.assert_allclose(np.array([[A, B], [B, Cc]]) @ np.array([[a, b], [b, c]]),
                                            np.eye(2), atol=1e-10)
+                # the completed square's factor: L L^T is the same inverse
+                l11, l21, l22 = p["chol"][0]
+                L = np.array([[l11, 0.0], [l21, l22]])
+                np.testing.assert_allclose(L @ L.T @ np.array([[a, b], [b, c]]), np.eye(2),
+                                           atol=1e-10)
                 np.testing.assert_allclose(p["means2d"][0], _pinhole(cam, t), rtol=1e-12)
                 np.testing.assert_allclose(p["depths"][0], t[2], rtol=1e-12)
 
@@ -204,3 +209,53 @@ def test_culling_rules():
     np.testing.assert_array_equal(p["radii"] > 0, [1, 0, 0, 0, 0, 0, 0, 1])
     assert np.all(p["conics"][p["radii"] == 0] == 0)
     np.testing.assert_array_equal(p["tiles"][p["radii"] == 0], 0)
+
+
+def test_completed_square_factor_on_fp32_key_path():
+    """In fp32, L11 = sqrt(A), L21 = B / L11, L22 = 1 / sqrt(c) reproduce the
+    conic to a few roundings per entry, including needle-like splats whose
+    conic is nearly singular (heavy-tailed scales)."""
+    scene = scenes.heavy_tail_scene(n=20000, seed=9)
+    cam = scenes.sphere_poses(1, 6.0, 51, 256, 256, scenes.focal_for(256))[0]
+    p = oracle.project(scene.means, scene.scales, scene.quats, scene.sh, 3, cam)
+    vis = p["radii"] > 0
+    A, B, C = p["conics"][vis].T
+    l11, l21, l22 = p["chol"][vis].T
+    a, b, c = p["cov2d"][vis].T
+    kappa = (a + c) ** 2 / (a * c - b * b)  # >= condition number of the 2D covariance
+    assert kappa.max() > 1e3  # needles are present
+    u = 2.0 ** -24
+    assert np.all(np.abs(l11 * l11 - A) <= 4 * u * A)
+    assert np.all(np.abs(l11 * l21 - B) <= 4 * u * np.abs(B))
+    assert np.all(np.abs(l21 * l21 + l22 * l22 - C) <= 8 * u * C)
+    np.testing.assert_array_equal(l22, (np.float32(1) / np.sqrt(c.astype(np.float32))))
+
+
+def test_completed_square_evaluates_needles_stably():
+    """Why the quadratic form is evaluated as a completed square: far along a
+    needle the expanded A dx^2 + 2B dx dy + C dy^2 cancels terms of order 1e5
+    down to q ~ 1, so its fp32 evaluation is off by ~1e-2, while the
+    completed square's fp32 evaluation stays within a few 1e-5 of the value
+    the same fp32 factors define."""
+    f32 = np.float32
+    # 2D covariance of a needle: sigma 300 px along (1,1)/sqrt2, 0.6 px across
+    R = np.array([[1.0, -1.0], [1.0, 1.0]]) / np.sqrt(2.0)
+    S = R @ np.diag([300.0 ** 2, 0.6 ** 2]) @ R.T
+    a, b, c = f32(S[0, 0]), f32(S[0, 1]), f32(S[1, 1])
+    det = f32(a * c - b * b)
+    A, B, C = f32(c / det), f32(-(b / det)), f32(a / det)
+    l11 = f32(np.sqrt(A))
+    l21 = f32(B / l11)
+    l22 = f32(1) / f32(np.sqrt(c))
+    t = np.linspace(-600.0, 600.0, 41)
+    dx = (t / np.sqrt(2.0) + 0.3).astype(f32)
+    dy = (t / np.sqrt(2.0) - 0.2).astype(f32)
+    q_ref = (float(l11) * dx.astype(float) + float(l21) * dy.astype(float)) ** 2 + \
+        (float(l22) * dy.astype(float)) ** 2
+    e1 = l11 * dx + l21 * dy
+    e2 = l22 * dy
+    q_sq = e1 * e1 + e2 * e2                                   # fp32
+    q_ex = A * dx * dx + f32(2) * B * dx * dy + C * dy * dy    # fp32
+    assert np.abs(q_sq - q_ref).max() < 1e-4
+    assert np.abs(q_ex - (float(A) * dx.astype(float) ** 2 + 2 * float(B) * dx.astype(float) *
+                          dy.astype(float) + float(C) * dy.astype(float) ** 2)).max() > 1e-3

@@ -79,7 +79,7 @@ def test_coverage_scene_exercises_every_branch():
     # some pixel of the clamped-opacity Gaussians has o * G > alpha_max
     img = f["raster"]
     m = oracle.composite(cam.width, cam.height, f["bins"]["ranges"], f["bins"]["ids"], p["means2d"],
-                         p["conics"], s.opacities, p["colors"], p["depths"], with_margin=True)
+                         p["chol"], s.opacities, p["colors"], p["depths"], with_margin=True)
     assert np.any(img["last"] > 0)
     hits = 0
     for i in range(6, 12):

@@ -3,21 +3,22 @@ inputs, through the C ABI.
 
 Cases span several tiles and ragged image edges, up to the full 100k-Gaussian
 1920x1080 SH3 scene and one pose of the 1M-Gaussian clustered scene at
-1920x1080 (the configuration the benchmark times).  Each stage is compared in
-isolation (the oracle is fed the GPU's inputs to that stage) and end to end.
+1920x1080 (the configuration the benchmark times).
+
+Data flows from the oracle to the GPU only.  End to end, each side runs its
+own whole path from the scene.  The backward stages are also compared in
+isolation by feeding the GPU the oracle's own upstream gradient: the
+oracle's dL/dimage (rounded to fp32) into the compositing backward, and the
+oracle's 2D gradients into the projection backward.
 """
 import functools
-import time
 
-import numpy as np
 import pytest
 
-import oracle
 from differentiable_rasterization_amd import scenes
 
-from parity_util import (COND_K, EPS32, ERR_C, FLIP_REL, G_ABS, G_REL, PIX_TOL,
-                         assert_bits_equal, compare_grad, compare_pixels, flip_tiles,
-                         gaussians_in_tiles, gpu_frame)
+from parity_util import (check_bins, check_e2e_grads, check_project_bwd, check_project_fwd,
+                         check_raster_bwd, check_raster_fwd, run_parity_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,183 +37,47 @@ def _case(name):
     if name == "box_100k_1080p":
         s, c = scenes.box_scene()
         return s, c, "l2", (0.0, 0.0, 0.0)
-    if name == "cluster_1m_1080p":
-        s, cams, loss = scenes.make_config("cluster_1m_1080p")
+    if name in ("cluster_1m_1080p", "cluster_1m_1280x832"):
+        s, cams, loss = scenes.make_config(name)
         return s, cams[0], loss, (0.0, 0.0, 0.0)
     raise KeyError(name)
 
 
 CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "box_100k_1080p",
-         "cluster_1m_1080p"]
+         "cluster_1m_1280x832", "cluster_1m_1080p"]
 
 
 @functools.lru_cache(maxsize=None)
 def run_case(name):
-    t0 = time.time()
-    print("\n[parity] case %s" % name, flush=True)
     scene, cam, loss, bg = _case(name)
-    target = scenes.target_image(cam, 7)
-    gpu = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=target)
-    t1 = time.time()
-    orc_fwd = oracle.render(scene, cam, None, bg, with_margin=True)
-    # stage-isolated compositing: the oracle is fed the GPU's projection and lists
-    iso = oracle.composite(cam.width, cam.height, gpu["ranges"], gpu["ids"], gpu["means2d"],
-                           gpu["conics"], scene.opacities, gpu["colors"], gpu["depths"], bg,
-                           with_margin=True)
-    iso_bwd = oracle.composite_bwd(cam.width, cam.height, gpu["ranges"], gpu["ids"],
-                                   gpu["means2d"], gpu["conics"], scene.opacities, gpu["colors"],
-                                   gpu["dL_dimage"], bg, with_abs=True)
-    iso_pbwd = oracle.project_bwd(scene.means, scene.scales, scene.quats, scene.sh,
-                                  scene.sh_degree, cam, gpu["radii"], gpu["g_means2d"],
-                                  gpu["g_conics"], gpu["g_colors"])
-    print("[parity] %s: N=%d M=%d gpu %.1fs oracle %.1fs" % (name, scene.n, gpu["M"], t1 - t0,
-                                                             time.time() - t1), flush=True)
-    return dict(scene=scene, cam=cam, loss=loss, bg=bg, target=target, gpu=gpu, orc=orc_fwd,
-                iso=iso, iso_bwd=iso_bwd, iso_pbwd=iso_pbwd)
+    return run_parity_case(name, scene, cam, loss, bg, scenes.target_image(cam, 7))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_project_fwd_bit_exact(name):
-    r = run_case(name)
-    g, p = r["gpu"], r["orc"]["proj"]
-    for k in ("means2d", "conics", "depths"):
-        assert_bits_equal(g[k], p[k].astype(np.float32), k)
-    assert_bits_equal(g["radii"], p["radii"], "radii")
-    assert_bits_equal(g["tiles"], p["tiles"], "tiles")
-    vis = p["radii"] > 0
-    assert vis.sum() > 0
-    err = np.abs(g["colors"][vis] - p["colors"][vis])
-    assert err.max() <= 2e-6 + 1e-5 * np.abs(p["colors"][vis]).max(), err.max()
-    assert np.all(g["colors"][~vis] == 0)
+    check_project_fwd(run_case(name))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_bin_and_sort_bit_exact(name):
-    r = run_case(name)
-    g, b = r["gpu"], r["orc"]["bins"]
-    assert g["M"] == b["M"]
-    assert_bits_equal(g["offsets"], b["offsets"], "offsets")
-    assert_bits_equal(g["keys"], b["keys"], "keys")
-    assert_bits_equal(g["ids"], b["ids"], "ids")
-    assert_bits_equal(g["ranges"], b["ranges"], "ranges")
-
-
-def _pixel_report(name, g, o):
-    res = {}
-    for k in ("image", "final_T"):
-        nf, nflip, md, where = compare_pixels(g[k], o[k], o["margin"], k)
-        res[k] = (nf, nflip, md, where)
-    return res
+    check_bins(run_case(name))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_rasterize_fwd(name):
-    r = run_case(name)
-    g, cam = r["gpu"], r["cam"]
-    npx = cam.width * cam.height
-    for label, o in (("isolated", r["iso"]), ("end-to-end", r["orc"]["raster"])):
-        rep = _pixel_report(name, g, o)
-        for k, (nf, nflip, md, where) in rep.items():
-            print("[parity] %s %s %s: max|d| %.3g (non-exempt), flips %d, unexplained %d" %
-                  (name, label, k, md, nflip, nf))
-            assert nf == 0, (k, where)
-            assert nflip <= max(2, 2e-5 * npx)
-        last_bad = (g["last"] != o["last"]) & (o["margin"] >= FLIP_REL)
-        assert last_bad.sum() == 0, np.argwhere(last_bad)[:5]
+    check_raster_fwd(run_case(name))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_rasterize_bwd(name):
-    r = run_case(name)
-    g, cam, ob = r["gpu"], r["cam"], r["iso_bwd"]
-    flips, _ = flip_tiles(r["iso"]["margin"], cam.width, cam.height,
-                          extra_pixels=(g["last"] != r["iso"]["last"]))
-    ex = gaussians_in_tiles(g["ranges"], g["ids"], flips)
-    abs_sum = ob["abs_sum"]
-    reps = [compare_grad(g["g_means2d"], ob["means2d"], abs_sum[:, 0:2], ex, "means2d"),
-            compare_grad(g["g_conics"], ob["conics"], abs_sum[:, 2:5], ex, "conics"),
-            compare_grad(g["g_opac2d"], ob["opacities"], abs_sum[:, 5], ex, "opacities"),
-            compare_grad(g["g_colors"], ob["colors"], abs_sum[:, 6:9], ex, "colors")]
-    for rep in reps:
-        print("[parity] %s raster_bwd %s" % (name, rep))
-    for rep in reps:
-        assert rep["fail"] == 0, rep
-        assert rep["cond"] <= 1e-3 * rep["checked"] + 2, rep
+    check_raster_bwd(run_case(name))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_project_bwd(name):
-    """Stage-isolated: the oracle gets the GPU's 2D gradients.  Elements outside
-    max(1e-3 |g|, 1e-5) must lie within ERR_C * u * e, e the first-order fp32
-    rounding scale of the same chain rule (cancellation, counted)."""
-    r = run_case(name)
-    g, o, scene, cam = r["gpu"], r["iso_pbwd"], r["scene"], r["cam"]
-    vis = g["radii"] > 0
-    for k in ("means", "scales", "quats", "sh", "opacities"):
-        assert np.all(g["g_" + k][~vis] == 0), k
-    # the opacity gradient passes through the projection backward unchanged
-    assert_bits_equal(g["g_opacities"][vis], g["g_opac2d"][vis], "opacities")
-    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
-                                    scene.sh_degree, cam, g["radii"], g["g_means2d"],
-                                    g["g_conics"], g["g_colors"])
-    for k in ("means", "scales", "quats", "sh"):
-        gg = np.asarray(g["g_" + k], np.float64).reshape(len(vis), -1)[vis]
-        oo = o[k].reshape(len(vis), -1)[vis]
-        ee = e[k].reshape(len(vis), -1)[vis]
-        err = np.abs(gg - oo)
-        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
-        cond = bad & (err <= ERR_C * EPS32 * ee)
-        print("[parity] %s project_bwd %s: outside tol %d, within fp32 cancellation bound %d, "
-              "of %d" % (name, k, bad.sum(), cond.sum(), bad.size))
-        assert (bad & ~cond).sum() == 0, (k, np.argwhere(bad & ~cond)[:5])
-        assert cond.sum() <= 1e-4 * bad.size + 4
+    check_project_bwd(run_case(name))
 
 
 @pytest.mark.parametrize("name", CASES)
 def test_end_to_end_gradients(name):
-    """Whole path: GPU gradients against the oracle's own forward + backward.
-    2D gradients: as in the stage test.  3D gradients: outside max(1e-3 |g|,
-    1e-5) they must lie within the first-order bound that propagates the 2D
-    allowance (max(1e-3|g|, 1e-5, COND_K u sum|terms|)) through the projection
-    backward plus its own fp32 rounding.  Gaussians listed in a tile with a
-    threshold-flip pixel are exempt (counted)."""
-    r = run_case(name)
-    g, scene, cam, bg = r["gpu"], r["scene"], r["cam"], r["bg"]
-    orc = r["orc"]
-    kind = oracle.LOSS_L2 if r["loss"] == "l2" else oracle.LOSS_L1
-    dl = oracle.loss_grad_image(orc["raster"]["image"], r["target"], kind)
-    bw = oracle.backward(scene, cam, orc, dl, None, bg, with_abs=True)
-    flips, _ = flip_tiles(orc["raster"]["margin"], cam.width, cam.height,
-                          extra_pixels=(g["last"] != orc["raster"]["last"]) |
-                          (np.sign(g["dL_dimage"]) != np.sign(dl)).any(axis=2))
-    ex = gaussians_in_tiles(g["ranges"], g["ids"], flips)
-    a = bw["g2"]["abs_sum"]
-    reps = [compare_grad(g["g_means2d"], bw["g2"]["means2d"], a[:, 0:2], ex, "means2d"),
-            compare_grad(g["g_conics"], bw["g2"]["conics"], a[:, 2:5], ex, "conics"),
-            compare_grad(g["g_opac2d"], bw["g2"]["opacities"], a[:, 5], ex, "opacities"),
-            compare_grad(g["g_colors"], bw["g2"]["colors"], a[:, 6:9], ex, "colors")]
-    for rep in reps:
-        print("[parity] %s e2e %s" % (name, rep))
-        assert rep["fail"] == 0, rep
-    allow = lambda go, ab: np.maximum(np.maximum(G_REL * np.abs(go), G_ABS), COND_K * EPS32 * ab)
-    s_m2 = np.abs(bw["g2"]["means2d"]) + allow(bw["g2"]["means2d"], a[:, 0:2]) / (ERR_C * EPS32)
-    s_con = np.abs(bw["g2"]["conics"]) + allow(bw["g2"]["conics"], a[:, 2:5]) / (ERR_C * EPS32)
-    s_col = np.abs(bw["g2"]["colors"]) + allow(bw["g2"]["colors"], a[:, 6:9]) / (ERR_C * EPS32)
-    e = oracle.project_bwd_errscale(scene.means, scene.scales, scene.quats, scene.sh,
-                                    scene.sh_degree, cam, orc["proj"]["radii"],
-                                    bw["g2"]["means2d"], bw["g2"]["conics"], bw["g2"]["colors"],
-                                    s_m2, s_con, s_col)
-    rows = np.zeros(scene.n, bool)
-    if ex:
-        rows[np.fromiter(ex, np.int64)] = True
-    for k in ("means", "scales", "quats", "sh"):
-        gg = np.asarray(g["g_" + k], np.float64).reshape(scene.n, -1)
-        oo = bw["g3"][k].reshape(scene.n, -1)
-        ee = e[k].reshape(scene.n, -1)
-        err = np.abs(gg - oo)
-        bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
-        cond = bad & ~rows[:, None] & (err <= ERR_C * EPS32 * ee)
-        unexplained = bad & ~rows[:, None] & ~cond
-        print("[parity] %s e2e %s: outside tol %d (flip rows %d, within propagated bound %d) "
-              "of %d" % (name, k, bad.sum(), (bad & rows[:, None]).sum(), cond.sum(), bad.size))
-        assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])
+    check_e2e_grads(run_case(name))
