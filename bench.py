@@ -31,13 +31,17 @@ HBM_PEAK_GBS = 8000.0
 # slots/s (one non-packed VALU instruction per lane per slot; transcendental
 # exp2/rcp take four slots).
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
-# VALU slots per pixel-splat pair of the compositing inner loops, counted in
-# the gfx950 assembly of raster.hip: forward 57 VALU per two unrolled pairs
-# plus 3 extra slots for v_exp_f32; backward 60 VALU per pair plus 6 extra for
-# v_exp_f32 and v_rcp_f32, and 28 VALU per executed 9-field wave reduction.
-FWD_SLOTS_PER_PAIR = 31.5
-BWD_SLOTS_PER_PAIR = 66.0
-BWD_SLOTS_PER_REDUCTION = 28.0
+# VALU slots of the compositing inner loops, counted in the gfx950 assembly
+# of raster.hip (a quarter-rate v_exp_f32 / v_rcp_f32 counts four slots):
+#   forward: 51 VALU and two v_exp_f32 per two unrolled pairs -> 28.5 / pair;
+#   backward: 30 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (36
+#   slots); a wavefront with a hit on the splat adds 21 VALU of gradient
+#   terms and 36 of the nine-field reduction (lane swaps + DPP row scan).
+FWD_SLOTS_PER_PAIR = 28.5
+BWD_EVAL_SLOTS = 36.0
+BWD_GRAD_SLOTS = 21.0
+BWD_REDUCE_SLOTS = 36.0
+BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
 
 
 def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
@@ -204,14 +208,14 @@ def main():
     dominant = max(names, key=lambda n: stage_ms[n])
     # The compositing kernels are bound by VALU issue.  Algorithmic work = the
     # pixel-splat pairs that blend (the pairs whose result the method uses)
-    # x VALU slots per pair of the kernel's loop; "issued" adds the pairs the
-    # kernel evaluated but that did not blend, and the wave reductions.
+    # x VALU slots such a pair costs in the kernel's loop; "issued" counts
+    # every pair the kernel evaluated and every wavefront reduction.
     alu = {
         "rasterize_fwd": (avg["blended"] * FWD_SLOTS_PER_PAIR,
                           avg["fwd_eval"] * FWD_SLOTS_PER_PAIR),
         "rasterize_bwd": (avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
-                          avg["bwd_eval"] * BWD_SLOTS_PER_PAIR +
-                          avg["bwd_reductions"] * 64 * BWD_SLOTS_PER_REDUCTION),
+                          avg["bwd_eval"] * BWD_EVAL_SLOTS +
+                          avg["bwd_reductions"] * 64 * (BWD_GRAD_SLOTS + BWD_REDUCE_SLOTS)),
     }
     work = {"pairs_blended": int(avg["blended"]), "pairs_evaluated_fwd": int(avg["fwd_eval"]),
             "pairs_evaluated_bwd": int(avg["bwd_eval"]),

@@ -220,18 +220,6 @@ __device__ inline void camera_centre(const Cam& cam, float c[3]) {
              cam.R[2 * 3 + j] * cam.t[2]);
 }
 
-// colour = max(0, offset + sum_j Y_j(d) c_j) per channel; raw values kept
-// for the clamp mask of the backward.
-__device__ inline void sh_colour(int deg, int K, const float* __restrict__ sh, int64_t ld,
-                                 int64_t i, const float d[3], float off, float raw[3],
-                                 float Y[16]) {
-  sh_basis(deg, d[0], d[1], d[2], Y);
-  raw[0] = raw[1] = raw[2] = off;
-  for (int j = 0; j < K; ++j)
-    for (int ch = 0; ch < 3; ++ch)
-      raw[ch] = fmaf(Y[j], sh[(int64_t)(j * 3 + ch) * ld + i], raw[ch]);
-}
-
 // Padded half-extents of the footprint where alpha = o exp(-q/2) can reach
 // alpha_min: q <= Q = 2 ln(o / alpha_min), whose ellipse lies inside
 // |dx| <= sqrt(Q a), |dy| <= sqrt(Q c) for the dilated 2D covariance
@@ -255,55 +243,66 @@ __device__ inline void footprint(float a, float b, float c, float o, float alpha
   ey = sqrtf(Q * c) + 0.02f;
 }
 
+template <int DEG>
 __global__ __launch_bounds__(256) void project_fwd_kernel(
-    int64_t N, int64_t ld, int deg, const float* __restrict__ means,
+    int64_t N, int64_t ld, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ opac, const float* __restrict__ sh, Cam cam, Settings st,
     float* __restrict__ means2d, float* __restrict__ conics, float* __restrict__ depths,
     int32_t* __restrict__ radii, float* __restrict__ colors, uint32_t* __restrict__ tiles,
     float4* __restrict__ splats) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
+  // all loads first: every lane keeps its parameters and SH coefficients in
+  // flight together (culled lanes share cache lines with visible ones, so
+  // their SH lines are fetched anyway)
   const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
   const float s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
   const float q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
+  const float o = opac[i];
+  float shv[3 * K];
+#pragma unroll
+  for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
+
   Geom g;
   float qn[5], Rq[9], Sig[6], Tm[6], tc[3];
   const bool vis = project_geom(m, s, q, cam, st, g, qn, Rq, Sig, Tm, tc);
-  if (!vis) {
-    means2d[i] = 0.0f; means2d[ld + i] = 0.0f;
-    conics[i] = 0.0f; conics[ld + i] = 0.0f; conics[2 * ld + i] = 0.0f;
-    depths[i] = 0.0f; radii[i] = 0; tiles[i] = 0u;
-    colors[i] = 0.0f; colors[ld + i] = 0.0f; colors[2 * ld + i] = 0.0f;
-    return;
+  float col[3] = {0.0f, 0.0f, 0.0f};
+  if (vis) {
+    float cc[3];
+    camera_centre(cam, cc);
+    const float dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
+    const float L = sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+    const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
+    float Y[16];
+    sh_basis(DEG, d[0], d[1], d[2], Y);
+    float raw[3] = {st.sh_offset, st.sh_offset, st.sh_offset};
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) raw[ch] = fmaf(Y[j], shv[j * 3 + ch], raw[ch]);
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) col[ch] = raw[ch] < 0.0f ? 0.0f : raw[ch];
+    float ex, ey;
+    footprint(g.a, g.b, g.c, o, st.alpha_min, ex, ey);
+    float4* rec = splats + 4 * i;
+    rec[0] = make_float4(g.u, g.v, kSqrtHalfLog2e * g.L11, kSqrtHalfLog2e * g.L21);
+    rec[1] = make_float4(kSqrtHalfLog2e * g.L22, o, col[0], col[1]);
+    rec[2] = make_float4(col[2], __int_as_float(g.radius), ex, ey);
+    rec[3] = make_float4(g.A, g.B, g.C, 0.0f);
   }
-  means2d[i] = g.u; means2d[ld + i] = g.v;
-  conics[i] = g.A; conics[ld + i] = g.B; conics[2 * ld + i] = g.C;
-  depths[i] = g.depth;
-  radii[i] = g.radius;
-  tiles[i] = (uint32_t)(g.x1 - g.x0) * (uint32_t)(g.y1 - g.y0);
-
-  float cc[3];
-  camera_centre(cam, cc);
-  float dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
-  const float L = sqrtf(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-  const float d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
-  const int K = (deg + 1) * (deg + 1);
-  float raw[3], Y[16];
-  sh_colour(deg, K, sh, ld, i, d, st.sh_offset, raw, Y);
-  float col[3];
-  for (int ch = 0; ch < 3; ++ch) {
-    col[ch] = raw[ch] < 0.0f ? 0.0f : raw[ch];
-    colors[(int64_t)ch * ld + i] = col[ch];
-  }
-  const float o = opac[i];
-  float ex, ey;
-  footprint(g.a, g.b, g.c, o, st.alpha_min, ex, ey);
-  float4* rec = splats + 4 * i;
-  rec[0] = make_float4(g.u, g.v, kSqrtHalfLog2e * g.L11, kSqrtHalfLog2e * g.L21);
-  rec[1] = make_float4(kSqrtHalfLog2e * g.L22, o, col[0], col[1]);
-  rec[2] = make_float4(col[2], __int_as_float(g.radius), ex, ey);
-  rec[3] = make_float4(g.A, g.B, g.C, 0.0f);
+  // one store path for culled (zeros) and visible lanes
+  means2d[i] = vis ? g.u : 0.0f;
+  means2d[ld + i] = vis ? g.v : 0.0f;
+  conics[i] = vis ? g.A : 0.0f;
+  conics[ld + i] = vis ? g.B : 0.0f;
+  conics[2 * ld + i] = vis ? g.C : 0.0f;
+  depths[i] = vis ? g.depth : 0.0f;
+  radii[i] = vis ? g.radius : 0;
+  tiles[i] = vis ? (uint32_t)(g.x1 - g.x0) * (uint32_t)(g.y1 - g.y0) : 0u;
+#pragma unroll
+  for (int ch = 0; ch < 3; ++ch) colors[(int64_t)ch * ld + i] = col[ch];
 }
 
 // Real SH basis and its gradient in fp64, for the backward (the same
@@ -372,199 +371,240 @@ __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, 
 // splats, condition numbers 1e4-1e5) loses about u times the condition
 // number in fp32; the kernel moves ~300 bytes per Gaussian against a few
 // hundred fp64 operations, so it stays memory-bound.
+template <int DEG>
 __global__ __launch_bounds__(256) void project_bwd_kernel(
-    int64_t N, int64_t ld, int deg, const float* __restrict__ means,
+    int64_t N, int64_t ld, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ sh, Cam cam, Settings st, const int32_t* __restrict__ radii,
     const float4* __restrict__ grads2d, float* __restrict__ o_means,
     float* __restrict__ o_scales, float* __restrict__ o_quats, float* __restrict__ o_opac,
     float* __restrict__ o_sh, int accumulate) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
-  const int K = (deg + 1) * (deg + 1);
-  if (!(radii[i] > 0)) {
-    if (!accumulate) {
-      for (int k = 0; k < 3; ++k) { o_means[(int64_t)k * ld + i] = 0.0f; o_scales[(int64_t)k * ld + i] = 0.0f; }
-      for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + i] = 0.0f;
-      for (int k = 0; k < 3 * K; ++k) o_sh[(int64_t)k * ld + i] = 0.0f;
-      o_opac[i] = 0.0f;
-    }
-    return;
-  }
-  const float4 r0 = grads2d[4 * i + 0], r1 = grads2d[4 * i + 1], r2 = grads2d[4 * i + 2];
-  // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
-  o_opac[i] = accumulate ? o_opac[i] + r1.y : r1.y;
-
-  const double m[3] = {means[i], means[ld + i], means[2 * ld + i]};
-  const double s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
-  const double q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
-  double W[9];
-  for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
-  const double fx = cam.fx, fy = cam.fy;
-  const double tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + (double)cam.t[0];
-  const double ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + (double)cam.t[1];
-  const double tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + (double)cam.t[2];
-
-  // unit quaternion, rotation, M = R diag(s), Sigma = M M^T
-  const double n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
-  const double nr = sqrt(n2);
-  const double w = q[0] / nr, x = q[1] / nr, y = q[2] / nr, z = q[3] / nr;
-  double Rq[9];
-  Rq[0] = 1.0 - 2.0 * (y * y + z * z);
-  Rq[1] = 2.0 * (x * y - w * z);
-  Rq[2] = 2.0 * (x * z + w * y);
-  Rq[3] = 2.0 * (x * y + w * z);
-  Rq[4] = 1.0 - 2.0 * (x * x + z * z);
-  Rq[5] = 2.0 * (y * z - w * x);
-  Rq[6] = 2.0 * (x * z - w * y);
-  Rq[7] = 2.0 * (y * z + w * x);
-  Rq[8] = 1.0 - 2.0 * (x * x + y * y);
-  double M[9];
-  for (int r = 0; r < 3; ++r)
-    for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
-  double Sf[9];
-  for (int r = 0; r < 3; ++r)
-    for (int j = r; j < 3; ++j) {
-      const double v = (M[r * 3] * M[j * 3] + M[r * 3 + 1] * M[j * 3 + 1]) + M[r * 3 + 2] * M[j * 3 + 2];
-      Sf[r * 3 + j] = v;
-      Sf[j * 3 + r] = v;
-    }
-
-  // EWA Jacobian with the fov clamp, T = J W, 2D covariance and conic
-  const double txz = tx / tz, tyz = ty / tz;
-  const double limx = (double)st.fov_clamp * ((0.5 * (double)cam.W) / fx);
-  const double limy = (double)st.fov_clamp * ((0.5 * (double)cam.H) / fy);
-  const bool clampx = (txz > limx) || (txz < -limx);
-  const bool clampy = (tyz > limy) || (tyz < -limy);
-  const double xc = (clampx ? (txz > 0.0 ? limx : -limx) : txz) * tz;
-  const double yc = (clampy ? (tyz > 0.0 ? limy : -limy) : tyz) * tz;
-  const double tz2 = tz * tz;
-  const double J00 = fx / tz, J02 = -((fx * xc) / tz2);
-  const double J11 = fy / tz, J12 = -((fy * yc) / tz2);
-  double Tm[6];
-  for (int j = 0; j < 3; ++j) {
-    Tm[j] = J00 * W[j] + J02 * W[6 + j];
-    Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
-  }
-  double ST0[3], ST1[3];
-  for (int r = 0; r < 3; ++r) {
-    ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
-    ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
-  }
-  const double a = (Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2]) + (double)st.eps2d;
-  const double b = Tm[0] * ST1[0] + Tm[1] * ST1[1] + Tm[2] * ST1[2];
-  const double c = (Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2]) + (double)st.eps2d;
-  const double det = a * c - b * b;
-  const double A = c / det, B = -(b / det), C = a / det;
-
-  // conic = Sigma2D^-1: dL/dSigma2D = -conic G conic, G = [[gA, gB/2], [gB/2, gC]]
-  const double gA = r0.z, gB = r0.w, gC = r1.x;
-  const double ga = -(gA * A * A + gB * A * B + gC * B * B);
-  const double gb = -(2.0 * gA * A * B + gB * (A * C + B * B) + 2.0 * gC * B * C);
-  const double gc = -(gA * B * B + gB * B * C + gC * C * C);
-
-  // Sigma2D = T Sigma T^T: dL/dSigma = T^T G2 T, dL/dT = 2 G2 T Sigma
-  double gSig[9];
-  for (int r = 0; r < 3; ++r)
-    for (int k = 0; k < 3; ++k)
-      gSig[r * 3 + k] = ga * Tm[r] * Tm[k] + gb * Tm[r] * Tm[3 + k] + gc * Tm[3 + r] * Tm[3 + k];
-  double gT0[3], gT1[3];
-  for (int r = 0; r < 3; ++r) {
-    gT0[r] = 2.0 * ga * ST0[r] + gb * ST1[r];
-    gT1[r] = gb * ST0[r] + 2.0 * gc * ST1[r];
-  }
-  double gJ00 = 0.0, gJ02 = 0.0, gJ11 = 0.0, gJ12 = 0.0;
-  for (int j = 0; j < 3; ++j) {
-    gJ00 += gT0[j] * W[j];
-    gJ02 += gT0[j] * W[6 + j];
-    gJ11 += gT1[j] * W[3 + j];
-    gJ12 += gT1[j] * W[6 + j];
-  }
-  const double itz = 1.0 / tz, itz2 = itz * itz, itz3 = itz2 * itz;
-  double gt[3] = {0.0, 0.0, 0.0};
-  gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
-  if (clampx) {
-    gt[2] += gJ02 * (fx * (txz > 0.0 ? limx : -limx) * itz2);
-  } else {
-    gt[0] += gJ02 * (-fx * itz2);
-    gt[2] += gJ02 * (2.0 * fx * tx * itz3);
-  }
-  if (clampy) {
-    gt[2] += gJ12 * (fy * (tyz > 0.0 ? limy : -limy) * itz2);
-  } else {
-    gt[1] += gJ12 * (-fy * itz2);
-    gt[2] += gJ12 * (2.0 * fy * ty * itz3);
-  }
-  const double gu = r0.x, gv = r0.y;
-  gt[0] += gu * fx * itz;
-  gt[2] += gu * (-fx * tx * itz2);
-  gt[1] += gv * fy * itz;
-  gt[2] += gv * (-fy * ty * itz2);
-  double gm[3];
-  for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
-
-  // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M
-  double gs[3] = {0.0, 0.0, 0.0}, gR[9];
-  for (int r = 0; r < 3; ++r)
+  const bool vis = radii[i] > 0;
+  // every load of a visible lane is issued here, ahead of the fp64 chain, so
+  // that each lane keeps its whole working set in flight (the kernel runs
+  // at two waves per SIMD)
+  float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
+  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
+#pragma unroll
+  for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
+  if (vis) {
+#pragma unroll
     for (int k = 0; k < 3; ++k) {
-      double acc = 0.0;
-      for (int j = 0; j < 3; ++j) acc += (gSig[r * 3 + j] + gSig[j * 3 + r]) * M[j * 3 + k];
-      gs[k] += acc * Rq[r * 3 + k];
-      gR[r * 3 + k] = acc * s[k];
+      pm[k] = means[(int64_t)k * ld + i];
+      ps[k] = scales[(int64_t)k * ld + i];
     }
-  double gqn[4];
-  gqn[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
-  gqn[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
-           4.0 * x * (gR[4] + gR[8]);
-  gqn[2] = 2.0 * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
-           4.0 * y * (gR[0] + gR[8]);
-  gqn[3] = 2.0 * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
-           4.0 * z * (gR[0] + gR[4]);
-  const double dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
-  double gq[4];
-  gq[0] = (gqn[0] - w * dot) / nr;
-  gq[1] = (gqn[1] - x * dot) / nr;
-  gq[2] = (gqn[2] - y * dot) / nr;
-  gq[3] = (gqn[3] - z * dot) / nr;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
+    r0 = grads2d[4 * i + 0];
+    r1 = grads2d[4 * i + 1];
+    r2 = grads2d[4 * i + 2];
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
+  }
+  // culled Gaussians get zeros (overwrite) or are left alone (accumulate);
+  // both kinds of lanes store through the same instructions below, so a
+  // cache line of a plane is written once
+  const bool store = vis || !accumulate;
+  float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
+  float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
+  float gcol[3] = {0.0f, 0.0f, 0.0f};
+  double d[3] = {0.0, 0.0, 1.0}, L = 1.0;
 
-  // colour -> SH coefficients and the view direction
-  double cc[3];
-  for (int j = 0; j < 3; ++j)
-    cc[j] = -((W[j] * (double)cam.t[0] + W[3 + j] * (double)cam.t[1]) + W[6 + j] * (double)cam.t[2]);
-  const double dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
-  const double L = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-  const double d[3] = {dir[0] / L, dir[1] / L, dir[2] / L};
-  double Y[16];
-  sh_basis64(deg, d[0], d[1], d[2], Y);
-  double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
-  for (int j = 0; j < K; ++j)
-    for (int ch = 0; ch < 3; ++ch)
-      raw[ch] = fma(Y[j], (double)sh[(int64_t)(j * 3 + ch) * ld + i], raw[ch]);
-  const double gin[3] = {r1.z, r1.w, r2.x};
-  double gcol[3];
-  for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0 : gin[ch];
-  double gd[3] = {0.0, 0.0, 0.0};
-  for (int j = 0; j < K; ++j) {
-    double wj = 0.0;
-    for (int ch = 0; ch < 3; ++ch) {
-      const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
-      const float gval = (float)(Y[j] * gcol[ch]);
-      o_sh[p] = accumulate ? o_sh[p] + gval : gval;
-      wj = fma(gcol[ch], (double)sh[p], wj);
+  if (vis) {
+    // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
+    oo = r1.y;
+    const double m[3] = {pm[0], pm[1], pm[2]};
+    const double s[3] = {ps[0], ps[1], ps[2]};
+    const double q[4] = {pq[0], pq[1], pq[2], pq[3]};
+    double W[9];
+    for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
+    const double fx = cam.fx, fy = cam.fy;
+    const double tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + (double)cam.t[0];
+    const double ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + (double)cam.t[1];
+    const double tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + (double)cam.t[2];
+
+    // unit quaternion, rotation, M = R diag(s), Sigma = M M^T
+    const double n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
+    // (fp64 reciprocals stand in for divisions: their rounding is far below
+    // the fp32 outputs')
+    const double nr = sqrt(n2), inr = 1.0 / nr;
+    const double w = q[0] * inr, x = q[1] * inr, y = q[2] * inr, z = q[3] * inr;
+    double Rq[9];
+    Rq[0] = 1.0 - 2.0 * (y * y + z * z);
+    Rq[1] = 2.0 * (x * y - w * z);
+    Rq[2] = 2.0 * (x * z + w * y);
+    Rq[3] = 2.0 * (x * y + w * z);
+    Rq[4] = 1.0 - 2.0 * (x * x + z * z);
+    Rq[5] = 2.0 * (y * z - w * x);
+    Rq[6] = 2.0 * (x * z - w * y);
+    Rq[7] = 2.0 * (y * z + w * x);
+    Rq[8] = 1.0 - 2.0 * (x * x + y * y);
+    double M[9];
+    for (int r = 0; r < 3; ++r)
+      for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
+    double Sf[9];
+    for (int r = 0; r < 3; ++r)
+      for (int j = r; j < 3; ++j) {
+        const double v = (M[r * 3] * M[j * 3] + M[r * 3 + 1] * M[j * 3 + 1]) +
+                         M[r * 3 + 2] * M[j * 3 + 2];
+        Sf[r * 3 + j] = v;
+        Sf[j * 3 + r] = v;
+      }
+
+    // EWA Jacobian with the fov clamp, T = J W, 2D covariance and conic
+    const double itz = 1.0 / tz, itz2 = itz * itz, itz3 = itz2 * itz;
+    const double txz = tx * itz, tyz = ty * itz;
+    const double limx = (double)st.fov_clamp * ((0.5 * (double)cam.W) / fx);
+    const double limy = (double)st.fov_clamp * ((0.5 * (double)cam.H) / fy);
+    const bool clampx = (txz > limx) || (txz < -limx);
+    const bool clampy = (tyz > limy) || (tyz < -limy);
+    const double xc = (clampx ? (txz > 0.0 ? limx : -limx) : txz) * tz;
+    const double yc = (clampy ? (tyz > 0.0 ? limy : -limy) : tyz) * tz;
+    const double J00 = fx * itz, J02 = -(fx * xc * itz2);
+    const double J11 = fy * itz, J12 = -(fy * yc * itz2);
+    double Tm[6];
+    for (int j = 0; j < 3; ++j) {
+      Tm[j] = J00 * W[j] + J02 * W[6 + j];
+      Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
     }
-    if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
-  }
-  const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
-  for (int e = 0; e < 3; ++e) gm[e] += (gd[e] - d[e] * dd) / L;
+    double ST0[3], ST1[3];
+    for (int r = 0; r < 3; ++r) {
+      ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
+      ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
+    }
+    const double a = (Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2]) + (double)st.eps2d;
+    const double b = Tm[0] * ST1[0] + Tm[1] * ST1[1] + Tm[2] * ST1[2];
+    const double c = (Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2]) + (double)st.eps2d;
+    const double idet = 1.0 / (a * c - b * b);
+    const double A = c * idet, B = -(b * idet), C = a * idet;
 
-  for (int k = 0; k < 3; ++k) {
-    const int64_t p = (int64_t)k * ld + i;
-    o_means[p] = accumulate ? o_means[p] + (float)gm[k] : (float)gm[k];
-    o_scales[p] = accumulate ? o_scales[p] + (float)gs[k] : (float)gs[k];
+    // conic = Sigma2D^-1: dL/dSigma2D = -conic G conic, G = [[gA, gB/2], [gB/2, gC]]
+    const double gA = r0.z, gB = r0.w, gC = r1.x;
+    const double ga = -(gA * A * A + gB * A * B + gC * B * B);
+    const double gb = -(2.0 * gA * A * B + gB * (A * C + B * B) + 2.0 * gC * B * C);
+    const double gc = -(gA * B * B + gB * B * C + gC * C * C);
+
+    // Sigma2D = T Sigma T^T: dL/dSigma = T^T G2 T, dL/dT = 2 G2 T Sigma
+    double gT0[3], gT1[3];
+    for (int r = 0; r < 3; ++r) {
+      gT0[r] = 2.0 * ga * ST0[r] + gb * ST1[r];
+      gT1[r] = gb * ST0[r] + 2.0 * gc * ST1[r];
+    }
+    double gJ00 = 0.0, gJ02 = 0.0, gJ11 = 0.0, gJ12 = 0.0;
+    for (int j = 0; j < 3; ++j) {
+      gJ00 += gT0[j] * W[j];
+      gJ02 += gT0[j] * W[6 + j];
+      gJ11 += gT1[j] * W[3 + j];
+      gJ12 += gT1[j] * W[6 + j];
+    }
+    double gt[3] = {0.0, 0.0, 0.0};
+    gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
+    if (clampx) {
+      gt[2] += gJ02 * (fx * (txz > 0.0 ? limx : -limx) * itz2);
+    } else {
+      gt[0] += gJ02 * (-fx * itz2);
+      gt[2] += gJ02 * (2.0 * fx * tx * itz3);
+    }
+    if (clampy) {
+      gt[2] += gJ12 * (fy * (tyz > 0.0 ? limy : -limy) * itz2);
+    } else {
+      gt[1] += gJ12 * (-fy * itz2);
+      gt[2] += gJ12 * (2.0 * fy * ty * itz3);
+    }
+    const double gu = r0.x, gv = r0.y;
+    gt[0] += gu * fx * itz;
+    gt[2] += gu * (-fx * tx * itz2);
+    gt[1] += gv * fy * itz;
+    gt[2] += gv * (-fy * ty * itz2);
+    double gm[3];
+    for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
+
+    // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M with
+    // G = dL/dSigma = ga T0^T T0 + gb T0^T T1 + gc T1^T T1 (formed row by row)
+    double gs[3] = {0.0, 0.0, 0.0}, gR[9];
+    for (int r = 0; r < 3; ++r) {
+      double Gr[3];
+      for (int j = 0; j < 3; ++j)
+        Gr[j] = 2.0 * (ga * Tm[r] * Tm[j] + gc * Tm[3 + r] * Tm[3 + j]) +
+                gb * (Tm[r] * Tm[3 + j] + Tm[3 + r] * Tm[j]);
+      for (int k = 0; k < 3; ++k) {
+        const double acc = (Gr[0] * M[k] + Gr[1] * M[3 + k]) + Gr[2] * M[6 + k];
+        gs[k] += acc * Rq[r * 3 + k];
+        gR[r * 3 + k] = acc * s[k];
+      }
+    }
+    double gqn[4];
+    gqn[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
+    gqn[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
+             4.0 * x * (gR[4] + gR[8]);
+    gqn[2] = 2.0 * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
+             4.0 * y * (gR[0] + gR[8]);
+    gqn[3] = 2.0 * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
+             4.0 * z * (gR[0] + gR[4]);
+    const double dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
+    oq[0] = (float)((gqn[0] - w * dot) * inr);
+    oq[1] = (float)((gqn[1] - x * dot) * inr);
+    oq[2] = (float)((gqn[2] - y * dot) * inr);
+    oq[3] = (float)((gqn[3] - z * dot) * inr);
+    for (int k = 0; k < 3; ++k) os[k] = (float)gs[k];
+
+    // view direction and the colour's clamp decision (fp64)
+    double cc[3];
+    for (int j = 0; j < 3; ++j)
+      cc[j] = -((W[j] * (double)cam.t[0] + W[3 + j] * (double)cam.t[1]) +
+                W[6 + j] * (double)cam.t[2]);
+    const double dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
+    L = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+    const double iL = 1.0 / L;
+    for (int j = 0; j < 3; ++j) d[j] = dir[j] * iL;
+    double Y[16];
+    sh_basis64(DEG, d[0], d[1], d[2], Y);
+    double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) raw[ch] = fma(Y[j], (double)shv[j * 3 + ch], raw[ch]);
+    const float gin[3] = {r1.z, r1.w, r2.x};
+    for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0f : gin[ch];
+    for (int k = 0; k < 3; ++k) om[k] = (float)gm[k];
   }
-  for (int k = 0; k < 4; ++k) {
-    const int64_t p = (int64_t)k * ld + i;
-    o_quats[p] = accumulate ? o_quats[p] + (float)gq[k] : (float)gq[k];
+
+  // colour -> SH coefficients (every lane: zeros where culled) and the view
+  // direction's share of the mean gradient
+  if (store) {
+    float Yf[16];
+    sh_basis(DEG, (float)d[0], (float)d[1], (float)d[2], Yf);
+    double gd[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      double wj = 0.0;
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) {
+        const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
+        const float gval = Yf[j] * gcol[ch];
+        o_sh[p] = accumulate ? o_sh[p] + gval : gval;
+        wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
+      }
+      if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
+    }
+    if (vis) {
+      const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+      const double iL = 1.0 / L;
+      for (int e = 0; e < 3; ++e) om[e] = (float)((double)om[e] + (gd[e] - d[e] * dd) * iL);
+    }
+    for (int k = 0; k < 3; ++k) {
+      const int64_t p = (int64_t)k * ld + i;
+      o_means[p] = accumulate ? o_means[p] + om[k] : om[k];
+      o_scales[p] = accumulate ? o_scales[p] + os[k] : os[k];
+    }
+    for (int k = 0; k < 4; ++k) {
+      const int64_t p = (int64_t)k * ld + i;
+      o_quats[p] = accumulate ? o_quats[p] + oq[k] : oq[k];
+    }
+    o_opac[i] = accumulate ? o_opac[i] + oo : oo;
   }
 }
 
@@ -579,9 +619,17 @@ extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, cons
                                             float* splats, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
-  hipLaunchKernelGGL(gs::project_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
-                     deg, means, scales, quats, opac, sh, cam, st, means2d, conics, depths, radii,
-                     colors, tiles, (float4*)splats);
+#define GS_PFWD(D)                                                                         \
+  hipLaunchKernelGGL(gs::project_fwd_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, \
+                     N, ld, means, scales, quats, opac, sh, cam, st, means2d, conics,       \
+                     depths, radii, colors, tiles, (float4*)splats)
+  switch (deg) {
+    case 0: GS_PFWD(0); break;
+    case 1: GS_PFWD(1); break;
+    case 2: GS_PFWD(2); break;
+    default: GS_PFWD(3); break;
+  }
+#undef GS_PFWD
   return hipGetLastError();
 }
 
@@ -594,8 +642,17 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, cons
                                             float* o_sh, int accumulate, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
-  hipLaunchKernelGGL(gs::project_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, N, ld,
-                     deg, means, scales, quats, sh, cam, st, radii, (const float4*)grads2d,
-                     o_means, o_scales, o_quats, o_opac, o_sh, accumulate);
+#define GS_PBWD(D)                                                                         \
+  hipLaunchKernelGGL(gs::project_bwd_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, \
+                     N, ld, means, scales, quats, sh, cam, st, radii,                      \
+                     (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, o_sh,     \
+                     accumulate)
+  switch (deg) {
+    case 0: GS_PBWD(0); break;
+    case 1: GS_PBWD(1); break;
+    case 2: GS_PBWD(2); break;
+    default: GS_PBWD(3); break;
+  }
+#undef GS_PBWD
   return hipGetLastError();
 }
