@@ -14,6 +14,7 @@ seeded poses.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -65,6 +66,26 @@ def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
         # mean, scale, quaternion, opacity and SH gradients out for all
         "project_bwd": 4 * N + (76 + 12 * K) * V + (44 + 12 * K) * N,
     }
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_rasterize_bwd_cluster_1m_1080p.md")
+
+
+def recorded_traffic():
+    """HBM bytes per gs_rasterize_bwd call from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, or None if the compositing source has changed
+    since they were taken (or the record is missing)."""
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        src = b"".join(open(os.path.join(ROOT, "differentiable_rasterization_amd", "csrc", f),
+                            "rb").read() for f in ("gs_common.h", "raster.hip"))
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines()
+                  if l.startswith(("source_sha256: ", "traffic_bytes_per_launch: ")))
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(scene, cams, targets, loss_kind, frames):
@@ -226,9 +247,11 @@ def main():
         useful, issued = alu[dominant]
         t = stage_ms[dominant] * 1e-3
         ach = useful / t / 1e12
+        traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and
+                                          args.config == "cluster_1m_1080p") else None)
         roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
                 "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
-                "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None,
+                "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": traffic,
                 "issued_frac": round(issued / t / 1e12 / VALU_PEAK_TOPS, 4),
                 "slots_per_pair": BWD_SLOTS_PER_PAIR if dominant == "rasterize_bwd"
                 else FWD_SLOTS_PER_PAIR, "work_per_launch": work}
