@@ -189,11 +189,11 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
   GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
-  uint64_t M = 0;
-  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, offsets, workspace, capacity, T, &M, s),
-                            "gs_bin_and_sort(scan)");
+  gs_status st = hip_status(
+      gs_launch_scan(N, tiles_touched, offsets, workspace, capacity, T, num_instances, s),
+      "gs_bin_and_sort(scan)");
   if (st != GS_OK) return st;
-  *num_instances = M;
+  const uint64_t M = *num_instances;
   if (M >= ((uint64_t)1 << 30))
     return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
   if (M > capacity) {

@@ -433,12 +433,12 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
   hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, s, tiles, N, w.scan_sums,
                      offsets);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  uint64_t tot = 0;
-  if ((e = hipMemcpyAsync(&tot, w.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+  // straight into the caller's host word: page-locked memory there makes
+  // this a direct transfer instead of a staged one
+  if ((e = hipMemcpyAsync(total_host, w.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s)) !=
+      hipSuccess)
     return e;
-  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-  *total_host = tot;
-  return hipSuccess;
+  return hipStreamSynchronize(s);
 }
 
 // Duplicate, sort and extract ranges for M instances (M <= capacity).

@@ -2,7 +2,7 @@
 // backward), plus the image loss gradient.
 //
 // One 256-lane workgroup (four wave64) per 16x16 tile, one lane per pixel;
-// a wave covers four pixel rows of the tile.  The tile's depth-sorted list
+// a wave covers one 8x8 quadrant of the tile.  The tile's depth-sorted list
 // is walked in batches of 256 splats that the workgroup first stages into
 // LDS (one gather per lane), after which every lane reads the batch with
 // broadcast LDS loads.  The work is bound by VALU issue (about a dozen
@@ -12,8 +12,9 @@
 //
 // Each staged batch is compacted per wavefront: a splat enters a wave's list
 // only if its alpha >= alpha_min footprint (a padded, conservative box) can
-// reach one of that wave's four pixel rows, so waves skip splats that cannot
-// touch them; the inner loops are branch-free.
+// reach that wave's quadrant, so waves skip splats that cannot touch them;
+// the inner loops are branch-free.  (Square 8x8 quadrants meet ~10% fewer
+// small splats than 16x4 bands of the same area.)
 //
 // The backward walks the same lists back to front from each pixel's last
 // blended entry.  Per splat each wave reduces its 64 pixels' nine gradient
@@ -52,20 +53,24 @@ __device__ inline void stage_splat(SplatLds& s, const float4* __restrict__ rec, 
   ey = c.w;
 }
 
-// Which of the tile's four 4-row bands (one wavefront each) can hold a pixel
-// centre where the splat reaches alpha_min, from the record's padded
+// Pixel of lane `tid` within its tile: wave w covers quadrant (w & 1, w >> 1),
+// lane l its pixel (l & 7, l >> 3).
+__device__ inline int quad_px(int tid) { return ((tid >> 6) & 1) * 8 + (tid & 7); }
+__device__ inline int quad_py(int tid) { return (tid >> 7) * 8 + ((tid >> 3) & 7); }
+
+// Which of the tile's four 8x8 quadrants (one wavefront each) can hold a
+// pixel centre where the splat reaches alpha_min, from the record's padded
 // footprint half-extents (a skipped pair is one the forward skips too).
-__device__ inline uint32_t band_mask(const SplatLds& s, float ex, float ey, int tx0, int ty0) {
+__device__ inline uint32_t quad_mask(const SplatLds& s, float ex, float ey, int tx0, int ty0) {
   if (!(ex >= 0.0f)) return 0u;  // opacity below alpha_min
-  const float x0 = (float)tx0 + 0.5f, x1 = (float)tx0 + 15.5f;
-  if (!(s.u + ex >= x0 && s.u - ex <= x1)) return 0u;
-  uint32_t m = 0u;
-#pragma unroll
-  for (int bnd = 0; bnd < 4; ++bnd) {
-    const float y0 = (float)(ty0 + 4 * bnd) + 0.5f, y1 = y0 + 3.0f;
-    if (s.v + ey >= y0 && s.v - ey <= y1) m |= 1u << bnd;
-  }
-  return m;
+  const float xa = (float)tx0 + 0.5f, ya = (float)ty0 + 0.5f;
+  // columns 0-7 and 8-15, rows 0-7 and 8-15 (pixel centres)
+  const bool c0 = s.u + ex >= xa && s.u - ex <= xa + 7.0f;
+  const bool c1 = s.u + ex >= xa + 8.0f && s.u - ex <= xa + 15.0f;
+  const bool r0 = s.v + ey >= ya && s.v - ey <= ya + 7.0f;
+  const bool r1 = s.v + ey >= ya + 8.0f && s.v - ey <= ya + 15.0f;
+  return (uint32_t)(c0 & r0) | ((uint32_t)(c1 & r0) << 1) | ((uint32_t)(c0 & r1) << 2) |
+         ((uint32_t)(c1 & r1) << 3);
 }
 
 __device__ inline uint64_t lanemask_lt64() {
@@ -73,7 +78,7 @@ __device__ inline uint64_t lanemask_lt64() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Order-preserving compaction of the batch slots by band: s_list[b] receives
+// Order-preserving compaction of the batch slots by quadrant: s_list[b] receives
 // the slots whose mask has bit b, in ascending slot order; s_cnt[b] their
 // number.  Called by all 256 threads.
 __device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[256], uint32_t* s_cnt,
@@ -109,7 +114,7 @@ __device__ inline float splat_power2(const SplatLds& s, float dx, float dy) {
 }
 
 // Work counters (optional diagnostics, one atomic per workgroup):
-//   [0] pixel-splat pairs the kernel evaluated (after the band culling),
+//   [0] pixel-splat pairs the kernel evaluated (after the quadrant culling),
 //   [1] pairs blended (alpha >= alpha_min before the pixel's stop),
 //   [2] pairs the plain method evaluates: per pixel, its tile's entries up to
 //       and including the one that stops it (all of them if none does),
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   const int tile = blockIdx.x;
   const int tx = tile % gx, ty = tile / gx;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int px = tx * kTile + (tid & 15), py = ty * kTile + (tid >> 4);
+  const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
   const float fpx = (float)px + 0.5f, fpy = (float)py + 0.5f;
   const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
       int32_t rad;
       stage_splat(s_sp[tid], splats + 4 * (size_t)id, rad, ex, ey);
       if (kDepth) s_sp[tid].z = depths[id];
-      mask = band_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
+      mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
     compact_bands(mask, s_list, s_cnt, s_wc);
     const int cnt = (int)s_cnt[wave];
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   const int tile = blockIdx.x;
   const int tx = tile % gx, ty = tile / gx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int px = tx * kTile + (tid & 15), py = ty * kTile + (tid >> 4);
+  const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
   const float fpx = (float)px + 0.5f, fpy = (float)py + 0.5f;
   const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       stage_splat(s_sp[tid], rec, my_rad, ex, ey);
       const float4 d = rec[3];
       cA = d.x; cB = d.y; cC = d.z;
-      mask = band_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
+      mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
 #pragma unroll
     for (int q = 0; q < kFields; ++q) {
@@ -504,24 +509,39 @@ __global__ void zero_f32_kernel(float* __restrict__ p) { *p = 0.0f; }
 
 // dL/dimage and (optionally) the summed loss: per-lane partial sums, a DPP
 // row reduction, a cross-wave sum in LDS, then one atomic per workgroup.
-__global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n,
+// float4 accesses when the three arrays are 16-byte aligned; the tail (and
+// unaligned arrays) go element by element.
+__device__ inline float loss_term(int kind, float r, float& acc) {
+  if (kind == 0) {
+    acc = fmaf(r, r, acc);
+    return 2.0f * r;
+  }
+  acc += fabsf(r);
+  return r > 0.0f ? 1.0f : (r < 0.0f ? -1.0f : 0.0f);
+}
+
+__global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n, int64_t n4,
                                                         const float* __restrict__ img,
                                                         const float* __restrict__ tgt,
                                                         float* __restrict__ g,
                                                         float* __restrict__ loss) {
   __shared__ float s_w[16];
   float acc = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const float r = img[i] - tgt[i];
-    if (kind == 0) {
-      g[i] = 2.0f * r;
-      acc = fmaf(r, r, acc);
-    } else {
-      g[i] = r > 0.0f ? 1.0f : (r < 0.0f ? -1.0f : 0.0f);
-      acc += fabsf(r);
-    }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const float4* img4 = (const float4*)img;
+  const float4* tgt4 = (const float4*)tgt;
+  float4* g4 = (float4*)g;
+  for (int64_t i = t0; i < n4; i += stride) {
+    const float4 x = img4[i], y = tgt4[i];
+    float4 o;
+    o.x = loss_term(kind, x.x - y.x, acc);
+    o.y = loss_term(kind, x.y - y.y, acc);
+    o.z = loss_term(kind, x.z - y.z, acc);
+    o.w = loss_term(kind, x.w - y.w, acc);
+    g4[i] = o;
   }
+  for (int64_t i = 4 * n4 + t0; i < n; i += stride) g[i] = loss_term(kind, img[i] - tgt[i], acc);
   if (!loss) return;
   acc = row_total_lane15(acc);
   const int lane = threadIdx.x & 63;
@@ -602,9 +622,11 @@ extern "C" hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img,
     if (e != hipSuccess) return e;
   }
   if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(gs::loss_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, kind, n, img,
-                     tgt, g, loss);
+  const bool al = (((uintptr_t)img | (uintptr_t)tgt | (uintptr_t)g) & 15u) == 0;
+  const int64_t n4 = al ? n / 4 : 0;
+  int64_t blocks = ((al ? n4 : n) + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(gs::loss_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, kind, n, n4,
+                     img, tgt, g, loss);
   return hipGetLastError();
 }

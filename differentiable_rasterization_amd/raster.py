@@ -152,16 +152,20 @@ def gs_bin_and_sort_workspace_size(N, capacity, width, height) -> int:
 
 
 def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
-                    capacity, keys, ids, tile_ranges, workspace, workspace_bytes, stream=None):
-    """Returns (status, M); GS_ERR_CAPACITY is returned, not raised."""
+                    capacity, keys, ids, tile_ranges, workspace, workspace_bytes, stream=None,
+                    num_instances=None):
+    """Returns (status, M); GS_ERR_CAPACITY is returned, not raised.
+    ``num_instances``: optional page-locked one-element int64 host tensor that
+    receives M (saves the runtime a staging copy)."""
     lib = load()
     M = C.c_uint64(0)
+    out = C.byref(M) if num_instances is None else _p(num_instances)
     st = lib.gs_bin_and_sort(N, ld, _p(means2d), _p(radii), _p(depths), _p(tiles_touched),
-                             width, height, _p(offsets), capacity, C.byref(M), _p(keys), _p(ids),
+                             width, height, _p(offsets), capacity, out, _p(keys), _p(ids),
                              _p(tile_ranges), _p(workspace), workspace_bytes, _stream(stream))
     if st not in (GS_OK, GS_ERR_CAPACITY):
         _check(st)
-    return st, int(M.value)
+    return st, int(M.value) if num_instances is None else int(num_instances[0])
 
 
 def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, background,
@@ -277,6 +281,8 @@ class Frame:
         self.g_quats, self.g_sh = z((4, ld), f32), z((3 * self.K, ld), f32)
         self.dL_dimage = z((height, width, 3), f32)
         self.loss = z((1,), f32)
+        # page-locked host word for the instance count (allocated pinned)
+        self.m_host = torch.zeros((1,), dtype=torch.int64, pin_memory=True)
         self.M = 0
         self._alloc_sort(capacity if capacity else max(1024, 4 * ld))
 
@@ -302,12 +308,13 @@ class Frame:
     def bin_and_sort(self, g: Gaussians):
         st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
                                 self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
-                                self.ranges, self.ws, self.ws_bytes)
+                                self.ranges, self.ws, self.ws_bytes, num_instances=self.m_host)
         if st == GS_ERR_CAPACITY:
             self._alloc_sort(int(M * 1.25) + 1024)
             st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
                                     self.W, self.H, self.offsets, self.capacity, self.keys,
-                                    self.ids, self.ranges, self.ws, self.ws_bytes)
+                                    self.ids, self.ranges, self.ws, self.ws_bytes,
+                                    num_instances=self.m_host)
             _check(st)
         self.M = M
         return M

@@ -145,7 +145,8 @@ GS_API size_t gs_bin_and_sort_workspace_size(int64_t N, uint64_t capacity, int32
 
 /* Stages 2-3 — binning and sort.  offsets = exclusive scan of tiles_touched
  * (Gaussian order); M = total.  *num_instances (HOST) receives M; this is the
- * one device-to-host read of a frame.  If M > capacity the call returns
+ * one device-to-host read of a frame (page-locked host memory there saves a
+ * staging copy).  If M > capacity the call returns
  * GS_ERR_CAPACITY with offsets valid and keys untouched: grow the buffers and
  * call again.  Otherwise every visible Gaussian i is duplicated once per
  * touched tile (row-major within its rect) at slot offsets[i] + k with key
