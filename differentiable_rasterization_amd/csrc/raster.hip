@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
       mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
     compact_bands(mask, s_list, s_cnt, s_wc);
-    const int cnt = (int)s_cnt[wave];
+    // wave-uniform trip count: the loop runs on scalar registers
+    const int cnt = __builtin_amdgcn_readfirstlane((int)s_cnt[wave]);
     const uint32_t base = b - start + 1u;
     if (__ballot(!done) == 0ull) continue;
     for (int i = 0; i < cnt; ++i) {
@@ -296,12 +297,24 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     float bg1, float bg2, Settings st, const float* __restrict__ final_T,
     const uint32_t* __restrict__ last_idx, const float* __restrict__ dL_dimage,
     float4* __restrict__ partials, uint64_t capacity, uint64_t* __restrict__ cnt) {
-  __shared__ SplatLds s_sp[256];
-  __shared__ uint8_t s_list[4][256];
-  __shared__ uint32_t s_cnt[4];
-  __shared__ uint32_t s_wc[4][4];
-  __shared__ float s_acc[2][kFields][256];  // one set per pair of wavefronts
-  __shared__ uint32_t s_maxlast;
+  // one LDS block with the staged splats at offset 0, so that the inner
+  // loop's three reads of a splat share one address (read2 immediates reach
+  // only 2 KB past it)
+  struct Lds {
+    SplatLds sp[256];
+    float acc[2][kFields][256];  // one set per pair of wavefronts
+    uint8_t list[4][256];
+    uint32_t cnt[4];
+    uint32_t wc[4][4];
+    uint32_t maxlast;
+  };
+  __shared__ Lds lds;
+  SplatLds* s_sp = lds.sp;
+  auto& s_acc = lds.acc;
+  auto& s_list = lds.list;
+  uint32_t* s_cnt = lds.cnt;
+  auto& s_wc = lds.wc;
+  uint32_t& s_maxlast = lds.maxlast;
   const int tile = blockIdx.x;
   const int tx = tile % gx, ty = tile / gx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -370,19 +383,20 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       s_acc[1][q][tid] = 0.0f;
     }
     compact_bands(mask, s_list, s_cnt, s_wc);
-    const int cnt_w = (int)s_cnt[wave];
-    const uint32_t relbase = b_end - 1u - start;
+    const int cnt_w = __builtin_amdgcn_readfirstlane((int)s_cnt[wave]);
+    // batch slot k holds list position rel = b_end - 1 - start - k; the pixel
+    // blended it only if rel < last, i.e. k > kthr
+    const int kthr = (int)(b_end - 1u - start) - (int)last;
     for (int i = 0; i < cnt_w; ++i) {
       const int k = s_list[wave][i];
       const SplatLds& s = s_sp[k];
-      const uint32_t rel = relbase - (uint32_t)k;  // list position in the tile
       const float dx = fpx - s.u, dy = fpy - s.v;
       const float p2 = splat_power2(s, dx, dy);
       const float G = __builtin_amdgcn_exp2f(p2);
       const float oG = s.o * G;
       const bool clamped = oG > amax;
       const float alpha = clamped ? amax : oG;
-      const bool hit = (rel < last) & !(alpha < amin);
+      const bool hit = (k > kthr) & !(alpha < amin);
       const float rom = __builtin_amdgcn_rcpf(1.0f - alpha);
       T = hit ? T * rom : T;  // transmittance in front of this splat
       const float wgt = hit ? alpha * T : 0.0f;
