@@ -192,6 +192,7 @@ constexpr int kMaxPasses = 8;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagPrefix = 2u << 30;
 constexpr uint32_t kCountMask = (1u << 30) - 1u;
+constexpr int kLookback = 8;  // partitions examined per look-back step
 
 // Global histogram of every pass's digit (one LDS histogram per pass).
 __global__ __launch_bounds__(256) void sort_histogram_kernel(const uint64_t* __restrict__ keys,
@@ -297,18 +298,32 @@ __global__ __launch_bounds__(256) void sort_pass_kernel(
     __hip_atomic_store(&st[d], kFlagPrefix | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     __hip_atomic_store(&st[d], kFlagAgg | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // look back kLookback partitions per step (all loads in flight at once):
+    // add aggregates up to the nearest inclusive prefix; resume at the first
+    // partition that has published nothing yet.  Partition 0 always
+    // publishes a prefix, so the walk ends there at the latest.
     int64_t p = (int64_t)part - 1;
     while (p >= 0) {
-      const uint32_t s = __hip_atomic_load(&status[(size_t)p * kRadix + d], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t flag = s & ~kCountMask;
-      if (flag == 0u) {
-        __builtin_amdgcn_s_sleep(1);
-        continue;
+      uint32_t sv[kLookback];
+#pragma unroll
+      for (int j = 0; j < kLookback; ++j)
+        sv[j] = (p - j >= 0) ? __hip_atomic_load(&status[(size_t)(p - j) * kRadix + d],
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : kFlagPrefix;
+      int j = 0;
+      bool done = false;
+      for (; j < kLookback; ++j) {
+        const uint32_t flag = sv[j] & ~kCountMask;
+        if (flag == 0u) break;
+        prefix += sv[j] & kCountMask;
+        if (flag == kFlagPrefix) {
+          done = true;
+          break;
+        }
       }
-      prefix += s & kCountMask;
-      if (flag == kFlagPrefix) break;
-      --p;
+      if (done) break;
+      p -= j;
+      if (j < kLookback) __builtin_amdgcn_s_sleep(1);
     }
     __hip_atomic_store(&st[d], kFlagPrefix | (prefix + mine), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
