@@ -408,11 +408,54 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   // both kinds of lanes store through the same instructions below, so a
   // cache line of a plane is written once
   const bool store = vis || !accumulate;
+
+  // Phase 1, the SH side (done first so that the 3K SH registers are free
+  // before the fp64 geometry chain): view direction, the colour's clamp
+  // decision (fp64), SH coefficient gradients (fp32 products; zeros where
+  // culled) and the view direction's share of the mean gradient.
+  double d[3] = {0.0, 0.0, 1.0}, iL = 1.0, vterm[3] = {0.0, 0.0, 0.0};
+  float gcol[3] = {0.0f, 0.0f, 0.0f};
+  if (vis) {
+    double cc[3];
+    for (int j = 0; j < 3; ++j)
+      cc[j] = -(((double)cam.R[j] * (double)cam.t[0] + (double)cam.R[3 + j] * (double)cam.t[1]) +
+                (double)cam.R[6 + j] * (double)cam.t[2]);
+    const double dir[3] = {(double)pm[0] - cc[0], (double)pm[1] - cc[1], (double)pm[2] - cc[2]};
+    iL = 1.0 / sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+    for (int j = 0; j < 3; ++j) d[j] = dir[j] * iL;
+    double Y[16];
+    sh_basis64(DEG, d[0], d[1], d[2], Y);
+    double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) raw[ch] = fma(Y[j], (double)shv[j * 3 + ch], raw[ch]);
+    const float gin[3] = {r1.z, r1.w, r2.x};
+    for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0f : gin[ch];
+  }
+  if (store) {
+    float Yf[16];
+    sh_basis(DEG, (float)d[0], (float)d[1], (float)d[2], Yf);
+    double gd[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      double wj = 0.0;
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) {
+        const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
+        const float gval = Yf[j] * gcol[ch];
+        o_sh[p] = accumulate ? o_sh[p] + gval : gval;
+        wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
+      }
+      if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
+    }
+    const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+    for (int e = 0; e < 3; ++e) vterm[e] = (gd[e] - d[e] * dd) * iL;
+  }
+
+  // Phase 2, the geometry chain in fp64.
   float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
   float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
-  float gcol[3] = {0.0f, 0.0f, 0.0f};
-  double d[3] = {0.0, 0.0, 1.0}, L = 1.0;
-
   if (vis) {
     // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
     oo = r1.y;
@@ -551,50 +594,9 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     oq[3] = (float)((gqn[3] - z * dot) * inr);
     for (int k = 0; k < 3; ++k) os[k] = (float)gs[k];
 
-    // view direction and the colour's clamp decision (fp64)
-    double cc[3];
-    for (int j = 0; j < 3; ++j)
-      cc[j] = -((W[j] * (double)cam.t[0] + W[3 + j] * (double)cam.t[1]) +
-                W[6 + j] * (double)cam.t[2]);
-    const double dir[3] = {m[0] - cc[0], m[1] - cc[1], m[2] - cc[2]};
-    L = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-    const double iL = 1.0 / L;
-    for (int j = 0; j < 3; ++j) d[j] = dir[j] * iL;
-    double Y[16];
-    sh_basis64(DEG, d[0], d[1], d[2], Y);
-    double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-#pragma unroll
-      for (int ch = 0; ch < 3; ++ch) raw[ch] = fma(Y[j], (double)shv[j * 3 + ch], raw[ch]);
-    const float gin[3] = {r1.z, r1.w, r2.x};
-    for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0f : gin[ch];
-    for (int k = 0; k < 3; ++k) om[k] = (float)gm[k];
+    for (int k = 0; k < 3; ++k) om[k] = (float)(gm[k] + vterm[k]);
   }
-
-  // colour -> SH coefficients (every lane: zeros where culled) and the view
-  // direction's share of the mean gradient
   if (store) {
-    float Yf[16];
-    sh_basis(DEG, (float)d[0], (float)d[1], (float)d[2], Yf);
-    double gd[3] = {0.0, 0.0, 0.0};
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      double wj = 0.0;
-#pragma unroll
-      for (int ch = 0; ch < 3; ++ch) {
-        const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
-        const float gval = Yf[j] * gcol[ch];
-        o_sh[p] = accumulate ? o_sh[p] + gval : gval;
-        wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
-      }
-      if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
-    }
-    if (vis) {
-      const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
-      const double iL = 1.0 / L;
-      for (int e = 0; e < 3; ++e) om[e] = (float)((double)om[e] + (gd[e] - d[e] * dd) * iL);
-    }
     for (int k = 0; k < 3; ++k) {
       const int64_t p = (int64_t)k * ld + i;
       o_means[p] = accumulate ? o_means[p] + om[k] : om[k];
