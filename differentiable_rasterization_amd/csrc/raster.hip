@@ -53,6 +53,30 @@ __device__ inline void stage_splat(SplatLds& s, const float4* __restrict__ rec, 
   ey = c.w;
 }
 
+// Workgroup -> tile mapping aware of the eight XCDs (each with its own L2):
+// workgroup b runs on XCD b % 8, so each XCD is handed whole 2x2 groups of
+// tiles (group x, x + 8, x + 16, ... for XCD x).  A splat that overlaps
+// neighbouring tiles of a group is then fetched into one L2, while groups
+// stay interleaved over the image for load balance.  Workgroups past the
+// tile grid return at once.
+constexpr int kXcds = 8, kGroupW = 2, kGroupH = 2, kGroup = kGroupW * kGroupH;
+
+__host__ __device__ inline int tile_groups(int gx, int gy) {
+  return ((gx + kGroupW - 1) / kGroupW) * ((gy + kGroupH - 1) / kGroupH);
+}
+__host__ inline unsigned tile_grid_blocks(int gx, int gy) {
+  const int ng = tile_groups(gx, gy);
+  return (unsigned)(((ng + kXcds - 1) / kXcds) * kXcds * kGroup);
+}
+__device__ inline bool block_tile(int b, int gx, int gy, int& tx, int& ty) {
+  const int xcd = b % kXcds, l = b / kXcds;
+  const int group = (l / kGroup) * kXcds + xcd, within = l % kGroup;
+  const int ggx = (gx + kGroupW - 1) / kGroupW;
+  tx = (group % ggx) * kGroupW + within % kGroupW;
+  ty = (group / ggx) * kGroupH + within / kGroupW;
+  return tx < gx && ty < gy;
+}
+
 // Pixel of lane `tid` within its tile: wave w covers quadrant (w & 1, w >> 1),
 // lane l its pixel (l & 7, l >> 3).
 __device__ inline int quad_px(int tid) { return ((tid >> 6) & 1) * 8 + (tid & 7); }
@@ -144,8 +168,9 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   __shared__ uint8_t s_list[4][256];
   __shared__ uint32_t s_cnt[4];
   __shared__ uint32_t s_wc[4][4];
-  const int tile = blockIdx.x;
-  const int tx = tile % gx, ty = tile / gx;
+  int tx, ty;
+  if (!block_tile((int)blockIdx.x, gx, grid_dim(H), tx, ty)) return;
+  const int tile = ty * gx + tx;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
@@ -315,8 +340,9 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   uint32_t* s_cnt = lds.cnt;
   auto& s_wc = lds.wc;
   uint32_t& s_maxlast = lds.maxlast;
-  const int tile = blockIdx.x;
-  const int tx = tile % gx, ty = tile / gx;
+  int tx, ty;
+  if (!block_tile((int)blockIdx.x, gx, grid_dim(H), tx, ty)) return;
+  const int tile = ty * gx + tx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
@@ -577,7 +603,7 @@ extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t*
                                            float* final_T, uint32_t* last_idx, float* out_depth,
                                            float* out_alpha, uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
-  const dim3 grid((unsigned)(gx * gy)), block(256);
+  const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
   const float4* sp = (const float4*)splats;
   if (counters) {
     if (out_depth)
@@ -610,7 +636,7 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, cons
                                            uint64_t capacity, float* grads2d, uint64_t* counters,
                                            hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
-  const dim3 grid((unsigned)(gx * gy)), block(256);
+  const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
   const float4* sp = (const float4*)splats;
   float4* part = (float4*)partials;
   if (counters)
