@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--config", default="cluster_1m_1080p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=4)
+    ap.add_argument("--absgrad", action="store_true",
+                    help="run the compositing backward with the absolute-gradient sums")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -165,7 +167,7 @@ def main():
         raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i % P], fr.dL_dimage, None)
         if ev is not None:
             ev[4].record()
-        fr.rasterize_backward(g)
+        fr.rasterize_backward(g, absgrad=args.absgrad)
         if ev is not None:
             ev[5].record()
         fr.project_backward(g)
@@ -247,7 +249,7 @@ def main():
         useful, issued = alu[dominant]
         t = stage_ms[dominant] * 1e-3
         ach = useful / t / 1e12
-        traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and
+        traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and not args.absgrad and
                                           args.config == "cluster_1m_1080p") else None)
         roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
                 "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
@@ -268,7 +270,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "gaussians": N, "width": W, "height": H,
                    "sh_degree": scene.sh_degree, "poses": P, "loss": loss_kind,
-                   "visible": int(avg["V"]), "instances": int(avg["M"])},
+                   "visible": int(avg["V"]), "instances": int(avg["M"]),
+                   "absgrad": bool(args.absgrad)},
         "fwd_fps": round(1e3 / fwd_ms, 2),
         "sort_keys_per_s": round(avg["M"] / (stage_ms["bin_and_sort"] * 1e-3), 1),
         "stages": stages,

@@ -39,7 +39,7 @@ hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t*
                                 const uint32_t* tiles, const float* bg, const gs::Settings& st,
                                 const float* final_T, const uint32_t* last_idx,
                                 const float* dL_dimage, float* partials, uint64_t capacity,
-                                float* grads2d, uint64_t* counters, hipStream_t s);
+                                float* grads2d, int absgrad, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
 }
@@ -236,14 +236,15 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            uint64_t num_instances, const float* background,
                            const gs_settings* settings, const float* final_T,
                            const uint32_t* last_idx, const float* dL_dimage, float* partials,
-                           uint64_t partials_capacity, float* grads2d, uint64_t* counters,
-                           void* stream) {
+                           uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                           uint64_t* counters, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_image(width, height));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(background != nullptr, "background is NULL");
   GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
   GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
+  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
   if (N > 0) {
     GS_REQUIRE(ids && splats && offsets && tiles_touched && grads2d,
                "NULL splat, offset or gradient pointer");
@@ -256,7 +257,7 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
   return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
-                                         grads2d, counters, (hipStream_t)stream),
+                                         grads2d, absgrad, counters, (hipStream_t)stream),
                     "gs_rasterize_bwd");
 }
 

@@ -131,10 +131,15 @@ __device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[256], uint
 
 // log2 of the Gaussian at pixel offset (dx, dy): -log2e * q / 2, from the
 // completed square (never positive).
-__device__ inline float splat_power2(const SplatLds& s, float dx, float dy) {
-  const float e1 = fmaf(s.l11, dx, s.l21 * dy);
-  const float e2 = s.l22 * dy;
+__device__ inline float splat_power2(const SplatLds& s, float dx, float dy, float& e1,
+                                     float& e2) {
+  e1 = fmaf(s.l11, dx, s.l21 * dy);
+  e2 = s.l22 * dy;
   return -fmaf(e1, e1, e2 * e2);
+}
+__device__ inline float splat_power2(const SplatLds& s, float dx, float dy) {
+  float e1, e2;
+  return splat_power2(s, dx, dy, e1, e2);
 }
 
 // Work counters (optional diagnostics, one atomic per workgroup):
@@ -271,20 +276,23 @@ __device__ inline float row_total_lane15(float v) {
 }
 #undef GS_ROW_ADD
 
-// Sums f[0..8] over the wavefront and adds field q to dst[q * stride] (LDS,
-// atomically).  Callers give each pair of wavefronts its own slots: from a
-// zero start, two float additions give the same bits in either order, so the
-// result does not depend on which wavefront of the pair came first.
-__device__ inline void reduce9_add(const float f[9], float* dst, int stride) {
+// Sums f[0..8] (and f[9], f[10] when kAbs) over the wavefront and adds field
+// q to dst[q * stride] (LDS, atomically).  Callers give each pair of
+// wavefronts its own slots: from a zero start, two float additions give the
+// same bits in either order, so the result does not depend on which
+// wavefront of the pair came first.
+template <bool kAbs>
+__device__ inline void reduce_add(const float* f, float* dst, int stride) {
   const float s01 = swap_add32(f[0], f[1]);
   const float s23 = swap_add32(f[2], f[3]);
   const float s45 = swap_add32(f[4], f[5]);
   const float s67 = swap_add32(f[6], f[7]);
-  const float s8 = swap_add32(f[8], 0.0f);
-  // rows of t0: fields 0, 2, 1, 3; of t1: 4, 6, 5, 7; of t2: 8, -, -, -
+  const float s89 = swap_add32(f[8], kAbs ? f[9] : 0.0f);
+  const float sA = kAbs ? swap_add32(f[10], 0.0f) : 0.0f;
+  // rows of t0: fields 0, 2, 1, 3; of t1: 4, 6, 5, 7; of t2: 8, 10, 9, -
   float t0 = swap_add16(s01, s23);
   float t1 = swap_add16(s45, s67);
-  float t2 = swap_add16(s8, 0.0f);
+  float t2 = swap_add16(s89, sA);
   t0 = row_total_lane15(t0);
   t1 = row_total_lane15(t1);
   t2 = row_total_lane15(t2);
@@ -295,6 +303,8 @@ __device__ inline void reduce9_add(const float f[9], float* dst, int stride) {
     atomicAdd(&dst[q * stride], t0);
     atomicAdd(&dst[(4 + q) * stride], t1);
     if (row == 0) atomicAdd(&dst[8 * stride], t2);
+    if (kAbs && row == 1) atomicAdd(&dst[10 * stride], t2);
+    if (kAbs && row == 2) atomicAdd(&dst[9 * stride], t2);
   }
 }
 
@@ -303,7 +313,13 @@ __device__ inline void reduce9_add(const float f[9], float* dst, int stride) {
 // mean and conic gradients follow after the reduction:
 //   dL/du = -2 (A Sx + B Sy), dL/dv = -2 (B Sx + C Sy),
 //   dL/dA = Sxx, dL/dB = 2 Sxy, dL/dC = Syy.
+// With absgrad, two more: the per-pixel |dL/du| and |dL/dv| summed over the
+// pixels (the absolute-gradient statistic of densification).
 constexpr int kFields = 9;
+constexpr int kFieldsAbs = 11;
+// |dL/du| = 2 |m (A dx + B dy)| and A dx + B dy = l11 e1 / k^2 with the
+// record's factors scaled by k = sqrt(log2(e) / 2): 2 / k^2 = 4 ln 2
+constexpr float kAbsScale = 2.772588722239781f;
 
 // Slot of Gaussian `id`'s instance for tile (tx, ty): its offset plus the
 // tile's row-major index inside the Gaussian's rect.
@@ -315,7 +331,7 @@ __device__ inline uint64_t instance_slot(float u, float v, int32_t radius, uint3
   return (uint64_t)offset + (uint64_t)((ty - y0) * w + (tx - x0));
 }
 
-template <bool kStats>
+template <bool kStats, bool kAbs>
 __global__ __launch_bounds__(256) void raster_bwd_kernel(
     int W, int H, int gx, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids,
     const float4* __restrict__ splats, const uint32_t* __restrict__ offsets, float bg0,
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   // only 2 KB past it)
   struct Lds {
     SplatLds sp[256];
-    float acc[2][kFields][256];  // one set per pair of wavefronts
+    float acc[2][kAbs ? kFieldsAbs : kFields][256];  // one set per pair of wavefronts
     uint8_t list[4][256];
     uint32_t cnt[4];
     uint32_t wc[4][4];
@@ -403,8 +419,9 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       cA = d.x; cB = d.y; cC = d.z;
       mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
+    constexpr int kF = kAbs ? kFieldsAbs : kFields;
 #pragma unroll
-    for (int q = 0; q < kFields; ++q) {
+    for (int q = 0; q < kF; ++q) {
       s_acc[0][q][tid] = 0.0f;
       s_acc[1][q][tid] = 0.0f;
     }
@@ -417,7 +434,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const int k = s_list[wave][i];
       const SplatLds& s = s_sp[k];
       const float dx = fpx - s.u, dy = fpy - s.v;
-      const float p2 = splat_power2(s, dx, dy);
+      float e1, e2;
+      const float p2 = splat_power2(s, dx, dy, e1, e2);
       const float G = __builtin_amdgcn_exp2f(p2);
       const float oG = s.o * G;
       const bool clamped = oG > amax;
@@ -426,7 +444,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const float rom = __builtin_amdgcn_rcpf(1.0f - alpha);
       T = hit ? T * rom : T;  // transmittance in front of this splat
       const float wgt = hit ? alpha * T : 0.0f;
-      float f[kFields];
+      float f[kF];
       f[6] = g0 * wgt;
       f[7] = g1 * wgt;
       f[8] = g2 * wgt;
@@ -447,20 +465,24 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       f[2] = mx * dx;
       f[3] = mx * dy;
       f[4] = my * dy;
+      if (kAbs) {
+        f[9] = fabsf(m * s.l11 * e1) * kAbsScale;
+        f[10] = fabsf(m * fmaf(s.l21, e1, s.l22 * e2)) * kAbsScale;
+      }
       if (kStats) {
         n_eval += inside ? 1u : 0u;
         n_hit += hit ? 1u : 0u;
       }
       if (__ballot(hit) != 0ull) {
         if (kStats) n_red += (lane == 0) ? 1u : 0u;
-        reduce9_add(f, &s_acc[wave >> 1][0][k], 256);
+        reduce_add<kAbs>(f, &s_acc[wave >> 1][0][k], 256);
       }
     }
     __syncthreads();
     if (tid < n) {
-      float acc[kFields];
+      float acc[kF];
 #pragma unroll
-      for (int q = 0; q < kFields; ++q) acc[q] = s_acc[0][q][tid] + s_acc[1][q][tid];
+      for (int q = 0; q < kF; ++q) acc[q] = s_acc[0][q][tid] + s_acc[1][q][tid];
       // moments -> gradients of u, v and the conic
       const float gu = -2.0f * fmaf(cA, acc[0], cB * acc[1]);
       const float gv = -2.0f * fmaf(cB, acc[0], cC * acc[1]);
@@ -469,7 +491,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       if (slot < capacity) {
         partials[4 * slot + 0] = make_float4(gu, gv, acc[2], 2.0f * acc[3]);
         partials[4 * slot + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        partials[4 * slot + 2] = make_float4(acc[8], 0.0f, 0.0f, 0.0f);
+        partials[4 * slot + 2] =
+            make_float4(acc[8], kAbs ? acc[kF - 2] : 0.0f, kAbs ? acc[kF - 1] : 0.0f, 0.0f);
       }
     }
     b_end = b_begin;
@@ -484,17 +507,17 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
 // workgroup with a fixed-shape tree.
 constexpr uint32_t kSmallSeg = 32;
 
-__device__ inline void add_rec(float a[kFields], const float4* __restrict__ p) {
+__device__ inline void add_rec(float a[kFieldsAbs], const float4* __restrict__ p) {
   const float4 x = p[0], y = p[1], z = p[2];
   a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
   a[4] += y.x; a[5] += y.y; a[6] += y.z; a[7] += y.w;
-  a[8] += z.x;
+  a[8] += z.x; a[9] += z.y; a[10] += z.z;
 }
 
-__device__ inline void store_rec(float4* __restrict__ r, const float a[kFields]) {
+__device__ inline void store_rec(float4* __restrict__ r, const float a[kFieldsAbs]) {
   r[0] = make_float4(a[0], a[1], a[2], a[3]);
   r[1] = make_float4(a[4], a[5], a[6], a[7]);
-  r[2] = make_float4(a[8], 0.0f, 0.0f, 0.0f);
+  r[2] = make_float4(a[8], a[9], a[10], 0.0f);
 }
 
 __global__ __launch_bounds__(256) void reduce_partials_kernel(
@@ -502,7 +525,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     const float4* __restrict__ partials, float4* __restrict__ grads2d) {
   __shared__ uint32_t s_big[256];
   __shared__ uint32_t s_nbig;
-  __shared__ float s_red[kFields][256];
+  __shared__ float s_red[kFieldsAbs][256];
   const int t = threadIdx.x;
   const int64_t i = (int64_t)blockIdx.x * 256 + t;
   if (t == 0) s_nbig = 0;
@@ -512,7 +535,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     if (cnt > kSmallSeg) {
       s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)t;
     } else if (cnt > 0) {
-      float a[kFields] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+      float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
       const uint64_t base = offsets[i];
       for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
       store_rec(grads2d + 4 * i, a);
@@ -524,21 +547,21 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     const int64_t gi = (int64_t)blockIdx.x * 256 + s_big[b];
     const uint32_t cnt = tiles[gi];
     const uint64_t base = offsets[gi];
-    float a[kFields] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     for (uint32_t k = (uint32_t)t; k < cnt; k += 256u) add_rec(a, partials + 4 * (base + k));
 #pragma unroll
-    for (int q = 0; q < kFields; ++q) s_red[q][t] = a[q];
+    for (int q = 0; q < kFieldsAbs; ++q) s_red[q][t] = a[q];
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
       if (t < h)
 #pragma unroll
-        for (int q = 0; q < kFields; ++q) s_red[q][t] += s_red[q][t + h];
+        for (int q = 0; q < kFieldsAbs; ++q) s_red[q][t] += s_red[q][t + h];
       __syncthreads();
     }
     if (t == 0) {
-      float r[kFields];
+      float r[kFieldsAbs];
 #pragma unroll
-      for (int q = 0; q < kFields; ++q) r[q] = s_red[q][0];
+      for (int q = 0; q < kFieldsAbs; ++q) r[q] = s_red[q][0];
       store_rec(grads2d + 4 * gi, r);
     }
     __syncthreads();
@@ -633,20 +656,22 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, cons
                                            const float* bg, const gs::Settings& st,
                                            const float* final_T, const uint32_t* last_idx,
                                            const float* dL_dimage, float* partials,
-                                           uint64_t capacity, float* grads2d, uint64_t* counters,
-                                           hipStream_t s) {
+                                           uint64_t capacity, float* grads2d, int absgrad,
+                                           uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
   const float4* sp = (const float4*)splats;
   float4* part = (float4*)partials;
-  if (counters)
-    hipLaunchKernelGGL(gs::raster_bwd_kernel<true>, grid, block, 0, s, W, H, gx, ranges, ids, sp,
-                       offsets, bg[0], bg[1], bg[2], st, final_T, last_idx, dL_dimage, part,
-                       capacity, counters);
-  else
-    hipLaunchKernelGGL(gs::raster_bwd_kernel<false>, grid, block, 0, s, W, H, gx, ranges, ids, sp,
-                       offsets, bg[0], bg[1], bg[2], st, final_T, last_idx, dL_dimage, part,
-                       capacity, nullptr);
+#define GS_RBWD(STATS, ABS)                                                                 \
+  hipLaunchKernelGGL((gs::raster_bwd_kernel<STATS, ABS>), grid, block, 0, s, W, H, gx, ranges, \
+                     ids, sp, offsets, bg[0], bg[1], bg[2], st, final_T, last_idx,          \
+                     dL_dimage, part, capacity, counters)
+  if (counters) {
+    if (absgrad) GS_RBWD(true, true); else GS_RBWD(true, false);
+  } else {
+    if (absgrad) GS_RBWD(false, true); else GS_RBWD(false, false);
+  }
+#undef GS_RBWD
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || N == 0) return e;
   hipLaunchKernelGGL(gs::reduce_partials_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,

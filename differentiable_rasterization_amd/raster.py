@@ -77,7 +77,7 @@ def load():
     lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 13
     lib.gs_rasterize_bwd.restype = C.c_int
     lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 5 + [u64] + [P] * 6 + \
-        [u64, P, P, P]
+        [u64, P, i32, P, P]
     lib.gs_project_bwd.restype = C.c_int
     lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 2 + [P] * 5 + \
         [i32, P]
@@ -181,14 +181,14 @@ def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, bac
 
 def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, splats, offsets, tiles_touched,
                      num_instances, background, settings, final_T, last_idx, dL_dimage, partials,
-                     partials_capacity, grads2d, counters=None, stream=None):
+                     partials_capacity, grads2d, absgrad=0, counters=None, stream=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
                                 _p(offsets), _p(tiles_touched), int(num_instances), bg,
                                 C.byref(settings), _p(final_T), _p(last_idx), _p(dL_dimage),
-                                _p(partials), int(partials_capacity), _p(grads2d), _p(counters),
-                                _stream(stream)))
+                                _p(partials), int(partials_capacity), _p(grads2d),
+                                int(absgrad), _p(counters), _stream(stream)))
 
 
 def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii, grads2d,
@@ -334,18 +334,18 @@ class Frame:
         gs_image_loss_grad(kind, self.W * self.H * 3, self.image, target, self.dL_dimage,
                            self.loss if with_loss else None)
 
-    def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None):
+    def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None, absgrad=False):
         dl = self.dL_dimage if dL_dimage is None else dL_dimage
         gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
                          self.offsets, self.tiles, self.M, self.background, self.settings,
                          self.final_T, self.last_idx, dl, self.partials, self.capacity,
-                         self.grads2d, counters)
+                         self.grads2d, absgrad=int(bool(absgrad)), counters=counters)
 
     def project_backward(self, g: Gaussians, accumulate=0):
         gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
                        self.settings, self.radii, self.grads2d, self.g_means, self.g_scales,
                        self.g_quats, self.g_opacities, self.g_sh, accumulate)
 
-    def backward(self, g: Gaussians, dL_dimage=None, accumulate=0):
-        self.rasterize_backward(g, dL_dimage)
+    def backward(self, g: Gaussians, dL_dimage=None, accumulate=0, absgrad=False):
+        self.rasterize_backward(g, dL_dimage, absgrad=absgrad)
         self.project_backward(g, accumulate)

@@ -50,7 +50,8 @@
  *       2D gradient record (gs_rasterize_bwd -> gs_project_bwd), and the
  *       same layout per tile instance in its partials buffer:
  *         [0] dL/du [1] dL/dv [2..4] dL/dA, dL/dB, dL/dC [5] dL/dopacity
- *         [6..8] dL/dcolour r,g,b  [9..11] 0.
+ *         [6..8] dL/dcolour r,g,b  [9..10] absolute gradients of u, v
+ *         (see gs_rasterize_bwd's absgrad; 0 without it)  [11] 0.
  *   - Images are row-major [H][W] (colour [H][W][3]); pixel (px,py) has its
  *     centre at (px+0.5, py+0.5); tiles are 16x16, T = ceil(W/16)*ceil(H/16),
  *     tile id = ty*ceil(W/16) + tx.
@@ -197,8 +198,14 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
  * adds each Gaussian's slots, in slot order, into its record of grads2d
  * [ld][16] (visible Gaussians only).  There are no atomics, so the result is
  * bit-for-bit reproducible.  Pairs whose alpha was clamped at alpha_max carry
- * no opacity/conic/mean gradient.  counters: NULL, or device uint64[4]:
- * [0] pairs evaluated, [1] pairs with a gradient, [3] wavefront reductions. */
+ * no opacity/conic/mean gradient.
+ * absgrad: 0 or 1.  With 1, fields [9] and [10] of each visible Gaussian's
+ * record receive the sums over pixels of |dL/du| and |dL/dv| of each
+ * pixel's own contribution: the absolute-gradient statistic that
+ * densification thresholds (gsplat guide §4.1 trains with it).  With 0
+ * they are 0 and the kernel skips that work.
+ * counters: NULL, or device uint64[4]: [0] pairs evaluated, [1] pairs with a
+ * gradient, [3] wavefront reductions. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
                            const float* splats, const uint32_t* offsets,
@@ -206,8 +213,8 @@ GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t 
                            const float* background, const gs_settings* settings,
                            const float* final_T, const uint32_t* last_idx,
                            const float* dL_dimage, float* partials,
-                           uint64_t partials_capacity, float* grads2d, uint64_t* counters,
-                           void* stream);
+                           uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                           uint64_t* counters, void* stream);
 
 /* Stage 5b — projection backward: chain rule from the 2D gradient records
  * grads2d [ld][16] to means [3][ld], scales [3][ld], quats [4][ld] (through

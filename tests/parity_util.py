@@ -41,7 +41,7 @@ def torch_cuda():
 
 def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
               loss_kind=None, target=None, backward=True, depth_alpha=False, capacity=None,
-              dL_dimage=None):
+              dL_dimage=None, absgrad=False):
     """Run the five stages on the GPU; returns numpy arrays in the natural
     [N, ...] layout plus the raw Frame."""
     import torch
@@ -55,11 +55,11 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
     if backward:
         if dL_dimage is not None:
             dl = torch.from_numpy(np.ascontiguousarray(dL_dimage, np.float32)).cuda()
-            fr.backward(g, dl)
+            fr.backward(g, dl, absgrad=absgrad)
         else:
             tgt = torch.from_numpy(np.ascontiguousarray(target, np.float32)).cuda()
             fr.loss_grad(tgt, 0 if loss_kind == "l2" else 1)
-            fr.backward(g)
+            fr.backward(g, absgrad=absgrad)
     torch.cuda.synchronize()
     N = scene.n
     T = lambda t, P=None: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
@@ -82,6 +82,7 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
                    loss=float(fr.loss.cpu().numpy()[0]),
                    g_means2d=rec[:, 0:2].copy(), g_conics=rec[:, 2:5].copy(),
                    g_opac2d=rec[:, 5].copy(), g_colors=rec[:, 6:9].copy(),
+                   g_absgrad=rec[:, 9:11].copy(),
                    g_opacities=T(fr.g_opacities),
                    g_means=T(fr.g_means), g_scales=T(fr.g_scales), g_quats=T(fr.g_quats),
                    g_sh=T(fr.g_sh).reshape(N, K, 3))
@@ -202,7 +203,9 @@ def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alp
         r.update(dl=dl, bw=bw)
     t2 = time.time()
     if backward:
-        r["gpu_iso"] = gpu_frame(scene, cam, background=bg, dL_dimage=r["dl"], ld=ld)
+        # the isolated run also exercises the absolute-gradient variant
+        r["gpu_iso"] = gpu_frame(scene, cam, background=bg, dL_dimage=r["dl"], ld=ld,
+                                 absgrad=True)
         r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld)
     print("[parity] %s: N=%d M=%d gpu %.1fs oracle %.1fs" % (
         name, scene.n, gpu["M"], t1 - t0 + time.time() - t2, t2 - t1), flush=True)
@@ -261,7 +264,9 @@ def check_raster_bwd(r):
     reps = [compare_grad(g["g_means2d"], ob["means2d"], a[:, 0:2], ex, "means2d"),
             compare_grad(g["g_conics"], ob["conics"], a[:, 2:5], ex, "conics"),
             compare_grad(g["g_opac2d"], ob["opacities"], a[:, 5], ex, "opacities"),
-            compare_grad(g["g_colors"], ob["colors"], a[:, 6:9], ex, "colors")]
+            compare_grad(g["g_colors"], ob["colors"], a[:, 6:9], ex, "colors"),
+            # sums of positive terms: no cancellation allowance
+            compare_grad(g["g_absgrad"], a[:, 0:2], None, ex, "absgrad")]
     for rep in reps:
         print("[parity] %s raster_bwd %s" % (r["name"], rep))
     for rep in reps:

@@ -135,15 +135,16 @@ def test_raster_and_loss_reject_bad_arguments(lib):
                              dummy, dummy, dummy, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # the depth output needs depths
 
-    def bwd(offsets=dummy, M=10, cap=10, partials=dummy, grads=dummy):
+    def bwd(offsets=dummy, M=10, cap=10, partials=dummy, grads=dummy, absgrad=0):
         return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, dummy, dummy, offsets, dummy, M, bg,
-                                    C.byref(st), dummy, dummy, dummy, partials, cap, grads, None,
-                                    None)
+                                    C.byref(st), dummy, dummy, dummy, partials, cap, grads,
+                                    absgrad, None, None)
     assert bwd(offsets=None) == raster.GS_ERR_INVALID_ARGUMENT     # offsets needed
     assert bwd(cap=9) == raster.GS_ERR_INVALID_ARGUMENT            # slots < instances
     assert bwd(partials=None) == raster.GS_ERR_INVALID_ARGUMENT
     assert bwd(partials=C.c_void_p(80)) == raster.GS_ERR_INVALID_ARGUMENT  # misaligned
     assert bwd(grads=C.c_void_p(72)) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(absgrad=2) == raster.GS_ERR_INVALID_ARGUMENT
     r = lib.gs_project_bwd(4, 4, 0, dummy, dummy, dummy, dummy, C.byref(_cam()), C.byref(st),
                            dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # accumulate must be 0/1

@@ -168,3 +168,23 @@ def test_loss_value_and_gradient():
         ref_l = np.sum(r * r) if kind == 0 else np.sum(np.abs(r))
         np.testing.assert_allclose(g.cpu().numpy(), ref_g, rtol=1e-6, atol=1e-7)
         np.testing.assert_allclose(float(loss.item()), ref_l, rtol=1e-5)
+
+
+def test_absgrad_variant_keeps_the_gradients():
+    """absgrad = 1 only adds record fields 9-10 (non-negative sums); every
+    other field is bit-identical to absgrad = 0, and without it 9-10 are 0."""
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    scene, cam = scenes.box_scene(n=20000, seed=14, width=320, height=200, fx=180.0)
+    out = gpu_frame(scene, cam, loss_kind="l1", target=scenes.target_image(cam, 8))
+    fr, g = out["frame"], raster.Gaussians.from_scene(scene)
+    plain = fr.grads2d[:g.N].clone()
+    fr.rasterize_backward(g, absgrad=True)
+    torch.cuda.synchronize()
+    vis = (fr.radii[:g.N] > 0).cpu().numpy()
+    a, b = plain.cpu().numpy()[vis], fr.grads2d[:g.N].cpu().numpy()[vis]
+    assert_bits_equal(b[:, 0:9], a[:, 0:9], "fields 0-8")
+    assert np.all(a[:, 9:12] == 0)
+    assert np.all(b[:, 9:11] >= 0) and np.count_nonzero(b[:, 9:11]) > 0
+    # |sum| <= sum |.|
+    assert np.all(np.abs(b[:, 0:2]) <= b[:, 9:11] * (1 + 1e-5) + 1e-30)
