@@ -105,6 +105,58 @@ def cpu_baseline(scene, cams, targets, loss_kind, frames):
                       (frames, frames - 1, dt)}
 
 
+def densify_bench(args):
+    """Times gs_densify_prune on the 6M-Gaussian heavy-tailed scene (2% clones,
+    opacity threshold 0.005) with the mean gradients of one camera's
+    fwd+bwd, and prints one JSON line."""
+    import torch
+    from differentiable_rasterization_amd import raster, scenes
+    torch.cuda.set_device(0)
+    scene, cams, _ = scenes.make_config("heavy_6m_1024")
+    g = raster.Gaussians.from_scene(scene)
+    fr = raster.Frame(g.ld, scene.sh_degree, cams[0].width, cams[0].height, capacity=4 * scene.n)
+    tgt = torch.from_numpy(scenes.target_image(cams[0], 0)).cuda()
+    fr.forward(g, cams[0])
+    fr.loss_grad(tgt, 1)
+    fr.backward(g)
+    torch.cuda.synchronize()
+    N = scene.n
+    K = (scene.sh_degree + 1) ** 2
+    P = 11 + 3 * K
+    n_clone = int(np.floor(float(np.float32(0.02)) * N + 0.5))
+    ld_out = N + n_clone
+    e = lambda rows: torch.empty((rows, ld_out), dtype=torch.float32, device="cuda")
+    outs = [e(3), e(3), e(4), e(1), e(3 * K)]
+    ws_bytes = raster.gs_densify_prune_workspace_size(N, 0.02)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+    times = []
+    n_out = 0
+    for i in range(args.warmup + args.steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_out = raster.gs_densify_prune(N, g.ld, scene.sh_degree, g.means, g.scales, g.quats,
+                                        g.opacities, g.sh, fr.g_means, 0.02, 0.005, ld_out,
+                                        *outs, ws, ws_bytes)
+        dt = time.perf_counter() - t0   # the call ends with its count read-back
+        if i >= args.warmup:
+            times.append(dt)
+    ms = 1e3 * float(np.median(times))
+    # algorithmic bytes: the gradient planes, every parameter plane once in,
+    # every output plane once out
+    byts = 12 * N + 4 * P * (N + n_out)
+    out = {"metric": "densify/prune ms per step at 6M Gaussians", "value": round(ms, 3),
+           "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "heavy_6m_1024", "gaussians": N, "gaussians_out": n_out,
+                      "clone_fraction": 0.02, "min_opacity": 0.005},
+           "roofline": {"bound": "hbm", "achieved": round(byts / (ms * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": None},
+           "note": "wall time of the gs_densify_prune call (its last step is the count read-back)"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +165,8 @@ def main():
     ap.add_argument("--config", default="cluster_1m_1080p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=4)
+    ap.add_argument("--densify", action="store_true",
+                    help="time gs_densify_prune on the 6M-Gaussian scene instead")
     ap.add_argument("--absgrad", action="store_true",
                     help="run the compositing backward with the absolute-gradient sums")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -123,6 +177,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.densify:
+        densify_bench(args)
+        return
 
     import torch
     from differentiable_rasterization_amd import raster, scenes

@@ -42,6 +42,12 @@ hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t*
                                 float* grads2d, int absgrad, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
+int64_t gs_densify_clone_count(int64_t N, float clone_fraction);
+size_t gs_densify_workspace_bytes(int64_t N, float clone_fraction);
+hipError_t gs_launch_densify(int64_t N, int nplanes, const float* const* in_planes, int64_t ld,
+                             const float* dL_dmeans, const float* opacities, float clone_fraction,
+                             float min_opacity, float* const* out_planes, int64_t* num_out,
+                             void* workspace, hipStream_t s);
 }
 
 namespace {
@@ -294,6 +300,57 @@ gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* image,
   return hip_status(gs_launch_loss_grad(kind, count, image, target, dL_dimage, loss,
                                         (hipStream_t)stream),
                     "gs_image_loss_grad");
+}
+
+size_t gs_densify_prune_workspace_size(int64_t N, float clone_fraction) {
+  if (N < 0 || !(clone_fraction >= 0.0f && clone_fraction <= 1.0f)) return 0;
+  return gs_densify_workspace_bytes(N, clone_fraction);
+}
+
+gs_status gs_densify_prune(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
+                           const float* scales, const float* quats, const float* opacities,
+                           const float* sh, const float* dL_dmeans, float clone_fraction,
+                           float min_opacity, int64_t ld_out, float* means_out,
+                           float* scales_out, float* quats_out, float* opacities_out,
+                           float* sh_out, int64_t* num_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_REQUIRE(clone_fraction >= 0.0f && clone_fraction <= 1.0f,
+             "clone_fraction must be in [0, 1]");
+  GS_REQUIRE(min_opacity == min_opacity, "min_opacity is NaN");
+  GS_REQUIRE(num_out != nullptr, "num_out is NULL");
+  const int64_t n_clone = gs_densify_clone_count(N, clone_fraction);
+  GS_REQUIRE(N + n_clone < ((int64_t)1 << 30), "N plus clones must be < 2^30");
+  GS_REQUIRE(ld_out >= N + n_clone, "ld_out must hold N plus the clones");
+  if (N > 0) {
+    GS_REQUIRE(means && scales && quats && opacities && sh && dL_dmeans && means_out &&
+                   scales_out && quats_out && opacities_out && sh_out,
+               "NULL array pointer");
+    GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+    GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+    GS_REQUIRE(workspace_bytes >= gs_densify_workspace_bytes(N, clone_fraction),
+               "workspace smaller than gs_densify_prune_workspace_size()");
+  }
+  const int K = (sh_degree + 1) * (sh_degree + 1);
+  const float* in[64];
+  float* out[64];
+  int n = 0;
+  auto add = [&](const float* a, float* b, int planes) {
+    for (int k = 0; k < planes; ++k, ++n) {
+      in[n] = a ? a + (int64_t)k * ld : nullptr;
+      out[n] = b ? b + (int64_t)k * ld_out : nullptr;
+    }
+  };
+  add(means, means_out, 3);
+  add(scales, scales_out, 3);
+  add(quats, quats_out, 4);
+  add(opacities, opacities_out, 1);
+  add(sh, sh_out, 3 * K);
+  return hip_status(gs_launch_densify(N, n, in, ld, dL_dmeans, opacities, clone_fraction,
+                                      min_opacity, out, num_out, workspace,
+                                      (hipStream_t)stream),
+                    "gs_densify_prune");
 }
 
 }  // extern "C"

@@ -511,3 +511,122 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, M32, (uint32_t)T, ranges);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Internal helpers for other stages (hidden, not part of the C ABI): a stable
+// sort of (key, value) pairs by the low `bits` bits of the keys, and an
+// exclusive scan of u32 values whose total stays on the device.
+// ---------------------------------------------------------------------------
+namespace gs {
+struct PairSortWs {
+  uint64_t* keys_alt;
+  uint32_t* vals_alt;
+  uint32_t* hist;
+  uint32_t* ticket;
+  uint32_t* status;
+  int passes;
+  uint32_t parts;
+  size_t bytes;
+};
+
+static PairSortWs carve_pairsort(void* base, uint64_t n, int bits) {
+  PairSortWs w;
+  w.passes = (bits + kRadixBits - 1) / kRadixBits;
+  w.parts = (uint32_t)((n + kPart - 1) / kPart);
+  char* p = (char*)base;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.keys_alt = (uint64_t*)take(sizeof(uint64_t) * (n ? n : 1));
+  w.vals_alt = (uint32_t*)take(sizeof(uint32_t) * (n ? n : 1));
+  w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
+  w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.passes * (w.parts ? w.parts : 1) * kRadix);
+  w.bytes = off;
+  return w;
+}
+}  // namespace gs
+
+extern "C" size_t gs_pairsort_workspace_bytes(uint64_t n, int bits) {
+  return gs::carve_pairsort(nullptr, n, bits).bytes;
+}
+
+// Sorts (keys, vals)[0, n) stably by the low `bits` bits of the keys; the
+// result lands back in keys / vals.  n < 2^30, bits in [1, 64].
+extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, int bits,
+                                  void* workspace, hipStream_t s) {
+  using namespace gs;
+  if (n == 0) return hipSuccess;
+  PairSortWs w = carve_pairsort(workspace, n, bits);
+  hipError_t e;
+  {
+    Segs sg = {{w.hist, w.ticket, w.status, w.status},
+               {(int64_t)kMaxPasses * kRadix, kMaxPasses,
+                (int64_t)w.passes * w.parts * kRadix, 0}};
+    int64_t blocks = (sg.n[2] + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // an odd pass count starts from a copy in the alternate buffers so that
+  // the last pass writes keys / vals
+  uint64_t* ka = keys;
+  uint32_t* ia = vals;
+  uint64_t* kb = w.keys_alt;
+  uint32_t* ib = w.vals_alt;
+  if (w.passes & 1) {
+    if ((e = hipMemcpyAsync(w.keys_alt, keys, n * sizeof(uint64_t), hipMemcpyDeviceToDevice, s)) !=
+        hipSuccess)
+      return e;
+    if ((e = hipMemcpyAsync(w.vals_alt, vals, n * sizeof(uint32_t), hipMemcpyDeviceToDevice, s)) !=
+        hipSuccess)
+      return e;
+    ka = w.keys_alt; ia = w.vals_alt; kb = keys; ib = vals;
+  }
+  const uint32_t n32 = (uint32_t)n;
+  unsigned hblocks = (unsigned)((n + 256 * 16 - 1) / (256 * 16));
+  if (hblocks > 1024) hblocks = 1024;
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, n32, w.passes,
+                     w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(256), 0, s, w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int p = 0; p < w.passes; ++p) {
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(256), 0, s, ka, ia, kb, ib, n32,
+                       p * kRadixBits, w.hist + p * kRadix,
+                       w.status + (size_t)p * w.parts * kRadix, w.ticket + p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint64_t* tk = ka; ka = kb; kb = tk;
+    uint32_t* ti = ia; ia = ib; ib = ti;
+  }
+  return hipSuccess;
+}
+
+extern "C" size_t gs_scan_workspace_bytes(int64_t n) {
+  const int64_t nb = (n + gs::kScanBlock - 1) / gs::kScanBlock;
+  return gs::align256(sizeof(uint64_t) * (size_t)(nb ? nb : 1));
+}
+
+// out[i] = in[0] + ... + in[i-1]; *total (device) = the whole sum.
+extern "C" hipError_t gs_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* total,
+                                  void* workspace, hipStream_t s) {
+  using namespace gs;
+  hipError_t e;
+  if (n == 0) {
+    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, (uint64_t*)workspace,
+                       (int64_t)0, total);
+    return hipGetLastError();
+  }
+  uint64_t* sums = (uint64_t*)workspace;
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, sums, nb, total);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums, out);
+  return hipGetLastError();
+}

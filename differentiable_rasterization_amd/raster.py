@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libgsraster.so")
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_tiles",
             "gs_project_fwd", "gs_bin_and_sort_workspace_size", "gs_bin_and_sort",
-            "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd", "gs_image_loss_grad")
+            "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd", "gs_image_loss_grad",
+            "gs_densify_prune_workspace_size", "gs_densify_prune")
 
 
 class GsError(RuntimeError):
@@ -83,6 +84,11 @@ def load():
         [i32, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
+    lib.gs_densify_prune_workspace_size.restype = C.c_size_t
+    lib.gs_densify_prune_workspace_size.argtypes = [i64, C.c_float]
+    lib.gs_densify_prune.restype = C.c_int
+    lib.gs_densify_prune.argtypes = [i64, i64, i32] + [P] * 6 + [C.c_float, C.c_float, i64] + \
+        [P] * 5 + [P, P, C.c_size_t, P]
     _lib = lib
     return lib
 
@@ -207,6 +213,24 @@ def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=
                                   _p(loss), _stream(stream)))
 
 
+def gs_densify_prune_workspace_size(N, clone_fraction) -> int:
+    return int(load().gs_densify_prune_workspace_size(int(N), float(clone_fraction)))
+
+
+def gs_densify_prune(N, ld, sh_degree, means, scales, quats, opacities, sh, dL_dmeans,
+                     clone_fraction, min_opacity, ld_out, means_out, scales_out, quats_out,
+                     opacities_out, sh_out, workspace, workspace_bytes, stream=None) -> int:
+    """Returns the new Gaussian count."""
+    lib = load()
+    n_out = C.c_int64(0)
+    _check(lib.gs_densify_prune(N, ld, sh_degree, _p(means), _p(scales), _p(quats),
+                                _p(opacities), _p(sh), _p(dL_dmeans), float(clone_fraction),
+                                float(min_opacity), ld_out, _p(means_out), _p(scales_out),
+                                _p(quats_out), _p(opacities_out), _p(sh_out), C.byref(n_out),
+                                _p(workspace), workspace_bytes, _stream(stream)))
+    return int(n_out.value)
+
+
 # ---------------------------------------------------------------------------
 # Device-resident Gaussians and a frame orchestrator
 # ---------------------------------------------------------------------------
@@ -241,6 +265,27 @@ class Gaussians:
             return out
         return Gaussians(planes(scene.means, 3), planes(scene.scales, 3), planes(scene.quats, 4),
                          planes(scene.opacities, 1), planes(scene.sh, 3 * K), scene.sh_degree, N)
+
+
+def densify_prune(g: "Gaussians", dL_dmeans, clone_fraction=0.02, min_opacity=0.005,
+                  ld_out=None) -> "Gaussians":
+    """gs_densify_prune into freshly allocated planes (leading dimension
+    ``ld_out``, default N plus the clones); returns the new Gaussians."""
+    import torch
+    K = (g.sh_degree + 1) ** 2
+    n_clone = int(np.floor(float(np.float32(clone_fraction)) * g.N + 0.5))
+    ld_out = g.N + n_clone if ld_out is None else int(ld_out)
+    dev = g.means.device
+    z = lambda P: torch.zeros((P, max(ld_out, 1)), dtype=torch.float32, device=dev)
+    out = Gaussians(z(3), z(3), z(4), z(1), z(3 * K), g.sh_degree, 0)
+    ws_bytes = gs_densify_prune_workspace_size(g.N, clone_fraction)
+    ws = torch.empty((ws_bytes + 256,), dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    out.N = gs_densify_prune(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.opacities,
+                             g.sh, dL_dmeans, clone_fraction, min_opacity, max(ld_out, 1),
+                             out.means, out.scales, out.quats, out.opacities, out.sh,
+                             ws[off:off + ws_bytes], ws_bytes)
+    return out
 
 
 class Frame:

@@ -187,21 +187,6 @@ def heavy_tail_scene(n=6_000_000, seed=5, sh_degree=3, n_clusters=512, box=24.0)
     return _finish(rng, means, log_s, sh_degree)
 
 
-def densify_prune(scene, grad_norm, clone_frac=0.02, min_opacity=0.005):
-    """The count-changing step between iterations of the 6M-Gaussian workload
-    (a harness operation, not part of the rasterizer): exact copies of the
-    ``clone_frac`` Gaussians with the largest ``grad_norm`` (ties by lower
-    index) are appended in index order, then every Gaussian with opacity
-    below ``min_opacity`` is removed.  The criterion follows the densify /
-    prune of the gsplat guide (lmnt.cn/news/262699) §4.1 (gradient threshold,
-    minimum opacity 0.005)."""
-    n_clone = int(round(clone_frac * scene.n))
-    order = np.argsort(-np.asarray(grad_norm, np.float64), kind="stable")
-    idx = np.concatenate([np.arange(scene.n), np.sort(order[:n_clone])])
-    keep = scene.opacities[idx] >= np.float32(min_opacity)
-    return scene.subset(idx[keep])
-
-
 def focal_for(width):
     return 1100.0 * width / 1920.0
 

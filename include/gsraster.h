@@ -239,6 +239,33 @@ GS_API gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* im
                              const float* target, float* dL_dimage, float* loss,
                              void* stream);
 
+/* Densify and prune between training steps (the count-changing step of the
+ * gsplat guide §4.1, which clones by the mean-gradient magnitude and prunes
+ * Gaussians of opacity below 0.005).  Out of place: the N Gaussians in
+ * (means ... sh, planes [P][ld]) become *num_out Gaussians in the output
+ * planes ([P][ld_out], distinct memory):
+ *   1. n_clone = floor(clone_fraction * N + 0.5) (in double) Gaussians are
+ *      selected by the key (gx*gx + gy*gy) + gz*gz of dL_dmeans [3][ld],
+ *      evaluated in fp32 in that order (NaN taken as +inf): the n_clone
+ *      largest keys, equal keys by lower index;
+ *   2. the candidates are the N originals in index order followed by exact
+ *      copies of the selected ones in index order;
+ *   3. candidates with opacity < min_opacity are dropped; the others keep
+ *      their order.
+ * clone_fraction in [0, 1]; ld_out >= N + n_clone; N + n_clone < 2^30.
+ * *num_out (HOST) receives the new count: the call's one device-to-host
+ * read.  workspace: at least gs_densify_prune_workspace_size() bytes,
+ * 256-byte aligned. */
+GS_API size_t gs_densify_prune_workspace_size(int64_t N, float clone_fraction);
+GS_API gs_status gs_densify_prune(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
+                                  const float* scales, const float* quats,
+                                  const float* opacities, const float* sh,
+                                  const float* dL_dmeans, float clone_fraction,
+                                  float min_opacity, int64_t ld_out, float* means_out,
+                                  float* scales_out, float* quats_out, float* opacities_out,
+                                  float* sh_out, int64_t* num_out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

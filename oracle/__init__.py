@@ -392,3 +392,28 @@ def render_f64(scene, cam, settings=None, background=(0.0, 0.0, 0.0)):
                        proj["chol"], scene.opacities, proj["colors"], proj["depths"],
                        background, settings)
     return dict(proj=proj, bins=bins, raster=raster)
+
+
+# --------------------------------------------------------------------------
+# Densify / prune between training steps (gsplat guide, lmnt.cn/news/262699,
+# section 4.1: clone by the mean-gradient magnitude, prune below opacity
+# 0.005).  The selection key is the fp32 value (gx*gx + gy*gy) + gz*gz of the
+# given fp32 gradients, as the step is defined to take it.
+# --------------------------------------------------------------------------
+def densify_prune(means, scales, quats, opacities, sh, dL_dmeans, clone_fraction=0.02,
+                  min_opacity=0.005):
+    """Returns dict(means, scales, quats, opacities, sh, src) for the new
+    Gaussians, src = the index each one was copied from."""
+    N = len(means)
+    g = np.asarray(dL_dmeans, np.float32).reshape(N, 3)
+    key = (g[:, 0] * g[:, 0] + g[:, 1] * g[:, 1]) + g[:, 2] * g[:, 2]  # fp32, this order
+    key = np.where(np.isnan(key), np.float32(np.inf), key).astype(np.float32)
+    n_clone = int(np.floor(float(np.float32(clone_fraction)) * N + 0.5))
+    # n_clone largest keys; equal keys by lower index
+    order = np.lexsort((np.arange(N), -key.astype(np.float64)))
+    chosen = np.sort(order[:n_clone].astype(np.int64))
+    src = np.concatenate([np.arange(N, dtype=np.int64), chosen])
+    src = src[np.asarray(opacities, np.float32)[src] >= np.float32(min_opacity)]
+    pick = lambda a: np.asarray(a)[src]
+    return dict(means=pick(means), scales=pick(scales), quats=pick(quats),
+                opacities=pick(opacities), sh=pick(sh), src=src)

@@ -35,7 +35,7 @@ def test_header_declares_the_five_stages():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) >= 11
+    assert len(names) >= 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(raster.EXPORTED)
@@ -152,6 +152,24 @@ def test_raster_and_loss_reject_bad_arguments(lib):
         raster.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_image_loss_grad(0, -1, dummy, dummy, dummy, None, None) == \
         raster.GS_ERR_INVALID_ARGUMENT
+
+
+def test_densify_rejects_bad_arguments(lib):
+    dummy = C.c_void_p(256)
+    n_out = C.c_int64(0)
+
+    def call(N=10, ld=10, deg=0, frac=0.2, ld_out=12, ws=dummy, wsb=1 << 30):
+        return lib.gs_densify_prune(N, ld, deg, dummy, dummy, dummy, dummy, dummy, dummy,
+                                    C.c_float(frac), C.c_float(0.005), ld_out, dummy, dummy,
+                                    dummy, dummy, dummy, C.byref(n_out), ws, wsb, None)
+    assert call(frac=1.5) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(frac=-0.1) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(ld_out=11) == raster.GS_ERR_INVALID_ARGUMENT   # 10 + 2 clones
+    assert call(deg=4) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(ws=C.c_void_p(260)) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(wsb=8) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_densify_prune_workspace_size(10, C.c_float(2.0)) == 0
+    assert lib.gs_densify_prune_workspace_size(1000, C.c_float(0.02)) > 0
 
 
 def test_status_strings(lib):

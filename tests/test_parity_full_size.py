@@ -5,9 +5,9 @@ configuration the benchmark uses (whole frames through the C ABI):
     alpha outputs, for each of the batch's 4 seeded poses;
   * 6M heavy-tailed Gaussians (Student-t log-scales), SH3, 1024x1024, where
     tiles carry thousands of Gaussians: a whole camera's forward and
-    backward; gradients summed over cameras with accumulate = 1; and, after a
-    densify/prune step that clones 2% and drops faint Gaussians (so N changes
-    and clones create exact depth ties), another camera on the new scene.
+    backward; gradients summed over cameras with accumulate = 1; and, after
+    gs_densify_prune clones 2% and drops faint Gaussians (so N changes and
+    clones create exact depth ties), another camera on the new scene.
 
 Each comparison is against the oracle's own run of the same seeded inputs,
 to the bars of the other parity tests.
@@ -19,7 +19,7 @@ import pytest
 
 from differentiable_rasterization_amd import scenes
 
-from parity_util import (check_bins, check_e2e_grads, check_project_bwd,
+from parity_util import (assert_bits_equal, check_bins, check_e2e_grads, check_project_bwd,
                          check_project_fwd, check_raster_bwd, check_raster_fwd,
                          run_parity_case)
 
@@ -99,20 +99,40 @@ def test_heavy_6m_1024_accumulate_over_cameras():
 
 
 def test_heavy_6m_1024_after_densify_prune():
+    """gs_densify_prune on the 6M scene with camera 0's mean gradients (the
+    oracle's, rounded to fp32): bit-exact against the oracle's step, then a
+    whole camera's parity on the new scene."""
+    import torch
+    import oracle
+    from differentiable_rasterization_amd import raster
     scene, cams, loss = _heavy_6m()
     if 0 not in _MEAN_GRAD:
-        import oracle
         cam = cams[0]
         orc = oracle.render(scene, cam)
         dl = oracle.loss_grad_image(orc["raster"]["image"], scenes.target_image(cam, 0),
                                     oracle.LOSS_L1).astype(np.float32)
         _MEAN_GRAD[0] = oracle.backward(scene, cam, orc, dl.astype(np.float64))["g3"]["means"]
-    norm = np.linalg.norm(_MEAN_GRAD[0], axis=1)
-    grown = scenes.densify_prune(scene, norm)
-    assert grown.n != scene.n
-    cam = cams[2]
+    grads = _MEAN_GRAD[0].astype(np.float32)
+    want = oracle.densify_prune(scene.means, scene.scales, scene.quats, scene.opacities, scene.sh,
+                                grads, 0.02, 0.005)
+    g = raster.Gaussians.from_scene(scene)
+    dlm = torch.from_numpy(np.ascontiguousarray(grads.T)).cuda()
     # the Gaussian arrays keep a leading dimension with room to grow
-    ld = int(max(grown.n, scene.n) * 1.05)
+    ld = int(scene.n * 1.05)
+    out = raster.densify_prune(g, dlm, 0.02, 0.005, ld_out=ld)
+    torch.cuda.synchronize()
+    n = out.N
+    print("[parity] heavy_6m_1024 densify/prune: %d -> %d" % (scene.n, n), flush=True)
+    assert n == len(want["src"]) and n != scene.n
+    T = lambda t: t[:, :n].T.contiguous().cpu().numpy()
+    assert_bits_equal(T(out.means), want["means"], "means")
+    assert_bits_equal(T(out.quats), want["quats"], "quats")
+    assert_bits_equal(T(out.opacities)[:, 0], want["opacities"], "opacities")
+    assert_bits_equal(T(out.sh).reshape(want["sh"].shape), want["sh"], "sh")
+    grown = scenes.Scene(want["means"], want["scales"], want["quats"], want["opacities"],
+                         want["sh"], scene.sh_degree)
+    del g, out, dlm
+    cam = cams[2]
     r = run_parity_case("heavy_6m_1024 densified, camera 2", grown, cam, loss, (0.0, 0.0, 0.0),
                         scenes.target_image(cam, 2), ld=ld)
     _all_checks(r)
