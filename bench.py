@@ -254,8 +254,9 @@ def main():
         inside = np.bincount(tile_of.ravel(), minlength=T)
         stats.append(dict(V=V, M=fr.M, M_bwd=int(maxlast.sum()),
                           pairs_tile=int((inside * lens).sum()), fwd_eval=int(c[0]),
-                          blended=int(c[1]), plain_pairs=int(c[2]), bwd_eval=int(c[4]),
-                          bwd_hit=int(c[5]), bwd_reductions=int(c[7])))
+                          blended=int(c[1]), plain_pairs=int(c[2]), fwd_plain_tile=int(c[3]),
+                          bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
+                          bwd_reductions=int(c[7])))
 
     for i in range(args.warmup):
         step(i)
@@ -288,30 +289,37 @@ def main():
     fwd_ms = stage_ms["project_fwd"] + stage_ms["bin_and_sort"] + stage_ms["rasterize_fwd"]
     dominant = max(names, key=lambda n: stage_ms[n])
     # The compositing kernels are bound by VALU issue.  Algorithmic work = the
-    # pixel-splat pairs that blend (the pairs whose result the method uses)
-    # x VALU slots such a pair costs in the kernel's loop; "issued" counts
-    # every pair the kernel evaluated and every wavefront reduction.
+    # pairs the plain tile loop evaluates (per tile, 256 x its entries up to
+    # the last of its pixels' stops; the backward walks up to the last
+    # blended entry) x the VALU slots a pair costs in the kernel's loop.
+    # "blended" counts only the pairs whose result the method uses; "issued"
+    # counts every pair the kernel evaluated and every wavefront reduction.
     alu = {
-        "rasterize_fwd": (avg["blended"] * FWD_SLOTS_PER_PAIR,
+        "rasterize_fwd": (avg["fwd_plain_tile"] * FWD_SLOTS_PER_PAIR,
+                          avg["blended"] * FWD_SLOTS_PER_PAIR,
                           avg["fwd_eval"] * FWD_SLOTS_PER_PAIR),
-        "rasterize_bwd": (avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
+        "rasterize_bwd": (avg["bwd_plain_tile"] * BWD_SLOTS_PER_PAIR,
+                          avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
                           avg["bwd_eval"] * BWD_EVAL_SLOTS +
                           avg["bwd_reductions"] * 64 * (BWD_GRAD_SLOTS + BWD_REDUCE_SLOTS)),
     }
     work = {"pairs_blended": int(avg["blended"]), "pairs_evaluated_fwd": int(avg["fwd_eval"]),
             "pairs_evaluated_bwd": int(avg["bwd_eval"]),
             "pairs_plain_method": int(avg["plain_pairs"]),
+            "pairs_plain_tile_loop_fwd": int(avg["fwd_plain_tile"]),
+            "pairs_plain_tile_loop_bwd": int(avg["bwd_plain_tile"]),
             "pairs_all_tile_pixels": int(avg["pairs_tile"]),
             "wave_reductions_bwd": int(avg["bwd_reductions"])}
     if dominant in alu:
-        useful, issued = alu[dominant]
+        algo, blended, issued = alu[dominant]
         t = stage_ms[dominant] * 1e-3
-        ach = useful / t / 1e12
+        ach = algo / t / 1e12
         traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and not args.absgrad and
                                           args.config == "cluster_1m_1080p") else None)
         roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
                 "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
                 "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": traffic,
+                "blended_frac": round(blended / t / 1e12 / VALU_PEAK_TOPS, 4),
                 "issued_frac": round(issued / t / 1e12 / VALU_PEAK_TOPS, 4),
                 "slots_per_pair": BWD_SLOTS_PER_PAIR if dominant == "rasterize_bwd"
                 else FWD_SLOTS_PER_PAIR, "work_per_launch": work}

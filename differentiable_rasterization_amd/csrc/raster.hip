@@ -145,9 +145,13 @@ __device__ inline float splat_power2(const SplatLds& s, float dx, float dy) {
 // Work counters (optional diagnostics, one atomic per workgroup):
 //   [0] pixel-splat pairs the kernel evaluated (after the quadrant culling),
 //   [1] pairs blended (alpha >= alpha_min before the pixel's stop),
-//   [2] pairs the plain method evaluates: per pixel, its tile's entries up to
-//       and including the one that stops it (all of them if none does),
-//   [3] wavefront reductions executed (backward only).
+//   [2] forward: pairs the plain per-pixel method evaluates (per pixel, its
+//       tile's entries up to and including the one that stops it, all of
+//       them if none does); backward: pairs the plain tile loop walks
+//       (256 x the tile's entries up to its pixels' last blended one),
+//   [3] forward: pairs the plain tile loop evaluates (256 x the tile's
+//       entries up to the last of its pixels' stops); backward: wavefront
+//       reductions executed.
 __device__ inline void add_counters(uint64_t* cnt, uint64_t a, uint64_t b, uint64_t c,
                                     uint64_t d) {
   __shared__ uint64_t s_c[4];
@@ -232,7 +236,13 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   }
   if (kStats) {
     const uint32_t plain = inside ? (stop_at ? stop_at : end - start) : 0u;
-    add_counters(cnt, inside ? n_eval : 0u, n_blend, plain, 0u);
+    __shared__ uint32_t s_tmax;
+    if (threadIdx.x == 0) s_tmax = 0u;
+    __syncthreads();
+    if (plain) atomicMax(&s_tmax, plain);
+    __syncthreads();
+    const uint64_t tile_plain = threadIdx.x == 0 ? 256ull * s_tmax : 0ull;
+    add_counters(cnt, inside ? n_eval : 0u, n_blend, plain, tile_plain);
   }
   if (!inside) return;
   const int64_t p = (int64_t)py * W + px;
@@ -497,7 +507,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     }
     b_end = b_begin;
   }
-  if (kStats) add_counters(cnt, n_eval, n_hit, 0u, n_red);
+  if (kStats)
+    add_counters(cnt, n_eval, n_hit, threadIdx.x == 0 ? 256ull * (stop - start) : 0ull, n_red);
 }
 
 // Sum each visible Gaussian's instance slots [offsets[i], offsets[i] +

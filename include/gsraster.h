@@ -177,8 +177,10 @@ GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, co
  * NULL).  background: HOST float[3].
  * counters: NULL, or device uint64[4] that the call adds work counts to:
  * [0] pixel-splat pairs evaluated by the kernel, [1] pairs blended, [2] pairs
- * the plain method evaluates (per pixel, its tile's entries up to the one
- * that stops it), [3] unused.  Counting uses a separate kernel variant. */
+ * the plain per-pixel method evaluates (per pixel, its tile's entries up to
+ * the one that stops it), [3] pairs the plain tile loop evaluates (256 x a
+ * tile's entries up to the last of its pixels' stops).  Counting uses a
+ * separate kernel variant. */
 GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
                            const float* splats, const float* depths, const float* background,
@@ -205,7 +207,8 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
  * densification thresholds (gsplat guide §4.1 trains with it).  With 0
  * they are 0 and the kernel skips that work.
  * counters: NULL, or device uint64[4]: [0] pairs evaluated, [1] pairs with a
- * gradient, [3] wavefront reductions. */
+ * gradient, [2] pairs the plain tile loop walks (256 x a tile's entries up
+ * to its pixels' last blended one), [3] wavefront reductions. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
                            const uint32_t* tile_ranges, const uint32_t* ids,
                            const float* splats, const uint32_t* offsets,

@@ -41,6 +41,9 @@ def test_counting_variant_matches_and_counts_consistently():
     assert c[1] <= c[0] and c[1] <= c[2]
     assert c[0] <= out["M"] * 256       # culling never adds work
     assert c[7] > 0
+    # the plain tile loops: per-pixel work <= the tile loop's <= every entry
+    assert c[2] <= c[3] <= out["M"] * 256
+    assert c[4] <= c[6] <= c[3]
 
 
 def test_zero_gaussians_and_all_culled():
