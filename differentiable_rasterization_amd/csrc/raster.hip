@@ -701,6 +701,7 @@ extern "C" hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img,
   const bool al = (((uintptr_t)img | (uintptr_t)tgt | (uintptr_t)g) & 15u) == 0;
   const int64_t n4 = al ? n / 4 : 0;
   int64_t blocks = ((al ? n4 : n) + 255) / 256;
+  if (blocks < 1) blocks = 1;  // fewer than four elements: the tail loop alone
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(gs::loss_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, kind, n, n4,
                      img, tgt, g, loss);

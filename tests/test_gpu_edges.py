@@ -163,6 +163,12 @@ def test_loss_value_and_gradient():
     ti, tt = torch.from_numpy(img).cuda(), torch.from_numpy(tgt).cuda()
     g = torch.empty_like(ti)
     loss = torch.zeros(1, device="cuda")
+    for m in (1, 3, 5):  # shorter than one float4: element-wise tail only
+        gs_ = torch.empty(m, device="cuda")
+        raster.gs_image_loss_grad(0, m, ti, tt, gs_, loss)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(gs_.cpu().numpy(), 2 * (img[:m].astype(np.float64) - tgt[:m]),
+                                   rtol=1e-6)
     for kind in (0, 1):
         raster.gs_image_loss_grad(kind, n, ti, tt, g, loss)
         torch.cuda.synchronize()
