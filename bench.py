@@ -45,9 +45,18 @@ BWD_REDUCE_SLOTS = 36.0
 BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
 
 
-def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P):
+def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P, packed=False):
     """Algorithmic HBM bytes of each stage (what the method must move with the
     intermediates the ABI materialises)."""
+    if packed:
+        b = stage_bytes(st, N, V, M, M_bwd, Px, T, K, P)
+        # the visible list written by the scan; the reduction reads it, then
+        # tiles + offsets of the visible only; the projection backward reads
+        # it and writes gradient rows for the visible only
+        b["bin_and_sort"] += 4 * V
+        b["rasterize_bwd"] += 12 * V - 8 * N
+        b["project_bwd"] = 8 * V + (76 + 12 * K) * V + (44 + 12 * K) * V
+        return b
     return {
         # means + radius/tiles for all; scales, quats, opacity, SH in and
         # means2d, conic, depth, colour planes plus the 64-byte splat record out
@@ -169,6 +178,8 @@ def main():
                     help="time gs_densify_prune on the 6M-Gaussian scene instead")
     ap.add_argument("--absgrad", action="store_true",
                     help="run the compositing backward with the absolute-gradient sums")
+    ap.add_argument("--packed", action="store_true",
+                    help="run the packed calls (visible list, sparse gradient rows)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -199,7 +210,7 @@ def main():
     targets_np = [scenes.target_image(c, i) for i, c in enumerate(cams)]
     targets = [torch.from_numpy(t).cuda() for t in targets_np]
     g = raster.Gaussians.from_scene(scene)
-    fr = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=4 * N)
+    fr = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=4 * N, packed=args.packed)
     gcams = [raster.make_camera(c) for c in cams]
     kind = 0 if loss_kind == "l2" else 1
     P = len(cams)
@@ -209,7 +220,7 @@ def main():
     names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "loss_grad", "rasterize_bwd",
              "project_bwd"]
 
-    def step(i, ev=None):
+    def step(i, ev=None, fr=fr):
         c = gcams[i % P]
         if ev is not None:
             ev[0].record()
@@ -258,27 +269,41 @@ def main():
                           bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
                           bwd_reductions=int(c[7])))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def timed(frame):
+        """Warm-up, then the timed steps; returns (seconds, per-stage ms)."""
+        for i in range(args.warmup):
+            step(i, fr=frame)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i], fr=frame)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ms = {n: 0.0 for n in names}
+        for ev in evs:
+            for k, n in enumerate(names):
+                ms[n] += ev[k].elapsed_time(ev[k + 1])
+        return dt, {n: v / args.steps for n, v in ms.items()}
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-
-    stage_ms = {n: 0.0 for n in names}
-    for ev in evs:
-        for k, n in enumerate(names):
-            stage_ms[n] += ev[k].elapsed_time(ev[k + 1])
-    stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
+    dt, stage_ms = timed(fr)
+    packed_line = None
+    if not args.packed:
+        # the same steps through the packed calls (visible list, sparse
+        # gradient rows), reported beside the dense headline
+        frp = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=fr.capacity, packed=True)
+        dtp, msp = timed(frp)
+        packed_line = {"value": round(args.steps / dtp, 2),
+                       "ms_per_step": round(1e3 * dtp / args.steps, 4),
+                       "stages_ms": {n: round(v, 4) for n, v in msp.items()}}
+        del frp
     # average workload over the poses the timed steps visited
     visited = [stats[i % P] for i in range(args.steps)]
     avg = {k: float(np.mean([s[k] for s in visited])) for k in visited[0]}
-    byts = stage_bytes(None, N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes)
+    byts = stage_bytes(None, N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes,
+                       packed=args.packed)
     stages = {}
     for n in names:
         ms = stage_ms[n]
@@ -315,6 +340,7 @@ def main():
         t = stage_ms[dominant] * 1e-3
         ach = algo / t / 1e12
         traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and not args.absgrad and
+                                          not args.packed and
                                           args.config == "cluster_1m_1080p") else None)
         roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
                 "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
@@ -337,12 +363,14 @@ def main():
         "config": {"workload": args.config, "gaussians": N, "width": W, "height": H,
                    "sh_degree": scene.sh_degree, "poses": P, "loss": loss_kind,
                    "visible": int(avg["V"]), "instances": int(avg["M"]),
-                   "absgrad": bool(args.absgrad)},
+                   "absgrad": bool(args.absgrad), "packed": bool(args.packed)},
         "fwd_fps": round(1e3 / fwd_ms, 2),
         "sort_keys_per_s": round(avg["M"] / (stage_ms["bin_and_sort"] * 1e-3), 1),
         "stages": stages,
         "roofline": roof,
     }
+    if packed_line is not None:
+        out["packed"] = packed_line
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
     print(json.dumps(out), flush=True)

@@ -13,15 +13,17 @@ hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* me
                                  float* means2d, float* conics, float* depths, int32_t* radii,
                                  float* colors, uint32_t* tiles, float* splats,
                                  hipStream_t stream);
-hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, const float* means,
+hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids, int64_t ldo,
+                                 int deg, const float* means,
                                  const float* scales, const float* quats, const float* sh,
                                  const gs::Cam& cam, const gs::Settings& st, const int32_t* radii,
                                  const float* grads2d, float* o_means, float* o_scales,
                                  float* o_quats, float* o_opac, float* o_sh, int accumulate,
                                  hipStream_t stream);
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
-hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, void* workspace,
-                          uint64_t capacity, int32_t T, uint64_t* total_host, hipStream_t s);
+hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, uint32_t* vis_ids,
+                          void* workspace, uint64_t capacity, int32_t T, uint64_t* totals_host,
+                          hipStream_t s);
 hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                      const int32_t* radii, const float* depths,
                                      const uint32_t* tiles, const uint32_t* offsets, int32_t W,
@@ -39,7 +41,8 @@ hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t*
                                 const uint32_t* tiles, const float* bg, const gs::Settings& st,
                                 const float* final_T, const uint32_t* last_idx,
                                 const float* dL_dimage, float* partials, uint64_t capacity,
-                                float* grads2d, int absgrad, uint64_t* counters, hipStream_t s);
+                                float* grads2d, int absgrad, const uint32_t* vis_ids,
+                                int64_t num_visible, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
 int64_t gs_densify_clone_count(int64_t N, float clone_fraction);
@@ -196,7 +199,8 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
   gs_status st = hip_status(
-      gs_launch_scan(N, tiles_touched, offsets, workspace, capacity, T, num_instances, s),
+      gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace, capacity, T, num_instances,
+                     s),
       "gs_bin_and_sort(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -263,7 +267,8 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
   return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
-                                         grads2d, absgrad, counters, (hipStream_t)stream),
+                                         grads2d, absgrad, nullptr, 0, counters,
+                                         (hipStream_t)stream),
                     "gs_rasterize_bwd");
 }
 
@@ -284,11 +289,116 @@ gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* 
                "NULL array pointer");
     GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
   }
-  return hip_status(gs_launch_project_bwd(N, ld, sh_degree, means, scales, quats, sh,
+  return hip_status(gs_launch_project_bwd(N, ld, nullptr, ld, sh_degree, means, scales, quats, sh,
                                           gs::make_cam(*cam), gs::make_settings(*settings), radii,
                                           grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities,
                                           dL_dsh, accumulate, (hipStream_t)stream),
                     "gs_project_bwd");
+}
+
+gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
+                                 const int32_t* radii, const float* depths,
+                                 const uint32_t* tiles_touched, int32_t width, int32_t height,
+                                 uint32_t* offsets, uint64_t capacity, uint64_t* counts,
+                                 uint64_t* keys, uint32_t* ids, uint32_t* tile_ranges,
+                                 uint32_t* vis_ids, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(counts != nullptr, "counts is NULL");
+  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+  GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
+  if (N > 0)
+    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets && vis_ids,
+               "NULL array pointer");
+  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
+  const int32_t T = gs_num_tiles(width, height);
+  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
+             "workspace smaller than gs_bin_and_sort_workspace_size()");
+  hipStream_t s = (hipStream_t)stream;
+  gs_status st = hip_status(
+      gs_launch_scan(N, tiles_touched, offsets, vis_ids, workspace, capacity, T, counts, s),
+      "gs_bin_and_sort_packed(scan)");
+  if (st != GS_OK) return st;
+  const uint64_t M = counts[0];
+  if (M >= ((uint64_t)1 << 30))
+    return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
+  if (M > capacity) {
+    snprintf(g_err, sizeof(g_err), "gs_bin_and_sort_packed: %llu instances exceed capacity %llu",
+             (unsigned long long)M, (unsigned long long)capacity);
+    return GS_ERR_CAPACITY;
+  }
+  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
+                                              offsets, width, height, M, keys, ids, tile_ranges,
+                                              workspace, capacity, s),
+                    "gs_bin_and_sort_packed");
+}
+
+gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
+                                  const uint32_t* tile_ranges, const uint32_t* ids,
+                                  const float* splats, const uint32_t* offsets,
+                                  const uint32_t* tiles_touched, uint64_t num_instances,
+                                  const uint32_t* vis_ids, int64_t num_visible,
+                                  const float* background, const gs_settings* settings,
+                                  const float* final_T, const uint32_t* last_idx,
+                                  const float* dL_dimage, float* partials,
+                                  uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                                  uint64_t* counters, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(num_visible >= 0 && num_visible <= N, "num_visible must be in [0, N]");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
+  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
+  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
+  if (N > 0) GS_REQUIRE(ids && splats && offsets && tiles_touched, "NULL splat or offset pointer");
+  if (num_visible > 0) {
+    GS_REQUIRE(vis_ids && grads2d, "NULL vis_ids or gradient pointer");
+    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
+  }
+  if (num_instances > 0) {
+    GS_REQUIRE(partials != nullptr, "partials is NULL");
+    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
+  }
+  // an empty list still needs a non-NULL pointer to select the packed rows
+  static const uint32_t kNoIds = 0;
+  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
+                                         tiles_touched, background, gs::make_settings(*settings),
+                                         final_T, last_idx, dL_dimage, partials, num_instances,
+                                         grads2d, absgrad, vis_ids ? vis_ids : &kNoIds,
+                                         num_visible, counters, (hipStream_t)stream),
+                    "gs_rasterize_bwd_packed");
+}
+
+gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, int64_t N,
+                                int64_t ld, int64_t ldv, int32_t sh_degree, const float* means,
+                                const float* scales, const float* quats, const float* sh,
+                                const gs_camera* cam, const gs_settings* settings,
+                                const int32_t* radii, const float* grads2d, float* dL_dmeans,
+                                float* dL_dscales, float* dL_dquats, float* dL_dopacities,
+                                float* dL_dsh, int32_t accumulate, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_REQUIRE(num_visible >= 0 && num_visible <= N, "num_visible must be in [0, N]");
+  GS_REQUIRE(ldv >= num_visible, "ldv must be >= num_visible");
+  GS_REQUIRE(ldv <= ((int64_t)1 << 40), "ldv too large");
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_CHECK(check_camera(cam));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+  if (num_visible == 0) return GS_OK;
+  GS_REQUIRE(vis_ids && means && scales && quats && sh && radii && grads2d && dL_dmeans &&
+                 dL_dscales && dL_dquats && dL_dopacities && dL_dsh,
+             "NULL array pointer");
+  GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
+  return hip_status(gs_launch_project_bwd(num_visible, ld, vis_ids, ldv, sh_degree, means, scales,
+                                          quats, sh, gs::make_cam(*cam),
+                                          gs::make_settings(*settings), radii, grads2d, dL_dmeans,
+                                          dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
+                                          accumulate, (hipStream_t)stream),
+                    "gs_project_bwd_packed");
 }
 
 gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* image,

@@ -80,28 +80,43 @@ __device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: exclusive scan of tiles_touched -> offsets, total M
+// Stage 2: exclusive scan of tiles_touched -> offsets, total M.  The packed
+// form (kVis) carries a second running sum in the same pass, the count of
+// Gaussians with tiles_touched > 0, and writes their indices in ascending
+// order to vis_ids; its per-block sums follow the first set at sums + nb.
 // ---------------------------------------------------------------------------
 constexpr int kScanItems = 8;
 constexpr int kScanBlock = 256 * kScanItems;
 
+template <bool kVis>
 __global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __restrict__ in,
                                                           int64_t N,
                                                           uint64_t* __restrict__ block_sums) {
   const int64_t base = (int64_t)blockIdx.x * kScanBlock;
-  uint64_t s = 0;
+  uint64_t s = 0, c = 0;
   for (int k = 0; k < kScanItems; ++k) {
     const int64_t i = base + (int64_t)k * 256 + threadIdx.x;
-    if (i < N) s += in[i];
+    if (i < N) {
+      const uint32_t x = in[i];
+      s += x;
+      c += x > 0u ? 1u : 0u;
+    }
   }
   uint64_t excl;
   const uint64_t tot = block_excl_scan_u64(s, excl);
   if (threadIdx.x == 0) block_sums[blockIdx.x] = tot;
+  if (kVis) {
+    const uint64_t ctot = block_excl_scan_u64(c, excl);
+    if (threadIdx.x == 0) block_sums[gridDim.x + blockIdx.x] = ctot;
+  }
 }
 
+// One workgroup per set of nb block sums (blockIdx.x selects the set):
+// exclusive scan in place, the set's total to total[blockIdx.x].
 __global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict__ sums,
                                                             int64_t nb,
                                                             uint64_t* __restrict__ total) {
+  sums += (int64_t)blockIdx.x * nb;
   uint64_t carry = 0;
   for (int64_t b = 0; b < nb; b += 256) {
     const int64_t i = b + threadIdx.x;
@@ -111,19 +126,22 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict
     if (i < nb) sums[i] = carry + excl;
     carry += tot;
   }
-  if (threadIdx.x == 0) *total = carry;
+  if (threadIdx.x == 0) total[blockIdx.x] = carry;
 }
 
+template <bool kVis>
 __global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restrict__ in, int64_t N,
                                                         const uint64_t* __restrict__ sums,
-                                                        uint32_t* __restrict__ out) {
+                                                        uint32_t* __restrict__ out,
+                                                        uint32_t* __restrict__ vis_ids) {
   const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanItems;
   uint32_t v[kScanItems];
-  uint64_t s = 0;
+  uint64_t s = 0, c = 0;
   for (int k = 0; k < kScanItems; ++k) {
     const int64_t i = base + k;
     v[k] = i < N ? in[i] : 0u;
     s += v[k];
+    c += v[k] > 0u ? 1u : 0u;
   }
   uint64_t excl;
   block_excl_scan_u64(s, excl);
@@ -132,6 +150,12 @@ __global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restri
     const int64_t i = base + k;
     if (i < N) out[i] = (uint32_t)run;
     run += v[k];
+  }
+  if (kVis) {
+    block_excl_scan_u64(c, excl);
+    uint64_t vrun = sums[gridDim.x + blockIdx.x] + excl;
+    for (int k = 0; k < kScanItems; ++k)
+      if (v[k] > 0u) vis_ids[vrun++] = (uint32_t)(base + k);
   }
 }
 
@@ -414,8 +438,8 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
   };
   w.keys_alt = (uint64_t*)take(sizeof(uint64_t) * (capacity ? capacity : 1));
   w.ids_alt = (uint32_t*)take(sizeof(uint32_t) * (capacity ? capacity : 1));
-  w.scan_sums = (uint64_t*)take(sizeof(uint64_t) * (nb ? nb : 1));
-  w.total = (uint64_t*)take(sizeof(uint64_t));
+  w.scan_sums = (uint64_t*)take(sizeof(uint64_t) * 2 * (nb ? nb : 1));
+  w.total = (uint64_t*)take(sizeof(uint64_t) * 2);
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
   w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
   w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
@@ -429,29 +453,43 @@ extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32
   return gs::carve(nullptr, N, capacity, T).bytes;
 }
 
-// Scan; writes offsets and the total to *total_host (one synchronising read).
+// Scan; writes offsets and M to totals_host[0] (one synchronising read).
+// With vis_ids non-NULL also the ascending indices of the Gaussians with
+// tiles, and their count V to totals_host[1], in the same read.
 extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets,
-                                     void* workspace, uint64_t capacity, int32_t T,
-                                     uint64_t* total_host, hipStream_t s) {
+                                     uint32_t* vis_ids, void* workspace, uint64_t capacity,
+                                     int32_t T, uint64_t* totals_host, hipStream_t s) {
   using namespace gs;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
+  const bool vis = vis_ids != nullptr;
   if (N == 0) {
-    *total_host = 0;
+    totals_host[0] = 0;
+    if (vis) totals_host[1] = 0;
     return hipSuccess;
   }
   const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
-  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, s, tiles, N, w.scan_sums);
+  if (vis)
+    hipLaunchKernelGGL(scan_reduce_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
+                       w.scan_sums);
+  else
+    hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
+                       w.scan_sums);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, w.scan_sums, nb, w.total);
+  hipLaunchKernelGGL(scan_partials_kernel, dim3(vis ? 2 : 1), dim3(256), 0, s, w.scan_sums, nb,
+                     w.total);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, s, tiles, N, w.scan_sums,
-                     offsets);
+  if (vis)
+    hipLaunchKernelGGL(scan_down_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
+                       w.scan_sums, offsets, vis_ids);
+  else
+    hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
+                       w.scan_sums, offsets, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // straight into the caller's host word: page-locked memory there makes
+  // straight into the caller's host words: page-locked memory there makes
   // this a direct transfer instead of a staged one
-  if ((e = hipMemcpyAsync(total_host, w.total, sizeof(uint64_t), hipMemcpyDeviceToHost, s)) !=
-      hipSuccess)
+  if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
+                          hipMemcpyDeviceToHost, s)) != hipSuccess)
     return e;
   return hipStreamSynchronize(s);
 }
@@ -623,10 +661,11 @@ extern "C" hipError_t gs_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, 
   }
   uint64_t* sums = (uint64_t*)workspace;
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
-  hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums);
+  hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, sums, nb, total);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums, out);
+  hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums,
+                     out, nullptr);
   return hipGetLastError();
 }

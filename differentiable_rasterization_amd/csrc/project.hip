@@ -371,17 +371,24 @@ __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, 
 // splats, condition numbers 1e4-1e5) loses about u times the condition
 // number in fp32; the kernel moves ~300 bytes per Gaussian against a few
 // hundred fp64 operations, so it stays memory-bound.
-template <int DEG>
+//
+// Packed form (kPacked): row r handles Gaussian vis_ids[r]; its 2D gradient
+// record is row r of grads2d and its gradients go to row r of the output
+// planes (leading dimension ldo), so nothing is written for Gaussians off
+// the list.  Otherwise row r is Gaussian r and ldo = ld.
+template <int DEG, bool kPacked>
 __global__ __launch_bounds__(256) void project_bwd_kernel(
-    int64_t N, int64_t ld, const float* __restrict__ means,
+    int64_t N, int64_t ld, const uint32_t* __restrict__ vis_ids, int64_t ldo,
+    const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ sh, Cam cam, Settings st, const int32_t* __restrict__ radii,
     const float4* __restrict__ grads2d, float* __restrict__ o_means,
     float* __restrict__ o_scales, float* __restrict__ o_quats, float* __restrict__ o_opac,
     float* __restrict__ o_sh, int accumulate) {
   constexpr int K = (DEG + 1) * (DEG + 1);
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N) return;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= N) return;
+  const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
   const bool vis = radii[i] > 0;
   // every load of a visible lane is issued here, ahead of the fp64 chain, so
   // that each lane keeps its whole working set in flight (the kernel runs
@@ -398,9 +405,9 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
-    r0 = grads2d[4 * i + 0];
-    r1 = grads2d[4 * i + 1];
-    r2 = grads2d[4 * i + 2];
+    r0 = grads2d[4 * r + 0];
+    r1 = grads2d[4 * r + 1];
+    r2 = grads2d[4 * r + 2];
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
   }
@@ -442,7 +449,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
       double wj = 0.0;
 #pragma unroll
       for (int ch = 0; ch < 3; ++ch) {
-        const int64_t p = (int64_t)(j * 3 + ch) * ld + i;
+        const int64_t p = (int64_t)(j * 3 + ch) * ldo + r;
         const float gval = Yf[j] * gcol[ch];
         o_sh[p] = accumulate ? o_sh[p] + gval : gval;
         wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
@@ -598,15 +605,15 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   }
   if (store) {
     for (int k = 0; k < 3; ++k) {
-      const int64_t p = (int64_t)k * ld + i;
+      const int64_t p = (int64_t)k * ldo + r;
       o_means[p] = accumulate ? o_means[p] + om[k] : om[k];
       o_scales[p] = accumulate ? o_scales[p] + os[k] : os[k];
     }
     for (int k = 0; k < 4; ++k) {
-      const int64_t p = (int64_t)k * ld + i;
+      const int64_t p = (int64_t)k * ldo + r;
       o_quats[p] = accumulate ? o_quats[p] + oq[k] : oq[k];
     }
-    o_opac[i] = accumulate ? o_opac[i] + oo : oo;
+    o_opac[r] = accumulate ? o_opac[r] + oo : oo;
   }
 }
 
@@ -635,7 +642,10 @@ extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, cons
   return hipGetLastError();
 }
 
-extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, const float* means,
+// vis_ids NULL: N Gaussians, outputs with leading dimension ld.  Otherwise
+// N rows of the packed list vis_ids, outputs with leading dimension ldo.
+extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
+                                            int64_t ldo, int deg, const float* means,
                                             const float* scales, const float* quats,
                                             const float* sh, const gs::Cam& cam,
                                             const gs::Settings& st, const int32_t* radii,
@@ -644,17 +654,20 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, int deg, cons
                                             float* o_sh, int accumulate, hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
-#define GS_PBWD(D)                                                                         \
-  hipLaunchKernelGGL(gs::project_bwd_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, \
-                     N, ld, means, scales, quats, sh, cam, st, radii,                      \
-                     (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, o_sh,     \
-                     accumulate)
+#define GS_PBWD(D, PK)                                                                    \
+  hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK>), dim3((unsigned)blocks), dim3(256), 0,  \
+                     stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh, cam,  \
+                     st, radii, (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, \
+                     o_sh, accumulate)
+#define GS_PBWD2(D) \
+  if (vis_ids) GS_PBWD(D, true); else GS_PBWD(D, false)
   switch (deg) {
-    case 0: GS_PBWD(0); break;
-    case 1: GS_PBWD(1); break;
-    case 2: GS_PBWD(2); break;
-    default: GS_PBWD(3); break;
+    case 0: GS_PBWD2(0); break;
+    case 1: GS_PBWD2(1); break;
+    case 2: GS_PBWD2(2); break;
+    default: GS_PBWD2(3); break;
   }
+#undef GS_PBWD2
 #undef GS_PBWD
   return hipGetLastError();
 }

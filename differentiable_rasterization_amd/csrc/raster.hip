@@ -531,17 +531,22 @@ __device__ inline void store_rec(float4* __restrict__ r, const float a[kFieldsAb
   r[2] = make_float4(a[8], a[9], a[10], 0.0f);
 }
 
+// Row r of grads2d sums the slots of Gaussian r, or of Gaussian vis_ids[r]
+// in the packed form (kPacked), where the rows follow that list.
+template <bool kPacked>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(
-    int64_t N, const uint32_t* __restrict__ offsets, const uint32_t* __restrict__ tiles,
-    const float4* __restrict__ partials, float4* __restrict__ grads2d) {
+    int64_t N, const uint32_t* __restrict__ vis_ids, const uint32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ tiles, const float4* __restrict__ partials,
+    float4* __restrict__ grads2d) {
   __shared__ uint32_t s_big[256];
   __shared__ uint32_t s_nbig;
   __shared__ float s_red[kFieldsAbs][256];
   const int t = threadIdx.x;
-  const int64_t i = (int64_t)blockIdx.x * 256 + t;
+  const int64_t r = (int64_t)blockIdx.x * 256 + t;
   if (t == 0) s_nbig = 0;
   __syncthreads();
-  if (i < N) {
+  if (r < N) {
+    const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
     const uint32_t cnt = tiles[i];
     if (cnt > kSmallSeg) {
       s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)t;
@@ -549,13 +554,14 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
       float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
       const uint64_t base = offsets[i];
       for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
-      store_rec(grads2d + 4 * i, a);
+      store_rec(grads2d + 4 * r, a);
     }
   }
   __syncthreads();
   const uint32_t nbig = s_nbig;
   for (uint32_t b = 0; b < nbig; ++b) {
-    const int64_t gi = (int64_t)blockIdx.x * 256 + s_big[b];
+    const int64_t gr = (int64_t)blockIdx.x * 256 + s_big[b];
+    const int64_t gi = kPacked ? (int64_t)vis_ids[gr] : gr;
     const uint32_t cnt = tiles[gi];
     const uint64_t base = offsets[gi];
     float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -570,10 +576,10 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
       __syncthreads();
     }
     if (t == 0) {
-      float r[kFieldsAbs];
+      float sum[kFieldsAbs];
 #pragma unroll
-      for (int q = 0; q < kFieldsAbs; ++q) r[q] = s_red[q][0];
-      store_rec(grads2d + 4 * gi, r);
+      for (int q = 0; q < kFieldsAbs; ++q) sum[q] = s_red[q][0];
+      store_rec(grads2d + 4 * gr, sum);
     }
     __syncthreads();
   }
@@ -668,6 +674,7 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, cons
                                            const float* final_T, const uint32_t* last_idx,
                                            const float* dL_dimage, float* partials,
                                            uint64_t capacity, float* grads2d, int absgrad,
+                                           const uint32_t* vis_ids, int64_t num_visible,
                                            uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
@@ -684,9 +691,16 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, cons
   }
 #undef GS_RBWD
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || N == 0) return e;
-  hipLaunchKernelGGL(gs::reduce_partials_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
-                     N, offsets, tiles, part, (float4*)grads2d);
+  // dense rows: one per Gaussian; packed rows: one per entry of vis_ids
+  const int64_t rows = vis_ids ? num_visible : N;
+  if (e != hipSuccess || rows == 0) return e;
+  const dim3 rgrid((unsigned)((rows + 255) / 256));
+  if (vis_ids)
+    hipLaunchKernelGGL(gs::reduce_partials_kernel<true>, rgrid, dim3(256), 0, s, rows, vis_ids,
+                       offsets, tiles, part, (float4*)grads2d);
+  else
+    hipLaunchKernelGGL(gs::reduce_partials_kernel<false>, rgrid, dim3(256), 0, s, rows, nullptr,
+                       offsets, tiles, part, (float4*)grads2d);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP = 0, 1, 2, 3
 EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_tiles",
             "gs_project_fwd", "gs_bin_and_sort_workspace_size", "gs_bin_and_sort",
             "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd", "gs_image_loss_grad",
-            "gs_densify_prune_workspace_size", "gs_densify_prune")
+            "gs_densify_prune_workspace_size", "gs_densify_prune", "gs_bin_and_sort_packed",
+            "gs_rasterize_bwd_packed", "gs_project_bwd_packed")
 
 
 class GsError(RuntimeError):
@@ -82,6 +83,15 @@ def load():
     lib.gs_project_bwd.restype = C.c_int
     lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 2 + [P] * 5 + \
         [i32, P]
+    lib.gs_bin_and_sort_packed.restype = C.c_int
+    lib.gs_bin_and_sort_packed.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
+                                           P, P, C.c_size_t, P]
+    lib.gs_rasterize_bwd_packed.restype = C.c_int
+    lib.gs_rasterize_bwd_packed.argtypes = [i64, i64, i32, i32] + [P] * 5 + [u64, P, i64] + \
+        [P] * 6 + [u64, P, i32, P, P]
+    lib.gs_project_bwd_packed.restype = C.c_int
+    lib.gs_project_bwd_packed.argtypes = [i64, P, i64, i64, i64, i32] + [P] * 4 + [P, P] + \
+        [P] * 2 + [P] * 5 + [i32, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -207,6 +217,48 @@ def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, ra
                               _p(dL_dsh), int(accumulate), _stream(stream)))
 
 
+def gs_bin_and_sort_packed(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                           capacity, keys, ids, tile_ranges, vis_ids, workspace, workspace_bytes,
+                           counts, stream=None):
+    """Returns (status, M, V); GS_ERR_CAPACITY is returned, not raised.
+    ``counts``: two-element int64 host tensor (page-locked saves a staging
+    copy) that receives M and V."""
+    lib = load()
+    st = lib.gs_bin_and_sort_packed(N, ld, _p(means2d), _p(radii), _p(depths),
+                                    _p(tiles_touched), width, height, _p(offsets), capacity,
+                                    _p(counts), _p(keys), _p(ids), _p(tile_ranges),
+                                    _p(vis_ids), _p(workspace), workspace_bytes,
+                                    _stream(stream))
+    if st not in (GS_OK, GS_ERR_CAPACITY):
+        _check(st)
+    return st, int(counts[0]), int(counts[1])
+
+
+def gs_rasterize_bwd_packed(N, ld, width, height, tile_ranges, ids, splats, offsets,
+                            tiles_touched, num_instances, vis_ids, num_visible, background,
+                            settings, final_T, last_idx, dL_dimage, partials, partials_capacity,
+                            grads2d, absgrad=0, counters=None, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_bwd_packed(N, ld, width, height, _p(tile_ranges), _p(ids),
+                                       _p(splats), _p(offsets), _p(tiles_touched),
+                                       int(num_instances), _p(vis_ids), int(num_visible), bg,
+                                       C.byref(settings), _p(final_T), _p(last_idx),
+                                       _p(dL_dimage), _p(partials), int(partials_capacity),
+                                       _p(grads2d), int(absgrad), _p(counters), _stream(stream)))
+
+
+def gs_project_bwd_packed(num_visible, vis_ids, N, ld, ldv, sh_degree, means, scales, quats, sh,
+                          cam, settings, radii, grads2d, dL_dmeans, dL_dscales, dL_dquats,
+                          dL_dopacities, dL_dsh, accumulate=0, stream=None):
+    lib = load()
+    _check(lib.gs_project_bwd_packed(int(num_visible), _p(vis_ids), N, ld, ldv, sh_degree,
+                                     _p(means), _p(scales), _p(quats), _p(sh), C.byref(cam),
+                                     C.byref(settings), _p(radii), _p(grads2d), _p(dL_dmeans),
+                                     _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
+                                     _p(dL_dsh), int(accumulate), _stream(stream)))
+
+
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
     lib = load()
     _check(lib.gs_image_loss_grad(int(kind), int(count), _p(image), _p(target), _p(dL_dimage),
@@ -292,10 +344,16 @@ class Frame:
     """Buffers and calls for one camera: projection, binning + sort,
     compositing, and the two backward stages.  All buffers are torch tensors
     on the current device; only ``gs_bin_and_sort`` synchronises (to read
-    the instance count)."""
+    the instance count).
+
+    ``packed=True`` runs the packed calls: ``vis_ids[:V]`` lists the visible
+    Gaussians, ``grads2d[:V]`` and columns ``[:, :V]`` of the gradient planes
+    hold their rows in that order (leading dimension ``ld``), and nothing is
+    written for the others."""
 
     def __init__(self, ld, sh_degree, width, height, capacity=None, settings=None,
-                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda"):
+                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda",
+                 packed=False):
         import torch
         self.torch = torch
         self.device = device
@@ -327,8 +385,11 @@ class Frame:
         self.dL_dimage = z((height, width, 3), f32)
         self.loss = z((1,), f32)
         # page-locked host word for the instance count (allocated pinned)
-        self.m_host = torch.zeros((1,), dtype=torch.int64, pin_memory=True)
+        self.m_host = torch.zeros((2,), dtype=torch.int64, pin_memory=True)
         self.M = 0
+        self.packed = bool(packed)
+        self.vis_ids = z((max(ld, 1),), u32) if packed else None
+        self.V = 0
         self._alloc_sort(capacity if capacity else max(1024, 4 * ld))
 
     def _alloc_sort(self, capacity):
@@ -350,7 +411,21 @@ class Frame:
                        self.cam, self.settings, self.means2d, self.conics, self.depths,
                        self.radii, self.colors, self.tiles, self.splats)
 
+    def _bin_and_sort_packed(self, g: Gaussians):
+        args = lambda: (g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles, self.W,
+                        self.H, self.offsets, self.capacity, self.keys, self.ids, self.ranges,
+                        self.vis_ids, self.ws, self.ws_bytes, self.m_host)
+        st, M, V = gs_bin_and_sort_packed(*args())
+        if st == GS_ERR_CAPACITY:
+            self._alloc_sort(int(M * 1.25) + 1024)
+            st, M, V = gs_bin_and_sort_packed(*args())
+            _check(st)
+        self.M, self.V = M, V
+        return M
+
     def bin_and_sort(self, g: Gaussians):
+        if self.packed:
+            return self._bin_and_sort_packed(g)
         st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
                                 self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
                                 self.ranges, self.ws, self.ws_bytes, num_instances=self.m_host)
@@ -381,12 +456,25 @@ class Frame:
 
     def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None, absgrad=False):
         dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        if self.packed:
+            gs_rasterize_bwd_packed(g.N, g.ld, self.W, self.H, self.ranges, self.ids,
+                                    self.splats, self.offsets, self.tiles, self.M, self.vis_ids,
+                                    self.V, self.background, self.settings, self.final_T,
+                                    self.last_idx, dl, self.partials, self.capacity,
+                                    self.grads2d, absgrad=int(bool(absgrad)), counters=counters)
+            return
         gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
                          self.offsets, self.tiles, self.M, self.background, self.settings,
                          self.final_T, self.last_idx, dl, self.partials, self.capacity,
                          self.grads2d, absgrad=int(bool(absgrad)), counters=counters)
 
     def project_backward(self, g: Gaussians, accumulate=0):
+        if self.packed:
+            gs_project_bwd_packed(self.V, self.vis_ids, g.N, g.ld, self.ld, g.sh_degree, g.means,
+                                  g.scales, g.quats, g.sh, self.cam, self.settings, self.radii,
+                                  self.grads2d, self.g_means, self.g_scales, self.g_quats,
+                                  self.g_opacities, self.g_sh, accumulate)
+            return
         gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
                        self.settings, self.radii, self.grads2d, self.g_means, self.g_scales,
                        self.g_quats, self.g_opacities, self.g_sh, accumulate)

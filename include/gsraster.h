@@ -232,6 +232,62 @@ GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const 
                          float* dL_dscales, float* dL_dquats, float* dL_dopacities,
                          float* dL_dsh, int32_t accumulate, void* stream);
 
+/* Packed mode (the gsplat guide §4.1 trains with its packed and sparse
+ * gradient switches on: only the Gaussians that reach the image take part
+ * after the projection, and only they receive gradients).  The visible set
+ * is the list of Gaussians with tiles_touched > 0, in ascending index order;
+ * V is its length.  The three calls below replace gs_bin_and_sort,
+ * gs_rasterize_bwd and gs_project_bwd of a frame; projection, compositing and
+ * the loss are the same calls as in the dense path.
+ *
+ * gs_bin_and_sort_packed: gs_bin_and_sort, and in the same pass the visible
+ * list vis_ids [N] (its first V entries are written).  counts (HOST
+ * uint64[2]) receives M then V in the call's one device-to-host read.
+ * Capacity handling and errors as gs_bin_and_sort (with GS_ERR_CAPACITY both
+ * counts and vis_ids are valid). */
+GS_API gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
+                                        const int32_t* radii, const float* depths,
+                                        const uint32_t* tiles_touched, int32_t width,
+                                        int32_t height, uint32_t* offsets, uint64_t capacity,
+                                        uint64_t* counts, uint64_t* keys, uint32_t* ids,
+                                        uint32_t* tile_ranges, uint32_t* vis_ids,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* gs_rasterize_bwd_packed: gs_rasterize_bwd with the segmented reduction run
+ * over the visible list: row r of grads2d [num_visible][16] receives the
+ * 2D gradient record of Gaussian vis_ids[r].  Nothing is written for
+ * Gaussians off the list.  vis_ids / num_visible as gs_bin_and_sort_packed
+ * returned them for the same frame (entries must be < N). */
+GS_API gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
+                                         const uint32_t* tile_ranges, const uint32_t* ids,
+                                         const float* splats, const uint32_t* offsets,
+                                         const uint32_t* tiles_touched, uint64_t num_instances,
+                                         const uint32_t* vis_ids, int64_t num_visible,
+                                         const float* background, const gs_settings* settings,
+                                         const float* final_T, const uint32_t* last_idx,
+                                         const float* dL_dimage, float* partials,
+                                         uint64_t partials_capacity, float* grads2d,
+                                         int32_t absgrad, uint64_t* counters, void* stream);
+
+/* gs_project_bwd_packed: gs_project_bwd for the num_visible Gaussians of
+ * vis_ids only, in sparse form: the parameters are read at vis_ids[r]
+ * (planes [p][ld] of the N Gaussians), the 2D record at row r of grads2d,
+ * and the gradients go to column r of the packed output planes
+ * (dL_dmeans [3][ldv], dL_dscales [3][ldv], dL_dquats [4][ldv],
+ * dL_dopacities [ldv], dL_dsh [K*3][ldv], ldv >= num_visible).  Together
+ * with vis_ids they are the gradient as (index, value) rows; Gaussians off
+ * the list have zero gradient and nothing is written for them.
+ * accumulate = 1 adds into the packed rows (the same list only). */
+GS_API gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, int64_t N,
+                                       int64_t ld, int64_t ldv, int32_t sh_degree,
+                                       const float* means, const float* scales,
+                                       const float* quats, const float* sh,
+                                       const gs_camera* cam, const gs_settings* settings,
+                                       const int32_t* radii, const float* grads2d,
+                                       float* dL_dmeans, float* dL_dscales, float* dL_dquats,
+                                       float* dL_dopacities, float* dL_dsh, int32_t accumulate,
+                                       void* stream);
+
 /* Loss gradient of a rendered image against a target, both [count] floats:
  * kind 0 = L2 (sum (x-y)^2, gradient 2(x-y)), kind 1 = L1 (sum |x-y|,
  * gradient sign(x-y), sign(0) = 0).  Writes dL_dimage [count]; if loss (a

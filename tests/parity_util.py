@@ -41,15 +41,18 @@ def torch_cuda():
 
 def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
               loss_kind=None, target=None, backward=True, depth_alpha=False, capacity=None,
-              dL_dimage=None, absgrad=False):
+              dL_dimage=None, absgrad=False, packed=False):
     """Run the five stages on the GPU; returns numpy arrays in the natural
-    [N, ...] layout plus the raw Frame."""
+    [N, ...] layout plus the raw Frame.  With ``packed`` the packed calls
+    run, and their rows are scattered back to the [N, ...] layout (zeros off
+    the visible list); ``vis_ids`` and ``V`` are returned too."""
     import torch
     from differentiable_rasterization_amd import raster
     g = raster.Gaussians.from_scene(scene, ld=ld)
     st = raster.default_settings(**(settings or {}))
     fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=capacity,
-                      settings=st, background=background, with_depth_alpha=depth_alpha)
+                      settings=st, background=background, with_depth_alpha=depth_alpha,
+                      packed=packed)
     fr.forward(g, cam)
     out = {}
     if backward:
@@ -73,11 +76,26 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
         final_T=fr.final_T.cpu().numpy(), last=fr.last_idx.cpu().numpy().view(np.uint32))
     if depth_alpha:
         out.update(depth=fr.out_depth.cpu().numpy(), alpha=fr.out_alpha.cpu().numpy())
+    if packed:
+        vis_ids = fr.vis_ids[:fr.V].cpu().numpy().view(np.uint32).copy()
+        out.update(vis_ids=vis_ids, V=fr.V)
+        rows = vis_ids.astype(np.int64)
+
+        def unpack(t):
+            a = (t[:, :fr.V].T.contiguous() if t.dim() == 2 else t[:fr.V]).cpu().numpy()
+            d = np.zeros((N,) + a.shape[1:], a.dtype)
+            d[rows] = a
+            return d
     if backward:
         K = (scene.sh_degree + 1) ** 2
-        rec = fr.grads2d[:N].cpu().numpy()
-        vis = out["radii"] > 0
-        rec[~vis] = 0.0  # records of culled Gaussians are not written
+        if packed:
+            rec = np.zeros((N, 16), np.float32)
+            rec[rows] = fr.grads2d[:fr.V].cpu().numpy()
+            T = unpack
+        else:
+            rec = fr.grads2d[:N].cpu().numpy()
+            vis = out["radii"] > 0
+            rec[~vis] = 0.0  # records of culled Gaussians are not written
         out.update(dL_dimage=fr.dL_dimage.cpu().numpy() if dL_dimage is None else dL_dimage,
                    loss=float(fr.loss.cpu().numpy()[0]),
                    g_means2d=rec[:, 0:2].copy(), g_conics=rec[:, 2:5].copy(),
@@ -90,26 +108,42 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
     return out
 
 
-def gpu_project_bwd(scene, cam, g2, ld=None):
+def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None):
     """GPU projection backward fed the given 2D gradients (dict with means2d
     [N,2], conics [N,3], opacities [N], colors [N,3]), packed into the 2D
-    gradient records; returns the 3D gradients in [N, ...] layout."""
+    gradient records; returns the 3D gradients in [N, ...] layout.  With
+    ``vis_ids`` the packed call runs over that list (rows in list order) and
+    its rows are scattered back (zeros off the list)."""
     import torch
     from differentiable_rasterization_amd import raster
     N = scene.n
     g = raster.Gaussians.from_scene(scene, ld=ld)
-    fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=1024)
+    fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=1024,
+                      packed=vis_ids is not None)
     fr.project(g, cam)
     rec = np.zeros(tuple(fr.grads2d.shape), np.float32)
     rec[:N, 0:2] = g2["means2d"]
     rec[:N, 2:5] = g2["conics"]
     rec[:N, 5] = g2["opacities"]
     rec[:N, 6:9] = g2["colors"]
+    if vis_ids is not None:
+        rows = np.asarray(vis_ids, np.int64)
+        V = len(rows)
+        rec[:V] = rec[rows].copy()
+        fr.V = V
+        if V:
+            fr.vis_ids[:V].copy_(torch.from_numpy(rows.astype(np.int32)))
     fr.grads2d.copy_(torch.from_numpy(rec))
     fr.project_backward(g)
     torch.cuda.synchronize()
     K = (scene.sh_degree + 1) ** 2
     T = lambda t: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
+    if vis_ids is not None:
+        def T(t):
+            a = t[:, :V].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:V].cpu().numpy()
+            d = np.zeros((N,) + a.shape[1:], a.dtype)
+            d[rows] = a
+            return d
     return dict(radii=fr.radii[:N].cpu().numpy(), g_means=T(fr.g_means), g_scales=T(fr.g_scales),
                 g_quats=T(fr.g_quats), g_sh=T(fr.g_sh).reshape(N, K, 3),
                 g_opacities=T(fr.g_opacities))
@@ -187,12 +221,12 @@ def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
 # stages in isolation (data flows from the oracle to the GPU only).
 # ---------------------------------------------------------------------------
 def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alpha=False,
-                    ld=None):
+                    ld=None, packed=False):
     import time
     t0 = time.time()
     print("\n[parity] case %s" % name, flush=True)
     gpu = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=target,
-                    backward=backward, depth_alpha=depth_alpha, ld=ld)
+                    backward=backward, depth_alpha=depth_alpha, ld=ld, packed=packed)
     t1 = time.time()
     orc = oracle.render(scene, cam, None, bg, with_margin=True)
     r = dict(name=name, scene=scene, cam=cam, loss=loss, bg=bg, target=target, gpu=gpu, orc=orc)
@@ -205,8 +239,10 @@ def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alp
     if backward:
         # the isolated run also exercises the absolute-gradient variant
         r["gpu_iso"] = gpu_frame(scene, cam, background=bg, dL_dimage=r["dl"], ld=ld,
-                                 absgrad=True)
-        r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld)
+                                 absgrad=True, packed=packed)
+        # packed: the projection backward runs over the oracle's visible list
+        vis_ids = np.flatnonzero(orc["proj"]["tiles"] > 0) if packed else None
+        r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld, vis_ids=vis_ids)
     print("[parity] %s: N=%d M=%d gpu %.1fs oracle %.1fs" % (
         name, scene.n, gpu["M"], t1 - t0 + time.time() - t2, t2 - t1), flush=True)
     return r

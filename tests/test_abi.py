@@ -154,6 +154,40 @@ def test_raster_and_loss_reject_bad_arguments(lib):
         raster.GS_ERR_INVALID_ARGUMENT
 
 
+def test_packed_calls_reject_bad_arguments(lib):
+    dummy = C.c_void_p(256)
+    st = raster.default_settings()
+    bg = (C.c_float * 3)(0, 0, 0)
+    counts = (C.c_uint64 * 2)()
+
+    def bas(N=4, ld=4, vis=dummy, cnt=counts):
+        return lib.gs_bin_and_sort_packed(N, ld, dummy, dummy, dummy, dummy, 64, 64, dummy, 100,
+                                          cnt, dummy, dummy, dummy, vis, dummy, 1 << 30, None)
+    assert bas(vis=None) == raster.GS_ERR_INVALID_ARGUMENT   # the visible list is required
+    assert bas(cnt=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bas(ld=3) == raster.GS_ERR_INVALID_ARGUMENT
+
+    def rbwd(V=2, vis=dummy, grads=dummy):
+        return lib.gs_rasterize_bwd_packed(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, 10,
+                                           vis, V, bg, C.byref(st), dummy, dummy, dummy, dummy,
+                                           10, grads, 0, None, None)
+    assert rbwd(V=5) == raster.GS_ERR_INVALID_ARGUMENT       # more rows than Gaussians
+    assert rbwd(V=-1) == raster.GS_ERR_INVALID_ARGUMENT
+    assert rbwd(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert rbwd(grads=C.c_void_p(72)) == raster.GS_ERR_INVALID_ARGUMENT
+
+    def pbwd(V=2, N=4, ldv=2, vis=dummy, acc=0, deg=3):
+        return lib.gs_project_bwd_packed(V, vis, N, N, ldv, deg, dummy, dummy, dummy, dummy,
+                                         C.byref(_cam()), C.byref(st), dummy, dummy, dummy,
+                                         dummy, dummy, dummy, dummy, acc, None)
+    assert pbwd(ldv=1) == raster.GS_ERR_INVALID_ARGUMENT      # ldv < num_visible
+    assert pbwd(V=5) == raster.GS_ERR_INVALID_ARGUMENT
+    assert pbwd(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert pbwd(acc=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert pbwd(deg=4) == raster.GS_ERR_INVALID_ARGUMENT
+    assert pbwd(V=0, ldv=0, vis=None) == raster.GS_OK         # empty list: nothing to launch
+
+
 def test_densify_rejects_bad_arguments(lib):
     dummy = C.c_void_p(256)
     n_out = C.c_int64(0)
