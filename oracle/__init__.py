@@ -417,3 +417,217 @@ def densify_prune(means, scales, quats, opacities, sh, dL_dmeans, clone_fraction
     pick = lambda a: np.asarray(a)[src]
     return dict(means=pick(means), scales=pick(scales), quats=pick(quats),
                 opacities=pick(opacities), sh=pick(sh), src=src)
+
+
+# --------------------------------------------------------------------------
+# Image loss of a training step (gsplat guide, lmnt.cn/news/262699, section
+# 4.1 training loop): the mean absolute error plus 0.2 times (1 - SSIM).  The
+# page calls an ssim() it does not define; this is the structural similarity
+# index of Wang et al. (2004) in its usual training form: per channel, an
+# 11 x 11 Gaussian window of standard deviation 1.5 normalised to sum 1,
+# zero padding outside the image (one value per pixel), C1 = 0.01^2 and
+# C2 = 0.03^2 (dynamic range 1), averaged over every pixel and channel.
+# --------------------------------------------------------------------------
+SSIM_WINDOW = 11
+SSIM_SIGMA = 1.5
+SSIM_C1 = 0.01 ** 2
+SSIM_C2 = 0.03 ** 2
+
+
+def ssim_window_1d(size=SSIM_WINDOW, sigma=SSIM_SIGMA):
+    """The 1D factor of the separable window: exp(-k^2 / (2 sigma^2)) for
+    k = -(size-1)/2 .. (size-1)/2, normalised to sum 1."""
+    k = np.arange(size, dtype=np.float64) - (size - 1) / 2.0
+    g = np.exp(-k * k / (2.0 * sigma * sigma))
+    return g / g.sum()
+
+
+def window_sum(plane, w1=None):
+    """Windowed sum of an [H, W] plane with the 2D window w1[a] w1[b]:
+    out[y, x] = sum over a, b of w1[a] w1[b] plane[y + a - r, x + b - r],
+    terms outside the plane taken as 0.  One array term per window offset."""
+    w1 = ssim_window_1d() if w1 is None else w1
+    plane = np.asarray(plane, np.float64)
+    H, W = plane.shape
+    r = len(w1) // 2
+    out = np.zeros((H, W))
+    for a in range(len(w1)):
+        dy = a - r
+        y0, y1 = max(0, -dy), min(H, H - dy)
+        for b in range(len(w1)):
+            dx = b - r
+            x0, x1 = max(0, -dx), min(W, W - dx)
+            if y0 < y1 and x0 < x1:
+                out[y0:y1, x0:x1] += w1[a] * w1[b] * plane[y0 + dy:y1 + dy, x0 + dx:x1 + dx]
+    return out
+
+
+def _channels(f, img):
+    return np.stack([f(img[..., c]) for c in range(img.shape[2])], axis=2)
+
+
+def ssim_stats(x, y):
+    """Windowed means and second moments of [H, W, C] images: mu_x, mu_y,
+    E[x^2], E[y^2], E[xy] per pixel and channel."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    return (_channels(window_sum, x), _channels(window_sum, y), _channels(window_sum, x * x),
+            _channels(window_sum, y * y), _channels(window_sum, x * y))
+
+
+def ssim_pointwise(mx, my, sxx, syy, sxy):
+    """SSIM index from the windowed statistics, and its partial derivatives
+    with respect to mu_x, E[x^2] and E[xy] (mu_y, E[y^2] held fixed):
+    sigma_x^2 = E[x^2] - mu_x^2, sigma_xy = E[xy] - mu_x mu_y,
+    s = (2 mu_x mu_y + C1)(2 sigma_xy + C2) / ((mu_x^2 + mu_y^2 + C1)(sigma_x^2 + sigma_y^2 + C2))."""
+    vx = sxx - mx * mx
+    vy = syy - my * my
+    cxy = sxy - mx * my
+    A1 = 2.0 * mx * my + SSIM_C1
+    A2 = 2.0 * cxy + SSIM_C2
+    B1 = mx * mx + my * my + SSIM_C1
+    B2 = vx + vy + SSIM_C2
+    s = A1 * A2 / (B1 * B2)
+    # dA1/dmu_x = 2 mu_y, dA2/dmu_x = -2 mu_y, dB1/dmu_x = 2 mu_x, dB2/dmu_x = -2 mu_x
+    d_mu = 2.0 * my * (A2 - A1) / (B1 * B2) + 2.0 * mx * s * (1.0 / B2 - 1.0 / B1)
+    d_xx = -s / B2               # dB2/dE[x^2] = 1
+    d_xy = 2.0 * A1 / (B1 * B2)  # dA2/dE[xy] = 2
+    return s, d_mu, d_xx, d_xy
+
+
+def ssim_map(x, y):
+    return ssim_pointwise(*ssim_stats(x, y))[0]
+
+
+def l1_dssim_loss_grad(image, target, lam=0.2):
+    """Loss = mean|x - y| + lam (1 - mean ssim(x, y)) over the n = H W C
+    elements of [H, W, C] images x = image, y = target, and dLoss/dx.
+
+    L1 part: sign(x - y) / n (sign(0) = 0).  SSIM part: with s(p) a function
+    of the windowed statistics at pixel p, d(sum_p s)/dx(q) = sum_p w(p - q)
+    [ds/dmu_x(p) + 2 x(q) ds/dE[x^2](p) + y(q) ds/dE[xy](p)] over the pixels
+    p of the image; the window is symmetric, so this is the same
+    zero-padded windowed sum applied to the three derivative maps.
+    Returns (loss, gradient, parts) with parts the per-pixel pieces that
+    the error scale uses."""
+    x = np.asarray(image, np.float64)
+    y = np.asarray(target, np.float64)
+    n = x.size
+    stats = ssim_stats(x, y)
+    s, d_mu, d_xx, d_xy = ssim_pointwise(*stats)
+    b_mu, b_xx, b_xy = (_channels(window_sum, d) for d in (d_mu, d_xx, d_xy))
+    g_ssim = b_mu + 2.0 * x * b_xx + y * b_xy
+    g = np.sign(x - y) / n - lam / n * g_ssim
+    loss = np.abs(x - y).sum() / n + lam * (1.0 - s.sum() / n)
+    return loss, g, dict(stats=stats, s=s, d=(d_mu, d_xx, d_xy), b=(b_mu, b_xx, b_xy))
+
+
+def l1_dssim_errscale(image, target, lam=0.2, parts=None, delta=None):
+    """First-order bound on the gradient error of an fp32 evaluation that
+    forms the five windowed statistics with relative error at most delta
+    each (non-negative images: sums of non-negative terms), then the three
+    derivative maps and their windowed sums in fp32.  The derivative maps'
+    sensitivities to the statistics are taken by central differences of
+    ssim_pointwise in fp64; the windowed sums of signed maps add delta times
+    the sums of their magnitudes.  Returns a map of the gradient's shape."""
+    x = np.asarray(image, np.float64)
+    y = np.asarray(target, np.float64)
+    n = x.size
+    delta = 32.0 * 2.0 ** -24 if delta is None else delta
+    if parts is None:
+        parts = l1_dssim_loss_grad(x, y, lam)[2]
+    stats = list(parts["stats"])
+    err_d = [np.zeros_like(x) for _ in range(3)]
+    for k in range(5):
+        h = 1e-7 * np.maximum(np.abs(stats[k]), 1e-6)
+        up, dn = list(stats), list(stats)
+        up[k] = stats[k] + h
+        dn[k] = stats[k] - h
+        dp = ssim_pointwise(*up)[1:]
+        dm = ssim_pointwise(*dn)[1:]
+        for j in range(3):
+            sens = np.abs(dp[j] - dm[j]) / (2.0 * h)
+            err_d[j] += sens * np.abs(stats[k]) * delta
+    d = parts["d"]
+    # fp32 rounding of the maps themselves
+    for j in range(3):
+        err_d[j] += 8.0 * 2.0 ** -24 * np.abs(d[j])
+    blur_err = [_channels(window_sum, e) for e in err_d]
+    blur_mag = [_channels(window_sum, np.abs(dj)) for dj in d]
+    b = parts["b"]
+    e = (blur_err[0] + 2.0 * np.abs(x) * blur_err[1] + np.abs(y) * blur_err[2]
+         + delta * (blur_mag[0] + 2.0 * np.abs(x) * blur_mag[1] + np.abs(y) * blur_mag[2])
+         + 4.0 * 2.0 ** -24 * (np.abs(b[0]) + 2.0 * np.abs(x * b[1]) + np.abs(y * b[2])))
+    return lam / n * e
+
+
+# --------------------------------------------------------------------------
+# Optimiser step (gsplat guide, lmnt.cn/news/262699, section 4.2: Adam with
+# one learning rate per parameter group, eps 1e-15, betas (0.9, 0.99)).  The
+# rasterizer takes activated scales (exp of the stored log-scales) and
+# opacities (sigmoid of the stored logits), so the step first carries their
+# gradients to the stored values: d/dlog_s = d/ds * s, d/dlogit = d/do *
+# o (1 - o), with s and o the values the forward used.
+# --------------------------------------------------------------------------
+ADAM_LR = dict(means=1.6e-4, scales=5e-3, quats=1e-3, opacities=5e-2, sh=2.5e-3)
+ADAM_BETAS = (0.9, 0.99)
+ADAM_EPS = 1e-15
+
+
+def adam_update(p, g, m, v, step, lr, betas=ADAM_BETAS, eps=ADAM_EPS):
+    """One step of Adam (Kingma and Ba, 2015): m and v are exponential moving
+    averages of g and g^2; with the bias corrections 1 - beta^step,
+    p -= lr m_hat / (sqrt(v_hat) + eps).  fp64; returns (p, m, v)."""
+    b1, b2 = betas
+    g = np.asarray(g, np.float64)
+    m = b1 * np.asarray(m, np.float64) + (1.0 - b1) * g
+    v = b2 * np.asarray(v, np.float64) + (1.0 - b2) * g * g
+    m_hat = m / (1.0 - b1 ** step)
+    v_hat = v / (1.0 - b2 ** step)
+    return np.asarray(p, np.float64) - lr * m_hat / (np.sqrt(v_hat) + eps), m, v
+
+
+def raw_grads(grads, act, sel):
+    """Gradients with respect to the stored parameters of the Gaussians sel,
+    from those with respect to the activated ones: log-scales through
+    s = exp(log_s) (ds/dlog_s = s), logits through o = 1 / (1 + exp(-x))
+    (do/dx = o (1 - o)); means, quaternions and SH pass unchanged."""
+    s_act = np.asarray(act["scales"], np.float64)[sel]
+    o_act = np.asarray(act["opacities"], np.float64)[sel]
+    return dict(means=np.asarray(grads["means"], np.float64),
+                log_scales=np.asarray(grads["scales"], np.float64) * s_act,
+                quats=np.asarray(grads["quats"], np.float64),
+                logits=np.asarray(grads["opacities"], np.float64) * o_act * (1.0 - o_act),
+                sh=np.asarray(grads["sh"], np.float64))
+
+
+def adam_train_step(raw, act, grads, m, v, step, rows=None, lr=None, betas=ADAM_BETAS,
+                    eps=ADAM_EPS):
+    """One optimiser step over the Gaussians.
+
+    raw: dict means [N,3], log_scales [N,3], quats [N,4], logits [N], sh [N,K,3]
+    (the stored parameters); act: dict scales [N,3], opacities [N] (the
+    activated values the forward used); grads: gradients with respect to
+    means, scales, quats, opacities, sh as the backward returns them (dense
+    [N,...], or with ``rows`` one gradient row per listed Gaussian: the
+    packed form, where only the listed Gaussians are updated and the others
+    keep parameters and moments); m, v: dicts of the moments, shaped as raw.
+    Returns (raw, act, m, v), new dicts in fp64."""
+    lr = dict(ADAM_LR, **(lr or {}))
+    N = len(raw["means"])
+    sel = np.arange(N) if rows is None else np.asarray(rows, np.int64)
+    g_raw = raw_grads(grads, act, sel)
+    group = dict(means="means", log_scales="scales", quats="quats", logits="opacities", sh="sh")
+    out_raw, out_m, out_v = {}, {}, {}
+    for k in ("means", "log_scales", "quats", "logits", "sh"):
+        p = np.array(raw[k], np.float64)
+        mk = np.array(m[k], np.float64)
+        vk = np.array(v[k], np.float64)
+        p[sel], mk[sel], vk[sel] = adam_update(p[sel], g_raw[k], mk[sel], vk[sel], step,
+                                               lr[group[k]], betas, eps)
+        out_raw[k], out_m[k], out_v[k] = p, mk, vk
+    out_act = dict(scales=np.array(act["scales"], np.float64),
+                   opacities=np.array(act["opacities"], np.float64))
+    out_act["scales"][sel] = np.exp(out_raw["log_scales"][sel])
+    out_act["opacities"][sel] = 1.0 / (1.0 + np.exp(-out_raw["logits"][sel]))
+    return out_raw, out_act, out_m, out_v
