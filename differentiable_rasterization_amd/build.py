@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgsraster.so")
-SOURCES = ["project.hip", "binsort.hip", "raster.hip", "densify.hip", "api.hip"]
+SOURCES = ["project.hip", "binsort.hip", "raster.hip", "densify.hip", "train.hip",
+           "api.hip"]
 ARCH = "gfx950"
 
 

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
+
 #include "gs_common.h"
 
 extern "C" {
@@ -45,6 +47,14 @@ hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t*
                                 int64_t num_visible, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
+size_t gs_ssim_workspace_bytes(int32_t W, int32_t H);
+hipError_t gs_launch_l1_dssim(int32_t W, int32_t H, const float* img, const float* tgt,
+                              float lambda, float* g, float* loss, void* workspace,
+                              hipStream_t s);
+hipError_t gs_launch_adam(int64_t rows, int64_t ld, int64_t ldg, const uint32_t* vis_ids, int deg,
+                          int64_t step, const gs_adam_config& cfg, float* const raw[5],
+                          const float* const grad[5], float* scales, float* opacities,
+                          float* m, float* v, hipStream_t s);
 int64_t gs_densify_clone_count(int64_t N, float clone_fraction);
 size_t gs_densify_workspace_bytes(int64_t N, float clone_fraction);
 hipError_t gs_launch_densify(int64_t N, int nplanes, const float* const* in_planes, int64_t ld,
@@ -399,6 +409,106 @@ gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, in
                                           dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
                                           accumulate, (hipStream_t)stream),
                     "gs_project_bwd_packed");
+}
+
+size_t gs_l1_dssim_workspace_size(int32_t width, int32_t height) {
+  if (width <= 0 || height <= 0) return 0;
+  return gs_ssim_workspace_bytes(width, height);
+}
+
+gs_status gs_l1_dssim_loss_grad(int32_t width, int32_t height, const float* image,
+                                const float* target, float lambda, float* dL_dimage,
+                                float* loss, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(std::isfinite(lambda) && lambda >= 0.0f, "lambda must be finite and >= 0");
+  GS_REQUIRE(image && target && dL_dimage, "NULL image pointer");
+  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
+  GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+  GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+  GS_REQUIRE(workspace_bytes >= gs_ssim_workspace_bytes(width, height),
+             "workspace smaller than gs_l1_dssim_workspace_size()");
+  return hip_status(gs_launch_l1_dssim(width, height, image, target, lambda, dL_dimage, loss,
+                                       workspace, (hipStream_t)stream),
+                    "gs_l1_dssim_loss_grad");
+}
+
+gs_adam_config gs_default_adam_config(void) {
+  gs_adam_config c;
+  c.lr_means = 1.6e-4f;
+  c.lr_scales = 5e-3f;
+  c.lr_quats = 1e-3f;
+  c.lr_opacities = 5e-2f;
+  c.lr_sh = 2.5e-3f;
+  c.beta1 = 0.9f;
+  c.beta2 = 0.99f;
+  c.eps = 1e-15f;
+  return c;
+}
+
+namespace {
+
+gs_status check_adam(int64_t step, const gs_adam_config* cfg, int32_t sh_degree) {
+  GS_REQUIRE(cfg != nullptr, "cfg is NULL");
+  GS_REQUIRE(step >= 1, "step must be >= 1");
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  const float lr[5] = {cfg->lr_means, cfg->lr_scales, cfg->lr_quats, cfg->lr_opacities,
+                       cfg->lr_sh};
+  for (float x : lr) GS_REQUIRE(std::isfinite(x) && x >= 0.0f, "learning rates must be >= 0");
+  GS_REQUIRE(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f, "beta1 must be in [0, 1)");
+  GS_REQUIRE(cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f, "beta2 must be in [0, 1)");
+  GS_REQUIRE(std::isfinite(cfg->eps) && cfg->eps >= 0.0f, "eps must be >= 0");
+  return GS_OK;
+}
+
+}  // namespace
+
+gs_status gs_adam_step(int64_t N, int64_t ld, int32_t sh_degree, int64_t step,
+                       const gs_adam_config* cfg, float* means, float* log_scales, float* quats,
+                       float* logit_opacities, float* sh, float* scales, float* opacities,
+                       const float* dL_dmeans, const float* dL_dscales, const float* dL_dquats,
+                       const float* dL_dopacities, const float* dL_dsh, float* exp_avg,
+                       float* exp_avg_sq, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_adam(step, cfg, sh_degree));
+  if (N == 0) return GS_OK;
+  GS_REQUIRE(means && log_scales && quats && logit_opacities && sh && scales && opacities,
+             "NULL parameter pointer");
+  GS_REQUIRE(dL_dmeans && dL_dscales && dL_dquats && dL_dopacities && dL_dsh,
+             "NULL gradient pointer");
+  GS_REQUIRE(exp_avg && exp_avg_sq, "NULL moment pointer");
+  float* raw[5] = {means, log_scales, quats, logit_opacities, sh};
+  const float* grad[5] = {dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh};
+  return hip_status(gs_launch_adam(N, ld, ld, nullptr, sh_degree, step, *cfg, raw, grad, scales,
+                                   opacities, exp_avg, exp_avg_sq, (hipStream_t)stream),
+                    "gs_adam_step");
+}
+
+gs_status gs_adam_step_packed(int64_t num_visible, const uint32_t* vis_ids, int64_t ldv,
+                              int64_t N, int64_t ld, int32_t sh_degree, int64_t step,
+                              const gs_adam_config* cfg, float* means, float* log_scales,
+                              float* quats, float* logit_opacities, float* sh, float* scales,
+                              float* opacities, const float* dL_dmeans, const float* dL_dscales,
+                              const float* dL_dquats, const float* dL_dopacities,
+                              const float* dL_dsh, float* exp_avg, float* exp_avg_sq,
+                              void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_adam(step, cfg, sh_degree));
+  GS_REQUIRE(num_visible >= 0 && num_visible <= N, "num_visible must be in [0, N]");
+  GS_REQUIRE(ldv >= num_visible && ldv <= ((int64_t)1 << 40), "ldv must be >= num_visible");
+  if (num_visible == 0) return GS_OK;
+  GS_REQUIRE(vis_ids != nullptr, "vis_ids is NULL");
+  GS_REQUIRE(means && log_scales && quats && logit_opacities && sh && scales && opacities,
+             "NULL parameter pointer");
+  GS_REQUIRE(dL_dmeans && dL_dscales && dL_dquats && dL_dopacities && dL_dsh,
+             "NULL gradient pointer");
+  GS_REQUIRE(exp_avg && exp_avg_sq, "NULL moment pointer");
+  float* raw[5] = {means, log_scales, quats, logit_opacities, sh};
+  const float* grad[5] = {dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh};
+  return hip_status(gs_launch_adam(num_visible, ld, ldv, vis_ids, sh_degree, step, *cfg, raw,
+                                   grad, scales, opacities, exp_avg, exp_avg_sq,
+                                   (hipStream_t)stream),
+                    "gs_adam_step_packed");
 }
 
 gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* image,

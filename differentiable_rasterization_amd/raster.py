@@ -27,7 +27,9 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_project_fwd", "gs_bin_and_sort_workspace_size", "gs_bin_and_sort",
             "gs_rasterize_fwd", "gs_rasterize_bwd", "gs_project_bwd", "gs_image_loss_grad",
             "gs_densify_prune_workspace_size", "gs_densify_prune", "gs_bin_and_sort_packed",
-            "gs_rasterize_bwd_packed", "gs_project_bwd_packed")
+            "gs_rasterize_bwd_packed", "gs_project_bwd_packed", "gs_l1_dssim_workspace_size",
+            "gs_l1_dssim_loss_grad", "gs_default_adam_config", "gs_adam_step",
+            "gs_adam_step_packed")
 
 
 class GsError(RuntimeError):
@@ -49,6 +51,11 @@ class gs_settings(C.Structure):
 
 
 _lib = None
+
+
+class gs_adam_config(C.Structure):
+    _fields_ = [(n, C.c_float) for n in ("lr_means", "lr_scales", "lr_quats", "lr_opacities",
+                                         "lr_sh", "beta1", "beta2", "eps")]
 
 
 def load():
@@ -92,6 +99,17 @@ def load():
     lib.gs_project_bwd_packed.restype = C.c_int
     lib.gs_project_bwd_packed.argtypes = [i64, P, i64, i64, i64, i32] + [P] * 4 + [P, P] + \
         [P] * 2 + [P] * 5 + [i32, P]
+    lib.gs_l1_dssim_workspace_size.restype = C.c_size_t
+    lib.gs_l1_dssim_workspace_size.argtypes = [i32, i32]
+    lib.gs_l1_dssim_loss_grad.restype = C.c_int
+    lib.gs_l1_dssim_loss_grad.argtypes = [i32, i32, P, P, C.c_float, P, P, P, C.c_size_t, P]
+    lib.gs_default_adam_config.restype = gs_adam_config
+    lib.gs_default_adam_config.argtypes = []
+    lib.gs_adam_step.restype = C.c_int
+    lib.gs_adam_step.argtypes = [i64, i64, i32, i64, P] + [P] * 7 + [P] * 5 + [P, P, P]
+    lib.gs_adam_step_packed.restype = C.c_int
+    lib.gs_adam_step_packed.argtypes = [i64, P, i64, i64, i64, i32, i64, P] + [P] * 7 + \
+        [P] * 5 + [P, P, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -263,6 +281,47 @@ def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=
     lib = load()
     _check(lib.gs_image_loss_grad(int(kind), int(count), _p(image), _p(target), _p(dL_dimage),
                                   _p(loss), _stream(stream)))
+
+
+def gs_l1_dssim_workspace_size(width, height) -> int:
+    return int(load().gs_l1_dssim_workspace_size(int(width), int(height)))
+
+
+def gs_l1_dssim_loss_grad(width, height, image, target, lam, dL_dimage, loss, workspace,
+                          workspace_bytes, stream=None):
+    lib = load()
+    _check(lib.gs_l1_dssim_loss_grad(int(width), int(height), _p(image), _p(target),
+                                     float(lam), _p(dL_dimage), _p(loss), _p(workspace),
+                                     int(workspace_bytes), _stream(stream)))
+
+
+def default_adam_config(**overrides) -> gs_adam_config:
+    c = load().gs_default_adam_config()
+    for k, v in overrides.items():
+        setattr(c, k, float(v))
+    return c
+
+
+def gs_adam_step(N, ld, sh_degree, step, cfg, means, log_scales, quats, logits, sh, scales,
+                 opacities, g_means, g_scales, g_quats, g_opacities, g_sh, exp_avg, exp_avg_sq,
+                 stream=None):
+    lib = load()
+    _check(lib.gs_adam_step(N, ld, sh_degree, int(step), C.byref(cfg), _p(means),
+                            _p(log_scales), _p(quats), _p(logits), _p(sh), _p(scales),
+                            _p(opacities), _p(g_means), _p(g_scales), _p(g_quats),
+                            _p(g_opacities), _p(g_sh), _p(exp_avg), _p(exp_avg_sq),
+                            _stream(stream)))
+
+
+def gs_adam_step_packed(num_visible, vis_ids, ldv, N, ld, sh_degree, step, cfg, means,
+                        log_scales, quats, logits, sh, scales, opacities, g_means, g_scales,
+                        g_quats, g_opacities, g_sh, exp_avg, exp_avg_sq, stream=None):
+    lib = load()
+    _check(lib.gs_adam_step_packed(int(num_visible), _p(vis_ids), int(ldv), N, ld, sh_degree,
+                                   int(step), C.byref(cfg), _p(means), _p(log_scales),
+                                   _p(quats), _p(logits), _p(sh), _p(scales), _p(opacities),
+                                   _p(g_means), _p(g_scales), _p(g_quats), _p(g_opacities),
+                                   _p(g_sh), _p(exp_avg), _p(exp_avg_sq), _stream(stream)))
 
 
 def gs_densify_prune_workspace_size(N, clone_fraction) -> int:

@@ -298,6 +298,70 @@ GS_API gs_status gs_image_loss_grad(int32_t kind, int64_t count, const float* im
                              const float* target, float* dL_dimage, float* loss,
                              void* stream);
 
+/* Image loss of a training step (the gsplat guide §4.1 trains on the mean
+ * absolute error plus 0.2 times (1 - SSIM)).  For [H][W][3] images x =
+ * image and y = target with n = 3 H W elements:
+ *   loss = sum|x - y| / n + lambda (1 - sum ssim / n),
+ * where ssim is the structural similarity index per pixel and channel:
+ * windowed means and second moments under an 11 x 11 Gaussian window
+ * (standard deviation 1.5, normalised to sum 1; zero outside the image),
+ * s = (2 mx my + C1)(2 sxy + C2) / ((mx^2 + my^2 + C1)(sx^2 + sy^2 + C2)),
+ * C1 = 0.01^2, C2 = 0.03^2.  Writes dL_dimage [H][W][3] (sign(0) = 0 in the
+ * L1 term) and, if loss (a device float) is non-NULL, the loss value; the
+ * value and the gradient are reproducible bit for bit.  workspace: device
+ * memory of gs_l1_dssim_workspace_size() bytes, 256-byte aligned.
+ * dL_dimage must not alias image or target. */
+GS_API size_t gs_l1_dssim_workspace_size(int32_t width, int32_t height);
+GS_API gs_status gs_l1_dssim_loss_grad(int32_t width, int32_t height, const float* image,
+                                       const float* target, float lambda, float* dL_dimage,
+                                       float* loss, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* One Adam step per parameter group (the gsplat guide §4.2: a learning rate
+ * per group, betas (0.9, 0.99), eps 1e-15; gs_default_adam_config() returns
+ * those, with the page's rates means 1.6e-4, scales 5e-3, quats 1e-3,
+ * opacities 5e-2, SH 2.5e-3). */
+typedef struct {
+  float lr_means, lr_scales, lr_quats, lr_opacities, lr_sh;
+  float beta1, beta2, eps;
+} gs_adam_config;
+
+GS_API gs_adam_config gs_default_adam_config(void);
+
+/* The step updates the stored parameters in place: means [3][ld],
+ * log_scales [3][ld], quats [4][ld], logit_opacities [ld], sh [K*3][ld].
+ * The gradients are those the backward returns, with respect to means,
+ * activated scales, quats, activated opacities and SH; they are first
+ * carried to the stored values through the activated ones the forward used
+ * (scales [3][ld] = exp(log_scales), opacities [ld] = sigmoid(logits)):
+ * d/dlog_s = d/ds * s, d/dlogit = d/do * o (1 - o).  Then, per element,
+ * m = beta1 m + (1 - beta1) g, v = beta2 v + (1 - beta2) g^2,
+ * p -= lr / (1 - beta1^step) * m / (sqrt(v) / sqrt(1 - beta2^step) + eps),
+ * and scales / opacities are rewritten from the new stored values.
+ * exp_avg and exp_avg_sq are the moments, [P][ld] each with P = 11 + 3K
+ * planes in the order means, scales, quats, opacity, SH (zero before the
+ * first step).  step counts from 1. */
+GS_API gs_status gs_adam_step(int64_t N, int64_t ld, int32_t sh_degree, int64_t step,
+                              const gs_adam_config* cfg, float* means, float* log_scales,
+                              float* quats, float* logit_opacities, float* sh, float* scales,
+                              float* opacities, const float* dL_dmeans, const float* dL_dscales,
+                              const float* dL_dquats, const float* dL_dopacities,
+                              const float* dL_dsh, float* exp_avg, float* exp_avg_sq,
+                              void* stream);
+
+/* The packed form: the gradients are the packed rows of
+ * gs_project_bwd_packed ([p][ldv], row r for Gaussian vis_ids[r]); only the
+ * listed Gaussians are updated, the others keep parameters and moments
+ * (sparse Adam). */
+GS_API gs_status gs_adam_step_packed(int64_t num_visible, const uint32_t* vis_ids, int64_t ldv,
+                                     int64_t N, int64_t ld, int32_t sh_degree, int64_t step,
+                                     const gs_adam_config* cfg, float* means, float* log_scales,
+                                     float* quats, float* logit_opacities, float* sh,
+                                     float* scales, float* opacities, const float* dL_dmeans,
+                                     const float* dL_dscales, const float* dL_dquats,
+                                     const float* dL_dopacities, const float* dL_dsh,
+                                     float* exp_avg, float* exp_avg_sq, void* stream);
+
 /* Densify and prune between training steps (the count-changing step of the
  * gsplat guide §4.1, which clones by the mean-gradient magnitude and prunes
  * Gaussians of opacity below 0.005).  Out of place: the N Gaussians in

@@ -188,6 +188,50 @@ def test_packed_calls_reject_bad_arguments(lib):
     assert pbwd(V=0, ldv=0, vis=None) == raster.GS_OK         # empty list: nothing to launch
 
 
+def test_training_step_calls_reject_bad_arguments(lib):
+    dummy = C.c_void_p(256)
+    ws = lib.gs_l1_dssim_workspace_size(64, 48)
+    assert ws >= 9 * 64 * 48 * 4
+    assert lib.gs_l1_dssim_workspace_size(0, 48) == 0
+
+    def loss(W=64, H=48, lam=0.2, img=dummy, g=C.c_void_p(512), wsp=dummy, wsb=ws):
+        return lib.gs_l1_dssim_loss_grad(W, H, img, dummy, C.c_float(lam), g, None, wsp, wsb,
+                                         None)
+    assert loss(W=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert loss(lam=-0.1) == raster.GS_ERR_INVALID_ARGUMENT
+    assert loss(lam=float("nan")) == raster.GS_ERR_INVALID_ARGUMENT
+    assert loss(img=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert loss(g=dummy) == raster.GS_ERR_INVALID_ARGUMENT        # aliases the image
+    assert loss(wsp=C.c_void_p(260)) == raster.GS_ERR_INVALID_ARGUMENT
+    assert loss(wsb=ws - 1) == raster.GS_ERR_INVALID_ARGUMENT
+
+    cfg = lib.gs_default_adam_config()
+    assert abs(cfg.lr_means - 1.6e-4) < 1e-10 and abs(cfg.lr_opacities - 5e-2) < 1e-9
+    assert abs(cfg.beta2 - 0.99) < 1e-7 and abs(cfg.eps - 1e-15) < 1e-22
+
+    def adam(N=10, step=1, deg=3, c=cfg, moment=dummy):
+        return lib.gs_adam_step(N, N, deg, step, C.byref(c), *([dummy] * 12), moment, dummy,
+                                None)
+    assert adam(step=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam(deg=4) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam(moment=None) == raster.GS_ERR_INVALID_ARGUMENT
+    bad = raster.gs_adam_config.from_buffer_copy(cfg)
+    bad.beta1 = 1.0
+    assert adam(c=bad) == raster.GS_ERR_INVALID_ARGUMENT
+    bad = raster.gs_adam_config.from_buffer_copy(cfg)
+    bad.lr_sh = -1.0
+    assert adam(c=bad) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam(N=0) == raster.GS_OK                               # nothing to launch
+
+    def adam_p(V=3, ldv=3, vis=dummy):
+        return lib.gs_adam_step_packed(V, vis, ldv, 10, 10, 3, 1, C.byref(cfg),
+                                       *([dummy] * 14), None)
+    assert adam_p(V=11, ldv=11) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam_p(ldv=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam_p(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert adam_p(V=0, ldv=0, vis=None) == raster.GS_OK
+
+
 def test_densify_rejects_bad_arguments(lib):
     dummy = C.c_void_p(256)
     n_out = C.c_int64(0)
