@@ -166,6 +166,87 @@ def densify_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def train_step_bench(args, scene, gcams, targets, capacity):
+    """A whole training step as the gsplat guide 4.1 loop runs it: packed
+    forward and backward, the mean-L1 + 0.2 D-SSIM loss gradient and the
+    per-group Adam step on the visible rows, on a copy of the Gaussians
+    (the parameters move every step)."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    g = raster.Gaussians.from_scene(scene)
+    N, K, deg = scene.n, (scene.sh_degree + 1) ** 2, scene.sh_degree
+    W, H = gcams[0].width, gcams[0].height
+    log_s = torch.log(g.scales)
+    logit = torch.log(g.opacities) - torch.log1p(-g.opacities)
+    P = 11 + 3 * K
+    m = torch.zeros((P, g.ld), device="cuda")
+    v = torch.zeros((P, g.ld), device="cuda")
+    fr = raster.Frame(g.ld, deg, W, H, capacity=capacity, packed=True)
+    wsb = raster.gs_l1_dssim_workspace_size(W, H)
+    buf = torch.empty(wsb + 256, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 256
+    ws = buf[off:off + wsb]
+    cfg = raster.default_adam_config()
+    names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "l1_dssim", "rasterize_bwd",
+             "project_bwd", "adam"]
+    n_cam = len(gcams)
+
+    def tstep(i, ev=None):
+        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        rec(0)
+        fr.project(g, gcams[i % n_cam])
+        rec(1)
+        fr.bin_and_sort(g)
+        rec(2)
+        fr.rasterize(g)
+        rec(3)
+        raster.gs_l1_dssim_loss_grad(W, H, fr.image, targets[i % n_cam], 0.2, fr.dL_dimage,
+                                     None, ws, wsb)
+        rec(4)
+        fr.rasterize_backward(g)
+        rec(5)
+        fr.project_backward(g)
+        rec(6)
+        raster.gs_adam_step_packed(fr.V, fr.vis_ids, fr.ld, N, g.ld, deg, i + 1, cfg, g.means,
+                                   log_s, g.quats, logit, g.sh, g.scales, g.opacities,
+                                   fr.g_means, fr.g_scales, fr.g_quats, fr.g_opacities, fr.g_sh,
+                                   m, v)
+        rec(7)
+
+    for i in range(args.warmup):
+        tstep(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        tstep(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = {n: sum(ev[k].elapsed_time(ev[k + 1]) for ev in evs) / args.steps
+          for k, n in enumerate(names)}
+    Px = W * H
+    # algorithmic bytes: the loss reads both images and writes the gradient
+    # (36 B/px); the two-pass kernels also write and read nine derivative
+    # planes (132 B/px moved).  Adam, per visible Gaussian: parameter,
+    # gradient, two moments in and three out per plane (28 B x P), the four
+    # activated planes in and out, the list entry.
+    V = fr.V
+    loss_b, loss_moved = 36 * Px, 132 * Px
+    adam_b = V * (28 * P + 8 * 4 + 4)
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9
+    return {"value": round(args.steps / dt, 2), "unit": "steps/s",
+            "ms_per_step": round(1e3 * dt / args.steps, 4),
+            "form": "packed forward/backward, mean L1 + 0.2 D-SSIM, per-group Adam on the "
+                    "visible rows",
+            "stages_ms": {n: round(t, 4) for n, t in ms.items()},
+            "l1_dssim": {"GB/s": round(gbs(loss_b, ms["l1_dssim"]), 1),
+                         "hbm_frac": round(gbs(loss_b, ms["l1_dssim"]) / HBM_PEAK_GBS, 4),
+                         "moved_GB/s": round(gbs(loss_moved, ms["l1_dssim"]), 1)},
+            "adam": {"GB/s": round(gbs(adam_b, ms["adam"]), 1),
+                     "hbm_frac": round(gbs(adam_b, ms["adam"]) / HBM_PEAK_GBS, 4),
+                     "visible": V}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +261,9 @@ def main():
                     help="run the compositing backward with the absolute-gradient sums")
     ap.add_argument("--packed", action="store_true",
                     help="run the packed calls (visible list, sparse gradient rows)")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="skip the training-step measurement (packed calls, L1 + 0.2 D-SSIM, "
+                         "per-group Adam)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -290,6 +374,8 @@ def main():
 
     dt, stage_ms = timed(fr)
     packed_line = None
+    train_line = None if args.no_train_step else train_step_bench(args, scene, gcams, targets,
+                                                                   fr.capacity)
     if not args.packed:
         # the same steps through the packed calls (visible list, sparse
         # gradient rows), reported beside the dense headline
@@ -371,6 +457,8 @@ def main():
     }
     if packed_line is not None:
         out["packed"] = packed_line
+    if train_line is not None:
+        out["train_step"] = train_line
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
     print(json.dumps(out), flush=True)

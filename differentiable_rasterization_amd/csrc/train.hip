@@ -8,7 +8,10 @@
 //     the exp / sigmoid activations of scales and opacities.
 //
 // SSIM is a stencil: each 32 x 16 output tile stages its 42 x 26 halo in
-// LDS and applies the separable window as a row pass then a column pass.
+// LDS, one channel at a time, and applies the separable window as a row
+// pass (four outputs per lane from a 14-value register window) then a
+// column pass (two outputs per lane).  Each XCD takes a contiguous band of
+// tiles so that halos are shared through its L2.
 // The gradient needs the window twice (statistics, then the adjoint on the
 // derivative maps), hence two kernels with the derivative maps in between.
 // Adam is one pass over the parameter planes, bound by HBM.
@@ -48,81 +51,121 @@ __device__ inline double block_sum_f64(double v, double* s_w) {
   return r;
 }
 
+constexpr int kSsimLd = 44;  // LDS row stride of a halo row (16-byte aligned rows)
+constexpr int kSsimXcds = 8;
+
+// Tile of a workgroup: each XCD (workgroups are dealt to the eight XCDs in
+// turn) takes a contiguous run of tiles in row-major order, so neighbouring
+// tiles share their halo rows through that XCD's L2.  -1 past the last tile.
+__device__ inline int ssim_tile(int nb) {
+  const int per = (nb + kSsimXcds - 1) / kSsimXcds;
+  const int tile = (int)(blockIdx.x % kSsimXcds) * per + (int)(blockIdx.x / kSsimXcds);
+  return tile < nb ? tile : -1;
+}
+
+// Row pass item: four adjacent outputs of one halo row from the 14 inputs
+// they span (a sliding window in registers).
+__device__ inline void load14(const float* row, float v[14]) {
+  const float4 a = *(const float4*)(row);
+  const float4 b = *(const float4*)(row + 4);
+  const float4 c = *(const float4*)(row + 8);
+  const float2 e = *(const float2*)(row + 12);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  v[8] = c.x; v[9] = c.y; v[10] = c.z; v[11] = c.w;
+  v[12] = e.x; v[13] = e.y;
+}
+
 // Pass 1.  For every pixel and channel: the windowed means and second
 // moments of x and y, the index s, and its partial derivatives with respect
 // to mu_x, E[x^2] and E[xy], written to d as nine planes [map][channel][H][W].
-// Per workgroup, the sums of s and |x - y| (fp64) go to partials[block][2].
-__global__ __launch_bounds__(256) void ssim_stats_kernel(int W, int H,
+// Per tile, the sums of s and |x - y| (fp64) go to partials[tile][2].  One
+// channel is staged at a time, which keeps LDS near 26 KB per workgroup.
+__global__ __launch_bounds__(256) void ssim_stats_kernel(int W, int H, int tiles_x, int nb,
                                                          const float* __restrict__ x,
                                                          const float* __restrict__ y,
                                                          SsimWindow win, float* __restrict__ d,
                                                          double* __restrict__ partials) {
-  __shared__ float sx[3][kSsimHy][kSsimHx];
-  __shared__ float sy[3][kSsimHy][kSsimHx];
+  __shared__ __align__(16) float sx[kSsimHy][kSsimLd];
+  __shared__ __align__(16) float sy[kSsimHy][kSsimLd];
   __shared__ float hb[5][kSsimHy][kSsimTx];
   __shared__ double s_w[4];
+  const int tile = ssim_tile(nb);
+  if (tile < 0) return;
   const int t = threadIdx.x;
-  const int x0 = blockIdx.x * kSsimTx, y0 = blockIdx.y * kSsimTy;
-  // the halo, zero outside the image; a halo row is 42 pixels x 3 channels
-  // contiguous in memory
-  constexpr int kRow = kSsimHx * 3;
-  for (int idx = t; idx < kSsimHy * kRow; idx += 256) {
-    const int r = idx / kRow, col = idx - r * kRow;
-    const int px = col / 3, c = col - px * 3;
-    const int gx = x0 - kSsimR + px, gy = y0 - kSsimR + r;
-    float vx = 0.0f, vy = 0.0f;
-    if (gx >= 0 && gx < W && gy >= 0 && gy < H) {
-      const int64_t o = ((int64_t)gy * W + gx) * 3 + c;
-      vx = x[o];
-      vy = y[o];
-    }
-    sx[c][r][px] = vx;
-    sy[c][r][px] = vy;
-  }
-  __syncthreads();
+  const int x0 = (tile % tiles_x) * kSsimTx, y0 = (tile / tiles_x) * kSsimTy;
   const int64_t plane = (int64_t)W * H;
   double acc_s = 0.0, acc_l1 = 0.0;
+  const int ox = t & 31, oy0 = (t >> 5) * 2;  // column pass: two rows per thread
   for (int c = 0; c < 3; ++c) {
-    // row pass: the five sums along x for every halo row
-    for (int idx = t; idx < kSsimHy * kSsimTx; idx += 256) {
-      const int r = idx >> 5, j = idx & 31;
-      float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kSsimTaps; ++k) {
-        const float xv = sx[c][r][j + k], yv = sy[c][r][j + k];
-        const float wx = win.w[k] * xv, wy = win.w[k] * yv;
-        a0 += wx;
-        a1 += wy;
-        a2 = fmaf(wx, xv, a2);
-        a3 = fmaf(wy, yv, a3);
-        a4 = fmaf(wx, yv, a4);
+    // channel c of the halo, zero outside the image (rows of 42 as 64 lanes)
+    for (int idx = t; idx < kSsimHy * 64; idx += 256) {
+      const int r = idx >> 6, px = idx & 63;
+      if (px >= kSsimHx) continue;
+      const int gx = x0 - kSsimR + px, gy = y0 - kSsimR + r;
+      float vx = 0.0f, vy = 0.0f;
+      if (gx >= 0 && gx < W && gy >= 0 && gy < H) {
+        const int64_t o = ((int64_t)gy * W + gx) * 3 + c;
+        vx = x[o];
+        vy = y[o];
       }
-      hb[0][r][j] = a0;
-      hb[1][r][j] = a1;
-      hb[2][r][j] = a2;
-      hb[3][r][j] = a3;
-      hb[4][r][j] = a4;
+      sx[r][px] = vx;
+      sy[r][px] = vy;
     }
     __syncthreads();
-    // column pass and the pointwise index
-    for (int idx = t; idx < kSsimTy * kSsimTx; idx += 256) {
-      const int oy = idx >> 5, ox = idx & 31;
-      float mx = 0.0f, my = 0.0f, exx = 0.0f, eyy = 0.0f, exy = 0.0f;
+    // row pass: 26 rows x 8 groups of four outputs
+    if (t < kSsimHy * 8) {
+      const int r = t >> 3, j0 = (t & 7) * 4;
+      float xv[14], yv[14];
+      load14(&sx[r][j0], xv);
+      load14(&sy[r][j0], yv);
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kSsimTaps; ++k) {
+          const float xk = xv[o + k], yk = yv[o + k];
+          const float wx = win.w[k] * xk, wy = win.w[k] * yk;
+          a0 += wx;
+          a1 += wy;
+          a2 = fmaf(wx, xk, a2);
+          a3 = fmaf(wy, yk, a3);
+          a4 = fmaf(wx, yk, a4);
+        }
+        hb[0][r][j0 + o] = a0;
+        hb[1][r][j0 + o] = a1;
+        hb[2][r][j0 + o] = a2;
+        hb[3][r][j0 + o] = a3;
+        hb[4][r][j0 + o] = a4;
+      }
+    }
+    __syncthreads();
+    // column pass: outputs (oy0, ox) and (oy0 + 1, ox) from 12 rows
+    float st[5][2];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      float col[12];
+#pragma unroll
+      for (int k = 0; k < 12; ++k) col[k] = hb[q][oy0 + k][ox];
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
       for (int k = 0; k < kSsimTaps; ++k) {
-        const float wk = win.w[k];
-        mx = fmaf(wk, hb[0][oy + k][ox], mx);
-        my = fmaf(wk, hb[1][oy + k][ox], my);
-        exx = fmaf(wk, hb[2][oy + k][ox], exx);
-        eyy = fmaf(wk, hb[3][oy + k][ox], eyy);
-        exy = fmaf(wk, hb[4][oy + k][ox], exy);
+        s0 = fmaf(win.w[k], col[k], s0);
+        s1 = fmaf(win.w[k], col[k + 1], s1);
       }
-      const int gx = x0 + ox, gy = y0 + oy;
+      st[q][0] = s0;
+      st[q][1] = s1;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int gx = x0 + ox, gy = y0 + oy0 + p;
       if (gx < W && gy < H) {
-        const float vx = exx - mx * mx, vy = eyy - my * my, cxy = exy - mx * my;
+        const float mx = st[0][p], my = st[1][p];
+        const float vx = st[2][p] - mx * mx, vy = st[3][p] - my * my;
+        const float cxy = st[4][p] - mx * my;
         const float A1 = 2.0f * mx * my + kSsimC1, A2 = 2.0f * cxy + kSsimC2;
         const float B1 = mx * mx + my * my + kSsimC1, B2 = vx + vy + kSsimC2;
-        const float iB1 = 1.0f / B1, iB2 = 1.0f / B2;
+        const float iB1 = __builtin_amdgcn_rcpf(B1), iB2 = __builtin_amdgcn_rcpf(B2);
         const float iB = iB1 * iB2;
         const float s = A1 * A2 * iB;
         const float dmu = 2.0f * my * (A2 - A1) * iB + 2.0f * mx * s * (iB2 - iB1);
@@ -133,92 +176,125 @@ __global__ __launch_bounds__(256) void ssim_stats_kernel(int W, int H,
         d[(int64_t)(3 + c) * plane + o] = dxx;
         d[(int64_t)(6 + c) * plane + o] = dxy;
         acc_s += (double)s;
-        acc_l1 += (double)fabsf(sx[c][oy + kSsimR][ox + kSsimR] - sy[c][oy + kSsimR][ox + kSsimR]);
+        acc_l1 += (double)fabsf(sx[oy0 + p + kSsimR][ox + kSsimR] -
+                                sy[oy0 + p + kSsimR][ox + kSsimR]);
       }
     }
-    __syncthreads();  // hb is rewritten for the next channel
+    __syncthreads();  // sx, sy and hb are rewritten for the next channel
   }
   const double ts = block_sum_f64(acc_s, s_w);
   const double tl = block_sum_f64(acc_l1, s_w);
   if (t == 0) {
-    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    partials[2 * b] = ts;
-    partials[2 * b + 1] = tl;
+    partials[2 * tile] = ts;
+    partials[2 * tile + 1] = tl;
   }
 }
 
 // Pass 2.  The adjoint of the windowed sums: the same window over the three
 // derivative maps (zero outside the image), combined per pixel and channel
 // into dL/dx = sign(x - y) / n - (lambda / n) (w*d_mu + 2 x w*d_xx + y w*d_xy).
-__global__ __launch_bounds__(256) void ssim_grad_kernel(int W, int H,
+// One channel's three maps are staged at a time; the next channel's are
+// loaded into registers while the current one is computed.
+__global__ __launch_bounds__(256) void ssim_grad_kernel(int W, int H, int tiles_x, int nb,
                                                         const float* __restrict__ x,
                                                         const float* __restrict__ y,
                                                         SsimWindow win,
                                                         const float* __restrict__ d,
                                                         float inv_n, float lam_n,
                                                         float* __restrict__ g) {
-  __shared__ float sd[9][kSsimHy][kSsimHx];
+  __shared__ __align__(16) float sd[3][kSsimHy][kSsimLd];
   __shared__ float hb[3][kSsimHy][kSsimTx];
+  const int tile = ssim_tile(nb);
+  if (tile < 0) return;
   const int t = threadIdx.x;
-  const int x0 = blockIdx.x * kSsimTx, y0 = blockIdx.y * kSsimTy;
+  const int x0 = (tile % tiles_x) * kSsimTx, y0 = (tile / tiles_x) * kSsimTy;
   const int64_t plane = (int64_t)W * H;
-  constexpr int kHalo = kSsimHy * kSsimHx;
-  for (int idx = t; idx < 9 * kHalo; idx += 256) {
-    const int q = idx / kHalo, rem = idx - q * kHalo;
-    const int r = rem / kSsimHx, px = rem - r * kSsimHx;
+  const int ox = t & 31, oy0 = (t >> 5) * 2;
+  // halo element k of this thread as in pass 1 (offset into a plane, -1
+  // outside); the next channel's three maps are loaded while one is computed
+  constexpr int kLd = (kSsimHy * 64 + 255) / 256;
+  int hpix[kLd];
+#pragma unroll
+  for (int k = 0; k < kLd; ++k) {
+    const int idx = t + 256 * k, r = idx >> 6, px = idx & 63;
     const int gx = x0 - kSsimR + px, gy = y0 - kSsimR + r;
-    float v = 0.0f;
-    if (gx >= 0 && gx < W && gy >= 0 && gy < H) v = d[(int64_t)q * plane + (int64_t)gy * W + gx];
-    sd[q][r][px] = v;
+    hpix[k] = (idx < kSsimHy * 64 && px < kSsimHx && gx >= 0 && gx < W && gy >= 0 && gy < H)
+                  ? gy * W + gx : -1;
   }
-  __syncthreads();
+  float pf[3][kLd];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int k = 0; k < kLd; ++k)
+      pf[m][k] = hpix[k] >= 0 ? d[(int64_t)(3 * m) * plane + hpix[k]] : 0.0f;
   float gv[2][3];
   for (int c = 0; c < 3; ++c) {
-    for (int idx = t; idx < kSsimHy * kSsimTx; idx += 256) {
-      const int r = idx >> 5, j = idx & 31;
-      float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kSsimTaps; ++k) {
-        const float wk = win.w[k];
-        b0 = fmaf(wk, sd[c][r][j + k], b0);
-        b1 = fmaf(wk, sd[3 + c][r][j + k], b1);
-        b2 = fmaf(wk, sd[6 + c][r][j + k], b2);
+    for (int k = 0; k < kLd; ++k) {
+      const int idx = t + 256 * k, px = idx & 63;
+      if (idx < kSsimHy * 64 && px < kSsimHx) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m) sd[m][idx >> 6][px] = pf[m][k];
       }
-      hb[0][r][j] = b0;
-      hb[1][r][j] = b1;
-      hb[2][r][j] = b2;
     }
     __syncthreads();
+    if (c < 2) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int idx = t + 256 * p;
-      const int oy = idx >> 5, ox = idx & 31;
-      float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f;
+      for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int k = 0; k < kLd; ++k)
+          pf[m][k] = hpix[k] >= 0 ? d[(int64_t)(3 * m + c + 1) * plane + hpix[k]] : 0.0f;
+    }
+    if (t < kSsimHy * 8) {
+      const int r = t >> 3, j0 = (t & 7) * 4;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        float v[14];
+        load14(&sd[m][r][j0], v);
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          float b = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kSsimTaps; ++k) b = fmaf(win.w[k], v[o + k], b);
+          hb[m][r][j0 + o] = b;
+        }
+      }
+    }
+    __syncthreads();
+    float bs[3][2];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      float col[12];
+#pragma unroll
+      for (int k = 0; k < 12; ++k) col[k] = hb[m][oy0 + k][ox];
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
       for (int k = 0; k < kSsimTaps; ++k) {
-        const float wk = win.w[k];
-        c0 = fmaf(wk, hb[0][oy + k][ox], c0);
-        c1 = fmaf(wk, hb[1][oy + k][ox], c1);
-        c2 = fmaf(wk, hb[2][oy + k][ox], c2);
+        s0 = fmaf(win.w[k], col[k], s0);
+        s1 = fmaf(win.w[k], col[k + 1], s1);
       }
-      const int gx = x0 + ox, gy = y0 + oy;
+      bs[m][0] = s0;
+      bs[m][1] = s1;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int gx = x0 + ox, gy = y0 + oy0 + p;
       float r = 0.0f;
       if (gx < W && gy < H) {
         const int64_t o = ((int64_t)gy * W + gx) * 3 + c;
         const float xv = x[o], yv = y[o];
         const float diff = xv - yv;
         const float sg = diff > 0.0f ? 1.0f : (diff < 0.0f ? -1.0f : 0.0f);
-        const float gs = c0 + 2.0f * xv * c1 + yv * c2;
+        const float gs = bs[0][p] + 2.0f * xv * bs[1][p] + yv * bs[2][p];
         r = sg * inv_n - lam_n * gs;
       }
       gv[p][c] = r;
     }
-    __syncthreads();
+    __syncthreads();  // sd and hb are rewritten for the next channel
   }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int idx = t + 256 * p;
-    const int gx = x0 + (idx & 31), gy = y0 + (idx >> 5);
+    const int gx = x0 + ox, gy = y0 + oy0 + p;
     if (gx < W && gy < H) {
       const int64_t o = ((int64_t)gy * W + gx) * 3;
       g[o] = gv[p][0];
@@ -327,16 +403,19 @@ extern "C" hipError_t gs_launch_l1_dssim(int32_t W, int32_t H, const float* img,
     }
     for (int k = 0; k < kSsimTaps; ++k) win.w[k] = (float)(wd[k] / sum);
   }
-  const dim3 grid((unsigned)((W + kSsimTx - 1) / kSsimTx), (unsigned)((H + kSsimTy - 1) / kSsimTy));
-  const int64_t nb = (int64_t)grid.x * grid.y;
+  const int tiles_x = (W + kSsimTx - 1) / kSsimTx;
+  const int nb = tiles_x * ((H + kSsimTy - 1) / kSsimTy);
+  const int per = (nb + kSsimXcds - 1) / kSsimXcds;
+  const dim3 grid((unsigned)(per * kSsimXcds));
   float* d = (float*)workspace;
   double* partials =
       (double*)((char*)workspace + talign(sizeof(float) * 9 * (size_t)W * (size_t)H));
   const double n = 3.0 * (double)W * (double)H;
-  hipLaunchKernelGGL(ssim_stats_kernel, grid, dim3(256), 0, s, W, H, img, tgt, win, d, partials);
+  hipLaunchKernelGGL(ssim_stats_kernel, grid, dim3(256), 0, s, W, H, tiles_x, nb, img, tgt, win,
+                     d, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ssim_grad_kernel, grid, dim3(256), 0, s, W, H, img, tgt, win, d,
+  hipLaunchKernelGGL(ssim_grad_kernel, grid, dim3(256), 0, s, W, H, tiles_x, nb, img, tgt, win, d,
                      (float)(1.0 / n), (float)((double)lambda / n), g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (loss) {

@@ -549,8 +549,19 @@ def l1_dssim_errscale(image, target, lam=0.2, parts=None, delta=None):
             sens = np.abs(dp[j] - dm[j]) / (2.0 * h)
             err_d[j] += sens * np.abs(stats[k]) * delta
     d = parts["d"]
-    # fp32 rounding of the maps themselves
-    for j in range(3):
+    # fp32 rounding of the maps themselves: a few ulp of each term, d_mu
+    # counted by the magnitudes of its four terms (A2 - A1 and 1/B2 - 1/B1
+    # can cancel)
+    mx, my, sxx, syy, sxy = stats
+    A1 = 2.0 * mx * my + SSIM_C1
+    A2 = 2.0 * (sxy - mx * my) + SSIM_C2
+    B1 = mx * mx + my * my + SSIM_C1
+    B2 = (sxx - mx * mx) + (syy - my * my) + SSIM_C2
+    s = A1 * A2 / (B1 * B2)
+    mag_mu = (np.abs(2.0 * my * A2 / (B1 * B2)) + np.abs(2.0 * my * A1 / (B1 * B2)) +
+              np.abs(2.0 * mx * s / B2) + np.abs(2.0 * mx * s / B1))
+    err_d[0] += 8.0 * 2.0 ** -24 * mag_mu
+    for j in (1, 2):
         err_d[j] += 8.0 * 2.0 ** -24 * np.abs(d[j])
     blur_err = [_channels(window_sum, e) for e in err_d]
     blur_mag = [_channels(window_sum, np.abs(dj)) for dj in d]
