@@ -152,6 +152,28 @@ def test_exact_depth_ties_keep_index_order():
     assert np.abs(out["image"] - o["raster"]["image"]).max() <= PIX_TOL
 
 
+@pytest.mark.parametrize("n", [6000, 40000])
+def test_long_tile_lists_keep_the_stable_order(n):
+    """Thousands of instances per tile (the 64 x 64 image has 16 tiles): lists
+    of about 900 and 6,000 entries, with exact depth ties from clones of
+    every fifth Gaussian.  Keys, ids and ranges must equal the oracle's
+    stable sort bit for bit."""
+    base, cam = scenes.tiny_scene(n=n, seed=13)
+    idx = np.concatenate([np.arange(n), np.arange(0, n, 5)])
+    scene = base.subset(idx)
+    out = gpu_frame(scene, cam, backward=False)
+    o = oracle.render(scene, cam)
+    lens = np.diff(o["bins"]["ranges"].reshape(-1, 2), axis=1)
+    print("[edges] n=%d: M=%d, longest tile list %d" % (len(idx), out["M"], lens.max()),
+          flush=True)
+    assert lens.max() > (4096 if n > 10000 else 512)
+    assert out["M"] == len(o["bins"]["keys"])
+    assert_bits_equal(out["keys"], o["bins"]["keys"], "keys")
+    assert_bits_equal(out["ids"], o["bins"]["ids"], "ids")
+    assert_bits_equal(out["ranges"], o["bins"]["ranges"], "ranges")
+    assert np.abs(out["image"] - o["raster"]["image"]).max() <= PIX_TOL
+
+
 def test_loss_value_and_gradient():
     torch = _torch()
     from differentiable_rasterization_amd import raster
