@@ -11,7 +11,8 @@
 extern "C" {
 hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
                                  const float* scales, const float* quats, const float* opac,
-                                 const float* sh, const gs::Cam& cam, const gs::Settings& st,
+                                 const float* sh, int ncams, const gs::Cam* cams,
+                                 const gs::Settings& st,
                                  float* means2d, float* conics, float* depths, int32_t* radii,
                                  float* colors, uint32_t* tiles, float* splats,
                                  hipStream_t stream);
@@ -29,10 +30,12 @@ hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, u
 hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                      const int32_t* radii, const float* depths,
                                      const uint32_t* tiles, const uint32_t* offsets, int32_t W,
-                                     int32_t H, uint64_t M, uint64_t* keys, uint32_t* ids,
+                                     int32_t H, int ncams, uint64_t M, uint64_t* keys,
+                                     uint32_t* ids,
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
-hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges, const uint32_t* ids,
+hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
+                                const uint32_t* ids,
                                 const float* splats, const float* depths, const float* bg,
                                 const gs::Settings& st,
                                 float* image, float* final_T, uint32_t* last_idx,
@@ -175,8 +178,9 @@ gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree, const float* 
                "NULL array pointer");
     GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
   }
+  const gs::Cam c = gs::make_cam(*cam);
   return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh,
-                                          gs::make_cam(*cam), gs::make_settings(*settings),
+                                          1, &c, gs::make_settings(*settings),
                                           means2d, conics, depths, radii, colors, tiles_touched,
                                           splats, (hipStream_t)stream),
                     "gs_project_fwd");
@@ -222,7 +226,7 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, M, keys, ids, tile_ranges,
+                                              offsets, width, height, 1, M, keys, ids, tile_ranges,
                                               workspace, capacity, s),
                     "gs_bin_and_sort");
 }
@@ -243,7 +247,7 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
     GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
     if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
   }
-  return hip_status(gs_launch_raster_fwd(width, height, tile_ranges, ids, splats, depths,
+  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, ids, splats, depths,
                                          background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
                                          out_depth, out_alpha, counters, (hipStream_t)stream),
@@ -341,7 +345,7 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, M, keys, ids, tile_ranges,
+                                              offsets, width, height, 1, M, keys, ids, tile_ranges,
                                               workspace, capacity, s),
                     "gs_bin_and_sort_packed");
 }
@@ -409,6 +413,121 @@ gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, in
                                           dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
                                           accumulate, (hipStream_t)stream),
                     "gs_project_bwd_packed");
+}
+
+namespace {
+
+gs_status check_batch(int32_t num_cams, int64_t ld) {
+  GS_REQUIRE(num_cams >= 1 && num_cams <= gs::kMaxCams, "num_cams must be in [1, 8]");
+  GS_REQUIRE((int64_t)num_cams * ld < ((int64_t)1 << 31), "num_cams * ld must be < 2^31");
+  return GS_OK;
+}
+
+}  // namespace
+
+gs_status gs_project_fwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N, int64_t ld,
+                                 int32_t sh_degree, const float* means, const float* scales,
+                                 const float* quats, const float* opacities, const float* sh,
+                                 const gs_settings* settings, float* means2d, float* conics,
+                                 float* depths, int32_t* radii, float* colors,
+                                 uint32_t* tiles_touched, float* splats, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_REQUIRE(cams != nullptr, "cams is NULL");
+  GS_CHECK(check_settings(settings));
+  gs::Cam cb[gs::kMaxCams];
+  for (int c = 0; c < num_cams; ++c) {
+    GS_CHECK(check_camera(&cams[c]));
+    GS_REQUIRE(cams[c].width == cams[0].width && cams[c].height == cams[0].height,
+               "the cameras of a batch must share one image size");
+    cb[c] = gs::make_cam(cams[c]);
+  }
+  if (ld > 0) {
+    GS_REQUIRE(means2d && conics && depths && radii && colors && tiles_touched && splats,
+               "NULL output pointer");
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
+  }
+  if (N > 0) GS_REQUIRE(means && scales && quats && opacities && sh, "NULL parameter pointer");
+  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh,
+                                          num_cams, cb, gs::make_settings(*settings), means2d,
+                                          conics, depths, radii, colors, tiles_touched, splats,
+                                          (hipStream_t)stream),
+                    "gs_project_fwd_batched");
+}
+
+size_t gs_bin_and_sort_batched_workspace_size(int32_t num_cams, int64_t ld, uint64_t capacity,
+                                              int32_t width, int32_t height) {
+  if (num_cams < 1 || num_cams > gs::kMaxCams || ld < 0) return 0;
+  return gs_binsort_workspace_bytes((int64_t)num_cams * ld, capacity,
+                                    num_cams * gs_num_tiles(width, height));
+}
+
+gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* means2d,
+                                  const int32_t* radii, const float* depths,
+                                  const uint32_t* tiles_touched, int32_t width, int32_t height,
+                                  uint32_t* offsets, uint64_t capacity, uint64_t* num_instances,
+                                  uint64_t* keys, uint32_t* ids, uint32_t* tile_ranges,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  GS_CHECK(check_sizes(0, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(num_instances != nullptr, "num_instances is NULL");
+  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+  GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
+  const int64_t rows = (int64_t)num_cams * ld;
+  const int64_t T = (int64_t)num_cams * gs_num_tiles(width, height);
+  GS_REQUIRE(T < ((int64_t)1 << 31), "too many tiles");
+  if (rows > 0)
+    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets, "NULL array pointer");
+  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
+  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(rows, capacity, (int32_t)T),
+             "workspace smaller than gs_bin_and_sort_batched_workspace_size()");
+  hipStream_t s = (hipStream_t)stream;
+  gs_status st = hip_status(gs_launch_scan(rows, tiles_touched, offsets, nullptr, workspace,
+                                           capacity, (int32_t)T, num_instances, s),
+                            "gs_bin_and_sort_batched(scan)");
+  if (st != GS_OK) return st;
+  const uint64_t M = *num_instances;
+  if (M >= ((uint64_t)1 << 30))
+    return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
+  if (M > capacity) {
+    snprintf(g_err, sizeof(g_err), "gs_bin_and_sort_batched: %llu instances exceed capacity %llu",
+             (unsigned long long)M, (unsigned long long)capacity);
+    return GS_ERR_CAPACITY;
+  }
+  return hip_status(gs_launch_dup_sort_ranges(rows, ld, means2d, radii, depths, tiles_touched,
+                                              offsets, width, height, num_cams, M, keys, ids,
+                                              tile_ranges, workspace, capacity, s),
+                    "gs_bin_and_sort_batched");
+}
+
+gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
+                                   const uint32_t* tile_ranges, const uint32_t* ids,
+                                   const float* splats, const float* depths,
+                                   const float* background, const gs_settings* settings,
+                                   float* image, float* final_T, uint32_t* last_idx,
+                                   float* out_depth, float* out_alpha, uint64_t* counters,
+                                   void* stream) {
+  GS_CHECK(check_sizes(0, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
+  if (ld > 0) {
+    GS_REQUIRE(ids && splats, "NULL splat pointer");
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
+    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  }
+  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, ids, splats,
+                                         depths, background, gs::make_settings(*settings),
+                                         image, final_T, last_idx, out_depth, out_alpha,
+                                         counters, (hipStream_t)stream),
+                    "gs_rasterize_fwd_batched");
 }
 
 size_t gs_l1_dssim_workspace_size(int32_t width, int32_t height) {

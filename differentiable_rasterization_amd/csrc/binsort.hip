@@ -162,14 +162,17 @@ __global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restri
 // ---------------------------------------------------------------------------
 // Stage 3a: duplicate each visible Gaussian once per touched tile
 // ---------------------------------------------------------------------------
+// A batch of cameras is one list of C * ld rows: row c * ld + i is Gaussian
+// i seen by camera c, whose means2d are [c][2][ld] and whose tiles are
+// numbered from c * T (batched = true).
 __global__ __launch_bounds__(256) void duplicate_kernel(
     int64_t N, const float* __restrict__ means2d, int64_t ld, const int32_t* __restrict__ radii,
     const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
-    const uint32_t* __restrict__ offsets, int gx, int gy, uint64_t* __restrict__ keys,
-    uint32_t* __restrict__ ids) {
+    const uint32_t* __restrict__ offsets, int gx, int gy, bool batched,
+    uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
   __shared__ uint32_t s_off[257];
   __shared__ int32_t s_x0[256], s_w[256], s_y0[256];
-  __shared__ uint32_t s_db[256];
+  __shared__ uint32_t s_db[256], s_tb[256];
   const int t = threadIdx.x;
   const int64_t g0 = (int64_t)blockIdx.x * 256;
   const int64_t i = g0 + t;
@@ -179,11 +182,14 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     const uint32_t cnt = tiles_touched[i];
     s_off[t] = off;
     int x0 = 0, x1 = 0, y0 = 0, y1 = 0;
-    if (cnt > 0) tile_rect(means2d[i], means2d[ld + i], radii[i], gx, gy, x0, x1, y0, y1);
+    const int64_t c = batched ? i / ld : 0;
+    if (cnt > 0)
+      tile_rect(means2d[i + c * ld], means2d[i + c * ld + ld], radii[i], gx, gy, x0, x1, y0, y1);
     s_x0[t] = x0;
     s_w[t] = (x1 > x0) ? (x1 - x0) : 1;
     s_y0[t] = y0;
     s_db[t] = __float_as_uint(depths[i]);
+    s_tb[t] = (uint32_t)c * (uint32_t)gx * (uint32_t)gy;
     if (i == N - 1 || t == 255) s_off[t + 1] = off + cnt;
   }
   __syncthreads();
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     const uint32_t w = (uint32_t)s_w[lo];
     const uint32_t ty = (uint32_t)s_y0[lo] + k / w;
     const uint32_t tx = (uint32_t)s_x0[lo] + k % w;
-    const uint32_t tile = ty * (uint32_t)gx + tx;
+    const uint32_t tile = s_tb[lo] + ty * (uint32_t)gx + tx;
     keys[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
     ids[slot] = (uint32_t)(g0 + lo);
   }
@@ -495,15 +501,16 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
 }
 
 // Duplicate, sort and extract ranges for M instances (M <= capacity).
+// ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
 extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                                 const int32_t* radii, const float* depths,
                                                 const uint32_t* tiles, const uint32_t* offsets,
-                                                int32_t W, int32_t H, uint64_t M,
+                                                int32_t W, int32_t H, int ncams, uint64_t M,
                                                 uint64_t* keys, uint32_t* ids, uint32_t* ranges,
                                                 void* workspace, uint64_t capacity, hipStream_t s) {
   using namespace gs;
   const int gx = grid_dim(W), gy = grid_dim(H);
-  const int32_t T = gx * gy;
+  const int32_t T = gx * gy * ncams;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
   if (M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
@@ -526,7 +533,7 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
   const int64_t nblk = (N + 255) / 256;
   hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
-                     depths, tiles, offsets, gx, gy, ka, ia);
+                     depths, tiles, offsets, gx, gy, ncams > 1, ka, ia);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const uint32_t M32 = (uint32_t)M;

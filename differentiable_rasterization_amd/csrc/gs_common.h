@@ -29,6 +29,12 @@ struct Cam {
   float near_p, far_p;
 };
 
+// Up to eight cameras of one batched launch (by value; blockIdx.y selects).
+constexpr int kMaxCams = 8;
+struct CamBatch {
+  Cam c[kMaxCams];
+};
+
 struct Settings {
   float eps2d, alpha_min, alpha_max, T_min, fov_clamp, sh_offset;
 };

@@ -243,17 +243,34 @@ __device__ inline void footprint(float a, float b, float c, float o, float alpha
   ey = sqrtf(Q * c) + 0.02f;
 }
 
+// Camera blockIdx.y of the batch writes its outputs to block c of each
+// output ([c][plane][ld] planes, records [c][ld]).  Rows N .. rows-1 (the
+// padding of a batch, rows = ld) get radius 0 and no tiles.
 template <int DEG>
 __global__ __launch_bounds__(256) void project_fwd_kernel(
-    int64_t N, int64_t ld, const float* __restrict__ means,
+    int64_t N, int64_t rows, int64_t ld, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ opac, const float* __restrict__ sh, Cam cam, Settings st,
+    const float* __restrict__ opac, const float* __restrict__ sh, CamBatch cams, Settings st,
     float* __restrict__ means2d, float* __restrict__ conics, float* __restrict__ depths,
     int32_t* __restrict__ radii, float* __restrict__ colors, uint32_t* __restrict__ tiles,
     float4* __restrict__ splats) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N) return;
+  if (i >= rows) return;
+  const int64_t cb = (int64_t)blockIdx.y;
+  means2d += cb * 2 * ld;
+  conics += cb * 3 * ld;
+  depths += cb * ld;
+  radii += cb * ld;
+  colors += cb * 3 * ld;
+  tiles += cb * ld;
+  splats += cb * 4 * ld;
+  if (i >= N) {
+    radii[i] = 0;
+    tiles[i] = 0u;
+    return;
+  }
+  const Cam cam = cams.c[blockIdx.y];
   // all loads first: every lane keeps its parameters and SH coefficients in
   // flight together (culled lanes share cache lines with visible ones, so
   // their SH lines are fetched anyway)
@@ -619,19 +636,24 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
 
 }  // namespace gs
 
+// One camera (ncams = 1: rows 0 .. N-1 written) or a batch of ncams
+// cameras (outputs [c][...], rows N .. ld-1 padded).
 extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
                                             const float* scales, const float* quats,
-                                            const float* opac, const float* sh,
-                                            const gs::Cam& cam, const gs::Settings& st,
+                                            const float* opac, const float* sh, int ncams,
+                                            const gs::Cam* cams, const gs::Settings& st,
                                             float* means2d, float* conics, float* depths,
                                             int32_t* radii, float* colors, uint32_t* tiles,
                                             float* splats, hipStream_t stream) {
-  if (N == 0) return hipSuccess;
-  const int64_t blocks = (N + 255) / 256;
-#define GS_PFWD(D)                                                                         \
-  hipLaunchKernelGGL(gs::project_fwd_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, \
-                     N, ld, means, scales, quats, opac, sh, cam, st, means2d, conics,       \
-                     depths, radii, colors, tiles, (float4*)splats)
+  const int64_t rows = ncams > 1 ? ld : N;
+  if (rows == 0) return hipSuccess;
+  gs::CamBatch cb;
+  for (int c = 0; c < ncams; ++c) cb.c[c] = cams[c];
+  const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)ncams);
+#define GS_PFWD(D)                                                                        \
+  hipLaunchKernelGGL(gs::project_fwd_kernel<D>, grid, dim3(256), 0, stream, N, rows, ld,    \
+                     means, scales, quats, opac, sh, cb, st, means2d, conics, depths,       \
+                     radii, colors, tiles, (float4*)splats)
   switch (deg) {
     case 0: GS_PFWD(0); break;
     case 1: GS_PFWD(1); break;

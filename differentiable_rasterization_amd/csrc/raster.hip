@@ -178,8 +178,11 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   __shared__ uint32_t s_cnt[4];
   __shared__ uint32_t s_wc[4][4];
   int tx, ty;
-  if (!block_tile((int)blockIdx.x, gx, grid_dim(H), tx, ty)) return;
-  const int tile = ty * gx + tx;
+  const int gy = grid_dim(H);
+  if (!block_tile((int)blockIdx.x, gx, gy, tx, ty)) return;
+  // camera blockIdx.y of a batch: its tiles follow the earlier cameras'
+  // (gx * gy each) and its pixels their images
+  const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     add_counters(cnt, inside ? n_eval : 0u, n_blend, plain, tile_plain);
   }
   if (!inside) return;
-  const int64_t p = (int64_t)py * W + px;
+  const int64_t p = ((int64_t)blockIdx.y * H + py) * W + px;
   image[3 * p + 0] = fmaf(T, bg0, C0);
   image[3 * p + 1] = fmaf(T, bg1, C1);
   image[3 * p + 2] = fmaf(T, bg2, C2);
@@ -636,14 +639,16 @@ __global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n, int
 
 }  // namespace gs
 
-extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, const uint32_t* ranges,
-                                           const uint32_t* ids, const float* splats,
-                                           const float* depths, const float* bg,
-                                           const gs::Settings& st, float* image,
+// ncams images of W x H (a batch: ranges over ncams * T tiles, outputs
+// [c][H][W]).
+extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
+                                           const uint32_t* ranges, const uint32_t* ids,
+                                           const float* splats, const float* depths,
+                                           const float* bg, const gs::Settings& st, float* image,
                                            float* final_T, uint32_t* last_idx, float* out_depth,
                                            float* out_alpha, uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
-  const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
+  const dim3 grid(gs::tile_grid_blocks(gx, gy), (unsigned)ncams), block(256);
   const float4* sp = (const float4*)splats;
   if (counters) {
     if (out_depth)

@@ -29,7 +29,9 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_densify_prune_workspace_size", "gs_densify_prune", "gs_bin_and_sort_packed",
             "gs_rasterize_bwd_packed", "gs_project_bwd_packed", "gs_l1_dssim_workspace_size",
             "gs_l1_dssim_loss_grad", "gs_default_adam_config", "gs_adam_step",
-            "gs_adam_step_packed")
+            "gs_adam_step_packed", "gs_project_fwd_batched",
+            "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
+            "gs_rasterize_fwd_batched")
 
 
 class GsError(RuntimeError):
@@ -110,6 +112,15 @@ def load():
     lib.gs_adam_step_packed.restype = C.c_int
     lib.gs_adam_step_packed.argtypes = [i64, P, i64, i64, i64, i32, i64, P] + [P] * 7 + \
         [P] * 5 + [P, P, P]
+    lib.gs_project_fwd_batched.restype = C.c_int
+    lib.gs_project_fwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 5 + [P] + [P] * 7 + [P]
+    lib.gs_bin_and_sort_batched_workspace_size.restype = C.c_size_t
+    lib.gs_bin_and_sort_batched_workspace_size.argtypes = [i32, i64, u64, i32, i32]
+    lib.gs_bin_and_sort_batched.restype = C.c_int
+    lib.gs_bin_and_sort_batched.argtypes = [i32, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
+                                            P, C.c_size_t, P]
+    lib.gs_rasterize_fwd_batched.restype = C.c_int
+    lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 13
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -275,6 +286,48 @@ def gs_project_bwd_packed(num_visible, vis_ids, N, ld, ldv, sh_degree, means, sc
                                      C.byref(settings), _p(radii), _p(grads2d), _p(dL_dmeans),
                                      _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
                                      _p(dL_dsh), int(accumulate), _stream(stream)))
+
+
+def gs_project_fwd_batched(cams, N, ld, sh_degree, means, scales, quats, opacities, sh,
+                           settings, means2d, conics, depths, radii, colors, tiles_touched,
+                           splats, stream=None):
+    lib = load()
+    arr = (gs_camera * len(cams))(*cams)
+    _check(lib.gs_project_fwd_batched(len(cams), arr, N, ld, sh_degree, _p(means), _p(scales),
+                                      _p(quats), _p(opacities), _p(sh), C.byref(settings),
+                                      _p(means2d), _p(conics), _p(depths), _p(radii),
+                                      _p(colors), _p(tiles_touched), _p(splats),
+                                      _stream(stream)))
+
+
+def gs_bin_and_sort_batched_workspace_size(num_cams, ld, capacity, width, height) -> int:
+    return int(load().gs_bin_and_sort_batched_workspace_size(num_cams, ld, capacity, width,
+                                                             height))
+
+
+def gs_bin_and_sort_batched(num_cams, ld, means2d, radii, depths, tiles_touched, width, height,
+                            offsets, capacity, keys, ids, tile_ranges, workspace,
+                            workspace_bytes, num_instances, stream=None):
+    """Returns (status, M); GS_ERR_CAPACITY is returned, not raised."""
+    lib = load()
+    st = lib.gs_bin_and_sort_batched(num_cams, ld, _p(means2d), _p(radii), _p(depths),
+                                     _p(tiles_touched), width, height, _p(offsets), capacity,
+                                     _p(num_instances), _p(keys), _p(ids), _p(tile_ranges),
+                                     _p(workspace), workspace_bytes, _stream(stream))
+    if st not in (GS_OK, GS_ERR_CAPACITY):
+        _check(st)
+    return st, int(num_instances[0])
+
+
+def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, depths,
+                             background, settings, image, final_T, last_idx, out_depth=None,
+                             out_alpha=None, counters=None, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_fwd_batched(num_cams, ld, width, height, _p(tile_ranges), _p(ids),
+                                        _p(splats), _p(depths), bg, C.byref(settings),
+                                        _p(image), _p(final_T), _p(last_idx), _p(out_depth),
+                                        _p(out_alpha), _p(counters), _stream(stream)))
 
 
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
@@ -541,3 +594,70 @@ class Frame:
     def backward(self, g: Gaussians, dL_dimage=None, accumulate=0, absgrad=False):
         self.rasterize_backward(g, dL_dimage, absgrad=absgrad)
         self.project_backward(g, accumulate)
+
+
+class BatchFrame:
+    """Forward of a batch of cameras (one image size) with one launch per
+    stage: projection, binning + sort, compositing.  Per-camera outputs are
+    blocks [c] of each buffer; only the binning synchronises."""
+
+    def __init__(self, ld, sh_degree, width, height, num_cams, capacity=None, settings=None,
+                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda"):
+        import torch
+        self.torch = torch
+        self.device = device
+        self.ld, self.sh_degree, self.W, self.H = int(ld), int(sh_degree), int(width), int(height)
+        self.C = int(num_cams)
+        self.settings = settings if settings is not None else default_settings()
+        self.background = tuple(float(x) for x in background)
+        self.T = num_tiles(width, height)
+        C_, ld_ = self.C, self.ld
+        f32, i32 = torch.float32, torch.int32
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.means2d, self.conics = z((C_, 2, ld_), f32), z((C_, 3, ld_), f32)
+        self.depths, self.radii = z((C_, ld_), f32), z((C_, ld_), i32)
+        self.colors, self.tiles = z((C_, 3, ld_), f32), z((C_, ld_), i32)
+        self.offsets = z((max(C_ * ld_, 1),), i32)
+        self.splats = z((max(C_ * ld_, 1), 16), f32)
+        self.ranges = z((C_ * self.T, 2), i32)
+        self.image = z((C_, height, width, 3), f32)
+        self.final_T = z((C_, height, width), f32)
+        self.last_idx = z((C_, height, width), i32)
+        self.out_depth = z((C_, height, width), f32) if with_depth_alpha else None
+        self.out_alpha = z((C_, height, width), f32) if with_depth_alpha else None
+        self.m_host = torch.zeros((1,), dtype=torch.int64, pin_memory=True)
+        self.M = 0
+        self._alloc_sort(capacity if capacity else max(1024, 4 * C_ * ld_))
+
+    def _alloc_sort(self, capacity):
+        torch = self.torch
+        self.capacity = int(capacity)
+        self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
+        self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
+        self.ws_bytes = gs_bin_and_sort_batched_workspace_size(self.C, self.ld, self.capacity,
+                                                               self.W, self.H)
+        self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8,
+                                     device=self.device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.ws = self.workspace[off:off + self.ws_bytes]
+
+    def forward(self, g: "Gaussians", cams):
+        assert len(cams) == self.C
+        self.cams = [c if isinstance(c, gs_camera) else make_camera(c) for c in cams]
+        gs_project_fwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
+                               g.opacities, g.sh, self.settings, self.means2d, self.conics,
+                               self.depths, self.radii, self.colors, self.tiles, self.splats)
+        args = lambda: (self.C, self.ld, self.means2d, self.radii, self.depths, self.tiles,
+                        self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
+                        self.ranges, self.ws, self.ws_bytes, self.m_host)
+        st, M = gs_bin_and_sort_batched(*args())
+        if st == GS_ERR_CAPACITY:
+            self._alloc_sort(int(M * 1.25) + 1024)
+            st, M = gs_bin_and_sort_batched(*args())
+            _check(st)
+        self.M = M
+        gs_rasterize_fwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
+                                 self.splats, self.depths, self.background, self.settings,
+                                 self.image, self.final_T, self.last_idx, self.out_depth,
+                                 self.out_alpha)
+        return self.image

@@ -232,6 +232,57 @@ GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const 
                          float* dL_dscales, float* dL_dquats, float* dL_dopacities,
                          float* dL_dsh, int32_t accumulate, void* stream);
 
+/* Batched cameras: one launch per stage for num_cams cameras (1 .. 8) of one
+ * image size, the Gaussians read once.  Row c * ld + i of the per-camera
+ * outputs is Gaussian i seen by camera c, and tile c * T + t is tile t of
+ * camera c, so a batch is one list of num_cams * ld rows over
+ * num_cams * T tiles and its results per camera equal those of the
+ * single-camera calls (keys carry the tile number c * T + t; ids the row
+ * c * ld + i, which indexes the batch's splat records).
+ *
+ * gs_project_fwd_batched: gs_project_fwd for every camera of cams (HOST
+ * array); outputs means2d [c][2][ld], conics [c][3][ld], depths [c][ld],
+ * radii [c][ld], colors [c][3][ld], tiles_touched [c][ld], splats
+ * [c][ld][16].  Rows N .. ld-1 of each camera get radius 0 and no tiles,
+ * so the outputs are valid input to gs_bin_and_sort_batched.
+ * num_cams * ld < 2^31. */
+GS_API gs_status gs_project_fwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N,
+                                        int64_t ld, int32_t sh_degree, const float* means,
+                                        const float* scales, const float* quats,
+                                        const float* opacities, const float* sh,
+                                        const gs_settings* settings, float* means2d,
+                                        float* conics, float* depths, int32_t* radii,
+                                        float* colors, uint32_t* tiles_touched, float* splats,
+                                        void* stream);
+
+/* gs_bin_and_sort_batched: gs_bin_and_sort over the num_cams * ld rows of a
+ * batch (offsets [num_cams * ld]; tile_ranges [num_cams * T][2]).  The
+ * sorted list holds camera 0's tiles first.  Capacity protocol and errors as
+ * gs_bin_and_sort; workspace of gs_bin_and_sort_batched_workspace_size()
+ * bytes (0 for an invalid num_cams). */
+GS_API size_t gs_bin_and_sort_batched_workspace_size(int32_t num_cams, int64_t ld,
+                                                     uint64_t capacity, int32_t width,
+                                                     int32_t height);
+GS_API gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* means2d,
+                                         const int32_t* radii, const float* depths,
+                                         const uint32_t* tiles_touched, int32_t width,
+                                         int32_t height, uint32_t* offsets, uint64_t capacity,
+                                         uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                                         uint32_t* tile_ranges, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* gs_rasterize_fwd_batched: gs_rasterize_fwd for every camera of a batch;
+ * image [c][H][W][3], final_T, last_idx, out_depth, out_alpha [c][H][W]
+ * (depths [c][ld] from the batch's projection).  last_idx counts entries of
+ * the tile's own list, as in the single-camera call. */
+GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width,
+                                          int32_t height, const uint32_t* tile_ranges,
+                                          const uint32_t* ids, const float* splats,
+                                          const float* depths, const float* background,
+                                          const gs_settings* settings, float* image,
+                                          float* final_T, uint32_t* last_idx, float* out_depth,
+                                          float* out_alpha, uint64_t* counters, void* stream);
+
 /* Packed mode (the gsplat guide §4.1 trains with its packed and sparse
  * gradient switches on: only the Gaussians that reach the image take part
  * after the projection, and only they receive gradients).  The visible set

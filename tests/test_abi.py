@@ -232,6 +232,36 @@ def test_training_step_calls_reject_bad_arguments(lib):
     assert adam_p(V=0, ldv=0, vis=None) == raster.GS_OK
 
 
+def test_batched_calls_reject_bad_arguments(lib):
+    dummy = C.c_void_p(256)
+    st = raster.default_settings()
+    cams = (raster.gs_camera * 9)(*([_cam()] * 9))
+
+    def proj(n=2, ld=10):
+        return lib.gs_project_fwd_batched(n, cams, 10, ld, 0, *([dummy] * 5), C.byref(st),
+                                          *([dummy] * 7), None)
+    assert proj(n=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert proj(n=9) == raster.GS_ERR_INVALID_ARGUMENT
+    assert proj(ld=9) == raster.GS_ERR_INVALID_ARGUMENT           # ld < N
+    assert proj(ld=1 << 29, n=4) == raster.GS_ERR_INVALID_ARGUMENT  # 4 ld >= 2^31
+    other = (raster.gs_camera * 2)(_cam(64, 64), _cam(32, 64))
+    assert lib.gs_project_fwd_batched(2, other, 10, 10, 0, *([dummy] * 5), C.byref(st),
+                                      *([dummy] * 7), None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_bin_and_sort_batched_workspace_size(0, 10, 100, 64, 64) == 0
+    assert lib.gs_bin_and_sort_batched_workspace_size(2, 10, 100, 64, 64) > 0
+    M = C.c_uint64(0)
+    r = lib.gs_bin_and_sort_batched(9, 10, *([dummy] * 4), 64, 64, dummy, 100, C.byref(M),
+                                    dummy, dummy, dummy, dummy, 1 << 30, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT
+    r = lib.gs_bin_and_sort_batched(2, 10, *([dummy] * 4), 64, 64, dummy, 100, C.byref(M),
+                                    dummy, dummy, dummy, dummy, 16, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # workspace too small
+    bg = (C.c_float * 3)(0, 0, 0)
+    r = lib.gs_rasterize_fwd_batched(2, 10, 64, 64, None, dummy, dummy, None, bg, C.byref(st),
+                                     dummy, dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # no tile ranges
+
+
 def test_densify_rejects_bad_arguments(lib):
     dummy = C.c_void_p(256)
     n_out = C.c_int64(0)

@@ -1,0 +1,112 @@
+"""GPU checks of the batched-camera forward (one launch per stage for a
+batch of cameras, the 3M-Gaussian 4K workload's batch of four poses): for
+every camera of a batch, the projection planes and records, the sorted keys
+and ids, the tile ranges and the images must equal the single-camera calls'
+bit for bit (those are checked against the oracle elsewhere), after removing
+the batch's numbering (tile c * T + t, row c * ld + i, camera c's instances
+after those of cameras 0 .. c-1).  One small batch is also checked against
+the oracle directly."""
+import numpy as np
+import pytest
+
+import oracle
+from differentiable_rasterization_amd import scenes
+from parity_util import PIX_TOL, assert_bits_equal, gpu_frame
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(scene, cams, ld=None):
+    import torch
+    from differentiable_rasterization_amd import raster
+    g = raster.Gaussians.from_scene(scene, ld=ld)
+    bf = raster.BatchFrame(g.ld, scene.sh_degree, cams[0].width, cams[0].height, len(cams),
+                           with_depth_alpha=True)
+    bf.forward(g, cams)
+    torch.cuda.synchronize()
+    return g, bf
+
+
+def _check_batch(name, scene, cams, ld=None):
+    g, bf = _batch(scene, cams, ld)
+    N, L, T = scene.n, g.ld, bf.T
+    keys = bf.keys[:bf.M].cpu().numpy().view(np.uint64)
+    ids = bf.ids[:bf.M].cpu().numpy().view(np.uint32)
+    ranges = bf.ranges.cpu().numpy().view(np.uint32).reshape(len(cams), T, 2)
+    rec = bf.splats.cpu().numpy().reshape(len(cams), L, 16)
+    base = 0
+    for c, cam in enumerate(cams):
+        one = gpu_frame(scene, cam, backward=False, depth_alpha=True, ld=ld)
+        col = lambda t: t[c][:, :N].T if t.dim() == 3 else t[c][:N]
+        for k in ("means2d", "conics", "depths", "radii", "colors"):
+            assert_bits_equal(col(getattr(bf, k)).cpu().numpy(), one[k], "%s cam %d" % (k, c))
+        assert_bits_equal(col(bf.tiles).cpu().numpy().view(np.uint32), one["tiles"], "tiles")
+        # padding rows of the batch: no tiles
+        assert np.all(bf.tiles[c][N:].cpu().numpy() == 0)
+        vis = one["radii"] > 0
+        one_rec = one["frame"].splats[:N].cpu().numpy()
+        assert_bits_equal(rec[c, :N][vis], one_rec[vis], "records cam %d" % c)
+        M = one["M"]
+        kc, ic = keys[base:base + M], ids[base:base + M]
+        assert_bits_equal((kc >> np.uint64(32)) - np.uint64(c * T), one["keys"] >> np.uint64(32),
+                          "key tiles cam %d" % c)
+        assert_bits_equal(kc & np.uint64(0xFFFFFFFF), one["keys"] & np.uint64(0xFFFFFFFF),
+                          "key depths cam %d" % c)
+        assert_bits_equal(ic - np.uint32(c * L), one["ids"], "ids cam %d" % c)
+        r = ranges[c].astype(np.int64)
+        r1 = one["ranges"].reshape(T, 2).astype(np.int64)
+        nz = r1[:, 1] > r1[:, 0]
+        assert np.array_equal(r[nz] - base, r1[nz]), "ranges cam %d" % c
+        assert np.all(r[~nz] == 0)
+        for k, a in (("image", bf.image), ("final_T", bf.final_T), ("depth", bf.out_depth),
+                     ("alpha", bf.out_alpha)):
+            assert_bits_equal(a[c].cpu().numpy(), one[k], "%s cam %d" % (k, c))
+        assert_bits_equal(bf.last_idx[c].cpu().numpy().view(np.uint32), one["last"], "last")
+        base += M
+    assert base == bf.M
+    print("[batch] %s: %d cameras, M=%d" % (name, len(cams), bf.M), flush=True)
+    return bf
+
+
+def test_batch_against_oracle_small():
+    scene = scenes.cluster_scene(n=20_000, seed=17)
+    cams = scenes.sphere_poses(3, 6.0, 31, 200, 136, scenes.focal_for(200))
+    g, bf = _batch(scene, cams)
+    T = bf.T
+    base = 0
+    for c, cam in enumerate(cams):
+        o = oracle.render(scene, cam)
+        M = len(o["bins"]["keys"])
+        kc = bf.keys[base:base + M].cpu().numpy().view(np.uint64)
+        want = o["bins"]["keys"] + (np.uint64(c * T) << np.uint64(32))
+        assert_bits_equal(kc, want, "keys cam %d" % c)
+        assert_bits_equal(bf.ids[base:base + M].cpu().numpy().view(np.uint32) -
+                          np.uint32(c * g.ld), o["bins"]["ids"], "ids cam %d" % c)
+        d = np.abs(bf.image[c].cpu().numpy() - o["raster"]["image"]).max()
+        assert d <= PIX_TOL, (c, d)
+        base += M
+    assert base == bf.M
+
+
+def test_batch_cluster_200k_three_poses():
+    scene = scenes.cluster_scene(n=200_000, seed=13)
+    cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
+    _check_batch("cluster_200k_640x416", scene, cams)
+
+
+def test_batch_ragged_box_padded_rows():
+    s, cam = scenes.box_scene(n=20000, seed=12, width=500, height=270, fx=290.0)
+    cam2 = scenes.look_at_camera(np.array([3.0, 2.0, -7.0]), 500, 270, 290.0)
+    _check_batch("box_20k_ragged", s, [cam, cam2], ld=20011)
+
+
+def test_batch_single_camera():
+    scene = scenes.cluster_scene(n=50_000, seed=14)
+    cams = scenes.sphere_poses(1, 6.0, 31, 320, 208, scenes.focal_for(320))
+    _check_batch("one camera", scene, cams)
+
+
+def test_batch_cluster_3m_4k_four_poses():
+    """The 3M-Gaussian 3840 x 2160 workload's batch of four poses."""
+    scene, cams, _ = scenes.make_config("cluster_3m_4k")
+    _check_batch("cluster_3m_4k", scene, cams)
