@@ -166,6 +166,45 @@ def densify_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
+    """Forward only, the poses in groups of ``batch``: each pose through the
+    single-camera calls, then each group through the batched calls (one
+    launch per stage).  Returns frames/s both ways."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    g = raster.Gaussians.from_scene(scene)
+    W, H = cams[0].width, cams[0].height
+    gc = [raster.make_camera(c) for c in cams]
+    groups = [gc[i:i + batch] for i in range(0, len(gc) - batch + 1, batch)]
+    fr = raster.Frame(g.ld, scene.sh_degree, W, H, with_depth_alpha=depth_alpha)
+    bf = raster.BatchFrame(g.ld, scene.sh_degree, W, H, batch, with_depth_alpha=depth_alpha)
+    reps = max(1, args.steps // (len(groups) * batch))
+
+    def single():
+        for grp in groups:
+            for c in grp:
+                fr.forward(g, c)
+
+    def batched():
+        for grp in groups:
+            bf.forward(g, grp)
+
+    out = {}
+    for name, fn in (("single", single), ("batched", batched)):
+        fn()  # warm-up (also sizes the sort buffers)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = reps * len(groups) * batch / (time.perf_counter() - t0)
+    return {"batch": batch, "frames": reps * len(groups) * batch,
+            "fwd_fps_single_calls": round(out["single"], 2),
+            "fwd_fps_batched_calls": round(out["batched"], 2),
+            "speedup": round(out["batched"] / out["single"], 3),
+            "depth_alpha": bool(depth_alpha)}
+
+
 def train_step_bench(args, scene, gcams, targets, capacity):
     """A whole training step as the gsplat guide 4.1 loop runs it: packed
     forward and backward, the mean-L1 + 0.2 D-SSIM loss gradient and the
@@ -264,6 +303,10 @@ def main():
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the training-step measurement (packed calls, L1 + 0.2 D-SSIM, "
                          "per-group Adam)")
+    ap.add_argument("--fwd-batch-only", action="store_true",
+                    help="only the forward of the poses in batches of --batch (single-camera "
+                         "calls against batched calls), e.g. with --config cluster_3m_4k")
+    ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -288,6 +331,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
     scene, cams, loss_kind = scenes.make_config(args.config)
+    if args.fwd_batch_only:
+        r = fwd_batch_bench(args, scene, cams, args.batch, depth_alpha=(loss_kind is None))
+        print(json.dumps({"metric": "forward frames/sec, batched-camera calls", "value":
+                          r["fwd_fps_batched_calls"], "unit": "frames/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+                          "config": {"workload": args.config, "gaussians": scene.n,
+                                     "width": cams[0].width, "height": cams[0].height,
+                                     "sh_degree": scene.sh_degree, "poses": len(cams)},
+                          "fwd_batch": r}), flush=True)
+        return
     loss_kind = loss_kind or "l1"
     W, H = cams[0].width, cams[0].height
     N, K = scene.n, (scene.sh_degree + 1) ** 2
@@ -376,6 +429,8 @@ def main():
     packed_line = None
     train_line = None if args.no_train_step else train_step_bench(args, scene, gcams, targets,
                                                                    fr.capacity)
+    batch_line = None if args.no_train_step else fwd_batch_bench(args, scene, cams, args.batch,
+                                                                  depth_alpha=False)
     if not args.packed:
         # the same steps through the packed calls (visible list, sparse
         # gradient rows), reported beside the dense headline
@@ -459,6 +514,8 @@ def main():
         out["packed"] = packed_line
     if train_line is not None:
         out["train_step"] = train_line
+    if batch_line is not None:
+        out["fwd_batch"] = batch_line
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
     print(json.dumps(out), flush=True)
