@@ -19,7 +19,8 @@ hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* me
 hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids, int64_t ldo,
                                  int deg, const float* means,
                                  const float* scales, const float* quats, const float* sh,
-                                 const gs::Cam& cam, const gs::Settings& st, const int32_t* radii,
+                                 int ncams, const gs::Cam* cams, const gs::Settings& st,
+                                 const int32_t* radii,
                                  const float* grads2d, float* o_means, float* o_scales,
                                  float* o_quats, float* o_opac, float* o_sh, int accumulate,
                                  hipStream_t stream);
@@ -41,7 +42,8 @@ hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t*
                                 float* image, float* final_T, uint32_t* last_idx,
                                 float* out_depth, float* out_alpha, uint64_t* counters,
                                 hipStream_t s);
-hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
+hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
+                                const uint32_t* ranges,
                                 const uint32_t* ids, const float* splats, const uint32_t* offsets,
                                 const uint32_t* tiles, const float* bg, const gs::Settings& st,
                                 const float* final_T, const uint32_t* last_idx,
@@ -278,7 +280,7 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
     GS_REQUIRE(partials != nullptr, "partials is NULL");
     GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
   }
-  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
+  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, ids, splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
                                          grads2d, absgrad, nullptr, 0, counters,
@@ -303,8 +305,9 @@ gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* 
                "NULL array pointer");
     GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
   }
+  const gs::Cam c = gs::make_cam(*cam);
   return hip_status(gs_launch_project_bwd(N, ld, nullptr, ld, sh_degree, means, scales, quats, sh,
-                                          gs::make_cam(*cam), gs::make_settings(*settings), radii,
+                                          1, &c, gs::make_settings(*settings), radii,
                                           grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities,
                                           dL_dsh, accumulate, (hipStream_t)stream),
                     "gs_project_bwd");
@@ -379,7 +382,7 @@ gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t 
   }
   // an empty list still needs a non-NULL pointer to select the packed rows
   static const uint32_t kNoIds = 0;
-  return hip_status(gs_launch_raster_bwd(N, width, height, tile_ranges, ids, splats, offsets,
+  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, ids, splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
                                          grads2d, absgrad, vis_ids ? vis_ids : &kNoIds,
@@ -407,8 +410,9 @@ gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, in
                  dL_dscales && dL_dquats && dL_dopacities && dL_dsh,
              "NULL array pointer");
   GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
+  const gs::Cam c = gs::make_cam(*cam);
   return hip_status(gs_launch_project_bwd(num_visible, ld, vis_ids, ldv, sh_degree, means, scales,
-                                          quats, sh, gs::make_cam(*cam),
+                                          quats, sh, 1, &c,
                                           gs::make_settings(*settings), radii, grads2d, dL_dmeans,
                                           dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
                                           accumulate, (hipStream_t)stream),
@@ -528,6 +532,73 @@ gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
                                          image, final_T, last_idx, out_depth, out_alpha,
                                          counters, (hipStream_t)stream),
                     "gs_rasterize_fwd_batched");
+}
+
+gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
+                                   const uint32_t* tile_ranges, const uint32_t* ids,
+                                   const float* splats, const uint32_t* offsets,
+                                   const uint32_t* tiles_touched, uint64_t num_instances,
+                                   const float* background, const gs_settings* settings,
+                                   const float* final_T, const uint32_t* last_idx,
+                                   const float* dL_dimage, float* partials,
+                                   uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                                   uint64_t* counters, void* stream) {
+  GS_CHECK(check_sizes(0, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
+  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
+  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
+  const int64_t rows = (int64_t)num_cams * ld;
+  if (rows > 0) {
+    GS_REQUIRE(ids && splats && offsets && tiles_touched && grads2d,
+               "NULL splat, offset or gradient pointer");
+    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
+  }
+  if (num_instances > 0) {
+    GS_REQUIRE(partials != nullptr, "partials is NULL");
+    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
+  }
+  return hip_status(gs_launch_raster_bwd(rows, width, height, num_cams, tile_ranges, ids, splats,
+                                         offsets, tiles_touched, background,
+                                         gs::make_settings(*settings), final_T, last_idx,
+                                         dL_dimage, partials, num_instances, grads2d, absgrad,
+                                         nullptr, 0, counters, (hipStream_t)stream),
+                    "gs_rasterize_bwd_batched");
+}
+
+gs_status gs_project_bwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N, int64_t ld,
+                                 int32_t sh_degree, const float* means, const float* scales,
+                                 const float* quats, const float* sh, const gs_settings* settings,
+                                 const int32_t* radii, const float* grads2d, float* dL_dmeans,
+                                 float* dL_dscales, float* dL_dquats, float* dL_dopacities,
+                                 float* dL_dsh, int32_t accumulate, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
+  GS_REQUIRE(cams != nullptr, "cams is NULL");
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+  gs::Cam cb[gs::kMaxCams];
+  for (int c = 0; c < num_cams; ++c) {
+    GS_CHECK(check_camera(&cams[c]));
+    cb[c] = gs::make_cam(cams[c]);
+  }
+  if (N > 0) {
+    GS_REQUIRE(means && scales && quats && sh && radii && grads2d && dL_dmeans && dL_dscales &&
+                   dL_dquats && dL_dopacities && dL_dsh,
+               "NULL array pointer");
+    GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
+  }
+  return hip_status(gs_launch_project_bwd(N, ld, nullptr, ld, sh_degree, means, scales, quats, sh,
+                                          num_cams, cb, gs::make_settings(*settings), radii,
+                                          grads2d, dL_dmeans, dL_dscales, dL_dquats,
+                                          dL_dopacities, dL_dsh, accumulate,
+                                          (hipStream_t)stream),
+                    "gs_project_bwd_batched");
 }
 
 size_t gs_l1_dssim_workspace_size(int32_t width, int32_t height) {

@@ -393,28 +393,32 @@ __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, 
 // record is row r of grads2d and its gradients go to row r of the output
 // planes (leading dimension ldo), so nothing is written for Gaussians off
 // the list.  Otherwise row r is Gaussian r and ldo = ld.
-template <int DEG, bool kPacked>
+// Batched form (kBatched): cameras 0 .. ncams-1 in turn, radii [c][ld] and
+// records [c * ld + i]; camera c > 0 adds to what the cameras before wrote,
+// so the outputs are the sum over the cameras that see the Gaussian.
+template <int DEG, bool kPacked, bool kBatched>
 __global__ __launch_bounds__(256) void project_bwd_kernel(
     int64_t N, int64_t ld, const uint32_t* __restrict__ vis_ids, int64_t ldo,
     const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ sh, Cam cam, Settings st, const int32_t* __restrict__ radii,
-    const float4* __restrict__ grads2d, float* __restrict__ o_means,
-    float* __restrict__ o_scales, float* __restrict__ o_quats, float* __restrict__ o_opac,
-    float* __restrict__ o_sh, int accumulate) {
+    const float* __restrict__ sh, CamBatch cams, int ncams, Settings st,
+    const int32_t* __restrict__ radii, const float4* __restrict__ grads2d,
+    float* __restrict__ o_means, float* __restrict__ o_scales, float* __restrict__ o_quats,
+    float* __restrict__ o_opac, float* __restrict__ o_sh, int accumulate) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= N) return;
   const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
-  const bool vis = radii[i] > 0;
-  // every load of a visible lane is issued here, ahead of the fp64 chain, so
-  // that each lane keeps its whole working set in flight (the kernel runs
-  // at two waves per SIMD)
+  const int nc = kBatched ? ncams : 1;
+  bool anyvis = false;
+  for (int c = 0; c < nc; ++c) anyvis |= radii[(int64_t)c * ld + i] > 0;
+  // every parameter load of a visible lane is issued here, ahead of the
+  // fp64 chain, so that each lane keeps its whole working set in flight
+  // (the kernel runs at two waves per SIMD)
   float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
-  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
 #pragma unroll
   for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
-  if (vis) {
+  if (anyvis) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       pm[k] = means[(int64_t)k * ld + i];
@@ -422,16 +426,24 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
-    r0 = grads2d[4 * r + 0];
-    r1 = grads2d[4 * r + 1];
-    r2 = grads2d[4 * r + 2];
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
   }
+  for (int c = 0; c < nc; ++c) {
+  const Cam cam = cams.c[c];
+  const bool vis = radii[(int64_t)c * ld + i] > 0;
+  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
+  if (vis) {
+    const int64_t rr = kBatched ? (int64_t)c * ld + r : r;
+    r0 = grads2d[4 * rr + 0];
+    r1 = grads2d[4 * rr + 1];
+    r2 = grads2d[4 * rr + 2];
+  }
+  const int acc = accumulate | (c > 0 ? 1 : 0);
   // culled Gaussians get zeros (overwrite) or are left alone (accumulate);
   // both kinds of lanes store through the same instructions below, so a
   // cache line of a plane is written once
-  const bool store = vis || !accumulate;
+  const bool store = vis || !acc;
 
   // Phase 1, the SH side (done first so that the 3K SH registers are free
   // before the fp64 geometry chain): view direction, the colour's clamp
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
       for (int ch = 0; ch < 3; ++ch) {
         const int64_t p = (int64_t)(j * 3 + ch) * ldo + r;
         const float gval = Yf[j] * gcol[ch];
-        o_sh[p] = accumulate ? o_sh[p] + gval : gval;
+        o_sh[p] = acc ? o_sh[p] + gval : gval;
         wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
       }
       if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
@@ -623,15 +635,16 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   if (store) {
     for (int k = 0; k < 3; ++k) {
       const int64_t p = (int64_t)k * ldo + r;
-      o_means[p] = accumulate ? o_means[p] + om[k] : om[k];
-      o_scales[p] = accumulate ? o_scales[p] + os[k] : os[k];
+      o_means[p] = acc ? o_means[p] + om[k] : om[k];
+      o_scales[p] = acc ? o_scales[p] + os[k] : os[k];
     }
     for (int k = 0; k < 4; ++k) {
       const int64_t p = (int64_t)k * ldo + r;
-      o_quats[p] = accumulate ? o_quats[p] + oq[k] : oq[k];
+      o_quats[p] = acc ? o_quats[p] + oq[k] : oq[k];
     }
-    o_opac[r] = accumulate ? o_opac[r] + oo : oo;
+    o_opac[r] = acc ? o_opac[r] + oo : oo;
   }
+  }  // cameras
 }
 
 }  // namespace gs
@@ -666,23 +679,28 @@ extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, cons
 
 // vis_ids NULL: N Gaussians, outputs with leading dimension ld.  Otherwise
 // N rows of the packed list vis_ids, outputs with leading dimension ldo.
+// ncams > 1: a batch of cameras (dense rows only), summed into the outputs.
 extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
                                             int64_t ldo, int deg, const float* means,
                                             const float* scales, const float* quats,
-                                            const float* sh, const gs::Cam& cam,
+                                            const float* sh, int ncams, const gs::Cam* cams,
                                             const gs::Settings& st, const int32_t* radii,
                                             const float* grads2d, float* o_means,
                                             float* o_scales, float* o_quats, float* o_opac,
                                             float* o_sh, int accumulate, hipStream_t stream) {
   if (N == 0) return hipSuccess;
+  gs::CamBatch cb;
+  for (int c = 0; c < ncams; ++c) cb.c[c] = cams[c];
   const int64_t blocks = (N + 255) / 256;
-#define GS_PBWD(D, PK)                                                                    \
-  hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK>), dim3((unsigned)blocks), dim3(256), 0,  \
-                     stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh, cam,  \
-                     st, radii, (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, \
-                     o_sh, accumulate)
-#define GS_PBWD2(D) \
-  if (vis_ids) GS_PBWD(D, true); else GS_PBWD(D, false)
+#define GS_PBWD(D, PK, BT)                                                                \
+  hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK, BT>), dim3((unsigned)blocks), dim3(256), \
+                     0, stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh, cb, \
+                     ncams, st, radii, (const float4*)grads2d, o_means, o_scales, o_quats,   \
+                     o_opac, o_sh, accumulate)
+#define GS_PBWD2(D)                          \
+  if (ncams > 1) GS_PBWD(D, false, true);     \
+  else if (vis_ids) GS_PBWD(D, true, false);  \
+  else GS_PBWD(D, false, false)
   switch (deg) {
     case 0: GS_PBWD2(0); break;
     case 1: GS_PBWD2(1); break;

@@ -370,8 +370,10 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   auto& s_wc = lds.wc;
   uint32_t& s_maxlast = lds.maxlast;
   int tx, ty;
-  if (!block_tile((int)blockIdx.x, gx, grid_dim(H), tx, ty)) return;
-  const int tile = ty * gx + tx;
+  const int gy = grid_dim(H);
+  if (!block_tile((int)blockIdx.x, gx, gy, tx, ty)) return;
+  // camera blockIdx.y of a batch (tiles and images after the earlier ones')
+  const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
   const bool inside = px < W && py < H;
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   float T = 1.0f, g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
   uint32_t last = 0;
   if (inside) {
-    const int64_t p = (int64_t)py * W + px;
+    const int64_t p = ((int64_t)blockIdx.y * H + py) * W + px;
     T = final_T[p];
     last = last_idx[p];
     g0 = dL_dimage[3 * p + 0];
@@ -398,7 +400,6 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   // nothing at or after `stop` is blended; last indices beyond the tile's
   // list (inputs that do not belong together) give the tile zero gradients
   const uint32_t stop = (s_maxlast > end - start) ? start : start + s_maxlast;
-  const int gy = grid_dim(H);
   uint32_t n_eval = 0, n_hit = 0, n_red = 0;  // counters (kStats only)
 
   // entries no pixel of the tile blends: their instance slots get zeros
@@ -672,7 +673,10 @@ extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
   return hipGetLastError();
 }
 
-extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, const uint32_t* ranges,
+// ncams > 1: a batch (N = ncams * ld rows, ranges over ncams * T tiles,
+// images [c][H][W]).
+extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
+                                           const uint32_t* ranges,
                                            const uint32_t* ids, const float* splats,
                                            const uint32_t* offsets, const uint32_t* tiles,
                                            const float* bg, const gs::Settings& st,
@@ -682,7 +686,7 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, cons
                                            const uint32_t* vis_ids, int64_t num_visible,
                                            uint64_t* counters, hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
-  const dim3 grid(gs::tile_grid_blocks(gx, gy)), block(256);
+  const dim3 grid(gs::tile_grid_blocks(gx, gy), (unsigned)ncams), block(256);
   const float4* sp = (const float4*)splats;
   float4* part = (float4*)partials;
 #define GS_RBWD(STATS, ABS)                                                                 \

@@ -31,7 +31,7 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_l1_dssim_loss_grad", "gs_default_adam_config", "gs_adam_step",
             "gs_adam_step_packed", "gs_project_fwd_batched",
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
-            "gs_rasterize_fwd_batched")
+            "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched")
 
 
 class GsError(RuntimeError):
@@ -121,6 +121,12 @@ def load():
                                             P, C.c_size_t, P]
     lib.gs_rasterize_fwd_batched.restype = C.c_int
     lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 13
+    lib.gs_rasterize_bwd_batched.restype = C.c_int
+    lib.gs_rasterize_bwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 5 + [u64] + [P] * 6 + \
+        [u64, P, i32, P, P]
+    lib.gs_project_bwd_batched.restype = C.c_int
+    lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 2 + \
+        [P] * 5 + [i32, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -328,6 +334,32 @@ def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, spla
                                         _p(splats), _p(depths), bg, C.byref(settings),
                                         _p(image), _p(final_T), _p(last_idx), _p(out_depth),
                                         _p(out_alpha), _p(counters), _stream(stream)))
+
+
+def gs_rasterize_bwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, offsets,
+                             tiles_touched, num_instances, background, settings, final_T,
+                             last_idx, dL_dimage, partials, partials_capacity, grads2d,
+                             absgrad=0, counters=None, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_bwd_batched(num_cams, ld, width, height, _p(tile_ranges), _p(ids),
+                                        _p(splats), _p(offsets), _p(tiles_touched),
+                                        int(num_instances), bg, C.byref(settings), _p(final_T),
+                                        _p(last_idx), _p(dL_dimage), _p(partials),
+                                        int(partials_capacity), _p(grads2d), int(absgrad),
+                                        _p(counters), _stream(stream)))
+
+
+def gs_project_bwd_batched(cams, N, ld, sh_degree, means, scales, quats, sh, settings, radii,
+                           grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
+                           accumulate=0, stream=None):
+    lib = load()
+    arr = (gs_camera * len(cams))(*cams)
+    _check(lib.gs_project_bwd_batched(len(cams), arr, N, ld, sh_degree, _p(means), _p(scales),
+                                      _p(quats), _p(sh), C.byref(settings), _p(radii),
+                                      _p(grads2d), _p(dL_dmeans), _p(dL_dscales),
+                                      _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
+                                      int(accumulate), _stream(stream)))
 
 
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
@@ -627,6 +659,14 @@ class BatchFrame:
         self.out_alpha = z((C_, height, width), f32) if with_depth_alpha else None
         self.m_host = torch.zeros((1,), dtype=torch.int64, pin_memory=True)
         self.M = 0
+        # backward: per-camera images and 2D records, gradients summed over
+        # the batch's cameras
+        K = (sh_degree + 1) ** 2
+        self.dL_dimage = z((C_, height, width, 3), f32)
+        self.grads2d = z((max(C_ * ld_, 1), 16), f32)
+        self.g_means, self.g_scales = z((3, ld_), f32), z((3, ld_), f32)
+        self.g_quats, self.g_opacities = z((4, ld_), f32), z((ld_,), f32)
+        self.g_sh = z((3 * K, ld_), f32)
         self._alloc_sort(capacity if capacity else max(1024, 4 * C_ * ld_))
 
     def _alloc_sort(self, capacity):
@@ -634,6 +674,7 @@ class BatchFrame:
         self.capacity = int(capacity)
         self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
         self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
+        self.partials = torch.empty((self.capacity, 16), dtype=torch.float32, device=self.device)
         self.ws_bytes = gs_bin_and_sort_batched_workspace_size(self.C, self.ld, self.capacity,
                                                                self.W, self.H)
         self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8,
@@ -661,3 +702,16 @@ class BatchFrame:
                                  self.image, self.final_T, self.last_idx, self.out_depth,
                                  self.out_alpha)
         return self.image
+
+    def backward(self, g: "Gaussians", dL_dimage=None, accumulate=0, absgrad=False):
+        """Compositing backward of every camera, then the projection backward
+        summed over the cameras into g_means ... g_sh."""
+        dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        gs_rasterize_bwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
+                                 self.splats, self.offsets, self.tiles, self.M, self.background,
+                                 self.settings, self.final_T, self.last_idx, dl, self.partials,
+                                 self.capacity, self.grads2d, int(bool(absgrad)))
+        gs_project_bwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
+                               g.sh, self.settings, self.radii, self.grads2d, self.g_means,
+                               self.g_scales, self.g_quats, self.g_opacities, self.g_sh,
+                               accumulate)

@@ -283,6 +283,35 @@ GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t 
                                           float* final_T, uint32_t* last_idx, float* out_depth,
                                           float* out_alpha, uint64_t* counters, void* stream);
 
+/* gs_rasterize_bwd_batched: gs_rasterize_bwd for every camera of a batch
+ * (final_T, last_idx [c][H][W], dL_dimage [c][H][W][3]); grads2d receives
+ * the 2D gradient record of every row c * ld + i [num_cams * ld][16]
+ * (visible rows only). */
+GS_API gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width,
+                                          int32_t height, const uint32_t* tile_ranges,
+                                          const uint32_t* ids, const float* splats,
+                                          const uint32_t* offsets, const uint32_t* tiles_touched,
+                                          uint64_t num_instances, const float* background,
+                                          const gs_settings* settings, const float* final_T,
+                                          const uint32_t* last_idx, const float* dL_dimage,
+                                          float* partials, uint64_t partials_capacity,
+                                          float* grads2d, int32_t absgrad, uint64_t* counters,
+                                          void* stream);
+
+/* gs_project_bwd_batched: gs_project_bwd summed over the cameras of a batch
+ * (radii [c][ld], grads2d [c * ld + i]): each Gaussian's parameters are read
+ * once and the cameras that see it add their chain-rule terms in camera
+ * order, as num_cams single-camera calls with accumulate would.
+ * accumulate = 0: Gaussians no camera sees get zeros. */
+GS_API gs_status gs_project_bwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N,
+                                        int64_t ld, int32_t sh_degree, const float* means,
+                                        const float* scales, const float* quats,
+                                        const float* sh, const gs_settings* settings,
+                                        const int32_t* radii, const float* grads2d,
+                                        float* dL_dmeans, float* dL_dscales, float* dL_dquats,
+                                        float* dL_dopacities, float* dL_dsh, int32_t accumulate,
+                                        void* stream);
+
 /* Packed mode (the gsplat guide §4.1 trains with its packed and sparse
  * gradient switches on: only the Gaussians that reach the image take part
  * after the projection, and only they receive gradients).  The visible set

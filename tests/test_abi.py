@@ -260,6 +260,18 @@ def test_batched_calls_reject_bad_arguments(lib):
     r = lib.gs_rasterize_fwd_batched(2, 10, 64, 64, None, dummy, dummy, None, bg, C.byref(st),
                                      dummy, dummy, dummy, None, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # no tile ranges
+    r = lib.gs_rasterize_bwd_batched(9, 10, 64, 64, *([dummy] * 5), 10, bg, C.byref(st),
+                                     dummy, dummy, dummy, dummy, 10, dummy, 0, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # too many cameras
+    r = lib.gs_rasterize_bwd_batched(2, 10, 64, 64, *([dummy] * 5), 11, bg, C.byref(st),
+                                     dummy, dummy, dummy, dummy, 10, dummy, 0, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # partials too small
+    r = lib.gs_project_bwd_batched(2, cams, 10, 10, 0, *([dummy] * 4), C.byref(st), dummy,
+                                   dummy, *([dummy] * 5), 2, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # accumulate 0/1
+    r = lib.gs_project_bwd_batched(0, cams, 10, 10, 0, *([dummy] * 4), C.byref(st), dummy,
+                                   dummy, *([dummy] * 5), 0, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT
 
 
 def test_densify_rejects_bad_arguments(lib):

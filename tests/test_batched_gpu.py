@@ -110,3 +110,50 @@ def test_batch_cluster_3m_4k_four_poses():
     """The 3M-Gaussian 3840 x 2160 workload's batch of four poses."""
     scene, cams, _ = scenes.make_config("cluster_3m_4k")
     _check_batch("cluster_3m_4k", scene, cams)
+
+
+def _check_backward(name, scene, cams, ld=None):
+    """Batched backward against single-camera calls with accumulate (camera 0
+    overwrites, the next ones add): the 2D records of every camera and the
+    summed 3D gradients, bit for bit."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    g, bf = _batch(scene, cams, ld)
+    N, L, C = scene.n, g.ld, len(cams)
+    tgt = torch.from_numpy(np.stack([scenes.target_image(c, k) for k, c in enumerate(cams)])).cuda()
+    raster.gs_image_loss_grad(1, tgt.numel(), bf.image, tgt, bf.dL_dimage, None)
+    bf.backward(g)
+    torch.cuda.synchronize()
+    fr = raster.Frame(g.ld, scene.sh_degree, cams[0].width, cams[0].height)
+    for c, cam in enumerate(cams):
+        fr.forward(g, cam)
+        fr.loss_grad(tgt[c], 1, with_loss=False)
+        fr.backward(g, accumulate=int(c > 0))
+        torch.cuda.synchronize()
+        assert_bits_equal(bf.dL_dimage[c].cpu().numpy(), fr.dL_dimage.cpu().numpy(), "dL/dimage")
+        vis = fr.radii[:N].cpu().numpy() > 0
+        assert_bits_equal(bf.grads2d[c * L:c * L + N].cpu().numpy()[vis],
+                          fr.grads2d[:N].cpu().numpy()[vis], "records cam %d" % c)
+    for k in ("g_means", "g_scales", "g_quats", "g_opacities", "g_sh"):
+        a, b = getattr(bf, k), getattr(fr, k)
+        a = a[..., :N].cpu().numpy()
+        b = b[..., :N].cpu().numpy()
+        assert_bits_equal(a, b, k)
+    print("[batch] %s backward: %d cameras, M=%d" % (name, C, bf.M), flush=True)
+
+
+def test_batch_backward_cluster_200k():
+    scene = scenes.cluster_scene(n=200_000, seed=13)
+    cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
+    _check_backward("cluster_200k_640x416", scene, cams)
+
+
+def test_batch_backward_ragged_padded():
+    s, cam = scenes.box_scene(n=20000, seed=12, width=500, height=270, fx=290.0)
+    cam2 = scenes.look_at_camera(np.array([3.0, 2.0, -7.0]), 500, 270, 290.0)
+    _check_backward("box_20k_ragged", s, [cam, cam2, cam], ld=20011)
+
+
+def test_batch_backward_cluster_1m_1080p_four_poses():
+    scene, cams, _ = scenes.make_config("cluster_1m_1080p")
+    _check_backward("cluster_1m_1080p", scene, cams[:4])
