@@ -166,6 +166,11 @@ def densify_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def scenes_target(cam, k):
+    from differentiable_rasterization_amd import scenes
+    return scenes.target_image(cam, k)
+
+
 def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
     """Forward only, the poses in groups of ``batch``: each pose through the
     single-camera calls, then each group through the batched calls (one
@@ -189,8 +194,24 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
         for grp in groups:
             bf.forward(g, grp)
 
+    # forward + backward of a group: the L1 loss gradient over the group's
+    # images, the batched compositing backward, and the projection backward
+    # summed over the group's cameras
+    tg = [torch.from_numpy(np.stack([scenes_target(c, k) for k, c in
+                                     enumerate(cams[i:i + batch])])).cuda()
+          for i in range(0, len(cams) - batch + 1, batch)]
+
+    def batched_fb():
+        for grp, t in zip(groups, tg):
+            bf.forward(g, grp)
+            raster.gs_image_loss_grad(1, t.numel(), bf.image, t, bf.dL_dimage, None)
+            bf.backward(g)
+
     out = {}
-    for name, fn in (("single", single), ("batched", batched)):
+    fns = [("single", single), ("batched", batched)]
+    if not depth_alpha:
+        fns.append(("batched_fb", batched_fb))
+    for name, fn in fns:
         fn()  # warm-up (also sizes the sort buffers)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -198,11 +219,14 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
             fn()
         torch.cuda.synchronize()
         out[name] = reps * len(groups) * batch / (time.perf_counter() - t0)
-    return {"batch": batch, "frames": reps * len(groups) * batch,
-            "fwd_fps_single_calls": round(out["single"], 2),
-            "fwd_fps_batched_calls": round(out["batched"], 2),
-            "speedup": round(out["batched"] / out["single"], 3),
-            "depth_alpha": bool(depth_alpha)}
+    r = {"batch": batch, "frames": reps * len(groups) * batch,
+         "fwd_fps_single_calls": round(out["single"], 2),
+         "fwd_fps_batched_calls": round(out["batched"], 2),
+         "speedup": round(out["batched"] / out["single"], 3),
+         "depth_alpha": bool(depth_alpha)}
+    if "batched_fb" in out:
+        r["fwdbwd_fps_batched_calls"] = round(out["batched_fb"], 2)
+    return r
 
 
 def train_step_bench(args, scene, gcams, targets, capacity):
