@@ -62,15 +62,17 @@ __device__ inline uint64_t wave_incl_scan_u64(uint64_t x) {
   return x;
 }
 
-// Exclusive scan of one value per thread; returns the block total.
+// Exclusive scan of one value per thread of an NW-wave workgroup; returns
+// the block total.
+template <int NW = 4>
 __device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
-  __shared__ uint64_t s_w[4];
+  __shared__ uint64_t s_w[NW];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t inc = wave_incl_scan_u64(x);
   if (lane == 63) s_w[w] = inc;
   __syncthreads();
   uint64_t off = 0, tot = 0;
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < NW; ++k) {
     if (k < w) off += s_w[k];
     tot += s_w[k];
   }
@@ -217,7 +219,10 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 16;
-constexpr int kPart = 256 * kSortItems;  // keys per partition
+constexpr int kSortWaves = 8;  // 512-lane workgroups of 8192 keys: half as many
+                               // partitions per pass
+constexpr int kSortThreads = 64 * kSortWaves;
+constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
 constexpr int kMaxPasses = 8;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagPrefix = 2u << 30;
@@ -257,21 +262,21 @@ __device__ inline uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-__global__ __launch_bounds__(256) void sort_pass_kernel(
+__global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
     uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, uint32_t M, int shift,
     const uint32_t* __restrict__ digit_offsets, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket) {
   __shared__ uint64_t s_keys[kPart];
   __shared__ uint32_t s_vals[kPart];
-  __shared__ uint32_t s_wh[4][kRadix];  // per-wave digit counts, later wave offsets
+  __shared__ uint32_t s_wh[kSortWaves][kRadix];  // per-wave digit counts, later wave offsets
   __shared__ uint32_t s_start[kRadix];  // block-local exclusive digit start
   __shared__ uint32_t s_gbase[kRadix];  // global base minus local start
   __shared__ uint32_t s_part;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_part = atomicAdd(ticket, 1u);
-  for (int k = tid; k < 4 * kRadix; k += 256) (&s_wh[0][0])[k] = 0;
+  for (int k = tid; k < kSortWaves * kRadix; k += kSortThreads) (&s_wh[0][0])[k] = 0;
   __syncthreads();
   const uint32_t part = s_part;
   const uint32_t base = part * (uint32_t)kPart;
@@ -307,24 +312,30 @@ __global__ __launch_bounds__(256) void sort_pass_kernel(
   }
   __syncthreads();
 
-  // per digit (thread = digit): wave offsets, block count, block-local start
-  const uint32_t d = (uint32_t)tid;
+  // per digit (thread = digit, the first 256 lanes): wave offsets, block
+  // count, block-local start
+  const bool dl = tid < kRadix;
+  const uint32_t d = dl ? (uint32_t)tid : 0u;
   uint32_t cnt = 0;
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t c = s_wh[w][d];
-    s_wh[w][d] = cnt;
-    cnt += c;
+  if (dl) {
+    for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = s_wh[w][d];
+      s_wh[w][d] = cnt;
+      cnt += c;
+    }
   }
   uint64_t excl64;
-  block_excl_scan_u64(cnt, excl64);
-  s_start[d] = (uint32_t)excl64;
+  block_excl_scan_u64<kSortWaves>(cnt, excl64);
+  if (dl) s_start[d] = (uint32_t)excl64;
   const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in digit 255
   const uint32_t mine = (d == kRadix - 1) ? cnt - pad : cnt;
 
   // decoupled look-back over earlier partitions, one lane per digit
   uint32_t* st = status + (size_t)part * kRadix;
   uint32_t prefix = 0;
-  if (part == 0) {
+  if (!dl) {
+    // lanes past the digits take no part
+  } else if (part == 0) {
     __hip_atomic_store(&st[d], kFlagPrefix | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     __hip_atomic_store(&st[d], kFlagAgg | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(256) void sort_pass_kernel(
     __hip_atomic_store(&st[d], kFlagPrefix | (prefix + mine), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  s_gbase[d] = digit_offsets[d] + prefix - s_start[d];
+  if (dl) s_gbase[d] = digit_offsets[d] + prefix - s_start[d];
   __syncthreads();
 
   // scatter into LDS in local sorted order
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(256) void sort_pass_kernel(
   }
   __syncthreads();
   // write out in local order: consecutive lanes hit consecutive slots of a digit run
-  for (uint32_t j = (uint32_t)tid; j < nvalid; j += 256u) {
+  for (uint32_t j = (uint32_t)tid; j < nvalid; j += (uint32_t)kSortThreads) {
     const uint64_t key = s_keys[j];
     const uint32_t dd = (uint32_t)(key >> shift) & (kRadix - 1);
     const uint32_t out = s_gbase[dd] + j;
@@ -545,7 +556,7 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(256), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < sp.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(256), 0, s, ka, ia, kb, ib, M32,
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib, M32,
                        p * kRadixBits, w.hist + p * kRadix,
                        w.status + (size_t)p * sp.parts * kRadix, w.ticket + p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -641,7 +652,7 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(256), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < w.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(256), 0, s, ka, ia, kb, ib, n32,
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib, n32,
                        p * kRadixBits, w.hist + p * kRadix,
                        w.status + (size_t)p * w.parts * kRadix, w.ticket + p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
