@@ -12,7 +12,7 @@
 //     computes every digit's global histogram, then each digit pass reads and
 //     writes the keys once.  A workgroup takes its partition from an atomic
 //     ticket (so it only ever waits on partitions already running), ranks
-//     its 4096 keys stably with wave64 ballots into LDS histograms, publishes
+//     its 8192 keys stably with wave64 ballots into LDS histograms, publishes
 //     per-digit counts and resolves its global offsets by decoupled
 //     look-back, then scatters through LDS so that global writes come out
 //     in digit runs.  Only the low 32 + ceil(log2 T) key bits are sorted.
