@@ -31,8 +31,8 @@ hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, u
 hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                      const int32_t* radii, const float* depths,
                                      const uint32_t* tiles, const uint32_t* offsets, int32_t W,
-                                     int32_t H, int ncams, uint64_t M, uint64_t* keys,
-                                     uint32_t* ids,
+                                     int32_t H, int ncams, uint64_t M, bool device_count,
+                                     uint64_t* counts, uint64_t* keys, uint32_t* ids,
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
 hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
@@ -228,9 +228,40 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, keys, ids, tile_ranges,
+                                              offsets, width, height, 1, M, false, nullptr, keys, ids,
+                                              tile_ranges,
                                               workspace, capacity, s),
                     "gs_bin_and_sort");
+}
+
+gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
+                                 const int32_t* radii, const float* depths,
+                                 const uint32_t* tiles_touched, int32_t width, int32_t height,
+                                 uint32_t* offsets, uint64_t capacity, uint64_t* counts,
+                                 uint64_t* keys, uint32_t* ids, uint32_t* tile_ranges,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(counts != nullptr, "counts is NULL");
+  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+  GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
+  if (N > 0)
+    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets, "NULL array pointer");
+  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
+  const int32_t T = gs_num_tiles(width, height);
+  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
+             "workspace smaller than gs_bin_and_sort_workspace_size()");
+  hipStream_t s = (hipStream_t)stream;
+  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace,
+                                           capacity, T, nullptr, s),
+                            "gs_bin_and_sort_device(scan)");
+  if (st != GS_OK) return st;
+  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
+                                              offsets, width, height, 1, 0, true, counts, keys,
+                                              ids, tile_ranges, workspace, capacity, s),
+                    "gs_bin_and_sort_device");
 }
 
 gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
@@ -348,7 +379,8 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, keys, ids, tile_ranges,
+                                              offsets, width, height, 1, M, false, nullptr, keys, ids,
+                                              tile_ranges,
                                               workspace, capacity, s),
                     "gs_bin_and_sort_packed");
 }
@@ -503,7 +535,7 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(rows, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, num_cams, M, keys, ids,
+                                              offsets, width, height, num_cams, M, false, nullptr, keys, ids,
                                               tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_batched");
 }

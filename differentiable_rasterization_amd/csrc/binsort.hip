@@ -171,7 +171,8 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     int64_t N, const float* __restrict__ means2d, int64_t ld, const int32_t* __restrict__ radii,
     const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
     const uint32_t* __restrict__ offsets, int gx, int gy, bool batched,
-    uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
+    const uint32_t* __restrict__ meff, uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
+  if (*meff == 0u) return;  // no instances, or more than the buffers hold
   __shared__ uint32_t s_off[257];
   __shared__ int32_t s_x0[256], s_w[256], s_y0[256];
   __shared__ uint32_t s_db[256], s_tb[256];
@@ -231,8 +232,10 @@ constexpr int kLookback = 8;  // partitions examined per look-back step
 
 // Global histogram of every pass's digit (one LDS histogram per pass).
 __global__ __launch_bounds__(256) void sort_histogram_kernel(const uint64_t* __restrict__ keys,
-                                                             uint32_t M, int passes,
+                                                             const uint32_t* __restrict__ meff,
+                                                             int passes,
                                                              uint32_t* __restrict__ hist) {
+  const uint32_t M = *meff;
   __shared__ uint32_t s_h[kMaxPasses][kRadix];
   for (int k = threadIdx.x; k < kMaxPasses * kRadix; k += 256) (&s_h[0][0])[k] = 0;
   __syncthreads();
@@ -264,9 +267,10 @@ __device__ inline uint64_t lanemask_lt() {
 
 __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
-    uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, uint32_t M, int shift,
-    const uint32_t* __restrict__ digit_offsets, uint32_t* __restrict__ status,
+    uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, const uint32_t* __restrict__ meff,
+    int shift, const uint32_t* __restrict__ digit_offsets, uint32_t* __restrict__ status,
     uint32_t* __restrict__ ticket) {
+  const uint32_t M = *meff;
   __shared__ uint64_t s_keys[kPart];
   __shared__ uint32_t s_vals[kPart];
   __shared__ uint32_t s_wh[kSortWaves][kRadix];  // per-wave digit counts, later wave offsets
@@ -279,6 +283,9 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   for (int k = tid; k < kSortWaves * kRadix; k += kSortThreads) (&s_wh[0][0])[k] = 0;
   __syncthreads();
   const uint32_t part = s_part;
+  // a grid sized for the buffers' capacity: workgroups past the last
+  // partition leave (nothing waits on a later partition)
+  if ((uint64_t)part * (uint64_t)kPart >= (uint64_t)M) return;
   const uint32_t base = part * (uint32_t)kPart;
   const uint32_t nvalid = (M - base) < (uint32_t)kPart ? (M - base) : (uint32_t)kPart;
 
@@ -397,14 +404,30 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
 // ---------------------------------------------------------------------------
 // Stage 3c: per-tile [start, end) ranges of the sorted keys
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void ranges_kernel(const uint64_t* __restrict__ keys, uint32_t M,
-                                                     uint32_t T, uint32_t* __restrict__ ranges) {
+__global__ __launch_bounds__(256) void ranges_kernel(const uint64_t* __restrict__ keys,
+                                                     const uint32_t* __restrict__ meff, uint32_t T,
+                                                     uint32_t* __restrict__ ranges) {
+  const uint32_t M = *meff;
   const uint32_t m = blockIdx.x * 256u + threadIdx.x;
   if (m >= M) return;
   const uint32_t tile = (uint32_t)(keys[m] >> 32);
   if (tile >= T) return;
   if (m == 0 || (uint32_t)(keys[m - 1] >> 32) != tile) ranges[2 * tile] = m;
   if (m == M - 1 || (uint32_t)(keys[m + 1] >> 32) != tile) ranges[2 * tile + 1] = m + 1;
+}
+
+// The instance count the binning kernels use: M when it fits the buffers,
+// else 0 (an empty list).  counts (device, optional) receives M and the
+// overflow flag.
+__global__ void bin_count_kernel(const uint64_t* __restrict__ total, uint64_t capacity,
+                                 uint32_t* __restrict__ meff, uint64_t* __restrict__ counts) {
+  const uint64_t M = *total;
+  const bool over = M > capacity;
+  *meff = over ? 0u : (uint32_t)M;
+  if (counts) {
+    counts[0] = M;
+    counts[1] = over ? 1ull : 0ull;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -436,6 +459,7 @@ struct Workspace {
   uint32_t* ids_alt;
   uint64_t* scan_sums;
   uint64_t* total;
+  uint32_t* meff;    // [1] instance count used by the binning kernels
   uint32_t* hist;    // [passes][256]
   uint32_t* ticket;  // [passes]
   uint32_t* status;  // [passes][parts][256]
@@ -457,6 +481,7 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
   w.ids_alt = (uint32_t*)take(sizeof(uint32_t) * (capacity ? capacity : 1));
   w.scan_sums = (uint64_t*)take(sizeof(uint64_t) * 2 * (nb ? nb : 1));
   w.total = (uint64_t*)take(sizeof(uint64_t) * 2);
+  w.meff = (uint32_t*)take(sizeof(uint32_t));
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
   w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
   w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
@@ -481,9 +506,15 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
   hipError_t e;
   const bool vis = vis_ids != nullptr;
   if (N == 0) {
-    totals_host[0] = 0;
-    if (vis) totals_host[1] = 0;
-    return hipSuccess;
+    if (totals_host) {
+      totals_host[0] = 0;
+      if (vis) totals_host[1] = 0;
+      return hipSuccess;
+    }
+    // the device count must still read 0
+    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, w.scan_sums, (int64_t)0,
+                       w.total);
+    return hipGetLastError();
   }
   const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
   if (vis)
@@ -503,6 +534,7 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
     hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
                        w.scan_sums, offsets, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!totals_host) return hipSuccess;  // the count stays on the device
   // straight into the caller's host words: page-locked memory there makes
   // this a direct transfer instead of a staged one
   if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
@@ -513,10 +545,15 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
 
 // Duplicate, sort and extract ranges for M instances (M <= capacity).
 // ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
+// M: the instance count read back by the caller, or, with device_count,
+// unknown on the host: the kernels then take it from the scan on the device,
+// grids are sized for `capacity`, and counts (device, optional) receives M
+// and an overflow flag (M > capacity leaves an empty list).
 extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                                 const int32_t* radii, const float* depths,
                                                 const uint32_t* tiles, const uint32_t* offsets,
                                                 int32_t W, int32_t H, int ncams, uint64_t M,
+                                                bool device_count, uint64_t* counts,
                                                 uint64_t* keys, uint32_t* ids, uint32_t* ranges,
                                                 void* workspace, uint64_t capacity, hipStream_t s) {
   using namespace gs;
@@ -524,8 +561,10 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   const int32_t T = gx * gy * ncams;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
-  if (M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
-  const SortPlan sp = sort_plan(M, T);
+  if (!device_count && M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
+  // grids for M, or for the largest count the buffers hold
+  const uint64_t Mg = device_count ? capacity : M;
+  const SortPlan sp = sort_plan(Mg, T);
   {
     Segs sg = {{ranges, w.hist, w.ticket, w.status},
                {2 * (int64_t)T, (int64_t)kMaxPasses * kRadix, kMaxPasses,
@@ -536,6 +575,10 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
     hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(bin_count_kernel, dim3(1), dim3(1), 0, s, w.total, capacity, w.meff,
+                     device_count ? counts : nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (Mg == 0) return hipSuccess;
   // land the final pass in (keys, ids): start from the alternate buffer when
   // the pass count is odd
   uint64_t* ka = (sp.passes & 1) ? w.keys_alt : keys;
@@ -544,27 +587,27 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
   const int64_t nblk = (N + 255) / 256;
   hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
-                     depths, tiles, offsets, gx, gy, ncams > 1, ka, ia);
+                     depths, tiles, offsets, gx, gy, ncams > 1, w.meff, ka, ia);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const uint32_t M32 = (uint32_t)M;
-  unsigned hblocks = (unsigned)((M + 256 * 16 - 1) / (256 * 16));
+  unsigned hblocks = (unsigned)((Mg + 256 * 16 - 1) / (256 * 16));
   if (hblocks > 1024) hblocks = 1024;
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, M32, sp.passes,
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, sp.passes,
                      w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(256), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < sp.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib, M32,
-                       p * kRadixBits, w.hist + p * kRadix,
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
+                       w.meff, p * kRadixBits, w.hist + p * kRadix,
                        w.status + (size_t)p * sp.parts * kRadix, w.ticket + p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint64_t* tk = ka; ka = kb; kb = tk;
     uint32_t* ti = ia; ia = ib; ib = ti;
   }
-  const unsigned rblocks = (unsigned)((M + 255) / 256);
-  hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, M32, (uint32_t)T, ranges);
+  const unsigned rblocks = (unsigned)((Mg + 255) / 256);
+  hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, w.meff, (uint32_t)T,
+                     ranges);
   return hipGetLastError();
 }
 
@@ -577,6 +620,7 @@ namespace gs {
 struct PairSortWs {
   uint64_t* keys_alt;
   uint32_t* vals_alt;
+  uint32_t* meff;
   uint32_t* hist;
   uint32_t* ticket;
   uint32_t* status;
@@ -598,6 +642,7 @@ static PairSortWs carve_pairsort(void* base, uint64_t n, int bits) {
   };
   w.keys_alt = (uint64_t*)take(sizeof(uint64_t) * (n ? n : 1));
   w.vals_alt = (uint32_t*)take(sizeof(uint32_t) * (n ? n : 1));
+  w.meff = (uint32_t*)take(sizeof(uint32_t));
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
   w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
   w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.passes * (w.parts ? w.parts : 1) * kRadix);
@@ -643,17 +688,17 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
       return e;
     ka = w.keys_alt; ia = w.vals_alt; kb = keys; ib = vals;
   }
-  const uint32_t n32 = (uint32_t)n;
+  if ((e = fill_u32(w.meff, 1, (uint32_t)n, s)) != hipSuccess) return e;
   unsigned hblocks = (unsigned)((n + 256 * 16 - 1) / (256 * 16));
   if (hblocks > 1024) hblocks = 1024;
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, n32, w.passes,
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, w.passes,
                      w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(256), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < w.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib, n32,
-                       p * kRadixBits, w.hist + p * kRadix,
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
+                       w.meff, p * kRadixBits, w.hist + p * kRadix,
                        w.status + (size_t)p * w.parts * kRadix, w.ticket + p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint64_t* tk = ka; ka = kb; kb = tk;

@@ -537,10 +537,12 @@ __device__ inline void store_rec(float4* __restrict__ r, const float a[kFieldsAb
 
 // Row r of grads2d sums the slots of Gaussian r, or of Gaussian vis_ids[r]
 // in the packed form (kPacked), where the rows follow that list.
+// Slots past `capacity` (a binning that overflowed its buffers and left an
+// empty list) are never read: such a Gaussian gets a zero record.
 template <bool kPacked>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(
     int64_t N, const uint32_t* __restrict__ vis_ids, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ tiles, const float4* __restrict__ partials,
+    const uint32_t* __restrict__ tiles, const float4* __restrict__ partials, uint64_t capacity,
     float4* __restrict__ grads2d) {
   __shared__ uint32_t s_big[256];
   __shared__ uint32_t s_nbig;
@@ -552,12 +554,14 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
   if (r < N) {
     const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
     const uint32_t cnt = tiles[i];
-    if (cnt > kSmallSeg) {
+    const bool fits = cnt == 0 || (uint64_t)offsets[i] + cnt <= capacity;
+    if (cnt > kSmallSeg && fits) {
       s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)t;
     } else if (cnt > 0) {
       float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
       const uint64_t base = offsets[i];
-      for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
+      if (fits)
+        for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
       store_rec(grads2d + 4 * r, a);
     }
   }
@@ -706,10 +710,10 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int 
   const dim3 rgrid((unsigned)((rows + 255) / 256));
   if (vis_ids)
     hipLaunchKernelGGL(gs::reduce_partials_kernel<true>, rgrid, dim3(256), 0, s, rows, vis_ids,
-                       offsets, tiles, part, (float4*)grads2d);
+                       offsets, tiles, part, capacity, (float4*)grads2d);
   else
     hipLaunchKernelGGL(gs::reduce_partials_kernel<false>, rgrid, dim3(256), 0, s, rows, nullptr,
-                       offsets, tiles, part, (float4*)grads2d);
+                       offsets, tiles, part, capacity, (float4*)grads2d);
   return hipGetLastError();
 }
 

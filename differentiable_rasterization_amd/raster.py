@@ -31,7 +31,8 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_l1_dssim_loss_grad", "gs_default_adam_config", "gs_adam_step",
             "gs_adam_step_packed", "gs_project_fwd_batched",
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
-            "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched")
+            "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
+            "gs_bin_and_sort_device")
 
 
 class GsError(RuntimeError):
@@ -127,6 +128,9 @@ def load():
     lib.gs_project_bwd_batched.restype = C.c_int
     lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 2 + \
         [P] * 5 + [i32, P]
+    lib.gs_bin_and_sort_device.restype = C.c_int
+    lib.gs_bin_and_sort_device.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
+                                           C.c_size_t, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -362,6 +366,18 @@ def gs_project_bwd_batched(cams, N, ld, sh_degree, means, scales, quats, sh, set
                                       int(accumulate), _stream(stream)))
 
 
+def gs_bin_and_sort_device(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                           capacity, counts, keys, ids, tile_ranges, workspace, workspace_bytes,
+                           stream=None):
+    """No read-back: ``counts`` (device int64[2]) receives M and the overflow
+    flag."""
+    lib = load()
+    _check(lib.gs_bin_and_sort_device(N, ld, _p(means2d), _p(radii), _p(depths),
+                                      _p(tiles_touched), width, height, _p(offsets), capacity,
+                                      _p(counts), _p(keys), _p(ids), _p(tile_ranges),
+                                      _p(workspace), workspace_bytes, _stream(stream)))
+
+
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
     lib = load()
     _check(lib.gs_image_loss_grad(int(kind), int(count), _p(image), _p(target), _p(dL_dimage),
@@ -493,11 +509,15 @@ class Frame:
     ``packed=True`` runs the packed calls: ``vis_ids[:V]`` lists the visible
     Gaussians, ``grads2d[:V]`` and columns ``[:, :V]`` of the gradient planes
     hold their rows in that order (leading dimension ``ld``), and nothing is
-    written for the others."""
+    written for the others.
+
+    ``device_count=True`` bins without the read-back (gs_bin_and_sort_device):
+    nothing in a frame waits for the GPU, so a frame can be captured into a
+    HIP graph; ``check_counts()`` reads M and the overflow flag afterwards."""
 
     def __init__(self, ld, sh_degree, width, height, capacity=None, settings=None,
                  background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda",
-                 packed=False):
+                 packed=False, device_count=False):
         import torch
         self.torch = torch
         self.device = device
@@ -532,6 +552,9 @@ class Frame:
         self.m_host = torch.zeros((2,), dtype=torch.int64, pin_memory=True)
         self.M = 0
         self.packed = bool(packed)
+        self.device_count = bool(device_count)
+        assert not (self.packed and self.device_count)
+        self.counts = z((2,), torch.int64)
         self.vis_ids = z((max(ld, 1),), u32) if packed else None
         self.V = 0
         self._alloc_sort(capacity if capacity else max(1024, 4 * ld))
@@ -567,9 +590,22 @@ class Frame:
         self.M, self.V = M, V
         return M
 
+    def check_counts(self):
+        """(M, overflowed) of the last device-count binning (synchronises)."""
+        c = self.counts.cpu().numpy()
+        return int(c[0]), bool(c[1])
+
     def bin_and_sort(self, g: Gaussians):
         if self.packed:
             return self._bin_and_sort_packed(g)
+        if self.device_count:
+            gs_bin_and_sort_device(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
+                                   self.W, self.H, self.offsets, self.capacity, self.counts,
+                                   self.keys, self.ids, self.ranges, self.ws, self.ws_bytes)
+            # the instance count stays on the device; the backward bounds its
+            # slots by the capacity
+            self.M = self.capacity
+            return None
         st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
                                 self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
                                 self.ranges, self.ws, self.ws_bytes, num_instances=self.m_host)

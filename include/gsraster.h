@@ -164,6 +164,23 @@ GS_API gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, co
                           uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* gs_bin_and_sort without the read-back: the instance count stays on the
+ * device, so the call never waits for the GPU and a whole frame can be
+ * captured into a HIP graph.  counts (DEVICE uint64[2]) receives M and an
+ * overflow flag: with M > capacity the flag is 1 and the list is left
+ * empty (every tile range (0, 0), so the compositing yields the
+ * background; the backward stays within its buffers but its gradients are
+ * not meaningful); the caller reads counts when convenient, grows the
+ * buffers and runs the frame again.  Otherwise as gs_bin_and_sort, with the same
+ * workspace size.  The kernels are sized for capacity, not M. */
+GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
+                                        const int32_t* radii, const float* depths,
+                                        const uint32_t* tiles_touched, int32_t width,
+                                        int32_t height, uint32_t* offsets, uint64_t capacity,
+                                        uint64_t* counts, uint64_t* keys, uint32_t* ids,
+                                        uint32_t* tile_ranges, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Stage 4 — front-to-back alpha compositing per 16x16 tile (gsplat guide
  * §2.1, its third, differentiable blending step).  Per pixel, over its
  * tile's sorted list: q, the conic's quadratic form at (px+0.5-u, py+0.5-v),
