@@ -229,6 +229,51 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
     return r
 
 
+def graph_bench(args, scene, gcams, targets, kind, capacity):
+    """The same fwd+bwd frames, each pose captured once into a HIP graph
+    (binning without the read-back) and replayed."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    g = raster.Gaussians.from_scene(scene)
+    W, H = gcams[0].width, gcams[0].height
+    Px = W * H
+    fr = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=capacity, device_count=True)
+
+    def frame(i):
+        fr.project(g, gcams[i])
+        fr.bin_and_sort(g)
+        fr.rasterize(g)
+        raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i], fr.dL_dimage, None)
+        fr.rasterize_backward(g)
+        fr.project_backward(g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(len(gcams)):
+            frame(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(len(gcams)):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            frame(i)
+        graphs.append(gr)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    over = any(fr.check_counts()[1] for _ in [0])
+    return {"value": round(args.steps / dt, 2), "ms_per_step": round(1e3 * dt / args.steps, 4),
+            "form": "fwd+bwd frame per pose as a HIP graph, binning without the read-back",
+            "overflow": bool(over)}
+
+
 def train_step_bench(args, scene, gcams, targets, capacity):
     """A whole training step as the gsplat guide 4.1 loop runs it: packed
     forward and backward, the mean-L1 + 0.2 D-SSIM loss gradient and the
@@ -455,6 +500,8 @@ def main():
                                                                    fr.capacity)
     batch_line = None if args.no_train_step else fwd_batch_bench(args, scene, cams, args.batch,
                                                                   depth_alpha=False)
+    graph_line = None if args.no_train_step else graph_bench(args, scene, gcams, targets, kind,
+                                                              fr.capacity)
     if not args.packed:
         # the same steps through the packed calls (visible list, sparse
         # gradient rows), reported beside the dense headline
@@ -540,6 +587,8 @@ def main():
         out["train_step"] = train_line
     if batch_line is not None:
         out["fwd_batch"] = batch_line
+    if graph_line is not None:
+        out["graph"] = graph_line
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
     print(json.dumps(out), flush=True)
