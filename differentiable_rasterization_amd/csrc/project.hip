@@ -416,6 +416,8 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   // fp64 chain, so that each lane keeps its whole working set in flight
   // (the kernel runs at two waves per SIMD)
   float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
+  // one camera: its 2D gradient record is loaded with the parameters
+  float4 s0 = make_float4(0, 0, 0, 0), s1 = s0, s2 = s0;
 #pragma unroll
   for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
   if (anyvis) {
@@ -426,15 +428,20 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
+    if (!kBatched) {
+      s0 = grads2d[4 * r + 0];
+      s1 = grads2d[4 * r + 1];
+      s2 = grads2d[4 * r + 2];
+    }
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
   }
   for (int c = 0; c < nc; ++c) {
   const Cam cam = cams.c[c];
   const bool vis = radii[(int64_t)c * ld + i] > 0;
-  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
-  if (vis) {
-    const int64_t rr = kBatched ? (int64_t)c * ld + r : r;
+  float4 r0 = s0, r1 = s1, r2 = s2;
+  if (kBatched && vis) {
+    const int64_t rr = (int64_t)c * ld + r;
     r0 = grads2d[4 * rr + 0];
     r1 = grads2d[4 * rr + 1];
     r2 = grads2d[4 * rr + 2];
