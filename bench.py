@@ -362,7 +362,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="cluster_1m_1080p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=4)
+    ap.add_argument("--cpu-frames", type=int, default=16)
     ap.add_argument("--densify", action="store_true",
                     help="time gs_densify_prune on the 6M-Gaussian scene instead")
     ap.add_argument("--absgrad", action="store_true",
