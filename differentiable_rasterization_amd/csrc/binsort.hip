@@ -8,7 +8,7 @@
 //   - duplication is balanced by output slot: a workgroup owns 256 Gaussians
 //     and writes all of their instances with consecutive, coalesced stores,
 //     so one Gaussian touching thousands of tiles does not serialise a lane;
-//   - the sort is a onesweep LSD radix sort with 8-bit digits: one pass
+//   - the sort is a onesweep LSD radix sort with 9-bit digits: one pass
 //     computes every digit's global histogram, then each digit pass reads and
 //     writes the keys once.  A workgroup takes its partition from an atomic
 //     ticket (so it only ever waits on partitions already running), ranks
@@ -217,13 +217,15 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 // ---------------------------------------------------------------------------
 // Stage 3b: onesweep radix sort
 // ---------------------------------------------------------------------------
-constexpr int kRadixBits = 8;
+constexpr int kRadixBits = 9;  // 45 key bits at 1080p: 5 passes
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 16;
 constexpr int kSortWaves = 8;  // 512-lane workgroups of 8192 keys: half as many
                                // partitions per pass
 constexpr int kSortThreads = 64 * kSortWaves;
 constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
+static_assert(kRadix <= kSortThreads, "a sort lane per digit");
+static_assert(kRadix % 64 == 0, "digits in whole wavefronts");
 constexpr int kMaxPasses = 8;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagPrefix = 2u << 30;
@@ -251,12 +253,12 @@ __global__ __launch_bounds__(256) void sort_histogram_kernel(const uint64_t* __r
   }
 }
 
-// hist[p][d] -> exclusive offsets, one workgroup per pass.
-__global__ __launch_bounds__(256) void sort_hist_scan_kernel(uint32_t* __restrict__ hist) {
+// hist[p][d] -> exclusive offsets, one workgroup per pass, a lane per digit.
+__global__ __launch_bounds__(kRadix) void sort_hist_scan_kernel(uint32_t* __restrict__ hist) {
   uint32_t* h = hist + blockIdx.x * kRadix;
   const uint64_t x = h[threadIdx.x];
   uint64_t excl;
-  block_excl_scan_u64(x, excl);
+  block_excl_scan_u64<kRadix / 64>(x, excl);
   h[threadIdx.x] = (uint32_t)excl;
 }
 
@@ -595,7 +597,7 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, sp.passes,
                      w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(256), 0, s, w.hist);
+  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(kRadix), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < sp.passes; ++p) {
     hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
@@ -694,7 +696,7 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, w.passes,
                      w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(256), 0, s, w.hist);
+  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(kRadix), 0, s, w.hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < w.passes; ++p) {
     hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
