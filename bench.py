@@ -422,7 +422,7 @@ def main():
     P = len(cams)
     T = fr.T
     Px = W * H
-    sort_passes = (32 + int(np.ceil(np.log2(max(T, 2)))) + 7) // 8
+    sort_passes = (32 + int(np.ceil(np.log2(max(T, 2)))) + 8) // 9  # 9-bit digits
     names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "loss_grad", "rasterize_bwd",
              "project_bwd"]
 
