@@ -62,9 +62,10 @@ def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P, packed=False):
         # means2d, conic, depth, colour planes plus the 64-byte splat record out
         "project_fwd": 20 * N + (132 + 12 * K) * V,
         "bin_and_sort": 8 * N + 20 * V + (28 + 24 * P) * M + 8 * T,
-        # id + the 48 used bytes of the splat record per instance; image out
-        "rasterize_fwd": 52 * M + 20 * Px,
-        "loss_grad": 24 * Px,
+        # id + the 48 used bytes of the splat record per instance; image,
+        # final T, last index out; the fused loss gradient: target in,
+        # dL/dimage out
+        "rasterize_fwd": 52 * M + 20 * Px + 24 * Px,
         # per instance walked: id, offset, 64-byte record, 48-byte partial
         # store; per instance past the tile's last blend: id, offset, 32
         # record bytes, zero store; final T, last index, dL/dimage in; then the
@@ -242,8 +243,7 @@ def graph_bench(args, scene, gcams, targets, kind, capacity):
     def frame(i):
         fr.project(g, gcams[i])
         fr.bin_and_sort(g)
-        fr.rasterize(g)
-        raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i], fr.dL_dimage, None)
+        fr.rasterize_loss(g, targets[i], kind)
         fr.rasterize_backward(g)
         fr.project_backward(g)
 
@@ -423,8 +423,7 @@ def main():
     T = fr.T
     Px = W * H
     sort_passes = (32 + int(np.ceil(np.log2(max(T, 2)))) + 8) // 9  # 9-bit digits
-    names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "loss_grad", "rasterize_bwd",
-             "project_bwd"]
+    names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "rasterize_bwd", "project_bwd"]
 
     def step(i, ev=None, fr=fr):
         c = gcams[i % P]
@@ -436,18 +435,16 @@ def main():
         fr.bin_and_sort(g)
         if ev is not None:
             ev[2].record()
-        fr.rasterize(g)
+        # compositing with the loss gradient fused in
+        fr.rasterize_loss(g, targets[i % P], kind)
         if ev is not None:
             ev[3].record()
-        raster.gs_image_loss_grad(kind, Px * 3, fr.image, targets[i % P], fr.dL_dimage, None)
-        if ev is not None:
-            ev[4].record()
         fr.rasterize_backward(g, absgrad=args.absgrad)
         if ev is not None:
-            ev[5].record()
+            ev[4].record()
         fr.project_backward(g)
         if ev is not None:
-            ev[6].record()
+            ev[5].record()
         return fr.M
 
     # workload statistics per pose (one untimed pass with the counting variants)
@@ -480,7 +477,7 @@ def main():
         for i in range(args.warmup):
             step(i, fr=frame)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
                for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()

@@ -36,12 +36,11 @@ hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
 hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
-                                const uint32_t* ids,
-                                const float* splats, const float* depths, const float* bg,
-                                const gs::Settings& st,
-                                float* image, float* final_T, uint32_t* last_idx,
-                                float* out_depth, float* out_alpha, uint64_t* counters,
-                                hipStream_t s);
+                                const uint32_t* ids, const float* splats, const float* depths,
+                                const float* bg, const gs::Settings& st, float* image,
+                                float* final_T, uint32_t* last_idx, float* out_depth,
+                                float* out_alpha, uint64_t* counters, int loss_kind,
+                                const float* target, float* dl, float* loss, hipStream_t s);
 hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
                                 const uint32_t* ranges,
                                 const uint32_t* ids, const float* splats, const uint32_t* offsets,
@@ -283,8 +282,37 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
   return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, ids, splats, depths,
                                          background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
-                                         out_depth, out_alpha, counters, (hipStream_t)stream),
+                                         out_depth, out_alpha, counters, -1, nullptr, nullptr,
+                                         nullptr, (hipStream_t)stream),
                     "gs_rasterize_fwd");
+}
+
+gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
+                                const uint32_t* tile_ranges, const uint32_t* ids,
+                                const float* splats, const float* depths,
+                                const float* background, const gs_settings* settings,
+                                int32_t kind, const float* target, float* image, float* final_T,
+                                uint32_t* last_idx, float* out_depth, float* out_alpha,
+                                float* dL_dimage, float* loss, uint64_t* counters,
+                                void* stream) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
+  GS_REQUIRE(target && dL_dimage, "NULL target or gradient pointer");
+  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
+  if (N > 0) {
+    GS_REQUIRE(ids && splats, "NULL splat pointer");
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
+    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  }
+  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, ids, splats, depths,
+                                         background, gs::make_settings(*settings), image,
+                                         final_T, last_idx, out_depth, out_alpha, counters, kind,
+                                         target, dL_dimage, loss, (hipStream_t)stream),
+                    "gs_rasterize_fwd_loss");
 }
 
 gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
@@ -562,7 +590,8 @@ gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
   return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, ids, splats,
                                          depths, background, gs::make_settings(*settings),
                                          image, final_T, last_idx, out_depth, out_alpha,
-                                         counters, (hipStream_t)stream),
+                                         counters, -1, nullptr, nullptr, nullptr,
+                                         (hipStream_t)stream),
                     "gs_rasterize_fwd_batched");
 }
 

@@ -166,13 +166,40 @@ __device__ inline void add_counters(uint64_t* cnt, uint64_t a, uint64_t b, uint6
     atomicAdd((unsigned long long*)&cnt[threadIdx.x], (unsigned long long)s_c[threadIdx.x]);
 }
 
+// Inclusive DPP row scan: each 16-lane row's total lands in its lane 15.
+#define GS_ROW_ADD(v, ctrl)                                                                \
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                              \
+                                     0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true))
+__device__ inline float row_total_lane15(float v) {
+  GS_ROW_ADD(v, 0x111);  // row_shr:1
+  GS_ROW_ADD(v, 0x112);  // row_shr:2
+  GS_ROW_ADD(v, 0x114);  // row_shr:4
+  GS_ROW_ADD(v, 0x118);  // row_shr:8
+  return v;
+}
+#undef GS_ROW_ADD
+
+__global__ void zero_f32_kernel(float* __restrict__ p) { *p = 0.0f; }
+
+// Per-element loss gradient (kind 0: L2, 2 (x - y); kind 1: L1, sign(x - y)),
+// adding the element's loss to acc.
+__device__ inline float loss_term(int kind, float r, float& acc) {
+  if (kind == 0) {
+    acc = fmaf(r, r, acc);
+    return 2.0f * r;
+  }
+  acc += fabsf(r);
+  return r > 0.0f ? 1.0f : (r < 0.0f ? -1.0f : 0.0f);
+}
+
 template <bool kDepth, bool kStats>
 __global__ __launch_bounds__(256) void raster_fwd_kernel(
     int W, int H, int gx, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids,
     const float4* __restrict__ splats, const float* __restrict__ depths, float bg0, float bg1,
     float bg2, Settings st, float* __restrict__ image, float* __restrict__ final_T,
     uint32_t* __restrict__ last_idx, float* __restrict__ out_depth,
-    float* __restrict__ out_alpha, uint64_t* __restrict__ cnt) {
+    float* __restrict__ out_alpha, uint64_t* __restrict__ cnt, int loss_kind,
+    const float* __restrict__ target, float* __restrict__ dl, float* __restrict__ loss) {
   __shared__ SplatLds s_sp[256];
   __shared__ uint8_t s_list[4][256];
   __shared__ uint32_t s_cnt[4];
@@ -247,15 +274,35 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     const uint64_t tile_plain = threadIdx.x == 0 ? 256ull * s_tmax : 0ull;
     add_counters(cnt, inside ? n_eval : 0u, n_blend, plain, tile_plain);
   }
-  if (!inside) return;
   const int64_t p = ((int64_t)blockIdx.y * H + py) * W + px;
-  image[3 * p + 0] = fmaf(T, bg0, C0);
-  image[3 * p + 1] = fmaf(T, bg1, C1);
-  image[3 * p + 2] = fmaf(T, bg2, C2);
-  final_T[p] = T;
-  last_idx[p] = last;
-  if (kDepth) out_depth[p] = D;
-  if (out_alpha) out_alpha[p] = 1.0f - T;
+  const float c0 = fmaf(T, bg0, C0), c1 = fmaf(T, bg1, C1), c2 = fmaf(T, bg2, C2);
+  float lacc = 0.0f;
+  if (inside) {
+    image[3 * p + 0] = c0;
+    image[3 * p + 1] = c1;
+    image[3 * p + 2] = c2;
+    final_T[p] = T;
+    last_idx[p] = last;
+    if (kDepth) out_depth[p] = D;
+    if (out_alpha) out_alpha[p] = 1.0f - T;
+    // the image loss gradient while the colour is in registers
+    if (loss_kind >= 0) {
+      dl[3 * p + 0] = loss_term(loss_kind, c0 - target[3 * p + 0], lacc);
+      dl[3 * p + 1] = loss_term(loss_kind, c1 - target[3 * p + 1], lacc);
+      dl[3 * p + 2] = loss_term(loss_kind, c2 - target[3 * p + 2], lacc);
+    }
+  }
+  if (loss_kind >= 0 && loss) {  // uniform: every lane of the workgroup arrives
+    __shared__ float s_l[16];
+    lacc = row_total_lane15(lacc);
+    if ((tid & 15) == 15) s_l[tid >> 4] = lacc;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
+      for (int k = 0; k < 16; ++k) t += s_l[k];
+      atomicAdd(loss, t);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -277,17 +324,6 @@ __device__ inline float swap_add16(float a, float b) {
                                                   false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-#define GS_ROW_ADD(v, ctrl)                                                                \
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                              \
-                                     0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true))
-__device__ inline float row_total_lane15(float v) {
-  GS_ROW_ADD(v, 0x111);  // row_shr:1
-  GS_ROW_ADD(v, 0x112);  // row_shr:2
-  GS_ROW_ADD(v, 0x114);  // row_shr:4
-  GS_ROW_ADD(v, 0x118);  // row_shr:8
-  return v;
-}
-#undef GS_ROW_ADD
 
 // Sums f[0..8] (and f[9], f[10] when kAbs) over the wavefront and adds field
 // q to dst[q * stride] (LDS, atomically).  Callers give each pair of
@@ -593,20 +629,11 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
   }
 }
 
-__global__ void zero_f32_kernel(float* __restrict__ p) { *p = 0.0f; }
 
 // dL/dimage and (optionally) the summed loss: per-lane partial sums, a DPP
 // row reduction, a cross-wave sum in LDS, then one atomic per workgroup.
 // float4 accesses when the three arrays are 16-byte aligned; the tail (and
 // unaligned arrays) go element by element.
-__device__ inline float loss_term(int kind, float r, float& acc) {
-  if (kind == 0) {
-    acc = fmaf(r, r, acc);
-    return 2.0f * r;
-  }
-  acc += fabsf(r);
-  return r > 0.0f ? 1.0f : (r < 0.0f ? -1.0f : 0.0f);
-}
 
 __global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n, int64_t n4,
                                                         const float* __restrict__ img,
@@ -645,35 +672,35 @@ __global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n, int
 }  // namespace gs
 
 // ncams images of W x H (a batch: ranges over ncams * T tiles, outputs
-// [c][H][W]).
+// [c][H][W]).  loss_kind >= 0: also dL/dimage against target (and the loss
+// value into *loss when non-NULL).
 extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
                                            const uint32_t* ranges, const uint32_t* ids,
                                            const float* splats, const float* depths,
                                            const float* bg, const gs::Settings& st, float* image,
                                            float* final_T, uint32_t* last_idx, float* out_depth,
-                                           float* out_alpha, uint64_t* counters, hipStream_t s) {
+                                           float* out_alpha, uint64_t* counters, int loss_kind,
+                                           const float* target, float* dl, float* loss,
+                                           hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid(gs::tile_grid_blocks(gx, gy), (unsigned)ncams), block(256);
   const float4* sp = (const float4*)splats;
-  if (counters) {
-    if (out_depth)
-      hipLaunchKernelGGL((gs::raster_fwd_kernel<true, true>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, sp, depths, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
-                         out_depth, out_alpha, counters);
-    else
-      hipLaunchKernelGGL((gs::raster_fwd_kernel<false, true>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, sp, nullptr, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
-                         nullptr, out_alpha, counters);
-  } else {
-    if (out_depth)
-      hipLaunchKernelGGL((gs::raster_fwd_kernel<true, false>), grid, block, 0, s, W, H, gx, ranges,
-                         ids, sp, depths, bg[0], bg[1], bg[2], st, image, final_T, last_idx,
-                         out_depth, out_alpha, nullptr);
-    else
-      hipLaunchKernelGGL((gs::raster_fwd_kernel<false, false>), grid, block, 0, s, W, H, gx,
-                         ranges, ids, sp, nullptr, bg[0], bg[1], bg[2], st, image, final_T,
-                         last_idx, nullptr, out_alpha, nullptr);
+  if (loss_kind >= 0 && loss) {
+    hipLaunchKernelGGL(gs::zero_f32_kernel, dim3(1), dim3(1), 0, s, loss);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+#define GS_RFWD(DEPTH, STATS)                                                                  \
+  hipLaunchKernelGGL((gs::raster_fwd_kernel<DEPTH, STATS>), grid, block, 0, s, W, H, gx, ranges, \
+                     ids, sp, DEPTH ? depths : nullptr, bg[0], bg[1], bg[2], st, image,        \
+                     final_T, last_idx, DEPTH ? out_depth : nullptr, out_alpha,               \
+                     STATS ? counters : nullptr, loss_kind, target, dl, loss)
+  if (counters) {
+    if (out_depth) GS_RFWD(true, true); else GS_RFWD(false, true);
+  } else {
+    if (out_depth) GS_RFWD(true, false); else GS_RFWD(false, false);
+  }
+#undef GS_RFWD
   return hipGetLastError();
 }
 

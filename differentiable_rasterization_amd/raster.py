@@ -32,7 +32,7 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_adam_step_packed", "gs_project_fwd_batched",
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
             "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
-            "gs_bin_and_sort_device")
+            "gs_bin_and_sort_device", "gs_rasterize_fwd_loss")
 
 
 class GsError(RuntimeError):
@@ -131,6 +131,8 @@ def load():
     lib.gs_bin_and_sort_device.restype = C.c_int
     lib.gs_bin_and_sort_device.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                            C.c_size_t, P]
+    lib.gs_rasterize_fwd_loss.restype = C.c_int
+    lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 6 + [i32] + [P] * 9 + [P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -378,6 +380,18 @@ def gs_bin_and_sort_device(N, ld, means2d, radii, depths, tiles_touched, width, 
                                       _p(workspace), workspace_bytes, _stream(stream)))
 
 
+def gs_rasterize_fwd_loss(N, ld, width, height, tile_ranges, ids, splats, depths, background,
+                          settings, kind, target, image, final_T, last_idx, dL_dimage,
+                          out_depth=None, out_alpha=None, loss=None, counters=None, stream=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_fwd_loss(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+                                     _p(depths), bg, C.byref(settings), int(kind), _p(target),
+                                     _p(image), _p(final_T), _p(last_idx), _p(out_depth),
+                                     _p(out_alpha), _p(dL_dimage), _p(loss), _p(counters),
+                                     _stream(stream)))
+
+
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
     lib = load()
     _check(lib.gs_image_loss_grad(int(kind), int(count), _p(image), _p(target), _p(dL_dimage),
@@ -618,6 +632,15 @@ class Frame:
             _check(st)
         self.M = M
         return M
+
+    def rasterize_loss(self, g: Gaussians, target, kind, with_loss=False, counters=None):
+        """Compositing with the loss gradient fused in: dL_dimage (and the
+        loss value when with_loss) against target."""
+        gs_rasterize_fwd_loss(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
+                              self.depths, self.background, self.settings, kind, target,
+                              self.image, self.final_T, self.last_idx, self.dL_dimage,
+                              self.out_depth, self.out_alpha,
+                              self.loss if with_loss else None, counters)
 
     def rasterize(self, g: Gaussians, counters=None):
         gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,

@@ -205,6 +205,22 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
                            uint32_t* last_idx, float* out_depth, float* out_alpha,
                            uint64_t* counters, void* stream);
 
+/* gs_rasterize_fwd with the image loss gradient fused in: while each
+ * pixel's colour is in registers, dL_dimage [H][W][3] receives the gradient
+ * of the sum-reduced loss against target [H][W][3] (kind 0: L2, 2 (x - y);
+ * kind 1: L1, sign(x - y) with sign(0) = 0), the same values
+ * gs_image_loss_grad writes, and *loss (a device float; NULL to skip) the
+ * loss value (its summation order across tiles is not fixed).  The image
+ * is not read back.  dL_dimage must not alias image or target. */
+GS_API gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
+                                       const uint32_t* tile_ranges, const uint32_t* ids,
+                                       const float* splats, const float* depths,
+                                       const float* background, const gs_settings* settings,
+                                       int32_t kind, const float* target, float* image,
+                                       float* final_T, uint32_t* last_idx, float* out_depth,
+                                       float* out_alpha, float* dL_dimage, float* loss,
+                                       uint64_t* counters, void* stream);
+
 /* Stage 5a — compositing backward (gsplat guide §2.2).  Walks each pixel's
  * blended list back to front from last_idx, recovering T by division and
  * accumulating the colour behind, and sums per Gaussian the gradients of the

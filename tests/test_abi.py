@@ -274,6 +274,22 @@ def test_batched_calls_reject_bad_arguments(lib):
     assert r == raster.GS_ERR_INVALID_ARGUMENT
 
 
+def test_fused_loss_rejects_bad_arguments(lib):
+    dummy, other = C.c_void_p(64), C.c_void_p(128)
+    st = raster.default_settings()
+    bg = (C.c_float * 3)(0, 0, 0)
+
+    def call(kind=1, target=other, dl=C.c_void_p(192)):
+        return lib.gs_rasterize_fwd_loss(4, 4, 64, 64, dummy, dummy, dummy, None, bg,
+                                         C.byref(st), kind, target, dummy, dummy, dummy, None,
+                                         None, dl, None, None, None)
+    assert call(kind=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(target=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(dl=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(dl=dummy) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the image
+    assert call(dl=other) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the target
+
+
 def test_densify_rejects_bad_arguments(lib):
     dummy = C.c_void_p(256)
     n_out = C.c_int64(0)

@@ -174,6 +174,35 @@ def test_long_tile_lists_keep_the_stable_order(n):
     assert np.abs(out["image"] - o["raster"]["image"]).max() <= PIX_TOL
 
 
+@pytest.mark.parametrize("kind", [0, 1])
+def test_fused_loss_equals_separate_call(kind):
+    """gs_rasterize_fwd_loss: the image and dL/dimage equal gs_rasterize_fwd
+    followed by gs_image_loss_grad bit for bit; the loss value is the sum
+    within fp32 rounding (its summation order is not fixed)."""
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    for scene, cam in ((scenes.cluster_scene(n=200_000, seed=13),
+                        scenes.sphere_poses(1, 6.0, 31, 640, 416, scenes.focal_for(640))[0]),
+                       scenes.box_scene(n=20000, seed=12, width=500, height=270, fx=290.0)):
+        g = raster.Gaussians.from_scene(scene)
+        tgt = torch.from_numpy(scenes.target_image(cam, 3)).cuda()
+        a = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height)
+        b = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height)
+        for fr in (a, b):
+            fr.project(g, cam)
+            fr.bin_and_sort(g)
+        a.rasterize(g)
+        a.loss_grad(tgt, kind)
+        b.dL_dimage.fill_(float("nan"))
+        b.rasterize_loss(g, tgt, kind, with_loss=True)
+        torch.cuda.synchronize()
+        assert_bits_equal(b.image.cpu().numpy(), a.image.cpu().numpy(), "image")
+        assert_bits_equal(b.dL_dimage.cpu().numpy(), a.dL_dimage.cpu().numpy(), "dL/dimage")
+        r = a.image.cpu().numpy().astype(np.float64) - tgt.cpu().numpy()
+        want = np.sum(r * r) if kind == 0 else np.sum(np.abs(r))
+        assert abs(float(b.loss.item()) - want) <= 1e-5 * want
+
+
 def test_loss_value_and_gradient():
     torch = _torch()
     from differentiable_rasterization_amd import raster
