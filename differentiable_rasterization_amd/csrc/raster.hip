@@ -480,9 +480,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     // batch slot k holds list position rel = b_end - 1 - start - k; the pixel
     // blended it only if rel < last, i.e. k > kthr
     const int kthr = (int)(b_end - 1u - start) - (int)last;
-    for (int i = 0; i < cnt_w; ++i) {
-      const int k = s_list[wave][i];
-      const SplatLds& s = s_sp[k];
+    // one list entry: slot k's splat s, evaluated for this lane's pixel
+    auto eval = [&](const SplatLds& s, int k) {
       const float dx = fpx - s.u, dy = fpy - s.v;
       float e1, e2;
       const float p2 = splat_power2(s, dx, dy, e1, e2);
@@ -527,6 +526,39 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
         if (kStats) n_red += (lane == 0) ? 1u : 0u;
         reduce_add<kAbs>(f, &s_acc[wave >> 1][0][k], 256);
       }
+    };
+    // Software pipeline over the wave's list: each splat record is read
+    // from LDS two entries ahead of its use, into three rotating register
+    // sets, so that a use never waits on the LDS additions of the entry just
+    // before it; the list (at most 256 one-byte slots) is held in one
+    // register, four slots per lane, and read with lane reads.  Reads past
+    // the end repeat the last entry.
+    if (cnt_w > 0) {
+      const uint32_t lw = reinterpret_cast<const uint32_t*>(s_list[wave])[lane];
+      const int lastp = cnt_w - 1;
+      auto slot_at = [&](int i) {
+        i = min(i, lastp);
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)lw, i >> 2);
+        return (int)((w >> (8 * (i & 3))) & 0xffu);
+      };
+      int k0 = slot_at(0), k1 = slot_at(1), k2;
+      SplatLds s0 = s_sp[k0], s1 = s_sp[k1], s2;
+      int i = 0;
+      // whole trips of three entries ...
+      for (; i + 2 <= lastp; i += 3) {
+        k2 = slot_at(i + 2);
+        s2 = s_sp[k2];
+        eval(s0, k0);
+        k0 = slot_at(i + 3);
+        s0 = s_sp[k0];
+        eval(s1, k1);
+        k1 = slot_at(i + 4);
+        s1 = s_sp[k1];
+        eval(s2, k2);
+      }
+      // ... then the one or two entries left, if any
+      if (i <= lastp) eval(s0, k0);
+      if (i + 1 <= lastp) eval(s1, k1);
     }
     __syncthreads();
     if (tid < n) {
