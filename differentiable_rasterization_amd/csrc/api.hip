@@ -35,14 +35,17 @@ hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d
                                      uint64_t* counts, uint64_t* keys, uint32_t* ids,
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
+hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
+                                uint32_t* order, hipStream_t s);
 hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
-                                const uint32_t* ids, const float* splats, const float* depths,
+                                const uint32_t* order, const uint32_t* ids, const float* splats,
+                                const float* depths,
                                 const float* bg, const gs::Settings& st, float* image,
                                 float* final_T, uint32_t* last_idx, float* out_depth,
                                 float* out_alpha, uint64_t* counters, int loss_kind,
                                 const float* target, float* dl, float* loss, hipStream_t s);
 hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
-                                const uint32_t* ranges,
+                                const uint32_t* ranges, const uint32_t* order,
                                 const uint32_t* ids, const float* splats, const uint32_t* offsets,
                                 const uint32_t* tiles, const float* bg, const gs::Settings& st,
                                 const float* final_T, const uint32_t* last_idx,
@@ -263,8 +266,21 @@ gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
                     "gs_bin_and_sort_device");
 }
 
+gs_status gs_tile_order(int32_t num_cams, int32_t width, int32_t height,
+                        const uint32_t* tile_ranges, uint32_t* tile_order, void* stream) {
+  GS_REQUIRE(num_cams >= 1 && num_cams <= gs::kMaxCams, "num_cams must be in [1, 8]");
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(tile_ranges && tile_order, "NULL range or order pointer");
+  GS_REQUIRE((const void*)tile_ranges != (const void*)tile_order,
+             "tile_order must not alias tile_ranges");
+  return hip_status(gs_launch_tile_order(width, height, num_cams, tile_ranges, tile_order,
+                                         (hipStream_t)stream),
+                    "gs_tile_order");
+}
+
 gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids, const float* splats,
+                           const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids, const float* splats,
                            const float* depths, const float* background,
                            const gs_settings* settings, float* image,
                            float* final_T, uint32_t* last_idx, float* out_depth, float* out_alpha,
@@ -279,7 +295,8 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
     GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
     if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
   }
-  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, ids, splats, depths,
+  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, tile_order, ids,
+                                         splats, depths,
                                          background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
                                          out_depth, out_alpha, counters, -1, nullptr, nullptr,
@@ -288,7 +305,8 @@ gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
 }
 
 gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                const uint32_t* tile_ranges, const uint32_t* ids,
+                                const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                                 const float* splats, const float* depths,
                                 const float* background, const gs_settings* settings,
                                 int32_t kind, const float* target, float* image, float* final_T,
@@ -308,7 +326,8 @@ gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t he
     GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
     if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
   }
-  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, ids, splats, depths,
+  return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, tile_order, ids,
+                                         splats, depths,
                                          background, gs::make_settings(*settings), image,
                                          final_T, last_idx, out_depth, out_alpha, counters, kind,
                                          target, dL_dimage, loss, (hipStream_t)stream),
@@ -316,7 +335,8 @@ gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t he
 }
 
 gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids, const float* splats,
+                           const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids, const float* splats,
                            const uint32_t* offsets, const uint32_t* tiles_touched,
                            uint64_t num_instances, const float* background,
                            const gs_settings* settings, const float* final_T,
@@ -339,7 +359,8 @@ gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
     GS_REQUIRE(partials != nullptr, "partials is NULL");
     GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
   }
-  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, ids, splats, offsets,
+  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, tile_order, ids,
+                                         splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
                                          grads2d, absgrad, nullptr, 0, counters,
@@ -414,7 +435,8 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
 }
 
 gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                  const uint32_t* tile_ranges, const uint32_t* ids,
+                                  const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                                   const float* splats, const uint32_t* offsets,
                                   const uint32_t* tiles_touched, uint64_t num_instances,
                                   const uint32_t* vis_ids, int64_t num_visible,
@@ -442,7 +464,8 @@ gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t 
   }
   // an empty list still needs a non-NULL pointer to select the packed rows
   static const uint32_t kNoIds = 0;
-  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, ids, splats, offsets,
+  return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, tile_order, ids,
+                                         splats, offsets,
                                          tiles_touched, background, gs::make_settings(*settings),
                                          final_T, last_idx, dL_dimage, partials, num_instances,
                                          grads2d, absgrad, vis_ids ? vis_ids : &kNoIds,
@@ -569,7 +592,8 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
 }
 
 gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
-                                   const uint32_t* tile_ranges, const uint32_t* ids,
+                                   const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                                    const float* splats, const float* depths,
                                    const float* background, const gs_settings* settings,
                                    float* image, float* final_T, uint32_t* last_idx,
@@ -587,7 +611,8 @@ gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
     GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
     if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
   }
-  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, ids, splats,
+  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order,
+                                         ids, splats,
                                          depths, background, gs::make_settings(*settings),
                                          image, final_T, last_idx, out_depth, out_alpha,
                                          counters, -1, nullptr, nullptr, nullptr,
@@ -596,7 +621,8 @@ gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
 }
 
 gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
-                                   const uint32_t* tile_ranges, const uint32_t* ids,
+                                   const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                                    const float* splats, const uint32_t* offsets,
                                    const uint32_t* tiles_touched, uint64_t num_instances,
                                    const float* background, const gs_settings* settings,
@@ -623,7 +649,8 @@ gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
     GS_REQUIRE(partials != nullptr, "partials is NULL");
     GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
   }
-  return hip_status(gs_launch_raster_bwd(rows, width, height, num_cams, tile_ranges, ids, splats,
+  return hip_status(gs_launch_raster_bwd(rows, width, height, num_cams, tile_ranges,
+                                         tile_order, ids, splats,
                                          offsets, tiles_touched, background,
                                          gs::make_settings(*settings), final_T, last_idx,
                                          dL_dimage, partials, num_instances, grads2d, absgrad,

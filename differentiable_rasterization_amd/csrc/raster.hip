@@ -77,6 +77,31 @@ __device__ inline bool block_tile(int b, int gx, int gy, int& tx, int& ty) {
   return tx < gx && ty < gy;
 }
 
+// Tile of this workgroup: with a schedule (tile_order_kernel), workgroup b
+// of camera c takes tile order[c * T + b], so that the longest lists start
+// first; without one, the XCD-aware mapping above.  Workgroups past the last
+// tile, and entries that are no tile index, return at once.
+__device__ inline bool schedule_tile(const uint32_t* __restrict__ order, int gx, int gy, int& tx,
+                                     int& ty) {
+  if (!order) return block_tile((int)blockIdx.x, gx, gy, tx, ty);
+  const int nt = gx * gy;
+  if ((int)blockIdx.x >= nt) return false;
+  const uint32_t t = order[(int64_t)blockIdx.y * nt + blockIdx.x];
+  if (t >= (uint32_t)nt) return false;
+  tx = (int)t % gx;
+  ty = (int)t / gx;
+  return true;
+}
+
+// Schedule bucket of a tile with n list entries: n itself below 8, else
+// eight buckets per power of two (about 12% apart), so 256 buckets cover
+// any 32-bit length.
+__device__ inline uint32_t length_bucket(uint32_t n) {
+  if (n < 8u) return n;
+  const uint32_t e = 31u - (uint32_t)__clz((int)n);  // 3 .. 31
+  return (e - 2u) * 8u + ((n >> (e - 3u)) & 7u);
+}
+
 // Pixel of lane `tid` within its tile: wave w covers quadrant (w & 1, w >> 1),
 // lane l its pixel (l & 7, l >> 3).
 __device__ inline int quad_px(int tid) { return ((tid >> 6) & 1) * 8 + (tid & 7); }
@@ -199,14 +224,15 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     float bg2, Settings st, float* __restrict__ image, float* __restrict__ final_T,
     uint32_t* __restrict__ last_idx, float* __restrict__ out_depth,
     float* __restrict__ out_alpha, uint64_t* __restrict__ cnt, int loss_kind,
-    const float* __restrict__ target, float* __restrict__ dl, float* __restrict__ loss) {
+    const float* __restrict__ target, float* __restrict__ dl, float* __restrict__ loss,
+    const uint32_t* __restrict__ order) {
   __shared__ SplatLds s_sp[256];
   __shared__ uint8_t s_list[4][256];
   __shared__ uint32_t s_cnt[4];
   __shared__ uint32_t s_wc[4][4];
   int tx, ty;
   const int gy = grid_dim(H);
-  if (!block_tile((int)blockIdx.x, gx, gy, tx, ty)) return;
+  if (!schedule_tile(order, gx, gy, tx, ty)) return;
   // camera blockIdx.y of a batch: its tiles follow the earlier cameras'
   // (gx * gy each) and its pixels their images
   const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
@@ -386,7 +412,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     const float4* __restrict__ splats, const uint32_t* __restrict__ offsets, float bg0,
     float bg1, float bg2, Settings st, const float* __restrict__ final_T,
     const uint32_t* __restrict__ last_idx, const float* __restrict__ dL_dimage,
-    float4* __restrict__ partials, uint64_t capacity, uint64_t* __restrict__ cnt) {
+    float4* __restrict__ partials, uint64_t capacity, uint64_t* __restrict__ cnt,
+    const uint32_t* __restrict__ order) {
   // one LDS block with the staged splats at offset 0, so that the inner
   // loop's three reads of a splat share one address (read2 immediates reach
   // only 2 KB past it)
@@ -407,7 +434,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   uint32_t& s_maxlast = lds.maxlast;
   int tx, ty;
   const int gy = grid_dim(H);
-  if (!block_tile((int)blockIdx.x, gx, gy, tx, ty)) return;
+  if (!schedule_tile(order, gx, gy, tx, ty)) return;
   // camera blockIdx.y of a batch (tiles and images after the earlier ones')
   const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -701,13 +728,84 @@ __global__ __launch_bounds__(256) void loss_grad_kernel(int kind, int64_t n, int
   }
 }
 
+// Workgroup c orders camera c's T tiles by decreasing list length (bucketed
+// by length_bucket; within a bucket the order is whatever the LDS counters
+// give).  The compositing kernels' results do not depend on it: it only
+// decides which tiles start first, so that the longest lists do not start
+// last and leave the GPU to a few workgroups at the end.  Each lane takes
+// kOrderItems tiles per round with all their range loads in flight; the
+// buckets of up to kOrderKeep tiles stay in LDS for the second pass.
+constexpr int kOrderThreads = 1024, kOrderItems = 8, kOrderKeep = 32768;
+
+__global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(
+    const uint32_t* __restrict__ ranges, int T, uint32_t* __restrict__ order) {
+  __shared__ uint32_t h[256];
+  __shared__ uint8_t kept[kOrderKeep];
+  const int tid = threadIdx.x;
+  const uint32_t* rr = ranges + 2 * (int64_t)blockIdx.y * T;
+  uint32_t* out = order + (int64_t)blockIdx.y * T;
+  const bool keep = T <= kOrderKeep;
+  if (tid < 256) h[tid] = 0u;
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += kOrderThreads * kOrderItems) {
+    uint32_t r0[kOrderItems], r1[kOrderItems];
+#pragma unroll
+    for (int j = 0; j < kOrderItems; ++j) {
+      const int t = t0 + j * kOrderThreads + tid;
+      r0[j] = t < T ? rr[2 * t] : 0u;
+      r1[j] = t < T ? rr[2 * t + 1] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kOrderItems; ++j) {
+      const int t = t0 + j * kOrderThreads + tid;
+      const uint32_t b = 255u - length_bucket(r1[j] - r0[j]);
+      if (t < T) {
+        if (keep) kept[t] = (uint8_t)b;
+        atomicAdd(&h[b], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan of the 256 counts, four per lane
+    uint32_t c[4], run = 0;
+    for (int j = 0; j < 4; ++j) { c[j] = h[4 * tid + j]; run += c[j]; }
+    uint32_t incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d);
+      if (tid >= d) incl += o;
+    }
+    uint32_t base = incl - run;
+    for (int j = 0; j < 4; ++j) { h[4 * tid + j] = base; base += c[j]; }
+  }
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += kOrderThreads) {
+    const int t = t0 + tid;
+    if (t < T) {
+      const uint32_t b =
+          keep ? (uint32_t)kept[t] : 255u - length_bucket(rr[2 * t + 1] - rr[2 * t]);
+      out[atomicAdd(&h[b], 1u)] = (uint32_t)t;
+    }
+  }
+}
+
 }  // namespace gs
+
+extern "C" hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams,
+                                           const uint32_t* ranges, uint32_t* order,
+                                           hipStream_t s) {
+  const int T = gs::grid_dim(W) * gs::grid_dim(H);
+  if (T == 0 || ncams == 0) return hipSuccess;
+  hipLaunchKernelGGL(gs::tile_order_kernel, dim3(1, (unsigned)ncams), dim3(1024), 0, s, ranges,
+                     T, order);
+  return hipGetLastError();
+}
 
 // ncams images of W x H (a batch: ranges over ncams * T tiles, outputs
 // [c][H][W]).  loss_kind >= 0: also dL/dimage against target (and the loss
 // value into *loss when non-NULL).
 extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
-                                           const uint32_t* ranges, const uint32_t* ids,
+                                           const uint32_t* ranges, const uint32_t* order,
+                                           const uint32_t* ids,
                                            const float* splats, const float* depths,
                                            const float* bg, const gs::Settings& st, float* image,
                                            float* final_T, uint32_t* last_idx, float* out_depth,
@@ -726,7 +824,7 @@ extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
   hipLaunchKernelGGL((gs::raster_fwd_kernel<DEPTH, STATS>), grid, block, 0, s, W, H, gx, ranges, \
                      ids, sp, DEPTH ? depths : nullptr, bg[0], bg[1], bg[2], st, image,        \
                      final_T, last_idx, DEPTH ? out_depth : nullptr, out_alpha,               \
-                     STATS ? counters : nullptr, loss_kind, target, dl, loss)
+                     STATS ? counters : nullptr, loss_kind, target, dl, loss, order)
   if (counters) {
     if (out_depth) GS_RFWD(true, true); else GS_RFWD(false, true);
   } else {
@@ -739,7 +837,7 @@ extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
 // ncams > 1: a batch (N = ncams * ld rows, ranges over ncams * T tiles,
 // images [c][H][W]).
 extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
-                                           const uint32_t* ranges,
+                                           const uint32_t* ranges, const uint32_t* order,
                                            const uint32_t* ids, const float* splats,
                                            const uint32_t* offsets, const uint32_t* tiles,
                                            const float* bg, const gs::Settings& st,
@@ -755,7 +853,7 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int 
 #define GS_RBWD(STATS, ABS)                                                                 \
   hipLaunchKernelGGL((gs::raster_bwd_kernel<STATS, ABS>), grid, block, 0, s, W, H, gx, ranges, \
                      ids, sp, offsets, bg[0], bg[1], bg[2], st, final_T, last_idx,          \
-                     dL_dimage, part, capacity, counters)
+                     dL_dimage, part, capacity, counters, order)
   if (counters) {
     if (absgrad) GS_RBWD(true, true); else GS_RBWD(true, false);
   } else {

@@ -32,7 +32,7 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_adam_step_packed", "gs_project_fwd_batched",
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
             "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
-            "gs_bin_and_sort_device", "gs_rasterize_fwd_loss")
+            "gs_bin_and_sort_device", "gs_rasterize_fwd_loss", "gs_tile_order")
 
 
 class GsError(RuntimeError):
@@ -86,9 +86,9 @@ def load():
     lib.gs_bin_and_sort.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                     C.c_size_t, P]
     lib.gs_rasterize_fwd.restype = C.c_int
-    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 13
+    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 14
     lib.gs_rasterize_bwd.restype = C.c_int
-    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 5 + [u64] + [P] * 6 + \
+    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 6 + [u64] + [P] * 6 + \
         [u64, P, i32, P, P]
     lib.gs_project_bwd.restype = C.c_int
     lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 2 + [P] * 5 + \
@@ -97,7 +97,7 @@ def load():
     lib.gs_bin_and_sort_packed.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
                                            P, P, C.c_size_t, P]
     lib.gs_rasterize_bwd_packed.restype = C.c_int
-    lib.gs_rasterize_bwd_packed.argtypes = [i64, i64, i32, i32] + [P] * 5 + [u64, P, i64] + \
+    lib.gs_rasterize_bwd_packed.argtypes = [i64, i64, i32, i32] + [P] * 6 + [u64, P, i64] + \
         [P] * 6 + [u64, P, i32, P, P]
     lib.gs_project_bwd_packed.restype = C.c_int
     lib.gs_project_bwd_packed.argtypes = [i64, P, i64, i64, i64, i32] + [P] * 4 + [P, P] + \
@@ -121,9 +121,9 @@ def load():
     lib.gs_bin_and_sort_batched.argtypes = [i32, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
                                             P, C.c_size_t, P]
     lib.gs_rasterize_fwd_batched.restype = C.c_int
-    lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 13
+    lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 14
     lib.gs_rasterize_bwd_batched.restype = C.c_int
-    lib.gs_rasterize_bwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 5 + [u64] + [P] * 6 + \
+    lib.gs_rasterize_bwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 6 + [u64] + [P] * 6 + \
         [u64, P, i32, P, P]
     lib.gs_project_bwd_batched.restype = C.c_int
     lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 2 + \
@@ -132,7 +132,9 @@ def load():
     lib.gs_bin_and_sort_device.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                            C.c_size_t, P]
     lib.gs_rasterize_fwd_loss.restype = C.c_int
-    lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 6 + [i32] + [P] * 9 + [P]
+    lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 7 + [i32] + [P] * 9 + [P]
+    lib.gs_tile_order.restype = C.c_int
+    lib.gs_tile_order.argtypes = [i32, i32, i32, P, P, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -227,10 +229,11 @@ def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height,
 
 def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, background,
                      settings, image, final_T, last_idx, out_depth=None, out_alpha=None,
-                     counters=None, stream=None):
+                     counters=None, stream=None, tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(tile_order), _p(ids),
+                                _p(splats),
                                 _p(depths), bg, C.byref(settings), _p(image), _p(final_T),
                                 _p(last_idx), _p(out_depth), _p(out_alpha), _p(counters),
                                 _stream(stream)))
@@ -238,10 +241,12 @@ def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, bac
 
 def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, splats, offsets, tiles_touched,
                      num_instances, background, settings, final_T, last_idx, dL_dimage, partials,
-                     partials_capacity, grads2d, absgrad=0, counters=None, stream=None):
+                     partials_capacity, grads2d, absgrad=0, counters=None, stream=None,
+                     tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+    _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(tile_order), _p(ids),
+                                _p(splats),
                                 _p(offsets), _p(tiles_touched), int(num_instances), bg,
                                 C.byref(settings), _p(final_T), _p(last_idx), _p(dL_dimage),
                                 _p(partials), int(partials_capacity), _p(grads2d),
@@ -278,10 +283,11 @@ def gs_bin_and_sort_packed(N, ld, means2d, radii, depths, tiles_touched, width, 
 def gs_rasterize_bwd_packed(N, ld, width, height, tile_ranges, ids, splats, offsets,
                             tiles_touched, num_instances, vis_ids, num_visible, background,
                             settings, final_T, last_idx, dL_dimage, partials, partials_capacity,
-                            grads2d, absgrad=0, counters=None, stream=None):
+                            grads2d, absgrad=0, counters=None, stream=None, tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_bwd_packed(N, ld, width, height, _p(tile_ranges), _p(ids),
+    _check(lib.gs_rasterize_bwd_packed(N, ld, width, height, _p(tile_ranges), _p(tile_order),
+                                       _p(ids),
                                        _p(splats), _p(offsets), _p(tiles_touched),
                                        int(num_instances), _p(vis_ids), int(num_visible), bg,
                                        C.byref(settings), _p(final_T), _p(last_idx),
@@ -333,10 +339,11 @@ def gs_bin_and_sort_batched(num_cams, ld, means2d, radii, depths, tiles_touched,
 
 def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, depths,
                              background, settings, image, final_T, last_idx, out_depth=None,
-                             out_alpha=None, counters=None, stream=None):
+                             out_alpha=None, counters=None, stream=None, tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_fwd_batched(num_cams, ld, width, height, _p(tile_ranges), _p(ids),
+    _check(lib.gs_rasterize_fwd_batched(num_cams, ld, width, height, _p(tile_ranges),
+                                        _p(tile_order), _p(ids),
                                         _p(splats), _p(depths), bg, C.byref(settings),
                                         _p(image), _p(final_T), _p(last_idx), _p(out_depth),
                                         _p(out_alpha), _p(counters), _stream(stream)))
@@ -345,10 +352,11 @@ def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, spla
 def gs_rasterize_bwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, offsets,
                              tiles_touched, num_instances, background, settings, final_T,
                              last_idx, dL_dimage, partials, partials_capacity, grads2d,
-                             absgrad=0, counters=None, stream=None):
+                             absgrad=0, counters=None, stream=None, tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_bwd_batched(num_cams, ld, width, height, _p(tile_ranges), _p(ids),
+    _check(lib.gs_rasterize_bwd_batched(num_cams, ld, width, height, _p(tile_ranges),
+                                        _p(tile_order), _p(ids),
                                         _p(splats), _p(offsets), _p(tiles_touched),
                                         int(num_instances), bg, C.byref(settings), _p(final_T),
                                         _p(last_idx), _p(dL_dimage), _p(partials),
@@ -382,14 +390,23 @@ def gs_bin_and_sort_device(N, ld, means2d, radii, depths, tiles_touched, width, 
 
 def gs_rasterize_fwd_loss(N, ld, width, height, tile_ranges, ids, splats, depths, background,
                           settings, kind, target, image, final_T, last_idx, dL_dimage,
-                          out_depth=None, out_alpha=None, loss=None, counters=None, stream=None):
+                          out_depth=None, out_alpha=None, loss=None, counters=None, stream=None,
+                          tile_order=None):
     lib = load()
     bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_fwd_loss(N, ld, width, height, _p(tile_ranges), _p(ids), _p(splats),
+    _check(lib.gs_rasterize_fwd_loss(N, ld, width, height, _p(tile_ranges), _p(tile_order),
+                                     _p(ids), _p(splats),
                                      _p(depths), bg, C.byref(settings), int(kind), _p(target),
                                      _p(image), _p(final_T), _p(last_idx), _p(out_depth),
                                      _p(out_alpha), _p(dL_dimage), _p(loss), _p(counters),
                                      _stream(stream)))
+
+
+def gs_tile_order(num_cams, width, height, tile_ranges, tile_order, stream=None):
+    """Longest-list-first schedule of each camera's tiles into tile_order
+    (device uint32 [num_cams * T]), for the gs_rasterize_* calls."""
+    _check(load().gs_tile_order(num_cams, width, height, _p(tile_ranges), _p(tile_order),
+                                _stream(stream)))
 
 
 def gs_image_loss_grad(kind, count, image, target, dL_dimage, loss=None, stream=None):
@@ -527,11 +544,15 @@ class Frame:
 
     ``device_count=True`` bins without the read-back (gs_bin_and_sort_device):
     nothing in a frame waits for the GPU, so a frame can be captured into a
-    HIP graph; ``check_counts()`` reads M and the overflow flag afterwards."""
+    HIP graph; ``check_counts()`` reads M and the overflow flag afterwards.
+
+    ``schedule=True`` (the default) runs gs_tile_order after the binning and
+    hands the schedule to the compositing calls (longest tiles first);
+    ``False`` keeps their fixed order.  The outputs are the same."""
 
     def __init__(self, ld, sh_degree, width, height, capacity=None, settings=None,
                  background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda",
-                 packed=False, device_count=False):
+                 packed=False, device_count=False, schedule=True):
         import torch
         self.torch = torch
         self.device = device
@@ -549,6 +570,7 @@ class Frame:
         self.colors, self.tiles = z((3, ld), f32), z((ld,), u32)
         self.offsets = z((max(ld, 1),), u32)
         self.ranges = z((self.T, 2), u32)
+        self.order = z((self.T,), u32) if schedule else None
         self.image = z((height, width, 3), f32)
         self.final_T = z((height, width), f32)
         self.last_idx = z((height, width), u32)
@@ -602,7 +624,12 @@ class Frame:
             st, M, V = gs_bin_and_sort_packed(*args())
             _check(st)
         self.M, self.V = M, V
+        self._schedule()
         return M
+
+    def _schedule(self):
+        if self.order is not None:
+            gs_tile_order(1, self.W, self.H, self.ranges, self.order)
 
     def check_counts(self):
         """(M, overflowed) of the last device-count binning (synchronises)."""
@@ -619,6 +646,7 @@ class Frame:
             # the instance count stays on the device; the backward bounds its
             # slots by the capacity
             self.M = self.capacity
+            self._schedule()
             return None
         st, M = gs_bin_and_sort(g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles,
                                 self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
@@ -631,6 +659,7 @@ class Frame:
                                     num_instances=self.m_host)
             _check(st)
         self.M = M
+        self._schedule()
         return M
 
     def rasterize_loss(self, g: Gaussians, target, kind, with_loss=False, counters=None):
@@ -640,12 +669,14 @@ class Frame:
                               self.depths, self.background, self.settings, kind, target,
                               self.image, self.final_T, self.last_idx, self.dL_dimage,
                               self.out_depth, self.out_alpha,
-                              self.loss if with_loss else None, counters)
+                              self.loss if with_loss else None, counters,
+                              tile_order=self.order)
 
     def rasterize(self, g: Gaussians, counters=None):
         gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
                          self.depths, self.background, self.settings, self.image, self.final_T,
-                         self.last_idx, self.out_depth, self.out_alpha, counters)
+                         self.last_idx, self.out_depth, self.out_alpha, counters,
+                         tile_order=self.order)
 
     def forward(self, g: Gaussians, cam):
         self.project(g, cam)
@@ -664,12 +695,14 @@ class Frame:
                                     self.splats, self.offsets, self.tiles, self.M, self.vis_ids,
                                     self.V, self.background, self.settings, self.final_T,
                                     self.last_idx, dl, self.partials, self.capacity,
-                                    self.grads2d, absgrad=int(bool(absgrad)), counters=counters)
+                                    self.grads2d, absgrad=int(bool(absgrad)), counters=counters,
+                                    tile_order=self.order)
             return
         gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
                          self.offsets, self.tiles, self.M, self.background, self.settings,
                          self.final_T, self.last_idx, dl, self.partials, self.capacity,
-                         self.grads2d, absgrad=int(bool(absgrad)), counters=counters)
+                         self.grads2d, absgrad=int(bool(absgrad)), counters=counters,
+                         tile_order=self.order)
 
     def project_backward(self, g: Gaussians, accumulate=0):
         if self.packed:
@@ -690,10 +723,12 @@ class Frame:
 class BatchFrame:
     """Forward of a batch of cameras (one image size) with one launch per
     stage: projection, binning + sort, compositing.  Per-camera outputs are
-    blocks [c] of each buffer; only the binning synchronises."""
+    blocks [c] of each buffer; only the binning synchronises.  ``schedule``
+    as for Frame."""
 
     def __init__(self, ld, sh_degree, width, height, num_cams, capacity=None, settings=None,
-                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda"):
+                 background=(0.0, 0.0, 0.0), with_depth_alpha=False, device="cuda",
+                 schedule=True):
         import torch
         self.torch = torch
         self.device = device
@@ -711,6 +746,7 @@ class BatchFrame:
         self.offsets = z((max(C_ * ld_, 1),), i32)
         self.splats = z((max(C_ * ld_, 1), 16), f32)
         self.ranges = z((C_ * self.T, 2), i32)
+        self.order = z((C_ * self.T,), i32) if schedule else None
         self.image = z((C_, height, width, 3), f32)
         self.final_T = z((C_, height, width), f32)
         self.last_idx = z((C_, height, width), i32)
@@ -756,10 +792,12 @@ class BatchFrame:
             st, M = gs_bin_and_sort_batched(*args())
             _check(st)
         self.M = M
+        if self.order is not None:
+            gs_tile_order(self.C, self.W, self.H, self.ranges, self.order)
         gs_rasterize_fwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
                                  self.splats, self.depths, self.background, self.settings,
                                  self.image, self.final_T, self.last_idx, self.out_depth,
-                                 self.out_alpha)
+                                 self.out_alpha, tile_order=self.order)
         return self.image
 
     def backward(self, g: "Gaussians", dL_dimage=None, accumulate=0, absgrad=False):
@@ -769,7 +807,8 @@ class BatchFrame:
         gs_rasterize_bwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
                                  self.splats, self.offsets, self.tiles, self.M, self.background,
                                  self.settings, self.final_T, self.last_idx, dl, self.partials,
-                                 self.capacity, self.grads2d, int(bool(absgrad)))
+                                 self.capacity, self.grads2d, int(bool(absgrad)),
+                                 tile_order=self.order)
         gs_project_bwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
                                g.sh, self.settings, self.radii, self.grads2d, self.g_means,
                                self.g_scales, self.g_quats, self.g_opacities, self.g_sh,

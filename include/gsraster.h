@@ -181,6 +181,18 @@ GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* mean
                                         uint32_t* tile_ranges, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* Schedule of the compositing kernels (no step of the method: a launch
+ * order).  For each of num_cams cameras, tile_order (DEVICE uint32
+ * [num_cams * T]) receives that camera's tile indices 0 .. T-1 ordered by
+ * decreasing list length in tile_ranges (lengths bucketed about 12% apart;
+ * the order within a bucket is not fixed).  Passed to the gs_rasterize_*
+ * calls, it makes their workgroups take the longest tiles first, so that a
+ * few long lists do not run on their own at the end of the launch.  Their
+ * results do not depend on it.  One workgroup per camera; it reads only
+ * tile_ranges, so it can run in a captured graph. */
+GS_API gs_status gs_tile_order(int32_t num_cams, int32_t width, int32_t height,
+                               const uint32_t* tile_ranges, uint32_t* tile_order, void* stream);
+
 /* Stage 4 — front-to-back alpha compositing per 16x16 tile (gsplat guide
  * §2.1, its third, differentiable blending step).  Per pixel, over its
  * tile's sorted list: q, the conic's quadratic form at (px+0.5-u, py+0.5-v),
@@ -192,6 +204,11 @@ GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* mean
  * (0 if none); out_depth [H][W] = sum alpha T depth and out_alpha [H][W] =
  * 1 - T when non-NULL (out_depth needs depths [ld]; otherwise depths may be
  * NULL).  background: HOST float[3].
+ * tile_order: NULL (a fixed XCD-aware order), or the schedule
+ * gs_tile_order wrote for these tile_ranges; it decides which workgroup
+ * takes which tile, never the outputs.  (With other contents, entries that
+ * are no tile index are skipped and tiles left out keep their old outputs.)
+ * The same argument of the other gs_rasterize_* calls means the same.
  * counters: NULL, or device uint64[4] that the call adds work counts to:
  * [0] pixel-splat pairs evaluated by the kernel, [1] pairs blended, [2] pairs
  * the plain per-pixel method evaluates (per pixel, its tile's entries up to
@@ -199,7 +216,8 @@ GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* mean
  * tile's entries up to the last of its pixels' stops).  Counting uses a
  * separate kernel variant. */
 GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                            const float* splats, const float* depths, const float* background,
                            const gs_settings* settings, float* image, float* final_T,
                            uint32_t* last_idx, float* out_depth, float* out_alpha,
@@ -213,7 +231,8 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
  * loss value (its summation order across tiles is not fixed).  The image
  * is not read back.  dL_dimage must not alias image or target. */
 GS_API gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                       const uint32_t* tile_ranges, const uint32_t* ids,
+                                       const uint32_t* tile_ranges,
+                                       const uint32_t* tile_order, const uint32_t* ids,
                                        const float* splats, const float* depths,
                                        const float* background, const gs_settings* settings,
                                        int32_t kind, const float* target, float* image,
@@ -243,7 +262,8 @@ GS_API gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int
  * gradient, [2] pairs the plain tile loop walks (256 x a tile's entries up
  * to its pixels' last blended one), [3] wavefront reductions. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges, const uint32_t* ids,
+                           const uint32_t* tile_ranges,
+                           const uint32_t* tile_order, const uint32_t* ids,
                            const float* splats, const uint32_t* offsets,
                            const uint32_t* tiles_touched, uint64_t num_instances,
                            const float* background, const gs_settings* settings,
@@ -310,6 +330,7 @@ GS_API gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const flo
  * the tile's own list, as in the single-camera call. */
 GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width,
                                           int32_t height, const uint32_t* tile_ranges,
+                                          const uint32_t* tile_order,
                                           const uint32_t* ids, const float* splats,
                                           const float* depths, const float* background,
                                           const gs_settings* settings, float* image,
@@ -322,6 +343,7 @@ GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t 
  * (visible rows only). */
 GS_API gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width,
                                           int32_t height, const uint32_t* tile_ranges,
+                                          const uint32_t* tile_order,
                                           const uint32_t* ids, const float* splats,
                                           const uint32_t* offsets, const uint32_t* tiles_touched,
                                           uint64_t num_instances, const float* background,
@@ -372,7 +394,8 @@ GS_API gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* mean
  * Gaussians off the list.  vis_ids / num_visible as gs_bin_and_sort_packed
  * returned them for the same frame (entries must be < N). */
 GS_API gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                         const uint32_t* tile_ranges, const uint32_t* ids,
+                                         const uint32_t* tile_ranges,
+                                         const uint32_t* tile_order, const uint32_t* ids,
                                          const float* splats, const uint32_t* offsets,
                                          const uint32_t* tiles_touched, uint64_t num_instances,
                                          const uint32_t* vis_ids, int64_t num_visible,

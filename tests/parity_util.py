@@ -41,18 +41,19 @@ def torch_cuda():
 
 def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
               loss_kind=None, target=None, backward=True, depth_alpha=False, capacity=None,
-              dL_dimage=None, absgrad=False, packed=False):
+              dL_dimage=None, absgrad=False, packed=False, schedule=True):
     """Run the five stages on the GPU; returns numpy arrays in the natural
     [N, ...] layout plus the raw Frame.  With ``packed`` the packed calls
     run, and their rows are scattered back to the [N, ...] layout (zeros off
-    the visible list); ``vis_ids`` and ``V`` are returned too."""
+    the visible list); ``vis_ids`` and ``V`` are returned too.  ``schedule``
+    selects the longest-tile-first compositing order (Frame's default)."""
     import torch
     from differentiable_rasterization_amd import raster
     g = raster.Gaussians.from_scene(scene, ld=ld)
     st = raster.default_settings(**(settings or {}))
     fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=capacity,
                       settings=st, background=background, with_depth_alpha=depth_alpha,
-                      packed=packed)
+                      packed=packed, schedule=schedule)
     fr.forward(g, cam)
     out = {}
     if backward:

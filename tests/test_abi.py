@@ -122,22 +122,22 @@ def test_raster_and_loss_reject_bad_arguments(lib):
     dummy = C.c_void_p(64)
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, dummy, dummy, None, bg, C.byref(st), dummy,
-                             dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # no tile ranges
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, C.c_void_p(68), None, bg, C.byref(st),
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, None, dummy, dummy, None, bg, C.byref(st),
                              dummy, dummy, dummy, None, None, None, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # no tile ranges
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, C.c_void_p(68), None, bg,
+                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # misaligned records
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, None, bg, C.byref(st), dummy,
-                             dummy, dummy, None, None, None, None)
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, None, dummy, None, bg, C.byref(st),
+                             dummy, dummy, dummy, None, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # ids needed when N > 0
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, dummy, dummy, None, bg, C.byref(st), dummy,
-                             dummy, dummy, dummy, None, None, None)
+    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, dummy, None, bg, C.byref(st),
+                             dummy, dummy, dummy, dummy, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # the depth output needs depths
 
     def bwd(offsets=dummy, M=10, cap=10, partials=dummy, grads=dummy, absgrad=0):
-        return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, dummy, dummy, offsets, dummy, M, bg,
-                                    C.byref(st), dummy, dummy, dummy, partials, cap, grads,
+        return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, None, dummy, dummy, offsets, dummy, M,
+                                    bg, C.byref(st), dummy, dummy, dummy, partials, cap, grads,
                                     absgrad, None, None)
     assert bwd(offsets=None) == raster.GS_ERR_INVALID_ARGUMENT     # offsets needed
     assert bwd(cap=9) == raster.GS_ERR_INVALID_ARGUMENT            # slots < instances
@@ -168,9 +168,9 @@ def test_packed_calls_reject_bad_arguments(lib):
     assert bas(ld=3) == raster.GS_ERR_INVALID_ARGUMENT
 
     def rbwd(V=2, vis=dummy, grads=dummy):
-        return lib.gs_rasterize_bwd_packed(4, 4, 64, 64, dummy, dummy, dummy, dummy, dummy, 10,
-                                           vis, V, bg, C.byref(st), dummy, dummy, dummy, dummy,
-                                           10, grads, 0, None, None)
+        return lib.gs_rasterize_bwd_packed(4, 4, 64, 64, dummy, None, dummy, dummy, dummy,
+                                           dummy, 10, vis, V, bg, C.byref(st), dummy, dummy, dummy,
+                                           dummy, 10, grads, 0, None, None)
     assert rbwd(V=5) == raster.GS_ERR_INVALID_ARGUMENT       # more rows than Gaussians
     assert rbwd(V=-1) == raster.GS_ERR_INVALID_ARGUMENT
     assert rbwd(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
@@ -257,14 +257,16 @@ def test_batched_calls_reject_bad_arguments(lib):
                                     dummy, dummy, dummy, dummy, 16, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # workspace too small
     bg = (C.c_float * 3)(0, 0, 0)
-    r = lib.gs_rasterize_fwd_batched(2, 10, 64, 64, None, dummy, dummy, None, bg, C.byref(st),
-                                     dummy, dummy, dummy, None, None, None, None)
+    r = lib.gs_rasterize_fwd_batched(2, 10, 64, 64, None, None, dummy, dummy, None, bg,
+                                     C.byref(st), dummy, dummy, dummy, None, None, None, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # no tile ranges
-    r = lib.gs_rasterize_bwd_batched(9, 10, 64, 64, *([dummy] * 5), 10, bg, C.byref(st),
-                                     dummy, dummy, dummy, dummy, 10, dummy, 0, None, None)
+    r = lib.gs_rasterize_bwd_batched(9, 10, 64, 64, dummy, None, *([dummy] * 4), 10, bg,
+                                     C.byref(st), dummy, dummy, dummy, dummy, 10, dummy, 0, None,
+                                     None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # too many cameras
-    r = lib.gs_rasterize_bwd_batched(2, 10, 64, 64, *([dummy] * 5), 11, bg, C.byref(st),
-                                     dummy, dummy, dummy, dummy, 10, dummy, 0, None, None)
+    r = lib.gs_rasterize_bwd_batched(2, 10, 64, 64, dummy, None, *([dummy] * 4), 11, bg,
+                                     C.byref(st), dummy, dummy, dummy, dummy, 10, dummy, 0, None,
+                                     None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # partials too small
     r = lib.gs_project_bwd_batched(2, cams, 10, 10, 0, *([dummy] * 4), C.byref(st), dummy,
                                    dummy, *([dummy] * 5), 2, None)
@@ -280,7 +282,7 @@ def test_fused_loss_rejects_bad_arguments(lib):
     bg = (C.c_float * 3)(0, 0, 0)
 
     def call(kind=1, target=other, dl=C.c_void_p(192)):
-        return lib.gs_rasterize_fwd_loss(4, 4, 64, 64, dummy, dummy, dummy, None, bg,
+        return lib.gs_rasterize_fwd_loss(4, 4, 64, 64, dummy, None, dummy, dummy, None, bg,
                                          C.byref(st), kind, target, dummy, dummy, dummy, None,
                                          None, dl, None, None, None)
     assert call(kind=2) == raster.GS_ERR_INVALID_ARGUMENT
@@ -288,6 +290,16 @@ def test_fused_loss_rejects_bad_arguments(lib):
     assert call(dl=None) == raster.GS_ERR_INVALID_ARGUMENT
     assert call(dl=dummy) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the image
     assert call(dl=other) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the target
+
+
+def test_tile_order_rejects_bad_arguments(lib):
+    dummy, other = C.c_void_p(64), C.c_void_p(128)
+    assert lib.gs_tile_order(0, 64, 64, dummy, other, None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_tile_order(9, 64, 64, dummy, other, None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_tile_order(1, 0, 64, dummy, other, None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_tile_order(1, 64, 64, None, other, None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_tile_order(1, 64, 64, dummy, None, None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert lib.gs_tile_order(1, 64, 64, dummy, dummy, None) == raster.GS_ERR_INVALID_ARGUMENT
 
 
 def test_densify_rejects_bad_arguments(lib):
