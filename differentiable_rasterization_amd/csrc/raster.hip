@@ -35,23 +35,35 @@ namespace gs {
 
 // Splat staged in LDS: mean, the conic's Cholesky factor scaled by
 // sqrt(log2(e)/2) (l11, l21, l22: the Gaussian is exp2(-(e1^2 + e2^2)) with
-// e1 = l11 dx + l21 dy, e2 = l22 dy), opacity, colour, depth.
+// e1 = l11 dx + l21 dy, e2 = l22 dy), opacity, colour, and z: the depth in
+// the forward, 1/opacity in the backward.
 struct SplatLds {
   float u, v, l11, l21, l22, o, r, g, b, z;
 };
 
-// Stage one splat record (three 16-byte loads of one 64-byte line) into LDS
-// and return the record's radius and footprint half-extents.
-__device__ inline void stage_splat(SplatLds& s, const float4* __restrict__ rec, int32_t& radius,
-                                   float& ex, float& ey) {
-  const float4 a = rec[0], b = rec[1], c = rec[2];
-  s.u = a.x; s.v = a.y; s.l11 = a.z; s.l21 = a.w;
-  s.l22 = b.x; s.o = b.y; s.r = b.z; s.g = b.w;
-  s.b = c.x; s.z = 0.0f;
-  radius = __float_as_int(c.y);
-  ex = c.z;
-  ey = c.w;
-}
+// A splat record (its first three 16-byte quarters, plus the depth when the
+// forward outputs depth) held in registers between its global load and its
+// staging into LDS; the forward fetches the next batch's records this way.
+struct RecordRegs {
+  float4 a, b, c;
+  float z;
+  __device__ inline void load(const float4* __restrict__ splats, const float* __restrict__ depths,
+                              uint32_t id, bool with_depth) {
+    const float4* r = splats + 4 * (size_t)id;
+    a = r[0];
+    b = r[1];
+    c = r[2];
+    z = with_depth ? depths[id] : 0.0f;
+  }
+  __device__ inline void stage(SplatLds& s, int32_t& radius, float& ex, float& ey) const {
+    s.u = a.x; s.v = a.y; s.l11 = a.z; s.l21 = a.w;
+    s.l22 = b.x; s.o = b.y; s.r = b.z; s.g = b.w;
+    s.b = c.x; s.z = z;
+    radius = __float_as_int(c.y);
+    ex = c.z;
+    ey = c.w;
+  }
+};
 
 // Workgroup -> tile mapping aware of the eight XCDs (each with its own L2):
 // workgroup b runs on XCD b % 8, so each XCD is handed whole 2x2 groups of
@@ -247,19 +259,29 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   uint32_t last = 0;
   bool done = !inside;
   uint32_t n_eval = 0, n_blend = 0, stop_at = 0;  // counters (kStats only)
+  // Each lane's record for the next batch is fetched from global memory
+  // while the current batch is composited (its index before the batch's
+  // compaction, the record itself after it), so a long list does not wait
+  // for two dependent global loads per batch.
+  RecordRegs rec;
+  if (start + (uint32_t)tid < end) rec.load(splats, depths, ids[start + tid], kDepth);
   for (uint32_t b = start; b < end; b += 256) {
     if (__syncthreads_count(done) == 256) break;
     const uint32_t j = b + (uint32_t)tid;
     uint32_t mask = 0u;
     if (j < end) {
-      const uint32_t id = ids[j];
       float ex, ey;
       int32_t rad;
-      stage_splat(s_sp[tid], splats + 4 * (size_t)id, rad, ex, ey);
-      if (kDepth) s_sp[tid].z = depths[id];
+      rec.stage(s_sp[tid], rad, ex, ey);
       mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
+    const uint32_t jn = j + 256u;
+    uint32_t next_id = jn < end ? ids[jn] : 0u;
     compact_bands(mask, s_list, s_cnt, s_wc);
+    // (an empty asm that takes the index: its first use stays here, after
+    // the compaction, so the wait for the index load is not hoisted above it)
+    asm volatile("" : "+v"(next_id));
+    if (jn < end) rec.load(splats, depths, next_id, kDepth);
     // wave-uniform trip count: the loop runs on scalar registers
     const int cnt = __builtin_amdgcn_readfirstlane((int)s_cnt[wave]);
     const uint32_t base = b - start + 1u;
@@ -362,8 +384,10 @@ __device__ inline void reduce_add(const float* f, float* dst, int stride) {
   const float s23 = swap_add32(f[2], f[3]);
   const float s45 = swap_add32(f[4], f[5]);
   const float s67 = swap_add32(f[6], f[7]);
-  const float s89 = swap_add32(f[8], kAbs ? f[9] : 0.0f);
-  const float sA = kAbs ? swap_add32(f[10], 0.0f) : 0.0f;
+  // without absgrad field 8 is paired with itself (its sums then fill both
+  // halves and every row; only row 0's total is used)
+  const float s89 = swap_add32(f[8], kAbs ? f[9] : f[8]);
+  const float sA = kAbs ? swap_add32(f[10], f[10]) : s89;
   // rows of t0: fields 0, 2, 1, 3; of t1: 4, 6, 5, 7; of t2: 8, 10, 9, -
   float t0 = swap_add16(s01, s23);
   float t1 = swap_add16(s45, s67);
@@ -383,18 +407,19 @@ __device__ inline void reduce_add(const float* f, float* dst, int stride) {
   }
 }
 
-// Gradient slots of one splat, in moment form: m dx, m dy, m dx^2, m dx dy,
-// m dy^2 with m = dL/dq, then dL/do and the three colour gradients.  The
-// mean and conic gradients follow after the reduction:
-//   dL/du = -2 (A Sx + B Sy), dL/dv = -2 (B Sx + C Sy),
-//   dL/dA = Sxx, dL/dB = 2 Sxy, dL/dC = Syy.
+// Gradient slots of one splat, in moment form: w dx, w dy, w dx^2, w dx dy,
+// w dy^2 with w = -2 dL/dq = alpha dL/dalpha, then dL/do and the three
+// colour gradients.  The mean and conic gradients follow after the
+// reduction (S the sums of the w moments):
+//   dL/du = A Sx + B Sy, dL/dv = B Sx + C Sy,
+//   dL/dA = -Sxx / 2, dL/dB = -Sxy, dL/dC = -Syy / 2.
 // With absgrad, two more: the per-pixel |dL/du| and |dL/dv| summed over the
 // pixels (the absolute-gradient statistic of densification).
 constexpr int kFields = 9;
 constexpr int kFieldsAbs = 11;
-// |dL/du| = 2 |m (A dx + B dy)| and A dx + B dy = l11 e1 / k^2 with the
-// record's factors scaled by k = sqrt(log2(e) / 2): 2 / k^2 = 4 ln 2
-constexpr float kAbsScale = 2.772588722239781f;
+// |dL/du| = |w (A dx + B dy)| and A dx + B dy = l11 e1 / k^2 with the
+// record's factors scaled by k = sqrt(log2(e) / 2): 1 / k^2 = 2 ln 2
+constexpr float kAbsScale = 1.3862943611198906f;
 
 // Slot of Gaussian `id`'s instance for tile (tx, ty): its offset plus the
 // tile's row-major index inside the Gaussian's rect.
@@ -454,8 +479,9 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     g1 = dL_dimage[3 * p + 1];
     g2 = dL_dimage[3 * p + 2];
   }
-  // colour accumulated behind the current splat, background included
-  float R0 = T * bg0, R1 = T * bg1, R2 = T * bg2;
+  // S = sum_c dL/dC_c R_c, with R the colour accumulated behind the current
+  // splat, background included
+  float S = T * fmaf(g0, bg0, fmaf(g1, bg1, g2 * bg2));
   if (tid == 0) s_maxlast = 0;
   __syncthreads();
   if (last) atomicMax(&s_maxlast, last);
@@ -488,11 +514,16 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     float cA = 0.0f, cB = 0.0f, cC = 0.0f;  // raw conic of the splat this thread stages
     if (tid < n) {
       const uint32_t my_id = ids[b_end - 1u - (uint32_t)tid];  // slot k = tid: back to front
-      const float4* rec = splats + 4 * (size_t)my_id;
       my_off = offsets[my_id];
+      RecordRegs rec;
+      rec.load(splats, nullptr, my_id, false);
       float ex, ey;
-      stage_splat(s_sp[tid], rec, my_rad, ex, ey);
-      const float4 d = rec[3];
+      rec.stage(s_sp[tid], my_rad, ex, ey);
+      // the backward keeps 1/o in the depth slot (o >= alpha_min > 0 for
+      // any splat that blends)
+      const float o = rec.b.y;
+      s_sp[tid].z = o > 0.0f ? 1.0f / o : 0.0f;
+      const float4 d = splats[4 * (size_t)my_id + 3];
       cA = d.x; cB = d.y; cC = d.z;
       mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
@@ -524,17 +555,16 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       f[6] = g0 * wgt;
       f[7] = g1 * wgt;
       f[8] = g2 * wgt;
-      // dC/dalpha = c T - R / (1 - alpha)
-      float dLda = g0 * fmaf(s.r, T, -R0 * rom);
-      dLda = fmaf(g1, fmaf(s.g, T, -R1 * rom), dLda);
-      dLda = fmaf(g2, fmaf(s.b, T, -R2 * rom), dLda);
-      R0 = fmaf(s.r, wgt, R0);
-      R1 = fmaf(s.g, wgt, R1);
-      R2 = fmaf(s.b, wgt, R2);
+      // dC_c/dalpha = c_c T - R_c / (1 - alpha), so with gc = sum_c dL/dC_c c_c:
+      // dL/dalpha = gc T - S / (1 - alpha), and S grows by gc wgt
+      const float gc = fmaf(g0, s.r, fmaf(g1, s.g, g2 * s.b));
+      const float dLda = fmaf(gc, T, -S * rom);
+      S = fmaf(gc, wgt, S);
       const bool geo = hit & !clamped;
-      // q = A dx^2 + 2B dx dy + C dy^2, alpha = o exp(-q/2): dL/dq = -alpha/2 dL/dalpha
-      const float m = geo ? (-0.5f * alpha) * dLda : 0.0f;
-      f[5] = geo ? dLda * G : 0.0f;
+      // q = A dx^2 + 2B dx dy + C dy^2, alpha = o exp(-q/2): dL/dq = -alpha/2
+      // dL/dalpha = -w/2; dL/do = G dL/dalpha = w / o (s.z holds 1/o)
+      const float m = geo ? alpha * dLda : 0.0f;
+      f[5] = m * s.z;
       const float mx = m * dx, my = m * dy;
       f[0] = mx;
       f[1] = my;
@@ -593,13 +623,13 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
 #pragma unroll
       for (int q = 0; q < kF; ++q) acc[q] = s_acc[0][q][tid] + s_acc[1][q][tid];
       // moments -> gradients of u, v and the conic
-      const float gu = -2.0f * fmaf(cA, acc[0], cB * acc[1]);
-      const float gv = -2.0f * fmaf(cB, acc[0], cC * acc[1]);
+      const float gu = fmaf(cA, acc[0], cB * acc[1]);
+      const float gv = fmaf(cB, acc[0], cC * acc[1]);
       const uint64_t slot =
           instance_slot(s_sp[tid].u, s_sp[tid].v, my_rad, my_off, tx, ty, gx, gy);
       if (slot < capacity) {
-        partials[4 * slot + 0] = make_float4(gu, gv, acc[2], 2.0f * acc[3]);
-        partials[4 * slot + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        partials[4 * slot + 0] = make_float4(gu, gv, -0.5f * acc[2], -acc[3]);
+        partials[4 * slot + 1] = make_float4(-0.5f * acc[4], acc[5], acc[6], acc[7]);
         partials[4 * slot + 2] =
             make_float4(acc[8], kAbs ? acc[kF - 2] : 0.0f, kAbs ? acc[kF - 1] : 0.0f, 0.0f);
       }
