@@ -34,14 +34,14 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # VALU slots of the compositing inner loops, counted in the gfx950 assembly
 # of raster.hip (a quarter-rate v_exp_f32 / v_rcp_f32 counts four slots):
-#   forward: 49 VALU and two v_exp_f32 per two unrolled pairs -> 27.5 / pair;
-#   backward: 25 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (31
-#   slots); a wavefront with a hit on the splat adds 21 VALU of gradient
-#   terms and 36 of the nine-field reduction (lane swaps + DPP row scan).
-FWD_SLOTS_PER_PAIR = 27.5
+#   forward: 48 VALU and two v_exp_f32 per two unrolled pairs -> 28 / pair;
+#   backward: 23 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (31
+#   slots); a wavefront with a hit on the splat adds 13 VALU of gradient
+#   terms and 35 of the nine-field reduction (lane swaps + DPP row scan).
+FWD_SLOTS_PER_PAIR = 28.0
 BWD_EVAL_SLOTS = 31.0
-BWD_GRAD_SLOTS = 21.0
-BWD_REDUCE_SLOTS = 36.0
+BWD_GRAD_SLOTS = 13.0
+BWD_REDUCE_SLOTS = 35.0
 BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
 
 
