@@ -134,6 +134,40 @@ __device__ inline uint32_t quad_mask(const SplatLds& s, float ex, float ey, int 
          ((uint32_t)(c1 & r1) << 3);
 }
 
+// The forward's pixel layout: wave w covers quadrant (w & 1, w >> 1) as in
+// the backward, but each 16-lane row r of it a 4x4 block of that quadrant,
+// at (r & 1, r >> 1) in 4-pixel steps; lane j of the row takes pixel
+// (j & 3, j >> 2) of the block.  Block index wave * 4 + r.
+__device__ inline int sub_px(int tid) {
+  return ((tid >> 6) & 1) * 8 + ((tid >> 4) & 1) * 4 + (tid & 3);
+}
+__device__ inline int sub_py(int tid) {
+  return (tid >> 7) * 8 + ((tid >> 5) & 1) * 4 + ((tid >> 2) & 3);
+}
+
+// Which of the tile's sixteen 4x4 blocks (numbered as above) can hold a
+// pixel centre where the splat reaches alpha_min, from the record's padded
+// footprint half-extents.
+__device__ inline uint32_t sub_mask(const SplatLds& s, float ex, float ey, int tx0, int ty0) {
+  if (!(ex >= 0.0f)) return 0u;  // opacity below alpha_min
+  const float xa = (float)tx0 + 0.5f, ya = (float)ty0 + 0.5f;
+  uint32_t cx = 0u, cy = 0u;  // 4-pixel column and row bands the box reaches
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = xa + (float)(4 * i), y0 = ya + (float)(4 * i);
+    cx |= (uint32_t)(s.u + ex >= x0 && s.u - ex <= x0 + 3.0f) << i;
+    cy |= (uint32_t)(s.v + ey >= y0 && s.v - ey <= y0 + 3.0f) << i;
+  }
+  uint32_t m = 0u;
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const int w = b >> 2, r = b & 3;
+    const int bx = (w & 1) * 2 + (r & 1), by = (w >> 1) * 2 + (r >> 1);
+    m |= ((cx >> bx) & (cy >> by) & 1u) << b;
+  }
+  return m;
+}
+
 __device__ inline uint64_t lanemask_lt64() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -142,27 +176,28 @@ __device__ inline uint64_t lanemask_lt64() {
 // Order-preserving compaction of the batch slots by quadrant: s_list[b] receives
 // the slots whose mask has bit b, in ascending slot order; s_cnt[b] their
 // number.  Called by all 256 threads.
-__device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[256], uint32_t* s_cnt,
+template <int NB, int LD>
+__device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[LD], uint32_t* s_cnt,
                                      uint32_t (*s_wc)[4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt = lanemask_lt64();
-  uint32_t pre[4];
+  uint32_t pre[NB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const uint64_t bal = __ballot((mask >> b) & 1u);
     pre[b] = (uint32_t)__popcll(bal & lt);
     if (lane == 0) s_wc[b][wave] = (uint32_t)__popcll(bal);
   }
   __syncthreads();
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < NB; ++b) {
     if ((mask >> b) & 1u) {
       uint32_t off = pre[b];
       for (int w = 0; w < wave; ++w) off += s_wc[b][w];
       s_list[b][off] = (uint8_t)tid;
     }
   }
-  if (tid < 4) s_cnt[tid] = s_wc[tid][0] + s_wc[tid][1] + s_wc[tid][2] + s_wc[tid][3];
+  if (tid < NB) s_cnt[tid] = s_wc[tid][0] + s_wc[tid][1] + s_wc[tid][2] + s_wc[tid][3];
   __syncthreads();
 }
 
@@ -239,17 +274,20 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     const float* __restrict__ target, float* __restrict__ dl, float* __restrict__ loss,
     const uint32_t* __restrict__ order) {
   __shared__ SplatLds s_sp[256];
-  __shared__ uint8_t s_list[4][256];
-  __shared__ uint32_t s_cnt[4];
-  __shared__ uint32_t s_wc[4][4];
+  // rows padded to 260 bytes: the four rows a wave reads at once sit in
+  // different LDS banks
+  __shared__ uint8_t s_list[16][260];
+  __shared__ uint32_t s_cnt[16];
+  __shared__ uint32_t s_wc[16][4];
   int tx, ty;
   const int gy = grid_dim(H);
   if (!schedule_tile(order, gx, gy, tx, ty)) return;
   // camera blockIdx.y of a batch: its tiles follow the earlier cameras'
   // (gx * gy each) and its pixels their images
   const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int px = tx * kTile + quad_px(tid), py = ty * kTile + quad_py(tid);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sb = tid >> 4;  // this lane's 4x4 block: each row of the wave walks its own list
+  const int px = tx * kTile + sub_px(tid), py = ty * kTile + sub_py(tid);
   const bool inside = px < W && py < H;
   const float fpx = (float)px + 0.5f, fpy = (float)py + 0.5f;
   const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
@@ -273,32 +311,37 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
       float ex, ey;
       int32_t rad;
       rec.stage(s_sp[tid], rad, ex, ey);
-      mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
+      mask = sub_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
     }
     const uint32_t jn = j + 256u;
     uint32_t next_id = jn < end ? ids[jn] : 0u;
-    compact_bands(mask, s_list, s_cnt, s_wc);
+    compact_bands<16, 260>(mask, s_list, s_cnt, s_wc);
     // (an empty asm that takes the index: its first use stays here, after
     // the compaction, so the wait for the index load is not hoisted above it)
     asm volatile("" : "+v"(next_id));
     if (jn < end) rec.load(splats, depths, next_id, kDepth);
-    // wave-uniform trip count: the loop runs on scalar registers
-    const int cnt = __builtin_amdgcn_readfirstlane((int)s_cnt[wave]);
+    // each row walks its block's list; the wave runs for the longest of its
+    // four (wave-uniform trip count, on scalar registers)
+    const int my_cnt = (int)s_cnt[sb];
+    const int c01 = max(__builtin_amdgcn_readlane(my_cnt, 0), __builtin_amdgcn_readlane(my_cnt, 16));
+    const int c23 = max(__builtin_amdgcn_readlane(my_cnt, 32), __builtin_amdgcn_readlane(my_cnt, 48));
+    const int cnt = max(c01, c23);
     const uint32_t base = b - start + 1u;
     if (__ballot(!done) == 0ull) continue;
     for (int i = 0; i < cnt; ++i) {
-      const int k = s_list[wave][i];
+      const bool act = i < my_cnt;  // past the end of this row's list: read, ignored
+      const int k = s_list[sb][i];
       const SplatLds& s = s_sp[k];
       const float dx = fpx - s.u, dy = fpy - s.v;
       const float p2 = splat_power2(s, dx, dy);
       const float oG = s.o * __builtin_amdgcn_exp2f(p2);
       const float alpha = oG > amax ? amax : oG;
-      const bool ok = !done & !(alpha < amin);
+      const bool ok = act & !done & !(alpha < amin);
       const float Tn = T * (1.0f - alpha);
       const bool low = Tn < Tmin;
       const bool blend = ok & !low;
       if (kStats) {
-        n_eval += 1u;
+        n_eval += act ? 1u : 0u;
         n_blend += blend ? 1u : 0u;
         stop_at = (ok & low) ? base + (uint32_t)k : stop_at;
       }
@@ -533,7 +576,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       s_acc[0][q][tid] = 0.0f;
       s_acc[1][q][tid] = 0.0f;
     }
-    compact_bands(mask, s_list, s_cnt, s_wc);
+    compact_bands<4, 256>(mask, s_list, s_cnt, s_wc);
     const int cnt_w = __builtin_amdgcn_readfirstlane((int)s_cnt[wave]);
     // batch slot k holds list position rel = b_end - 1 - start - k; the pixel
     // blended it only if rel < last, i.e. k > kthr
