@@ -5,16 +5,18 @@
 // a wave covers one 8x8 quadrant of the tile.  The tile's depth-sorted list
 // is walked in batches of 256 splats that the workgroup first stages into
 // LDS (one gather per lane), after which every lane reads the batch with
-// broadcast LDS loads.  The work is bound by VALU issue (about a dozen
-// operations per pixel-splat pair plus one transcendental), not by memory,
-// so nothing here is shaped for MFMA.  The forward stops the whole tile as
-// soon as every pixel has terminated.
+// LDS loads.  The work is bound by VALU issue (about a dozen operations per
+// pixel-splat pair plus one or two transcendentals), not by memory, so
+// nothing here is shaped for MFMA.  The forward stops the whole tile as soon
+// as every pixel has terminated.  With a schedule (tile_order_kernel, below)
+// workgroups take the tiles with the longest lists first.
 //
-// Each staged batch is compacted per wavefront: a splat enters a wave's list
-// only if its alpha >= alpha_min footprint (a padded, conservative box) can
-// reach that wave's quadrant, so waves skip splats that cannot touch them;
-// the inner loops are branch-free.  (Square 8x8 quadrants meet ~10% fewer
-// small splats than 16x4 bands of the same area.)
+// Each staged batch is compacted: a splat enters a list only if its
+// alpha >= alpha_min footprint (a padded, conservative box) can reach the
+// list's pixels, so lanes skip splats that cannot touch them; the inner
+// loops are branch-free.  The backward keeps one list per wave (its 8x8
+// quadrant); the forward one per 4x4 block, each 16-lane row of a wave
+// walking its own block's list.
 //
 // The backward walks the same lists back to front from each pixel's last
 // blended entry.  Per splat each wave reduces its 64 pixels' nine gradient
