@@ -271,7 +271,7 @@ def graph_bench(args, scene, gcams, targets, kind, capacity):
     over = any(fr.check_counts()[1] for _ in [0])
     return {"value": round(args.steps / dt, 2), "ms_per_step": round(1e3 * dt / args.steps, 4),
             "form": "fwd+bwd frame per pose as a HIP graph, binning without the read-back",
-            "overflow": bool(over)}
+            "capacity": int(capacity), "overflow": bool(over)}
 
 
 def train_step_bench(args, scene, gcams, targets, capacity):
@@ -509,8 +509,13 @@ def main():
                                                                    fr.capacity)
     batch_line = None if args.no_train_step else fwd_batch_bench(args, scene, cams, args.batch,
                                                                   depth_alpha=False)
+    # the graph frames bin without reading M back, so their grids are sized
+    # for the buffers' capacity: give them buffers 25% above the largest M
+    # seen over the poses (the eager frame's 4N would launch 2.7x the sort
+    # workgroups, most of them idle)
+    graph_cap = int(1.25 * max(s_["M"] for s_ in stats)) + 8192
     graph_line = None if args.no_train_step else graph_bench(args, scene, gcams, targets, kind,
-                                                              fr.capacity)
+                                                              graph_cap)
     if not args.packed:
         # the same steps through the packed calls (visible list, sparse
         # gradient rows), reported beside the dense headline
