@@ -331,8 +331,11 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     const uint32_t base = b - start + 1u;
     if (__ballot(!done) == 0ull) continue;
     for (int i = 0; i < cnt; ++i) {
-      const bool act = i < my_cnt;  // past the end of this row's list: read, ignored
-      const int k = s_list[sb][i];
+      // past the end of this row's list the lane evaluates slot 0, a record
+      // of this batch, and ignores it (a stale slot could hold a non-finite
+      // record, and 0 * NaN would reach the sums)
+      const bool act = i < my_cnt;
+      const int k = act ? (int)s_list[sb][i] : 0;
       const SplatLds& s = s_sp[k];
       const float dx = fpx - s.u, dy = fpy - s.v;
       const float p2 = splat_power2(s, dx, dy);
