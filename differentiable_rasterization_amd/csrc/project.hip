@@ -388,20 +388,209 @@ __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, 
 // splats, condition numbers 1e4-1e5) loses about u times the condition
 // number in fp32; the kernel moves ~300 bytes per Gaussian against a few
 // hundred fp64 operations, so it stays memory-bound.
-//
+
+// The SH side of one camera: view direction d (and 1 / distance), the
+// colour clamp decision in fp64, and the colour gradient gcol that passes it.
+template <int DEG>
+__device__ inline void sh_view(const Cam& cam, const float pm[3], const float* shv,
+                               float sh_offset, const float gin[3], double d[3], double& iL,
+                               float gcol[3]) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  double cc[3];
+  for (int j = 0; j < 3; ++j)
+    cc[j] = -(((double)cam.R[j] * (double)cam.t[0] + (double)cam.R[3 + j] * (double)cam.t[1]) +
+              (double)cam.R[6 + j] * (double)cam.t[2]);
+  const double dir[3] = {(double)pm[0] - cc[0], (double)pm[1] - cc[1], (double)pm[2] - cc[2]};
+  iL = 1.0 / sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+  for (int j = 0; j < 3; ++j) d[j] = dir[j] * iL;
+  double Y[16];
+  sh_basis64(DEG, d[0], d[1], d[2], Y);
+  double raw[3] = {(double)sh_offset, (double)sh_offset, (double)sh_offset};
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) raw[ch] = fma(Y[j], (double)shv[j * 3 + ch], raw[ch]);
+  for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0f : gin[ch];
+}
+
+// SH coefficient gradients Y_j(d) gcol (fp32 products, handed to `sink` as
+// (coefficient index, value)) and the view direction's share of the mean
+// gradient, vterm.
+template <int DEG, typename Sink>
+__device__ inline void sh_grads(const double d[3], double iL, const float gcol[3],
+                                const float* shv, Sink sink, double vterm[3]) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  float Yf[16];
+  sh_basis(DEG, (float)d[0], (float)d[1], (float)d[2], Yf);
+  double gd[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    double wj = 0.0;
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) {
+      sink(j * 3 + ch, Yf[j] * gcol[ch]);
+      wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
+    }
+    if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
+  }
+  const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+  for (int e = 0; e < 3; ++e) vterm[e] = (gd[e] - d[e] * dd) * iL;
+}
+
+// The geometry chain of one camera in fp64: mean (with the view-direction
+// term vterm added before rounding), scale and quaternion gradients.
+// r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1.x = dL/dC.
+__device__ inline void geom_grads(const Cam& cam, const Settings& st, const float pm[3],
+                                  const float ps[3], const float pq[4], float4 r0, float4 r1,
+                                  const double vterm[3], float om[3], float os[3], float oq[4]) {
+  const double m[3] = {pm[0], pm[1], pm[2]};
+  const double s[3] = {ps[0], ps[1], ps[2]};
+  const double q[4] = {pq[0], pq[1], pq[2], pq[3]};
+  double W[9];
+  for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
+  const double fx = cam.fx, fy = cam.fy;
+  const double tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + (double)cam.t[0];
+  const double ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + (double)cam.t[1];
+  const double tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + (double)cam.t[2];
+
+  // unit quaternion, rotation, M = R diag(s), Sigma = M M^T
+  const double n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
+  // (fp64 reciprocals stand in for divisions: their rounding is far below
+  // the fp32 outputs')
+  const double nr = sqrt(n2), inr = 1.0 / nr;
+  const double w = q[0] * inr, x = q[1] * inr, y = q[2] * inr, z = q[3] * inr;
+  double Rq[9];
+  Rq[0] = 1.0 - 2.0 * (y * y + z * z);
+  Rq[1] = 2.0 * (x * y - w * z);
+  Rq[2] = 2.0 * (x * z + w * y);
+  Rq[3] = 2.0 * (x * y + w * z);
+  Rq[4] = 1.0 - 2.0 * (x * x + z * z);
+  Rq[5] = 2.0 * (y * z - w * x);
+  Rq[6] = 2.0 * (x * z - w * y);
+  Rq[7] = 2.0 * (y * z + w * x);
+  Rq[8] = 1.0 - 2.0 * (x * x + y * y);
+  double M[9];
+  for (int r = 0; r < 3; ++r)
+    for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
+  double Sf[9];
+  for (int r = 0; r < 3; ++r)
+    for (int j = r; j < 3; ++j) {
+      const double v = (M[r * 3] * M[j * 3] + M[r * 3 + 1] * M[j * 3 + 1]) +
+                       M[r * 3 + 2] * M[j * 3 + 2];
+      Sf[r * 3 + j] = v;
+      Sf[j * 3 + r] = v;
+    }
+
+  // EWA Jacobian with the fov clamp, T = J W, 2D covariance and conic
+  const double itz = 1.0 / tz, itz2 = itz * itz, itz3 = itz2 * itz;
+  const double txz = tx * itz, tyz = ty * itz;
+  const double limx = (double)st.fov_clamp * ((0.5 * (double)cam.W) / fx);
+  const double limy = (double)st.fov_clamp * ((0.5 * (double)cam.H) / fy);
+  const bool clampx = (txz > limx) || (txz < -limx);
+  const bool clampy = (tyz > limy) || (tyz < -limy);
+  const double xc = (clampx ? (txz > 0.0 ? limx : -limx) : txz) * tz;
+  const double yc = (clampy ? (tyz > 0.0 ? limy : -limy) : tyz) * tz;
+  const double J00 = fx * itz, J02 = -(fx * xc * itz2);
+  const double J11 = fy * itz, J12 = -(fy * yc * itz2);
+  double Tm[6];
+  for (int j = 0; j < 3; ++j) {
+    Tm[j] = J00 * W[j] + J02 * W[6 + j];
+    Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
+  }
+  double ST0[3], ST1[3];
+  for (int r = 0; r < 3; ++r) {
+    ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
+    ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
+  }
+  const double a = (Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2]) + (double)st.eps2d;
+  const double b = Tm[0] * ST1[0] + Tm[1] * ST1[1] + Tm[2] * ST1[2];
+  const double c = (Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2]) + (double)st.eps2d;
+  const double idet = 1.0 / (a * c - b * b);
+  const double A = c * idet, B = -(b * idet), C = a * idet;
+
+  // conic = Sigma2D^-1: dL/dSigma2D = -conic G conic, G = [[gA, gB/2], [gB/2, gC]]
+  const double gA = r0.z, gB = r0.w, gC = r1.x;
+  const double ga = -(gA * A * A + gB * A * B + gC * B * B);
+  const double gb = -(2.0 * gA * A * B + gB * (A * C + B * B) + 2.0 * gC * B * C);
+  const double gc = -(gA * B * B + gB * B * C + gC * C * C);
+
+  // Sigma2D = T Sigma T^T: dL/dSigma = T^T G2 T, dL/dT = 2 G2 T Sigma
+  double gT0[3], gT1[3];
+  for (int r = 0; r < 3; ++r) {
+    gT0[r] = 2.0 * ga * ST0[r] + gb * ST1[r];
+    gT1[r] = gb * ST0[r] + 2.0 * gc * ST1[r];
+  }
+  double gJ00 = 0.0, gJ02 = 0.0, gJ11 = 0.0, gJ12 = 0.0;
+  for (int j = 0; j < 3; ++j) {
+    gJ00 += gT0[j] * W[j];
+    gJ02 += gT0[j] * W[6 + j];
+    gJ11 += gT1[j] * W[3 + j];
+    gJ12 += gT1[j] * W[6 + j];
+  }
+  double gt[3] = {0.0, 0.0, 0.0};
+  gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
+  if (clampx) {
+    gt[2] += gJ02 * (fx * (txz > 0.0 ? limx : -limx) * itz2);
+  } else {
+    gt[0] += gJ02 * (-fx * itz2);
+    gt[2] += gJ02 * (2.0 * fx * tx * itz3);
+  }
+  if (clampy) {
+    gt[2] += gJ12 * (fy * (tyz > 0.0 ? limy : -limy) * itz2);
+  } else {
+    gt[1] += gJ12 * (-fy * itz2);
+    gt[2] += gJ12 * (2.0 * fy * ty * itz3);
+  }
+  const double gu = r0.x, gv = r0.y;
+  gt[0] += gu * fx * itz;
+  gt[2] += gu * (-fx * tx * itz2);
+  gt[1] += gv * fy * itz;
+  gt[2] += gv * (-fy * ty * itz2);
+  double gm[3];
+  for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
+
+  // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M with
+  // G = dL/dSigma = ga T0^T T0 + gb T0^T T1 + gc T1^T T1 (formed row by row)
+  double gs[3] = {0.0, 0.0, 0.0}, gR[9];
+  for (int r = 0; r < 3; ++r) {
+    double Gr[3];
+    for (int j = 0; j < 3; ++j)
+      Gr[j] = 2.0 * (ga * Tm[r] * Tm[j] + gc * Tm[3 + r] * Tm[3 + j]) +
+              gb * (Tm[r] * Tm[3 + j] + Tm[3 + r] * Tm[j]);
+    for (int k = 0; k < 3; ++k) {
+      const double acc = (Gr[0] * M[k] + Gr[1] * M[3 + k]) + Gr[2] * M[6 + k];
+      gs[k] += acc * Rq[r * 3 + k];
+      gR[r * 3 + k] = acc * s[k];
+    }
+  }
+  double gqn[4];
+  gqn[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
+  gqn[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
+           4.0 * x * (gR[4] + gR[8]);
+  gqn[2] = 2.0 * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
+           4.0 * y * (gR[0] + gR[8]);
+  gqn[3] = 2.0 * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
+           4.0 * z * (gR[0] + gR[4]);
+  const double dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
+  oq[0] = (float)((gqn[0] - w * dot) * inr);
+  oq[1] = (float)((gqn[1] - x * dot) * inr);
+  oq[2] = (float)((gqn[2] - y * dot) * inr);
+  oq[3] = (float)((gqn[3] - z * dot) * inr);
+  for (int k = 0; k < 3; ++k) os[k] = (float)gs[k];
+
+  for (int k = 0; k < 3; ++k) om[k] = (float)(gm[k] + vterm[k]);
+}
+
 // Packed form (kPacked): row r handles Gaussian vis_ids[r]; its 2D gradient
 // record is row r of grads2d and its gradients go to row r of the output
 // planes (leading dimension ldo), so nothing is written for Gaussians off
 // the list.  Otherwise row r is Gaussian r and ldo = ld.
-// Batched form (kBatched): cameras 0 .. ncams-1 in turn, radii [c][ld] and
-// records [c * ld + i]; camera c > 0 adds to what the cameras before wrote,
-// so the outputs are the sum over the cameras that see the Gaussian.
-template <int DEG, bool kPacked, bool kBatched>
+template <int DEG, bool kPacked>
 __global__ __launch_bounds__(256) void project_bwd_kernel(
     int64_t N, int64_t ld, const uint32_t* __restrict__ vis_ids, int64_t ldo,
     const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ sh, CamBatch cams, int ncams, Settings st,
+    const float* __restrict__ sh, Cam cam, Settings st,
     const int32_t* __restrict__ radii, const float4* __restrict__ grads2d,
     float* __restrict__ o_means, float* __restrict__ o_scales, float* __restrict__ o_quats,
     float* __restrict__ o_opac, float* __restrict__ o_sh, int accumulate) {
@@ -409,18 +598,16 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= N) return;
   const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
-  const int nc = kBatched ? ncams : 1;
-  bool anyvis = false;
-  for (int c = 0; c < nc; ++c) anyvis |= radii[(int64_t)c * ld + i] > 0;
-  // every parameter load of a visible lane is issued here, ahead of the
-  // fp64 chain, so that each lane keeps its whole working set in flight
-  // (the kernel runs at two waves per SIMD)
+  const bool vis = radii[i] > 0;
+  // every load of a visible lane (parameters, its 2D gradient record, all 3K
+  // SH coefficients) is issued here, ahead of the fp64 chain, so that each
+  // lane keeps its whole working set in flight (the kernel runs at two
+  // waves per SIMD)
   float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
-  // one camera: its 2D gradient record is loaded with the parameters
-  float4 s0 = make_float4(0, 0, 0, 0), s1 = s0, s2 = s0;
+  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
 #pragma unroll
   for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
-  if (anyvis) {
+  if (vis) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       pm[k] = means[(int64_t)k * ld + i];
@@ -428,230 +615,156 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
-    if (!kBatched) {
-      s0 = grads2d[4 * r + 0];
-      s1 = grads2d[4 * r + 1];
-      s2 = grads2d[4 * r + 2];
-    }
+    r0 = grads2d[4 * r + 0];
+    r1 = grads2d[4 * r + 1];
+    r2 = grads2d[4 * r + 2];
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
   }
-  for (int c = 0; c < nc; ++c) {
-  const Cam cam = cams.c[c];
-  const bool vis = radii[(int64_t)c * ld + i] > 0;
-  float4 r0 = s0, r1 = s1, r2 = s2;
-  if (kBatched && vis) {
-    const int64_t rr = (int64_t)c * ld + r;
-    r0 = grads2d[4 * rr + 0];
-    r1 = grads2d[4 * rr + 1];
-    r2 = grads2d[4 * rr + 2];
-  }
-  const int acc = accumulate | (c > 0 ? 1 : 0);
   // culled Gaussians get zeros (overwrite) or are left alone (accumulate);
   // both kinds of lanes store through the same instructions below, so a
   // cache line of a plane is written once
-  const bool store = vis || !acc;
+  const bool store = vis || !accumulate;
 
   // Phase 1, the SH side (done first so that the 3K SH registers are free
-  // before the fp64 geometry chain): view direction, the colour's clamp
-  // decision (fp64), SH coefficient gradients (fp32 products; zeros where
-  // culled) and the view direction's share of the mean gradient.
+  // before the fp64 geometry chain).
   double d[3] = {0.0, 0.0, 1.0}, iL = 1.0, vterm[3] = {0.0, 0.0, 0.0};
   float gcol[3] = {0.0f, 0.0f, 0.0f};
   if (vis) {
-    double cc[3];
-    for (int j = 0; j < 3; ++j)
-      cc[j] = -(((double)cam.R[j] * (double)cam.t[0] + (double)cam.R[3 + j] * (double)cam.t[1]) +
-                (double)cam.R[6 + j] * (double)cam.t[2]);
-    const double dir[3] = {(double)pm[0] - cc[0], (double)pm[1] - cc[1], (double)pm[2] - cc[2]};
-    iL = 1.0 / sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-    for (int j = 0; j < 3; ++j) d[j] = dir[j] * iL;
-    double Y[16];
-    sh_basis64(DEG, d[0], d[1], d[2], Y);
-    double raw[3] = {(double)st.sh_offset, (double)st.sh_offset, (double)st.sh_offset};
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-#pragma unroll
-      for (int ch = 0; ch < 3; ++ch) raw[ch] = fma(Y[j], (double)shv[j * 3 + ch], raw[ch]);
     const float gin[3] = {r1.z, r1.w, r2.x};
-    for (int ch = 0; ch < 3; ++ch) gcol[ch] = raw[ch] < 0.0 ? 0.0f : gin[ch];
+    sh_view<DEG>(cam, pm, shv, st.sh_offset, gin, d, iL, gcol);
   }
-  if (store) {
-    float Yf[16];
-    sh_basis(DEG, (float)d[0], (float)d[1], (float)d[2], Yf);
-    double gd[3] = {0.0, 0.0, 0.0};
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      double wj = 0.0;
-#pragma unroll
-      for (int ch = 0; ch < 3; ++ch) {
-        const int64_t p = (int64_t)(j * 3 + ch) * ldo + r;
-        const float gval = Yf[j] * gcol[ch];
-        o_sh[p] = acc ? o_sh[p] + gval : gval;
-        wj = fma((double)gcol[ch], (double)shv[j * 3 + ch], wj);
-      }
-      if (j > 0) sh_basis_grad_acc64(j, wj, d[0], d[1], d[2], gd);
-    }
-    const double dd = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
-    for (int e = 0; e < 3; ++e) vterm[e] = (gd[e] - d[e] * dd) * iL;
-  }
+  if (store)
+    sh_grads<DEG>(
+        d, iL, gcol, shv,
+        [&](int k, float g) {
+          const int64_t p = (int64_t)k * ldo + r;
+          o_sh[p] = accumulate ? o_sh[p] + g : g;
+        },
+        vterm);
 
   // Phase 2, the geometry chain in fp64.
   float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
   float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
   if (vis) {
-    // r0 = (dL/du, dL/dv, dL/dA, dL/dB), r1 = (dL/dC, dL/do, dL/dr, dL/dg), r2.x = dL/db
     oo = r1.y;
-    const double m[3] = {pm[0], pm[1], pm[2]};
-    const double s[3] = {ps[0], ps[1], ps[2]};
-    const double q[4] = {pq[0], pq[1], pq[2], pq[3]};
-    double W[9];
-    for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
-    const double fx = cam.fx, fy = cam.fy;
-    const double tx = ((W[0] * m[0] + W[1] * m[1]) + W[2] * m[2]) + (double)cam.t[0];
-    const double ty = ((W[3] * m[0] + W[4] * m[1]) + W[5] * m[2]) + (double)cam.t[1];
-    const double tz = ((W[6] * m[0] + W[7] * m[1]) + W[8] * m[2]) + (double)cam.t[2];
-
-    // unit quaternion, rotation, M = R diag(s), Sigma = M M^T
-    const double n2 = ((q[0] * q[0] + q[1] * q[1]) + q[2] * q[2]) + q[3] * q[3];
-    // (fp64 reciprocals stand in for divisions: their rounding is far below
-    // the fp32 outputs')
-    const double nr = sqrt(n2), inr = 1.0 / nr;
-    const double w = q[0] * inr, x = q[1] * inr, y = q[2] * inr, z = q[3] * inr;
-    double Rq[9];
-    Rq[0] = 1.0 - 2.0 * (y * y + z * z);
-    Rq[1] = 2.0 * (x * y - w * z);
-    Rq[2] = 2.0 * (x * z + w * y);
-    Rq[3] = 2.0 * (x * y + w * z);
-    Rq[4] = 1.0 - 2.0 * (x * x + z * z);
-    Rq[5] = 2.0 * (y * z - w * x);
-    Rq[6] = 2.0 * (x * z - w * y);
-    Rq[7] = 2.0 * (y * z + w * x);
-    Rq[8] = 1.0 - 2.0 * (x * x + y * y);
-    double M[9];
-    for (int r = 0; r < 3; ++r)
-      for (int j = 0; j < 3; ++j) M[r * 3 + j] = Rq[r * 3 + j] * s[j];
-    double Sf[9];
-    for (int r = 0; r < 3; ++r)
-      for (int j = r; j < 3; ++j) {
-        const double v = (M[r * 3] * M[j * 3] + M[r * 3 + 1] * M[j * 3 + 1]) +
-                         M[r * 3 + 2] * M[j * 3 + 2];
-        Sf[r * 3 + j] = v;
-        Sf[j * 3 + r] = v;
-      }
-
-    // EWA Jacobian with the fov clamp, T = J W, 2D covariance and conic
-    const double itz = 1.0 / tz, itz2 = itz * itz, itz3 = itz2 * itz;
-    const double txz = tx * itz, tyz = ty * itz;
-    const double limx = (double)st.fov_clamp * ((0.5 * (double)cam.W) / fx);
-    const double limy = (double)st.fov_clamp * ((0.5 * (double)cam.H) / fy);
-    const bool clampx = (txz > limx) || (txz < -limx);
-    const bool clampy = (tyz > limy) || (tyz < -limy);
-    const double xc = (clampx ? (txz > 0.0 ? limx : -limx) : txz) * tz;
-    const double yc = (clampy ? (tyz > 0.0 ? limy : -limy) : tyz) * tz;
-    const double J00 = fx * itz, J02 = -(fx * xc * itz2);
-    const double J11 = fy * itz, J12 = -(fy * yc * itz2);
-    double Tm[6];
-    for (int j = 0; j < 3; ++j) {
-      Tm[j] = J00 * W[j] + J02 * W[6 + j];
-      Tm[3 + j] = J11 * W[3 + j] + J12 * W[6 + j];
-    }
-    double ST0[3], ST1[3];
-    for (int r = 0; r < 3; ++r) {
-      ST0[r] = Sf[r * 3] * Tm[0] + Sf[r * 3 + 1] * Tm[1] + Sf[r * 3 + 2] * Tm[2];
-      ST1[r] = Sf[r * 3] * Tm[3] + Sf[r * 3 + 1] * Tm[4] + Sf[r * 3 + 2] * Tm[5];
-    }
-    const double a = (Tm[0] * ST0[0] + Tm[1] * ST0[1] + Tm[2] * ST0[2]) + (double)st.eps2d;
-    const double b = Tm[0] * ST1[0] + Tm[1] * ST1[1] + Tm[2] * ST1[2];
-    const double c = (Tm[3] * ST1[0] + Tm[4] * ST1[1] + Tm[5] * ST1[2]) + (double)st.eps2d;
-    const double idet = 1.0 / (a * c - b * b);
-    const double A = c * idet, B = -(b * idet), C = a * idet;
-
-    // conic = Sigma2D^-1: dL/dSigma2D = -conic G conic, G = [[gA, gB/2], [gB/2, gC]]
-    const double gA = r0.z, gB = r0.w, gC = r1.x;
-    const double ga = -(gA * A * A + gB * A * B + gC * B * B);
-    const double gb = -(2.0 * gA * A * B + gB * (A * C + B * B) + 2.0 * gC * B * C);
-    const double gc = -(gA * B * B + gB * B * C + gC * C * C);
-
-    // Sigma2D = T Sigma T^T: dL/dSigma = T^T G2 T, dL/dT = 2 G2 T Sigma
-    double gT0[3], gT1[3];
-    for (int r = 0; r < 3; ++r) {
-      gT0[r] = 2.0 * ga * ST0[r] + gb * ST1[r];
-      gT1[r] = gb * ST0[r] + 2.0 * gc * ST1[r];
-    }
-    double gJ00 = 0.0, gJ02 = 0.0, gJ11 = 0.0, gJ12 = 0.0;
-    for (int j = 0; j < 3; ++j) {
-      gJ00 += gT0[j] * W[j];
-      gJ02 += gT0[j] * W[6 + j];
-      gJ11 += gT1[j] * W[3 + j];
-      gJ12 += gT1[j] * W[6 + j];
-    }
-    double gt[3] = {0.0, 0.0, 0.0};
-    gt[2] += gJ00 * (-fx * itz2) + gJ11 * (-fy * itz2);
-    if (clampx) {
-      gt[2] += gJ02 * (fx * (txz > 0.0 ? limx : -limx) * itz2);
-    } else {
-      gt[0] += gJ02 * (-fx * itz2);
-      gt[2] += gJ02 * (2.0 * fx * tx * itz3);
-    }
-    if (clampy) {
-      gt[2] += gJ12 * (fy * (tyz > 0.0 ? limy : -limy) * itz2);
-    } else {
-      gt[1] += gJ12 * (-fy * itz2);
-      gt[2] += gJ12 * (2.0 * fy * ty * itz3);
-    }
-    const double gu = r0.x, gv = r0.y;
-    gt[0] += gu * fx * itz;
-    gt[2] += gu * (-fx * tx * itz2);
-    gt[1] += gv * fy * itz;
-    gt[2] += gv * (-fy * ty * itz2);
-    double gm[3];
-    for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
-
-    // Sigma = M M^T, M = R diag(s): dL/dM = (G + G^T) M with
-    // G = dL/dSigma = ga T0^T T0 + gb T0^T T1 + gc T1^T T1 (formed row by row)
-    double gs[3] = {0.0, 0.0, 0.0}, gR[9];
-    for (int r = 0; r < 3; ++r) {
-      double Gr[3];
-      for (int j = 0; j < 3; ++j)
-        Gr[j] = 2.0 * (ga * Tm[r] * Tm[j] + gc * Tm[3 + r] * Tm[3 + j]) +
-                gb * (Tm[r] * Tm[3 + j] + Tm[3 + r] * Tm[j]);
-      for (int k = 0; k < 3; ++k) {
-        const double acc = (Gr[0] * M[k] + Gr[1] * M[3 + k]) + Gr[2] * M[6 + k];
-        gs[k] += acc * Rq[r * 3 + k];
-        gR[r * 3 + k] = acc * s[k];
-      }
-    }
-    double gqn[4];
-    gqn[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
-    gqn[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - w * gR[5] + z * gR[6] + w * gR[7]) -
-             4.0 * x * (gR[4] + gR[8]);
-    gqn[2] = 2.0 * (x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7]) -
-             4.0 * y * (gR[0] + gR[8]);
-    gqn[3] = 2.0 * (-w * gR[1] + x * gR[2] + w * gR[3] + y * gR[5] + x * gR[6] + y * gR[7]) -
-             4.0 * z * (gR[0] + gR[4]);
-    const double dot = w * gqn[0] + x * gqn[1] + y * gqn[2] + z * gqn[3];
-    oq[0] = (float)((gqn[0] - w * dot) * inr);
-    oq[1] = (float)((gqn[1] - x * dot) * inr);
-    oq[2] = (float)((gqn[2] - y * dot) * inr);
-    oq[3] = (float)((gqn[3] - z * dot) * inr);
-    for (int k = 0; k < 3; ++k) os[k] = (float)gs[k];
-
-    for (int k = 0; k < 3; ++k) om[k] = (float)(gm[k] + vterm[k]);
+    geom_grads(cam, st, pm, ps, pq, r0, r1, vterm, om, os, oq);
   }
   if (store) {
     for (int k = 0; k < 3; ++k) {
       const int64_t p = (int64_t)k * ldo + r;
-      o_means[p] = acc ? o_means[p] + om[k] : om[k];
-      o_scales[p] = acc ? o_scales[p] + os[k] : os[k];
+      o_means[p] = accumulate ? o_means[p] + om[k] : om[k];
+      o_scales[p] = accumulate ? o_scales[p] + os[k] : os[k];
     }
     for (int k = 0; k < 4; ++k) {
       const int64_t p = (int64_t)k * ldo + r;
-      o_quats[p] = acc ? o_quats[p] + oq[k] : oq[k];
+      o_quats[p] = accumulate ? o_quats[p] + oq[k] : oq[k];
     }
-    o_opac[r] = acc ? o_opac[r] + oo : oo;
+    o_opac[r] = accumulate ? o_opac[r] + oo : oo;
   }
-  }  // cameras
+}
+
+// Batched form: Gaussian r seen by cameras 0 .. ncams-1 (radii [c][ld],
+// records [c * ld + r]); the outputs are the sums over the cameras, in
+// camera order, with the same fp32 additions as ncams single-camera calls
+// with accumulate (the first overwriting unless `accumulate`).  The sums
+// stay in registers and are written once.  Two passes over the cameras keep
+// the register set of each side apart: the SH side for every camera first
+// (its view-direction terms parked in LDS, three doubles per camera and
+// lane), then the geometry chain for every camera.  -0.0f starts a sum:
+// adding it leaves every value's bits unchanged.
+template <int DEG>
+__global__ __launch_bounds__(256) void project_bwd_batched_kernel(
+    int64_t N, int64_t ld, const float* __restrict__ means, const float* __restrict__ scales,
+    const float* __restrict__ quats, const float* __restrict__ sh, CamBatch cams, int ncams,
+    Settings st, const int32_t* __restrict__ radii, const float4* __restrict__ grads2d,
+    float* __restrict__ o_means, float* __restrict__ o_scales, float* __restrict__ o_quats,
+    float* __restrict__ o_opac, float* __restrict__ o_sh, int accumulate) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  extern __shared__ double s_vterm[];  // [ncams][3][256]
+  const int t = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + t;
+  if (r >= N) return;
+  bool anyvis = false;
+  for (int c = 0; c < ncams; ++c) anyvis |= radii[(int64_t)c * ld + r] > 0;
+  if (accumulate && !anyvis) return;  // nothing to add
+  float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
+#pragma unroll
+  for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
+  if (anyvis) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      pm[k] = means[(int64_t)k * ld + r];
+      ps[k] = scales[(int64_t)k * ld + r];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + r];
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + r];
+  }
+
+  // pass 1: the SH side of every camera
+  {
+    float a_sh[3 * K];
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) a_sh[k] = accumulate ? o_sh[(int64_t)k * ld + r] : -0.0f;
+    for (int c = 0; c < ncams; ++c) {
+      const bool vis = radii[(int64_t)c * ld + r] > 0;
+      // a camera adds where it sees the Gaussian; the first one of an
+      // overwriting call also stands for the zeros a culled lane writes
+      const bool store = vis || (c == 0 && !accumulate);
+      double d[3] = {0.0, 0.0, 1.0}, iL = 1.0, vterm[3] = {0.0, 0.0, 0.0};
+      float gcol[3] = {0.0f, 0.0f, 0.0f};
+      if (vis) {
+        const int64_t rr = (int64_t)c * ld + r;
+        const float4 r1 = grads2d[4 * rr + 1], r2 = grads2d[4 * rr + 2];
+        const float gin[3] = {r1.z, r1.w, r2.x};
+        sh_view<DEG>(cams.c[c], pm, shv, st.sh_offset, gin, d, iL, gcol);
+      }
+      if (store)
+        sh_grads<DEG>(d, iL, gcol, shv, [&](int k, float g) { a_sh[k] += g; }, vterm);
+      for (int e = 0; e < 3; ++e) s_vterm[(c * 3 + e) * 256 + t] = vterm[e];
+    }
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) o_sh[(int64_t)k * ld + r] = a_sh[k];
+  }
+
+  // pass 2: the geometry chain of every camera
+  float a_m[3], a_s[3], a_q[4], a_o;
+  for (int k = 0; k < 3; ++k) {
+    a_m[k] = accumulate ? o_means[(int64_t)k * ld + r] : -0.0f;
+    a_s[k] = accumulate ? o_scales[(int64_t)k * ld + r] : -0.0f;
+  }
+  for (int k = 0; k < 4; ++k) a_q[k] = accumulate ? o_quats[(int64_t)k * ld + r] : -0.0f;
+  a_o = accumulate ? o_opac[r] : -0.0f;
+  for (int c = 0; c < ncams; ++c) {
+    const bool vis = radii[(int64_t)c * ld + r] > 0;
+    const bool store = vis || (c == 0 && !accumulate);
+    float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
+    float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
+    if (vis) {
+      const int64_t rr = (int64_t)c * ld + r;
+      const float4 r0 = grads2d[4 * rr + 0], r1 = grads2d[4 * rr + 1];
+      double vterm[3];
+      for (int e = 0; e < 3; ++e) vterm[e] = s_vterm[(c * 3 + e) * 256 + t];
+      oo = r1.y;
+      geom_grads(cams.c[c], st, pm, ps, pq, r0, r1, vterm, om, os, oq);
+    }
+    if (store) {
+      for (int k = 0; k < 3; ++k) {
+        a_m[k] += om[k];
+        a_s[k] += os[k];
+      }
+      for (int k = 0; k < 4; ++k) a_q[k] += oq[k];
+      a_o += oo;
+    }
+  }
+  for (int k = 0; k < 3; ++k) {
+    o_means[(int64_t)k * ld + r] = a_m[k];
+    o_scales[(int64_t)k * ld + r] = a_s[k];
+  }
+  for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + r] = a_q[k];
+  o_opac[r] = a_o;
 }
 
 }  // namespace gs
@@ -699,15 +812,21 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_
   gs::CamBatch cb;
   for (int c = 0; c < ncams; ++c) cb.c[c] = cams[c];
   const int64_t blocks = (N + 255) / 256;
-#define GS_PBWD(D, PK, BT)                                                                \
-  hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK, BT>), dim3((unsigned)blocks), dim3(256), \
-                     0, stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh, cb, \
-                     ncams, st, radii, (const float4*)grads2d, o_means, o_scales, o_quats,   \
+  const size_t vterm_lds = sizeof(double) * 3 * 256 * (size_t)ncams;
+#define GS_PBWD(D, PK)                                                                    \
+  hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK>), dim3((unsigned)blocks), dim3(256), 0,  \
+                     stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh,       \
+                     cams[0], st, radii, (const float4*)grads2d, o_means, o_scales, o_quats, \
                      o_opac, o_sh, accumulate)
-#define GS_PBWD2(D)                          \
-  if (ncams > 1) GS_PBWD(D, false, true);     \
-  else if (vis_ids) GS_PBWD(D, true, false);  \
-  else GS_PBWD(D, false, false)
+#define GS_PBWD_B(D)                                                                       \
+  hipLaunchKernelGGL(gs::project_bwd_batched_kernel<D>, dim3((unsigned)blocks), dim3(256),    \
+                     vterm_lds, stream, N, ld, means, scales, quats, sh, cb, ncams, st,      \
+                     radii, (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, o_sh, \
+                     accumulate)
+#define GS_PBWD2(D)                     \
+  if (ncams > 1) GS_PBWD_B(D);          \
+  else if (vis_ids) GS_PBWD(D, true);   \
+  else GS_PBWD(D, false)
   switch (deg) {
     case 0: GS_PBWD2(0); break;
     case 1: GS_PBWD2(1); break;
@@ -715,6 +834,7 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_
     default: GS_PBWD2(3); break;
   }
 #undef GS_PBWD2
+#undef GS_PBWD_B
 #undef GS_PBWD
   return hipGetLastError();
 }

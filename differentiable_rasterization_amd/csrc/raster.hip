@@ -733,8 +733,27 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     } else if (cnt > 0) {
       float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
       const uint64_t base = offsets[i];
-      if (fits)
-        for (uint32_t k = 0; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
+      if (fits) {
+        // four slots' loads in flight before their (in-order) additions
+        uint32_t k = 0;
+        for (; k + 4 <= cnt; k += 4) {
+          const float4* p = partials + 4 * (base + k);
+          float4 x[4][3];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j][0] = p[4 * j];
+            x[j][1] = p[4 * j + 1];
+            x[j][2] = p[4 * j + 2];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a[0] += x[j][0].x; a[1] += x[j][0].y; a[2] += x[j][0].z; a[3] += x[j][0].w;
+            a[4] += x[j][1].x; a[5] += x[j][1].y; a[6] += x[j][1].z; a[7] += x[j][1].w;
+            a[8] += x[j][2].x; a[9] += x[j][2].y; a[10] += x[j][2].z;
+          }
+        }
+        for (; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
+      }
       store_rec(grads2d + 4 * r, a);
     }
   }
