@@ -6,10 +6,14 @@ A step is one whole pass of the hot path for one camera: projection, binning
 + radix sort, compositing, loss gradient, compositing backward and
 projection backward.  Inputs (Gaussians, targets, cameras) are resident in
 HBM before the timed region; each step renders the next of the workload's
-seeded poses.
+seeded poses.  The poses' frames are independent (the parameters do not
+change between them), so --in-flight frames run concurrently, each on its
+own HIP stream with its own buffers and gradients, step i on stream
+i mod --in-flight; the per-stage times, the roofline and the "serial" figure
+come from passes with one frame at a time.
 
   python bench.py [--steps K] [--warmup W] [--config cluster_1m_1080p]
-                  [--no-cpu-baseline] [--gpus 1]
+                  [--in-flight F] [--no-cpu-baseline] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -374,6 +378,11 @@ def main():
                     help="run the compositing backward with the absolute-gradient sums")
     ap.add_argument("--packed", action="store_true",
                     help="run the packed calls (visible list, sparse gradient rows)")
+    ap.add_argument("--in-flight", type=int, default=3,
+                    help="frames processed concurrently, each on its own stream and buffers")
+    ap.add_argument("--no-packed-leg", action="store_true",
+                    help="leave out the packed calls' leg (hardware counter runs use it, so "
+                         "that every dispatch of a kernel belongs to the headline's frames)")
     ap.add_argument("--no-train-step", action="store_true",
                     help="skip the training-step measurement (packed calls, L1 + 0.2 D-SSIM, "
                          "per-group Adam)")
@@ -421,7 +430,11 @@ def main():
     targets_np = [scenes.target_image(c, i) for i, c in enumerate(cams)]
     targets = [torch.from_numpy(t).cuda() for t in targets_np]
     g = raster.Gaussians.from_scene(scene)
-    fr = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=4 * N, packed=args.packed)
+    nf = max(1, args.in_flight)
+    frames = [raster.Frame(g.ld, scene.sh_degree, W, H, capacity=4 * N, packed=args.packed)
+              for _ in range(nf)]
+    streams = [torch.cuda.Stream() for _ in range(nf)]
+    fr = frames[0]
     gcams = [raster.make_camera(c) for c in cams]
     kind = 0 if loss_kind == "l2" else 1
     P = len(cams)
@@ -477,33 +490,47 @@ def main():
                           bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
                           bwd_reductions=int(c[7])))
 
-    def timed(frame):
-        """Warm-up, then the timed steps; returns (seconds, per-stage ms).
-        The timed steps run without instrumentation: an event recorded on
-        the stream leaves the GPU idle for several microseconds, and six per
-        step would be counted in the throughput.  The per-stage times come
-        from a second pass over the same steps with an event between
-        stages."""
-        for i in range(args.warmup):
-            step(i, fr=frame)
+    def run_steps(frs, first, count):
+        """Steps first .. first+count-1, step i on frame/stream i mod len(frs)
+        (one frame: the current stream)."""
+        for i in range(first, first + count):
+            k = i % len(frs)
+            if len(frs) == 1:
+                step(i, fr=frs[0])
+            else:
+                with torch.cuda.stream(streams[k]):
+                    step(i, fr=frs[k])
+
+    def timed(frs):
+        """Warm-up, then the timed steps with len(frs) frames in flight;
+        returns (seconds, serial seconds, per-stage ms).  The timed steps run
+        without instrumentation: an event recorded on the stream leaves the
+        GPU idle for several microseconds, and six per step would be counted
+        in the throughput.  Then the same steps one frame at a time (serial
+        seconds), and a third pass, one frame at a time with an event between
+        stages, for the per-stage times."""
+        run_steps(frs, 0, args.warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i, fr=frame)
+        run_steps(frs, 0, args.steps)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        run_steps(frs[:1], 0, args.steps)
+        torch.cuda.synchronize()
+        dt_serial = time.perf_counter() - t0
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
                for _ in range(args.steps)]
         for i in range(args.steps):
-            step(i, evs[i], fr=frame)
+            step(i, evs[i], fr=frs[0])
         torch.cuda.synchronize()
         ms = {n: 0.0 for n in names}
         for ev in evs:
             for k, n in enumerate(names):
                 ms[n] += ev[k].elapsed_time(ev[k + 1])
-        return dt, {n: v / args.steps for n, v in ms.items()}
+        return dt, dt_serial, {n: v / args.steps for n, v in ms.items()}
 
-    dt, stage_ms = timed(fr)
+    dt, dt_serial, stage_ms = timed(frames)
     packed_line = None
     train_line = None if args.no_train_step else train_step_bench(args, scene, gcams, targets,
                                                                    fr.capacity)
@@ -516,15 +543,17 @@ def main():
     graph_cap = int(1.25 * max(s_["M"] for s_ in stats)) + 8192
     graph_line = None if args.no_train_step else graph_bench(args, scene, gcams, targets, kind,
                                                               graph_cap)
-    if not args.packed:
+    if not args.packed and not args.no_packed_leg:
         # the same steps through the packed calls (visible list, sparse
         # gradient rows), reported beside the dense headline
-        frp = raster.Frame(g.ld, scene.sh_degree, W, H, capacity=fr.capacity, packed=True)
-        dtp, msp = timed(frp)
+        frps = [raster.Frame(g.ld, scene.sh_degree, W, H, capacity=fr.capacity, packed=True)
+                for _ in range(nf)]
+        dtp, dtps, msp = timed(frps)
         packed_line = {"value": round(args.steps / dtp, 2),
                        "ms_per_step": round(1e3 * dtp / args.steps, 4),
+                       "serial_value": round(args.steps / dtps, 2),
                        "stages_ms": {n: round(v, 4) for n, v in msp.items()}}
-        del frp
+        del frps
     # average workload over the poses the timed steps visited
     visited = [stats[i % P] for i in range(args.steps)]
     avg = {k: float(np.mean([s[k] for s in visited])) for k in visited[0]}
@@ -589,7 +618,11 @@ def main():
         "config": {"workload": args.config, "gaussians": N, "width": W, "height": H,
                    "sh_degree": scene.sh_degree, "poses": P, "loss": loss_kind,
                    "visible": int(avg["V"]), "instances": int(avg["M"]),
-                   "absgrad": bool(args.absgrad), "packed": bool(args.packed)},
+                   "absgrad": bool(args.absgrad), "packed": bool(args.packed),
+                   "frames_in_flight": nf},
+        "serial": {"value": round(args.steps / dt_serial, 2),
+                   "ms_per_step": round(1e3 * dt_serial / args.steps, 4),
+                   "form": "the same steps one frame at a time on one stream"},
         "fwd_fps": round(1e3 / fwd_ms, 2),
         "sort_keys_per_s": round(avg["M"] / (stage_ms["bin_and_sort"] * 1e-3), 1),
         "stages": stages,
