@@ -12,7 +12,7 @@
 //     computes every digit's global histogram, then each digit pass reads and
 //     writes the keys once.  A workgroup takes its partition from an atomic
 //     ticket (so it only ever waits on partitions already running), ranks
-//     its 8192 keys stably with wave64 ballots into LDS histograms, publishes
+//     its 4096 keys stably with wave64 ballots into LDS histograms, publishes
 //     per-digit counts and resolves its global offsets by decoupled
 //     look-back, then scatters through LDS so that global writes come out
 //     in digit runs.  Only the low 32 + ceil(log2 T) key bits are sorted.
@@ -219,9 +219,10 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kRadixBits = 9;  // 45 key bits at 1080p: 5 passes
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kSortItems = 16;
-constexpr int kSortWaves = 8;  // 512-lane workgroups of 8192 keys: half as many
-                               // partitions per pass
+constexpr int kSortItems = 8;
+// 512-lane workgroups (a lane per digit) of 4096 keys: ~66 KB of LDS, so a
+// partition finds room on a CU beside other kernels' workgroups
+constexpr int kSortWaves = 8;
 constexpr int kSortThreads = 64 * kSortWaves;
 constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
 static_assert(kRadix <= kSortThreads, "a sort lane per digit");
