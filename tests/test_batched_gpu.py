@@ -112,9 +112,10 @@ def test_batch_cluster_3m_4k_four_poses():
     _check_batch("cluster_3m_4k", scene, cams)
 
 
-def _check_backward(name, scene, cams, ld=None):
+def _check_backward(name, scene, cams, ld=None, accumulate=0):
     """Batched backward against single-camera calls with accumulate (camera 0
-    overwrites, the next ones add): the 2D records of every camera and the
+    overwrites, the next ones add; with ``accumulate`` every camera adds to
+    the same seeded starting values): the 2D records of every camera and the
     summed 3D gradients, bit for bit."""
     import torch
     from differentiable_rasterization_amd import raster
@@ -122,13 +123,20 @@ def _check_backward(name, scene, cams, ld=None):
     N, L, C = scene.n, g.ld, len(cams)
     tgt = torch.from_numpy(np.stack([scenes.target_image(c, k) for k, c in enumerate(cams)])).cuda()
     raster.gs_image_loss_grad(1, tgt.numel(), bf.image, tgt, bf.dL_dimage, None)
-    bf.backward(g)
-    torch.cuda.synchronize()
     fr = raster.Frame(g.ld, scene.sh_degree, cams[0].width, cams[0].height)
+    if accumulate:
+        rng = np.random.default_rng(17)
+        for k in ("g_means", "g_scales", "g_quats", "g_opacities", "g_sh"):
+            start = torch.from_numpy(
+                rng.normal(0.0, 1.0, tuple(getattr(bf, k).shape)).astype(np.float32)).cuda()
+            getattr(bf, k).copy_(start)
+            getattr(fr, k).copy_(start)
+    bf.backward(g, accumulate=accumulate)
+    torch.cuda.synchronize()
     for c, cam in enumerate(cams):
         fr.forward(g, cam)
         fr.loss_grad(tgt[c], 1, with_loss=False)
-        fr.backward(g, accumulate=int(c > 0))
+        fr.backward(g, accumulate=int(c > 0 or bool(accumulate)))
         torch.cuda.synchronize()
         assert_bits_equal(bf.dL_dimage[c].cpu().numpy(), fr.dL_dimage.cpu().numpy(), "dL/dimage")
         vis = fr.radii[:N].cpu().numpy() > 0
@@ -146,6 +154,12 @@ def test_batch_backward_cluster_200k():
     scene = scenes.cluster_scene(n=200_000, seed=13)
     cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
     _check_backward("cluster_200k_640x416", scene, cams)
+
+
+def test_batch_backward_accumulate_cluster_200k():
+    scene = scenes.cluster_scene(n=200_000, seed=13)
+    cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
+    _check_backward("cluster_200k_640x416 accumulate", scene, cams, accumulate=1)
 
 
 def test_batch_backward_ragged_padded():
