@@ -206,16 +206,34 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
                                      enumerate(cams[i:i + batch])])).cuda()
           for i in range(0, len(cams) - batch + 1, batch)]
 
+    def group_fb(b, grp, t):
+        b.forward(g, grp)
+        raster.gs_image_loss_grad(1, t.numel(), b.image, t, b.dL_dimage, None)
+        b.backward(g)
+
     def batched_fb():
         for grp, t in zip(groups, tg):
-            bf.forward(g, grp)
-            raster.gs_image_loss_grad(1, t.numel(), bf.image, t, bf.dL_dimage, None)
-            bf.backward(g)
+            group_fb(bf, grp, t)
+
+    # the groups are independent too: --in-flight of them at once, each on
+    # its own stream with its own buffers, group k on stream k mod in-flight
+    nf = max(1, args.in_flight)
+    bfs = [bf] + [raster.BatchFrame(g.ld, scene.sh_degree, W, H, batch) for _ in range(nf - 1)]
+    streams = [torch.cuda.Stream() for _ in range(nf)]
+
+    issued = [0]
+
+    def batched_fb_in_flight():
+        for grp, t in zip(groups, tg):
+            k = issued[0] % nf
+            issued[0] += 1
+            with torch.cuda.stream(streams[k]):
+                group_fb(bfs[k], grp, t)
 
     out = {}
     fns = [("single", single), ("batched", batched)]
     if not depth_alpha:
-        fns.append(("batched_fb", batched_fb))
+        fns += [("batched_fb", batched_fb), ("batched_fb_in_flight", batched_fb_in_flight)]
     for name, fn in fns:
         fn()  # warm-up (also sizes the sort buffers)
         torch.cuda.synchronize()
@@ -231,6 +249,8 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
          "depth_alpha": bool(depth_alpha)}
     if "batched_fb" in out:
         r["fwdbwd_fps_batched_calls"] = round(out["batched_fb"], 2)
+        r["fwdbwd_fps_batched_in_flight"] = round(out["batched_fb_in_flight"], 2)
+        r["groups_in_flight"] = nf
     return r
 
 
