@@ -207,8 +207,8 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
           for i in range(0, len(cams) - batch + 1, batch)]
 
     def group_fb(b, grp, t):
-        b.forward(g, grp)
-        raster.gs_image_loss_grad(1, t.numel(), b.image, t, b.dL_dimage, None)
+        # the L1 loss gradient fused into the batch's compositing forward
+        b.forward(g, grp, target=t, kind=1)
         b.backward(g)
 
     def batched_fb():

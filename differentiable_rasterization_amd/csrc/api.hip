@@ -620,6 +620,38 @@ gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, 
                     "gs_rasterize_fwd_batched");
 }
 
+gs_status gs_rasterize_fwd_loss_batched(int32_t num_cams, int64_t ld, int32_t width,
+                                        int32_t height, const uint32_t* tile_ranges,
+                                        const uint32_t* tile_order, const uint32_t* ids,
+                                        const float* splats, const float* depths,
+                                        const float* background, const gs_settings* settings,
+                                        int32_t kind, const float* target, float* image,
+                                        float* final_T, uint32_t* last_idx, float* out_depth,
+                                        float* out_alpha, float* dL_dimage, float* loss,
+                                        uint64_t* counters, void* stream) {
+  GS_CHECK(check_sizes(0, ld));
+  GS_CHECK(check_batch(num_cams, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
+  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
+  GS_REQUIRE(target && dL_dimage, "NULL target or gradient pointer");
+  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
+  if (ld > 0) {
+    GS_REQUIRE(ids && splats, "NULL splat pointer");
+    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
+    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  }
+  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order,
+                                         ids, splats, depths, background,
+                                         gs::make_settings(*settings), image, final_T, last_idx,
+                                         out_depth, out_alpha, counters, kind, target,
+                                         dL_dimage, loss, (hipStream_t)stream),
+                    "gs_rasterize_fwd_loss_batched");
+}
+
 gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
                                    const uint32_t* tile_ranges,
                            const uint32_t* tile_order, const uint32_t* ids,

@@ -32,7 +32,8 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_adam_step_packed", "gs_project_fwd_batched",
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
             "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
-            "gs_bin_and_sort_device", "gs_rasterize_fwd_loss", "gs_tile_order")
+            "gs_bin_and_sort_device", "gs_rasterize_fwd_loss", "gs_tile_order",
+            "gs_rasterize_fwd_loss_batched")
 
 
 class GsError(RuntimeError):
@@ -135,6 +136,9 @@ def load():
     lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 7 + [i32] + [P] * 9 + [P]
     lib.gs_tile_order.restype = C.c_int
     lib.gs_tile_order.argtypes = [i32, i32, i32, P, P, P]
+    lib.gs_rasterize_fwd_loss_batched.restype = C.c_int
+    lib.gs_rasterize_fwd_loss_batched.argtypes = [i32, i64, i32, i32] + [P] * 7 + [i32] + \
+        [P] * 9 + [P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -400,6 +404,20 @@ def gs_rasterize_fwd_loss(N, ld, width, height, tile_ranges, ids, splats, depths
                                      _p(image), _p(final_T), _p(last_idx), _p(out_depth),
                                      _p(out_alpha), _p(dL_dimage), _p(loss), _p(counters),
                                      _stream(stream)))
+
+
+def gs_rasterize_fwd_loss_batched(num_cams, ld, width, height, tile_ranges, ids, splats,
+                                  depths, background, settings, kind, target, image, final_T,
+                                  last_idx, dL_dimage, out_depth=None, out_alpha=None, loss=None,
+                                  counters=None, stream=None, tile_order=None):
+    lib = load()
+    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_fwd_loss_batched(num_cams, ld, width, height, _p(tile_ranges),
+                                             _p(tile_order), _p(ids), _p(splats), _p(depths),
+                                             bg, C.byref(settings), int(kind), _p(target),
+                                             _p(image), _p(final_T), _p(last_idx),
+                                             _p(out_depth), _p(out_alpha), _p(dL_dimage),
+                                             _p(loss), _p(counters), _stream(stream)))
 
 
 def gs_tile_order(num_cams, width, height, tile_ranges, tile_order, stream=None):
@@ -777,7 +795,10 @@ class BatchFrame:
         off = (-self.workspace.data_ptr()) % 256
         self.ws = self.workspace[off:off + self.ws_bytes]
 
-    def forward(self, g: "Gaussians", cams):
+    def forward(self, g: "Gaussians", cams, target=None, kind=1, loss=None):
+        """The batch's forward; with ``target`` ([C][H][W][3]) the loss
+        gradient (kind 0: L2, 1: L1) goes to dL_dimage in the same pass, and
+        the summed loss to ``loss`` (a device float) when given."""
         assert len(cams) == self.C
         self.cams = [c if isinstance(c, gs_camera) else make_camera(c) for c in cams]
         gs_project_fwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
@@ -794,10 +815,19 @@ class BatchFrame:
         self.M = M
         if self.order is not None:
             gs_tile_order(self.C, self.W, self.H, self.ranges, self.order)
-        gs_rasterize_fwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
-                                 self.splats, self.depths, self.background, self.settings,
-                                 self.image, self.final_T, self.last_idx, self.out_depth,
-                                 self.out_alpha, tile_order=self.order)
+        if target is None:
+            gs_rasterize_fwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
+                                     self.splats, self.depths, self.background, self.settings,
+                                     self.image, self.final_T, self.last_idx, self.out_depth,
+                                     self.out_alpha, tile_order=self.order)
+        else:
+            # the loss gradient into dL_dimage, fused into the compositing
+            gs_rasterize_fwd_loss_batched(self.C, self.ld, self.W, self.H, self.ranges,
+                                          self.ids, self.splats, self.depths, self.background,
+                                          self.settings, kind, target, self.image,
+                                          self.final_T, self.last_idx, self.dL_dimage,
+                                          self.out_depth, self.out_alpha, loss=loss,
+                                          tile_order=self.order)
         return self.image
 
     def backward(self, g: "Gaussians", dL_dimage=None, accumulate=0, absgrad=False):

@@ -337,6 +337,24 @@ GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t 
                                           float* final_T, uint32_t* last_idx, float* out_depth,
                                           float* out_alpha, uint64_t* counters, void* stream);
 
+/* gs_rasterize_fwd_loss_batched: gs_rasterize_fwd_loss for every camera of
+ * a batch (layouts as gs_rasterize_fwd_batched): target and dL_dimage are
+ * [c][H][W][3], each camera's pixels against its own target, and *loss
+ * (NULL to skip) the sum over all cameras' pixels.  The values equal
+ * gs_rasterize_fwd_batched followed by gs_image_loss_grad over the batch's
+ * images. */
+GS_API gs_status gs_rasterize_fwd_loss_batched(int32_t num_cams, int64_t ld, int32_t width,
+                                               int32_t height, const uint32_t* tile_ranges,
+                                               const uint32_t* tile_order, const uint32_t* ids,
+                                               const float* splats, const float* depths,
+                                               const float* background,
+                                               const gs_settings* settings, int32_t kind,
+                                               const float* target, float* image,
+                                               float* final_T, uint32_t* last_idx,
+                                               float* out_depth, float* out_alpha,
+                                               float* dL_dimage, float* loss,
+                                               uint64_t* counters, void* stream);
+
 /* gs_rasterize_bwd_batched: gs_rasterize_bwd for every camera of a batch
  * (final_T, last_idx [c][H][W], dL_dimage [c][H][W][3]); grads2d receives
  * the 2D gradient record of every row c * ld + i [num_cams * ld][16]

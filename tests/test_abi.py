@@ -292,6 +292,25 @@ def test_fused_loss_rejects_bad_arguments(lib):
     assert call(dl=other) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the target
 
 
+def test_batched_fused_loss_rejects_bad_arguments(lib):
+    dummy, other = C.c_void_p(64), C.c_void_p(128)
+    st = raster.default_settings()
+    bg = (C.c_float * 3)(0, 0, 0)
+
+    def call(cams=2, kind=1, target=other, dl=C.c_void_p(192), ranges=dummy):
+        return lib.gs_rasterize_fwd_loss_batched(cams, 10, 64, 64, ranges, None, dummy, dummy,
+                                                 None, bg, C.byref(st), kind, target, dummy,
+                                                 dummy, dummy, None, None, dl, None, None, None)
+    assert call(cams=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(cams=9) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(kind=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(ranges=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(target=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(dl=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(dl=dummy) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the image
+    assert call(dl=other) == raster.GS_ERR_INVALID_ARGUMENT     # aliases the target
+
+
 def test_tile_order_rejects_bad_arguments(lib):
     dummy, other = C.c_void_p(64), C.c_void_p(128)
     assert lib.gs_tile_order(0, 64, 64, dummy, other, None) == raster.GS_ERR_INVALID_ARGUMENT

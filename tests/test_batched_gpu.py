@@ -150,6 +150,35 @@ def _check_backward(name, scene, cams, ld=None, accumulate=0):
     print("[batch] %s backward: %d cameras, M=%d" % (name, C, bf.M), flush=True)
 
 
+def test_batch_fused_loss_matches_separate_loss():
+    """gs_rasterize_fwd_loss_batched against gs_rasterize_fwd_batched followed
+    by gs_image_loss_grad over the batch: images, T, last indices and the
+    loss gradient bit for bit, for L1 and L2; the loss value to float
+    summation tolerance."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    scene = scenes.cluster_scene(n=200_000, seed=13)
+    cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
+    g, bf = _batch(scene, cams)
+    tgt = torch.from_numpy(np.stack([scenes.target_image(c, k) for k, c in enumerate(cams)])).cuda()
+    for kind in (0, 1):
+        bf.forward(g, cams)
+        ref_loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+        raster.gs_image_loss_grad(kind, tgt.numel(), bf.image, tgt, bf.dL_dimage, ref_loss)
+        torch.cuda.synchronize()
+        ref = {k: getattr(bf, k).clone() for k in ("image", "final_T", "last_idx", "dL_dimage")}
+        bf.dL_dimage.zero_()
+        loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+        bf.forward(g, cams, target=tgt, kind=kind, loss=loss)
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert_bits_equal(getattr(bf, k).cpu().numpy(), v.cpu().numpy(), "%s kind %d" % (k, kind))
+        a, b = float(loss.item()), float(ref_loss.item())
+        assert abs(a - b) <= 1e-5 * abs(b) + 1e-3, (kind, a, b)
+    print("[batch] fused loss: 3 cameras, L1 and L2 bit-identical to the separate pass",
+          flush=True)
+
+
 def test_batch_backward_cluster_200k():
     scene = scenes.cluster_scene(n=200_000, seed=13)
     cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
