@@ -85,8 +85,8 @@ def _load():
         lib.orc_composite_bwd.restype = C.c_int
         lib.orc_project_bwd.argtypes = [C.c_int64, C.c_int] + [P] * 14
         lib.orc_project_bwd.restype = C.c_int
-        lib.orc_project_bwd_errscale.argtypes = [C.c_int64, C.c_int] + [P] * 17
-        lib.orc_project_bwd_errscale.restype = C.c_int
+        lib.orc_project_bwd_bound.argtypes = [C.c_int64, C.c_int] + [P] * 14
+        lib.orc_project_bwd_bound.restype = C.c_int
         lib.orc_loss_jvp.argtypes = [C.c_int64, C.c_int] + [P] * 13 + [C.c_int] + [P] * 5
         lib.orc_loss_jvp.restype = C.c_int64
         for name in ("orc_rotation",):
@@ -254,33 +254,33 @@ def project_bwd(means, scales, quats, sh, sh_degree, cam, radii, g_means2d, g_co
                sh=np.zeros((N, K, 3)))
     cs, ss = camera_struct(cam), settings_struct(settings)
     lib.orc_project_bwd(N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
-                        C.addressof(cs), C.addressof(ss), _ptr(rad), _ptr(gm2), _ptr(gc),
-                        _ptr(gcol), _ptr(out["means"]), _ptr(out["scales"]), _ptr(out["quats"]),
-                        _ptr(out["sh"]))
+       C.addressof(cs), C.addressof(ss), _ptr(rad), _ptr(gm2), _ptr(gc),
+       _ptr(gcol), _ptr(out["means"]), _ptr(out["scales"]), _ptr(out["quats"]),
+       _ptr(out["sh"]))
     return out
 
 
-def project_bwd_errscale(means, scales, quats, sh, sh_degree, cam, radii, g_means2d, g_conics,
-                         g_colors, s_means2d=None, s_conics=None, s_colors=None, settings=None):
-    """First-order fp32 rounding-error scales of :func:`project_bwd` (see
-    oracle.h).  Input scales default to |g|.  Returns dict like project_bwd."""
+def project_bwd_bound(means, scales, quats, sh, sh_degree, cam, radii, s_means2d, s_conics,
+                      s_colors, settings=None):
+    """Bound on how much :func:`project_bwd`'s outputs move when its 2D
+    gradient inputs move by at most ``s_*`` each (elementwise, same shapes
+    as the gradients): e = sum_k |d out / d g2_k| s_k, exact because the
+    projection backward is linear in its 2D gradients (see oracle.h).
+    Returns dict like project_bwd."""
     lib = _load()
     means, scales, quats = _f64(means), _f64(scales), _f64(quats)
     N = means.shape[0]
     K = (sh_degree + 1) ** 2
     sh = _f64(sh, (N, K, 3))
     rad = np.ascontiguousarray(np.asarray(radii, dtype=np.int32))
-    gm2, gc, gcol = _f64(g_means2d, (N, 2)), _f64(g_conics, (N, 3)), _f64(g_colors, (N, 3))
-    sm2 = np.abs(gm2) if s_means2d is None else _f64(s_means2d, (N, 2))
-    sc = np.abs(gc) if s_conics is None else _f64(s_conics, (N, 3))
-    scol = np.abs(gcol) if s_colors is None else _f64(s_colors, (N, 3))
+    sm2, sc, scol = _f64(s_means2d, (N, 2)), _f64(s_conics, (N, 3)), _f64(s_colors, (N, 3))
     out = dict(means=np.zeros((N, 3)), scales=np.zeros((N, 3)), quats=np.zeros((N, 4)),
                sh=np.zeros((N, K, 3)))
     cs, ss = camera_struct(cam), settings_struct(settings)
-    lib.orc_project_bwd_errscale(N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
-                                 C.addressof(cs), C.addressof(ss), _ptr(rad), _ptr(gm2), _ptr(gc),
-                                 _ptr(gcol), _ptr(sm2), _ptr(sc), _ptr(scol), _ptr(out["means"]),
-                                 _ptr(out["scales"]), _ptr(out["quats"]), _ptr(out["sh"]))
+    lib.orc_project_bwd_bound(N, sh_degree, _ptr(means), _ptr(scales), _ptr(quats), _ptr(sh),
+                              C.addressof(cs), C.addressof(ss), _ptr(rad), _ptr(sm2), _ptr(sc),
+                              _ptr(scol), _ptr(out["means"]), _ptr(out["scales"]),
+                              _ptr(out["quats"]), _ptr(out["sh"]))
     return out
 
 

@@ -64,36 +64,9 @@ inline bool operator>(Dual a, Dual b) { return a.v > b.v; }
 inline bool operator<=(Dual a, Dual b) { return a.v <= b.v; }
 inline bool operator>=(Dual a, Dual b) { return a.v >= b.v; }
 
-/* Value with a first-order rounding-error scale m (>= |v|): sums add the
- * scales, products and quotients propagate them to first order, so that an
- * fp32 evaluation of the same expression errs by at most about u * m. */
-struct ErrScale {
-  double v, m;
-  ErrScale() : v(0), m(0) {}
-  ErrScale(double x) : v(x), m(std::fabs(x)) {}
-  ErrScale(double x, double mm) : v(x), m(mm) {}
-};
-inline ErrScale operator+(ErrScale a, ErrScale b) { return ErrScale(a.v + b.v, a.m + b.m); }
-inline ErrScale operator-(ErrScale a, ErrScale b) { return ErrScale(a.v - b.v, a.m + b.m); }
-inline ErrScale operator-(ErrScale a) { return ErrScale(-a.v, a.m); }
-inline ErrScale operator*(ErrScale a, ErrScale b) {
-  return ErrScale(a.v * b.v, a.m * std::fabs(b.v) + std::fabs(a.v) * b.m);
-}
-inline ErrScale operator/(ErrScale a, ErrScale b) {
-  return ErrScale(a.v / b.v, a.m / std::fabs(b.v) + std::fabs(a.v) * b.m / (b.v * b.v));
-}
-inline ErrScale& operator+=(ErrScale& a, ErrScale b) { return a = a + b; }
-inline bool operator<(ErrScale a, ErrScale b) { return a.v < b.v; }
-inline bool operator>(ErrScale a, ErrScale b) { return a.v > b.v; }
-inline ErrScale s_sqrt(ErrScale a) {
-  double r = std::sqrt(a.v);
-  return ErrScale(r, r > 0 ? a.m / r : a.m);
-}
-
 inline double val(float x) { return x; }
 inline double val(double x) { return x; }
 inline double val(Dual x) { return x.v; }
-inline double val(ErrScale x) { return x.v; }
 
 inline float s_sqrt(float x) { return std::sqrt(x); }
 inline double s_sqrt(double x) { return std::sqrt(x); }
@@ -714,11 +687,9 @@ void composite_bwd_impl(int W, int H, int64_t N, const uint32_t* ranges,
 
 /* ------------------------------------------------------------------------ */
 /* Step 13b: projection backward, chain rule from (u, v), the conic and the  */
-/* colour to mean, scale, quaternion and SH coefficients.  S = S is the */
-/* reference; S = ErrScale carries, next to each value, a first-order bound  */
-/* on the rounding error an fp32 evaluation of the same expressions can      */
-/* accumulate (in units of the unit roundoff), used only to classify fp32    */
-/* cancellation in the parity tests.                                         */
+/* colour to mean, scale, quaternion and SH coefficients.  With every        */
+/* discrete decision (visibility, fov clamp, colour clamp) fixed by the      */
+/* parameters, it is linear in the 2D gradients it is given.                 */
 /* ------------------------------------------------------------------------ */
 template <class S>
 void project_bwd_one(int deg, const S* mean, const S* scale, const S* quat, const S* sh,
@@ -930,6 +901,45 @@ int64_t full_loss(int64_t N, int deg, const std::vector<T>& means, const std::ve
   return (int64_t)inst.size();
 }
 
+/* Projection backward of every Gaussian (fp64).  Culled Gaussians (radius
+ * 0) get zeros. */
+template <class S>
+void project_bwd_all(int64_t N, int deg, const double* means, const double* scales,
+                     const double* quats, const double* sh, const orc_camera& camd,
+                     const orc_settings& st, const int32_t* radii, const double* g_means2d,
+                     const double* g_conics, const double* g_colors, double* g_means,
+                     double* g_scales, double* g_quats, double* g_sh) {
+  const int K = (deg + 1) * (deg + 1);
+  Cam<S> cam = cam_as<S>(camd);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) {
+    double* gm = &g_means[3 * i];
+    double* gs = &g_scales[3 * i];
+    double* gq = &g_quats[4 * i];
+    double* gsh = &g_sh[(size_t)K * 3 * i];
+    if (radii[i] <= 0) {
+      std::fill(gm, gm + 3, 0.0);
+      std::fill(gs, gs + 3, 0.0);
+      std::fill(gq, gq + 4, 0.0);
+      std::fill(gsh, gsh + 3 * K, 0.0);
+      continue;
+    }
+    S m[3], sc[3], q[4], shv[48], gm2[2], gc[3], gcol[3], om[3], os[3], oq[4], osh[48];
+    for (int k = 0; k < 3; ++k) { m[k] = S(means[3 * i + k]); sc[k] = S(scales[3 * i + k]); }
+    for (int k = 0; k < 4; ++k) q[k] = S(quats[4 * i + k]);
+    for (int k = 0; k < 3 * K; ++k) shv[k] = S(sh[(size_t)K * 3 * i + k]);
+    for (int k = 0; k < 2; ++k) gm2[k] = S(g_means2d[2 * i + k]);
+    for (int k = 0; k < 3; ++k) {
+      gc[k] = S(g_conics[3 * i + k]);
+      gcol[k] = S(g_colors[3 * i + k]);
+    }
+    project_bwd_one(deg, m, sc, q, shv, cam, st, gm2, gc, gcol, om, os, oq, osh);
+    for (int k = 0; k < 3; ++k) { gm[k] = val(om[k]); gs[k] = val(os[k]); }
+    for (int k = 0; k < 4; ++k) gq[k] = val(oq[k]);
+    for (int k = 0; k < 3 * K; ++k) gsh[k] = val(osh[k]);
+  }
+}
+
 }  // namespace
 
 /* ======================================================================== */
@@ -1084,64 +1094,50 @@ int orc_project_bwd(int64_t N, int deg, const double* means, const double* scale
                     const orc_settings* st, const int32_t* radii, const double* g_means2d,
                     const double* g_conics, const double* g_colors, double* g_means,
                     double* g_scales, double* g_quats, double* g_sh) {
-  const int K = (deg + 1) * (deg + 1);
-  Cam<double> cam = cam_as<double>(*camd);
-#pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < N; ++i) {
-    double* gm = &g_means[3 * i];
-    double* gs = &g_scales[3 * i];
-    double* gq = &g_quats[4 * i];
-    double* gsh = &g_sh[(size_t)K * 3 * i];
-    if (radii[i] <= 0) {
-      std::fill(gm, gm + 3, 0.0);
-      std::fill(gs, gs + 3, 0.0);
-      std::fill(gq, gq + 4, 0.0);
-      std::fill(gsh, gsh + 3 * K, 0.0);
-      continue;
-    }
-    project_bwd_one(deg, &means[3 * i], &scales[3 * i], &quats[4 * i], &sh[(size_t)K * 3 * i],
-                    cam, *st, &g_means2d[2 * i], &g_conics[3 * i], &g_colors[3 * i], gm, gs, gq,
-                    gsh);
-  }
+  project_bwd_all<double>(N, deg, means, scales, quats, sh, *camd, *st, radii, g_means2d,
+                          g_conics, g_colors, g_means, g_scales, g_quats, g_sh);
   return 0;
 }
 
-int orc_project_bwd_errscale(int64_t N, int deg, const double* means, const double* scales,
-                             const double* quats, const double* sh, const orc_camera* camd,
-                             const orc_settings* st, const int32_t* radii,
-                             const double* g_means2d, const double* g_conics,
-                             const double* g_colors, const double* s_means2d,
-                             const double* s_conics, const double* s_colors, double* e_means,
-                             double* e_scales, double* e_quats, double* e_sh) {
+int orc_project_bwd_bound(int64_t N, int deg, const double* means, const double* scales,
+                          const double* quats, const double* sh, const orc_camera* camd,
+                          const orc_settings* st, const int32_t* radii,
+                          const double* s_means2d, const double* s_conics,
+                          const double* s_colors, double* e_means, double* e_scales,
+                          double* e_quats, double* e_sh) {
   const int K = (deg + 1) * (deg + 1);
-  Cam<ErrScale> cam = cam_as<ErrScale>(*camd);
+  Cam<double> cam = cam_as<double>(*camd);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < N; ++i) {
     double* em = &e_means[3 * i];
     double* es = &e_scales[3 * i];
     double* eq = &e_quats[4 * i];
     double* esh = &e_sh[(size_t)K * 3 * i];
-    if (radii[i] <= 0) {
-      std::fill(em, em + 3, 0.0);
-      std::fill(es, es + 3, 0.0);
-      std::fill(eq, eq + 4, 0.0);
-      std::fill(esh, esh + 3 * K, 0.0);
-      continue;
+    std::fill(em, em + 3, 0.0);
+    std::fill(es, es + 3, 0.0);
+    std::fill(eq, eq + 4, 0.0);
+    std::fill(esh, esh + 3 * K, 0.0);
+    if (radii[i] <= 0) continue;
+    const double* mean = &means[3 * i];
+    const double* scale = &scales[3 * i];
+    const double* quat = &quats[4 * i];
+    const double* shv = &sh[(size_t)K * 3 * i];
+    /* column k of the Jacobian = the backward of the k-th unit 2D gradient
+     * (u, v, A, B, C, r, g, b); each output's bound adds |column| * s_k */
+    const double s_in[8] = {s_means2d[2 * i], s_means2d[2 * i + 1], s_conics[3 * i],
+                            s_conics[3 * i + 1], s_conics[3 * i + 2], s_colors[3 * i],
+                            s_colors[3 * i + 1], s_colors[3 * i + 2]};
+    for (int k = 0; k < 8; ++k) {
+      if (s_in[k] == 0.0) continue;
+      double g2[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      g2[k] = 1.0;
+      double om[3], os[3], oq[4], osh[48];
+      project_bwd_one(deg, mean, scale, quat, shv, cam, *st, &g2[0], &g2[2], &g2[5], om, os,
+                      oq, osh);
+      for (int j = 0; j < 3; ++j) { em[j] += std::fabs(om[j]) * s_in[k]; es[j] += std::fabs(os[j]) * s_in[k]; }
+      for (int j = 0; j < 4; ++j) eq[j] += std::fabs(oq[j]) * s_in[k];
+      for (int j = 0; j < 3 * K; ++j) esh[j] += std::fabs(osh[j]) * s_in[k];
     }
-    ErrScale m[3], sc[3], q[4], shv[48], gm2[2], gc[3], gcol[3];
-    ErrScale om[3], os[3], oq[4], osh[48];
-    for (int k = 0; k < 3; ++k) { m[k] = ErrScale(means[3 * i + k]); sc[k] = ErrScale(scales[3 * i + k]); }
-    for (int k = 0; k < 4; ++k) q[k] = ErrScale(quats[4 * i + k]);
-    for (int k = 0; k < 3 * K; ++k) shv[k] = ErrScale(sh[(size_t)K * 3 * i + k]);
-    for (int k = 0; k < 2; ++k) gm2[k] = ErrScale(g_means2d[2 * i + k], s_means2d[2 * i + k]);
-    for (int k = 0; k < 3; ++k) {
-      gc[k] = ErrScale(g_conics[3 * i + k], s_conics[3 * i + k]);
-      gcol[k] = ErrScale(g_colors[3 * i + k], s_colors[3 * i + k]);
-    }
-    project_bwd_one(deg, m, sc, q, shv, cam, *st, gm2, gc, gcol, om, os, oq, osh);
-    for (int k = 0; k < 3; ++k) { em[k] = om[k].m; es[k] = os[k].m; }
-    for (int k = 0; k < 4; ++k) eq[k] = oq[k].m;
-    for (int k = 0; k < 3 * K; ++k) esh[k] = osh[k].m;
   }
   return 0;
 }

@@ -117,22 +117,22 @@ int orc_project_bwd(int64_t N, int sh_degree, const double* means,
                     const double* g_colors, double* g_means, double* g_scales,
                     double* g_quats, double* g_sh);
 
-/* First-order rounding-error scales of the projection backward: the same
- * chain rule evaluated on (value, scale) pairs, where a sum adds scales and
- * products/quotients propagate them to first order.  The inputs' scales are
- * given (s_* arrays, e.g. |g| or |g| plus an error allowance divided by the
- * unit roundoff); an IEEE fp32 evaluation of these expressions from the same
- * inputs errs by about unit_roundoff * e_* at most.  Used by the parity tests
- * to tell fp32 cancellation from real disagreement. */
-int orc_project_bwd_errscale(int64_t N, int sh_degree, const double* means,
-                             const double* scales, const double* quats,
-                             const double* sh, const orc_camera* cam,
-                             const orc_settings* st, const int32_t* radii,
-                             const double* g_means2d, const double* g_conics,
-                             const double* g_colors, const double* s_means2d,
-                             const double* s_conics, const double* s_colors,
-                             double* e_means, double* e_scales, double* e_quats,
-                             double* e_sh);
+/* Sensitivity bound of the projection backward to its 2D gradient inputs.
+ * With the discrete decisions fixed by the parameters, orc_project_bwd is
+ * linear in (g_means2d, g_conics, g_colors), so changing those inputs by
+ * d with |d_k| <= s_k changes each output o by at most
+ *   e_o = sum_k |d o / d g2_k| s_k,
+ * and exactly that much for d_k = s_k sign(d o / d g2_k).  Writes e for
+ * every output (zeros for culled Gaussians).  The parity tests use it to
+ * bound what a projection backward inherits from 2D gradients known only to
+ * within s (fp32 rounding, or the 2D tolerance end to end). */
+int orc_project_bwd_bound(int64_t N, int sh_degree, const double* means,
+                          const double* scales, const double* quats,
+                          const double* sh, const orc_camera* cam,
+                          const orc_settings* st, const int32_t* radii,
+                          const double* s_means2d, const double* s_conics,
+                          const double* s_colors, double* e_means, double* e_scales,
+                          double* e_quats, double* e_sh);
 
 /* Whole forward in fp64 (or with forward-mode dual numbers when any
  * direction pointer is non-NULL) followed by the loss against target

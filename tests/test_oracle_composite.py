@@ -195,3 +195,56 @@ def test_order_independence():
     f2 = oracle.render(scene.subset(perm), cam)
     np.testing.assert_array_equal(f1["raster"]["image"], f2["raster"]["image"])
     np.testing.assert_array_equal(f1["raster"]["final_T"], f2["raster"]["final_T"])
+
+
+def _margin_at_centre(opacities):
+    """Margin of pixel (5, 9) of a 16x16 image whose one tile lists the given
+    splats front to back, each centred on that pixel (so G = 1 there and
+    alpha = min(alpha_max, o) exactly), with the fp32 default constants."""
+    n = len(opacities)
+    means2d = np.tile([5.5, 9.5], (n, 1))
+    chol = np.tile([0.7, 0.1, 0.6], (n, 1))
+    out = oracle.composite(16, 16, np.array([[0, n]]), np.arange(n), means2d, chol,
+                           np.asarray(opacities, float), np.full((n, 3), 0.5), np.ones(n),
+                           with_margin=True)
+    return out["margin"][9, 5], out["last"][9, 5]
+
+
+def test_margin_is_the_distance_to_the_nearest_threshold():
+    """The compositing margin (the parity tests' threshold-flip classifier) is
+    the smallest relative distance |x - t| / t of a decision the pixel took:
+    alpha against alpha_min, o G against alpha_max, T (1 - alpha) against
+    T_min.  Pixels are built at known distances from each threshold."""
+    for d in (1e-3, 1e-5, -1e-5, -1e-3):
+        # alpha just above / below alpha_min (below: skipped, nothing blended)
+        m, last = _margin_at_centre([A_MIN * (1 + d)])
+        assert abs(m - abs(d)) <= 1e-9 * abs(d), (d, m)
+        assert last == (1 if d > 0 else 0)
+        # o G just below / above alpha_max (above: clamped to alpha_max)
+        m, last = _margin_at_centre([A_MAX * (1 + d)])
+        assert abs(m - abs(d)) <= 1e-9 * abs(d), (d, m)
+        assert last == 1
+        # T' just above / below T_min after three layers of 0.9 (below: stop)
+        T3 = ((1.0 * (1 - 0.9)) * (1 - 0.9)) * (1 - 0.9)
+        o4 = 1.0 - T_MIN * (1 + d) / T3
+        m, last = _margin_at_centre([0.9, 0.9, 0.9, o4])
+        assert abs(m - abs(d)) <= 1e-9 * abs(d), (d, m)
+        assert last == (4 if d > 0 else 3)
+
+
+def test_margin_counts_skips_but_not_pairs_after_the_stop():
+    # a skipped pair's distance counts: 2e-5 below alpha_min, then a plain layer
+    m, last = _margin_at_centre([A_MIN * (1 - 2e-5), 0.5])
+    assert abs(m - 2e-5) <= 1e-12 and last == 2
+    # after the stop nothing is evaluated: the pair 1e-6 above alpha_min
+    # behind it does not count; the nearest decision is then the stopping
+    # pair's own o G = 0.95 against alpha_max
+    T3 = ((1.0 * (1 - 0.9)) * (1 - 0.9)) * (1 - 0.9)
+    stop = 1.0 - 0.5 * T_MIN / T3
+    m, last = _margin_at_centre([0.9, 0.9, 0.9, stop, A_MIN * (1 + 1e-6)])
+    assert abs(m - abs(stop - A_MAX) / A_MAX) <= 1e-12 and last == 3
+    # a pixel with no list has no decision: infinite margin
+    out = oracle.composite(16, 16, np.array([[0, 0]]), np.zeros(0, np.uint32), np.zeros((0, 2)),
+                           np.zeros((0, 3)), np.zeros(0), np.zeros((0, 3)), np.zeros(0),
+                           with_margin=True)
+    assert np.all(np.isinf(out["margin"]))
