@@ -345,9 +345,10 @@ def _inherited(r, s_m2, s_con, s_col):
 
 def _classify_3d(r, g, o, e, rows, what):
     """3D gradients outside max(1e-3 |g|, 1e-5): explained if within the
-    inherited bound e plus the fp32 output rounding (counted, bounded), or
-    exempt if the Gaussian is reached by a near-threshold pixel (counted,
-    bounded); nothing else may fail."""
+    inherited bound e plus the fp32 output rounding (counted, bounded), else
+    exempt if the Gaussian is reached by a near-threshold pixel, whose 2D
+    gradients may lie outside the allowance e assumes (counted, bounded);
+    nothing else may fail."""
     n = r["scene"].n
     for k in ("means", "scales", "quats", "sh"):
         gg = np.asarray(g["g_" + k], np.float64).reshape(n, -1)
@@ -355,9 +356,9 @@ def _classify_3d(r, g, o, e, rows, what):
         ee = e[k].reshape(n, -1)
         err = np.abs(gg - oo)
         bad = err > np.maximum(G_REL * np.abs(oo), G_ABS)
-        flip = bad & rows[:, None]
-        inh = bad & ~flip & (err <= ee + 2 * EPS32 * np.abs(oo))
-        unexplained = bad & ~flip & ~inh
+        inh = bad & (err <= ee + 2 * EPS32 * np.abs(oo))
+        flip = bad & ~inh & rows[:, None]
+        unexplained = bad & ~inh & ~flip
         print("[parity] %s %s %s: outside tol %d (flip rows %d, inherited %d) of %d" %
               (r["name"], what, k, bad.sum(), flip.sum(), inh.sum(), bad.size))
         assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])
