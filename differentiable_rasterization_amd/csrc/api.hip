@@ -6,7 +6,13 @@
 
 #include <cmath>
 
+#include <mutex>
+
 #include "gs_common.h"
+
+// The scratch of gs_bin_and_sort_noalloc (see noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 extern "C" {
 hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
@@ -135,6 +141,77 @@ bool aligned64(const void* p) { return ((uintptr_t)p & 63u) == 0; }
     if (_s != GS_OK) return _s;      \
   } while (0)
 
+gs_status check_bin_args(int64_t N, int64_t ld, const float* means2d, const int32_t* radii,
+                         const float* depths, const uint32_t* tiles_touched, int32_t width,
+                         int32_t height, uint32_t* offsets, uint64_t capacity,
+                         uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                         uint32_t* tile_ranges) {
+  GS_CHECK(check_sizes(N, ld));
+  GS_CHECK(check_image(width, height));
+  GS_REQUIRE(num_instances != nullptr, "num_instances is NULL");
+  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
+  if (N > 0)
+    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets, "NULL array pointer");
+  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
+  return GS_OK;
+}
+
+// Scan, read M back, then duplicate, sort and extract the ranges, with the
+// sort's scratch in `workspace` (at least gs_binsort_workspace_bytes).
+gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const int32_t* radii,
+                            const float* depths, const uint32_t* tiles_touched, int32_t width,
+                            int32_t height, uint32_t* offsets, uint64_t capacity,
+                            uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                            uint32_t* tile_ranges, void* workspace, hipStream_t s,
+                            const char* name) {
+  const int32_t T = gs_num_tiles(width, height);
+  gs_status st = hip_status(
+      gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace, capacity, T, num_instances,
+                     s),
+      name);
+  if (st != GS_OK) return st;
+  const uint64_t M = *num_instances;
+  if (M >= ((uint64_t)1 << 30))
+    return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
+  if (M > capacity) {
+    snprintf(g_err, sizeof(g_err), "%s: %llu instances exceed capacity %llu", name,
+             (unsigned long long)M, (unsigned long long)capacity);
+    return GS_ERR_CAPACITY;
+  }
+  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
+                                              offsets, width, height, 1, M, false, nullptr, keys,
+                                              ids, tile_ranges, workspace, capacity, s),
+                    name);
+}
+
+// Scratch of gs_bin_and_sort_noalloc: a file-scope device array, so that the
+// call never allocates.  Each device holds its own copy at its own address;
+// the host-side name is only a stand-in, so the address is looked up once
+// per device with hipGetSymbolAddress and kept.  Calls on one device share
+// the array (overlapping calls there race).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gs_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gs_bin_and_sort_noalloc(hipGetDevice)");
+  GS_REQUIRE(dev >= 0 && dev < kMaxDevices, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "gs_bin_and_sort_noalloc(hipGetSymbolAddress)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,38 +279,39 @@ gs_status gs_bin_and_sort(int64_t N, int64_t ld, const float* means2d, const int
                           uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
                           uint32_t* tile_ranges, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  GS_CHECK(check_sizes(N, ld));
-  GS_CHECK(check_image(width, height));
-  GS_REQUIRE(num_instances != nullptr, "num_instances is NULL");
-  GS_REQUIRE(tile_ranges != nullptr, "tile_ranges is NULL");
+  GS_CHECK(check_bin_args(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                          capacity, num_instances, keys, ids, tile_ranges));
   GS_REQUIRE(workspace != nullptr, "workspace is NULL");
   GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
-  GS_REQUIRE(capacity < ((uint64_t)1 << 30), "capacity must be < 2^30");
-  if (N > 0)
-    GS_REQUIRE(means2d && radii && depths && tiles_touched && offsets, "NULL array pointer");
-  if (capacity > 0) GS_REQUIRE(keys && ids, "keys/ids are NULL");
-  const int32_t T = gs_num_tiles(width, height);
-  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
+  GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, gs_num_tiles(width, height)),
              "workspace smaller than gs_bin_and_sort_workspace_size()");
-  hipStream_t s = (hipStream_t)stream;
-  gs_status st = hip_status(
-      gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace, capacity, T, num_instances,
-                     s),
-      "gs_bin_and_sort(scan)");
-  if (st != GS_OK) return st;
-  const uint64_t M = *num_instances;
-  if (M >= ((uint64_t)1 << 30))
-    return fail(GS_ERR_INVALID_ARGUMENT, "%s", "tile instance count must be < 2^30");
-  if (M > capacity) {
-    snprintf(g_err, sizeof(g_err), "gs_bin_and_sort: %llu instances exceed capacity %llu",
-             (unsigned long long)M, (unsigned long long)capacity);
-    return GS_ERR_CAPACITY;
+  return bin_and_sort_impl(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                           capacity, num_instances, keys, ids, tile_ranges, workspace,
+                           (hipStream_t)stream, "gs_bin_and_sort");
+}
+
+gs_status gs_bin_and_sort_noalloc(int64_t N, int64_t ld, const float* means2d,
+                                  const int32_t* radii, const float* depths,
+                                  const uint32_t* tiles_touched, int32_t width, int32_t height,
+                                  uint32_t* offsets, uint64_t capacity, uint64_t* num_instances,
+                                  uint64_t* keys, uint32_t* ids, uint32_t* tile_ranges,
+                                  void* stream) {
+  GS_CHECK(check_bin_args(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                          capacity, num_instances, keys, ids, tile_ranges));
+  const size_t need = gs_binsort_workspace_bytes(N, capacity, gs_num_tiles(width, height));
+  if (need > kNoAllocScratchBytes) {
+    snprintf(g_err, sizeof(g_err),
+             "gs_bin_and_sort_noalloc: N = %lld, capacity = %llu and a %dx%d image need %zu "
+             "bytes of scratch, more than its %zu",
+             (long long)N, (unsigned long long)capacity, (int)width, (int)height, need,
+             kNoAllocScratchBytes);
+    return GS_ERR_INVALID_ARGUMENT;
   }
-  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, false, nullptr, keys, ids,
-                                              tile_ranges,
-                                              workspace, capacity, s),
-                    "gs_bin_and_sort");
+  void* ws = nullptr;
+  GS_CHECK(noalloc_scratch(&ws));
+  return bin_and_sort_impl(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
+                           capacity, num_instances, keys, ids, tile_ranges, ws,
+                           (hipStream_t)stream, "gs_bin_and_sort_noalloc");
 }
 
 gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,

@@ -33,7 +33,7 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
             "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
             "gs_bin_and_sort_device", "gs_rasterize_fwd_loss", "gs_tile_order",
-            "gs_rasterize_fwd_loss_batched")
+            "gs_rasterize_fwd_loss_batched", "gs_bin_and_sort_noalloc")
 
 
 class GsError(RuntimeError):
@@ -129,6 +129,9 @@ def load():
     lib.gs_project_bwd_batched.restype = C.c_int
     lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 2 + \
         [P] * 5 + [i32, P]
+    lib.gs_bin_and_sort_noalloc.restype = C.c_int
+    lib.gs_bin_and_sort_noalloc.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
+                                            P]
     lib.gs_bin_and_sort_device.restype = C.c_int
     lib.gs_bin_and_sort_device.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                            C.c_size_t, P]
@@ -226,6 +229,23 @@ def gs_bin_and_sort(N, ld, means2d, radii, depths, tiles_touched, width, height,
     st = lib.gs_bin_and_sort(N, ld, _p(means2d), _p(radii), _p(depths), _p(tiles_touched),
                              width, height, _p(offsets), capacity, out, _p(keys), _p(ids),
                              _p(tile_ranges), _p(workspace), workspace_bytes, _stream(stream))
+    if st not in (GS_OK, GS_ERR_CAPACITY):
+        _check(st)
+    return st, int(M.value) if num_instances is None else int(num_instances[0])
+
+
+def gs_bin_and_sort_noalloc(N, ld, means2d, radii, depths, tiles_touched, width, height,
+                            offsets, capacity, keys, ids, tile_ranges, stream=None,
+                            num_instances=None):
+    """gs_bin_and_sort with the library's own scratch (no workspace, no
+    allocation).  Returns (status, M); GS_ERR_CAPACITY is returned, not
+    raised."""
+    lib = load()
+    M = C.c_uint64(0)
+    out = C.byref(M) if num_instances is None else _p(num_instances)
+    st = lib.gs_bin_and_sort_noalloc(N, ld, _p(means2d), _p(radii), _p(depths),
+                                     _p(tiles_touched), width, height, _p(offsets), capacity, out,
+                                     _p(keys), _p(ids), _p(tile_ranges), _stream(stream))
     if st not in (GS_OK, GS_ERR_CAPACITY):
         _check(st)
     return st, int(M.value) if num_instances is None else int(num_instances[0])

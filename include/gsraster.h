@@ -18,7 +18,9 @@
  * Conventions shared by every entry point
  *   - Device pointers unless marked HOST.  Every buffer is owned by the
  *     caller; the library allocates nothing and keeps no state between calls
- *     (calls on different streams may run concurrently on distinct buffers).
+ *     (calls on different streams may run concurrently on distinct buffers),
+ *     except for the scratch array of gs_bin_and_sort_noalloc, described
+ *     there.
  *   - Per-Gaussian arrays are fp32/int32 structure-of-arrays planes with a
  *     leading dimension ld >= N: plane p of array X starts at X + p*ld.
  *       means [3][ld] (world x,y,z)   scales [3][ld] (activated, > 0)
@@ -180,6 +182,28 @@ GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* mean
                                         uint64_t* counts, uint64_t* keys, uint32_t* ids,
                                         uint32_t* tile_ranges, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* gs_bin_and_sort for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the sort's scratch in
+ * a 64 MiB array inside the library instead of a workspace argument.  The
+ * caller still passes every input and output.  Limit: the
+ * gs_bin_and_sort_workspace_size() of (N, capacity, width, height) must be
+ * at most 64 MiB (capacity up to about 4.8 million instances for a million
+ * Gaussians at 1920x1080); larger requests return GS_ERR_INVALID_ARGUMENT
+ * before anything runs.  The call allocates nothing: each device holds its
+ * own copy of the array from the library's first use on it until the
+ * process ends.  Every call on one device uses that device's array, so calls
+ * that overlap on one device (other streams, other host threads) race; the
+ * array keeps the last call's contents, and each call clears what must start
+ * at zero itself.  Otherwise as gs_bin_and_sort, including the one
+ * device-to-host read of M and the GS_ERR_CAPACITY protocol. */
+GS_API gs_status gs_bin_and_sort_noalloc(int64_t N, int64_t ld, const float* means2d,
+                                         const int32_t* radii, const float* depths,
+                                         const uint32_t* tiles_touched, int32_t width,
+                                         int32_t height, uint32_t* offsets, uint64_t capacity,
+                                         uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
+                                         uint32_t* tile_ranges, void* stream);
 
 /* Schedule of the compositing kernels (no step of the method: a launch
  * order).  For each of num_cams cameras, tile_order (DEVICE uint32

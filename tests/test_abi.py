@@ -118,6 +118,26 @@ def test_bin_and_sort_rejects_bad_arguments(lib):
     assert call(cap=1 << 30) == raster.GS_ERR_INVALID_ARGUMENT
 
 
+def test_bin_and_sort_noalloc_rejects_bad_and_oversized_arguments(lib):
+    dummy = C.c_void_p(256)
+    M = C.c_uint64(0)
+    base = dict(N=4, ld=4, W=64, H=64, cap=100)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.gs_bin_and_sort_noalloc(a["N"], a["ld"], dummy, dummy, dummy, dummy, a["W"],
+                                           a["H"], dummy, a["cap"], C.byref(M), dummy, dummy,
+                                           dummy, None)
+    assert call(ld=3) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(W=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert call(cap=1 << 30) == raster.GS_ERR_INVALID_ARGUMENT
+    # scratch beyond the library's 64 MiB: refused on the host, with the sizes
+    big = 6_000_000
+    assert raster.gs_bin_and_sort_workspace_size(4, big, 64, 64) > 64 << 20
+    assert call(cap=big) == raster.GS_ERR_INVALID_ARGUMENT
+    assert b"more than its 67108864" in lib.gs_last_error()
+
+
 def test_raster_and_loss_reject_bad_arguments(lib):
     dummy = C.c_void_p(64)
     st = raster.default_settings()
