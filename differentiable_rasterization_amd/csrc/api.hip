@@ -16,20 +16,18 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 extern "C" {
 hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
-                                 const float* scales, const float* quats, const float* opac,
-                                 const float* sh, int ncams, const gs::Cam* cams,
-                                 const gs::Settings& st,
-                                 float* means2d, float* conics, float* depths, int32_t* radii,
-                                 float* colors, uint32_t* tiles, float* splats,
-                                 hipStream_t stream);
-hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids, int64_t ldo,
-                                 int deg, const float* means,
                                  const float* scales, const float* quats, const float* sh,
                                  int ncams, const gs::Cam* cams, const gs::Settings& st,
-                                 const int32_t* radii,
-                                 const float* grads2d, float* o_means, float* o_scales,
-                                 float* o_quats, float* o_opac, float* o_sh, int accumulate,
+                                 float* means2d, float* conics, float* chol, float* depths,
+                                 int32_t* radii, float* colors, uint32_t* tiles,
                                  hipStream_t stream);
+hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids, int64_t ldo,
+                                 int deg, const float* means, const float* scales,
+                                 const float* quats, const float* sh, int ncams,
+                                 const gs::Cam* cams, const gs::Settings& st,
+                                 const int32_t* radii, const gs::Grad2D& g, float* o_means,
+                                 float* o_scales, float* o_quats, float* o_opac, float* o_sh,
+                                 int accumulate, hipStream_t stream);
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
 hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, uint32_t* vis_ids,
                           void* workspace, uint64_t capacity, int32_t T, uint64_t* totals_host,
@@ -43,6 +41,10 @@ hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d
                                      hipStream_t s);
 hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
                                 uint32_t* order, hipStream_t s);
+hipError_t gs_launch_pack_splats(int64_t rows, int64_t ld, const float* means2d,
+                                 const float* conics, const float* chol, const float* opac,
+                                 const float* colors, const int32_t* radii, float alpha_min,
+                                 float* rec, hipStream_t s);
 hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
                                 const uint32_t* order, const uint32_t* ids, const float* splats,
                                 const float* depths,
@@ -56,7 +58,7 @@ hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
                                 const uint32_t* tiles, const float* bg, const gs::Settings& st,
                                 const float* final_T, const uint32_t* last_idx,
                                 const float* dL_dimage, float* partials, uint64_t capacity,
-                                float* grads2d, int absgrad, const uint32_t* vis_ids,
+                                const gs::Grad2D& g, int accumulate, const uint32_t* vis_ids,
                                 int64_t num_visible, uint64_t* counters, hipStream_t s);
 hipError_t gs_launch_loss_grad(int kind, int64_t n, const float* img, const float* tgt, float* g,
                                float* loss, hipStream_t s);
@@ -185,6 +187,97 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
                     name);
 }
 
+gs_status check_batch(int32_t num_cams, int64_t ld) {
+  GS_REQUIRE(num_cams >= 1 && num_cams <= gs::kMaxCams, "num_cams must be in [1, 8]");
+  GS_REQUIRE((int64_t)num_cams * ld < ((int64_t)1 << 31), "num_cams * ld must be < 2^31");
+  return GS_OK;
+}
+
+size_t staging_bytes(int64_t rows) { return (size_t)(rows > 0 ? rows : 1) * 64; }
+
+// Arguments shared by the compositing calls: `rows` splat rows are staged
+// (N for one camera, ncams * ld for a batch).
+gs_status check_raster_common(int ncams, int64_t rows, int64_t N, int64_t ld, int32_t width,
+                              int32_t height,
+                              const uint32_t* tile_ranges, const uint32_t* ids,
+                              const float* means2d, const float* conics, const float* chol,
+                              const float* opacities, const float* colors, const int32_t* radii,
+                              const float* background, const gs_settings* settings,
+                              const float* final_T, const uint32_t* last_idx, void* workspace,
+                              size_t workspace_bytes) {
+  GS_CHECK(check_sizes(N, ld));
+  if (ncams > 1) GS_CHECK(check_batch(ncams, ld));
+  GS_CHECK(check_image(width, height));
+  GS_CHECK(check_settings(settings));
+  GS_REQUIRE((int64_t)ncams * width * height < ((int64_t)1 << 31), "images too large");
+  GS_REQUIRE(background != nullptr, "background is NULL");
+  GS_REQUIRE(tile_ranges && final_T && last_idx, "NULL range, T or last-index pointer");
+  if (rows > 0) {
+    GS_REQUIRE(ids && means2d && conics && chol && opacities && colors && radii,
+               "NULL plane or id pointer");
+    GS_REQUIRE(workspace != nullptr, "workspace is NULL");
+    GS_REQUIRE(((uintptr_t)workspace & 255u) == 0, "workspace must be 256-byte aligned");
+    GS_REQUIRE(workspace_bytes >= staging_bytes(rows),
+               "workspace smaller than gs_rasterize_workspace_size()");
+  }
+  return GS_OK;
+}
+
+gs_status check_fwd(int ncams, int64_t rows, int64_t N, int64_t ld, int32_t width,
+                    int32_t height,
+                    const uint32_t* tile_ranges, const uint32_t* ids, const float* means2d,
+                    const float* conics, const float* chol, const float* opacities,
+                    const float* colors, const int32_t* radii, const float* depths,
+                    const float* background, const gs_settings* settings, float* image,
+                    float* final_T, uint32_t* last_idx, float* out_depth, void* workspace,
+                    size_t workspace_bytes) {
+  GS_CHECK(check_raster_common(ncams, rows, N, ld, width, height, tile_ranges, ids, means2d,
+                               conics, chol, opacities, colors, radii, background, settings,
+                               final_T, last_idx, workspace, workspace_bytes));
+  GS_REQUIRE(image != nullptr, "image is NULL");
+  if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
+  return GS_OK;
+}
+
+gs_status check_loss(int32_t kind, const float* target, const float* image,
+                     const float* dL_dimage) {
+  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
+  GS_REQUIRE(target && dL_dimage, "NULL target or gradient pointer");
+  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
+  return GS_OK;
+}
+
+// out_rows: rows of the 2D gradient planes written (N for one camera,
+// ncams * ld for a batch, the visible count for packed rows).
+gs_status check_bwd(int ncams, int64_t rows, int64_t N, int64_t ld, int64_t out_rows,
+                    int32_t width, int32_t height, const uint32_t* tile_ranges, const uint32_t* ids,
+                    const float* means2d, const float* conics, const float* chol,
+                    const float* opacities, const float* colors, const int32_t* radii,
+                    const uint32_t* offsets, const uint32_t* tiles_touched,
+                    uint64_t num_instances, const float* background,
+                    const gs_settings* settings, const float* final_T, const uint32_t* last_idx,
+                    const float* dL_dimage, void* workspace, size_t workspace_bytes,
+                    int32_t staged, float* partials, uint64_t partials_capacity,
+                    float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
+                    float* dL_dcolors, int32_t accumulate) {
+  GS_CHECK(check_raster_common(ncams, rows, N, ld, width, height, tile_ranges, ids, means2d,
+                               conics, chol, opacities, colors, radii, background, settings,
+                               final_T, last_idx, workspace, workspace_bytes));
+  GS_REQUIRE(dL_dimage != nullptr, "dL_dimage is NULL");
+  GS_REQUIRE(staged == 0 || staged == 1, "staged must be 0 or 1");
+  GS_REQUIRE(accumulate >= 0 && accumulate <= 2, "accumulate must be 0, 1 or 2");
+  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
+  if (rows > 0) GS_REQUIRE(offsets && tiles_touched, "NULL offset or tile-count pointer");
+  if (out_rows > 0)
+    GS_REQUIRE(dL_dmeans2d && dL_dconics && dL_dopacities && dL_dcolors,
+               "NULL gradient plane pointer");
+  if (num_instances > 0) {
+    GS_REQUIRE(partials != nullptr, "partials is NULL");
+    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
+  }
+  return GS_OK;
+}
+
 // Scratch of gs_bin_and_sort_noalloc: a file-scope device array, so that the
 // call never allocates.  Each device holds its own copy at its own address;
 // the host-side name is only a stand-in, so the address is looked up once
@@ -245,25 +338,23 @@ int32_t gs_num_tiles(int32_t width, int32_t height) {
 }
 
 gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
-                         const float* scales, const float* quats, const float* opacities,
-                         const float* sh, const gs_camera* cam, const gs_settings* settings,
-                         float* means2d, float* conics, float* depths, int32_t* radii,
-                         float* colors, uint32_t* tiles_touched, float* splats, void* stream) {
+                         const float* scales, const float* quats, const float* sh,
+                         const gs_camera* cam, const gs_settings* settings, float* means2d,
+                         float* conics, float* chol, float* depths, int32_t* radii,
+                         float* colors, uint32_t* tiles_touched, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
   GS_CHECK(check_camera(cam));
   GS_CHECK(check_settings(settings));
-  if (N > 0) {
-    GS_REQUIRE(means && scales && quats && opacities && sh && means2d && conics && depths &&
-                   radii && colors && tiles_touched && splats,
+  if (N > 0)
+    GS_REQUIRE(means && scales && quats && sh && means2d && conics && chol && depths && radii &&
+                   colors && tiles_touched,
                "NULL array pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-  }
   const gs::Cam c = gs::make_cam(*cam);
-  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh,
-                                          1, &c, gs::make_settings(*settings),
-                                          means2d, conics, depths, radii, colors, tiles_touched,
-                                          splats, (hipStream_t)stream),
+  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, sh, 1, &c,
+                                          gs::make_settings(*settings), means2d, conics, chol,
+                                          depths, radii, colors, tiles_touched,
+                                          (hipStream_t)stream),
                     "gs_project_fwd");
 }
 
@@ -356,118 +447,116 @@ gs_status gs_tile_order(int32_t num_cams, int32_t width, int32_t height,
                     "gs_tile_order");
 }
 
+size_t gs_rasterize_workspace_size(int64_t rows) {
+  if (rows < 0) return 0;
+  return (size_t)(rows > 0 ? rows : 1) * 64;
+}
+
 gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids, const float* splats,
-                           const float* depths, const float* background,
-                           const gs_settings* settings, float* image,
-                           float* final_T, uint32_t* last_idx, float* out_depth, float* out_alpha,
-                           uint64_t* counters, void* stream) {
-  GS_CHECK(check_sizes(N, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
-  if (N > 0) {
-    GS_REQUIRE(ids && splats, "NULL splat pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
-  }
+                           const uint32_t* tile_ranges, const uint32_t* tile_order,
+                           const uint32_t* ids, const float* means2d, const float* conics,
+                           const float* chol, const float* opacities, const float* colors,
+                           const int32_t* radii, const float* depths, const float* background,
+                           const gs_settings* settings, float* image, float* final_T,
+                           uint32_t* last_idx, float* out_depth, float* out_alpha,
+                           void* workspace, size_t workspace_bytes, uint64_t* counters,
+                           void* stream) {
+  GS_CHECK(check_fwd(1, N, N, ld, width, height, tile_ranges, ids, means2d, conics, chol,
+                     opacities, colors, radii, depths, background, settings, image, final_T,
+                     last_idx, out_depth, workspace, workspace_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  GS_CHECK(hip_status(gs_launch_pack_splats(N, ld, means2d, conics, chol, opacities, colors,
+                                            radii, settings->alpha_min, (float*)workspace, s),
+                      "gs_rasterize_fwd(stage)"));
   return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, tile_order, ids,
-                                         splats, depths,
-                                         background,
+                                         (const float*)workspace, depths, background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
                                          out_depth, out_alpha, counters, -1, nullptr, nullptr,
-                                         nullptr, (hipStream_t)stream),
+                                         nullptr, s),
                     "gs_rasterize_fwd");
 }
 
 gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                                const float* splats, const float* depths,
+                                const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                const uint32_t* ids, const float* means2d, const float* conics,
+                                const float* chol, const float* opacities, const float* colors,
+                                const int32_t* radii, const float* depths,
                                 const float* background, const gs_settings* settings,
                                 int32_t kind, const float* target, float* image, float* final_T,
                                 uint32_t* last_idx, float* out_depth, float* out_alpha,
-                                float* dL_dimage, float* loss, uint64_t* counters,
-                                void* stream) {
-  GS_CHECK(check_sizes(N, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
-  GS_REQUIRE(target && dL_dimage, "NULL target or gradient pointer");
-  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
-  if (N > 0) {
-    GS_REQUIRE(ids && splats, "NULL splat pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
-  }
+                                float* dL_dimage, float* loss, void* workspace,
+                                size_t workspace_bytes, uint64_t* counters, void* stream) {
+  GS_CHECK(check_fwd(1, N, N, ld, width, height, tile_ranges, ids, means2d, conics, chol,
+                     opacities, colors, radii, depths, background, settings, image, final_T,
+                     last_idx, out_depth, workspace, workspace_bytes));
+  GS_CHECK(check_loss(kind, target, image, dL_dimage));
+  hipStream_t s = (hipStream_t)stream;
+  GS_CHECK(hip_status(gs_launch_pack_splats(N, ld, means2d, conics, chol, opacities, colors,
+                                            radii, settings->alpha_min, (float*)workspace, s),
+                      "gs_rasterize_fwd_loss(stage)"));
   return hip_status(gs_launch_raster_fwd(width, height, 1, tile_ranges, tile_order, ids,
-                                         splats, depths,
-                                         background, gs::make_settings(*settings), image,
-                                         final_T, last_idx, out_depth, out_alpha, counters, kind,
-                                         target, dL_dimage, loss, (hipStream_t)stream),
+                                         (const float*)workspace, depths, background,
+                                         gs::make_settings(*settings), image, final_T, last_idx,
+                                         out_depth, out_alpha, counters, kind, target, dL_dimage,
+                                         loss, s),
                     "gs_rasterize_fwd_loss");
 }
 
 gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids, const float* splats,
-                           const uint32_t* offsets, const uint32_t* tiles_touched,
-                           uint64_t num_instances, const float* background,
-                           const gs_settings* settings, const float* final_T,
-                           const uint32_t* last_idx, const float* dL_dimage, float* partials,
-                           uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                           const uint32_t* tile_ranges, const uint32_t* tile_order,
+                           const uint32_t* ids, const float* means2d, const float* conics,
+                           const float* chol, const float* opacities, const float* colors,
+                           const int32_t* radii, const uint32_t* offsets,
+                           const uint32_t* tiles_touched, uint64_t num_instances,
+                           const float* background, const gs_settings* settings,
+                           const float* final_T, const uint32_t* last_idx,
+                           const float* dL_dimage, void* workspace, size_t workspace_bytes,
+                           int32_t staged, float* partials, uint64_t partials_capacity,
+                           float* dL_dmeans2d, float* dL_dconics, float* dL_dopacities,
+                           float* dL_dcolors, float* dL_dmeans2d_abs, int32_t accumulate,
                            uint64_t* counters, void* stream) {
-  GS_CHECK(check_sizes(N, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
-  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
-  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
-  if (N > 0) {
-    GS_REQUIRE(ids && splats && offsets && tiles_touched && grads2d,
-               "NULL splat, offset or gradient pointer");
-    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
-  }
-  if (num_instances > 0) {
-    GS_REQUIRE(partials != nullptr, "partials is NULL");
-    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
-  }
+  GS_CHECK(check_bwd(1, N, N, ld, N, width, height, tile_ranges, ids, means2d, conics, chol,
+                     opacities, colors, radii, offsets, tiles_touched, num_instances, background,
+                     settings, final_T, last_idx, dL_dimage, workspace, workspace_bytes, staged,
+                     partials, partials_capacity, dL_dmeans2d, dL_dconics, dL_dopacities,
+                     dL_dcolors, accumulate));
+  hipStream_t s = (hipStream_t)stream;
+  if (!staged)
+    GS_CHECK(hip_status(gs_launch_pack_splats(N, ld, means2d, conics, chol, opacities, colors,
+                                              radii, settings->alpha_min, (float*)workspace, s),
+                        "gs_rasterize_bwd(stage)"));
+  const gs::Grad2D g{dL_dmeans2d, dL_dconics, dL_dopacities, dL_dcolors, dL_dmeans2d_abs, ld};
   return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, tile_order, ids,
-                                         splats, offsets,
-                                         tiles_touched, background, gs::make_settings(*settings),
-                                         final_T, last_idx, dL_dimage, partials, num_instances,
-                                         grads2d, absgrad, nullptr, 0, counters,
-                                         (hipStream_t)stream),
+                                         (const float*)workspace, offsets, tiles_touched,
+                                         background, gs::make_settings(*settings), final_T,
+                                         last_idx, dL_dimage, partials, num_instances, g,
+                                         accumulate, nullptr, 0, counters, s),
                     "gs_rasterize_bwd");
 }
 
 gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
                          const float* scales, const float* quats, const float* sh,
                          const gs_camera* cam, const gs_settings* settings,
-                         const int32_t* radii, const float* grads2d, float* dL_dmeans,
-                         float* dL_dscales, float* dL_dquats, float* dL_dopacities,
-                         float* dL_dsh, int32_t accumulate, void* stream) {
+                         const int32_t* radii, const float* dL_dmeans2d,
+                         const float* dL_dconics, const float* dL_dcolors, float* dL_dmeans,
+                         float* dL_dscales, float* dL_dquats, float* dL_dsh,
+                         int32_t accumulate, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
   GS_CHECK(check_camera(cam));
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
-  if (N > 0) {
-    GS_REQUIRE(means && scales && quats && sh && radii && grads2d && dL_dmeans && dL_dscales &&
-                   dL_dquats && dL_dopacities && dL_dsh,
+  if (N > 0)
+    GS_REQUIRE(means && scales && quats && sh && radii && dL_dmeans2d && dL_dconics &&
+                   dL_dcolors && dL_dmeans && dL_dscales && dL_dquats && dL_dsh,
                "NULL array pointer");
-    GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
-  }
   const gs::Cam c = gs::make_cam(*cam);
+  const gs::Grad2D g{(float*)dL_dmeans2d, (float*)dL_dconics, nullptr, (float*)dL_dcolors,
+                     nullptr, ld};
   return hip_status(gs_launch_project_bwd(N, ld, nullptr, ld, sh_degree, means, scales, quats, sh,
-                                          1, &c, gs::make_settings(*settings), radii,
-                                          grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities,
-                                          dL_dsh, accumulate, (hipStream_t)stream),
+                                          1, &c, gs::make_settings(*settings), radii, g,
+                                          dL_dmeans, dL_dscales, dL_dquats, nullptr, dL_dsh,
+                                          accumulate, (hipStream_t)stream),
                     "gs_project_bwd");
 }
 
@@ -513,41 +602,44 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
 }
 
 gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
-                                  const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                                  const float* splats, const uint32_t* offsets,
+                                  const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                  const uint32_t* ids, const float* means2d,
+                                  const float* conics, const float* chol,
+                                  const float* opacities, const float* colors,
+                                  const int32_t* radii, const uint32_t* offsets,
                                   const uint32_t* tiles_touched, uint64_t num_instances,
-                                  const uint32_t* vis_ids, int64_t num_visible,
+                                  const uint32_t* vis_ids, int64_t num_visible, int64_t ldv,
                                   const float* background, const gs_settings* settings,
                                   const float* final_T, const uint32_t* last_idx,
-                                  const float* dL_dimage, float* partials,
-                                  uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                                  const float* dL_dimage, void* workspace,
+                                  size_t workspace_bytes, int32_t staged, float* partials,
+                                  uint64_t partials_capacity, float* dL_dmeans2d,
+                                  float* dL_dconics, float* dL_dopacities, float* dL_dcolors,
+                                  float* dL_dmeans2d_abs, int32_t accumulate,
                                   uint64_t* counters, void* stream) {
-  GS_CHECK(check_sizes(N, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
   GS_REQUIRE(num_visible >= 0 && num_visible <= N, "num_visible must be in [0, N]");
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
-  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
-  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
-  if (N > 0) GS_REQUIRE(ids && splats && offsets && tiles_touched, "NULL splat or offset pointer");
-  if (num_visible > 0) {
-    GS_REQUIRE(vis_ids && grads2d, "NULL vis_ids or gradient pointer");
-    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
-  }
-  if (num_instances > 0) {
-    GS_REQUIRE(partials != nullptr, "partials is NULL");
-    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
-  }
+  GS_REQUIRE(ldv >= num_visible && ldv <= ((int64_t)1 << 40), "ldv must be >= num_visible");
+  GS_CHECK(check_bwd(1, N, N, ld, num_visible, width, height, tile_ranges, ids, means2d, conics,
+                     chol, opacities, colors, radii, offsets, tiles_touched, num_instances,
+                     background, settings, final_T, last_idx, dL_dimage, workspace,
+                     workspace_bytes, staged, partials, partials_capacity, dL_dmeans2d,
+                     dL_dconics, dL_dopacities, dL_dcolors, accumulate));
+  if (num_visible > 0) GS_REQUIRE(vis_ids != nullptr, "vis_ids is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  if (!staged)
+    GS_CHECK(hip_status(gs_launch_pack_splats(N, ld, means2d, conics, chol, opacities, colors,
+                                              radii, settings->alpha_min, (float*)workspace, s),
+                        "gs_rasterize_bwd_packed(stage)"));
   // an empty list still needs a non-NULL pointer to select the packed rows
   static const uint32_t kNoIds = 0;
+  const gs::Grad2D g{dL_dmeans2d, dL_dconics, dL_dopacities, dL_dcolors, dL_dmeans2d_abs,
+                     ldv > 0 ? ldv : 1};
   return hip_status(gs_launch_raster_bwd(N, width, height, 1, tile_ranges, tile_order, ids,
-                                         splats, offsets,
-                                         tiles_touched, background, gs::make_settings(*settings),
-                                         final_T, last_idx, dL_dimage, partials, num_instances,
-                                         grads2d, absgrad, vis_ids ? vis_ids : &kNoIds,
-                                         num_visible, counters, (hipStream_t)stream),
+                                         (const float*)workspace, offsets, tiles_touched,
+                                         background, gs::make_settings(*settings), final_T,
+                                         last_idx, dL_dimage, partials, num_instances, g,
+                                         accumulate, vis_ids ? vis_ids : &kNoIds, num_visible,
+                                         counters, s),
                     "gs_rasterize_bwd_packed");
 }
 
@@ -555,8 +647,9 @@ gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, in
                                 int64_t ld, int64_t ldv, int32_t sh_degree, const float* means,
                                 const float* scales, const float* quats, const float* sh,
                                 const gs_camera* cam, const gs_settings* settings,
-                                const int32_t* radii, const float* grads2d, float* dL_dmeans,
-                                float* dL_dscales, float* dL_dquats, float* dL_dopacities,
+                                const int32_t* radii, const float* dL_dmeans2d,
+                                const float* dL_dconics, const float* dL_dcolors,
+                                float* dL_dmeans, float* dL_dscales, float* dL_dquats,
                                 float* dL_dsh, int32_t accumulate, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_REQUIRE(num_visible >= 0 && num_visible <= N, "num_visible must be in [0, N]");
@@ -567,35 +660,25 @@ gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, in
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
   if (num_visible == 0) return GS_OK;
-  GS_REQUIRE(vis_ids && means && scales && quats && sh && radii && grads2d && dL_dmeans &&
-                 dL_dscales && dL_dquats && dL_dopacities && dL_dsh,
+  GS_REQUIRE(vis_ids && means && scales && quats && sh && radii && dL_dmeans2d && dL_dconics &&
+                 dL_dcolors && dL_dmeans && dL_dscales && dL_dquats && dL_dsh,
              "NULL array pointer");
-  GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
   const gs::Cam c = gs::make_cam(*cam);
+  const gs::Grad2D g{(float*)dL_dmeans2d, (float*)dL_dconics, nullptr, (float*)dL_dcolors,
+                     nullptr, ldv};
   return hip_status(gs_launch_project_bwd(num_visible, ld, vis_ids, ldv, sh_degree, means, scales,
-                                          quats, sh, 1, &c,
-                                          gs::make_settings(*settings), radii, grads2d, dL_dmeans,
-                                          dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
+                                          quats, sh, 1, &c, gs::make_settings(*settings), radii,
+                                          g, dL_dmeans, dL_dscales, dL_dquats, nullptr, dL_dsh,
                                           accumulate, (hipStream_t)stream),
                     "gs_project_bwd_packed");
 }
 
-namespace {
-
-gs_status check_batch(int32_t num_cams, int64_t ld) {
-  GS_REQUIRE(num_cams >= 1 && num_cams <= gs::kMaxCams, "num_cams must be in [1, 8]");
-  GS_REQUIRE((int64_t)num_cams * ld < ((int64_t)1 << 31), "num_cams * ld must be < 2^31");
-  return GS_OK;
-}
-
-}  // namespace
-
 gs_status gs_project_fwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N, int64_t ld,
                                  int32_t sh_degree, const float* means, const float* scales,
-                                 const float* quats, const float* opacities, const float* sh,
+                                 const float* quats, const float* sh,
                                  const gs_settings* settings, float* means2d, float* conics,
-                                 float* depths, int32_t* radii, float* colors,
-                                 uint32_t* tiles_touched, float* splats, void* stream) {
+                                 float* chol, float* depths, int32_t* radii, float* colors,
+                                 uint32_t* tiles_touched, void* stream) {
   GS_CHECK(check_sizes(N, ld));
   GS_CHECK(check_batch(num_cams, ld));
   GS_REQUIRE(sh_degree >= 0 && sh_degree <= 3, "sh_degree must be in [0, 3]");
@@ -608,15 +691,13 @@ gs_status gs_project_fwd_batched(int32_t num_cams, const gs_camera* cams, int64_
                "the cameras of a batch must share one image size");
     cb[c] = gs::make_cam(cams[c]);
   }
-  if (ld > 0) {
-    GS_REQUIRE(means2d && conics && depths && radii && colors && tiles_touched && splats,
+  if (ld > 0)
+    GS_REQUIRE(means2d && conics && chol && depths && radii && colors && tiles_touched,
                "NULL output pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-  }
-  if (N > 0) GS_REQUIRE(means && scales && quats && opacities && sh, "NULL parameter pointer");
-  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh,
-                                          num_cams, cb, gs::make_settings(*settings), means2d,
-                                          conics, depths, radii, colors, tiles_touched, splats,
+  if (N > 0) GS_REQUIRE(means && scales && quats && sh, "NULL parameter pointer");
+  return hip_status(gs_launch_project_fwd(N, ld, sh_degree, means, scales, quats, sh, num_cams,
+                                          cb, gs::make_settings(*settings), means2d, conics,
+                                          chol, depths, radii, colors, tiles_touched,
                                           (hipStream_t)stream),
                     "gs_project_fwd_batched");
 }
@@ -670,108 +751,108 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
 }
 
 gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
-                                   const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                                   const float* splats, const float* depths,
+                                   const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                   const uint32_t* ids, const float* means2d,
+                                   const float* conics, const float* chol,
+                                   const float* opacities, const float* colors,
+                                   const int32_t* radii, const float* depths,
                                    const float* background, const gs_settings* settings,
                                    float* image, float* final_T, uint32_t* last_idx,
-                                   float* out_depth, float* out_alpha, uint64_t* counters,
-                                   void* stream) {
-  GS_CHECK(check_sizes(0, ld));
+                                   float* out_depth, float* out_alpha, void* workspace,
+                                   size_t workspace_bytes, uint64_t* counters, void* stream) {
   GS_CHECK(check_batch(num_cams, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
-  if (ld > 0) {
-    GS_REQUIRE(ids && splats, "NULL splat pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
-  }
-  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order,
-                                         ids, splats,
-                                         depths, background, gs::make_settings(*settings),
-                                         image, final_T, last_idx, out_depth, out_alpha,
-                                         counters, -1, nullptr, nullptr, nullptr,
-                                         (hipStream_t)stream),
+  GS_CHECK(check_fwd(num_cams, (int64_t)num_cams * ld, ld, ld, width, height, tile_ranges, ids,
+                     means2d, conics, chol, opacities, colors, radii, depths, background,
+                     settings, image, final_T, last_idx, out_depth, workspace,
+                     workspace_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  GS_CHECK(hip_status(gs_launch_pack_splats((int64_t)num_cams * ld, ld, means2d, conics, chol,
+                                            opacities, colors, radii, settings->alpha_min,
+                                            (float*)workspace, s),
+                      "gs_rasterize_fwd_batched(stage)"));
+  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order, ids,
+                                         (const float*)workspace, depths, background,
+                                         gs::make_settings(*settings), image, final_T, last_idx,
+                                         out_depth, out_alpha, counters, -1, nullptr, nullptr,
+                                         nullptr, s),
                     "gs_rasterize_fwd_batched");
 }
 
 gs_status gs_rasterize_fwd_loss_batched(int32_t num_cams, int64_t ld, int32_t width,
                                         int32_t height, const uint32_t* tile_ranges,
                                         const uint32_t* tile_order, const uint32_t* ids,
-                                        const float* splats, const float* depths,
-                                        const float* background, const gs_settings* settings,
-                                        int32_t kind, const float* target, float* image,
-                                        float* final_T, uint32_t* last_idx, float* out_depth,
-                                        float* out_alpha, float* dL_dimage, float* loss,
-                                        uint64_t* counters, void* stream) {
-  GS_CHECK(check_sizes(0, ld));
+                                        const float* means2d, const float* conics,
+                                        const float* chol, const float* opacities,
+                                        const float* colors, const int32_t* radii,
+                                        const float* depths, const float* background,
+                                        const gs_settings* settings, int32_t kind,
+                                        const float* target, float* image, float* final_T,
+                                        uint32_t* last_idx, float* out_depth, float* out_alpha,
+                                        float* dL_dimage, float* loss, void* workspace,
+                                        size_t workspace_bytes, uint64_t* counters,
+                                        void* stream) {
   GS_CHECK(check_batch(num_cams, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
-  GS_REQUIRE(kind == 0 || kind == 1, "kind must be 0 (L2) or 1 (L1)");
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && image && final_T && last_idx, "NULL output or range pointer");
-  GS_REQUIRE(target && dL_dimage, "NULL target or gradient pointer");
-  GS_REQUIRE(dL_dimage != image && dL_dimage != target, "dL_dimage must not alias the images");
-  if (ld > 0) {
-    GS_REQUIRE(ids && splats, "NULL splat pointer");
-    GS_REQUIRE(aligned64(splats), "splats must be 64-byte aligned");
-    if (out_depth) GS_REQUIRE(depths != nullptr, "out_depth needs depths");
-  }
-  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order,
-                                         ids, splats, depths, background,
+  GS_CHECK(check_fwd(num_cams, (int64_t)num_cams * ld, ld, ld, width, height, tile_ranges, ids,
+                     means2d, conics, chol, opacities, colors, radii, depths, background,
+                     settings, image, final_T, last_idx, out_depth, workspace,
+                     workspace_bytes));
+  GS_CHECK(check_loss(kind, target, image, dL_dimage));
+  hipStream_t s = (hipStream_t)stream;
+  GS_CHECK(hip_status(gs_launch_pack_splats((int64_t)num_cams * ld, ld, means2d, conics, chol,
+                                            opacities, colors, radii, settings->alpha_min,
+                                            (float*)workspace, s),
+                      "gs_rasterize_fwd_loss_batched(stage)"));
+  return hip_status(gs_launch_raster_fwd(width, height, num_cams, tile_ranges, tile_order, ids,
+                                         (const float*)workspace, depths, background,
                                          gs::make_settings(*settings), image, final_T, last_idx,
-                                         out_depth, out_alpha, counters, kind, target,
-                                         dL_dimage, loss, (hipStream_t)stream),
+                                         out_depth, out_alpha, counters, kind, target, dL_dimage,
+                                         loss, s),
                     "gs_rasterize_fwd_loss_batched");
 }
 
 gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width, int32_t height,
-                                   const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                                   const float* splats, const uint32_t* offsets,
+                                   const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                   const uint32_t* ids, const float* means2d,
+                                   const float* conics, const float* chol,
+                                   const float* opacities, const float* colors,
+                                   const int32_t* radii, const uint32_t* offsets,
                                    const uint32_t* tiles_touched, uint64_t num_instances,
                                    const float* background, const gs_settings* settings,
                                    const float* final_T, const uint32_t* last_idx,
-                                   const float* dL_dimage, float* partials,
-                                   uint64_t partials_capacity, float* grads2d, int32_t absgrad,
+                                   const float* dL_dimage, void* workspace,
+                                   size_t workspace_bytes, int32_t staged, float* partials,
+                                   uint64_t partials_capacity, float* dL_dmeans2d,
+                                   float* dL_dconics, float* dL_dopacities, float* dL_dcolors,
+                                   float* dL_dmeans2d_abs, int32_t accumulate,
                                    uint64_t* counters, void* stream) {
-  GS_CHECK(check_sizes(0, ld));
   GS_CHECK(check_batch(num_cams, ld));
-  GS_CHECK(check_image(width, height));
-  GS_CHECK(check_settings(settings));
-  GS_REQUIRE((int64_t)num_cams * width * height < ((int64_t)1 << 31), "images too large");
-  GS_REQUIRE(background != nullptr, "background is NULL");
-  GS_REQUIRE(tile_ranges && final_T && last_idx && dL_dimage, "NULL input pointer");
-  GS_REQUIRE(num_instances <= partials_capacity, "partials smaller than num_instances");
-  GS_REQUIRE(absgrad == 0 || absgrad == 1, "absgrad must be 0 or 1");
   const int64_t rows = (int64_t)num_cams * ld;
-  if (rows > 0) {
-    GS_REQUIRE(ids && splats && offsets && tiles_touched && grads2d,
-               "NULL splat, offset or gradient pointer");
-    GS_REQUIRE(aligned64(splats) && aligned64(grads2d), "records must be 64-byte aligned");
-  }
-  if (num_instances > 0) {
-    GS_REQUIRE(partials != nullptr, "partials is NULL");
-    GS_REQUIRE(aligned64(partials), "partials must be 64-byte aligned");
-  }
-  return hip_status(gs_launch_raster_bwd(rows, width, height, num_cams, tile_ranges,
-                                         tile_order, ids, splats,
-                                         offsets, tiles_touched, background,
-                                         gs::make_settings(*settings), final_T, last_idx,
-                                         dL_dimage, partials, num_instances, grads2d, absgrad,
-                                         nullptr, 0, counters, (hipStream_t)stream),
+  GS_CHECK(check_bwd(num_cams, rows, ld, ld, rows, width, height, tile_ranges, ids,
+                     means2d, conics, chol, opacities, colors, radii, offsets, tiles_touched,
+                     num_instances, background, settings, final_T, last_idx, dL_dimage,
+                     workspace, workspace_bytes, staged, partials, partials_capacity,
+                     dL_dmeans2d, dL_dconics, dL_dopacities, dL_dcolors, accumulate));
+  hipStream_t s = (hipStream_t)stream;
+  if (!staged)
+    GS_CHECK(hip_status(gs_launch_pack_splats(rows, ld, means2d, conics, chol, opacities, colors,
+                                              radii, settings->alpha_min, (float*)workspace, s),
+                        "gs_rasterize_bwd_batched(stage)"));
+  const gs::Grad2D g{dL_dmeans2d, dL_dconics, dL_dopacities, dL_dcolors, dL_dmeans2d_abs,
+                     ld > 0 ? ld : 1};
+  return hip_status(gs_launch_raster_bwd(rows, width, height, num_cams, tile_ranges, tile_order,
+                                         ids, (const float*)workspace, offsets, tiles_touched,
+                                         background, gs::make_settings(*settings), final_T,
+                                         last_idx, dL_dimage, partials, num_instances, g,
+                                         accumulate, nullptr, 0, counters, s),
                     "gs_rasterize_bwd_batched");
 }
 
 gs_status gs_project_bwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N, int64_t ld,
                                  int32_t sh_degree, const float* means, const float* scales,
                                  const float* quats, const float* sh, const gs_settings* settings,
-                                 const int32_t* radii, const float* grads2d, float* dL_dmeans,
+                                 const int32_t* radii, const float* dL_dmeans2d,
+                                 const float* dL_dconics, const float* dL_dcolors,
+                                 const float* dL_dopacities_cams, float* dL_dmeans,
                                  float* dL_dscales, float* dL_dquats, float* dL_dopacities,
                                  float* dL_dsh, int32_t accumulate, void* stream) {
   GS_CHECK(check_sizes(N, ld));
@@ -780,22 +861,23 @@ gs_status gs_project_bwd_batched(int32_t num_cams, const gs_camera* cams, int64_
   GS_REQUIRE(cams != nullptr, "cams is NULL");
   GS_CHECK(check_settings(settings));
   GS_REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+  GS_REQUIRE((dL_dopacities_cams == nullptr) == (dL_dopacities == nullptr),
+             "dL_dopacities_cams and dL_dopacities go together");
   gs::Cam cb[gs::kMaxCams];
   for (int c = 0; c < num_cams; ++c) {
     GS_CHECK(check_camera(&cams[c]));
     cb[c] = gs::make_cam(cams[c]);
   }
-  if (N > 0) {
-    GS_REQUIRE(means && scales && quats && sh && radii && grads2d && dL_dmeans && dL_dscales &&
-                   dL_dquats && dL_dopacities && dL_dsh,
+  if (N > 0)
+    GS_REQUIRE(means && scales && quats && sh && radii && dL_dmeans2d && dL_dconics &&
+                   dL_dcolors && dL_dmeans && dL_dscales && dL_dquats && dL_dsh,
                "NULL array pointer");
-    GS_REQUIRE(aligned64(grads2d), "grads2d must be 64-byte aligned");
-  }
+  const gs::Grad2D g{(float*)dL_dmeans2d, (float*)dL_dconics, (float*)dL_dopacities_cams,
+                     (float*)dL_dcolors, nullptr, ld};
   return hip_status(gs_launch_project_bwd(N, ld, nullptr, ld, sh_degree, means, scales, quats, sh,
-                                          num_cams, cb, gs::make_settings(*settings), radii,
-                                          grads2d, dL_dmeans, dL_dscales, dL_dquats,
-                                          dL_dopacities, dL_dsh, accumulate,
-                                          (hipStream_t)stream),
+                                          num_cams, cb, gs::make_settings(*settings), radii, g,
+                                          dL_dmeans, dL_dscales, dL_dquats, dL_dopacities,
+                                          dL_dsh, accumulate, (hipStream_t)stream),
                     "gs_project_bwd_batched");
 }
 

@@ -55,6 +55,20 @@ __host__ inline Settings make_settings(const gs_settings& s) {
 
 __host__ __device__ inline int grid_dim(int pixels) { return (pixels + kTile - 1) / kTile; }
 
+// 2D gradient planes of the compositing backward (and the projection
+// backward's input).  Field q of row r is at base + c*P*ld + q*ld + i with
+// c = r / ld, i = r % ld: one camera (rows < ld), a batch of cameras (row
+// c*ld + i, camera-major blocks of P planes), or packed rows (ld = the
+// packed leading dimension).  abs may be NULL (no absolute-gradient sums).
+struct Grad2D {
+  float* m2;   // dL/du, dL/dv            [.][2][ld]
+  float* con;  // dL/dA, dL/dB, dL/dC     [.][3][ld]
+  float* op;   // dL/dopacity             [.][1][ld]
+  float* col;  // dL/dcolour r, g, b      [.][3][ld]
+  float* abs;  // sum |dL/du|, |dL/dv|    [.][2][ld]
+  int64_t ld;
+};
+
 // Tile rect of the square [u-r, u+r] x [v-r, v+r]: tiles [x0,x1) x [y0,y1).
 // Division by 16 is exact in fp32; the clamp happens before the integer
 // conversion so that off-screen means stay in range.

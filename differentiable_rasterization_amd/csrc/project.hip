@@ -220,51 +220,27 @@ __device__ inline void camera_centre(const Cam& cam, float c[3]) {
              cam.R[2 * 3 + j] * cam.t[2]);
 }
 
-// Padded half-extents of the footprint where alpha = o exp(-q/2) can reach
-// alpha_min: q <= Q = 2 ln(o / alpha_min), whose ellipse lies inside
-// |dx| <= sqrt(Q a), |dy| <= sqrt(Q c) for the dilated 2D covariance
-// (a, b, c) = conic^-1.  Q and the extents are padded (2% + constants) so
-// that the compositing kernels' fp32 pixel test can never reach alpha_min
-// outside the box; nearly singular covariances (kappa > ~1e4) are left
-// unbounded.  Negative: the Gaussian never reaches alpha_min (o < alpha_min).
-__device__ inline void footprint(float a, float b, float c, float o, float alpha_min, float& ex,
-                                 float& ey) {
-  if (!(o >= alpha_min)) {
-    ex = ey = -1.0f;
-    return;
-  }
-  const float tr = a + c;
-  if (!(a * c - b * b > 1e-4f * tr * tr)) {
-    ex = ey = __builtin_inff();
-    return;
-  }
-  const float Q = fmaf(2.0f * (__logf(o) - __logf(alpha_min)), 1.02f, 0.05f);
-  ex = sqrtf(Q * a) + 0.02f;
-  ey = sqrtf(Q * c) + 0.02f;
-}
-
 // Camera blockIdx.y of the batch writes its outputs to block c of each
-// output ([c][plane][ld] planes, records [c][ld]).  Rows N .. rows-1 (the
-// padding of a batch, rows = ld) get radius 0 and no tiles.
+// output ([c][plane][ld] planes).  Rows N .. rows-1 (the padding of a batch,
+// rows = ld) get radius 0 and no tiles.
 template <int DEG>
 __global__ __launch_bounds__(256) void project_fwd_kernel(
     int64_t N, int64_t rows, int64_t ld, const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
-    const float* __restrict__ opac, const float* __restrict__ sh, CamBatch cams, Settings st,
-    float* __restrict__ means2d, float* __restrict__ conics, float* __restrict__ depths,
-    int32_t* __restrict__ radii, float* __restrict__ colors, uint32_t* __restrict__ tiles,
-    float4* __restrict__ splats) {
+    const float* __restrict__ sh, CamBatch cams, Settings st, float* __restrict__ means2d,
+    float* __restrict__ conics, float* __restrict__ chol, float* __restrict__ depths,
+    int32_t* __restrict__ radii, float* __restrict__ colors, uint32_t* __restrict__ tiles) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows) return;
   const int64_t cb = (int64_t)blockIdx.y;
   means2d += cb * 2 * ld;
   conics += cb * 3 * ld;
+  chol += cb * 3 * ld;
   depths += cb * ld;
   radii += cb * ld;
   colors += cb * 3 * ld;
   tiles += cb * ld;
-  splats += cb * 4 * ld;
   if (i >= N) {
     radii[i] = 0;
     tiles[i] = 0u;
@@ -277,7 +253,6 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
   const float m[3] = {means[i], means[ld + i], means[2 * ld + i]};
   const float s[3] = {scales[i], scales[ld + i], scales[2 * ld + i]};
   const float q[4] = {quats[i], quats[ld + i], quats[2 * ld + i], quats[3 * ld + i]};
-  const float o = opac[i];
   float shv[3 * K];
 #pragma unroll
   for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
@@ -301,13 +276,6 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
       for (int ch = 0; ch < 3; ++ch) raw[ch] = fmaf(Y[j], shv[j * 3 + ch], raw[ch]);
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch) col[ch] = raw[ch] < 0.0f ? 0.0f : raw[ch];
-    float ex, ey;
-    footprint(g.a, g.b, g.c, o, st.alpha_min, ex, ey);
-    float4* rec = splats + 4 * i;
-    rec[0] = make_float4(g.u, g.v, kSqrtHalfLog2e * g.L11, kSqrtHalfLog2e * g.L21);
-    rec[1] = make_float4(kSqrtHalfLog2e * g.L22, o, col[0], col[1]);
-    rec[2] = make_float4(col[2], __int_as_float(g.radius), ex, ey);
-    rec[3] = make_float4(g.A, g.B, g.C, 0.0f);
   }
   // one store path for culled (zeros) and visible lanes
   means2d[i] = vis ? g.u : 0.0f;
@@ -315,6 +283,9 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
   conics[i] = vis ? g.A : 0.0f;
   conics[ld + i] = vis ? g.B : 0.0f;
   conics[2 * ld + i] = vis ? g.C : 0.0f;
+  chol[i] = vis ? g.L11 : 0.0f;
+  chol[ld + i] = vis ? g.L21 : 0.0f;
+  chol[2 * ld + i] = vis ? g.L22 : 0.0f;
   depths[i] = vis ? g.depth : 0.0f;
   radii[i] = vis ? g.radius : 0;
   tiles[i] = vis ? (uint32_t)(g.x1 - g.x0) * (uint32_t)(g.y1 - g.y0) : 0u;
@@ -581,30 +552,33 @@ __device__ inline void geom_grads(const Cam& cam, const Settings& st, const floa
   for (int k = 0; k < 3; ++k) om[k] = (float)(gm[k] + vterm[k]);
 }
 
-// Packed form (kPacked): row r handles Gaussian vis_ids[r]; its 2D gradient
-// record is row r of grads2d and its gradients go to row r of the output
-// planes (leading dimension ldo), so nothing is written for Gaussians off
-// the list.  Otherwise row r is Gaussian r and ldo = ld.
+// Packed form (kPacked): row r handles Gaussian vis_ids[r]; its 2D
+// gradients are row r of the 2D gradient planes and its gradients go to row
+// r of the output planes (leading dimension ldo for both), so nothing is
+// written for Gaussians off the list.  Otherwise row r is Gaussian r and
+// ldo = ld.
 template <int DEG, bool kPacked>
 __global__ __launch_bounds__(256) void project_bwd_kernel(
     int64_t N, int64_t ld, const uint32_t* __restrict__ vis_ids, int64_t ldo,
     const float* __restrict__ means,
     const float* __restrict__ scales, const float* __restrict__ quats,
     const float* __restrict__ sh, Cam cam, Settings st,
-    const int32_t* __restrict__ radii, const float4* __restrict__ grads2d,
+    const int32_t* __restrict__ radii, const float* __restrict__ g_m2,
+    const float* __restrict__ g_con, const float* __restrict__ g_col,
     float* __restrict__ o_means, float* __restrict__ o_scales, float* __restrict__ o_quats,
-    float* __restrict__ o_opac, float* __restrict__ o_sh, int accumulate) {
+    float* __restrict__ o_sh, int accumulate) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= N) return;
   const int64_t i = kPacked ? (int64_t)vis_ids[r] : r;
   const bool vis = radii[i] > 0;
-  // every load of a visible lane (parameters, its 2D gradient record, all 3K
-  // SH coefficients) is issued here, ahead of the fp64 chain, so that each
-  // lane keeps its whole working set in flight (the kernel runs at two
-  // waves per SIMD)
+  // every load of a visible lane (parameters, its 2D gradients, all 3K SH
+  // coefficients) is issued here, ahead of the fp64 chain, so that each lane
+  // keeps its whole working set in flight (the kernel runs at two waves per
+  // SIMD)
   float pm[3] = {0, 0, 0}, ps[3] = {0, 0, 0}, pq[4] = {1, 0, 0, 0}, shv[3 * K];
-  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0, r2 = r0;
+  float4 r0 = make_float4(0, 0, 0, 0), r1 = r0;
+  float gin[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < 3 * K; ++k) shv[k] = 0.0f;
   if (vis) {
@@ -615,9 +589,10 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pq[k] = quats[(int64_t)k * ld + i];
-    r0 = grads2d[4 * r + 0];
-    r1 = grads2d[4 * r + 1];
-    r2 = grads2d[4 * r + 2];
+    r0 = make_float4(g_m2[r], g_m2[ldo + r], g_con[r], g_con[ldo + r]);
+    r1.x = g_con[2 * ldo + r];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) gin[k] = g_col[(int64_t)k * ldo + r];
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shv[k] = sh[(int64_t)k * ld + i];
   }
@@ -630,10 +605,7 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
   // before the fp64 geometry chain).
   double d[3] = {0.0, 0.0, 1.0}, iL = 1.0, vterm[3] = {0.0, 0.0, 0.0};
   float gcol[3] = {0.0f, 0.0f, 0.0f};
-  if (vis) {
-    const float gin[3] = {r1.z, r1.w, r2.x};
-    sh_view<DEG>(cam, pm, shv, st.sh_offset, gin, d, iL, gcol);
-  }
+  if (vis) sh_view<DEG>(cam, pm, shv, st.sh_offset, gin, d, iL, gcol);
   if (store)
     sh_grads<DEG>(
         d, iL, gcol, shv,
@@ -645,11 +617,8 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
 
   // Phase 2, the geometry chain in fp64.
   float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
-  float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
-  if (vis) {
-    oo = r1.y;
-    geom_grads(cam, st, pm, ps, pq, r0, r1, vterm, om, os, oq);
-  }
+  float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (vis) geom_grads(cam, st, pm, ps, pq, r0, r1, vterm, om, os, oq);
   if (store) {
     for (int k = 0; k < 3; ++k) {
       const int64_t p = (int64_t)k * ldo + r;
@@ -660,26 +629,28 @@ __global__ __launch_bounds__(256) void project_bwd_kernel(
       const int64_t p = (int64_t)k * ldo + r;
       o_quats[p] = accumulate ? o_quats[p] + oq[k] : oq[k];
     }
-    o_opac[r] = accumulate ? o_opac[r] + oo : oo;
   }
 }
 
-// Batched form: Gaussian r seen by cameras 0 .. ncams-1 (radii [c][ld],
-// records [c * ld + r]); the outputs are the sums over the cameras, in
+// Batched form: Gaussian r seen by cameras 0 .. ncams-1 (radii [c][ld], 2D
+// gradient planes [c][P][ld]); the outputs are the sums over the cameras, in
 // camera order, with the same fp32 additions as ncams single-camera calls
 // with accumulate (the first overwriting unless `accumulate`).  The sums
 // stay in registers and are written once.  Two passes over the cameras keep
 // the register set of each side apart: the SH side for every camera first
 // (its view-direction terms parked in LDS, three doubles per camera and
 // lane), then the geometry chain for every camera.  -0.0f starts a sum:
-// adding it leaves every value's bits unchanged.
+// adding it leaves every value's bits unchanged.  With o_opac, the
+// per-camera opacity gradients g_op [c][ld] are summed the same way.
 template <int DEG>
 __global__ __launch_bounds__(256) void project_bwd_batched_kernel(
     int64_t N, int64_t ld, const float* __restrict__ means, const float* __restrict__ scales,
     const float* __restrict__ quats, const float* __restrict__ sh, CamBatch cams, int ncams,
-    Settings st, const int32_t* __restrict__ radii, const float4* __restrict__ grads2d,
-    float* __restrict__ o_means, float* __restrict__ o_scales, float* __restrict__ o_quats,
-    float* __restrict__ o_opac, float* __restrict__ o_sh, int accumulate) {
+    Settings st, const int32_t* __restrict__ radii, const float* __restrict__ g_m2,
+    const float* __restrict__ g_con, const float* __restrict__ g_op,
+    const float* __restrict__ g_col, float* __restrict__ o_means,
+    float* __restrict__ o_scales, float* __restrict__ o_quats, float* __restrict__ o_opac,
+    float* __restrict__ o_sh, int accumulate) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   extern __shared__ double s_vterm[];  // [ncams][3][256]
   const int t = threadIdx.x;
@@ -716,9 +687,8 @@ __global__ __launch_bounds__(256) void project_bwd_batched_kernel(
       double d[3] = {0.0, 0.0, 1.0}, iL = 1.0, vterm[3] = {0.0, 0.0, 0.0};
       float gcol[3] = {0.0f, 0.0f, 0.0f};
       if (vis) {
-        const int64_t rr = (int64_t)c * ld + r;
-        const float4 r1 = grads2d[4 * rr + 1], r2 = grads2d[4 * rr + 2];
-        const float gin[3] = {r1.z, r1.w, r2.x};
+        const float* gc = g_col + (int64_t)c * 3 * ld + r;
+        const float gin[3] = {gc[0], gc[ld], gc[2 * ld]};
         sh_view<DEG>(cams.c[c], pm, shv, st.sh_offset, gin, d, iL, gcol);
       }
       if (store)
@@ -736,18 +706,20 @@ __global__ __launch_bounds__(256) void project_bwd_batched_kernel(
     a_s[k] = accumulate ? o_scales[(int64_t)k * ld + r] : -0.0f;
   }
   for (int k = 0; k < 4; ++k) a_q[k] = accumulate ? o_quats[(int64_t)k * ld + r] : -0.0f;
-  a_o = accumulate ? o_opac[r] : -0.0f;
+  a_o = (o_opac && accumulate) ? o_opac[r] : -0.0f;
   for (int c = 0; c < ncams; ++c) {
     const bool vis = radii[(int64_t)c * ld + r] > 0;
     const bool store = vis || (c == 0 && !accumulate);
     float om[3] = {0.0f, 0.0f, 0.0f}, os[3] = {0.0f, 0.0f, 0.0f};
     float oq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, oo = 0.0f;
     if (vis) {
-      const int64_t rr = (int64_t)c * ld + r;
-      const float4 r0 = grads2d[4 * rr + 0], r1 = grads2d[4 * rr + 1];
+      const float* gm = g_m2 + (int64_t)c * 2 * ld + r;
+      const float* gn = g_con + (int64_t)c * 3 * ld + r;
+      const float4 r0 = make_float4(gm[0], gm[ld], gn[0], gn[ld]);
+      const float4 r1 = make_float4(gn[2 * ld], 0.0f, 0.0f, 0.0f);
       double vterm[3];
       for (int e = 0; e < 3; ++e) vterm[e] = s_vterm[(c * 3 + e) * 256 + t];
-      oo = r1.y;
+      if (o_opac) oo = g_op[(int64_t)c * ld + r];
       geom_grads(cams.c[c], st, pm, ps, pq, r0, r1, vterm, om, os, oq);
     }
     if (store) {
@@ -764,7 +736,7 @@ __global__ __launch_bounds__(256) void project_bwd_batched_kernel(
     o_scales[(int64_t)k * ld + r] = a_s[k];
   }
   for (int k = 0; k < 4; ++k) o_quats[(int64_t)k * ld + r] = a_q[k];
-  o_opac[r] = a_o;
+  if (o_opac) o_opac[r] = a_o;
 }
 
 }  // namespace gs
@@ -773,11 +745,11 @@ __global__ __launch_bounds__(256) void project_bwd_batched_kernel(
 // cameras (outputs [c][...], rows N .. ld-1 padded).
 extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, const float* means,
                                             const float* scales, const float* quats,
-                                            const float* opac, const float* sh, int ncams,
-                                            const gs::Cam* cams, const gs::Settings& st,
-                                            float* means2d, float* conics, float* depths,
+                                            const float* sh, int ncams, const gs::Cam* cams,
+                                            const gs::Settings& st, float* means2d,
+                                            float* conics, float* chol, float* depths,
                                             int32_t* radii, float* colors, uint32_t* tiles,
-                                            float* splats, hipStream_t stream) {
+                                            hipStream_t stream) {
   const int64_t rows = ncams > 1 ? ld : N;
   if (rows == 0) return hipSuccess;
   gs::CamBatch cb;
@@ -785,8 +757,8 @@ extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, cons
   const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)ncams);
 #define GS_PFWD(D)                                                                        \
   hipLaunchKernelGGL(gs::project_fwd_kernel<D>, grid, dim3(256), 0, stream, N, rows, ld,    \
-                     means, scales, quats, opac, sh, cb, st, means2d, conics, depths,       \
-                     radii, colors, tiles, (float4*)splats)
+                     means, scales, quats, sh, cb, st, means2d, conics, chol, depths, radii, \
+                     colors, tiles)
   switch (deg) {
     case 0: GS_PFWD(0); break;
     case 1: GS_PFWD(1); break;
@@ -797,15 +769,17 @@ extern "C" hipError_t gs_launch_project_fwd(int64_t N, int64_t ld, int deg, cons
   return hipGetLastError();
 }
 
-// vis_ids NULL: N Gaussians, outputs with leading dimension ld.  Otherwise
-// N rows of the packed list vis_ids, outputs with leading dimension ldo.
-// ncams > 1: a batch of cameras (dense rows only), summed into the outputs.
+// vis_ids NULL: N Gaussians, 2D gradients and outputs with leading dimension
+// ld.  Otherwise N rows of the packed list vis_ids, 2D gradients and outputs
+// with leading dimension ldo.  ncams > 1: a batch of cameras (dense rows
+// only, 2D gradients [c][P][ld]), summed into the outputs; o_opac (batch
+// only, optional) receives the sum of the per-camera opacity gradients g.op.
 extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
                                             int64_t ldo, int deg, const float* means,
                                             const float* scales, const float* quats,
                                             const float* sh, int ncams, const gs::Cam* cams,
                                             const gs::Settings& st, const int32_t* radii,
-                                            const float* grads2d, float* o_means,
+                                            const gs::Grad2D& g, float* o_means,
                                             float* o_scales, float* o_quats, float* o_opac,
                                             float* o_sh, int accumulate, hipStream_t stream) {
   if (N == 0) return hipSuccess;
@@ -816,13 +790,13 @@ extern "C" hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_
 #define GS_PBWD(D, PK)                                                                    \
   hipLaunchKernelGGL((gs::project_bwd_kernel<D, PK>), dim3((unsigned)blocks), dim3(256), 0,  \
                      stream, N, ld, vis_ids, PK ? ldo : ld, means, scales, quats, sh,       \
-                     cams[0], st, radii, (const float4*)grads2d, o_means, o_scales, o_quats, \
-                     o_opac, o_sh, accumulate)
+                     cams[0], st, radii, g.m2, g.con, g.col, o_means, o_scales, o_quats,    \
+                     o_sh, accumulate)
 #define GS_PBWD_B(D)                                                                       \
   hipLaunchKernelGGL(gs::project_bwd_batched_kernel<D>, dim3((unsigned)blocks), dim3(256),    \
                      vterm_lds, stream, N, ld, means, scales, quats, sh, cb, ncams, st,      \
-                     radii, (const float4*)grads2d, o_means, o_scales, o_quats, o_opac, o_sh, \
-                     accumulate)
+                     radii, g.m2, g.con, g.op, g.col, o_means, o_scales, o_quats, o_opac,    \
+                     o_sh, accumulate)
 #define GS_PBWD2(D)                     \
   if (ncams > 1) GS_PBWD_B(D);          \
   else if (vis_ids) GS_PBWD(D, true);   \

@@ -28,6 +28,10 @@
 // slots in a fixed order.  No global atomics: device-scope float atomics go
 // to memory on this part, and a fixed order makes gradients reproducible.
 //
+// The calls take the projection's planes; pack_splats_kernel first stages
+// each visible row into a 64-byte record in the caller's workspace, so that
+// staging a tile instance costs one cache line.
+//
 // Decisions (alpha < alpha_min, alpha clamp, stop at T < T_min) are
 // taken by the same inline code in both kernels, compiled without
 // contraction, so the backward replays exactly the forward's choices.
@@ -66,6 +70,68 @@ struct RecordRegs {
     ey = c.w;
   }
 };
+
+// Padded half-extents of the footprint where alpha = o exp(-q/2) can reach
+// alpha_min: q <= Q = 2 ln(o / alpha_min), whose ellipse lies inside
+// |dx| <= sqrt(Q a), |dy| <= sqrt(Q c) for the 2D covariance (a, b, c) =
+// conic^-1.  From the conic's Cholesky factor L (conic = L L^T) without
+// cancellation: c = 1 / L22^2, a = (1 + (L21 / L22)^2) / L11^2, and
+// det = 1 / (L11 L22)^2.  Q and the extents are padded (2% + constants) so
+// that the compositing kernels' fp32 pixel test can never reach alpha_min
+// outside the box; nearly singular covariances (det <= 1e-4 (a + c)^2,
+// condition numbers above ~1e4) are left unbounded.  Negative: the Gaussian
+// never reaches alpha_min (o < alpha_min).
+__device__ inline void footprint(float L11, float L21, float L22, float o, float alpha_min,
+                                 float& ex, float& ey) {
+  if (!(o >= alpha_min)) {
+    ex = ey = -1.0f;
+    return;
+  }
+  const float t = L21 / L22;
+  const float c = 1.0f / (L22 * L22);
+  const float a = fmaf(t, t, 1.0f) / (L11 * L11);
+  const float det = 1.0f / ((L11 * L22) * (L11 * L22));
+  const float tr = a + c;
+  if (!(det > 1e-4f * tr * tr)) {
+    ex = ey = __builtin_inff();
+    return;
+  }
+  const float Q = fmaf(2.0f * (__logf(o) - __logf(alpha_min)), 1.02f, 0.05f);
+  ex = sqrtf(Q * a) + 0.02f;
+  ey = sqrtf(Q * c) + 0.02f;
+}
+
+// Stages row r of the projection's planes into record r of rec when its
+// radius is > 0 (rows of other Gaussians are never referenced by a tile
+// list).  Row r is Gaussian i = r % ld seen by camera c = r / ld (one camera:
+// r < ld); plane p of camera c starts at c * P * ld + p * ld, opacities are
+// per Gaussian.  Record: u, v, k L11, k L21, k L22 (k = sqrt(log2(e) / 2), so
+// that the Gaussian is exp2(-(e1^2 + e2^2))), opacity, colour, radius,
+// footprint extents, conic.
+__global__ __launch_bounds__(256) void pack_splats_kernel(
+    int64_t rows, int64_t ld, const float* __restrict__ means2d, const float* __restrict__ conics,
+    const float* __restrict__ chol, const float* __restrict__ opac,
+    const float* __restrict__ colors, const int32_t* __restrict__ radii, float alpha_min,
+    float4* __restrict__ rec) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int32_t rad = radii[r];
+  if (rad <= 0) return;
+  const int64_t c = r / ld, i = r - c * ld;
+  const float* m2 = means2d + c * 2 * ld + i;
+  const float* cn = conics + c * 3 * ld + i;
+  const float* ch = chol + c * 3 * ld + i;
+  const float* co = colors + c * 3 * ld + i;
+  const float L11 = ch[0], L21 = ch[ld], L22 = ch[2 * ld];
+  const float o = opac[i];
+  float ex, ey;
+  footprint(L11, L21, L22, o, alpha_min, ex, ey);
+  float4* out = rec + 4 * r;
+  out[0] = make_float4(m2[0], m2[ld], kSqrtHalfLog2e * L11, kSqrtHalfLog2e * L21);
+  out[1] = make_float4(kSqrtHalfLog2e * L22, o, co[0], co[ld]);
+  out[2] = make_float4(co[2 * ld], __int_as_float(rad), ex, ey);
+  out[3] = make_float4(cn[0], cn[ld], cn[2 * ld], 0.0f);
+}
 
 // Workgroup -> tile mapping aware of the eight XCDs (each with its own L2):
 // workgroup b runs on XCD b % 8, so each XCD is handed whole 2x2 groups of
@@ -287,7 +353,7 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
   // camera blockIdx.y of a batch: its tiles follow the earlier cameras'
   // (gx * gy each) and its pixels their images
   const int tile = (int)blockIdx.y * gx * gy + ty * gx + tx;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int sb = tid >> 4;  // this lane's 4x4 block: each row of the wave walks its own list
   const int px = tx * kTile + sub_px(tid), py = ty * kTile + sub_py(tid);
   const bool inside = px < W && py < H;
@@ -702,21 +768,49 @@ __device__ inline void add_rec(float a[kFieldsAbs], const float4* __restrict__ p
   a[8] += z.x; a[9] += z.y; a[10] += z.z;
 }
 
-__device__ inline void store_rec(float4* __restrict__ r, const float a[kFieldsAbs]) {
-  r[0] = make_float4(a[0], a[1], a[2], a[3]);
-  r[1] = make_float4(a[4], a[5], a[6], a[7]);
-  r[2] = make_float4(a[8], a[9], a[10], 0.0f);
+// Writes row r's eleven sums to the 2D gradient planes.  mode 0 overwrites
+// every plane, 1 adds to every plane, 2 adds to the per-Gaussian results
+// that are final after this stage (opacity, absolute sums) and overwrites
+// the per-camera ones the projection backward reads (mean, conic, colour).
+// has: the row has tiles; without, the added planes are left alone.
+__device__ inline void store_grads(const Grad2D& g, int64_t r, const float a[kFieldsAbs],
+                                   int mode, bool has) {
+  const int64_t c = r / g.ld, i = r - c * g.ld;
+  auto put = [&](float* base, int P, int q, float v, bool add) {
+    float* p = base + c * P * g.ld + q * g.ld + i;
+    if (add) {
+      if (has) *p = *p + v;
+    } else {
+      *p = v;
+    }
+  };
+  const bool add_cam = mode == 1, add_fin = mode != 0;
+  put(g.m2, 2, 0, a[0], add_cam);
+  put(g.m2, 2, 1, a[1], add_cam);
+  put(g.con, 3, 0, a[2], add_cam);
+  put(g.con, 3, 1, a[3], add_cam);
+  put(g.con, 3, 2, a[4], add_cam);
+  put(g.op, 1, 0, a[5], add_fin);
+  put(g.col, 3, 0, a[6], add_cam);
+  put(g.col, 3, 1, a[7], add_cam);
+  put(g.col, 3, 2, a[8], add_cam);
+  if (g.abs) {
+    put(g.abs, 2, 0, a[9], add_fin);
+    put(g.abs, 2, 1, a[10], add_fin);
+  }
 }
 
-// Row r of grads2d sums the slots of Gaussian r, or of Gaussian vis_ids[r]
-// in the packed form (kPacked), where the rows follow that list.
+// Row r of the 2D gradient planes sums the slots of Gaussian row r, or of
+// Gaussian vis_ids[r] in the packed form (kPacked), where the rows follow
+// that list.  Rows without tiles get zeros in the overwritten planes (mode,
+// see store_grads).
 // Slots past `capacity` (a binning that overflowed its buffers and left an
-// empty list) are never read: such a Gaussian gets a zero record.
+// empty list) are never read: such a Gaussian gets zeros.
 template <bool kPacked>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(
     int64_t N, const uint32_t* __restrict__ vis_ids, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ tiles, const float4* __restrict__ partials, uint64_t capacity,
-    float4* __restrict__ grads2d) {
+    Grad2D g, int mode) {
   __shared__ uint32_t s_big[256];
   __shared__ uint32_t s_nbig;
   __shared__ float s_red[kFieldsAbs][256];
@@ -730,7 +824,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     const bool fits = cnt == 0 || (uint64_t)offsets[i] + cnt <= capacity;
     if (cnt > kSmallSeg && fits) {
       s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)t;
-    } else if (cnt > 0) {
+    } else if (cnt > 0 || mode != 1) {
       float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
       const uint64_t base = offsets[i];
       if (fits) {
@@ -754,7 +848,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
         }
         for (; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
       }
-      store_rec(grads2d + 4 * r, a);
+      store_grads(g, r, a, mode, cnt > 0);
     }
   }
   __syncthreads();
@@ -779,7 +873,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
       float sum[kFieldsAbs];
 #pragma unroll
       for (int q = 0; q < kFieldsAbs; ++q) sum[q] = s_red[q][0];
-      store_rec(grads2d + 4 * gr, sum);
+      store_grads(g, gr, sum, mode, true);
     }
     __syncthreads();
   }
@@ -897,9 +991,22 @@ extern "C" hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams,
   return hipGetLastError();
 }
 
+// Stages the records of rows [0, rows) (a batch: rows = ncams * ld) into rec.
+extern "C" hipError_t gs_launch_pack_splats(int64_t rows, int64_t ld, const float* means2d,
+                                            const float* conics, const float* chol,
+                                            const float* opac, const float* colors,
+                                            const int32_t* radii, float alpha_min, float* rec,
+                                            hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gs::pack_splats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     s, rows, ld, means2d, conics, chol, opac, colors, radii, alpha_min,
+                     (float4*)rec);
+  return hipGetLastError();
+}
+
 // ncams images of W x H (a batch: ranges over ncams * T tiles, outputs
-// [c][H][W]).  loss_kind >= 0: also dL/dimage against target (and the loss
-// value into *loss when non-NULL).
+// [c][H][W]), from the staged records.  loss_kind >= 0: also dL/dimage
+// against target (and the loss value into *loss when non-NULL).
 extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
                                            const uint32_t* ranges, const uint32_t* order,
                                            const uint32_t* ids,
@@ -932,7 +1039,8 @@ extern "C" hipError_t gs_launch_raster_fwd(int32_t W, int32_t H, int ncams,
 }
 
 // ncams > 1: a batch (N = ncams * ld rows, ranges over ncams * T tiles,
-// images [c][H][W]).
+// images [c][H][W]).  The 2D gradients go to the planes of g (rows as
+// Grad2D describes; packed rows follow vis_ids).
 extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int ncams,
                                            const uint32_t* ranges, const uint32_t* order,
                                            const uint32_t* ids, const float* splats,
@@ -940,13 +1048,15 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int 
                                            const float* bg, const gs::Settings& st,
                                            const float* final_T, const uint32_t* last_idx,
                                            const float* dL_dimage, float* partials,
-                                           uint64_t capacity, float* grads2d, int absgrad,
-                                           const uint32_t* vis_ids, int64_t num_visible,
-                                           uint64_t* counters, hipStream_t s) {
+                                           uint64_t capacity, const gs::Grad2D& g,
+                                           int accumulate, const uint32_t* vis_ids,
+                                           int64_t num_visible, uint64_t* counters,
+                                           hipStream_t s) {
   const int gx = gs::grid_dim(W), gy = gs::grid_dim(H);
   const dim3 grid(gs::tile_grid_blocks(gx, gy), (unsigned)ncams), block(256);
   const float4* sp = (const float4*)splats;
   float4* part = (float4*)partials;
+  const bool absgrad = g.abs != nullptr;
 #define GS_RBWD(STATS, ABS)                                                                 \
   hipLaunchKernelGGL((gs::raster_bwd_kernel<STATS, ABS>), grid, block, 0, s, W, H, gx, ranges, \
                      ids, sp, offsets, bg[0], bg[1], bg[2], st, final_T, last_idx,          \
@@ -964,10 +1074,10 @@ extern "C" hipError_t gs_launch_raster_bwd(int64_t N, int32_t W, int32_t H, int 
   const dim3 rgrid((unsigned)((rows + 255) / 256));
   if (vis_ids)
     hipLaunchKernelGGL(gs::reduce_partials_kernel<true>, rgrid, dim3(256), 0, s, rows, vis_ids,
-                       offsets, tiles, part, capacity, (float4*)grads2d);
+                       offsets, tiles, part, capacity, g, accumulate);
   else
     hipLaunchKernelGGL(gs::reduce_partials_kernel<false>, rgrid, dim3(256), 0, s, rows, nullptr,
-                       offsets, tiles, part, capacity, (float4*)grads2d);
+                       offsets, tiles, part, capacity, g, accumulate);
   return hipGetLastError();
 }
 

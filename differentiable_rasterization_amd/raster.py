@@ -33,7 +33,8 @@ EXPORTED = ("gs_default_settings", "gs_status_string", "gs_last_error", "gs_num_
             "gs_bin_and_sort_batched_workspace_size", "gs_bin_and_sort_batched",
             "gs_rasterize_fwd_batched", "gs_rasterize_bwd_batched", "gs_project_bwd_batched",
             "gs_bin_and_sort_device", "gs_rasterize_fwd_loss", "gs_tile_order",
-            "gs_rasterize_fwd_loss_batched", "gs_bin_and_sort_noalloc")
+            "gs_rasterize_fwd_loss_batched", "gs_bin_and_sort_noalloc",
+            "gs_rasterize_workspace_size")
 
 
 class GsError(RuntimeError):
@@ -80,29 +81,34 @@ def load():
     lib.gs_num_tiles.restype = i32
     lib.gs_num_tiles.argtypes = [i32, i32]
     lib.gs_project_fwd.restype = C.c_int
-    lib.gs_project_fwd.argtypes = [i64, i64, i32] + [P] * 5 + [P, P] + [P] * 7 + [P]
+    lib.gs_project_fwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 7 + [P]
+    lib.gs_rasterize_workspace_size.restype = C.c_size_t
+    lib.gs_rasterize_workspace_size.argtypes = [i64]
     lib.gs_bin_and_sort_workspace_size.restype = C.c_size_t
     lib.gs_bin_and_sort_workspace_size.argtypes = [i64, u64, i32, i32]
     lib.gs_bin_and_sort.restype = C.c_int
     lib.gs_bin_and_sort.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                     C.c_size_t, P]
     lib.gs_rasterize_fwd.restype = C.c_int
-    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 14
+    SZ = C.c_size_t
+    lib.gs_rasterize_fwd.argtypes = [i64, i64, i32, i32] + [P] * 3 + [P] * 7 + [P, P] + \
+        [P] * 5 + [P, SZ, P, P]
     lib.gs_rasterize_bwd.restype = C.c_int
-    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 6 + [u64] + [P] * 6 + \
-        [u64, P, i32, P, P]
+    lib.gs_rasterize_bwd.argtypes = [i64, i64, i32, i32] + [P] * 3 + [P] * 6 + [P, P, u64] + \
+        [P, P] + [P] * 3 + [P, SZ, i32, P, u64] + [P] * 5 + [i32, P, P]
     lib.gs_project_bwd.restype = C.c_int
-    lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P] + [P] * 2 + [P] * 5 + \
+    lib.gs_project_bwd.argtypes = [i64, i64, i32] + [P] * 4 + [P, P, P] + [P] * 3 + [P] * 4 + \
         [i32, P]
     lib.gs_bin_and_sort_packed.restype = C.c_int
     lib.gs_bin_and_sort_packed.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
                                            P, P, C.c_size_t, P]
     lib.gs_rasterize_bwd_packed.restype = C.c_int
-    lib.gs_rasterize_bwd_packed.argtypes = [i64, i64, i32, i32] + [P] * 6 + [u64, P, i64] + \
-        [P] * 6 + [u64, P, i32, P, P]
+    lib.gs_rasterize_bwd_packed.argtypes = [i64, i64, i32, i32] + [P] * 3 + [P] * 6 + \
+        [P, P, u64, P, i64, i64] + [P, P] + [P] * 3 + [P, SZ, i32, P, u64] + [P] * 5 + \
+        [i32, P, P]
     lib.gs_project_bwd_packed.restype = C.c_int
-    lib.gs_project_bwd_packed.argtypes = [i64, P, i64, i64, i64, i32] + [P] * 4 + [P, P] + \
-        [P] * 2 + [P] * 5 + [i32, P]
+    lib.gs_project_bwd_packed.argtypes = [i64, P, i64, i64, i64, i32] + [P] * 4 + [P, P, P] + \
+        [P] * 3 + [P] * 4 + [i32, P]
     lib.gs_l1_dssim_workspace_size.restype = C.c_size_t
     lib.gs_l1_dssim_workspace_size.argtypes = [i32, i32]
     lib.gs_l1_dssim_loss_grad.restype = C.c_int
@@ -115,20 +121,21 @@ def load():
     lib.gs_adam_step_packed.argtypes = [i64, P, i64, i64, i64, i32, i64, P] + [P] * 7 + \
         [P] * 5 + [P, P, P]
     lib.gs_project_fwd_batched.restype = C.c_int
-    lib.gs_project_fwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 5 + [P] + [P] * 7 + [P]
+    lib.gs_project_fwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 7 + [P]
     lib.gs_bin_and_sort_batched_workspace_size.restype = C.c_size_t
     lib.gs_bin_and_sort_batched_workspace_size.argtypes = [i32, i64, u64, i32, i32]
     lib.gs_bin_and_sort_batched.restype = C.c_int
     lib.gs_bin_and_sort_batched.argtypes = [i32, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
                                             P, C.c_size_t, P]
     lib.gs_rasterize_fwd_batched.restype = C.c_int
-    lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 14
+    lib.gs_rasterize_fwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 3 + [P] * 7 + [P, P] + \
+        [P] * 5 + [P, SZ, P, P]
     lib.gs_rasterize_bwd_batched.restype = C.c_int
-    lib.gs_rasterize_bwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 6 + [u64] + [P] * 6 + \
-        [u64, P, i32, P, P]
+    lib.gs_rasterize_bwd_batched.argtypes = [i32, i64, i32, i32] + [P] * 3 + [P] * 6 + \
+        [P, P, u64] + [P, P] + [P] * 3 + [P, SZ, i32, P, u64] + [P] * 5 + [i32, P, P]
     lib.gs_project_bwd_batched.restype = C.c_int
-    lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P] + [P] * 2 + \
-        [P] * 5 + [i32, P]
+    lib.gs_project_bwd_batched.argtypes = [i32, P, i64, i64, i32] + [P] * 4 + [P, P] + \
+        [P] * 3 + [P] + [P] * 5 + [i32, P]
     lib.gs_bin_and_sort_noalloc.restype = C.c_int
     lib.gs_bin_and_sort_noalloc.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P,
                                             P]
@@ -136,12 +143,13 @@ def load():
     lib.gs_bin_and_sort_device.argtypes = [i64, i64, P, P, P, P, i32, i32, P, u64, P, P, P, P, P,
                                            C.c_size_t, P]
     lib.gs_rasterize_fwd_loss.restype = C.c_int
-    lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 7 + [i32] + [P] * 9 + [P]
+    lib.gs_rasterize_fwd_loss.argtypes = [i64, i64, i32, i32] + [P] * 3 + [P] * 7 + [P, P] + \
+        [i32, P] + [P] * 5 + [P, P] + [P, SZ, P, P]
     lib.gs_tile_order.restype = C.c_int
     lib.gs_tile_order.argtypes = [i32, i32, i32, P, P, P]
     lib.gs_rasterize_fwd_loss_batched.restype = C.c_int
-    lib.gs_rasterize_fwd_loss_batched.argtypes = [i32, i64, i32, i32] + [P] * 7 + [i32] + \
-        [P] * 9 + [P]
+    lib.gs_rasterize_fwd_loss_batched.argtypes = [i32, i64, i32, i32] + [P] * 3 + [P] * 7 + \
+        [P, P] + [i32, P] + [P] * 5 + [P, P] + [P, SZ, P, P]
     lib.gs_image_loss_grad.restype = C.c_int
     lib.gs_image_loss_grad.argtypes = [i32, i64, P, P, P, P, P]
     lib.gs_densify_prune_workspace_size.restype = C.c_size_t
@@ -204,12 +212,12 @@ def num_tiles(width, height) -> int:
 # ---------------------------------------------------------------------------
 # The entry points
 # ---------------------------------------------------------------------------
-def gs_project_fwd(N, ld, sh_degree, means, scales, quats, opacities, sh, cam, settings,
-                   means2d, conics, depths, radii, colors, tiles_touched, splats, stream=None):
+def gs_project_fwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, means2d, conics,
+                   chol, depths, radii, colors, tiles_touched, stream=None):
     lib = load()
-    _check(lib.gs_project_fwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(opacities),
-                              _p(sh), C.byref(cam), C.byref(settings), _p(means2d), _p(conics),
-                              _p(depths), _p(radii), _p(colors), _p(tiles_touched), _p(splats),
+    _check(lib.gs_project_fwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
+                              C.byref(cam), C.byref(settings), _p(means2d), _p(conics),
+                              _p(chol), _p(depths), _p(radii), _p(colors), _p(tiles_touched),
                               _stream(stream)))
 
 
@@ -251,40 +259,84 @@ def gs_bin_and_sort_noalloc(N, ld, means2d, radii, depths, tiles_touched, width,
     return st, int(M.value) if num_instances is None else int(num_instances[0])
 
 
-def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, splats, depths, background,
-                     settings, image, final_T, last_idx, out_depth=None, out_alpha=None,
-                     counters=None, stream=None, tile_order=None):
-    lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(tile_order), _p(ids),
-                                _p(splats),
-                                _p(depths), bg, C.byref(settings), _p(image), _p(final_T),
-                                _p(last_idx), _p(out_depth), _p(out_alpha), _p(counters),
-                                _stream(stream)))
+@dataclasses.dataclass
+class SplatPlanes:
+    """The projection's planes that the compositing calls read (device
+    tensors): means2d [2][ld], conics [3][ld], chol [3][ld], the caller's
+    opacities [ld], colors [3][ld], radii [ld] and (for a depth output)
+    depths [ld]; a batch's per-camera planes are blocks [c][P][ld]."""
+    means2d: "object"
+    conics: "object"
+    chol: "object"
+    opacities: "object"
+    colors: "object"
+    radii: "object"
+    depths: "object" = None
+
+    def args(self):
+        return [_p(self.means2d), _p(self.conics), _p(self.chol), _p(self.opacities),
+                _p(self.colors), _p(self.radii)]
 
 
-def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, splats, offsets, tiles_touched,
-                     num_instances, background, settings, final_T, last_idx, dL_dimage, partials,
-                     partials_capacity, grads2d, absgrad=0, counters=None, stream=None,
+@dataclasses.dataclass
+class Grad2D:
+    """2D gradient planes of the compositing backward: means2d [2][ld],
+    conics [3][ld], opacities [ld], colors [3][ld] and, optionally, the
+    absolute-gradient sums abs [2][ld]."""
+    means2d: "object"
+    conics: "object"
+    opacities: "object"
+    colors: "object"
+    abs: "object" = None
+
+    def args(self):
+        return [_p(self.means2d), _p(self.conics), _p(self.opacities), _p(self.colors),
+                _p(self.abs)]
+
+
+def gs_rasterize_workspace_size(rows) -> int:
+    return int(load().gs_rasterize_workspace_size(int(rows)))
+
+
+def _bg(background):
+    return (C.c_float * 3)(*[float(x) for x in background])
+
+
+def gs_rasterize_fwd(N, ld, width, height, tile_ranges, ids, sp: SplatPlanes, background,
+                     settings, image, final_T, last_idx, workspace, workspace_bytes,
+                     out_depth=None, out_alpha=None, counters=None, stream=None,
                      tile_order=None):
     lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
+    _check(lib.gs_rasterize_fwd(N, ld, width, height, _p(tile_ranges), _p(tile_order), _p(ids),
+                                *sp.args(), _p(sp.depths), _bg(background), C.byref(settings),
+                                _p(image), _p(final_T), _p(last_idx), _p(out_depth),
+                                _p(out_alpha), _p(workspace), int(workspace_bytes),
+                                _p(counters), _stream(stream)))
+
+
+def gs_rasterize_bwd(N, ld, width, height, tile_ranges, ids, sp: SplatPlanes, offsets,
+                     tiles_touched, num_instances, background, settings, final_T, last_idx,
+                     dL_dimage, workspace, workspace_bytes, staged, partials,
+                     partials_capacity, g2: Grad2D, accumulate=0, counters=None, stream=None,
+                     tile_order=None):
+    lib = load()
     _check(lib.gs_rasterize_bwd(N, ld, width, height, _p(tile_ranges), _p(tile_order), _p(ids),
-                                _p(splats),
-                                _p(offsets), _p(tiles_touched), int(num_instances), bg,
-                                C.byref(settings), _p(final_T), _p(last_idx), _p(dL_dimage),
-                                _p(partials), int(partials_capacity), _p(grads2d),
-                                int(absgrad), _p(counters), _stream(stream)))
+                                *sp.args(), _p(offsets), _p(tiles_touched),
+                                int(num_instances), _bg(background), C.byref(settings),
+                                _p(final_T), _p(last_idx), _p(dL_dimage), _p(workspace),
+                                int(workspace_bytes), int(staged), _p(partials),
+                                int(partials_capacity), *g2.args(), int(accumulate),
+                                _p(counters), _stream(stream)))
 
 
-def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii, grads2d,
-                   dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh, accumulate=0,
-                   stream=None):
+def gs_project_bwd(N, ld, sh_degree, means, scales, quats, sh, cam, settings, radii,
+                   dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans, dL_dscales, dL_dquats,
+                   dL_dsh, accumulate=0, stream=None):
     lib = load()
     _check(lib.gs_project_bwd(N, ld, sh_degree, _p(means), _p(scales), _p(quats), _p(sh),
-                              C.byref(cam), C.byref(settings), _p(radii), _p(grads2d),
-                              _p(dL_dmeans), _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
-                              _p(dL_dsh), int(accumulate), _stream(stream)))
+                              C.byref(cam), C.byref(settings), _p(radii), _p(dL_dmeans2d),
+                              _p(dL_dconics), _p(dL_dcolors), _p(dL_dmeans), _p(dL_dscales),
+                              _p(dL_dquats), _p(dL_dsh), int(accumulate), _stream(stream)))
 
 
 def gs_bin_and_sort_packed(N, ld, means2d, radii, depths, tiles_touched, width, height, offsets,
@@ -304,42 +356,42 @@ def gs_bin_and_sort_packed(N, ld, means2d, radii, depths, tiles_touched, width, 
     return st, int(counts[0]), int(counts[1])
 
 
-def gs_rasterize_bwd_packed(N, ld, width, height, tile_ranges, ids, splats, offsets,
-                            tiles_touched, num_instances, vis_ids, num_visible, background,
-                            settings, final_T, last_idx, dL_dimage, partials, partials_capacity,
-                            grads2d, absgrad=0, counters=None, stream=None, tile_order=None):
+def gs_rasterize_bwd_packed(N, ld, width, height, tile_ranges, ids, sp: SplatPlanes, offsets,
+                            tiles_touched, num_instances, vis_ids, num_visible, ldv, background,
+                            settings, final_T, last_idx, dL_dimage, workspace, workspace_bytes,
+                            staged, partials, partials_capacity, g2: Grad2D, accumulate=0,
+                            counters=None, stream=None, tile_order=None):
     lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_bwd_packed(N, ld, width, height, _p(tile_ranges), _p(tile_order),
-                                       _p(ids),
-                                       _p(splats), _p(offsets), _p(tiles_touched),
-                                       int(num_instances), _p(vis_ids), int(num_visible), bg,
-                                       C.byref(settings), _p(final_T), _p(last_idx),
-                                       _p(dL_dimage), _p(partials), int(partials_capacity),
-                                       _p(grads2d), int(absgrad), _p(counters), _stream(stream)))
+                                       _p(ids), *sp.args(), _p(offsets), _p(tiles_touched),
+                                       int(num_instances), _p(vis_ids), int(num_visible),
+                                       int(ldv), _bg(background), C.byref(settings),
+                                       _p(final_T), _p(last_idx), _p(dL_dimage), _p(workspace),
+                                       int(workspace_bytes), int(staged), _p(partials),
+                                       int(partials_capacity), *g2.args(), int(accumulate),
+                                       _p(counters), _stream(stream)))
 
 
 def gs_project_bwd_packed(num_visible, vis_ids, N, ld, ldv, sh_degree, means, scales, quats, sh,
-                          cam, settings, radii, grads2d, dL_dmeans, dL_dscales, dL_dquats,
-                          dL_dopacities, dL_dsh, accumulate=0, stream=None):
+                          cam, settings, radii, dL_dmeans2d, dL_dconics, dL_dcolors, dL_dmeans,
+                          dL_dscales, dL_dquats, dL_dsh, accumulate=0, stream=None):
     lib = load()
     _check(lib.gs_project_bwd_packed(int(num_visible), _p(vis_ids), N, ld, ldv, sh_degree,
                                      _p(means), _p(scales), _p(quats), _p(sh), C.byref(cam),
-                                     C.byref(settings), _p(radii), _p(grads2d), _p(dL_dmeans),
-                                     _p(dL_dscales), _p(dL_dquats), _p(dL_dopacities),
-                                     _p(dL_dsh), int(accumulate), _stream(stream)))
+                                     C.byref(settings), _p(radii), _p(dL_dmeans2d),
+                                     _p(dL_dconics), _p(dL_dcolors), _p(dL_dmeans),
+                                     _p(dL_dscales), _p(dL_dquats), _p(dL_dsh),
+                                     int(accumulate), _stream(stream)))
 
 
-def gs_project_fwd_batched(cams, N, ld, sh_degree, means, scales, quats, opacities, sh,
-                           settings, means2d, conics, depths, radii, colors, tiles_touched,
-                           splats, stream=None):
+def gs_project_fwd_batched(cams, N, ld, sh_degree, means, scales, quats, sh, settings, means2d,
+                           conics, chol, depths, radii, colors, tiles_touched, stream=None):
     lib = load()
     arr = (gs_camera * len(cams))(*cams)
     _check(lib.gs_project_fwd_batched(len(cams), arr, N, ld, sh_degree, _p(means), _p(scales),
-                                      _p(quats), _p(opacities), _p(sh), C.byref(settings),
-                                      _p(means2d), _p(conics), _p(depths), _p(radii),
-                                      _p(colors), _p(tiles_touched), _p(splats),
-                                      _stream(stream)))
+                                      _p(quats), _p(sh), C.byref(settings), _p(means2d),
+                                      _p(conics), _p(chol), _p(depths), _p(radii), _p(colors),
+                                      _p(tiles_touched), _stream(stream)))
 
 
 def gs_bin_and_sort_batched_workspace_size(num_cams, ld, capacity, width, height) -> int:
@@ -361,41 +413,45 @@ def gs_bin_and_sort_batched(num_cams, ld, means2d, radii, depths, tiles_touched,
     return st, int(num_instances[0])
 
 
-def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, depths,
-                             background, settings, image, final_T, last_idx, out_depth=None,
-                             out_alpha=None, counters=None, stream=None, tile_order=None):
+def gs_rasterize_fwd_batched(num_cams, ld, width, height, tile_ranges, ids, sp: SplatPlanes,
+                             background, settings, image, final_T, last_idx, workspace,
+                             workspace_bytes, out_depth=None, out_alpha=None, counters=None,
+                             stream=None, tile_order=None):
     lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_fwd_batched(num_cams, ld, width, height, _p(tile_ranges),
-                                        _p(tile_order), _p(ids),
-                                        _p(splats), _p(depths), bg, C.byref(settings),
-                                        _p(image), _p(final_T), _p(last_idx), _p(out_depth),
-                                        _p(out_alpha), _p(counters), _stream(stream)))
-
-
-def gs_rasterize_bwd_batched(num_cams, ld, width, height, tile_ranges, ids, splats, offsets,
-                             tiles_touched, num_instances, background, settings, final_T,
-                             last_idx, dL_dimage, partials, partials_capacity, grads2d,
-                             absgrad=0, counters=None, stream=None, tile_order=None):
-    lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
-    _check(lib.gs_rasterize_bwd_batched(num_cams, ld, width, height, _p(tile_ranges),
-                                        _p(tile_order), _p(ids),
-                                        _p(splats), _p(offsets), _p(tiles_touched),
-                                        int(num_instances), bg, C.byref(settings), _p(final_T),
-                                        _p(last_idx), _p(dL_dimage), _p(partials),
-                                        int(partials_capacity), _p(grads2d), int(absgrad),
+                                        _p(tile_order), _p(ids), *sp.args(), _p(sp.depths),
+                                        _bg(background), C.byref(settings), _p(image),
+                                        _p(final_T), _p(last_idx), _p(out_depth),
+                                        _p(out_alpha), _p(workspace), int(workspace_bytes),
                                         _p(counters), _stream(stream)))
 
 
+def gs_rasterize_bwd_batched(num_cams, ld, width, height, tile_ranges, ids, sp: SplatPlanes,
+                             offsets, tiles_touched, num_instances, background, settings,
+                             final_T, last_idx, dL_dimage, workspace, workspace_bytes, staged,
+                             partials, partials_capacity, g2: Grad2D, accumulate=0,
+                             counters=None, stream=None, tile_order=None):
+    lib = load()
+    _check(lib.gs_rasterize_bwd_batched(num_cams, ld, width, height, _p(tile_ranges),
+                                        _p(tile_order), _p(ids), *sp.args(), _p(offsets),
+                                        _p(tiles_touched), int(num_instances), _bg(background),
+                                        C.byref(settings), _p(final_T), _p(last_idx),
+                                        _p(dL_dimage), _p(workspace), int(workspace_bytes),
+                                        int(staged), _p(partials), int(partials_capacity),
+                                        *g2.args(), int(accumulate), _p(counters),
+                                        _stream(stream)))
+
+
 def gs_project_bwd_batched(cams, N, ld, sh_degree, means, scales, quats, sh, settings, radii,
-                           grads2d, dL_dmeans, dL_dscales, dL_dquats, dL_dopacities, dL_dsh,
-                           accumulate=0, stream=None):
+                           dL_dmeans2d, dL_dconics, dL_dcolors, dL_dopacities_cams, dL_dmeans,
+                           dL_dscales, dL_dquats, dL_dopacities, dL_dsh, accumulate=0,
+                           stream=None):
     lib = load()
     arr = (gs_camera * len(cams))(*cams)
     _check(lib.gs_project_bwd_batched(len(cams), arr, N, ld, sh_degree, _p(means), _p(scales),
                                       _p(quats), _p(sh), C.byref(settings), _p(radii),
-                                      _p(grads2d), _p(dL_dmeans), _p(dL_dscales),
+                                      _p(dL_dmeans2d), _p(dL_dconics), _p(dL_dcolors),
+                                      _p(dL_dopacities_cams), _p(dL_dmeans), _p(dL_dscales),
                                       _p(dL_dquats), _p(dL_dopacities), _p(dL_dsh),
                                       int(accumulate), _stream(stream)))
 
@@ -412,32 +468,33 @@ def gs_bin_and_sort_device(N, ld, means2d, radii, depths, tiles_touched, width, 
                                       _p(workspace), workspace_bytes, _stream(stream)))
 
 
-def gs_rasterize_fwd_loss(N, ld, width, height, tile_ranges, ids, splats, depths, background,
+def gs_rasterize_fwd_loss(N, ld, width, height, tile_ranges, ids, sp: SplatPlanes, background,
                           settings, kind, target, image, final_T, last_idx, dL_dimage,
-                          out_depth=None, out_alpha=None, loss=None, counters=None, stream=None,
-                          tile_order=None):
+                          workspace, workspace_bytes, out_depth=None, out_alpha=None,
+                          loss=None, counters=None, stream=None, tile_order=None):
     lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_fwd_loss(N, ld, width, height, _p(tile_ranges), _p(tile_order),
-                                     _p(ids), _p(splats),
-                                     _p(depths), bg, C.byref(settings), int(kind), _p(target),
-                                     _p(image), _p(final_T), _p(last_idx), _p(out_depth),
-                                     _p(out_alpha), _p(dL_dimage), _p(loss), _p(counters),
-                                     _stream(stream)))
+                                     _p(ids), *sp.args(), _p(sp.depths), _bg(background),
+                                     C.byref(settings), int(kind), _p(target), _p(image),
+                                     _p(final_T), _p(last_idx), _p(out_depth), _p(out_alpha),
+                                     _p(dL_dimage), _p(loss), _p(workspace),
+                                     int(workspace_bytes), _p(counters), _stream(stream)))
 
 
-def gs_rasterize_fwd_loss_batched(num_cams, ld, width, height, tile_ranges, ids, splats,
-                                  depths, background, settings, kind, target, image, final_T,
-                                  last_idx, dL_dimage, out_depth=None, out_alpha=None, loss=None,
-                                  counters=None, stream=None, tile_order=None):
+def gs_rasterize_fwd_loss_batched(num_cams, ld, width, height, tile_ranges, ids,
+                                  sp: SplatPlanes, background, settings, kind, target, image,
+                                  final_T, last_idx, dL_dimage, workspace, workspace_bytes,
+                                  out_depth=None, out_alpha=None, loss=None, counters=None,
+                                  stream=None, tile_order=None):
     lib = load()
-    bg = (C.c_float * 3)(*[float(x) for x in background])
     _check(lib.gs_rasterize_fwd_loss_batched(num_cams, ld, width, height, _p(tile_ranges),
-                                             _p(tile_order), _p(ids), _p(splats), _p(depths),
-                                             bg, C.byref(settings), int(kind), _p(target),
+                                             _p(tile_order), _p(ids), *sp.args(),
+                                             _p(sp.depths), _bg(background),
+                                             C.byref(settings), int(kind), _p(target),
                                              _p(image), _p(final_T), _p(last_idx),
                                              _p(out_depth), _p(out_alpha), _p(dL_dimage),
-                                             _p(loss), _p(counters), _stream(stream)))
+                                             _p(loss), _p(workspace), int(workspace_bytes),
+                                             _p(counters), _stream(stream)))
 
 
 def gs_tile_order(num_cams, width, height, tile_ranges, tile_order, stream=None):
@@ -575,10 +632,17 @@ class Frame:
     on the current device; only ``gs_bin_and_sort`` synchronises (to read
     the instance count).
 
+    The stages exchange the documented planes: means2d, conics, chol,
+    depths, radii, colors, tiles from the projection; g_means2d, g_conics,
+    g_opacities, g_colors (and g_abs with absgrad) from the compositing
+    backward; g_means, g_scales, g_quats, g_sh from the projection backward.
+    ``records`` is the compositing calls' staging workspace; the backward
+    reuses what the forward staged there.
+
     ``packed=True`` runs the packed calls: ``vis_ids[:V]`` lists the visible
-    Gaussians, ``grads2d[:V]`` and columns ``[:, :V]`` of the gradient planes
-    hold their rows in that order (leading dimension ``ld``), and nothing is
-    written for the others.
+    Gaussians, and columns ``[:, :V]`` of the 2D and 3D gradient planes hold
+    their rows in that order (leading dimension ``ld``); nothing is written
+    for the others.
 
     ``device_count=True`` bins without the read-back (gs_bin_and_sort_device):
     nothing in a frame waits for the GPU, so a frame can be captured into a
@@ -603,7 +667,7 @@ class Frame:
         # reads them as uint32/uint64 and torch only supplies the storage
         f32, i32, u32 = torch.float32, torch.int32, torch.int32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
-        self.means2d, self.conics = z((2, ld), f32), z((3, ld), f32)
+        self.means2d, self.conics, self.chol = z((2, ld), f32), z((3, ld), f32), z((3, ld), f32)
         self.depths, self.radii = z((ld,), f32), z((ld,), i32)
         self.colors, self.tiles = z((3, ld), f32), z((ld,), u32)
         self.offsets = z((max(ld, 1),), u32)
@@ -614,10 +678,12 @@ class Frame:
         self.last_idx = z((height, width), u32)
         self.out_depth = z((height, width), f32) if with_depth_alpha else None
         self.out_alpha = z((height, width), f32) if with_depth_alpha else None
-        # 64-byte records (torch allocations are 256-byte aligned)
-        self.splats = z((max(ld, 1), 16), f32)
-        self.grads2d = z((max(ld, 1), 16), f32)
-        self.g_opacities = z((ld,), f32)
+        # staged 64-byte records (torch allocations are 256-byte aligned)
+        self.rec_bytes = gs_rasterize_workspace_size(ld)
+        self.records = z((self.rec_bytes // 4,), f32)
+        self.g_means2d, self.g_conics = z((2, ld), f32), z((3, ld), f32)
+        self.g_opacities, self.g_colors = z((ld,), f32), z((3, ld), f32)
+        self.g_abs = z((2, ld), f32)
         self.g_means, self.g_scales = z((3, ld), f32), z((3, ld), f32)
         self.g_quats, self.g_sh = z((4, ld), f32), z((3 * self.K, ld), f32)
         self.dL_dimage = z((height, width, 3), f32)
@@ -631,6 +697,7 @@ class Frame:
         self.counts = z((2,), torch.int64)
         self.vis_ids = z((max(ld, 1),), u32) if packed else None
         self.V = 0
+        self.staged = False
         self._alloc_sort(capacity if capacity else max(1024, 4 * ld))
 
     def _alloc_sort(self, capacity):
@@ -646,11 +713,20 @@ class Frame:
         off = (-self.workspace.data_ptr()) % 256
         self.ws = self.workspace[off:off + self.ws_bytes]
 
+    def planes(self, g: "Gaussians") -> SplatPlanes:
+        return SplatPlanes(self.means2d, self.conics, self.chol, g.opacities, self.colors,
+                           self.radii, self.depths)
+
+    def grads2d(self, absgrad=False) -> Grad2D:
+        return Grad2D(self.g_means2d, self.g_conics, self.g_opacities, self.g_colors,
+                      self.g_abs if absgrad else None)
+
     def project(self, g: Gaussians, cam):
         self.cam = cam if isinstance(cam, gs_camera) else make_camera(cam)
-        gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.opacities, g.sh,
-                       self.cam, self.settings, self.means2d, self.conics, self.depths,
-                       self.radii, self.colors, self.tiles, self.splats)
+        self.staged = False
+        gs_project_fwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
+                       self.settings, self.means2d, self.conics, self.chol, self.depths,
+                       self.radii, self.colors, self.tiles)
 
     def _bin_and_sort_packed(self, g: Gaussians):
         args = lambda: (g.N, g.ld, self.means2d, self.radii, self.depths, self.tiles, self.W,
@@ -703,18 +779,20 @@ class Frame:
     def rasterize_loss(self, g: Gaussians, target, kind, with_loss=False, counters=None):
         """Compositing with the loss gradient fused in: dL_dimage (and the
         loss value when with_loss) against target."""
-        gs_rasterize_fwd_loss(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
-                              self.depths, self.background, self.settings, kind, target,
-                              self.image, self.final_T, self.last_idx, self.dL_dimage,
-                              self.out_depth, self.out_alpha,
+        gs_rasterize_fwd_loss(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.planes(g),
+                              self.background, self.settings, kind, target, self.image,
+                              self.final_T, self.last_idx, self.dL_dimage, self.records,
+                              self.rec_bytes, self.out_depth, self.out_alpha,
                               self.loss if with_loss else None, counters,
                               tile_order=self.order)
+        self.staged = True
 
     def rasterize(self, g: Gaussians, counters=None):
-        gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
-                         self.depths, self.background, self.settings, self.image, self.final_T,
-                         self.last_idx, self.out_depth, self.out_alpha, counters,
-                         tile_order=self.order)
+        gs_rasterize_fwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.planes(g),
+                         self.background, self.settings, self.image, self.final_T,
+                         self.last_idx, self.records, self.rec_bytes, self.out_depth,
+                         self.out_alpha, counters, tile_order=self.order)
+        self.staged = True
 
     def forward(self, g: Gaussians, cam):
         self.project(g, cam)
@@ -726,35 +804,40 @@ class Frame:
         gs_image_loss_grad(kind, self.W * self.H * 3, self.image, target, self.dL_dimage,
                            self.loss if with_loss else None)
 
-    def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None, absgrad=False):
+    def rasterize_backward(self, g: Gaussians, dL_dimage=None, counters=None, absgrad=False,
+                           accumulate=0):
         dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        common = (g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.planes(g), self.offsets,
+                  self.tiles, self.M)
         if self.packed:
-            gs_rasterize_bwd_packed(g.N, g.ld, self.W, self.H, self.ranges, self.ids,
-                                    self.splats, self.offsets, self.tiles, self.M, self.vis_ids,
-                                    self.V, self.background, self.settings, self.final_T,
-                                    self.last_idx, dl, self.partials, self.capacity,
-                                    self.grads2d, absgrad=int(bool(absgrad)), counters=counters,
-                                    tile_order=self.order)
-            return
-        gs_rasterize_bwd(g.N, g.ld, self.W, self.H, self.ranges, self.ids, self.splats,
-                         self.offsets, self.tiles, self.M, self.background, self.settings,
-                         self.final_T, self.last_idx, dl, self.partials, self.capacity,
-                         self.grads2d, absgrad=int(bool(absgrad)), counters=counters,
-                         tile_order=self.order)
+            gs_rasterize_bwd_packed(*common, self.vis_ids, self.V, self.ld, self.background,
+                                    self.settings, self.final_T, self.last_idx, dl, self.records,
+                                    self.rec_bytes, int(self.staged), self.partials,
+                                    self.capacity, self.grads2d(absgrad), accumulate,
+                                    counters=counters, tile_order=self.order)
+        else:
+            gs_rasterize_bwd(*common, self.background, self.settings, self.final_T,
+                             self.last_idx, dl, self.records, self.rec_bytes, int(self.staged),
+                             self.partials, self.capacity, self.grads2d(absgrad), accumulate,
+                             counters=counters, tile_order=self.order)
+        self.staged = True
 
     def project_backward(self, g: Gaussians, accumulate=0):
         if self.packed:
             gs_project_bwd_packed(self.V, self.vis_ids, g.N, g.ld, self.ld, g.sh_degree, g.means,
                                   g.scales, g.quats, g.sh, self.cam, self.settings, self.radii,
-                                  self.grads2d, self.g_means, self.g_scales, self.g_quats,
-                                  self.g_opacities, self.g_sh, accumulate)
+                                  self.g_means2d, self.g_conics, self.g_colors, self.g_means,
+                                  self.g_scales, self.g_quats, self.g_sh, accumulate)
             return
         gs_project_bwd(g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats, g.sh, self.cam,
-                       self.settings, self.radii, self.grads2d, self.g_means, self.g_scales,
-                       self.g_quats, self.g_opacities, self.g_sh, accumulate)
+                       self.settings, self.radii, self.g_means2d, self.g_conics, self.g_colors,
+                       self.g_means, self.g_scales, self.g_quats, self.g_sh, accumulate)
 
     def backward(self, g: Gaussians, dL_dimage=None, accumulate=0, absgrad=False):
-        self.rasterize_backward(g, dL_dimage, absgrad=absgrad)
+        """accumulate: add this frame's gradients with respect to the
+        Gaussians (the opacities' and absolute sums included) to the
+        buffers' contents; the 2D planes hold this frame's own."""
+        self.rasterize_backward(g, dL_dimage, absgrad=absgrad, accumulate=2 if accumulate else 0)
         self.project_backward(g, accumulate)
 
 
@@ -779,10 +862,12 @@ class BatchFrame:
         f32, i32 = torch.float32, torch.int32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
         self.means2d, self.conics = z((C_, 2, ld_), f32), z((C_, 3, ld_), f32)
+        self.chol = z((C_, 3, ld_), f32)
         self.depths, self.radii = z((C_, ld_), f32), z((C_, ld_), i32)
         self.colors, self.tiles = z((C_, 3, ld_), f32), z((C_, ld_), i32)
         self.offsets = z((max(C_ * ld_, 1),), i32)
-        self.splats = z((max(C_ * ld_, 1), 16), f32)
+        self.rec_bytes = gs_rasterize_workspace_size(C_ * ld_)
+        self.records = z((self.rec_bytes // 4,), f32)
         self.ranges = z((C_ * self.T, 2), i32)
         self.order = z((C_ * self.T,), i32) if schedule else None
         self.image = z((C_, height, width, 3), f32)
@@ -792,11 +877,13 @@ class BatchFrame:
         self.out_alpha = z((C_, height, width), f32) if with_depth_alpha else None
         self.m_host = torch.zeros((1,), dtype=torch.int64, pin_memory=True)
         self.M = 0
-        # backward: per-camera images and 2D records, gradients summed over
-        # the batch's cameras
+        # backward: per-camera images and 2D gradient planes, 3D gradients
+        # (and the opacity gradient) summed over the batch's cameras
         K = (sh_degree + 1) ** 2
         self.dL_dimage = z((C_, height, width, 3), f32)
-        self.grads2d = z((max(C_ * ld_, 1), 16), f32)
+        self.g_means2d, self.g_conics = z((C_, 2, ld_), f32), z((C_, 3, ld_), f32)
+        self.g_opacities_cams, self.g_colors = z((C_, ld_), f32), z((C_, 3, ld_), f32)
+        self.g_abs = z((C_, 2, ld_), f32)
         self.g_means, self.g_scales = z((3, ld_), f32), z((3, ld_), f32)
         self.g_quats, self.g_opacities = z((4, ld_), f32), z((ld_,), f32)
         self.g_sh = z((3 * K, ld_), f32)
@@ -815,6 +902,10 @@ class BatchFrame:
         off = (-self.workspace.data_ptr()) % 256
         self.ws = self.workspace[off:off + self.ws_bytes]
 
+    def planes(self, g: "Gaussians") -> SplatPlanes:
+        return SplatPlanes(self.means2d, self.conics, self.chol, g.opacities, self.colors,
+                           self.radii, self.depths)
+
     def forward(self, g: "Gaussians", cams, target=None, kind=1, loss=None):
         """The batch's forward; with ``target`` ([C][H][W][3]) the loss
         gradient (kind 0: L2, 1: L1) goes to dL_dimage in the same pass, and
@@ -822,8 +913,8 @@ class BatchFrame:
         assert len(cams) == self.C
         self.cams = [c if isinstance(c, gs_camera) else make_camera(c) for c in cams]
         gs_project_fwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
-                               g.opacities, g.sh, self.settings, self.means2d, self.conics,
-                               self.depths, self.radii, self.colors, self.tiles, self.splats)
+                               g.sh, self.settings, self.means2d, self.conics, self.chol,
+                               self.depths, self.radii, self.colors, self.tiles)
         args = lambda: (self.C, self.ld, self.means2d, self.radii, self.depths, self.tiles,
                         self.W, self.H, self.offsets, self.capacity, self.keys, self.ids,
                         self.ranges, self.ws, self.ws_bytes, self.m_host)
@@ -837,29 +928,33 @@ class BatchFrame:
             gs_tile_order(self.C, self.W, self.H, self.ranges, self.order)
         if target is None:
             gs_rasterize_fwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
-                                     self.splats, self.depths, self.background, self.settings,
-                                     self.image, self.final_T, self.last_idx, self.out_depth,
-                                     self.out_alpha, tile_order=self.order)
+                                     self.planes(g), self.background, self.settings,
+                                     self.image, self.final_T, self.last_idx, self.records,
+                                     self.rec_bytes, self.out_depth, self.out_alpha,
+                                     tile_order=self.order)
         else:
             # the loss gradient into dL_dimage, fused into the compositing
             gs_rasterize_fwd_loss_batched(self.C, self.ld, self.W, self.H, self.ranges,
-                                          self.ids, self.splats, self.depths, self.background,
+                                          self.ids, self.planes(g), self.background,
                                           self.settings, kind, target, self.image,
                                           self.final_T, self.last_idx, self.dL_dimage,
-                                          self.out_depth, self.out_alpha, loss=loss,
-                                          tile_order=self.order)
+                                          self.records, self.rec_bytes, self.out_depth,
+                                          self.out_alpha, loss=loss, tile_order=self.order)
         return self.image
 
     def backward(self, g: "Gaussians", dL_dimage=None, accumulate=0, absgrad=False):
-        """Compositing backward of every camera, then the projection backward
-        summed over the cameras into g_means ... g_sh."""
+        """Compositing backward of every camera (per-camera 2D gradient
+        planes), then the projection backward summed over the cameras into
+        g_means ... g_sh, and the opacity gradients summed into g_opacities."""
         dl = self.dL_dimage if dL_dimage is None else dL_dimage
+        g2 = Grad2D(self.g_means2d, self.g_conics, self.g_opacities_cams, self.g_colors,
+                    self.g_abs if absgrad else None)
         gs_rasterize_bwd_batched(self.C, self.ld, self.W, self.H, self.ranges, self.ids,
-                                 self.splats, self.offsets, self.tiles, self.M, self.background,
-                                 self.settings, self.final_T, self.last_idx, dl, self.partials,
-                                 self.capacity, self.grads2d, int(bool(absgrad)),
-                                 tile_order=self.order)
+                                 self.planes(g), self.offsets, self.tiles, self.M,
+                                 self.background, self.settings, self.final_T, self.last_idx,
+                                 dl, self.records, self.rec_bytes, 1, self.partials,
+                                 self.capacity, g2, 0, tile_order=self.order)
         gs_project_bwd_batched(self.cams, g.N, g.ld, g.sh_degree, g.means, g.scales, g.quats,
-                               g.sh, self.settings, self.radii, self.grads2d, self.g_means,
-                               self.g_scales, self.g_quats, self.g_opacities, self.g_sh,
-                               accumulate)
+                               g.sh, self.settings, self.radii, self.g_means2d, self.g_conics,
+                               self.g_colors, self.g_opacities_cams, self.g_means, self.g_scales,
+                               self.g_quats, self.g_opacities, self.g_sh, accumulate)

@@ -33,33 +33,35 @@
  *     (Opacity = sigmoid(logit), scale = exp(log-scale) and the quaternion's
  *     w-first order are those of the gsplat guide §3.3; the activations stay
  *     with the caller, so gradients are with respect to activated values.)
- *   - Between stages, projected Gaussians and their 2D gradients travel as
- *     64-byte records, one per Gaussian ([ld][16] floats, record i at
- *     X + 16*i, 64-byte aligned): a tile instance then costs one cache line
- *     to stage and one 48-byte gradient store in the backward.
- *       splat record (gs_project_fwd -> compositing), visible Gaussians only:
- *         [0] u  [1] v  [2..4] l11, l21, l22  [5] opacity  [6..8] colour
- *         r,g,b  [9] radius (int32 bits)  [10] ex  [11] ey  [12..14] conic
- *         A, B, C  [15] 0
- *       with (l11, l21, l22) = sqrt(log2(e)/2) (L11, L21, L22), L the
- *       Cholesky factor of the conic (L11 = sqrt(A), L21 = B / L11,
- *       L22 = 1 / sqrt(c), c the dilated 2D covariance's yy entry), so that
- *       the Gaussian at pixel offset (dx, dy) is exp2(-(e1^2 + e2^2)) with
- *       e1 = l11 dx + l21 dy, e2 = l22 dy (the quadratic form as a completed
- *       square, free of cancellation for needle-like splats), and (ex, ey)
- *       padded half-extents of the footprint where alpha can reach
- *       alpha_min (negative: never; +inf: not bounded);
- *       2D gradient record (gs_rasterize_bwd -> gs_project_bwd), and the
- *       same layout per tile instance in its partials buffer:
- *         [0] dL/du [1] dL/dv [2..4] dL/dA, dL/dB, dL/dC [5] dL/dopacity
- *         [6..8] dL/dcolour r,g,b  [9..10] absolute gradients of u, v
- *         (see gs_rasterize_bwd's absgrad; 0 without it)  [11] 0.
+ *   - Between stages, projected Gaussians and their gradients travel as the
+ *     same [p][ld] planes (gsplat guide §3.3 passes its Gaussians to the
+ *     rasterizer as such arrays; §2.2 makes the backward callable on its
+ *     own):
+ *       means2d [2][ld] (u, v: pixel coordinates of the mean),
+ *       conics [3][ld] (A, B, C of q = A dx^2 + 2B dx dy + C dy^2, the
+ *       inverse of the dilated 2D covariance),
+ *       chol [3][ld] (L11, L21, L22: the conic's lower Cholesky factor,
+ *       conic = L L^T, L11 = sqrt(A), L21 = B / L11, L22 = 1 / sqrt(c) with
+ *       c the dilated 2D covariance's yy entry),
+ *       depths [ld] (camera z), radii [ld] (int32, 0 = culled),
+ *       colors [3][ld] (SH colour), tiles_touched [ld] (uint32);
+ *     and backwards dL_dmeans2d [2][ld], dL_dconics [3][ld] (A, B, C as
+ *     independent scalars), dL_dopacities [ld], dL_dcolors [3][ld].
+ *     The compositing calls evaluate q as the completed square
+ *     (L11 dx + L21 dy)^2 + (L22 dy)^2, which is why they take chol beside
+ *     conics: the expanded form cancels for needle-like splats (terms up to
+ *     1e5 times q), and L22 cannot be rebuilt from the conic in fp32 without
+ *     the same cancellation.  Internally each compositing call first stages
+ *     every visible row into a 64-byte record (one cache line per tile
+ *     instance) in the caller's workspace; the backward may reuse the
+ *     forward's records ("staged").
  *   - Images are row-major [H][W] (colour [H][W][3]); pixel (px,py) has its
  *     centre at (px+0.5, py+0.5); tiles are 16x16, T = ceil(W/16)*ceil(H/16),
  *     tile id = ty*ceil(W/16) + tx.
  *   - stream is a hipStream_t (NULL = the default stream).  Every call is
- *     asynchronous on it except gs_bin_and_sort, which reads the instance
- *     count back to the host once.
+ *     asynchronous on it except the binning calls that return M to the host
+ *     (gs_bin_and_sort and its packed, batched and no-allocation forms),
+ *     which read it back once.
  *   - Errors: invalid arguments are rejected on the host before anything is
  *     launched (GS_ERR_INVALID_ARGUMENT); a failed launch returns GS_ERR_HIP.
  *     gs_last_error() gives a thread-local message.  Per-Gaussian pointers
@@ -123,23 +125,19 @@ GS_API int32_t gs_num_tiles(int32_t width, int32_t height);
  * and rotation, MUSA article §3.3).  Per Gaussian: t = R mean + t; cull
  * outside (near, far) or non-finite; Sigma = R(q) S S^T R(q)^T; 2D covariance
  * J W Sigma W^T J^T plus eps2d on the diagonal, with J the pinhole Jacobian
- * (culled unless positive definite); conic = its
- * inverse; radius = ceil(3 sqrt(lambda_max)); pixel mean; number of 16x16
+ * (culled unless positive definite); conic = its inverse and its Cholesky
+ * factor; radius = ceil(3 sqrt(lambda_max)); pixel mean; number of 16x16
  * tiles the square [u-r,u+r]x[v-r,v+r] touches; SH colour.
- * Outputs ([p][ld] planes): means2d [2][ld] (u,v), conics [3][ld] (A,B,C of
- * q = A dx^2 + 2B dx dy + C dy^2), depths [ld] (camera z), radii [ld],
- * colors [3][ld], tiles_touched [ld], and the splat record [ld][16] of
- * every visible Gaussian (opacities [ld] is read for it).  Culled Gaussians
- * get radius 0, tiles 0 and zeros in the planes; their records are not
- * written.  The geometric outputs are computed in IEEE fp32 in a fixed
- * operation order without contraction, so they are reproducible bit for
- * bit. */
+ * Outputs ([p][ld] planes, see the conventions above): means2d, conics,
+ * chol, depths, radii, colors, tiles_touched.  Culled Gaussians get radius
+ * 0, tiles 0 and zeros in the other planes.  The geometric outputs are
+ * computed in IEEE fp32 in a fixed operation order without contraction, so
+ * they are reproducible bit for bit. */
 GS_API gs_status gs_project_fwd(int64_t N, int64_t ld, int32_t sh_degree,
                          const float* means, const float* scales, const float* quats,
-                         const float* opacities, const float* sh, const gs_camera* cam,
-                         const gs_settings* settings, float* means2d, float* conics,
-                         float* depths, int32_t* radii, float* colors,
-                         uint32_t* tiles_touched, float* splats, void* stream);
+                         const float* sh, const gs_camera* cam, const gs_settings* settings,
+                         float* means2d, float* conics, float* chol, float* depths,
+                         int32_t* radii, float* colors, uint32_t* tiles_touched, void* stream);
 
 /* Workspace needed by gs_bin_and_sort for N Gaussians and up to `capacity`
  * tile instances on a width x height image. */
@@ -217,10 +215,17 @@ GS_API gs_status gs_bin_and_sort_noalloc(int64_t N, int64_t ld, const float* mea
 GS_API gs_status gs_tile_order(int32_t num_cams, int32_t width, int32_t height,
                                const uint32_t* tile_ranges, uint32_t* tile_order, void* stream);
 
+/* Workspace of the compositing calls: the staged 64-byte record of each of
+ * `rows` splat rows (rows = N for one camera, num_cams * ld for a batch),
+ * 256-byte aligned. */
+GS_API size_t gs_rasterize_workspace_size(int64_t rows);
+
 /* Stage 4 — front-to-back alpha compositing per 16x16 tile (gsplat guide
- * §2.1, its third, differentiable blending step).  Per pixel, over its
- * tile's sorted list: q, the conic's quadratic form at (px+0.5-u, py+0.5-v),
- * evaluated as the completed square of the splat record;
+ * §2.1, its third, differentiable blending step).  Reads the projection's
+ * planes means2d, conics, chol, colors, radii and the caller's opacities
+ * [ld] (activated, in [0,1]); stages the visible rows into workspace
+ * (gs_rasterize_workspace_size(N) bytes), then per pixel, over its tile's
+ * sorted list: q at (px+0.5-u, py+0.5-v) as the completed square of chol;
  * alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop (without
  * blending) when T (1-alpha) < T_min; else C += colour alpha T, T *= 1-alpha.
  * Outputs: image [H][W][3] = C + T bg; final_T [H][W]; last_idx [H][W] =
@@ -240,12 +245,15 @@ GS_API gs_status gs_tile_order(int32_t num_cams, int32_t width, int32_t height,
  * tile's entries up to the last of its pixels' stops).  Counting uses a
  * separate kernel variant. */
 GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                           const float* splats, const float* depths, const float* background,
-                           const gs_settings* settings, float* image, float* final_T,
-                           uint32_t* last_idx, float* out_depth, float* out_alpha,
-                           uint64_t* counters, void* stream);
+                                  const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                  const uint32_t* ids, const float* means2d,
+                                  const float* conics, const float* chol,
+                                  const float* opacities, const float* colors,
+                                  const int32_t* radii, const float* depths,
+                                  const float* background, const gs_settings* settings,
+                                  float* image, float* final_T, uint32_t* last_idx,
+                                  float* out_depth, float* out_alpha, void* workspace,
+                                  size_t workspace_bytes, uint64_t* counters, void* stream);
 
 /* gs_rasterize_fwd with the image loss gradient fused in: while each
  * pixel's colour is in registers, dL_dimage [H][W][3] receives the gradient
@@ -257,80 +265,102 @@ GS_API gs_status gs_rasterize_fwd(int64_t N, int64_t ld, int32_t width, int32_t 
 GS_API gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int32_t height,
                                        const uint32_t* tile_ranges,
                                        const uint32_t* tile_order, const uint32_t* ids,
-                                       const float* splats, const float* depths,
-                                       const float* background, const gs_settings* settings,
-                                       int32_t kind, const float* target, float* image,
-                                       float* final_T, uint32_t* last_idx, float* out_depth,
-                                       float* out_alpha, float* dL_dimage, float* loss,
-                                       uint64_t* counters, void* stream);
+                                       const float* means2d, const float* conics,
+                                       const float* chol, const float* opacities,
+                                       const float* colors, const int32_t* radii,
+                                       const float* depths, const float* background,
+                                       const gs_settings* settings, int32_t kind,
+                                       const float* target, float* image, float* final_T,
+                                       uint32_t* last_idx, float* out_depth, float* out_alpha,
+                                       float* dL_dimage, float* loss, void* workspace,
+                                       size_t workspace_bytes, uint64_t* counters,
+                                       void* stream);
 
-/* Stage 5a — compositing backward (gsplat guide §2.2).  Walks each pixel's
- * blended list back to front from last_idx, recovering T by division and
- * accumulating the colour behind, and sums per Gaussian the gradients of the
- * loss with respect to u, v, the conic (A, B, C as scalars of
+/* Stage 5a — compositing backward (gsplat guide §2.2).  The same planes as
+ * the forward, plus offsets and tiles_touched of the binning and the
+ * forward's final_T and last_idx.  staged: 1 when workspace still holds
+ * what gs_rasterize_fwd (or _fwd_loss) staged from these same planes
+ * (nothing is staged again), 0 to stage here.  Walks each pixel's blended
+ * list back to front from last_idx, recovering T by division and
+ * accumulating the colour behind, and sums per Gaussian the gradients of
+ * the loss with respect to u, v, the conic (A, B, C as scalars of
  * q = A dx^2 + 2B dx dy + C dy^2), opacity and colour, given dL_dimage
- * [H][W][3].  Each tile writes its nine sums for each of its Gaussians with a
+ * [H][W][3].  Each tile writes its sums for each of its Gaussians with a
  * plain store into that instance's slot of partials (offsets[i] + k for the
- * k-th tile, row-major, of Gaussian i's rect; partials [capacity][16],
- * capacity >= num_instances of gs_bin_and_sort); a segmented reduction then
- * adds each Gaussian's slots, in slot order, into its record of grads2d
- * [ld][16] (visible Gaussians only).  There are no atomics, so the result is
- * bit-for-bit reproducible.  Pairs whose alpha was clamped at alpha_max carry
- * no opacity/conic/mean gradient.
- * absgrad: 0 or 1.  With 1, fields [9] and [10] of each visible Gaussian's
- * record receive the sums over pixels of |dL/du| and |dL/dv| of each
- * pixel's own contribution: the absolute-gradient statistic that
- * densification thresholds (gsplat guide §4.1 trains with it).  With 0
- * they are 0 and the kernel skips that work.
+ * k-th tile, row-major, of Gaussian i's rect; partials [capacity][16] floats,
+ * 64-byte aligned, capacity >= num_instances); a segmented reduction then
+ * adds each Gaussian's slots, in slot order, into dL_dmeans2d [2][ld],
+ * dL_dconics [3][ld], dL_dopacities [ld], dL_dcolors [3][ld].  There are no
+ * atomics, so the result is bit-for-bit reproducible.  accumulate = 0
+ * overwrites every plane (zeros for Gaussians without tiles); 1 adds to
+ * every plane (Gaussians without tiles are left alone); 2 adds to the
+ * gradients that are final after this stage (dL_dopacities and the
+ * absolute sums) and overwrites the per-camera ones (dL_dmeans2d,
+ * dL_dconics, dL_dcolors), which is how a loop over cameras sums them: the
+ * projection backward of each camera then reads that camera's planes and
+ * adds its own terms with its own accumulate.
+ * Pairs whose alpha was clamped at alpha_max carry no opacity/conic/mean
+ * gradient.  The opacity gradient comes from this stage only (opacity enters
+ * only compositing).
+ * dL_dmeans2d_abs: NULL, or [2][ld] receiving (or, with accumulate, adding)
+ * the sums over pixels of |dL/du| and |dL/dv| of each pixel's own
+ * contribution: the absolute-gradient statistic that densification
+ * thresholds (gsplat guide §4.1 trains with it).  NULL skips that work.
  * counters: NULL, or device uint64[4]: [0] pairs evaluated, [1] pairs with a
  * gradient, [2] pairs the plain tile loop walks (256 x a tile's entries up
  * to its pixels' last blended one), [3] wavefront reductions. */
 GS_API gs_status gs_rasterize_bwd(int64_t N, int64_t ld, int32_t width, int32_t height,
-                           const uint32_t* tile_ranges,
-                           const uint32_t* tile_order, const uint32_t* ids,
-                           const float* splats, const uint32_t* offsets,
-                           const uint32_t* tiles_touched, uint64_t num_instances,
-                           const float* background, const gs_settings* settings,
-                           const float* final_T, const uint32_t* last_idx,
-                           const float* dL_dimage, float* partials,
-                           uint64_t partials_capacity, float* grads2d, int32_t absgrad,
-                           uint64_t* counters, void* stream);
+                                  const uint32_t* tile_ranges, const uint32_t* tile_order,
+                                  const uint32_t* ids, const float* means2d,
+                                  const float* conics, const float* chol,
+                                  const float* opacities, const float* colors,
+                                  const int32_t* radii, const uint32_t* offsets,
+                                  const uint32_t* tiles_touched, uint64_t num_instances,
+                                  const float* background, const gs_settings* settings,
+                                  const float* final_T, const uint32_t* last_idx,
+                                  const float* dL_dimage, void* workspace,
+                                  size_t workspace_bytes, int32_t staged, float* partials,
+                                  uint64_t partials_capacity, float* dL_dmeans2d,
+                                  float* dL_dconics, float* dL_dopacities, float* dL_dcolors,
+                                  float* dL_dmeans2d_abs, int32_t accumulate,
+                                  uint64_t* counters, void* stream);
 
-/* Stage 5b — projection backward: chain rule from the 2D gradient records
- * grads2d [ld][16] to means [3][ld], scales [3][ld], quats [4][ld] (through
- * the normalisation), opacities [ld] and sh [K*3][ld].  Visibility comes from
- * radii (the forward's decisions are kept: the fov clamp and the colour clamp
- * are re-evaluated from the same fp32 inputs).  accumulate = 0 overwrites
+/* Stage 5b — projection backward: chain rule from dL_dmeans2d [2][ld],
+ * dL_dconics [3][ld] and dL_dcolors [3][ld] to means [3][ld], scales [3][ld],
+ * quats [4][ld] (through the normalisation) and sh [K*3][ld].  The geometry
+ * is recomputed from the parameters in fp64; visibility comes from radii
+ * (the forward's decisions are kept: the fov clamp and the colour clamp are
+ * re-evaluated from the same fp32 inputs).  accumulate = 0 overwrites
  * (zeros for culled Gaussians); 1 adds, which sums cameras. */
 GS_API gs_status gs_project_bwd(int64_t N, int64_t ld, int32_t sh_degree, const float* means,
-                         const float* scales, const float* quats, const float* sh,
-                         const gs_camera* cam, const gs_settings* settings,
-                         const int32_t* radii, const float* grads2d, float* dL_dmeans,
-                         float* dL_dscales, float* dL_dquats, float* dL_dopacities,
-                         float* dL_dsh, int32_t accumulate, void* stream);
+                                const float* scales, const float* quats, const float* sh,
+                                const gs_camera* cam, const gs_settings* settings,
+                                const int32_t* radii, const float* dL_dmeans2d,
+                                const float* dL_dconics, const float* dL_dcolors,
+                                float* dL_dmeans, float* dL_dscales, float* dL_dquats,
+                                float* dL_dsh, int32_t accumulate, void* stream);
 
 /* Batched cameras: one launch per stage for num_cams cameras (1 .. 8) of one
  * image size, the Gaussians read once.  Row c * ld + i of the per-camera
- * outputs is Gaussian i seen by camera c, and tile c * T + t is tile t of
- * camera c, so a batch is one list of num_cams * ld rows over
+ * outputs is Gaussian i seen by camera c: each per-camera plane set is a
+ * block [c][P][ld] (radii, depths, tiles_touched [c][ld]), and tile c * T + t
+ * is tile t of camera c, so a batch is one list of num_cams * ld rows over
  * num_cams * T tiles and its results per camera equal those of the
  * single-camera calls (keys carry the tile number c * T + t; ids the row
- * c * ld + i, which indexes the batch's splat records).
+ * c * ld + i).
  *
  * gs_project_fwd_batched: gs_project_fwd for every camera of cams (HOST
- * array); outputs means2d [c][2][ld], conics [c][3][ld], depths [c][ld],
- * radii [c][ld], colors [c][3][ld], tiles_touched [c][ld], splats
- * [c][ld][16].  Rows N .. ld-1 of each camera get radius 0 and no tiles,
- * so the outputs are valid input to gs_bin_and_sort_batched.
- * num_cams * ld < 2^31. */
+ * array); outputs means2d [c][2][ld], conics [c][3][ld], chol [c][3][ld],
+ * depths [c][ld], radii [c][ld], colors [c][3][ld], tiles_touched [c][ld].
+ * Rows N .. ld-1 of each camera get radius 0 and no tiles, so the outputs
+ * are valid input to gs_bin_and_sort_batched.  num_cams * ld < 2^31. */
 GS_API gs_status gs_project_fwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N,
                                         int64_t ld, int32_t sh_degree, const float* means,
                                         const float* scales, const float* quats,
-                                        const float* opacities, const float* sh,
-                                        const gs_settings* settings, float* means2d,
-                                        float* conics, float* depths, int32_t* radii,
-                                        float* colors, uint32_t* tiles_touched, float* splats,
-                                        void* stream);
+                                        const float* sh, const gs_settings* settings,
+                                        float* means2d, float* conics, float* chol,
+                                        float* depths, int32_t* radii, float* colors,
+                                        uint32_t* tiles_touched, void* stream);
 
 /* gs_bin_and_sort_batched: gs_bin_and_sort over the num_cams * ld rows of a
  * batch (offsets [num_cams * ld]; tile_ranges [num_cams * T][2]).  The
@@ -348,18 +378,24 @@ GS_API gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const flo
                                          uint32_t* tile_ranges, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
-/* gs_rasterize_fwd_batched: gs_rasterize_fwd for every camera of a batch;
- * image [c][H][W][3], final_T, last_idx, out_depth, out_alpha [c][H][W]
- * (depths [c][ld] from the batch's projection).  last_idx counts entries of
- * the tile's own list, as in the single-camera call. */
+/* gs_rasterize_fwd_batched: gs_rasterize_fwd for every camera of a batch
+ * (planes [c][P][ld] as gs_project_fwd_batched wrote them, opacities [ld]
+ * shared by the cameras; workspace of gs_rasterize_workspace_size(num_cams *
+ * ld) bytes); image [c][H][W][3], final_T, last_idx, out_depth, out_alpha
+ * [c][H][W] (depths [c][ld]).  last_idx counts entries of the tile's own
+ * list, as in the single-camera call. */
 GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t width,
                                           int32_t height, const uint32_t* tile_ranges,
-                                          const uint32_t* tile_order,
-                                          const uint32_t* ids, const float* splats,
+                                          const uint32_t* tile_order, const uint32_t* ids,
+                                          const float* means2d, const float* conics,
+                                          const float* chol, const float* opacities,
+                                          const float* colors, const int32_t* radii,
                                           const float* depths, const float* background,
                                           const gs_settings* settings, float* image,
                                           float* final_T, uint32_t* last_idx, float* out_depth,
-                                          float* out_alpha, uint64_t* counters, void* stream);
+                                          float* out_alpha, void* workspace,
+                                          size_t workspace_bytes, uint64_t* counters,
+                                          void* stream);
 
 /* gs_rasterize_fwd_loss_batched: gs_rasterize_fwd_loss for every camera of
  * a batch (layouts as gs_rasterize_fwd_batched): target and dL_dimage are
@@ -370,44 +406,59 @@ GS_API gs_status gs_rasterize_fwd_batched(int32_t num_cams, int64_t ld, int32_t 
 GS_API gs_status gs_rasterize_fwd_loss_batched(int32_t num_cams, int64_t ld, int32_t width,
                                                int32_t height, const uint32_t* tile_ranges,
                                                const uint32_t* tile_order, const uint32_t* ids,
-                                               const float* splats, const float* depths,
-                                               const float* background,
+                                               const float* means2d, const float* conics,
+                                               const float* chol, const float* opacities,
+                                               const float* colors, const int32_t* radii,
+                                               const float* depths, const float* background,
                                                const gs_settings* settings, int32_t kind,
                                                const float* target, float* image,
                                                float* final_T, uint32_t* last_idx,
                                                float* out_depth, float* out_alpha,
-                                               float* dL_dimage, float* loss,
-                                               uint64_t* counters, void* stream);
+                                               float* dL_dimage, float* loss, void* workspace,
+                                               size_t workspace_bytes, uint64_t* counters,
+                                               void* stream);
 
 /* gs_rasterize_bwd_batched: gs_rasterize_bwd for every camera of a batch
- * (final_T, last_idx [c][H][W], dL_dimage [c][H][W][3]); grads2d receives
- * the 2D gradient record of every row c * ld + i [num_cams * ld][16]
- * (visible rows only). */
+ * (final_T, last_idx [c][H][W], dL_dimage [c][H][W][3]); the 2D gradient
+ * planes are per camera: dL_dmeans2d [c][2][ld], dL_dconics [c][3][ld],
+ * dL_dopacities [c][ld], dL_dcolors [c][3][ld] (dL_dmeans2d_abs [c][2][ld]
+ * or NULL).  gs_project_bwd_batched sums them over the cameras. */
 GS_API gs_status gs_rasterize_bwd_batched(int32_t num_cams, int64_t ld, int32_t width,
                                           int32_t height, const uint32_t* tile_ranges,
-                                          const uint32_t* tile_order,
-                                          const uint32_t* ids, const float* splats,
+                                          const uint32_t* tile_order, const uint32_t* ids,
+                                          const float* means2d, const float* conics,
+                                          const float* chol, const float* opacities,
+                                          const float* colors, const int32_t* radii,
                                           const uint32_t* offsets, const uint32_t* tiles_touched,
                                           uint64_t num_instances, const float* background,
                                           const gs_settings* settings, const float* final_T,
                                           const uint32_t* last_idx, const float* dL_dimage,
-                                          float* partials, uint64_t partials_capacity,
-                                          float* grads2d, int32_t absgrad, uint64_t* counters,
+                                          void* workspace, size_t workspace_bytes,
+                                          int32_t staged, float* partials,
+                                          uint64_t partials_capacity, float* dL_dmeans2d,
+                                          float* dL_dconics, float* dL_dopacities,
+                                          float* dL_dcolors, float* dL_dmeans2d_abs,
+                                          int32_t accumulate, uint64_t* counters,
                                           void* stream);
 
 /* gs_project_bwd_batched: gs_project_bwd summed over the cameras of a batch
- * (radii [c][ld], grads2d [c * ld + i]): each Gaussian's parameters are read
- * once and the cameras that see it add their chain-rule terms in camera
- * order, as num_cams single-camera calls with accumulate would.
- * accumulate = 0: Gaussians no camera sees get zeros. */
+ * (radii [c][ld], 2D gradient planes [c][P][ld]): each Gaussian's
+ * parameters are read once and the cameras that see it add their chain-rule
+ * terms in camera order, as num_cams single-camera calls with accumulate
+ * would.  With dL_dopacities_cams [c][ld] and dL_dopacities [ld] (both or
+ * neither), the per-camera opacity gradients are summed the same way, so a
+ * batch's opacity gradient comes out beside the others.  accumulate = 0:
+ * Gaussians no camera sees get zeros. */
 GS_API gs_status gs_project_bwd_batched(int32_t num_cams, const gs_camera* cams, int64_t N,
                                         int64_t ld, int32_t sh_degree, const float* means,
                                         const float* scales, const float* quats,
                                         const float* sh, const gs_settings* settings,
-                                        const int32_t* radii, const float* grads2d,
-                                        float* dL_dmeans, float* dL_dscales, float* dL_dquats,
-                                        float* dL_dopacities, float* dL_dsh, int32_t accumulate,
-                                        void* stream);
+                                        const int32_t* radii, const float* dL_dmeans2d,
+                                        const float* dL_dconics, const float* dL_dcolors,
+                                        const float* dL_dopacities_cams, float* dL_dmeans,
+                                        float* dL_dscales, float* dL_dquats,
+                                        float* dL_dopacities, float* dL_dsh,
+                                        int32_t accumulate, void* stream);
 
 /* Packed mode (the gsplat guide §4.1 trains with its packed and sparse
  * gradient switches on: only the Gaussians that reach the image take part
@@ -431,40 +482,51 @@ GS_API gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* mean
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* gs_rasterize_bwd_packed: gs_rasterize_bwd with the segmented reduction run
- * over the visible list: row r of grads2d [num_visible][16] receives the
- * 2D gradient record of Gaussian vis_ids[r].  Nothing is written for
- * Gaussians off the list.  vis_ids / num_visible as gs_bin_and_sort_packed
- * returned them for the same frame (entries must be < N). */
+ * over the visible list: row r of the 2D gradient planes (leading dimension
+ * ldv >= num_visible: dL_dmeans2d [2][ldv], dL_dconics [3][ldv],
+ * dL_dopacities [ldv], dL_dcolors [3][ldv], dL_dmeans2d_abs [2][ldv] or
+ * NULL) receives the gradients of Gaussian vis_ids[r].  Nothing is written
+ * for Gaussians off the list.  vis_ids / num_visible as
+ * gs_bin_and_sort_packed returned them for the same frame (entries must be
+ * < N). */
 GS_API gs_status gs_rasterize_bwd_packed(int64_t N, int64_t ld, int32_t width, int32_t height,
                                          const uint32_t* tile_ranges,
                                          const uint32_t* tile_order, const uint32_t* ids,
-                                         const float* splats, const uint32_t* offsets,
-                                         const uint32_t* tiles_touched, uint64_t num_instances,
-                                         const uint32_t* vis_ids, int64_t num_visible,
+                                         const float* means2d, const float* conics,
+                                         const float* chol, const float* opacities,
+                                         const float* colors, const int32_t* radii,
+                                         const uint32_t* offsets, const uint32_t* tiles_touched,
+                                         uint64_t num_instances, const uint32_t* vis_ids,
+                                         int64_t num_visible, int64_t ldv,
                                          const float* background, const gs_settings* settings,
                                          const float* final_T, const uint32_t* last_idx,
-                                         const float* dL_dimage, float* partials,
-                                         uint64_t partials_capacity, float* grads2d,
-                                         int32_t absgrad, uint64_t* counters, void* stream);
+                                         const float* dL_dimage, void* workspace,
+                                         size_t workspace_bytes, int32_t staged,
+                                         float* partials, uint64_t partials_capacity,
+                                         float* dL_dmeans2d, float* dL_dconics,
+                                         float* dL_dopacities, float* dL_dcolors,
+                                         float* dL_dmeans2d_abs, int32_t accumulate,
+                                         uint64_t* counters, void* stream);
 
 /* gs_project_bwd_packed: gs_project_bwd for the num_visible Gaussians of
  * vis_ids only, in sparse form: the parameters are read at vis_ids[r]
- * (planes [p][ld] of the N Gaussians), the 2D record at row r of grads2d,
- * and the gradients go to column r of the packed output planes
- * (dL_dmeans [3][ldv], dL_dscales [3][ldv], dL_dquats [4][ldv],
- * dL_dopacities [ldv], dL_dsh [K*3][ldv], ldv >= num_visible).  Together
- * with vis_ids they are the gradient as (index, value) rows; Gaussians off
- * the list have zero gradient and nothing is written for them.
- * accumulate = 1 adds into the packed rows (the same list only). */
+ * (planes [p][ld] of the N Gaussians), the 2D gradients at row r of the
+ * packed 2D planes, and the gradients go to column r of the packed output
+ * planes (dL_dmeans [3][ldv], dL_dscales [3][ldv], dL_dquats [4][ldv],
+ * dL_dsh [K*3][ldv], ldv >= num_visible; the packed opacity gradients are
+ * those gs_rasterize_bwd_packed wrote).  Together with vis_ids they are the
+ * gradient as (index, value) rows; Gaussians off the list have zero
+ * gradient and nothing is written for them.  accumulate = 1 adds into the
+ * packed rows (the same list only). */
 GS_API gs_status gs_project_bwd_packed(int64_t num_visible, const uint32_t* vis_ids, int64_t N,
                                        int64_t ld, int64_t ldv, int32_t sh_degree,
                                        const float* means, const float* scales,
                                        const float* quats, const float* sh,
                                        const gs_camera* cam, const gs_settings* settings,
-                                       const int32_t* radii, const float* grads2d,
+                                       const int32_t* radii, const float* dL_dmeans2d,
+                                       const float* dL_dconics, const float* dL_dcolors,
                                        float* dL_dmeans, float* dL_dscales, float* dL_dquats,
-                                       float* dL_dopacities, float* dL_dsh, int32_t accumulate,
-                                       void* stream);
+                                       float* dL_dsh, int32_t accumulate, void* stream);
 
 /* Loss gradient of a rendered image against a target, both [count] floats:
  * kind 0 = L2 (sum (x-y)^2, gradient 2(x-y)), kind 1 = L1 (sum |x-y|,

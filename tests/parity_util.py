@@ -77,8 +77,8 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
     T = lambda t, P=None: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
     M = fr.M
     out.update(
-        means2d=T(fr.means2d), conics=T(fr.conics), depths=T(fr.depths), radii=T(fr.radii),
-        colors=T(fr.colors), tiles=T(fr.tiles).view(np.uint32),
+        means2d=T(fr.means2d), conics=T(fr.conics), chol=T(fr.chol), depths=T(fr.depths),
+        radii=T(fr.radii), colors=T(fr.colors), tiles=T(fr.tiles).view(np.uint32),
         offsets=fr.offsets[:N].cpu().numpy().view(np.uint32), M=M,
         keys=fr.keys[:M].cpu().numpy().view(np.uint64), ids=fr.ids[:M].cpu().numpy().view(np.uint32),
         ranges=fr.ranges.cpu().numpy().view(np.uint32), image=fr.image.cpu().numpy(),
@@ -95,21 +95,14 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
             d = np.zeros((N,) + a.shape[1:], a.dtype)
             d[rows] = a
             return d
+        T = unpack
     if backward:
         K = (scene.sh_degree + 1) ** 2
-        if packed:
-            rec = np.zeros((N, 16), np.float32)
-            rec[rows] = fr.grads2d[:fr.V].cpu().numpy()
-            T = unpack
-        else:
-            rec = fr.grads2d[:N].cpu().numpy()
-            vis = out["radii"] > 0
-            rec[~vis] = 0.0  # records of culled Gaussians are not written
         out.update(dL_dimage=fr.dL_dimage.cpu().numpy() if dL_dimage is None else dL_dimage,
                    loss=float(fr.loss.cpu().numpy()[0]),
-                   g_means2d=rec[:, 0:2].copy(), g_conics=rec[:, 2:5].copy(),
-                   g_opac2d=rec[:, 5].copy(), g_colors=rec[:, 6:9].copy(),
-                   g_absgrad=rec[:, 9:11].copy(),
+                   g_means2d=T(fr.g_means2d), g_conics=T(fr.g_conics),
+                   g_opac2d=T(fr.g_opacities), g_colors=T(fr.g_colors),
+                   g_absgrad=T(fr.g_abs) if absgrad else np.zeros((N, 2), np.float32),
                    g_opacities=T(fr.g_opacities),
                    g_means=T(fr.g_means), g_scales=T(fr.g_scales), g_quats=T(fr.g_quats),
                    g_sh=T(fr.g_sh).reshape(N, K, 3))
@@ -117,12 +110,22 @@ def gpu_frame(scene, cam, *, ld=None, settings=None, background=(0.0, 0.0, 0.0),
     return out
 
 
+def grad2d_rows(fr, n, absgrad=False):
+    """A Frame's 2D gradient planes as [n, 9] rows (u, v, A, B, C, opacity,
+    r, g, b; [n, 11] with the absolute sums), for bitwise comparisons."""
+    import torch
+    planes = [fr.g_means2d, fr.g_conics, fr.g_opacities[None], fr.g_colors]
+    if absgrad:
+        planes.append(fr.g_abs)
+    return torch.cat([p[:, :n] for p in planes], 0).T.contiguous()
+
+
 def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None):
     """GPU projection backward fed the given 2D gradients (dict with means2d
-    [N,2], conics [N,3], opacities [N], colors [N,3]), packed into the 2D
-    gradient records; returns the 3D gradients in [N, ...] layout.  With
-    ``vis_ids`` the packed call runs over that list (rows in list order) and
-    its rows are scattered back (zeros off the list)."""
+    [N,2], conics [N,3], colors [N,3]), rounded to fp32 into its 2D gradient
+    planes; returns the 3D gradients in [N, ...] layout.  With ``vis_ids``
+    the packed call runs over that list (rows in list order) and its rows are
+    scattered back (zeros off the list)."""
     import torch
     from differentiable_rasterization_amd import raster
     N = scene.n
@@ -130,32 +133,32 @@ def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None):
     fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=1024,
                       packed=vis_ids is not None)
     fr.project(g, cam)
-    rec = np.zeros(tuple(fr.grads2d.shape), np.float32)
-    rec[:N, 0:2] = g2["means2d"]
-    rec[:N, 2:5] = g2["conics"]
-    rec[:N, 5] = g2["opacities"]
-    rec[:N, 6:9] = g2["colors"]
+    rows = np.arange(N) if vis_ids is None else np.asarray(vis_ids, np.int64)
+    V = len(rows)
+
+    def put(plane, a):
+        a = np.asarray(a, np.float32).reshape(N, -1)[rows]
+        plane.zero_()
+        if V:
+            plane[:, :V].copy_(torch.from_numpy(np.ascontiguousarray(a.T)))
+    put(fr.g_means2d, g2["means2d"])
+    put(fr.g_conics, g2["conics"])
+    put(fr.g_colors, g2["colors"])
     if vis_ids is not None:
-        rows = np.asarray(vis_ids, np.int64)
-        V = len(rows)
-        rec[:V] = rec[rows].copy()
         fr.V = V
         if V:
             fr.vis_ids[:V].copy_(torch.from_numpy(rows.astype(np.int32)))
-    fr.grads2d.copy_(torch.from_numpy(rec))
     fr.project_backward(g)
     torch.cuda.synchronize()
     K = (scene.sh_degree + 1) ** 2
-    T = lambda t: t[:, :N].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
-    if vis_ids is not None:
-        def T(t):
-            a = t[:, :V].T.contiguous().cpu().numpy() if t.dim() == 2 else t[:V].cpu().numpy()
-            d = np.zeros((N,) + a.shape[1:], a.dtype)
-            d[rows] = a
-            return d
+
+    def T(t):
+        a = t[:, :V].T.contiguous().cpu().numpy()
+        d = np.zeros((N,) + a.shape[1:], a.dtype)
+        d[rows] = a
+        return d
     return dict(radii=fr.radii[:N].cpu().numpy(), g_means=T(fr.g_means), g_scales=T(fr.g_scales),
-                g_quats=T(fr.g_quats), g_sh=T(fr.g_sh).reshape(N, K, 3),
-                g_opacities=T(fr.g_opacities))
+                g_quats=T(fr.g_quats), g_sh=T(fr.g_sh).reshape(N, K, 3))
 
 
 def assert_bits_equal(a, b, what):
@@ -262,7 +265,7 @@ def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alp
 
 def check_project_fwd(r):
     g, p = r["gpu"], r["orc"]["proj"]
-    for k in ("means2d", "conics", "depths"):
+    for k in ("means2d", "conics", "chol", "depths"):
         assert_bits_equal(g[k], p[k].astype(np.float32), k)
     assert_bits_equal(g["radii"], p["radii"], "radii")
     assert_bits_equal(g["tiles"], p["tiles"], "tiles")

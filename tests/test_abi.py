@@ -77,8 +77,7 @@ def _call_project(lib, N=4, ld=4, deg=0, cam=None, st=None, null_means=False):
     cam = cam if cam is not None else _cam()
     st = st if st is not None else raster.default_settings()
     return lib.gs_project_fwd(N, ld, deg, None if null_means else dummy, dummy, dummy, dummy,
-                              dummy, C.byref(cam), C.byref(st), dummy, dummy, dummy, dummy, dummy,
-                              dummy, C.c_void_p(64), None)
+                              C.byref(cam), C.byref(st), *([dummy] * 7), None)
 
 
 @pytest.mark.parametrize("kw", [dict(N=-1), dict(N=5, ld=4), dict(deg=4), dict(deg=-1),
@@ -138,36 +137,60 @@ def test_bin_and_sort_noalloc_rejects_bad_and_oversized_arguments(lib):
     assert b"more than its 67108864" in lib.gs_last_error()
 
 
+def _planes(dummy, **kw):
+    """means2d, conics, chol, opacities, colors, radii (overridable by name)."""
+    names = ("means2d", "conics", "chol", "opacities", "colors", "radii")
+    return [kw.get(n, dummy) for n in names]
+
+
+def _grads(dummy, **kw):
+    names = ("g_means2d", "g_conics", "g_opacities", "g_colors")
+    return [kw.get(n, dummy) for n in names] + [kw.get("g_abs", None)]
+
+
 def test_raster_and_loss_reject_bad_arguments(lib):
-    dummy = C.c_void_p(64)
+    dummy = C.c_void_p(256)
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, None, None, dummy, dummy, None, bg, C.byref(st),
-                             dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # no tile ranges
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, C.c_void_p(68), None, bg,
-                             C.byref(st), dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # misaligned records
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, None, dummy, None, bg, C.byref(st),
-                             dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # ids needed when N > 0
-    r = lib.gs_rasterize_fwd(4, 4, 64, 64, dummy, None, dummy, dummy, None, bg, C.byref(st),
-                             dummy, dummy, dummy, dummy, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT  # the depth output needs depths
+    assert lib.gs_rasterize_workspace_size(10) >= 640
+    assert lib.gs_rasterize_workspace_size(-1) == 0
 
-    def bwd(offsets=dummy, M=10, cap=10, partials=dummy, grads=dummy, absgrad=0):
-        return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, None, dummy, dummy, offsets, dummy, M,
-                                    bg, C.byref(st), dummy, dummy, dummy, partials, cap, grads,
-                                    absgrad, None, None)
+    def fwd(ranges=dummy, ids=dummy, depths=None, out_depth=None, ws=dummy, wsb=1 << 20, **kw):
+        return lib.gs_rasterize_fwd(4, 4, 64, 64, ranges, None, ids, *_planes(dummy, **kw),
+                                    depths, bg, C.byref(st), dummy, dummy, dummy, out_depth,
+                                    None, ws, wsb, None, None)
+    assert fwd(ranges=None) == raster.GS_ERR_INVALID_ARGUMENT      # no tile ranges
+    assert fwd(ids=None) == raster.GS_ERR_INVALID_ARGUMENT         # ids needed when N > 0
+    assert fwd(chol=None) == raster.GS_ERR_INVALID_ARGUMENT        # every plane is read
+    assert fwd(opacities=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert fwd(radii=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert fwd(out_depth=dummy) == raster.GS_ERR_INVALID_ARGUMENT  # depth output needs depths
+    assert fwd(ws=None) == raster.GS_ERR_INVALID_ARGUMENT          # staging workspace
+    assert fwd(ws=C.c_void_p(260)) == raster.GS_ERR_INVALID_ARGUMENT  # misaligned
+    assert fwd(wsb=255) == raster.GS_ERR_INVALID_ARGUMENT          # 4 records need 256 bytes
+
+    def bwd(offsets=dummy, M=10, cap=10, partials=dummy, staged=0, acc=0, wsb=1 << 20, **kw):
+        pl = {k: v for k, v in kw.items() if not k.startswith("g_")}
+        gr = {k: v for k, v in kw.items() if k.startswith("g_")}
+        return lib.gs_rasterize_bwd(4, 4, 64, 64, dummy, None, dummy, *_planes(dummy, **pl),
+                                    offsets, dummy, M, bg, C.byref(st), dummy, dummy, dummy,
+                                    dummy, wsb, staged, partials, cap, *_grads(dummy, **gr), acc,
+                                    None, None)
     assert bwd(offsets=None) == raster.GS_ERR_INVALID_ARGUMENT     # offsets needed
     assert bwd(cap=9) == raster.GS_ERR_INVALID_ARGUMENT            # slots < instances
     assert bwd(partials=None) == raster.GS_ERR_INVALID_ARGUMENT
     assert bwd(partials=C.c_void_p(80)) == raster.GS_ERR_INVALID_ARGUMENT  # misaligned
-    assert bwd(grads=C.c_void_p(72)) == raster.GS_ERR_INVALID_ARGUMENT
-    assert bwd(absgrad=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(g_conics=None) == raster.GS_ERR_INVALID_ARGUMENT    # every 2D plane is written
+    assert bwd(g_opacities=None) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(staged=2) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(acc=3) == raster.GS_ERR_INVALID_ARGUMENT
+    assert bwd(wsb=16) == raster.GS_ERR_INVALID_ARGUMENT
     r = lib.gs_project_bwd(4, 4, 0, dummy, dummy, dummy, dummy, C.byref(_cam()), C.byref(st),
-                           dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None)
+                           dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT  # accumulate must be 0/1
+    r = lib.gs_project_bwd(4, 4, 0, dummy, dummy, dummy, dummy, C.byref(_cam()), C.byref(st),
+                           dummy, dummy, None, dummy, dummy, dummy, dummy, dummy, 0, None)
+    assert r == raster.GS_ERR_INVALID_ARGUMENT  # the conic gradients are read
     assert lib.gs_image_loss_grad(2, 10, dummy, dummy, dummy, None, None) == \
         raster.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_image_loss_grad(0, -1, dummy, dummy, dummy, None, None) == \
@@ -187,19 +210,21 @@ def test_packed_calls_reject_bad_arguments(lib):
     assert bas(cnt=None) == raster.GS_ERR_INVALID_ARGUMENT
     assert bas(ld=3) == raster.GS_ERR_INVALID_ARGUMENT
 
-    def rbwd(V=2, vis=dummy, grads=dummy):
-        return lib.gs_rasterize_bwd_packed(4, 4, 64, 64, dummy, None, dummy, dummy, dummy,
-                                           dummy, 10, vis, V, bg, C.byref(st), dummy, dummy, dummy,
-                                           dummy, 10, grads, 0, None, None)
-    assert rbwd(V=5) == raster.GS_ERR_INVALID_ARGUMENT       # more rows than Gaussians
+    def rbwd(V=2, ldv=2, vis=dummy, **gr):
+        return lib.gs_rasterize_bwd_packed(4, 4, 64, 64, dummy, None, dummy, *_planes(dummy),
+                                           dummy, dummy, 10, vis, V, ldv, bg, C.byref(st), dummy,
+                                           dummy, dummy, dummy, 1 << 20, 0, dummy, 10,
+                                           *_grads(dummy, **gr), 0, None, None)
+    assert rbwd(V=5, ldv=5) == raster.GS_ERR_INVALID_ARGUMENT  # more rows than Gaussians
     assert rbwd(V=-1) == raster.GS_ERR_INVALID_ARGUMENT
+    assert rbwd(ldv=1) == raster.GS_ERR_INVALID_ARGUMENT       # ldv < num_visible
     assert rbwd(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
-    assert rbwd(grads=C.c_void_p(72)) == raster.GS_ERR_INVALID_ARGUMENT
+    assert rbwd(g_colors=None) == raster.GS_ERR_INVALID_ARGUMENT
 
     def pbwd(V=2, N=4, ldv=2, vis=dummy, acc=0, deg=3):
         return lib.gs_project_bwd_packed(V, vis, N, N, ldv, deg, dummy, dummy, dummy, dummy,
                                          C.byref(_cam()), C.byref(st), dummy, dummy, dummy,
-                                         dummy, dummy, dummy, dummy, acc, None)
+                                         dummy, dummy, dummy, dummy, dummy, acc, None)
     assert pbwd(ldv=1) == raster.GS_ERR_INVALID_ARGUMENT      # ldv < num_visible
     assert pbwd(V=5) == raster.GS_ERR_INVALID_ARGUMENT
     assert pbwd(vis=None) == raster.GS_ERR_INVALID_ARGUMENT
@@ -258,14 +283,14 @@ def test_batched_calls_reject_bad_arguments(lib):
     cams = (raster.gs_camera * 9)(*([_cam()] * 9))
 
     def proj(n=2, ld=10):
-        return lib.gs_project_fwd_batched(n, cams, 10, ld, 0, *([dummy] * 5), C.byref(st),
+        return lib.gs_project_fwd_batched(n, cams, 10, ld, 0, *([dummy] * 4), C.byref(st),
                                           *([dummy] * 7), None)
     assert proj(n=0) == raster.GS_ERR_INVALID_ARGUMENT
     assert proj(n=9) == raster.GS_ERR_INVALID_ARGUMENT
     assert proj(ld=9) == raster.GS_ERR_INVALID_ARGUMENT           # ld < N
     assert proj(ld=1 << 29, n=4) == raster.GS_ERR_INVALID_ARGUMENT  # 4 ld >= 2^31
     other = (raster.gs_camera * 2)(_cam(64, 64), _cam(32, 64))
-    assert lib.gs_project_fwd_batched(2, other, 10, 10, 0, *([dummy] * 5), C.byref(st),
+    assert lib.gs_project_fwd_batched(2, other, 10, 10, 0, *([dummy] * 4), C.byref(st),
                                       *([dummy] * 7), None) == raster.GS_ERR_INVALID_ARGUMENT
     assert lib.gs_bin_and_sort_batched_workspace_size(0, 10, 100, 64, 64) == 0
     assert lib.gs_bin_and_sort_batched_workspace_size(2, 10, 100, 64, 64) > 0
@@ -277,34 +302,41 @@ def test_batched_calls_reject_bad_arguments(lib):
                                     dummy, dummy, dummy, dummy, 16, None)
     assert r == raster.GS_ERR_INVALID_ARGUMENT                       # workspace too small
     bg = (C.c_float * 3)(0, 0, 0)
-    r = lib.gs_rasterize_fwd_batched(2, 10, 64, 64, None, None, dummy, dummy, None, bg,
-                                     C.byref(st), dummy, dummy, dummy, None, None, None, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # no tile ranges
-    r = lib.gs_rasterize_bwd_batched(9, 10, 64, 64, dummy, None, *([dummy] * 4), 10, bg,
-                                     C.byref(st), dummy, dummy, dummy, dummy, 10, dummy, 0, None,
-                                     None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # too many cameras
-    r = lib.gs_rasterize_bwd_batched(2, 10, 64, 64, dummy, None, *([dummy] * 4), 11, bg,
-                                     C.byref(st), dummy, dummy, dummy, dummy, 10, dummy, 0, None,
-                                     None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # partials too small
-    r = lib.gs_project_bwd_batched(2, cams, 10, 10, 0, *([dummy] * 4), C.byref(st), dummy,
-                                   dummy, *([dummy] * 5), 2, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT                       # accumulate 0/1
-    r = lib.gs_project_bwd_batched(0, cams, 10, 10, 0, *([dummy] * 4), C.byref(st), dummy,
-                                   dummy, *([dummy] * 5), 0, None)
-    assert r == raster.GS_ERR_INVALID_ARGUMENT
+
+    def fwd(n=2, ranges=dummy, wsb=1 << 20):
+        return lib.gs_rasterize_fwd_batched(n, 10, 64, 64, ranges, None, dummy, *_planes(dummy),
+                                            None, bg, C.byref(st), dummy, dummy, dummy, None,
+                                            None, dummy, wsb, None, None)
+    assert fwd(ranges=None) == raster.GS_ERR_INVALID_ARGUMENT        # no tile ranges
+    assert fwd(n=9) == raster.GS_ERR_INVALID_ARGUMENT
+    assert fwd(wsb=2 * 10 * 64 - 1) == raster.GS_ERR_INVALID_ARGUMENT  # 20 records
+
+    def bwd(n=2, M=10, cap=10):
+        return lib.gs_rasterize_bwd_batched(n, 10, 64, 64, dummy, None, dummy, *_planes(dummy),
+                                            dummy, dummy, M, bg, C.byref(st), dummy, dummy,
+                                            dummy, dummy, 1 << 20, 1, dummy, cap,
+                                            *_grads(dummy), 0, None, None)
+    assert bwd(n=9) == raster.GS_ERR_INVALID_ARGUMENT                # too many cameras
+    assert bwd(M=11) == raster.GS_ERR_INVALID_ARGUMENT               # partials too small
+
+    def pbwd(n=2, acc=0, op_cams=dummy, op=dummy):
+        return lib.gs_project_bwd_batched(n, cams, 10, 10, 0, *([dummy] * 4), C.byref(st),
+                                          dummy, dummy, dummy, dummy, op_cams, dummy, dummy,
+                                          dummy, op, dummy, acc, None)
+    assert pbwd(acc=2) == raster.GS_ERR_INVALID_ARGUMENT             # accumulate 0/1
+    assert pbwd(n=0) == raster.GS_ERR_INVALID_ARGUMENT
+    assert pbwd(op=None) == raster.GS_ERR_INVALID_ARGUMENT           # the opacity pair together
 
 
 def test_fused_loss_rejects_bad_arguments(lib):
-    dummy, other = C.c_void_p(64), C.c_void_p(128)
+    dummy, other = C.c_void_p(256), C.c_void_p(512)
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
 
-    def call(kind=1, target=other, dl=C.c_void_p(192)):
-        return lib.gs_rasterize_fwd_loss(4, 4, 64, 64, dummy, None, dummy, dummy, None, bg,
-                                         C.byref(st), kind, target, dummy, dummy, dummy, None,
-                                         None, dl, None, None, None)
+    def call(kind=1, target=other, dl=C.c_void_p(768)):
+        return lib.gs_rasterize_fwd_loss(4, 4, 64, 64, dummy, None, dummy, *_planes(dummy), None,
+                                         bg, C.byref(st), kind, target, dummy, dummy, dummy, None,
+                                         None, dl, None, dummy, 1 << 20, None, None)
     assert call(kind=2) == raster.GS_ERR_INVALID_ARGUMENT
     assert call(target=None) == raster.GS_ERR_INVALID_ARGUMENT
     assert call(dl=None) == raster.GS_ERR_INVALID_ARGUMENT
@@ -313,14 +345,15 @@ def test_fused_loss_rejects_bad_arguments(lib):
 
 
 def test_batched_fused_loss_rejects_bad_arguments(lib):
-    dummy, other = C.c_void_p(64), C.c_void_p(128)
+    dummy, other = C.c_void_p(256), C.c_void_p(512)
     st = raster.default_settings()
     bg = (C.c_float * 3)(0, 0, 0)
 
-    def call(cams=2, kind=1, target=other, dl=C.c_void_p(192), ranges=dummy):
-        return lib.gs_rasterize_fwd_loss_batched(cams, 10, 64, 64, ranges, None, dummy, dummy,
-                                                 None, bg, C.byref(st), kind, target, dummy,
-                                                 dummy, dummy, None, None, dl, None, None, None)
+    def call(cams=2, kind=1, target=other, dl=C.c_void_p(768), ranges=dummy):
+        return lib.gs_rasterize_fwd_loss_batched(cams, 10, 64, 64, ranges, None, dummy,
+                                                 *_planes(dummy), None, bg, C.byref(st), kind,
+                                                 target, dummy, dummy, dummy, None, None, dl,
+                                                 None, dummy, 1 << 20, None, None)
     assert call(cams=0) == raster.GS_ERR_INVALID_ARGUMENT
     assert call(cams=9) == raster.GS_ERR_INVALID_ARGUMENT
     assert call(kind=2) == raster.GS_ERR_INVALID_ARGUMENT

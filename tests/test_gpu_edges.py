@@ -6,7 +6,7 @@ import pytest
 import oracle
 from differentiable_rasterization_amd import scenes
 
-from parity_util import PIX_TOL, assert_bits_equal, gpu_frame
+from parity_util import PIX_TOL, assert_bits_equal, gpu_frame, grad2d_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -26,15 +26,14 @@ def test_counting_variant_matches_and_counts_consistently():
     fr, g = out["frame"], raster.Gaussians.from_scene(scene)
     cnt = torch.zeros(8, dtype=torch.int64, device="cuda")
     img, fT, last = fr.image.clone(), fr.final_T.clone(), fr.last_idx.clone()
-    rec = fr.grads2d.clone()
+    rec = grad2d_rows(fr, g.N).clone()
     fr.rasterize(g, counters=cnt[0:4])
     fr.rasterize_backward(g, counters=cnt[4:8])
     torch.cuda.synchronize()
     assert torch.equal(img, fr.image) and torch.equal(fT, fr.final_T)
     assert torch.equal(last, fr.last_idx)
-    vis = fr.radii[:g.N] > 0
     # the backward sums in a fixed order: identical bits
-    assert torch.equal(rec[:g.N][vis], fr.grads2d[:g.N][vis])
+    assert torch.equal(rec, grad2d_rows(fr, g.N))
     c = cnt.cpu().numpy()
     print("counters fwd", c[:4], "bwd", c[4:])
     assert c[5] == c[1] > 0            # gradient pairs == blended pairs
@@ -231,20 +230,22 @@ def test_loss_value_and_gradient():
 
 
 def test_absgrad_variant_keeps_the_gradients():
-    """absgrad = 1 only adds record fields 9-10 (non-negative sums); every
-    other field is bit-identical to absgrad = 0, and without it 9-10 are 0."""
+    """With the absolute-gradient planes the call only adds their sums
+    (non-negative); every other plane is bit-identical to the call without
+    them."""
     torch = _torch()
     from differentiable_rasterization_amd import raster
     scene, cam = scenes.box_scene(n=20000, seed=14, width=320, height=200, fx=180.0)
     out = gpu_frame(scene, cam, loss_kind="l1", target=scenes.target_image(cam, 8))
     fr, g = out["frame"], raster.Gaussians.from_scene(scene)
-    plain = fr.grads2d[:g.N].clone()
+    plain = grad2d_rows(fr, g.N).clone()
+    fr.g_abs.fill_(-3.0)
     fr.rasterize_backward(g, absgrad=True)
     torch.cuda.synchronize()
-    vis = (fr.radii[:g.N] > 0).cpu().numpy()
-    a, b = plain.cpu().numpy()[vis], fr.grads2d[:g.N].cpu().numpy()[vis]
+    a, b = plain.cpu().numpy(), grad2d_rows(fr, g.N, absgrad=True).cpu().numpy()
     assert_bits_equal(b[:, 0:9], a[:, 0:9], "fields 0-8")
-    assert np.all(a[:, 9:12] == 0)
+    vis = (fr.radii[:g.N] > 0).cpu().numpy()
+    assert np.all(b[~vis, 9:11] == 0)  # overwritten, zeros without tiles
     assert np.all(b[:, 9:11] >= 0) and np.count_nonzero(b[:, 9:11]) > 0
     # |sum| <= sum |.|
     assert np.all(np.abs(b[:, 0:2]) <= b[:, 9:11] * (1 + 1e-5) + 1e-30)

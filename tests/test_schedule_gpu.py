@@ -86,6 +86,6 @@ def test_batched_schedule():
     ranges = a.ranges.cpu().numpy().view(np.uint32).reshape(len(cams), T, 2)
     for c in range(len(cams)):
         check_order(order[c], ranges[c], T)
-    for k in ("image", "final_T", "last_idx", "grads2d", "g_means", "g_scales", "g_quats",
-              "g_opacities", "g_sh"):
+    for k in ("image", "final_T", "last_idx", "g_means2d", "g_conics", "g_opacities_cams",
+              "g_colors", "g_means", "g_scales", "g_quats", "g_opacities", "g_sh"):
         assert_bits_equal(getattr(a, k).cpu().numpy(), getattr(b, k).cpu().numpy(), k)
