@@ -150,16 +150,20 @@ __device__ inline bool project_geom(const float m[3], const float s[3], const fl
 // N_lm = sqrt((2l+1)/(4 pi) (l-|m|)!/(l+|m|)!) (times sqrt 2 for m != 0)
 // times the integer factor of the Cartesian polynomial of P_l^|m|.
 namespace shc {
-constexpr float C0 = 0.28209479177387814f;
-constexpr float C1 = 0.4886025119029199f;
-constexpr float C2a = 1.0925484305920792f;   // xy, yz, xz
-constexpr float C2b = 0.31539156525252005f;  // 3z^2 - 1
-constexpr float C2c = 0.5462742152960396f;   // x^2 - y^2
-constexpr float C3a = 0.5900435899266435f;   // y(3x^2-y^2), x(x^2-3y^2)
-constexpr float C3b = 2.890611442640554f;    // xyz
-constexpr float C3c = 0.4570457994644658f;   // y(5z^2-1), x(5z^2-1)
-constexpr float C3d = 0.3731763325901154f;   // z(5z^2-3)
-constexpr float C3e = 1.445305721320277f;    // z(x^2-y^2)
+constexpr double D0 = 0.28209479177387814;
+constexpr double D1 = 0.4886025119029199;
+constexpr double D2a = 1.0925484305920792;   // xy, yz, xz
+constexpr double D2b = 0.31539156525252005;  // 3z^2 - 1
+constexpr double D2c = 0.5462742152960396;   // x^2 - y^2
+constexpr double D3a = 0.5900435899266435;   // y(3x^2-y^2), x(x^2-3y^2)
+constexpr double D3b = 2.890611442640554;    // xyz
+constexpr double D3c = 0.4570457994644658;   // y(5z^2-1), x(5z^2-1)
+constexpr double D3d = 0.3731763325901154;   // z(5z^2-3)
+constexpr double D3e = 1.445305721320277;    // z(x^2-y^2)
+// the fp32 forward's constants: the same values rounded to fp32
+constexpr float C0 = (float)D0, C1 = (float)D1, C2a = (float)D2a, C2b = (float)D2b,
+                C2c = (float)D2c, C3a = (float)D3a, C3b = (float)D3b, C3c = (float)D3c,
+                C3d = (float)D3d, C3e = (float)D3e;
 }  // namespace shc
 
 __device__ inline void sh_basis(int deg, float x, float y, float z, float Y[16]) {
@@ -294,29 +298,32 @@ __global__ __launch_bounds__(256) void project_fwd_kernel(
 }
 
 // Real SH basis and its gradient in fp64, for the backward (the same
-// polynomials and constants as the fp32 forward above).
+// polynomials as the fp32 forward above, with the constants in fp64: the
+// colour clamp is decided on this fp64 value, and fp32-rounded constants
+// (relative error up to 3e-8) would decide it differently for a colour
+// within ~1e-8 of zero).
 __device__ inline void sh_basis64(int deg, double x, double y, double z, double Y[16]) {
   using namespace shc;
-  Y[0] = (double)C0;
+  Y[0] = D0;
   if (deg < 1) return;
-  Y[1] = -(double)C1 * y;
-  Y[2] = (double)C1 * z;
-  Y[3] = -(double)C1 * x;
+  Y[1] = -D1 * y;
+  Y[2] = D1 * z;
+  Y[3] = -D1 * x;
   if (deg < 2) return;
   const double xx = x * x, yy = y * y, zz = z * z;
-  Y[4] = (double)C2a * (x * y);
-  Y[5] = -(double)C2a * (y * z);
-  Y[6] = (double)C2b * (3.0 * zz - 1.0);
-  Y[7] = -(double)C2a * (x * z);
-  Y[8] = (double)C2c * (xx - yy);
+  Y[4] = D2a * (x * y);
+  Y[5] = -D2a * (y * z);
+  Y[6] = D2b * (3.0 * zz - 1.0);
+  Y[7] = -D2a * (x * z);
+  Y[8] = D2c * (xx - yy);
   if (deg < 3) return;
-  Y[9] = -(double)C3a * (y * (3.0 * xx - yy));
-  Y[10] = (double)C3b * (x * y * z);
-  Y[11] = -(double)C3c * (y * (5.0 * zz - 1.0));
-  Y[12] = (double)C3d * (z * (5.0 * zz - 3.0));
-  Y[13] = -(double)C3c * (x * (5.0 * zz - 1.0));
-  Y[14] = (double)C3e * (z * (xx - yy));
-  Y[15] = -(double)C3a * (x * (xx - 3.0 * yy));
+  Y[9] = -D3a * (y * (3.0 * xx - yy));
+  Y[10] = D3b * (x * y * z);
+  Y[11] = -D3c * (y * (5.0 * zz - 1.0));
+  Y[12] = D3d * (z * (5.0 * zz - 3.0));
+  Y[13] = -D3c * (x * (5.0 * zz - 1.0));
+  Y[14] = D3e * (z * (xx - yy));
+  Y[15] = -D3a * (x * (xx - 3.0 * yy));
 }
 
 __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, double z,
@@ -325,24 +332,24 @@ __device__ inline void sh_basis_grad_acc64(int j, double w, double x, double y, 
   const double xx = x * x, yy = y * y, zz = z * z;
   double dx = 0.0, dy = 0.0, dz = 0.0;
   switch (j) {
-    case 1: dy = -(double)C1; break;
-    case 2: dz = (double)C1; break;
-    case 3: dx = -(double)C1; break;
-    case 4: dx = (double)C2a * y; dy = (double)C2a * x; break;
-    case 5: dy = -(double)C2a * z; dz = -(double)C2a * y; break;
-    case 6: dz = 6.0 * (double)C2b * z; break;
-    case 7: dx = -(double)C2a * z; dz = -(double)C2a * x; break;
-    case 8: dx = 2.0 * (double)C2c * x; dy = -2.0 * (double)C2c * y; break;
-    case 9: dx = -(double)C3a * 6.0 * x * y; dy = -(double)C3a * (3.0 * xx - 3.0 * yy); break;
-    case 10: dx = (double)C3b * y * z; dy = (double)C3b * x * z; dz = (double)C3b * x * y; break;
-    case 11: dy = -(double)C3c * (5.0 * zz - 1.0); dz = -(double)C3c * 10.0 * y * z; break;
-    case 12: dz = (double)C3d * (15.0 * zz - 3.0); break;
-    case 13: dx = -(double)C3c * (5.0 * zz - 1.0); dz = -(double)C3c * 10.0 * x * z; break;
+    case 1: dy = -D1; break;
+    case 2: dz = D1; break;
+    case 3: dx = -D1; break;
+    case 4: dx = D2a * y; dy = D2a * x; break;
+    case 5: dy = -D2a * z; dz = -D2a * y; break;
+    case 6: dz = 6.0 * D2b * z; break;
+    case 7: dx = -D2a * z; dz = -D2a * x; break;
+    case 8: dx = 2.0 * D2c * x; dy = -2.0 * D2c * y; break;
+    case 9: dx = -D3a * 6.0 * x * y; dy = -D3a * (3.0 * xx - 3.0 * yy); break;
+    case 10: dx = D3b * y * z; dy = D3b * x * z; dz = D3b * x * y; break;
+    case 11: dy = -D3c * (5.0 * zz - 1.0); dz = -D3c * 10.0 * y * z; break;
+    case 12: dz = D3d * (15.0 * zz - 3.0); break;
+    case 13: dx = -D3c * (5.0 * zz - 1.0); dz = -D3c * 10.0 * x * z; break;
     case 14:
-      dx = 2.0 * (double)C3e * x * z; dy = -2.0 * (double)C3e * y * z;
-      dz = (double)C3e * (xx - yy);
+      dx = 2.0 * D3e * x * z; dy = -2.0 * D3e * y * z;
+      dz = D3e * (xx - yy);
       break;
-    case 15: dx = -(double)C3a * (3.0 * xx - 3.0 * yy); dy = (double)C3a * 6.0 * x * y; break;
+    case 15: dx = -D3a * (3.0 * xx - 3.0 * yy); dy = D3a * 6.0 * x * y; break;
     default: break;
   }
   g[0] = fma(w, dx, g[0]);

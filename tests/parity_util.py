@@ -364,6 +364,9 @@ def _classify_3d(r, g, o, e, rows, what):
         unexplained = bad & ~inh & ~flip
         print("[parity] %s %s %s: outside tol %d (flip rows %d, inherited %d) of %d" %
               (r["name"], what, k, bad.sum(), flip.sum(), inh.sum(), bad.size))
+        for i, j in np.argwhere(unexplained)[:5]:
+            print("[parity]   unexplained %s[%d, %d]: gpu %.9g oracle %.9g |d| %.3g bound %.3g"
+                  % (k, i, j, gg[i, j], oo[i, j], err[i, j], ee[i, j]))
         assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])
         assert bounded(inh.sum(), bad.size), (k, inh.sum())
         assert bounded(flip.sum(), bad.size, 1e-4, 16), (k, flip.sum())
@@ -388,17 +391,24 @@ def check_project_bwd(r):
     _classify_3d(r, g, o, e, np.zeros(scene.n, bool), "project_bwd")
 
 
-def check_e2e_grads(r):
-    """Whole path: GPU gradients against the oracle's own forward + backward.
-    2D gradients: as in the stage check.  3D gradients: the GPU's 2D
-    gradients feed its projection backward, and outside their near-threshold
-    rows each is within a = max(1e-3 |g2|, 1e-5, COND_K u sum|terms|) of the
-    oracle's; a 3D element outside max(1e-3 |g|, 1e-5) must lie within the
-    exact bound inherited from 2D inputs known to within a."""
-    g, scene = r["gpu"], r["scene"]
-    orc, bw, dl = r["orc"], r["bw"], r["dl"]
+def _allow2d(g2, a, cols):
+    """The 2D tolerance max(1e-3 |g|, 1e-5, COND_K u sum|terms|) per element."""
+    return np.maximum(np.maximum(G_REL * np.abs(g2), G_ABS), COND_K * EPS32 * a[:, cols])
+
+
+def _e2e_rows(r, g):
+    """Rows reached by near-threshold pixels, L1 sign flips of dL/dimage and
+    pixels whose last blended entry differs."""
+    orc, dl = r["orc"], r["dl"]
     sign_flip = (np.sign(g["dL_dimage"]) != np.sign(dl)).any(axis=2)
-    ex, n_near = _flip_rows(r, g, extra_pixels=(g["last"] != orc["raster"]["last"]) | sign_flip)
+    return _flip_rows(r, g, extra_pixels=(g["last"] != orc["raster"]["last"]) | sign_flip)
+
+
+def check_e2e_2d(r, g=None):
+    """The 2D gradients of a whole GPU path against the oracle's own."""
+    g = r["gpu"] if g is None else g
+    bw = r["bw"]
+    ex, n_near = _e2e_rows(r, g)
     a = bw["g2"]["abs_sum"]
     reps = [compare_grad(g["g_means2d"], bw["g2"]["means2d"], a[:, 0:2], ex, "means2d"),
             compare_grad(g["g_conics"], bw["g2"]["conics"], a[:, 2:5], ex, "conics"),
@@ -407,9 +417,73 @@ def check_e2e_grads(r):
     print("[parity] %s e2e: %d near-threshold or sign-flip pixels reach %d Gaussians" %
           (r["name"], n_near, len(ex)))
     _assert_2d(r, reps, "e2e")
-    allow = lambda go, ab: np.maximum(np.maximum(G_REL * np.abs(go), G_ABS), COND_K * EPS32 * ab)
-    e = _inherited(r, allow(bw["g2"]["means2d"], a[:, 0:2]), allow(bw["g2"]["conics"], a[:, 2:5]),
-                   allow(bw["g2"]["colors"], a[:, 6:9]))
-    rows = np.zeros(scene.n, bool)
+    return ex
+
+
+def _e2e_inherited(r):
+    bw = r["bw"]
+    a = bw["g2"]["abs_sum"]
+    return _inherited(r, _allow2d(bw["g2"]["means2d"], a, slice(0, 2)),
+                      _allow2d(bw["g2"]["conics"], a, slice(2, 5)),
+                      _allow2d(bw["g2"]["colors"], a, slice(6, 9)))
+
+
+def check_e2e_grads(r):
+    """Whole path: GPU gradients against the oracle's own forward + backward.
+    2D gradients: as in the stage check.  3D gradients: the GPU's 2D
+    gradients feed its projection backward, and outside their near-threshold
+    rows each is within a = max(1e-3 |g2|, 1e-5, COND_K u sum|terms|) of the
+    oracle's; a 3D element outside max(1e-3 |g|, 1e-5) must lie within the
+    exact bound inherited from 2D inputs known to within a."""
+    ex = check_e2e_2d(r)
+    rows = np.zeros(r["scene"].n, bool)
     rows[ex] = True
-    _classify_3d(r, g, bw["g3"], e, rows, "e2e")
+    _classify_3d(r, r["gpu"], r["bw"]["g3"], _e2e_inherited(r), rows, "e2e")
+
+
+def check_summed_grads(rs, got, what):
+    """Gradients summed over several cameras (accumulate, or a batch)
+    against the sum of the oracle's per-camera gradients.  ``rs``: the
+    per-camera parity records (their GPU forward outputs locate the
+    near-threshold rows); ``got``: the GPU sums, dict with means, scales,
+    quats, sh ([N, ...]) and opacities [N].  Per camera, an element may miss
+    the oracle by its own allowance (the 2D tolerance for the opacity, the
+    tolerance or the inherited bound for the 3D gradients); a sum outside
+    max(1e-3 |sum|, 1e-5) must lie within the sum of those allowances plus
+    one fp32 rounding per addition (counted, bounded), else in a
+    near-threshold row of some camera (counted, bounded)."""
+    n = rs[0]["scene"].n
+    rows = np.zeros(n, bool)
+    keys = ("means", "scales", "quats", "sh", "opacities")
+    want = {k: 0.0 for k in keys}
+    allow = {k: 0.0 for k in keys}
+    mag = {k: 0.0 for k in keys}
+    for r in rs:
+        ex, _ = _e2e_rows(r, r["gpu"])
+        rows[ex] = True
+        bw = r["bw"]
+        e = _e2e_inherited(r)
+        for k in keys[:4]:
+            oo = bw["g3"][k].reshape(n, -1)
+            tol = np.maximum(G_REL * np.abs(oo), G_ABS)
+            allow[k] = allow[k] + np.maximum(tol, e[k].reshape(n, -1) + 2 * EPS32 * np.abs(oo))
+            want[k] = want[k] + oo
+            mag[k] = mag[k] + np.abs(oo)
+        o2 = bw["g2"]["opacities"].reshape(n, 1)
+        allow["opacities"] = allow["opacities"] + _allow2d(
+            o2, bw["g2"]["abs_sum"][:, 5:6], slice(0, 1))
+        want["opacities"] = want["opacities"] + o2
+        mag["opacities"] = mag["opacities"] + np.abs(o2)
+    for k in keys:
+        gg = np.asarray(got[k], np.float64).reshape(n, -1)
+        err = np.abs(gg - want[k])
+        bad = err > np.maximum(G_REL * np.abs(want[k]), G_ABS)
+        inh = bad & (err <= allow[k] + len(rs) * EPS32 * mag[k])
+        flip = bad & ~inh & rows[:, None]
+        unexplained = bad & ~inh & ~flip
+        print("[parity] %s sum of %d cameras %s: outside tol %d (flip rows %d, within the "
+              "cameras' allowances %d) of %d" % (what, len(rs), k, bad.sum(), flip.sum(),
+                                                inh.sum(), bad.size))
+        assert unexplained.sum() == 0, (k, np.argwhere(unexplained)[:5])
+        assert bounded(inh.sum(), bad.size), (k, inh.sum())
+        assert bounded(flip.sum(), bad.size, 1e-4, 16), (k, flip.sum())

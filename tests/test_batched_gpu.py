@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from differentiable_rasterization_amd import scenes
-from parity_util import PIX_TOL, assert_bits_equal, gpu_frame
+from parity_util import (PIX_TOL, assert_bits_equal, check_e2e_2d, check_raster_fwd,
+                         check_summed_grads, gpu_frame)
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +83,45 @@ def test_batch_against_oracle_small():
         assert d <= PIX_TOL, (c, d)
         base += M
     assert base == bf.M
+
+
+def test_batch_cluster_1m_1080p_four_poses_against_oracle():
+    """Four poses of the timed workload (1M Gaussians, 1920x1080, L1) as one
+    batch, forward with the fused loss gradient and backward, against the
+    oracle run per camera: each camera's image, T, last indices and 2D
+    gradient planes to the parity bars, and the 3D and opacity gradients
+    summed over the batch against the sum of the oracle's."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    scene, cams, _ = scenes.make_config("cluster_1m_1080p")
+    cams = cams[:4]
+    g = raster.Gaussians.from_scene(scene)
+    bf = raster.BatchFrame(g.ld, scene.sh_degree, cams[0].width, cams[0].height, len(cams))
+    tg = np.stack([scenes.target_image(c, 7) for c in cams])
+    bf.forward(g, cams, target=torch.from_numpy(tg).cuda(), kind=1)
+    bf.backward(g)
+    torch.cuda.synchronize()
+    n, K = scene.n, (scene.sh_degree + 1) ** 2
+    P = lambda t, c: t[c][:, :n].T.contiguous().cpu().numpy()
+    rs = []
+    for c, cam in enumerate(cams):
+        orc = oracle.render(scene, cam, None, (0.0, 0.0, 0.0), with_margin=True)
+        dl = oracle.loss_grad_image(orc["raster"]["image"], tg[c], oracle.LOSS_L1)
+        bw = oracle.backward(scene, cam, orc, dl, None, (0.0, 0.0, 0.0), with_abs=True)
+        gpu = dict(image=bf.image[c].cpu().numpy(), final_T=bf.final_T[c].cpu().numpy(),
+                   last=bf.last_idx[c].cpu().numpy().view(np.uint32),
+                   dL_dimage=bf.dL_dimage[c].cpu().numpy(), g_means2d=P(bf.g_means2d, c),
+                   g_conics=P(bf.g_conics, c), g_colors=P(bf.g_colors, c),
+                   g_opac2d=bf.g_opacities_cams[c][:n].cpu().numpy())
+        r = dict(name="cluster_1m_1080p batch camera %d" % c, scene=scene, cam=cam, orc=orc,
+                 gpu=gpu, bw=bw, dl=dl.astype(np.float32))
+        check_raster_fwd(r)
+        check_e2e_2d(r)
+        rs.append(r)
+    T = lambda t: t[:, :n].T.contiguous().cpu().numpy()
+    got = dict(means=T(bf.g_means), scales=T(bf.g_scales), quats=T(bf.g_quats),
+               sh=T(bf.g_sh).reshape(n, K, 3), opacities=bf.g_opacities[:n].cpu().numpy())
+    check_summed_grads(rs, got, "cluster_1m_1080p batch of 4")
 
 
 def test_batch_cluster_200k_three_poses():

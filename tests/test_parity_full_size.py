@@ -5,7 +5,8 @@ configuration the benchmark uses (whole frames through the C ABI):
     alpha outputs, for each of the batch's 4 seeded poses;
   * 6M heavy-tailed Gaussians (Student-t log-scales), SH3, 1024x1024, where
     tiles carry thousands of Gaussians: a whole camera's forward and
-    backward; gradients summed over cameras with accumulate = 1; and, after
+    backward; gradients summed over two cameras with accumulate, against the
+    oracle's two-camera sum; and, after
     gs_densify_prune clones 2% and drops faint Gaussians (so N changes and
     clones create exact depth ties), another camera on the new scene.
 
@@ -19,9 +20,9 @@ import pytest
 
 from differentiable_rasterization_amd import scenes
 
-from parity_util import (assert_bits_equal, check_bins, check_e2e_grads, check_project_bwd,
-                         check_project_fwd, check_raster_bwd, check_raster_fwd,
-                         run_parity_case)
+from parity_util import (assert_bits_equal, check_bins, check_e2e_2d, check_e2e_grads,
+                         check_project_bwd, check_project_fwd, check_raster_bwd,
+                         check_raster_fwd, check_summed_grads, run_parity_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,24 +59,32 @@ def _all_checks(r):
     check_e2e_grads(r)
 
 
-def test_heavy_6m_1024_camera0():
+@functools.lru_cache(maxsize=2)
+def _heavy_case(j):
     scene, cams, loss = _heavy_6m()
-    cam = cams[0]
-    r = run_parity_case("heavy_6m_1024 camera 0", scene, cam, loss, (0.0, 0.0, 0.0),
-                        scenes.target_image(cam, 0))
+    cam = cams[j]
+    return run_parity_case("heavy_6m_1024 camera %d" % j, scene, cam, loss, (0.0, 0.0, 0.0),
+                           scenes.target_image(cam, j))
+
+
+def test_heavy_6m_1024_camera0():
+    r = _heavy_case(0)
     assert r["gpu"]["M"] > 10_000_000
     _all_checks(r)
     _MEAN_GRAD[0] = r["bw"]["g3"]["means"]
 
 
 def test_heavy_6m_1024_accumulate_over_cameras():
-    """accumulate = 1 adds the second camera's gradients into the first's:
-    the result equals the fp32 sum of the two cameras' separate gradients
-    exactly (each backward is deterministic; a Gaussian culled in the second
-    camera keeps its first value, so a -0.0 may stay where the sum has +0.0)."""
+    """Two cameras summed with accumulate: against the oracle's two-camera
+    sum (each camera's allowances added), and bit for bit the fp32 sum of
+    the GPU's two separate frames (each backward is deterministic; a
+    Gaussian culled in the second camera keeps its first value, so a -0.0
+    may stay where the sum has +0.0)."""
     import torch
     from differentiable_rasterization_amd import raster
     scene, cams, loss = _heavy_6m()
+    rs = [_heavy_case(0), _heavy_case(1)]
+    check_e2e_2d(rs[1])
     g = raster.Gaussians.from_scene(scene)
     fr = raster.Frame(g.ld, scene.sh_degree, cams[0].width, cams[0].height)
     names = ("g_means", "g_scales", "g_quats", "g_opacities", "g_sh")
@@ -96,6 +105,11 @@ def test_heavy_6m_1024_accumulate_over_cameras():
     for k in names:
         want = (per_cam[0][k] + per_cam[1][k]).cpu().numpy()
         np.testing.assert_array_equal(getattr(fr, k).cpu().numpy(), want, err_msg=k)
+    n, K = scene.n, (scene.sh_degree + 1) ** 2
+    T = lambda t: t[:, :n].T.contiguous().cpu().numpy()
+    got = dict(means=T(fr.g_means), scales=T(fr.g_scales), quats=T(fr.g_quats),
+               sh=T(fr.g_sh).reshape(n, K, 3), opacities=fr.g_opacities[:n].cpu().numpy())
+    check_summed_grads(rs, got, "heavy_6m_1024 accumulate")
 
 
 def test_heavy_6m_1024_after_densify_prune():
@@ -107,12 +121,9 @@ def test_heavy_6m_1024_after_densify_prune():
     from differentiable_rasterization_amd import raster
     scene, cams, loss = _heavy_6m()
     if 0 not in _MEAN_GRAD:
-        cam = cams[0]
-        orc = oracle.render(scene, cam)
-        dl = oracle.loss_grad_image(orc["raster"]["image"], scenes.target_image(cam, 0),
-                                    oracle.LOSS_L1).astype(np.float32)
-        _MEAN_GRAD[0] = oracle.backward(scene, cam, orc, dl.astype(np.float64))["g3"]["means"]
+        _MEAN_GRAD[0] = _heavy_case(0)["bw"]["g3"]["means"]
     grads = _MEAN_GRAD[0].astype(np.float32)
+    _heavy_case.cache_clear()  # the cameras' records are not needed further
     want = oracle.densify_prune(scene.means, scene.scales, scene.quats, scene.opacities, scene.sh,
                                 grads, 0.02, 0.005)
     g = raster.Gaussians.from_scene(scene)
