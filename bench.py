@@ -49,36 +49,63 @@ BWD_REDUCE_SLOTS = 35.0
 BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
 
 
-def stage_bytes(st, N, V, M, M_bwd, Px, T, K, P, packed=False):
-    """Algorithmic HBM bytes of each stage (what the method must move with the
-    intermediates the ABI materialises)."""
+def algorithmic_bytes(N, V, M, M_fwd, M_bwd, Px, T, K, P, depth_alpha=False):
+    """Algorithmic HBM bytes of each stage by its per-unit figures: N
+    Gaussians, V visible, M tile instances (M_fwd / M_bwd of them staged by
+    the compositing forward / backward before their tiles stop), Px pixels,
+    T tiles, K SH coefficients per channel, P radix-sort passes.
+      projection: mean in and radius, tile count out for every Gaussian
+        (20 B); scales, quaternion, SH in and 2D mean, conic, depth, colour
+        out for the visible (64 + 12 K B);
+      binning and sort: the scan (8 N), the visible's rect inputs (20 V),
+        keys and ids written and P passes of read + write (28 + 24 P per
+        instance), the ranges (8 T);
+      compositing: a 40-byte splat per staged instance, 20 B per pixel out
+        (+8 with depth and alpha);
+      compositing backward: the zero-filled 2D gradients (36 N), their
+        visible rows (36 V), a 40-byte splat per staged instance, 20 B per
+        pixel in;
+      projection backward: radii (4 N), parameters, SH and 2D gradients in
+        for the visible (72 + 12 K), gradients out for every Gaussian
+        (40 + 12 K)."""
+    return {
+        "project_fwd": 20 * N + (64 + 12 * K) * V,
+        "bin_and_sort": 8 * N + 20 * V + (28 + 24 * P) * M + 8 * T,
+        "rasterize_fwd": 40 * M_fwd + 20 * Px + (8 * Px if depth_alpha else 0),
+        "rasterize_bwd": 36 * N + 36 * V + 40 * M_bwd + 20 * Px,
+        "project_bwd": 4 * N + (72 + 12 * K) * V + (40 + 12 * K) * N,
+    }
+
+
+def moved_bytes(N, V, M, M_bwd, Px, T, K, P, packed=False):
+    """The bytes these kernels move, with the intermediates they keep: the
+    staged 64-byte records, per-instance gradient slots, the fused loss
+    gradient's target and dL/dimage."""
     if packed:
-        b = stage_bytes(st, N, V, M, M_bwd, Px, T, K, P)
-        # the visible list written by the scan; the reduction reads it, then
-        # tiles + offsets of the visible only; the projection backward reads
-        # it and writes gradient rows for the visible only
+        b = moved_bytes(N, V, M, M_bwd, Px, T, K, P)
+        # the visible list written by the scan; the reduction reads it and
+        # writes rows for the visible only; so does the projection backward
         b["bin_and_sort"] += 4 * V
-        b["rasterize_bwd"] += 12 * V - 8 * N
-        b["project_bwd"] = 8 * V + (76 + 12 * K) * V + (44 + 12 * K) * V
+        b["rasterize_bwd"] += 4 * V + 36 * V - 36 * N
+        b["project_bwd"] = 4 * V + (72 + 12 * K) * V + (40 + 12 * K) * V
         return b
     return {
-        # means + radius/tiles for all; scales, quats, opacity, SH in and
-        # means2d, conic, depth, colour planes plus the 64-byte splat record out
-        "project_fwd": 20 * N + (132 + 12 * K) * V,
+        # means for all; scales, quats, SH for the visible; the seven output
+        # planes (2D mean, conic, Cholesky factor, depth, radius, colour,
+        # tile count: 56 B) for every Gaussian
+        "project_fwd": 12 * N + (28 + 12 * K) * V + 56 * N,
         "bin_and_sort": 8 * N + 20 * V + (28 + 24 * P) * M + 8 * T,
-        # id + the 48 used bytes of the splat record per instance; image,
+        # staging: radii for all, 48 B of planes in and a 64-byte record out
+        # per visible Gaussian; then id + 48 record bytes per instance; image,
         # final T, last index out; the fused loss gradient: target in,
         # dL/dimage out
-        "rasterize_fwd": 52 * M + 20 * Px + 24 * Px,
-        # per instance walked: id, offset, 64-byte record, 48-byte partial
-        # store; per instance past the tile's last blend: id, offset, 32
-        # record bytes, zero store; final T, last index, dL/dimage in; then the
-        # reduction: tiles + offsets, every partial read, the visible records
-        "rasterize_bwd": 120 * M_bwd + 88 * (M - M_bwd) + 20 * Px
-                         + 8 * N + 48 * M + 48 * V,
-        # radii; parameters, SH and the 2D gradient record in for the visible;
-        # mean, scale, quaternion, opacity and SH gradients out for all
-        "project_bwd": 4 * N + (76 + 12 * K) * V + (44 + 12 * K) * N,
+        "rasterize_fwd": 4 * N + 112 * V + 52 * M + 20 * Px + 24 * Px,
+        # per instance walked: id, offset, 64-byte record, 48-byte slot store;
+        # per instance past the tile's last blend: id, offset, 32 record bytes,
+        # zero store; final T, last index, dL/dimage in; then the reduction:
+        # tiles + offsets, every slot read, nine 2D gradient planes written
+        "rasterize_bwd": 120 * M_bwd + 88 * (M - M_bwd) + 20 * Px + 8 * N + 48 * M + 36 * N,
+        "project_bwd": 4 * N + (72 + 12 * K) * V + (40 + 12 * K) * N,
     }
 
 
@@ -102,21 +129,95 @@ def recorded_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(scene, cams, targets, loss_kind, frames):
-    """The oracle as it stands, fwd+bwd on `frames` poses of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(scene, cams, targets, loss_kind, frames, frames_one):
+    """The oracle as it stands, fwd+bwd on poses of the same workload, on all
+    the host's cores (OpenMP over Gaussians and tiles) and on one thread."""
     import oracle
     kind = oracle.LOSS_L2 if loss_kind == "l2" else oracle.LOSS_L1
-    t0 = time.perf_counter()
-    for i in range(frames):
-        cam = cams[i % len(cams)]
-        f = oracle.render(scene, cam)
-        dl = oracle.loss_grad_image(f["raster"]["image"], targets[i % len(cams)], kind)
-        oracle.backward(scene, cam, f, dl)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        t0 = time.perf_counter()
+        for i in range(n):
+            cam = cams[i % len(cams)]
+            f = oracle.render(scene, cam)
+            dl = oracle.loss_grad_image(f["raster"]["image"], targets[i % len(cams)], kind)
+            oracle.backward(scene, cam, f, dl)
+        return time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    dt = run(frames)
+    oracle.set_threads(1)
+    dt1 = run(frames_one)
+    oracle.set_threads(threads)
     return {"value": frames / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
             "sample": "%d fwd+bwd frame(s) of the same workload (poses 0..%d), %.1f s" %
-                      (frames, frames - 1, dt)}
+                      (frames, frames - 1, dt),
+            "one_thread": {"value": frames_one / dt1, "unit": "frames/s", "cores": 1,
+                           "sample": "%d fwd+bwd frame(s), pose 0.., %.1f s" % (frames_one,
+                                                                              dt1)},
+            "cpu_model": cpu_model()}
+
+
+def stream_copy_gbs(torch, mib=1024, reps=20):
+    """A plain device-to-device copy of `mib` MiB, read + write bytes per
+    second (the HBM rate a streaming kernel reaches on this part)."""
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * 4 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbs
+
+
+def kernel_times(torch, fn, count):
+    """Average device time (ms) and launch count of every kernel that `count`
+    calls of fn() launch, from torch's profiler (None where it is missing)."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(count):
+                fn(i)
+            torch.cuda.synchronize()
+        out = {}
+        for e in prof.key_averages():
+            t = getattr(e, "device_time_total", None)
+            if t is None:
+                t = getattr(e, "cuda_time_total", 0.0)
+            if e.count and t:
+                out[e.key] = (t / 1e3 / e.count, e.count)
+        return out
+    except Exception:  # profiler unavailable on this build
+        return None
+
+
+def _sum_kernels(kt, prefixes, launches_per_call):
+    """Per-call ms of the kernels whose names start with one of prefixes."""
+    if not kt:
+        return None
+    tot = 0.0
+    for name, (ms, n) in kt.items():
+        short = name.split("(")[0].replace("void ", "")
+        if any(short.startswith(p) for p in prefixes):
+            tot += ms * n
+    return tot / launches_per_call if tot else None
 
 
 def densify_bench(args):
@@ -384,6 +485,69 @@ def train_step_bench(args, scene, gcams, targets, capacity):
                      "visible": V}}
 
 
+def box_100k_bench(args):
+    """The 100k-Gaussian box at 1920x1080 (SH3, L2), one frame at a time:
+    forward frames/s (projection, binning, compositing) and fwd+bwd
+    frames/s, with the per-stage times of an instrumented pass.  The gsplat
+    guide (2.1) reports about 2.3 ms of forward rasterization for 100k
+    Gaussians at 1920x1080 on an RTX 4090: quoted as context, another GPU
+    and unstated scene, not a target."""
+    import torch
+    from differentiable_rasterization_amd import raster, scenes
+    scene, cams, _ = scenes.make_config("box_100k_1080p")
+    cam = raster.make_camera(cams[0])
+    W, H = cams[0].width, cams[0].height
+    g = raster.Gaussians.from_scene(scene)
+    fr = raster.Frame(g.ld, scene.sh_degree, W, H)
+    tgt = torch.from_numpy(scenes.target_image(cams[0], 7)).cuda()
+
+    def fwd():
+        fr.project(g, cam)
+        fr.bin_and_sort(g)
+        fr.rasterize(g)
+
+    def fwdbwd():
+        fr.project(g, cam)
+        fr.bin_and_sort(g)
+        fr.rasterize_loss(g, tgt, 0)
+        fr.rasterize_backward(g)
+        fr.project_backward(g)
+    out = {}
+    reps = max(8, args.steps // 2)
+    for name, fn in (("fwd", fwd), ("fwdbwd", fwdbwd)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = reps / (time.perf_counter() - t0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ms = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        ev[0].record()
+        fr.project(g, cam)
+        ev[1].record()
+        fr.bin_and_sort(g)
+        ev[2].record()
+        fr.rasterize(g)
+        ev[3].record()
+        torch.cuda.synchronize()
+        for k in range(3):
+            ms[k] += ev[k].elapsed_time(ev[k + 1]) / reps
+    return {"workload": "box_100k_1080p", "gaussians": scene.n, "width": W, "height": H,
+            "sh_degree": scene.sh_degree, "instances": int(fr.M),
+            "fwd_fps": round(out["fwd"], 2), "fwdbwd_fps": round(out["fwdbwd"], 2),
+            "fwd_stages_ms": {"project_fwd": round(ms[0], 4), "bin_and_sort": round(ms[1], 4),
+                              "rasterize_fwd": round(ms[2], 4)},
+            "context": {"ms_fwd": 2.3, "hardware": "RTX 4090",
+                        "source": "gsplat guide (lmnt.cn/news/262699) 2.1: forward "
+                                  "rasterization of 100k Gaussians at 1920x1080",
+                        "note": "another GPU and an unstated scene and SH degree; context, "
+                                "not a target"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +556,7 @@ def main():
     ap.add_argument("--config", default="cluster_1m_1080p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=16)
+    ap.add_argument("--cpu-frames-one-thread", type=int, default=1)
     ap.add_argument("--densify", action="store_true",
                     help="time gs_densify_prune on the 6M-Gaussian scene instead")
     ap.add_argument("--absgrad", action="store_true",
@@ -577,55 +742,72 @@ def main():
     # average workload over the poses the timed steps visited
     visited = [stats[i % P] for i in range(args.steps)]
     avg = {k: float(np.mean([s[k] for s in visited])) for k in visited[0]}
-    byts = stage_bytes(None, N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes,
-                       packed=args.packed)
+    algo_b = algorithmic_bytes(N, avg["V"], avg["M"], avg["fwd_plain_tile"] / 256.0,
+                               avg["M_bwd"], Px, T, K, sort_passes)
+    moved_b = moved_bytes(N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes,
+                          packed=args.packed)
     stages = {}
     for n in names:
         ms = stage_ms[n]
-        gbs = byts[n] / (ms * 1e-3) / 1e9
+        gbs = algo_b[n] / (ms * 1e-3) / 1e9
         stages[n] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "moved_GB/s": round(moved_b[n] / (ms * 1e-3) / 1e9, 1)}
     fps = args.steps / dt
     fwd_ms = stage_ms["project_fwd"] + stage_ms["bin_and_sort"] + stage_ms["rasterize_fwd"]
-    dominant = max(names, key=lambda n: stage_ms[n])
-    # The compositing kernels are bound by VALU issue.  Algorithmic work = the
-    # pairs the plain tile loop evaluates (per tile, 256 x its entries up to
-    # the last of its pixels' stops; the backward walks up to the last
-    # blended entry) x the VALU slots a pair costs in the kernel's loop.
-    # "blended" counts only the pairs whose result the method uses; "issued"
-    # counts every pair the kernel evaluated and every wavefront reduction.
-    alu = {
-        "rasterize_fwd": (avg["fwd_plain_tile"] * FWD_SLOTS_PER_PAIR,
-                          avg["blended"] * FWD_SLOTS_PER_PAIR,
-                          avg["fwd_eval"] * FWD_SLOTS_PER_PAIR),
-        "rasterize_bwd": (avg["bwd_plain_tile"] * BWD_SLOTS_PER_PAIR,
-                          avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
-                          avg["bwd_eval"] * BWD_EVAL_SLOTS +
-                          avg["bwd_reductions"] * 64 * (BWD_GRAD_SLOTS + BWD_REDUCE_SLOTS)),
-    }
+    frame_ms = sum(stage_ms.values())
+    # kernel-level device times of one-frame-at-a-time steps (untimed pass)
+    kt = kernel_times(torch, lambda i: step(i, fr=fr), P)
+    sort_ms = _sum_kernels(kt, ("gs::sort_histogram_kernel", "gs::sort_hist_scan_kernel",
+                                "gs::sort_pass_kernel"), P)
+    bwd_kernel_ms = _sum_kernels(kt, ("gs::raster_bwd_kernel",), P)
+    reduce_ms = _sum_kernels(kt, ("gs::reduce_partials_kernel",), P)
+    # The compositing backward is bound by VALU issue.  Its work per call is
+    # counted by its counting variant: the pairs the kernel evaluated (31
+    # slots each) and the wavefront reductions it ran (64 lanes x 48 slots of
+    # gradient terms and lane-swap reduction).  frac = those issued slots per
+    # second of the whole gs_rasterize_bwd call (its segmented reduction
+    # included) against the VALU peak; blended_frac counts only the pairs
+    # whose result the method uses (a floor any loop must evaluate).
+    issued = {"rasterize_bwd": avg["bwd_eval"] * BWD_EVAL_SLOTS +
+              avg["bwd_reductions"] * 64 * (BWD_GRAD_SLOTS + BWD_REDUCE_SLOTS),
+              "rasterize_fwd": avg["fwd_eval"] * FWD_SLOTS_PER_PAIR}
+    useful = {"rasterize_bwd": avg["bwd_hit"] * BWD_SLOTS_PER_PAIR,
+              "rasterize_fwd": avg["blended"] * FWD_SLOTS_PER_PAIR}
+    plain = {"rasterize_bwd": avg["bwd_plain_tile"] * BWD_SLOTS_PER_PAIR,
+             "rasterize_fwd": avg["fwd_plain_tile"] * FWD_SLOTS_PER_PAIR}
     work = {"pairs_blended": int(avg["blended"]), "pairs_evaluated_fwd": int(avg["fwd_eval"]),
             "pairs_evaluated_bwd": int(avg["bwd_eval"]),
             "pairs_plain_method": int(avg["plain_pairs"]),
             "pairs_plain_tile_loop_fwd": int(avg["fwd_plain_tile"]),
             "pairs_plain_tile_loop_bwd": int(avg["bwd_plain_tile"]),
             "pairs_all_tile_pixels": int(avg["pairs_tile"]),
-            "wave_reductions_bwd": int(avg["bwd_reductions"])}
-    if dominant in alu:
-        algo, blended, issued = alu[dominant]
+            "wave_reductions_bwd": int(avg["bwd_reductions"]),
+            "slots_per_evaluated_pair_bwd": BWD_EVAL_SLOTS,
+            "slots_per_reduction_lane_bwd": BWD_GRAD_SLOTS + BWD_REDUCE_SLOTS}
+    dominant = max(names, key=lambda n: stage_ms[n])
+    if dominant in issued:
         t = stage_ms[dominant] * 1e-3
-        ach = algo / t / 1e12
+        ach = issued[dominant] / t / 1e12
         traffic = (recorded_traffic() if (dominant == "rasterize_bwd" and not args.absgrad and
                                           not args.packed and
                                           args.config == "cluster_1m_1080p") else None)
-        roof = {"bound": "alu", "kernel": dominant, "achieved": round(ach, 3),
-                "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+        roof = {"bound": "alu", "kernel": "gs_rasterize_bwd" if dominant == "rasterize_bwd"
+                else "gs_rasterize_fwd_loss",
+                "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
                 "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": traffic,
-                "blended_frac": round(blended / t / 1e12 / VALU_PEAK_TOPS, 4),
-                "issued_frac": round(issued / t / 1e12 / VALU_PEAK_TOPS, 4),
-                "slots_per_pair": BWD_SLOTS_PER_PAIR if dominant == "rasterize_bwd"
-                else FWD_SLOTS_PER_PAIR, "work_per_launch": work}
+                "blended_frac": round(useful[dominant] / t / 1e12 / VALU_PEAK_TOPS, 4),
+                "speedup_over_plain_tile_loop_at_peak":
+                    round(plain[dominant] / t / 1e12 / VALU_PEAK_TOPS, 4),
+                "hbm_frac": stages[dominant]["hbm_frac"], "call_ms": round(stage_ms[dominant], 4),
+                "work_per_launch": work}
+        if dominant == "rasterize_bwd" and bwd_kernel_ms:
+            roof["kernels_ms"] = {"raster_bwd_kernel": round(bwd_kernel_ms, 4),
+                                  "reduce_partials_kernel": round(reduce_ms or 0.0, 4)}
+            roof["frac_compositing_kernel_alone"] = round(
+                issued[dominant] / (bwd_kernel_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4)
     else:
-        ach = byts[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
+        ach = algo_b[dominant] / (stage_ms[dominant] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                 "traffic": None}
@@ -638,15 +820,23 @@ def main():
         "config": {"workload": args.config, "gaussians": N, "width": W, "height": H,
                    "sh_degree": scene.sh_degree, "poses": P, "loss": loss_kind,
                    "visible": int(avg["V"]), "instances": int(avg["M"]),
+                   "sort_passes": sort_passes,
                    "absgrad": bool(args.absgrad), "packed": bool(args.packed),
                    "frames_in_flight": nf},
         "serial": {"value": round(args.steps / dt_serial, 2),
                    "ms_per_step": round(1e3 * dt_serial / args.steps, 4),
                    "form": "the same steps one frame at a time on one stream"},
+        "one_frame": {"value": round(1e3 / frame_ms, 2), "ms": round(frame_ms, 4),
+                      "form": "1 / (sum of the five stage times of one frame, measured one "
+                              "frame at a time with events between the stages)"},
         "fwd_fps": round(1e3 / fwd_ms, 2),
         "sort_keys_per_s": round(avg["M"] / (stage_ms["bin_and_sort"] * 1e-3), 1),
+        "sort_keys_per_s_sort_kernels": (round(avg["M"] / (sort_ms * 1e-3), 1)
+                                         if sort_ms else None),
+        "sort_kernels_ms": round(sort_ms, 4) if sort_ms else None,
         "stages": stages,
         "roofline": roof,
+        "stream_copy_GB/s": round(stream_copy_gbs(torch), 1),
     }
     if packed_line is not None:
         out["packed"] = packed_line
@@ -656,8 +846,11 @@ def main():
         out["fwd_batch"] = batch_line
     if graph_line is not None:
         out["graph"] = graph_line
+    if not args.no_train_step and args.config == "cluster_1m_1080p":
+        out["box_100k_1080p"] = box_100k_bench(args)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames)
+        out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames,
+                                           args.cpu_frames_one_thread)
     print(json.dumps(out), flush=True)
 
 

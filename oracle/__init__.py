@@ -92,6 +92,8 @@ def _load():
         for name in ("orc_rotation",):
             getattr(lib, name).argtypes = [P, P]
         lib.orc_cov3d.argtypes = [P, P, P]
+        lib.orc_set_threads.argtypes = [C.c_int]
+        lib.orc_set_threads.restype = C.c_int
         lib.orc_sh_basis.argtypes = [C.c_int, P, P]
         lib.orc_sh_basis_grad.argtypes = [C.c_int, P, P]
         _lib = lib
@@ -314,6 +316,12 @@ def loss_jvp(means, scales, quats, opacities, sh, sh_degree, cam, target, loss_k
     if return_image:
         return loss.value, dloss.value, sig.value, int(M), img
     return loss.value, dloss.value, sig.value, int(M)
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops from now on (n > 0); returns
+    the current setting."""
+    return int(_load().orc_set_threads(int(n)))
 
 
 def rotation(quat):

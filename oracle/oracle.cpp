@@ -32,6 +32,8 @@
  */
 #include "oracle.h"
 
+#include <omp.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -1178,6 +1180,11 @@ int64_t orc_loss_jvp(int64_t N, int deg, const double* means, const double* scal
   }
   if (signature) *signature = sig;
   return M;
+}
+
+int orc_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
 }
 
 void orc_rotation(const double* quat, double* R) {

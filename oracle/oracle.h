@@ -152,6 +152,10 @@ int64_t orc_loss_jvp(int64_t N, int sh_degree, const double* means,
                      int loss_kind, const double* target, double* loss,
                      double* dloss, uint64_t* signature, double* image_out);
 
+/* Threads the oracle's parallel loops use from now on (n > 0), for timing
+ * it in one-thread and all-core modes; returns the current setting. */
+int orc_set_threads(int n);
+
 /* Building blocks exposed for the pins. */
 void orc_rotation(const double* quat, double* R);          /* R [3,3] of q/|q| */
 void orc_cov3d(const double* quat, const double* scale, double* Sigma); /* [3,3] */
