@@ -10,6 +10,7 @@ Flags:
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -19,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgsraster.so")
+# sha256 of the sources and flags a library was built from, written beside it
+HASH_FILE = LIB + ".srchash"
 SOURCES = ["project.hip", "binsort.hip", "raster.hip", "densify.hip", "train.hip",
            "api.hip"]
 ARCH = "gfx950"
@@ -39,6 +42,21 @@ def flags():
             "-Wall", "-Wno-unused-result"]
 
 
+def source_hash() -> str:
+    """sha256 over the HIP sources, their headers, the C ABI header and the
+    compile flags."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "gsraster.h"), "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(flags()).replace(ROOT, "").encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + flags() + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
@@ -49,6 +67,8 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libgsraster.so")
     os.replace(tmp, LIB)
+    with open(HASH_FILE, "w") as fh:
+        fh.write(source_hash() + "\n")
     return LIB
 
 

@@ -70,6 +70,14 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libgsraster.so is not built: run differentiable_rasterization_amd/build.py")
+    from . import build
+    try:
+        built = open(build.HASH_FILE).read().strip()
+    except OSError:
+        built = None
+    if built != build.source_hash():
+        raise RuntimeError("libgsraster.so was not built from the current csrc/ and include/ "
+                           "sources: run differentiable_rasterization_amd/build.py")
     lib = C.CDLL(LIB_PATH)
     P, i64, i32, u64 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint64
     lib.gs_default_settings.restype = gs_settings

@@ -395,3 +395,13 @@ def test_densify_rejects_bad_arguments(lib):
 def test_status_strings(lib):
     assert lib.gs_status_string(0) == b"GS_OK"
     assert lib.gs_status_string(2) == b"GS_ERR_CAPACITY"
+
+
+def test_load_refuses_a_library_built_from_other_sources(lib, monkeypatch):
+    """The library records the hash of the sources it was built from; a tree
+    whose sources differ is refused rather than run with a stale build."""
+    from differentiable_rasterization_amd import build
+    monkeypatch.setattr(raster, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 64)
+    with pytest.raises(RuntimeError, match="current csrc"):
+        raster.load()
