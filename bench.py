@@ -625,7 +625,16 @@ def main():
     P = len(cams)
     T = fr.T
     Px = W * H
-    sort_passes = (32 + int(np.ceil(np.log2(max(T, 2)))) + 8) // 9  # 9-bit digits
+    tile_bits = int(np.ceil(np.log2(max(T, 2))))
+
+    def sort_passes_of(fr):
+        """The radix passes the sort runs on this frame: 10-bit digits over
+        the tile bits and the bits that the depths of the rows with tiles
+        span."""
+        has = (fr.tiles[:N] > 0).cpu().numpy()
+        db = fr.depths[:N].cpu().numpy().view(np.uint32)[has].astype(np.int64)
+        span = int(db.max() - db.min()) if db.size else 0
+        return max(1, -(-(tile_bits + span.bit_length()) // 10))
     names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "rasterize_bwd", "project_bwd"]
 
     def step(i, ev=None, fr=fr):
@@ -673,7 +682,7 @@ def main():
                           pairs_tile=int((inside * lens).sum()), fwd_eval=int(c[0]),
                           blended=int(c[1]), plain_pairs=int(c[2]), fwd_plain_tile=int(c[3]),
                           bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
-                          bwd_reductions=int(c[7])))
+                          bwd_reductions=int(c[7]), sort_passes=sort_passes_of(fr)))
 
     def run_steps(frs, first, count):
         """Steps first .. first+count-1, step i on frame/stream i mod len(frs)
@@ -742,6 +751,7 @@ def main():
     # average workload over the poses the timed steps visited
     visited = [stats[i % P] for i in range(args.steps)]
     avg = {k: float(np.mean([s[k] for s in visited])) for k in visited[0]}
+    sort_passes = avg["sort_passes"]
     algo_b = algorithmic_bytes(N, avg["V"], avg["M"], avg["fwd_plain_tile"] / 256.0,
                                avg["M_bwd"], Px, T, K, sort_passes)
     moved_b = moved_bytes(N, avg["V"], avg["M"], avg["M_bwd"], Px, T, K, sort_passes,

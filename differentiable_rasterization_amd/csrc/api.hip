@@ -29,13 +29,13 @@ hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
                                  float* o_scales, float* o_quats, float* o_opac, float* o_sh,
                                  int accumulate, hipStream_t stream);
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
-hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets, uint32_t* vis_ids,
-                          void* workspace, uint64_t capacity, int32_t T, uint64_t* totals_host,
-                          hipStream_t s);
+hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
+                          uint32_t* offsets, uint32_t* vis_ids, void* workspace, uint64_t capacity,
+                          int32_t T, uint64_t* totals_host, int* dbits, hipStream_t s);
 hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                      const int32_t* radii, const float* depths,
                                      const uint32_t* tiles, const uint32_t* offsets, int32_t W,
-                                     int32_t H, int ncams, uint64_t M, bool device_count,
+                                     int32_t H, int ncams, uint64_t M, int dbits, bool device_count,
                                      uint64_t* counts, uint64_t* keys, uint32_t* ids,
                                      uint32_t* ranges, void* workspace, uint64_t capacity,
                                      hipStream_t s);
@@ -168,10 +168,10 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
                             uint32_t* tile_ranges, void* workspace, hipStream_t s,
                             const char* name) {
   const int32_t T = gs_num_tiles(width, height);
-  gs_status st = hip_status(
-      gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace, capacity, T, num_instances,
-                     s),
-      name);
+  int dbits = 32;
+  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
+                                           capacity, T, num_instances, &dbits, s),
+                            name);
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
   if (M >= ((uint64_t)1 << 30))
@@ -182,8 +182,8 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, false, nullptr, keys,
-                                              ids, tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, 1, M, dbits, false, nullptr,
+                                              keys, ids, tile_ranges, workspace, capacity, s),
                     name);
 }
 
@@ -425,13 +425,13 @@ gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
   GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
-  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, offsets, nullptr, workspace,
-                                           capacity, T, nullptr, s),
+  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
+                                           capacity, T, nullptr, nullptr, s),
                             "gs_bin_and_sort_device(scan)");
   if (st != GS_OK) return st;
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, 0, true, counts, keys,
-                                              ids, tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, 1, 0, 32, true, counts,
+                                              keys, ids, tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_device");
 }
 
@@ -582,9 +582,10 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
   GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
-  gs_status st = hip_status(
-      gs_launch_scan(N, tiles_touched, offsets, vis_ids, workspace, capacity, T, counts, s),
-      "gs_bin_and_sort_packed(scan)");
+  int dbits = 32;
+  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, vis_ids, workspace,
+                                           capacity, T, counts, &dbits, s),
+                            "gs_bin_and_sort_packed(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = counts[0];
   if (M >= ((uint64_t)1 << 30))
@@ -595,9 +596,8 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, false, nullptr, keys, ids,
-                                              tile_ranges,
-                                              workspace, capacity, s),
+                                              offsets, width, height, 1, M, dbits, false, nullptr,
+                                              keys, ids, tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_packed");
 }
 
@@ -732,8 +732,10 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
   GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(rows, capacity, (int32_t)T),
              "workspace smaller than gs_bin_and_sort_batched_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
-  gs_status st = hip_status(gs_launch_scan(rows, tiles_touched, offsets, nullptr, workspace,
-                                           capacity, (int32_t)T, num_instances, s),
+  int dbits = 32;
+  gs_status st = hip_status(gs_launch_scan(rows, tiles_touched, depths, offsets, nullptr,
+                                           workspace, capacity, (int32_t)T, num_instances, &dbits,
+                                           s),
                             "gs_bin_and_sort_batched(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -745,8 +747,9 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(rows, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, num_cams, M, false, nullptr, keys, ids,
-                                              tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, num_cams, M, dbits, false,
+                                              nullptr, keys, ids, tile_ranges, workspace, capacity,
+                                              s),
                     "gs_bin_and_sort_batched");
 }
 

@@ -8,14 +8,20 @@
 //   - duplication is balanced by output slot: a workgroup owns 256 Gaussians
 //     and writes all of their instances with consecutive, coalesced stores,
 //     so one Gaussian touching thousands of tiles does not serialise a lane;
-//   - the sort is a onesweep LSD radix sort with 9-bit digits: one pass
-//     computes every digit's global histogram, then each digit pass reads and
-//     writes the keys once.  A workgroup takes its partition from an atomic
-//     ticket (so it only ever waits on partitions already running), ranks
-//     its 4096 keys stably with wave64 ballots into LDS histograms, publishes
-//     per-digit counts and resolves its global offsets by decoupled
-//     look-back, then scatters through LDS so that global writes come out
-//     in digit runs.  Only the low 32 + ceil(log2 T) key bits are sorted.
+//   - the sort is a onesweep LSD radix sort with 10-bit digits: one pass
+//     computes every digit's global histogram (partial histograms per block,
+//     summed by the digit scan), then each digit pass reads and writes the
+//     keys once.  A workgroup takes its partition from an atomic ticket (so
+//     it only ever waits on partitions already running), ranks its 8192
+//     keys stably with wave64 ballots into LDS histograms, publishes
+//     per-digit counts and resolves its global offsets by a two-level
+//     look-back (within a group of 16 partitions, then over groups), then
+//     scatters through LDS so that global writes come out in digit runs.
+//     Only the bits that vary within the frame are sorted: the scan also
+//     finds the smallest and largest depth bits of the rows with tiles, and
+//     the passes sort (tile, depth bits - smallest) in ceil(log2 T) +
+//     bits(largest - smallest) bits; with the depths of a typical frame
+//     spanning ~2^26 fp32 codes that is four passes at 1080p.
 #include "gs_common.h"
 
 namespace gs {
@@ -88,20 +94,51 @@ __device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
 // order to vis_ids; its per-block sums follow the first set at sums + nb.
 // ---------------------------------------------------------------------------
 constexpr int kScanItems = 8;
+constexpr int kDbitsShift = 58;
+constexpr uint64_t kCountBits = (1ull << kDbitsShift) - 1ull;
 constexpr int kScanBlock = 256 * kScanItems;
 
+// Smallest and largest u32 over a 256-lane workgroup (valid in every lane).
+__device__ inline void block_minmax_u32(uint32_t& lo, uint32_t& hi) {
+  __shared__ uint32_t s_lo[4], s_hi[4];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_lo[threadIdx.x >> 6] = lo;
+    s_hi[threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
+  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
+  __syncthreads();
+}
+
+// Per block: the sum of tiles (and with kVis the count of rows with tiles),
+// and, with depths and minmax, the smallest and largest depth bits of the
+// rows with tiles (their keys' low words) at minmax[2 * block].
 template <bool kVis>
 __global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __restrict__ in,
+                                                          const float* __restrict__ depths,
                                                           int64_t N,
-                                                          uint64_t* __restrict__ block_sums) {
+                                                          uint64_t* __restrict__ block_sums,
+                                                          uint32_t* __restrict__ minmax) {
   const int64_t base = (int64_t)blockIdx.x * kScanBlock;
   uint64_t s = 0, c = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for (int k = 0; k < kScanItems; ++k) {
     const int64_t i = base + (int64_t)k * 256 + threadIdx.x;
     if (i < N) {
       const uint32_t x = in[i];
       s += x;
       c += x > 0u ? 1u : 0u;
+      if (x > 0u && depths) {
+        const uint32_t db = __float_as_uint(depths[i]);
+        lo = min(lo, db);
+        hi = max(hi, db);
+      }
     }
   }
   uint64_t excl;
@@ -111,24 +148,53 @@ __global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __rest
     const uint64_t ctot = block_excl_scan_u64(c, excl);
     if (threadIdx.x == 0) block_sums[gridDim.x + blockIdx.x] = ctot;
   }
+  if (!minmax) return;
+  block_minmax_u32(lo, hi);
+  if (threadIdx.x == 0) {
+    minmax[2 * blockIdx.x] = lo;
+    minmax[2 * blockIdx.x + 1] = hi;
+  }
 }
 
 // One workgroup per set of nb block sums (blockIdx.x selects the set):
-// exclusive scan in place, the set's total to total[blockIdx.x].
+// exclusive scan in place, the set's total to total[blockIdx.x].  With
+// minmax, the first also folds the blocks' depth-bit ranges into the sort's
+// key map (keymap[0] = smallest depth bits, keymap[1] = bits the range
+// needs) and puts that bit count above the total, in total[0] bits 58-63,
+// so that the host reads it with M.  (M < 2^54: fewer than 2^31 rows, each
+// touching fewer than 2^23 tiles.)
 __global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict__ sums,
                                                             int64_t nb,
-                                                            uint64_t* __restrict__ total) {
+                                                            const uint32_t* __restrict__ minmax,
+                                                            uint64_t* __restrict__ total,
+                                                            uint32_t* __restrict__ keymap) {
   sums += (int64_t)blockIdx.x * nb;
   uint64_t carry = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for (int64_t b = 0; b < nb; b += 256) {
     const int64_t i = b + threadIdx.x;
     const uint64_t x = i < nb ? sums[i] : 0;
+    if (i < nb && blockIdx.x == 0 && minmax) {
+      lo = min(lo, minmax[2 * i]);
+      hi = max(hi, minmax[2 * i + 1]);
+    }
     uint64_t excl;
     const uint64_t tot = block_excl_scan_u64(x, excl);
     if (i < nb) sums[i] = carry + excl;
     carry += tot;
   }
-  if (threadIdx.x == 0) total[blockIdx.x] = carry;
+  if (blockIdx.x == 0 && minmax) block_minmax_u32(lo, hi);
+  if (threadIdx.x == 0) {
+    uint64_t word = carry;
+    if (blockIdx.x == 0 && minmax) {
+      const uint32_t span = lo <= hi ? hi - lo : 0u;
+      const uint32_t dbits = span ? 32u - (uint32_t)__clz((int)span) : 0u;
+      keymap[0] = lo <= hi ? lo : 0u;
+      keymap[1] = dbits;
+      word |= (uint64_t)dbits << kDbitsShift;
+    }
+    total[blockIdx.x] = word;
+  }
 }
 
 template <bool kVis>
@@ -217,50 +283,102 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 // ---------------------------------------------------------------------------
 // Stage 3b: onesweep radix sort
 // ---------------------------------------------------------------------------
-constexpr int kRadixBits = 9;  // 45 key bits at 1080p: 5 passes
+// 10-bit digits: a frame's keys need only the bits that vary (see KeyMap),
+// about 39 at 1080p, so four passes.
+constexpr int kRadixBits = 10;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 8;
-// 512-lane workgroups (a lane per digit) of 4096 keys: ~66 KB of LDS, so a
-// partition finds room on a CU beside other kernels' workgroups
-constexpr int kSortWaves = 8;
+// 1024-lane workgroups of 8192 keys, one digit per lane in the per-digit
+// phase; ~134 KB of LDS, one partition per CU.  Large partitions keep the
+// number of partitions, and with it the look-back, short.
+constexpr int kSortWaves = 16;
 constexpr int kSortThreads = 64 * kSortWaves;
 constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
-static_assert(kRadix <= kSortThreads, "a sort lane per digit");
-static_assert(kRadix % 64 == 0, "digits in whole wavefronts");
+static_assert(kSortThreads == kRadix, "one digit per sort lane");
+static_assert(kPart <= 65535, "per-wave counts and local starts fit 16 bits");
 constexpr int kMaxPasses = 8;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagPrefix = 2u << 30;
 constexpr uint32_t kCountMask = (1u << 30) - 1u;
-constexpr int kLookback = 8;  // partitions examined per look-back step
+// Look-back in two levels: partitions form groups of kGroupParts; a
+// partition sums the aggregates of the earlier partitions of its group and
+// takes the group-level prefix, which the group's last partition finds by a
+// look-back over group statuses, kGroupLookback at a time.
+constexpr int kGroupParts = 16;
+constexpr int kGroupLookback = 8;
+// Most blocks of the first digit's histogram.
+constexpr int kHistBlocks = 256;
 
-// Global histogram of every pass's digit (one LDS histogram per pass).
-__global__ __launch_bounds__(256) void sort_histogram_kernel(const uint64_t* __restrict__ keys,
-                                                             const uint32_t* __restrict__ meff,
-                                                             int passes,
-                                                             uint32_t* __restrict__ hist) {
-  const uint32_t M = *meff;
-  __shared__ uint32_t s_h[kMaxPasses][kRadix];
-  for (int k = threadIdx.x; k < kMaxPasses * kRadix; k += 256) (&s_h[0][0])[k] = 0;
-  __syncthreads();
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < M; i += gridDim.x * 256u) {
-    const uint64_t key = keys[i];
-    for (int p = 0; p < passes; ++p)
-      atomicAdd(&s_h[p][(key >> (p * kRadixBits)) & (kRadix - 1)], 1u);
-  }
-  __syncthreads();
-  for (int k = threadIdx.x; k < passes * kRadix; k += 256) {
-    const uint32_t v = (&s_h[0][0])[k];
-    if (v) atomicAdd(&hist[k], v);
-  }
+// The key a pass takes its digit from: the tile id above the depth bits
+// minus the frame's smallest depth bits, in dbits bits.  Within a frame this
+// is monotone and one-to-one in the stored key (every depth lies in
+// [dmin, dmin + 2^dbits)), so sorting by it orders the stored keys; dbits =
+// 32, dmin = 0 (a NULL key map in the kernels) is the stored key itself.
+// The all-ones padding key stays all ones (last in every digit).
+struct KeyMap {
+  uint32_t dmin;
+  int dbits;
+};
+__device__ inline KeyMap load_keymap(const uint32_t* keymap) {
+  return keymap ? KeyMap{keymap[0], (int)keymap[1]} : KeyMap{0u, 32};
+}
+__device__ inline uint64_t sort_key(uint64_t k, KeyMap m) {
+  if (k == ~0ull) return ~0ull;
+  return ((k >> 32) << m.dbits) | (uint64_t)((uint32_t)k - m.dmin);
+}
+__device__ inline uint32_t sort_digit(uint64_t k, KeyMap m, int shift) {
+  return (uint32_t)(sort_key(k, m) >> shift) & (uint32_t)(kRadix - 1);
 }
 
-// hist[p][d] -> exclusive offsets, one workgroup per pass, a lane per digit.
-__global__ __launch_bounds__(kRadix) void sort_hist_scan_kernel(uint32_t* __restrict__ hist) {
-  uint32_t* h = hist + blockIdx.x * kRadix;
-  const uint64_t x = h[threadIdx.x];
+// Digit offsets of the first pass: each block histograms a contiguous share
+// of the keys in LDS and adds it to sum[] (agent-scope atomics, at most
+// kRadix per block); the last block to finish turns the totals into
+// exclusive offsets hist[].  The later passes' offsets come from the pass
+// before (sort_pass_kernel).
+constexpr int kHistThreads = 1024;
+constexpr int kHistItems = 8;
+__device__ inline void finish_digit_offsets(uint32_t* sum, uint32_t* hist) {
+  const uint32_t x = __hip_atomic_load(&sum[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint64_t excl;
   block_excl_scan_u64<kRadix / 64>(x, excl);
-  h[threadIdx.x] = (uint32_t)excl;
+  hist[threadIdx.x] = (uint32_t)excl;
+}
+
+__global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
+    const uint64_t* __restrict__ keys, const uint32_t* __restrict__ meff,
+    const uint32_t* __restrict__ keymap, uint32_t* __restrict__ sum, uint32_t* __restrict__ ctr,
+    uint32_t* __restrict__ hist) {
+  static_assert(kHistThreads == kRadix, "a lane per digit");
+  const uint32_t M = *meff;
+  const KeyMap km = load_keymap(keymap);
+  __shared__ uint32_t s_h[kRadix];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  s_h[tid] = 0u;
+  __syncthreads();
+  const uint32_t share = (uint32_t)(((uint64_t)M + gridDim.x - 1) / gridDim.x);
+  const uint32_t lo = blockIdx.x * share;
+  const uint32_t hi = (uint64_t)lo + share < (uint64_t)M ? lo + share : M;
+  for (uint32_t b = lo; b < hi; b += kHistThreads * kHistItems) {
+    uint64_t k[kHistItems];
+#pragma unroll
+    for (int it = 0; it < kHistItems; ++it) {
+      const uint32_t i = b + (uint32_t)(it * kHistThreads + tid);
+      k[it] = i < hi ? keys[i] : ~0ull;
+    }
+#pragma unroll
+    for (int it = 0; it < kHistItems; ++it)
+      if (b + (uint32_t)(it * kHistThreads + tid) < hi) atomicAdd(&s_h[sort_digit(k[it], km, 0)], 1u);
+  }
+  __syncthreads();
+  if (s_h[tid]) atomicAdd(&sum[tid], s_h[tid]);
+  // every lane's add has completed before the block counts itself done (a
+  // barrier alone does not wait for outstanding global atomics)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(ctr, 1u) == gridDim.x - 1u;
+  __syncthreads();
+  if (s_last) finish_digit_offsets(sum, hist);
 }
 
 __device__ inline uint64_t lanemask_lt() {
@@ -268,27 +386,43 @@ __device__ inline uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+#define GS_LD(p) __hip_atomic_load((p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+#define GS_ST(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+
+// One digit pass.  pstat[part][digit] holds a partition's flagged digit
+// count; gstat[group][digit] a group's flagged aggregate, then its
+// inclusive prefix.  Every wait is on a partition with a smaller ticket
+// (one that started earlier), so the passes cannot deadlock.
 __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
     uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, const uint32_t* __restrict__ meff,
-    int shift, const uint32_t* __restrict__ digit_offsets, uint32_t* __restrict__ status,
-    uint32_t* __restrict__ ticket) {
+    int shift, const uint32_t* __restrict__ keymap, const uint32_t* __restrict__ digit_offsets,
+    uint32_t* __restrict__ pstat, uint32_t* __restrict__ gstat, uint32_t* __restrict__ ticket,
+    uint32_t* __restrict__ next_sum, uint32_t* __restrict__ next_ctr,
+    uint32_t* __restrict__ next_hist) {
   const uint32_t M = *meff;
+  const KeyMap km = load_keymap(keymap);
+  const bool has_next = next_sum != nullptr;  // the next pass's offsets are built here
   __shared__ uint64_t s_keys[kPart];
   __shared__ uint32_t s_vals[kPart];
-  __shared__ uint32_t s_wh[kSortWaves][kRadix];  // per-wave digit counts, later wave offsets
-  __shared__ uint32_t s_start[kRadix];  // block-local exclusive digit start
+  __shared__ uint16_t s_wh[kSortWaves][kRadix];  // per-wave digit counts, later wave offsets
+  __shared__ uint16_t s_start[kRadix];  // block-local exclusive digit start
   __shared__ uint32_t s_gbase[kRadix];  // global base minus local start
+  __shared__ uint32_t s_next[kRadix];   // histogram of the next pass's digit
   __shared__ uint32_t s_part;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_part = atomicAdd(ticket, 1u);
-  for (int k = tid; k < kSortWaves * kRadix; k += kSortThreads) (&s_wh[0][0])[k] = 0;
+  for (int k = tid; k < kSortWaves * kRadix / 2; k += kSortThreads)
+    reinterpret_cast<uint32_t*>(&s_wh[0][0])[k] = 0u;
+  s_next[tid] = 0u;
   __syncthreads();
   const uint32_t part = s_part;
+  const uint32_t parts = (uint32_t)(((uint64_t)M + kPart - 1) / kPart);
   // a grid sized for the buffers' capacity: workgroups past the last
   // partition leave (nothing waits on a later partition)
-  if ((uint64_t)part * (uint64_t)kPart >= (uint64_t)M) return;
+  if (part >= parts) return;
   const uint32_t base = part * (uint32_t)kPart;
   const uint32_t nvalid = (M - base) < (uint32_t)kPart ? (M - base) : (uint32_t)kPart;
 
@@ -300,13 +434,14 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   for (int it = 0; it < kSortItems; ++it) {
     const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
     const bool valid = idx < M;
-    k[it] = valid ? kin[idx] : ~0ull;  // padding ranks last in digit 255
+    k[it] = valid ? kin[idx] : ~0ull;  // padding ranks last in the last digit
     v[it] = valid ? vin[idx] : 0u;
   }
+  // stable rank within the wave: keys in (item, lane) order
   const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int it = 0; it < kSortItems; ++it) {
-    const uint32_t d = (uint32_t)(k[it] >> shift) & (kRadix - 1);
+    const uint32_t d = sort_digit(k[it], km, shift);
     uint64_t match = ~0ull;
 #pragma unroll
     for (int b = 0; b < kRadixBits; ++b) {
@@ -317,69 +452,95 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     rank[it] = before + (uint32_t)__popcll(match & lt);
     const int leader = __ffsll((long long)match) - 1;
     __builtin_amdgcn_wave_barrier();
-    if (lane == leader) s_wh[wave][d] = before + (uint32_t)__popcll(match);
+    if (lane == leader) s_wh[wave][d] = (uint16_t)(before + (uint32_t)__popcll(match));
     __builtin_amdgcn_wave_barrier();
+    if (has_next && wbase + (uint32_t)it * 64u + (uint32_t)lane < M)
+      atomicAdd(&s_next[sort_digit(k[it], km, shift + kRadixBits)], 1u);
   }
   __syncthreads();
+  // this partition's share of the next pass's digit totals
+  if (has_next && s_next[tid]) atomicAdd(&next_sum[tid], s_next[tid]);
 
-  // per digit (thread = digit, the first 256 lanes): wave offsets, block
-  // count, block-local start
-  const bool dl = tid < kRadix;
-  const uint32_t d = dl ? (uint32_t)tid : 0u;
+  // lane tid takes digit tid: wave offsets, block count, block-local start
+  const int d = tid;
   uint32_t cnt = 0;
-  if (dl) {
-    for (int w = 0; w < kSortWaves; ++w) {
-      const uint32_t c = s_wh[w][d];
-      s_wh[w][d] = cnt;
-      cnt += c;
-    }
+  for (int w = 0; w < kSortWaves; ++w) {
+    const uint32_t x = s_wh[w][d];
+    s_wh[w][d] = (uint16_t)cnt;
+    cnt += x;
   }
-  uint64_t excl64;
-  block_excl_scan_u64<kSortWaves>(cnt, excl64);
-  if (dl) s_start[d] = (uint32_t)excl64;
-  const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in digit 255
+  uint64_t ex;
+  block_excl_scan_u64<kSortWaves>(cnt, ex);
+  const uint32_t start = (uint32_t)ex;
+  s_start[d] = (uint16_t)start;
+  const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in the last digit
   const uint32_t mine = (d == kRadix - 1) ? cnt - pad : cnt;
 
-  // decoupled look-back over earlier partitions, one lane per digit
-  uint32_t* st = status + (size_t)part * kRadix;
-  uint32_t prefix = 0;
-  if (!dl) {
-    // lanes past the digits take no part
-  } else if (part == 0) {
-    __hip_atomic_store(&st[d], kFlagPrefix | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    __hip_atomic_store(&st[d], kFlagAgg | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // look back kLookback partitions per step (all loads in flight at once):
-    // add aggregates up to the nearest inclusive prefix; resume at the first
-    // partition that has published nothing yet.  Partition 0 always
-    // publishes a prefix, so the walk ends there at the latest.
-    int64_t p = (int64_t)part - 1;
-    while (p >= 0) {
-      uint32_t sv[kLookback];
+  // look-back, level 1: the earlier partitions of this group (each
+  // publishes its count without waiting)
+  const uint32_t g = part / kGroupParts, r = part % kGroupParts;
+  const bool glast = r == kGroupParts - 1 || part == parts - 1;
+  GS_ST(&pstat[(size_t)part * kRadix + d], kFlagAgg | mine);
+  uint32_t sin = 0;
+  if (r > 0) {
+    const uint32_t need = (1u << r) - 1u;
+    uint32_t have = 0;  // bit q: partition g * kGroupParts + q added
+    for (;;) {
+      uint32_t sv[kGroupParts - 1];
 #pragma unroll
-      for (int j = 0; j < kLookback; ++j)
-        sv[j] = (p - j >= 0) ? __hip_atomic_load(&status[(size_t)(p - j) * kRadix + d],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : kFlagPrefix;
-      int j = 0;
-      bool done = false;
-      for (; j < kLookback; ++j) {
-        const uint32_t flag = sv[j] & ~kCountMask;
-        if (flag == 0u) break;
-        prefix += sv[j] & kCountMask;
-        if (flag == kFlagPrefix) {
-          done = true;
-          break;
+      for (int q = 0; q < kGroupParts - 1; ++q)
+        sv[q] = ((uint32_t)q < r && !((have >> q) & 1u))
+                    ? GS_LD(&pstat[(size_t)(g * kGroupParts + q) * kRadix + d])
+                    : 0u;
+#pragma unroll
+      for (int q = 0; q < kGroupParts - 1; ++q)
+        if (sv[q] & ~kCountMask) {
+          sin += sv[q] & kCountMask;
+          have |= 1u << q;
         }
-      }
-      if (done) break;
-      p -= j;
-      if (j < kLookback) __builtin_amdgcn_s_sleep(1);
+      if (have == need) break;
+      __builtin_amdgcn_s_sleep(1);
     }
-    __hip_atomic_store(&st[d], kFlagPrefix | (prefix + mine), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (dl) s_gbase[d] = digit_offsets[d] + prefix - s_start[d];
+  // level 2: the prefix of the earlier groups
+  uint32_t gp = 0;
+  if (glast) {
+    GS_ST(&gstat[(size_t)g * kRadix + d], (g == 0 ? kFlagPrefix : kFlagAgg) | (sin + mine));
+    if (g > 0) {
+      // add group aggregates back to the nearest inclusive prefix; group 0
+      // always publishes one, so the walk ends there at the latest
+      int64_t q = (int64_t)g - 1;
+      for (;;) {
+        uint32_t sv[kGroupLookback];
+#pragma unroll
+        for (int j = 0; j < kGroupLookback; ++j)
+          sv[j] = q - j >= 0 ? GS_LD(&gstat[(size_t)(q - j) * kRadix + d]) : kFlagPrefix;
+        int j = 0;
+        bool done = false;
+        for (; j < kGroupLookback; ++j) {
+          const uint32_t flag = sv[j] & ~kCountMask;
+          if (flag == 0u) break;
+          gp += sv[j] & kCountMask;
+          if (flag == kFlagPrefix) {
+            done = true;
+            break;
+          }
+        }
+        if (done) break;
+        q -= j;
+        if (j < kGroupLookback) __builtin_amdgcn_s_sleep(1);
+      }
+      GS_ST(&gstat[(size_t)g * kRadix + d], kFlagPrefix | (gp + sin + mine));
+    }
+  } else if (g > 0) {
+    // the previous group's inclusive prefix (its last partition has a
+    // smaller ticket)
+    uint32_t x;
+    while (((x = GS_LD(&gstat[(size_t)(g - 1) * kRadix + d])) & ~kCountMask) != kFlagPrefix)
+      __builtin_amdgcn_s_sleep(1);
+    gp = x & kCountMask;
+  }
+  s_gbase[d] = digit_offsets[d] + gp + sin - start;
   __syncthreads();
 
   // scatter into LDS in local sorted order
@@ -387,8 +548,8 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   for (int it = 0; it < kSortItems; ++it) {
     const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
     if (idx < M) {
-      const uint32_t dd = (uint32_t)(k[it] >> shift) & (kRadix - 1);
-      const uint32_t pos = s_start[dd] + s_wh[wave][dd] + rank[it];
+      const uint32_t dd = sort_digit(k[it], km, shift);
+      const uint32_t pos = (uint32_t)s_start[dd] + (uint32_t)s_wh[wave][dd] + rank[it];
       s_keys[pos] = k[it];
       s_vals[pos] = v[it];
     }
@@ -397,12 +558,23 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   // write out in local order: consecutive lanes hit consecutive slots of a digit run
   for (uint32_t j = (uint32_t)tid; j < nvalid; j += (uint32_t)kSortThreads) {
     const uint64_t key = s_keys[j];
-    const uint32_t dd = (uint32_t)(key >> shift) & (kRadix - 1);
+    const uint32_t dd = sort_digit(key, km, shift);
     const uint32_t out = s_gbase[dd] + j;
     kout[out] = key;
     vout[out] = s_vals[j];
   }
+  if (!has_next) return;
+  // the last partition to finish turns the next digit's totals into offsets
+  // (each lane's add to next_sum has completed before the block counts
+  // itself done)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(next_ctr, 1u) == parts - 1u;
+  __syncthreads();
+  if (s_last) finish_digit_offsets(next_sum, next_hist);
 }
+#undef GS_LD
+#undef GS_ST
 
 // ---------------------------------------------------------------------------
 // Stage 3c: per-tile [start, end) ranges of the sorted keys
@@ -424,7 +596,7 @@ __global__ __launch_bounds__(256) void ranges_kernel(const uint64_t* __restrict_
 // overflow flag.
 __global__ void bin_count_kernel(const uint64_t* __restrict__ total, uint64_t capacity,
                                  uint32_t* __restrict__ meff, uint64_t* __restrict__ counts) {
-  const uint64_t M = *total;
+  const uint64_t M = *total & kCountBits;
   const bool over = M > capacity;
   *meff = over ? 0u : (uint32_t)M;
   if (counts) {
@@ -439,6 +611,8 @@ __global__ void bin_count_kernel(const uint64_t* __restrict__ total, uint64_t ca
 struct SortPlan {
   int passes;
   uint32_t parts;
+  uint32_t groups;
+  int hblocks;  // blocks of the first digit's histogram
 };
 
 static inline int ceil_log2(uint32_t x) {
@@ -447,11 +621,16 @@ static inline int ceil_log2(uint32_t x) {
   return b;
 }
 
-static inline SortPlan sort_plan(uint64_t M, int32_t T) {
-  const int bits = 32 + ceil_log2((uint32_t)T);
+// dbits: the depth bits the frame's key map keeps (32 when unknown on the
+// host).
+static inline SortPlan sort_plan(uint64_t M, int32_t T, int dbits = 32) {
+  const int bits = dbits + ceil_log2((uint32_t)T);
   SortPlan p;
-  p.passes = (bits + kRadixBits - 1) / kRadixBits;
+  p.passes = bits > 0 ? (bits + kRadixBits - 1) / kRadixBits : 1;
   p.parts = (uint32_t)((M + kPart - 1) / kPart);
+  p.groups = (p.parts + kGroupParts - 1) / kGroupParts;
+  const uint64_t hb = (M + kHistThreads * kHistItems - 1) / (kHistThreads * kHistItems);
+  p.hblocks = hb < 1 ? 1 : (hb > (uint64_t)kHistBlocks ? kHistBlocks : (int)hb);
   return p;
 }
 
@@ -463,10 +642,15 @@ struct Workspace {
   uint64_t* scan_sums;
   uint64_t* total;
   uint32_t* meff;    // [1] instance count used by the binning kernels
-  uint32_t* hist;    // [passes][256]
-  uint32_t* ticket;  // [passes]
-  uint32_t* status;  // [passes][parts][256]
-  size_t bytes;
+  uint32_t* minmax;  // [nb][2] per scan block: smallest, largest depth bits
+  uint32_t* keymap;  // [2] the sort's key map: smallest depth bits, bits kept
+  uint32_t* hist;     // [kMaxPasses][kRadix] digit offsets
+  uint32_t* dsum;     // [kMaxPasses][kRadix] digit totals (zeroed per call)
+  uint32_t* ticket;   // [kMaxPasses] partition tickets, then [kMaxPasses]
+                      // completion counters (zeroed per call)
+  uint32_t* pstat;    // [passes][parts][kRadix] partition statuses
+  uint32_t* gstat;    // [passes][groups][kRadix] group statuses
+  size_t bytes;       // (passes, parts, groups as planned for 32 depth bits)
 };
 
 static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
@@ -485,11 +669,44 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
   w.scan_sums = (uint64_t*)take(sizeof(uint64_t) * 2 * (nb ? nb : 1));
   w.total = (uint64_t*)take(sizeof(uint64_t) * 2);
   w.meff = (uint32_t*)take(sizeof(uint32_t));
+  w.minmax = (uint32_t*)take(sizeof(uint32_t) * 2 * (nb ? nb : 1));
+  w.keymap = (uint32_t*)take(sizeof(uint32_t) * 2);
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
-  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
-  w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
+  w.dsum = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * 2 * kMaxPasses);
+  w.pstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
+  w.gstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.groups ? sp.groups : 1) * kRadix);
   w.bytes = off;
   return w;
+}
+
+// Digit offsets and the passes, ping-ponging between (ka, ia) and
+// (kb, ib); an even pass count ends in (ka, ia).  dsum and ticket must be
+// zero.
+static hipError_t launch_sort_passes(const SortPlan& sp, const uint32_t* meff,
+                                     const uint32_t* keymap, uint32_t* hist, uint32_t* dsum,
+                                     uint32_t* ticket, uint32_t* pstat, uint32_t* gstat,
+                                     uint64_t* ka, uint32_t* ia, uint64_t* kb, uint32_t* ib,
+                                     hipStream_t s) {
+  hipError_t e;
+  uint32_t* ctr = ticket + kMaxPasses;
+  hipLaunchKernelGGL(sort_first_hist_kernel, dim3((unsigned)sp.hblocks), dim3(kHistThreads), 0, s,
+                     (const uint64_t*)ka, meff, keymap, dsum, ctr, hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int p = 0; p < sp.passes; ++p) {
+    const bool next = p + 1 < sp.passes;
+    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s,
+                       (const uint64_t*)ka, (const uint32_t*)ia, kb, ib, meff, p * kRadixBits,
+                       keymap, (const uint32_t*)(hist + p * kRadix),
+                       pstat + (size_t)p * sp.parts * kRadix,
+                       gstat + (size_t)p * sp.groups * kRadix, ticket + p,
+                       next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
+                       next ? hist + (p + 1) * kRadix : nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint64_t* tk = ka; ka = kb; kb = tk;
+    uint32_t* ti = ia; ia = ib; ib = ti;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gs
@@ -498,12 +715,15 @@ extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32
   return gs::carve(nullptr, N, capacity, T).bytes;
 }
 
-// Scan; writes offsets and M to totals_host[0] (one synchronising read).
-// With vis_ids non-NULL also the ascending indices of the Gaussians with
-// tiles, and their count V to totals_host[1], in the same read.
-extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t* offsets,
-                                     uint32_t* vis_ids, void* workspace, uint64_t capacity,
-                                     int32_t T, uint64_t* totals_host, hipStream_t s) {
+// Scan; writes offsets and M to totals_host[0] (one synchronising read),
+// and the depth bits the sort's key map keeps to *dbits.  With vis_ids
+// non-NULL also the ascending indices of the Gaussians with tiles, and their
+// count V to totals_host[1], in the same read.  totals_host NULL: the counts
+// and the key map stay on the device (dbits is not written).
+extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
+                                     uint32_t* offsets, uint32_t* vis_ids, void* workspace,
+                                     uint64_t capacity, int32_t T, uint64_t* totals_host,
+                                     int* dbits, hipStream_t s) {
   using namespace gs;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
@@ -512,23 +732,24 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
     if (totals_host) {
       totals_host[0] = 0;
       if (vis) totals_host[1] = 0;
+      *dbits = 0;
       return hipSuccess;
     }
-    // the device count must still read 0
+    // the device count must still read 0 (and the key map be defined)
     hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, w.scan_sums, (int64_t)0,
-                       w.total);
+                       w.minmax, w.total, w.keymap);
     return hipGetLastError();
   }
   const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
   if (vis)
-    hipLaunchKernelGGL(scan_reduce_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
-                       w.scan_sums);
+    hipLaunchKernelGGL(scan_reduce_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles,
+                       depths, N, w.scan_sums, w.minmax);
   else
-    hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
-                       w.scan_sums);
+    hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles,
+                       depths, N, w.scan_sums, w.minmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_partials_kernel, dim3(vis ? 2 : 1), dim3(256), 0, s, w.scan_sums, nb,
-                     w.total);
+                     w.minmax, w.total, w.keymap);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (vis)
     hipLaunchKernelGGL(scan_down_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
@@ -543,20 +764,24 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, uint32_t*
   if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
                           hipMemcpyDeviceToHost, s)) != hipSuccess)
     return e;
-  return hipStreamSynchronize(s);
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  *dbits = (int)(totals_host[0] >> kDbitsShift);
+  totals_host[0] &= kCountBits;
+  return hipSuccess;
 }
 
 // Duplicate, sort and extract ranges for M instances (M <= capacity).
 // ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
-// M: the instance count read back by the caller, or, with device_count,
-// unknown on the host: the kernels then take it from the scan on the device,
-// grids are sized for `capacity`, and counts (device, optional) receives M
-// and an overflow flag (M > capacity leaves an empty list).
+// M, dbits: the instance count and the key map's depth bits read back by the
+// caller, or, with device_count, unknown on the host: the kernels then take
+// M from the scan on the device, grids are sized for `capacity`, the passes
+// cover 32 depth bits, and counts (device, optional) receives M and an
+// overflow flag (M > capacity leaves an empty list).
 extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                                 const int32_t* radii, const float* depths,
                                                 const uint32_t* tiles, const uint32_t* offsets,
                                                 int32_t W, int32_t H, int ncams, uint64_t M,
-                                                bool device_count, uint64_t* counts,
+                                                int dbits, bool device_count, uint64_t* counts,
                                                 uint64_t* keys, uint32_t* ids, uint32_t* ranges,
                                                 void* workspace, uint64_t capacity, hipStream_t s) {
   using namespace gs;
@@ -567,12 +792,13 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   if (!device_count && M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   // grids for M, or for the largest count the buffers hold
   const uint64_t Mg = device_count ? capacity : M;
-  const SortPlan sp = sort_plan(Mg, T);
+  const SortPlan sp = sort_plan(Mg, T, device_count ? 32 : dbits);
   {
-    Segs sg = {{ranges, w.hist, w.ticket, w.status},
-               {2 * (int64_t)T, (int64_t)kMaxPasses * kRadix, kMaxPasses,
-                (int64_t)sp.passes * sp.parts * kRadix}};
-    int64_t big = sg.n[0] > sg.n[3] ? sg.n[0] : sg.n[3];
+    // dsum follows hist, ticket follows dsum: one segment of hist .. ticket
+    Segs sg = {{ranges, w.dsum, w.pstat, w.gstat},
+               {2 * (int64_t)T, (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
+                (int64_t)sp.passes * sp.parts * kRadix, (int64_t)sp.passes * sp.groups * kRadix}};
+    int64_t big = sg.n[0] > sg.n[2] ? sg.n[0] : sg.n[2];
     int64_t blocks = (big + 255) / 256;
     if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
@@ -593,21 +819,9 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
                      depths, tiles, offsets, gx, gy, ncams > 1, w.meff, ka, ia);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  unsigned hblocks = (unsigned)((Mg + 256 * 16 - 1) / (256 * 16));
-  if (hblocks > 1024) hblocks = 1024;
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, sp.passes,
-                     w.hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(sp.passes), dim3(kRadix), 0, s, w.hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int p = 0; p < sp.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
-                       w.meff, p * kRadixBits, w.hist + p * kRadix,
-                       w.status + (size_t)p * sp.parts * kRadix, w.ticket + p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint64_t* tk = ka; ka = kb; kb = tk;
-    uint32_t* ti = ia; ia = ib; ib = ti;
-  }
+  if ((e = launch_sort_passes(sp, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum, w.ticket,
+                               w.pstat, w.gstat, ka, ia, kb, ib, s)) != hipSuccess)
+    return e;
   const unsigned rblocks = (unsigned)((Mg + 255) / 256);
   hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, w.meff, (uint32_t)T,
                      ranges);
@@ -625,17 +839,17 @@ struct PairSortWs {
   uint32_t* vals_alt;
   uint32_t* meff;
   uint32_t* hist;
+  uint32_t* dsum;
   uint32_t* ticket;
-  uint32_t* status;
-  int passes;
-  uint32_t parts;
+  uint32_t* pstat;
+  uint32_t* gstat;
+  SortPlan sp;
   size_t bytes;
 };
 
 static PairSortWs carve_pairsort(void* base, uint64_t n, int bits) {
   PairSortWs w;
-  w.passes = (bits + kRadixBits - 1) / kRadixBits;
-  w.parts = (uint32_t)((n + kPart - 1) / kPart);
+  w.sp = sort_plan(n, 1, bits);
   char* p = (char*)base;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -647,8 +861,12 @@ static PairSortWs carve_pairsort(void* base, uint64_t n, int bits) {
   w.vals_alt = (uint32_t*)take(sizeof(uint32_t) * (n ? n : 1));
   w.meff = (uint32_t*)take(sizeof(uint32_t));
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
-  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
-  w.status = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.passes * (w.parts ? w.parts : 1) * kRadix);
+  w.dsum = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * 2 * kMaxPasses);
+  w.pstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.sp.passes * (w.sp.parts ? w.sp.parts : 1) *
+                            kRadix);
+  w.gstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.sp.passes * (w.sp.groups ? w.sp.groups : 1) *
+                            kRadix);
   w.bytes = off;
   return w;
 }
@@ -667,10 +885,11 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   PairSortWs w = carve_pairsort(workspace, n, bits);
   hipError_t e;
   {
-    Segs sg = {{w.hist, w.ticket, w.status, w.status},
-               {(int64_t)kMaxPasses * kRadix, kMaxPasses,
-                (int64_t)w.passes * w.parts * kRadix, 0}};
-    int64_t blocks = (sg.n[2] + 255) / 256;
+    Segs sg = {{w.dsum, w.pstat, w.gstat, w.gstat},
+               {(int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
+                (int64_t)w.sp.passes * w.sp.parts * kRadix,
+                (int64_t)w.sp.passes * w.sp.groups * kRadix, 0}};
+    int64_t blocks = (sg.n[1] + 255) / 256;
     if (blocks > 2048) blocks = 2048;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
@@ -682,7 +901,7 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   uint32_t* ia = vals;
   uint64_t* kb = w.keys_alt;
   uint32_t* ib = w.vals_alt;
-  if (w.passes & 1) {
+  if (w.sp.passes & 1) {
     if ((e = hipMemcpyAsync(w.keys_alt, keys, n * sizeof(uint64_t), hipMemcpyDeviceToDevice, s)) !=
         hipSuccess)
       return e;
@@ -692,22 +911,8 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
     ka = w.keys_alt; ia = w.vals_alt; kb = keys; ib = vals;
   }
   if ((e = fill_u32(w.meff, 1, (uint32_t)n, s)) != hipSuccess) return e;
-  unsigned hblocks = (unsigned)((n + 256 * 16 - 1) / (256 * 16));
-  if (hblocks > 1024) hblocks = 1024;
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3(hblocks), dim3(256), 0, s, ka, w.meff, w.passes,
-                     w.hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sort_hist_scan_kernel, dim3(w.passes), dim3(kRadix), 0, s, w.hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int p = 0; p < w.passes; ++p) {
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(w.parts), dim3(kSortThreads), 0, s, ka, ia, kb, ib,
-                       w.meff, p * kRadixBits, w.hist + p * kRadix,
-                       w.status + (size_t)p * w.parts * kRadix, w.ticket + p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    uint64_t* tk = ka; ka = kb; kb = tk;
-    uint32_t* ti = ia; ia = ib; ib = ti;
-  }
-  return hipSuccess;
+  return launch_sort_passes(w.sp, w.meff, nullptr, w.hist, w.dsum, w.ticket, w.pstat, w.gstat,
+                            ka, ia, kb, ib, s);
 }
 
 extern "C" size_t gs_scan_workspace_bytes(int64_t n) {
@@ -722,14 +927,16 @@ extern "C" hipError_t gs_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, 
   hipError_t e;
   if (n == 0) {
     hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, (uint64_t*)workspace,
-                       (int64_t)0, total);
+                       (int64_t)0, (const uint32_t*)nullptr, total, (uint32_t*)nullptr);
     return hipGetLastError();
   }
   uint64_t* sums = (uint64_t*)workspace;
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
-  hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums);
+  hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in,
+                     (const float*)nullptr, n, sums, (uint32_t*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, sums, nb, total);
+  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, sums, nb,
+                     (const uint32_t*)nullptr, total, (uint32_t*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums,
                      out, nullptr);
