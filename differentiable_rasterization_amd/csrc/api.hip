@@ -31,14 +31,14 @@ hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
 hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
                           uint32_t* offsets, uint32_t* vis_ids, void* workspace, uint64_t capacity,
-                          int32_t T, uint64_t* totals_host, int* dbits, hipStream_t s);
+                          int32_t T, uint64_t* totals_host, int* dbits, uint64_t* dev_counts,
+                          hipStream_t s);
 hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                      const int32_t* radii, const float* depths,
                                      const uint32_t* tiles, const uint32_t* offsets, int32_t W,
                                      int32_t H, int ncams, uint64_t M, int dbits, bool device_count,
-                                     uint64_t* counts, uint64_t* keys, uint32_t* ids,
-                                     uint32_t* ranges, void* workspace, uint64_t capacity,
-                                     hipStream_t s);
+                                     uint64_t* keys, uint32_t* ids, uint32_t* ranges,
+                                     void* workspace, uint64_t capacity, hipStream_t s);
 hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
                                 uint32_t* order, hipStream_t s);
 hipError_t gs_launch_pack_splats(int64_t rows, int64_t ld, const float* means2d,
@@ -170,7 +170,7 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
   const int32_t T = gs_num_tiles(width, height);
   int dbits = 32;
   gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
-                                           capacity, T, num_instances, &dbits, s),
+                                           capacity, T, num_instances, &dbits, nullptr, s),
                             name);
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -182,8 +182,8 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, dbits, false, nullptr,
-                                              keys, ids, tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, 1, M, dbits, false, keys,
+                                              ids, tile_ranges, workspace, capacity, s),
                     name);
 }
 
@@ -426,12 +426,12 @@ gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
   gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
-                                           capacity, T, nullptr, nullptr, s),
+                                           capacity, T, nullptr, nullptr, counts, s),
                             "gs_bin_and_sort_device(scan)");
   if (st != GS_OK) return st;
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, 0, 32, true, counts,
-                                              keys, ids, tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, 1, 0, 32, true, keys, ids,
+                                              tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_device");
 }
 
@@ -584,7 +584,7 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
   hipStream_t s = (hipStream_t)stream;
   int dbits = 32;
   gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, vis_ids, workspace,
-                                           capacity, T, counts, &dbits, s),
+                                           capacity, T, counts, &dbits, nullptr, s),
                             "gs_bin_and_sort_packed(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = counts[0];
@@ -596,8 +596,8 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
     return GS_ERR_CAPACITY;
   }
   return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, dbits, false, nullptr,
-                                              keys, ids, tile_ranges, workspace, capacity, s),
+                                              offsets, width, height, 1, M, dbits, false, keys,
+                                              ids, tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_packed");
 }
 
@@ -735,7 +735,7 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
   int dbits = 32;
   gs_status st = hip_status(gs_launch_scan(rows, tiles_touched, depths, offsets, nullptr,
                                            workspace, capacity, (int32_t)T, num_instances, &dbits,
-                                           s),
+                                           nullptr, s),
                             "gs_bin_and_sort_batched(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -748,8 +748,7 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
   }
   return hip_status(gs_launch_dup_sort_ranges(rows, ld, means2d, radii, depths, tiles_touched,
                                               offsets, width, height, num_cams, M, dbits, false,
-                                              nullptr, keys, ids, tile_ranges, workspace, capacity,
-                                              s),
+                                              keys, ids, tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_batched");
 }
 

@@ -94,6 +94,10 @@ __device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
 // order to vis_ids; its per-block sums follow the first set at sums + nb.
 // ---------------------------------------------------------------------------
 constexpr int kScanItems = 8;
+// sort shapes the duplication's zeroing needs (see the sort below)
+constexpr int kDigits = 1024;          // radix of a sort pass
+constexpr int kPartKeys = 8192;        // keys per sort partition
+constexpr int kGroupPartitions = 16;   // partitions per look-back group
 constexpr int kDbitsShift = 58;
 constexpr uint64_t kCountBits = (1ull << kDbitsShift) - 1ull;
 constexpr int kScanBlock = 256 * kScanItems;
@@ -163,11 +167,18 @@ __global__ __launch_bounds__(256) void scan_reduce_kernel(const uint32_t* __rest
 // needs) and puts that bit count above the total, in total[0] bits 58-63,
 // so that the host reads it with M.  (M < 2^54: fewer than 2^31 rows, each
 // touching fewer than 2^23 tiles.)
+//
+// With meff, the first also writes the instance count the binning kernels
+// use: M when it fits `capacity`, else 0 (an empty list); counts (optional)
+// receives M and the overflow flag.
 __global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict__ sums,
                                                             int64_t nb,
                                                             const uint32_t* __restrict__ minmax,
                                                             uint64_t* __restrict__ total,
-                                                            uint32_t* __restrict__ keymap) {
+                                                            uint32_t* __restrict__ keymap,
+                                                            uint64_t capacity,
+                                                            uint32_t* __restrict__ meff,
+                                                            uint64_t* __restrict__ counts) {
   sums += (int64_t)blockIdx.x * nb;
   uint64_t carry = 0;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -192,6 +203,14 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(uint64_t* __restrict
       keymap[0] = lo <= hi ? lo : 0u;
       keymap[1] = dbits;
       word |= (uint64_t)dbits << kDbitsShift;
+    }
+    if (blockIdx.x == 0 && meff) {
+      const bool over = carry > capacity;
+      *meff = over ? 0u : (uint32_t)carry;
+      if (counts) {
+        counts[0] = carry;
+        counts[1] = over ? 1ull : 0ull;
+      }
     }
     total[blockIdx.x] = word;
   }
@@ -233,12 +252,47 @@ __global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restri
 // A batch of cameras is one list of C * ld rows: row c * ld + i is Gaussian
 // i seen by camera c, whose means2d are [c][2][ld] and whose tiles are
 // numbered from c * T (batched = true).
+// What the sort and the ranges need zeroed before they run: the ranges, the
+// digit totals and counters, and for each of `passes` passes (laid out for
+// `parts` partitions and `groups` groups) the statuses of the partitions and
+// groups the instance count actually uses.
+struct SortZero {
+  uint32_t* ranges;
+  int64_t nranges;
+  uint32_t* small;
+  int64_t nsmall;
+  uint32_t* pstat;
+  uint32_t* gstat;
+  uint32_t parts, groups;
+  int passes;
+};
+__device__ inline void zero_span(uint32_t* p, int64_t n, int64_t first, int64_t stride) {
+  for (int64_t i = first; i < n; i += stride) p[i] = 0u;
+}
+
+// Every block first takes its share of the zeroing (the grid may be larger
+// than the rows need), then duplicates its 256 rows.
 __global__ __launch_bounds__(256) void duplicate_kernel(
     int64_t N, const float* __restrict__ means2d, int64_t ld, const int32_t* __restrict__ radii,
     const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
     const uint32_t* __restrict__ offsets, int gx, int gy, bool batched,
-    const uint32_t* __restrict__ meff, uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
-  if (*meff == 0u) return;  // no instances, or more than the buffers hold
+    const uint32_t* __restrict__ meff, SortZero z, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ ids) {
+  const uint32_t Meff = *meff;
+  {
+    const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    zero_span(z.ranges, z.nranges, first, stride);
+    zero_span(z.small, z.nsmall, first, stride);
+    const uint32_t parts = (uint32_t)(((uint64_t)Meff + kPartKeys - 1) / kPartKeys);
+    const uint32_t groups = (parts + kGroupPartitions - 1) / kGroupPartitions;
+    for (int p = 0; p < z.passes; ++p) {
+      zero_span(z.pstat + (size_t)p * z.parts * kDigits, (int64_t)parts * kDigits, first, stride);
+      zero_span(z.gstat + (size_t)p * z.groups * kDigits, (int64_t)groups * kDigits, first,
+                stride);
+    }
+  }
+  if (Meff == 0u || (int64_t)blockIdx.x * 256 >= N) return;  // no instances, or too many
   __shared__ uint32_t s_off[257];
   __shared__ int32_t s_x0[256], s_w[256], s_y0[256];
   __shared__ uint32_t s_db[256], s_tb[256];
@@ -306,6 +360,8 @@ constexpr uint32_t kCountMask = (1u << 30) - 1u;
 // look-back over group statuses, kGroupLookback at a time.
 constexpr int kGroupParts = 16;
 constexpr int kGroupLookback = 8;
+static_assert(kDigits == kRadix && kPartKeys == kPart && kGroupPartitions == kGroupParts,
+              "the duplication zeroes what the sort uses");
 // Most blocks of the first digit's histogram.
 constexpr int kHistBlocks = 256;
 
@@ -591,20 +647,6 @@ __global__ __launch_bounds__(256) void ranges_kernel(const uint64_t* __restrict_
   if (m == M - 1 || (uint32_t)(keys[m + 1] >> 32) != tile) ranges[2 * tile + 1] = m + 1;
 }
 
-// The instance count the binning kernels use: M when it fits the buffers,
-// else 0 (an empty list).  counts (device, optional) receives M and the
-// overflow flag.
-__global__ void bin_count_kernel(const uint64_t* __restrict__ total, uint64_t capacity,
-                                 uint32_t* __restrict__ meff, uint64_t* __restrict__ counts) {
-  const uint64_t M = *total & kCountBits;
-  const bool over = M > capacity;
-  *meff = over ? 0u : (uint32_t)M;
-  if (counts) {
-    counts[0] = M;
-    counts[1] = over ? 1ull : 0ull;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Workspace layout
 // ---------------------------------------------------------------------------
@@ -719,11 +761,12 @@ extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32
 // and the depth bits the sort's key map keeps to *dbits.  With vis_ids
 // non-NULL also the ascending indices of the Gaussians with tiles, and their
 // count V to totals_host[1], in the same read.  totals_host NULL: the counts
-// and the key map stay on the device (dbits is not written).
+// and the key map stay on the device (dbits is not written), and
+// dev_counts (device, optional) receives M and the overflow flag.
 extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
                                      uint32_t* offsets, uint32_t* vis_ids, void* workspace,
                                      uint64_t capacity, int32_t T, uint64_t* totals_host,
-                                     int* dbits, hipStream_t s) {
+                                     int* dbits, uint64_t* dev_counts, hipStream_t s) {
   using namespace gs;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
@@ -737,7 +780,7 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const flo
     }
     // the device count must still read 0 (and the key map be defined)
     hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, w.scan_sums, (int64_t)0,
-                       w.minmax, w.total, w.keymap);
+                       w.minmax, w.total, w.keymap, capacity, w.meff, dev_counts);
     return hipGetLastError();
   }
   const int64_t nb = (N + kScanBlock - 1) / kScanBlock;
@@ -749,7 +792,8 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const flo
                        depths, N, w.scan_sums, w.minmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_partials_kernel, dim3(vis ? 2 : 1), dim3(256), 0, s, w.scan_sums, nb,
-                     w.minmax, w.total, w.keymap);
+                     w.minmax, w.total, w.keymap, capacity, w.meff,
+                     totals_host ? nullptr : dev_counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (vis)
     hipLaunchKernelGGL(scan_down_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
@@ -774,16 +818,15 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const flo
 // ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
 // M, dbits: the instance count and the key map's depth bits read back by the
 // caller, or, with device_count, unknown on the host: the kernels then take
-// M from the scan on the device, grids are sized for `capacity`, the passes
-// cover 32 depth bits, and counts (device, optional) receives M and an
-// overflow flag (M > capacity leaves an empty list).
+// M from the scan on the device (0 when it exceeded `capacity`), grids are
+// sized for `capacity` and the passes cover 32 depth bits.
 extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
                                                 const int32_t* radii, const float* depths,
                                                 const uint32_t* tiles, const uint32_t* offsets,
                                                 int32_t W, int32_t H, int ncams, uint64_t M,
-                                                int dbits, bool device_count, uint64_t* counts,
-                                                uint64_t* keys, uint32_t* ids, uint32_t* ranges,
-                                                void* workspace, uint64_t capacity, hipStream_t s) {
+                                                int dbits, bool device_count, uint64_t* keys,
+                                                uint32_t* ids, uint32_t* ranges, void* workspace,
+                                                uint64_t capacity, hipStream_t s) {
   using namespace gs;
   const int gx = grid_dim(W), gy = grid_dim(H);
   const int32_t T = gx * gy * ncams;
@@ -792,31 +835,24 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   if (!device_count && M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   // grids for M, or for the largest count the buffers hold
   const uint64_t Mg = device_count ? capacity : M;
+  if (Mg == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   const SortPlan sp = sort_plan(Mg, T, device_count ? 32 : dbits);
-  {
-    // dsum follows hist, ticket follows dsum: one segment of hist .. ticket
-    Segs sg = {{ranges, w.dsum, w.pstat, w.gstat},
-               {2 * (int64_t)T, (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
-                (int64_t)sp.passes * sp.parts * kRadix, (int64_t)sp.passes * sp.groups * kRadix}};
-    int64_t big = sg.n[0] > sg.n[2] ? sg.n[0] : sg.n[2];
-    int64_t blocks = (big + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(zero_segs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sg);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(bin_count_kernel, dim3(1), dim3(1), 0, s, w.total, capacity, w.meff,
-                     device_count ? counts : nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (Mg == 0) return hipSuccess;
+  // dsum follows hist, ticket follows dsum: one span from dsum to the counters
+  const SortZero z = {ranges, 2 * (int64_t)T, w.dsum, (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
+                      w.pstat, w.gstat, sp.parts, sp.groups, sp.passes};
   // land the final pass in (keys, ids): start from the alternate buffer when
   // the pass count is odd
   uint64_t* ka = (sp.passes & 1) ? w.keys_alt : keys;
   uint32_t* ia = (sp.passes & 1) ? w.ids_alt : ids;
   uint64_t* kb = (sp.passes & 1) ? keys : w.keys_alt;
   uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
-  const int64_t nblk = (N + 255) / 256;
+  // enough blocks for the rows and for a few zeroing strides
+  int64_t nblk = (N + 255) / 256;
+  const int64_t zblk = (2 * (int64_t)T + (int64_t)sp.parts * kRadix + 4095) / 4096;
+  if (nblk < zblk) nblk = zblk;
+  if (nblk < 1) nblk = 1;
   hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
-                     depths, tiles, offsets, gx, gy, ncams > 1, w.meff, ka, ia);
+                     depths, tiles, offsets, gx, gy, ncams > 1, (const uint32_t*)w.meff, z, ka, ia);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if ((e = launch_sort_passes(sp, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum, w.ticket,
@@ -927,7 +963,8 @@ extern "C" hipError_t gs_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, 
   hipError_t e;
   if (n == 0) {
     hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, (uint64_t*)workspace,
-                       (int64_t)0, (const uint32_t*)nullptr, total, (uint32_t*)nullptr);
+                       (int64_t)0, (const uint32_t*)nullptr, total, (uint32_t*)nullptr,
+                       (uint64_t)0, (uint32_t*)nullptr, (uint64_t*)nullptr);
     return hipGetLastError();
   }
   uint64_t* sums = (uint64_t*)workspace;
@@ -936,7 +973,8 @@ extern "C" hipError_t gs_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, 
                      (const float*)nullptr, n, sums, (uint32_t*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(256), 0, s, sums, nb,
-                     (const uint32_t*)nullptr, total, (uint32_t*)nullptr);
+                     (const uint32_t*)nullptr, total, (uint32_t*)nullptr, (uint64_t)0,
+                     (uint32_t*)nullptr, (uint64_t*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, in, n, sums,
                      out, nullptr);
