@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
     uint8_t list[4][256];
     uint32_t cnt[4];
     uint32_t wc[4][4];
-    uint32_t maxlast;
+    uint32_t wlast[4];  // per wavefront: the largest last index of its pixels
   };
   __shared__ Lds lds;
   SplatLds* s_sp = lds.sp;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   auto& s_list = lds.list;
   uint32_t* s_cnt = lds.cnt;
   auto& s_wc = lds.wc;
-  uint32_t& s_maxlast = lds.maxlast;
+  uint32_t* s_wlast = lds.wlast;
   int tx, ty;
   const int gy = grid_dim(H);
   if (!schedule_tile(order, gx, gy, tx, ty)) return;
@@ -596,13 +596,14 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
   // S = sum_c dL/dC_c R_c, with R the colour accumulated behind the current
   // splat, background included
   float S = T * fmaf(g0, bg0, fmaf(g1, bg1, g2 * bg2));
-  if (tid == 0) s_maxlast = 0;
+  if (tid < 4) s_wlast[tid] = 0;
   __syncthreads();
-  if (last) atomicMax(&s_maxlast, last);
+  if (last) atomicMax(&s_wlast[wave], last);
   __syncthreads();
+  const uint32_t maxlast = max(max(s_wlast[0], s_wlast[1]), max(s_wlast[2], s_wlast[3]));
   // nothing at or after `stop` is blended; last indices beyond the tile's
   // list (inputs that do not belong together) give the tile zero gradients
-  const uint32_t stop = (s_maxlast > end - start) ? start : start + s_maxlast;
+  const uint32_t stop = (maxlast > end - start) ? start : start + maxlast;
   uint32_t n_eval = 0, n_hit = 0, n_red = 0;  // counters (kStats only)
 
   // entries no pixel of the tile blends: their instance slots get zeros
@@ -640,6 +641,12 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const float4 d = splats[4 * (size_t)my_id + 3];
       cA = d.x; cB = d.y; cC = d.z;
       mask = quad_mask(s_sp[tid], ex, ey, tx * kTile, ty * kTile);
+      // a wavefront whose pixels all stopped in front of this entry (list
+      // position rel) skips it
+      const uint32_t rel = b_end - 1u - start - (uint32_t)tid;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (rel >= s_wlast[q]) mask &= ~(1u << q);
     }
     constexpr int kF = kAbs ? kFieldsAbs : kFields;
 #pragma unroll
