@@ -343,7 +343,7 @@ constexpr int kRadixBits = 10;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 8;
 // 1024-lane workgroups of 8192 keys, one digit per lane in the per-digit
-// phase; ~134 KB of LDS, one partition per CU.  Large partitions keep the
+// phase; ~76 KB of LDS (see sort_pass_kernel).  Large partitions keep the
 // number of partitions, and with it the look-back, short.
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = 64 * kSortWaves;
@@ -459,9 +459,13 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   const uint32_t M = *meff;
   const KeyMap km = load_keymap(keymap);
   const bool has_next = next_sum != nullptr;  // the next pass's offsets are built here
-  __shared__ uint64_t s_keys[kPart];
-  __shared__ uint32_t s_vals[kPart];
-  __shared__ uint16_t s_wh[kSortWaves][kRadix];  // per-wave digit counts, later wave offsets
+  // One 64 KB buffer in three roles, one after another: the per-wave digit
+  // counts (then offsets) while ranking, the keys in local sorted order,
+  // then the values.  ~74 KB of LDS in all, so two partitions fit on a CU,
+  // or one beside other kernels' workgroups.
+  __shared__ uint64_t s_buf[kPart];
+  uint16_t(*s_wh)[kRadix] = reinterpret_cast<uint16_t(*)[kRadix]>(s_buf);
+  uint32_t* s_vals = reinterpret_cast<uint32_t*>(s_buf);
   __shared__ uint16_t s_start[kRadix];  // block-local exclusive digit start
   __shared__ uint32_t s_gbase[kRadix];  // global base minus local start
   __shared__ uint32_t s_next[kRadix];   // histogram of the next pass's digit
@@ -531,6 +535,14 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   s_start[d] = (uint16_t)start;
   const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in the last digit
   const uint32_t mine = (d == kRadix - 1) ? cnt - pad : cnt;
+  __syncthreads();
+  // each key's position in local sorted order (the counts' buffer is free
+  // after this)
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it) {
+    const uint32_t dd = sort_digit(k[it], km, shift);
+    rank[it] += (uint32_t)s_start[dd] + (uint32_t)s_wh[wave][dd];
+  }
 
   // look-back, level 1: the earlier partitions of this group (each
   // publishes its count without waiting)
@@ -599,25 +611,32 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   s_gbase[d] = digit_offsets[d] + gp + sin - start;
   __syncthreads();
 
-  // scatter into LDS in local sorted order
+  // keys, then values, through LDS in local sorted order; written out in
+  // that order, consecutive lanes hit consecutive slots of a digit run
 #pragma unroll
-  for (int it = 0; it < kSortItems; ++it) {
-    const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
-    if (idx < M) {
-      const uint32_t dd = sort_digit(k[it], km, shift);
-      const uint32_t pos = (uint32_t)s_start[dd] + (uint32_t)s_wh[wave][dd] + rank[it];
-      s_keys[pos] = k[it];
-      s_vals[pos] = v[it];
+  for (int it = 0; it < kSortItems; ++it)
+    if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_buf[rank[it]] = k[it];
+  __syncthreads();
+  uint32_t outj[kSortItems];
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
+    if (j < nvalid) {
+      const uint64_t key = s_buf[j];
+      const uint32_t out = s_gbase[sort_digit(key, km, shift)] + j;
+      kout[out] = key;
+      outj[i] = out;
     }
   }
   __syncthreads();
-  // write out in local order: consecutive lanes hit consecutive slots of a digit run
-  for (uint32_t j = (uint32_t)tid; j < nvalid; j += (uint32_t)kSortThreads) {
-    const uint64_t key = s_keys[j];
-    const uint32_t dd = sort_digit(key, km, shift);
-    const uint32_t out = s_gbase[dd] + j;
-    kout[out] = key;
-    vout[out] = s_vals[j];
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it)
+    if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_vals[rank[it]] = v[it];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
+    if (j < nvalid) vout[outj[i]] = s_vals[j];
   }
   if (!has_next) return;
   // the last partition to finish turns the next digit's totals into offsets
