@@ -383,6 +383,8 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     }
     const uint32_t jn = j + 256u;
     uint32_t next_id = jn < end ? ids[jn] : 0u;
+    // zero lists: past the end of its block's list a row reads slot 0
+    for (int q = tid; q < 16 * 260 / 4; q += 256) reinterpret_cast<uint32_t*>(&s_list[0][0])[q] = 0u;
     compact_bands<16, 260>(mask, s_list, s_cnt, s_wc);
     // (an empty asm that takes the index: its first use stays here, after
     // the compaction, so the wait for the index load is not hoisted above it)
@@ -397,16 +399,18 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
     const uint32_t base = b - start + 1u;
     if (__ballot(!done) == 0ull) continue;
     for (int i = 0; i < cnt; ++i) {
-      // past the end of this row's list the lane evaluates slot 0, a record
-      // of this batch, and ignores it (a stale slot could hold a non-finite
-      // record, and 0 * NaN would reach the sums)
+      // past the end of this row's list the lane reads slot 0 (the lists'
+      // zeroed tail), a record of this batch, and ignores it (a stale slot
+      // could hold a non-finite record, and 0 * NaN would reach the sums)
       const bool act = i < my_cnt;
-      const int k = act ? (int)s_list[sb][i] : 0;
+      const int k = (int)s_list[sb][i];
       const SplatLds& s = s_sp[k];
       const float dx = fpx - s.u, dy = fpy - s.v;
       const float p2 = splat_power2(s, dx, dy);
       const float oG = s.o * __builtin_amdgcn_exp2f(p2);
-      const float alpha = oG > amax ? amax : oG;
+      // the backward's choice (oG > amax ? amax : oG) for every finite oG; a
+      // non-finite oG belongs to a lane that ignores it
+      const float alpha = fminf(oG, amax);
       const bool ok = act & !done & !(alpha < amin);
       const float Tn = T * (1.0f - alpha);
       const bool low = Tn < Tmin;
