@@ -526,11 +526,11 @@ __device__ inline void reduce_add(const float* f, float* dst, int stride) {
 }
 
 // Gradient slots of one splat, in moment form: w dx, w dy, w dx^2, w dx dy,
-// w dy^2 with w = -2 dL/dq = alpha dL/dalpha, then dL/do and the three
-// colour gradients.  The mean and conic gradients follow after the
-// reduction (S the sums of the w moments):
+// w dy^2 with w = -2 dL/dq = alpha dL/dalpha, then w itself and the three
+// colour gradients.  The mean, conic and opacity gradients follow after the
+// reduction (S the sums of the w moments, Sw the sum of w):
 //   dL/du = A Sx + B Sy, dL/dv = B Sx + C Sy,
-//   dL/dA = -Sxx / 2, dL/dB = -Sxy, dL/dC = -Syy / 2.
+//   dL/dA = -Sxx / 2, dL/dB = -Sxy, dL/dC = -Syy / 2, dL/do = Sw / o.
 // With absgrad, two more: the per-pixel |dL/du| and |dL/dv| summed over the
 // pixels (the absolute-gradient statistic of densification).
 constexpr int kFields = 9;
@@ -671,11 +671,16 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const float G = __builtin_amdgcn_exp2f(p2);
       const float oG = s.o * G;
       const bool clamped = oG > amax;
-      const float alpha = clamped ? amax : oG;
+      // the forward's alpha for every finite oG (a non-finite one belongs to
+      // no evaluated list entry: its footprint mask is empty)
+      const float alpha = fminf(oG, amax);
       const bool hit = (k > kthr) & !(alpha < amin);
-      const float rom = __builtin_amdgcn_rcpf(1.0f - alpha);
-      T = hit ? T * rom : T;  // transmittance in front of this splat
-      const float wgt = hit ? alpha * T : 0.0f;
+      // a lane that does not blend this splat takes alpha 0: its T is
+      // multiplied by 1/(1 - 0) = 1 exactly and its weight is 0
+      const float ah = hit ? alpha : 0.0f;
+      const float rom = __builtin_amdgcn_rcpf(1.0f - ah);
+      T = T * rom;  // transmittance in front of this splat
+      const float wgt = ah * T;
       float f[kF];
       f[6] = g0 * wgt;
       f[7] = g1 * wgt;
@@ -687,9 +692,10 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       S = fmaf(gc, wgt, S);
       const bool geo = hit & !clamped;
       // q = A dx^2 + 2B dx dy + C dy^2, alpha = o exp(-q/2): dL/dq = -alpha/2
-      // dL/dalpha = -w/2; dL/do = G dL/dalpha = w / o (s.z holds 1/o)
+      // dL/dalpha = -w/2; dL/do = G dL/dalpha = w / o, summed as w and
+      // divided by o once per splat
       const float m = geo ? alpha * dLda : 0.0f;
-      f[5] = m * s.z;
+      f[5] = m;
       const float mx = m * dx, my = m * dy;
       f[0] = mx;
       f[1] = my;
@@ -754,7 +760,8 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
           instance_slot(s_sp[tid].u, s_sp[tid].v, my_rad, my_off, tx, ty, gx, gy);
       if (slot < capacity) {
         partials[4 * slot + 0] = make_float4(gu, gv, -0.5f * acc[2], -acc[3]);
-        partials[4 * slot + 1] = make_float4(-0.5f * acc[4], acc[5], acc[6], acc[7]);
+        partials[4 * slot + 1] =
+            make_float4(-0.5f * acc[4], acc[5] * s_sp[tid].z, acc[6], acc[7]);
         partials[4 * slot + 2] =
             make_float4(acc[8], kAbs ? acc[kF - 2] : 0.0f, kAbs ? acc[kF - 1] : 0.0f, 0.0f);
       }
