@@ -38,12 +38,12 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # VALU slots of the compositing inner loops, counted in the gfx950 assembly
 # of raster.hip (a quarter-rate v_exp_f32 / v_rcp_f32 counts four slots):
-#   forward: 52 VALU and two v_exp_f32 per two unrolled pairs -> 30 / pair;
-#   backward: 23 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (31
+#   forward: 50 VALU and two v_exp_f32 per two unrolled pairs -> 29 / pair;
+#   backward: 20 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (28
 #   slots); a wavefront with a hit on the splat adds 13 VALU of gradient
 #   terms and 35 of the nine-field reduction (lane swaps + DPP row scan).
-FWD_SLOTS_PER_PAIR = 30.0
-BWD_EVAL_SLOTS = 31.0
+FWD_SLOTS_PER_PAIR = 29.0
+BWD_EVAL_SLOTS = 28.0
 BWD_GRAD_SLOTS = 13.0
 BWD_REDUCE_SLOTS = 35.0
 BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
