@@ -243,7 +243,9 @@ __device__ inline uint64_t lanemask_lt64() {
 
 // Order-preserving compaction of the batch slots by quadrant: s_list[b] receives
 // the slots whose mask has bit b, in ascending slot order; s_cnt[b] their
-// number.  Called by all 256 threads.
+// number.  Called by all 256 threads.  s_wc[b][w] first holds wave w's
+// count for band b, then (NB * 4 lanes, one pass) the count of the waves
+// before it.
 template <int NB, int LD>
 __device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[LD], uint32_t* s_cnt,
                                      uint32_t (*s_wc)[4]) {
@@ -257,15 +259,22 @@ __device__ inline void compact_bands(uint32_t mask, uint8_t (*s_list)[LD], uint3
     if (lane == 0) s_wc[b][wave] = (uint32_t)__popcll(bal);
   }
   __syncthreads();
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if ((mask >> b) & 1u) {
-      uint32_t off = pre[b];
-      for (int w = 0; w < wave; ++w) off += s_wc[b][w];
-      s_list[b][off] = (uint8_t)tid;
-    }
+  uint32_t c4 = 0, ex = 0;
+  if (tid < NB * 4) {
+    const int b = tid >> 2, w = tid & 3;
+    const uint32_t c0 = s_wc[b][0], c1 = s_wc[b][1], c2 = s_wc[b][2], c3 = s_wc[b][3];
+    ex = (w > 0 ? c0 : 0u) + (w > 1 ? c1 : 0u) + (w > 2 ? c2 : 0u);
+    c4 = c0 + c1 + c2 + c3;
   }
-  if (tid < NB) s_cnt[tid] = s_wc[tid][0] + s_wc[tid][1] + s_wc[tid][2] + s_wc[tid][3];
+  __syncthreads();
+  if (tid < NB * 4) {
+    s_wc[tid >> 2][tid & 3] = ex;
+    if ((tid & 3) == 0) s_cnt[tid >> 2] = c4;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if ((mask >> b) & 1u) s_list[b][pre[b] + s_wc[b][wave]] = (uint8_t)tid;
   __syncthreads();
 }
 
