@@ -1,0 +1,104 @@
+"""The radix sort at the edges of its key map.  The passes sort the tile id
+above the depth bits minus the frame's smallest, in as many bits as the
+frame's depths span (none when every depth is equal, up to 32), and the
+binning without the read-back sorts 32 depth bits through the same map.
+Keys, ids and ranges are compared with the oracle's stable sort of the full
+64-bit keys, bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from differentiable_rasterization_amd import scenes
+
+from parity_util import assert_bits_equal, gpu_frame
+
+pytestmark = pytest.mark.gpu
+
+
+def _scene_with(base, means, log_scale_shift):
+    return scenes.Scene(means.astype(np.float32),
+                        (base.scales * np.exp(log_scale_shift)[:, None]).astype(np.float32),
+                        base.quats, base.opacities, base.sh, base.sh_degree)
+
+
+def _depth_bits_span(o):
+    keys = o["bins"]["keys"]
+    db = (keys & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    return int(db.max() - db.min()).bit_length() if db.size else 0
+
+
+def _check(out, o, name):
+    print("[keymap] %s: M=%d, depth bits spanned %d" % (name, out["M"], _depth_bits_span(o)),
+          flush=True)
+    assert out["M"] == len(o["bins"]["keys"])
+    assert_bits_equal(out["keys"], o["bins"]["keys"], "keys")
+    assert_bits_equal(out["ids"], o["bins"]["ids"], "ids")
+    assert_bits_equal(out["ranges"], o["bins"]["ranges"], "ranges")
+
+
+def test_every_depth_equal():
+    """No depth bit varies: the passes sort the tile bits alone, and equal
+    keys (every Gaussian of a tile) keep ascending index."""
+    base, cam = scenes.tiny_scene(n=3000, seed=21)
+    means = base.means.copy()
+    means[:, 2] = 4.0
+    scene = _scene_with(base, means, np.zeros(base.n))
+    out = gpu_frame(scene, cam, backward=False)
+    o = oracle.render(scene, cam)
+    assert _depth_bits_span(o) == 0
+    _check(out, o, "equal depths")
+
+
+def test_depths_spanning_five_decades():
+    """Depths from 0.03 to 3,000 (about 2^29 fp32 codes), sizes scaled with
+    depth so that every Gaussian stays a few pixels wide."""
+    base, cam = scenes.tiny_scene(n=4000, seed=22)
+    rng = np.random.default_rng(22)
+    z = 10.0 ** rng.uniform(-1.5, 3.5, base.n)
+    xy = rng.uniform(-0.45, 0.45, (base.n, 2)) * z[:, None]
+    scene = _scene_with(base, np.concatenate([xy, z[:, None]], 1), np.log(z / 4.0))
+    out = gpu_frame(scene, cam, backward=False)
+    o = oracle.render(scene, cam)
+    assert _depth_bits_span(o) >= 27
+    _check(out, o, "five decades")
+
+
+def _full_hd_scene(n, seed):
+    base, _ = scenes.tiny_scene(n=n, seed=seed)
+    cam = scenes.identity_camera(1920, 1080, 1100.0)
+    rng = np.random.default_rng(seed)
+    z = 10.0 ** rng.uniform(-1.9, 6.0, n)
+    xy = rng.uniform(-0.8, 0.8, (n, 2)) * np.array([960.0, 540.0]) / 1100.0 * z[:, None]
+    return _scene_with(base, np.concatenate([xy, z[:, None]], 1), np.log(z / 20.0)), cam
+
+
+def test_full_hd_frame_with_wide_depths():
+    """1920x1080 (13 tile bits) with depths from 0.013 to 10^6: five passes."""
+    scene, cam = _full_hd_scene(20000, 23)
+    out = gpu_frame(scene, cam, backward=False)
+    o = oracle.render(scene, cam)
+    assert _depth_bits_span(o) + 13 > 40  # more than four 10-bit digits
+    _check(out, o, "1080p wide depths")
+
+
+def test_binning_without_the_read_back():
+    """gs_bin_and_sort_device: the count stays on the device, the passes
+    cover 32 depth bits over the same key map, the grids are sized for the
+    buffers' capacity; the list is the oracle's."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    scene, cam = _full_hd_scene(20000, 24)
+    o = oracle.render(scene, cam)
+    M = len(o["bins"]["keys"])
+    g = raster.Gaussians.from_scene(scene)
+    fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=M + 5000,
+                      device_count=True)
+    fr.project(g, raster.make_camera(cam))
+    fr.bin_and_sort(g)
+    torch.cuda.synchronize()
+    m, over = fr.check_counts()
+    assert (m, over) == (M, False)
+    out = dict(M=m, keys=fr.keys[:m].cpu().numpy().view(np.uint64),
+               ids=fr.ids[:m].cpu().numpy().view(np.uint32),
+               ranges=fr.ranges.cpu().numpy().view(np.uint32))
+    _check(out, o, "device count")
