@@ -246,6 +246,74 @@ __global__ __launch_bounds__(256) void scan_down_kernel(const uint32_t* __restri
   }
 }
 
+// The down-sweep of the binning's scan without a separate pass over the
+// block sums: block b adds up the sums of the blocks before it itself (at
+// most a few hundred values), and the last block also forms the totals, the
+// key map and the instance count the binning kernels use (as
+// scan_partials_kernel does).
+template <bool kVis>
+__global__ __launch_bounds__(256) void scan_down_bin_kernel(
+    const uint32_t* __restrict__ in, int64_t N, const uint64_t* __restrict__ block_sums,
+    const uint32_t* __restrict__ minmax, uint32_t* __restrict__ out,
+    uint32_t* __restrict__ vis_ids, uint64_t* __restrict__ total, uint32_t* __restrict__ keymap,
+    uint64_t capacity, uint32_t* __restrict__ meff, uint64_t* __restrict__ counts) {
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  uint64_t ps = 0, pc = 0;
+  for (int64_t j = threadIdx.x; j < b; j += 256) {
+    ps += block_sums[j];
+    if (kVis) pc += block_sums[nb + j];
+  }
+  uint64_t excl;
+  const uint64_t sbase = block_excl_scan_u64(ps, excl);
+  const uint64_t cbase = kVis ? block_excl_scan_u64(pc, excl) : 0;
+
+  const int64_t base = b * kScanBlock + (int64_t)threadIdx.x * kScanItems;
+  uint32_t v[kScanItems];
+  uint64_t s = 0, c = 0;
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    v[k] = i < N ? in[i] : 0u;
+    s += v[k];
+    c += v[k] > 0u ? 1u : 0u;
+  }
+  const uint64_t stot = block_excl_scan_u64(s, excl);
+  uint64_t run = sbase + excl;
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    if (i < N) out[i] = (uint32_t)run;
+    run += v[k];
+  }
+  uint64_t ctot = 0;
+  if (kVis) {
+    ctot = block_excl_scan_u64(c, excl);
+    uint64_t vrun = cbase + excl;
+    for (int k = 0; k < kScanItems; ++k)
+      if (v[k] > 0u) vis_ids[vrun++] = (uint32_t)(base + k);
+  }
+  if (b != nb - 1) return;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int64_t j = threadIdx.x; j < nb; j += 256) {
+    lo = min(lo, minmax[2 * j]);
+    hi = max(hi, minmax[2 * j + 1]);
+  }
+  block_minmax_u32(lo, hi);
+  if (threadIdx.x == 0) {
+    const uint64_t M = sbase + stot;
+    const uint32_t span = lo <= hi ? hi - lo : 0u;
+    const uint32_t dbits = span ? 32u - (uint32_t)__clz((int)span) : 0u;
+    keymap[0] = lo <= hi ? lo : 0u;
+    keymap[1] = dbits;
+    total[0] = M | ((uint64_t)dbits << kDbitsShift);
+    if (kVis) total[1] = cbase + ctot;
+    const bool over = M > capacity;
+    *meff = over ? 0u : (uint32_t)M;
+    if (counts) {
+      counts[0] = M;
+      counts[1] = over ? 1ull : 0ull;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Stage 3a: duplicate each visible Gaussian once per touched tile
 // ---------------------------------------------------------------------------
@@ -898,16 +966,15 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const flo
     hipLaunchKernelGGL(scan_reduce_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles,
                        depths, N, w.scan_sums, w.minmax);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_partials_kernel, dim3(vis ? 2 : 1), dim3(256), 0, s, w.scan_sums, nb,
-                     w.minmax, w.total, w.keymap, capacity, w.meff,
-                     totals_host ? nullptr : dev_counts);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint64_t* dcounts = totals_host ? nullptr : dev_counts;
   if (vis)
-    hipLaunchKernelGGL(scan_down_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
-                       w.scan_sums, offsets, vis_ids);
+    hipLaunchKernelGGL(scan_down_bin_kernel<true>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
+                       (const uint64_t*)w.scan_sums, (const uint32_t*)w.minmax, offsets, vis_ids,
+                       w.total, w.keymap, capacity, w.meff, dcounts);
   else
-    hipLaunchKernelGGL(scan_down_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles, N,
-                       w.scan_sums, offsets, nullptr);
+    hipLaunchKernelGGL(scan_down_bin_kernel<false>, dim3((unsigned)nb), dim3(256), 0, s, tiles,
+                       N, (const uint64_t*)w.scan_sums, (const uint32_t*)w.minmax, offsets,
+                       (uint32_t*)nullptr, w.total, w.keymap, capacity, w.meff, dcounts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!totals_host) return hipSuccess;  // the count stays on the device
   // straight into the caller's host words: page-locked memory there makes
