@@ -768,7 +768,7 @@ def main():
     frame_ms = sum(stage_ms.values())
     # kernel-level device times of one-frame-at-a-time steps (untimed pass)
     kt = kernel_times(torch, lambda i: step(i, fr=fr), P)
-    sort_ms = _sum_kernels(kt, ("gs::sort_histogram_kernel", "gs::sort_hist_scan_kernel",
+    sort_ms = _sum_kernels(kt, ("gs::sort_first_hist_kernel",
                                 "gs::sort_pass_kernel"), P)
     bwd_kernel_ms = _sum_kernels(kt, ("gs::raster_bwd_kernel",), P)
     reduce_ms = _sum_kernels(kt, ("gs::reduce_partials_kernel",), P)
