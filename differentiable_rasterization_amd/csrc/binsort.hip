@@ -344,8 +344,8 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     int64_t N, const float* __restrict__ means2d, int64_t ld, const int32_t* __restrict__ radii,
     const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
     const uint32_t* __restrict__ offsets, int gx, int gy, bool batched,
-    const uint32_t* __restrict__ meff, SortZero z, uint64_t* __restrict__ keys,
-    uint32_t* __restrict__ ids) {
+    const uint32_t* __restrict__ meff, SortZero z, const uint32_t* __restrict__ keymap,
+    int idbits, uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
   const uint32_t Meff = *meff;
   {
     const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -385,6 +385,8 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
   }
   __syncthreads();
   const uint32_t begin = s_off[0], end = s_off[nloc];
+  const uint32_t dmin = idbits >= 0 ? keymap[0] : 0u;
+  const int dbits = idbits >= 0 ? (int)keymap[1] : 32;
   for (uint32_t slot = begin + t; slot < end; slot += 256) {
     // last j with s_off[j] <= slot (zero-count Gaussians share offsets)
     int lo = 0, hi = (int)nloc;  // invariant: s_off[lo] <= slot < s_off[hi]
@@ -397,8 +399,15 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     const uint32_t ty = (uint32_t)s_y0[lo] + k / w;
     const uint32_t tx = (uint32_t)s_x0[lo] + k % w;
     const uint32_t tile = s_tb[lo] + ty * (uint32_t)gx + tx;
-    keys[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
-    ids[slot] = (uint32_t)(g0 + lo);
+    if (idbits >= 0) {
+      // the sort's own key (tile above the depth bits less the frame's
+      // smallest) with the row index below it, in one word
+      const uint64_t mk = ((uint64_t)tile << dbits) | (uint64_t)(s_db[lo] - dmin);
+      keys[slot] = (mk << idbits) | (uint64_t)(g0 + lo);
+    } else {
+      keys[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
+      ids[slot] = (uint32_t)(g0 + lo);
+    }
   }
 }
 
@@ -457,6 +466,24 @@ __device__ inline uint64_t sort_key(uint64_t k, KeyMap m) {
 __device__ inline uint32_t sort_digit(uint64_t k, KeyMap m, int shift) {
   return (uint32_t)(sort_key(k, m) >> shift) & (uint32_t)(kRadix - 1);
 }
+// Key-id words: (sort key << idbits) | row index, written by the
+// duplication when both fit 64 bits with every pass's digit inside the word
+// (idbits + kRadixBits * passes <= 64, so the all-ones padding word is in the
+// last digit of every pass).  A pass then moves one 8-byte word per instance
+// instead of a key and an id, and the last pass writes the stored key and the
+// id back out.  The words are whole keys of a stable sort by the sort key:
+// equal sort keys come from different rows and leave the duplication in row
+// order, which the row index in the low bits keeps.
+template <bool kIdInKey>
+__device__ inline uint32_t pass_digit(uint64_t k, KeyMap m, int shift) {
+  if constexpr (kIdInKey) return (uint32_t)(k >> shift) & (uint32_t)(kRadix - 1);
+  else return sort_digit(k, m, shift);
+}
+__device__ inline uint64_t unpack_key(uint64_t w, KeyMap m, int idbits) {
+  const uint64_t mk = w >> idbits;
+  const uint64_t dmask = (1ull << m.dbits) - 1ull;  // dbits <= 32
+  return ((mk >> m.dbits) << 32) | (uint64_t)((uint32_t)(mk & dmask) + m.dmin);
+}
 
 // Digit offsets of the first pass: each block histograms a contiguous share
 // of the keys in LDS and adds it to sum[] (agent-scope atomics, at most
@@ -483,10 +510,11 @@ __device__ inline void finish_digit_offsets(uint32_t* sum, uint32_t* hist) {
   }
 }
 
+template <bool kIdInKey>
 __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
     const uint64_t* __restrict__ keys, const uint32_t* __restrict__ meff,
-    const uint32_t* __restrict__ keymap, uint32_t* __restrict__ sum, uint32_t* __restrict__ ctr,
-    uint32_t* __restrict__ hist) {
+    const uint32_t* __restrict__ keymap, int shift0, uint32_t* __restrict__ sum,
+    uint32_t* __restrict__ ctr, uint32_t* __restrict__ hist) {
   static_assert(kHistThreads == kRadix, "a lane per digit");
   const uint32_t M = *meff;
   const KeyMap km = load_keymap(keymap);
@@ -507,7 +535,8 @@ __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
     }
 #pragma unroll
     for (int it = 0; it < kHistItems; ++it)
-      if (b + (uint32_t)(it * kHistThreads + tid) < hi) atomicAdd(&s_h[sort_digit(k[it], km, 0)], 1u);
+      if (b + (uint32_t)(it * kHistThreads + tid) < hi)
+        atomicAdd(&s_h[pass_digit<kIdInKey>(k[it], km, shift0)], 1u);
   }
   __syncthreads();
   if (s_h[tid]) atomicAdd(&sum[tid], s_h[tid]);
@@ -532,10 +561,14 @@ __device__ inline uint64_t lanemask_lt() {
 // count; gstat[group][digit] a group's flagged aggregate, then its
 // inclusive prefix.  Every wait is on a partition with a smaller ticket
 // (one that started earlier), so the passes cannot deadlock.
+// kIdInKey: the keys are key-id words (vin unused; vout NULL except in the
+// last pass, which writes the stored keys and the ids).
+template <bool kIdInKey>
 __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
     uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, const uint32_t* __restrict__ meff,
-    int shift, const uint32_t* __restrict__ keymap, const uint32_t* __restrict__ digit_offsets,
+    int shift, int idbits, const uint32_t* __restrict__ keymap,
+    const uint32_t* __restrict__ digit_offsets,
     uint32_t* __restrict__ pstat, uint32_t* __restrict__ gstat, uint32_t* __restrict__ ticket,
     uint32_t* __restrict__ next_sum, uint32_t* __restrict__ next_ctr,
     uint32_t* __restrict__ next_hist) {
@@ -580,13 +613,13 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint32_t idx = wbase + (uint32_t)it * 64u + (uint32_t)lane;
     const bool valid = idx < M;
     k[it] = valid ? kin[idx] : ~0ull;  // padding ranks last in the last digit
-    v[it] = valid ? vin[idx] : 0u;
+    if constexpr (!kIdInKey) v[it] = valid ? vin[idx] : 0u;
   }
   // stable rank within the wave: keys in (item, lane) order
   const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int it = 0; it < kSortItems; ++it) {
-    const uint32_t d = sort_digit(k[it], km, shift);
+    const uint32_t d = pass_digit<kIdInKey>(k[it], km, shift);
     uint64_t match = ~0ull;
 #pragma unroll
     for (int b = 0; b < kRadixBits; ++b) {
@@ -600,7 +633,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     if (lane == leader) s_wh[wave][d] = (uint16_t)(before + (uint32_t)__popcll(match));
     __builtin_amdgcn_wave_barrier();
     if (has_next && wbase + (uint32_t)it * 64u + (uint32_t)lane < M)
-      atomicAdd(&s_next[sort_digit(k[it], km, shift + kRadixBits)], 1u);
+      atomicAdd(&s_next[pass_digit<kIdInKey>(k[it], km, shift + kRadixBits)], 1u);
   }
   __syncthreads();
   // this partition's share of the next pass's digit totals
@@ -648,7 +681,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   // after this)
 #pragma unroll
   for (int it = 0; it < kSortItems; ++it) {
-    const uint32_t dd = sort_digit(k[it], km, shift);
+    const uint32_t dd = pass_digit<kIdInKey>(k[it], km, shift);
     rank[it] += (uint32_t)s_start[dd] + (uint32_t)s_wh[wave][dd];
   }
 
@@ -767,32 +800,50 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   }
   __syncthreads();
 
-  // keys, then values, through LDS in local sorted order; written out in
+  // keys (then values) through LDS in local sorted order; written out in
   // that order, consecutive lanes hit consecutive slots of a digit run
 #pragma unroll
   for (int it = 0; it < kSortItems; ++it)
     if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_buf[rank[it]] = k[it];
   __syncthreads();
-  uint32_t outj[kSortItems];
+  if constexpr (kIdInKey) {
+    const uint64_t idmask = (1ull << idbits) - 1ull;  // idbits < 64
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
-    if (j < nvalid) {
-      const uint64_t key = s_buf[j];
-      const uint32_t out = s_gbase[sort_digit(key, km, shift)] + j;
-      kout[out] = key;
-      outj[i] = out;
+    for (int i = 0; i < kSortItems; ++i) {
+      const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
+      if (j < nvalid) {
+        const uint64_t word = s_buf[j];
+        const uint32_t out = s_gbase[pass_digit<true>(word, km, shift)] + j;
+        if (vout) {
+          kout[out] = unpack_key(word, km, idbits);
+          vout[out] = (uint32_t)(word & idmask);
+        } else {
+          kout[out] = word;
+        }
+      }
     }
-  }
-  __syncthreads();
+  } else {
+    uint32_t outj[kSortItems];
 #pragma unroll
-  for (int it = 0; it < kSortItems; ++it)
-    if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_vals[rank[it]] = v[it];
-  __syncthreads();
+    for (int i = 0; i < kSortItems; ++i) {
+      const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
+      if (j < nvalid) {
+        const uint64_t key = s_buf[j];
+        const uint32_t out = s_gbase[sort_digit(key, km, shift)] + j;
+        kout[out] = key;
+        outj[i] = out;
+      }
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
-    if (j < nvalid) vout[outj[i]] = s_vals[j];
+    for (int it = 0; it < kSortItems; ++it)
+      if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_vals[rank[it]] = v[it];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+      const uint32_t j = (uint32_t)tid + (uint32_t)i * kSortThreads;
+      if (j < nvalid) vout[outj[i]] = s_vals[j];
+    }
   }
   if (!has_next) return;
   // the last partition to finish turns the next digit's totals into offsets
@@ -835,6 +886,11 @@ struct SortPlan {
 static inline int ceil_log2(uint32_t x) {
   int b = 0;
   while ((1ull << b) < x) ++b;
+  return b;
+}
+static inline int ceil_log2_u64(uint64_t x) {
+  int b = 0;
+  while (b < 64 && (1ull << b) < x) ++b;
   return b;
 }
 
@@ -899,26 +955,45 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
 
 // Digit offsets and the passes, ping-ponging between (ka, ia) and
 // (kb, ib); an even pass count ends in (ka, ia).  dsum and ticket must be
-// zero.
+// zero.  idbits >= 0: ka holds key-id words (pass_digit); the passes move
+// only the words, and the last writes the stored keys and the ids.
 static hipError_t launch_sort_passes(const SortPlan& sp, const uint32_t* meff,
                                      const uint32_t* keymap, uint32_t* hist, uint32_t* dsum,
                                      uint32_t* ticket, uint32_t* pstat, uint32_t* gstat,
                                      uint64_t* ka, uint32_t* ia, uint64_t* kb, uint32_t* ib,
-                                     hipStream_t s) {
+                                     int idbits, hipStream_t s) {
   hipError_t e;
   uint32_t* ctr = ticket + kMaxPasses;
-  hipLaunchKernelGGL(sort_first_hist_kernel, dim3((unsigned)sp.hblocks), dim3(kHistThreads), 0, s,
-                     (const uint64_t*)ka, meff, keymap, dsum, ctr, hist);
+  const bool words = idbits >= 0;
+  const int s0 = words ? idbits : 0;
+  if (words)
+    hipLaunchKernelGGL(sort_first_hist_kernel<true>, dim3((unsigned)sp.hblocks),
+                       dim3(kHistThreads), 0, s, (const uint64_t*)ka, meff, keymap, s0, dsum, ctr,
+                       hist);
+  else
+    hipLaunchKernelGGL(sort_first_hist_kernel<false>, dim3((unsigned)sp.hblocks),
+                       dim3(kHistThreads), 0, s, (const uint64_t*)ka, meff, keymap, s0, dsum, ctr,
+                       hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < sp.passes; ++p) {
     const bool next = p + 1 < sp.passes;
-    hipLaunchKernelGGL(sort_pass_kernel, dim3(sp.parts), dim3(kSortThreads), 0, s,
-                       (const uint64_t*)ka, (const uint32_t*)ia, kb, ib, meff, p * kRadixBits,
-                       keymap, (const uint32_t*)(hist + p * kRadix),
-                       pstat + (size_t)p * sp.parts * kRadix,
-                       gstat + (size_t)p * sp.groups * kRadix, ticket + p,
-                       next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
-                       next ? hist + (p + 1) * kRadix : nullptr);
+    if (words)
+      hipLaunchKernelGGL(sort_pass_kernel<true>, dim3(sp.parts), dim3(kSortThreads), 0, s,
+                         (const uint64_t*)ka, (const uint32_t*)nullptr, kb,
+                         next ? (uint32_t*)nullptr : ib, meff, s0 + p * kRadixBits, idbits,
+                         keymap, (const uint32_t*)(hist + p * kRadix),
+                         pstat + (size_t)p * sp.parts * kRadix,
+                         gstat + (size_t)p * sp.groups * kRadix, ticket + p,
+                         next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
+                         next ? hist + (p + 1) * kRadix : nullptr);
+    else
+      hipLaunchKernelGGL(sort_pass_kernel<false>, dim3(sp.parts), dim3(kSortThreads), 0, s,
+                         (const uint64_t*)ka, (const uint32_t*)ia, kb, ib, meff, p * kRadixBits,
+                         0, keymap, (const uint32_t*)(hist + p * kRadix),
+                         pstat + (size_t)p * sp.parts * kRadix,
+                         gstat + (size_t)p * sp.groups * kRadix, ticket + p,
+                         next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
+                         next ? hist + (p + 1) * kRadix : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint64_t* tk = ka; ka = kb; kb = tk;
     uint32_t* ti = ia; ia = ib; ib = ti;
@@ -1025,12 +1100,18 @@ extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const flo
   const int64_t zblk = (2 * (int64_t)T + (int64_t)sp.parts * kRadix + 4095) / 4096;
   if (nblk < zblk) nblk = zblk;
   if (nblk < 1) nblk = 1;
+  // key-id words when the sort key, the row index and every pass's digit
+  // fit one word (1080p, 1M rows: 39 + 20 bits, four passes)
+  const int idbits = ceil_log2_u64((uint64_t)N);
+  const bool words = !device_count && idbits + kRadixBits * sp.passes <= 64;
   hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
-                     depths, tiles, offsets, gx, gy, ncams > 1, (const uint32_t*)w.meff, z, ka, ia);
+                     depths, tiles, offsets, gx, gy, ncams > 1, (const uint32_t*)w.meff, z,
+                     (const uint32_t*)w.keymap, words ? idbits : -1, ka, ia);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if ((e = launch_sort_passes(sp, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum, w.ticket,
-                               w.pstat, w.gstat, ka, ia, kb, ib, s)) != hipSuccess)
+                               w.pstat, w.gstat, ka, ia, kb, ib, words ? idbits : -1, s)) !=
+      hipSuccess)
     return e;
   const unsigned rblocks = (unsigned)((Mg + 255) / 256);
   hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, w.meff, (uint32_t)T,
@@ -1122,7 +1203,7 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   }
   if ((e = fill_u32(w.meff, 1, (uint32_t)n, s)) != hipSuccess) return e;
   return launch_sort_passes(w.sp, w.meff, nullptr, w.hist, w.dsum, w.ticket, w.pstat, w.gstat,
-                            ka, ia, kb, ib, s);
+                            ka, ia, kb, ib, -1, s);
 }
 
 extern "C" size_t gs_scan_workspace_bytes(int64_t n) {
