@@ -29,16 +29,15 @@ hipError_t gs_launch_project_bwd(int64_t N, int64_t ld, const uint32_t* vis_ids,
                                  float* o_scales, float* o_quats, float* o_opac, float* o_sh,
                                  int accumulate, hipStream_t stream);
 size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32_t T);
-hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
-                          uint32_t* offsets, uint32_t* vis_ids, void* workspace, uint64_t capacity,
-                          int32_t T, uint64_t* totals_host, int* dbits, uint64_t* dev_counts,
-                          hipStream_t s);
-hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
-                                     const int32_t* radii, const float* depths,
-                                     const uint32_t* tiles, const uint32_t* offsets, int32_t W,
-                                     int32_t H, int ncams, uint64_t M, int dbits, bool device_count,
-                                     uint64_t* keys, uint32_t* ids, uint32_t* ranges,
-                                     void* workspace, uint64_t capacity, hipStream_t s);
+hipError_t gs_launch_bin_front(int64_t N, int64_t ld, const float* means2d,
+                               const int32_t* radii, const float* depths, const uint32_t* tiles,
+                               uint32_t* offsets, uint32_t* vis_ids, int32_t W, int32_t H,
+                               int ncams, uint64_t* keys, uint32_t* ids, uint32_t* ranges,
+                               void* workspace, uint64_t capacity, uint64_t* totals_host,
+                               int* dbits, uint64_t* dev_counts, hipStream_t s);
+hipError_t gs_launch_bin_back(int64_t N, int32_t W, int32_t H, int ncams, uint64_t M, int dbits,
+                              bool device_count, uint64_t* keys, uint32_t* ids, uint32_t* ranges,
+                              void* workspace, uint64_t capacity, hipStream_t s);
 hipError_t gs_launch_tile_order(int32_t W, int32_t H, int ncams, const uint32_t* ranges,
                                 uint32_t* order, hipStream_t s);
 hipError_t gs_launch_pack_splats(int64_t rows, int64_t ld, const float* means2d,
@@ -159,18 +158,20 @@ gs_status check_bin_args(int64_t N, int64_t ld, const float* means2d, const int3
   return GS_OK;
 }
 
-// Scan, read M back, then duplicate, sort and extract the ranges, with the
-// sort's scratch in `workspace` (at least gs_binsort_workspace_bytes).
+// Scan and duplicate while M is read back, then sort and extract the
+// ranges, with the sort's scratch in `workspace` (at least
+// gs_binsort_workspace_bytes).
 gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const int32_t* radii,
                             const float* depths, const uint32_t* tiles_touched, int32_t width,
                             int32_t height, uint32_t* offsets, uint64_t capacity,
                             uint64_t* num_instances, uint64_t* keys, uint32_t* ids,
                             uint32_t* tile_ranges, void* workspace, hipStream_t s,
                             const char* name) {
-  const int32_t T = gs_num_tiles(width, height);
   int dbits = 32;
-  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
-                                           capacity, T, num_instances, &dbits, nullptr, s),
+  gs_status st = hip_status(gs_launch_bin_front(N, ld, means2d, radii, depths, tiles_touched,
+                                                offsets, nullptr, width, height, 1, keys, ids,
+                                                tile_ranges, workspace, capacity, num_instances,
+                                                &dbits, nullptr, s),
                             name);
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -181,9 +182,8 @@ gs_status bin_and_sort_impl(int64_t N, int64_t ld, const float* means2d, const i
              (unsigned long long)M, (unsigned long long)capacity);
     return GS_ERR_CAPACITY;
   }
-  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, dbits, false, keys,
-                                              ids, tile_ranges, workspace, capacity, s),
+  return hip_status(gs_launch_bin_back(N, width, height, 1, M, dbits, false, keys, ids,
+                                       tile_ranges, workspace, capacity, s),
                     name);
 }
 
@@ -425,13 +425,14 @@ gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* means2d,
   GS_REQUIRE(workspace_bytes >= gs_binsort_workspace_bytes(N, capacity, T),
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
-  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, nullptr, workspace,
-                                           capacity, T, nullptr, nullptr, counts, s),
+  gs_status st = hip_status(gs_launch_bin_front(N, ld, means2d, radii, depths, tiles_touched,
+                                                offsets, nullptr, width, height, 1, keys, ids,
+                                                tile_ranges, workspace, capacity, nullptr,
+                                                nullptr, counts, s),
                             "gs_bin_and_sort_device(scan)");
   if (st != GS_OK) return st;
-  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, 0, 32, true, keys, ids,
-                                              tile_ranges, workspace, capacity, s),
+  return hip_status(gs_launch_bin_back(N, width, height, 1, 0, 32, true, keys, ids, tile_ranges,
+                                       workspace, capacity, s),
                     "gs_bin_and_sort_device");
 }
 
@@ -583,8 +584,10 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
              "workspace smaller than gs_bin_and_sort_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
   int dbits = 32;
-  gs_status st = hip_status(gs_launch_scan(N, tiles_touched, depths, offsets, vis_ids, workspace,
-                                           capacity, T, counts, &dbits, nullptr, s),
+  gs_status st = hip_status(gs_launch_bin_front(N, ld, means2d, radii, depths, tiles_touched,
+                                                offsets, vis_ids, width, height, 1, keys, ids,
+                                                tile_ranges, workspace, capacity, counts, &dbits,
+                                                nullptr, s),
                             "gs_bin_and_sort_packed(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = counts[0];
@@ -595,9 +598,8 @@ gs_status gs_bin_and_sort_packed(int64_t N, int64_t ld, const float* means2d,
              (unsigned long long)M, (unsigned long long)capacity);
     return GS_ERR_CAPACITY;
   }
-  return hip_status(gs_launch_dup_sort_ranges(N, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, 1, M, dbits, false, keys,
-                                              ids, tile_ranges, workspace, capacity, s),
+  return hip_status(gs_launch_bin_back(N, width, height, 1, M, dbits, false, keys, ids,
+                                       tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_packed");
 }
 
@@ -733,9 +735,10 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
              "workspace smaller than gs_bin_and_sort_batched_workspace_size()");
   hipStream_t s = (hipStream_t)stream;
   int dbits = 32;
-  gs_status st = hip_status(gs_launch_scan(rows, tiles_touched, depths, offsets, nullptr,
-                                           workspace, capacity, (int32_t)T, num_instances, &dbits,
-                                           nullptr, s),
+  gs_status st = hip_status(gs_launch_bin_front(rows, ld, means2d, radii, depths, tiles_touched,
+                                                offsets, nullptr, width, height, num_cams, keys,
+                                                ids, tile_ranges, workspace, capacity,
+                                                num_instances, &dbits, nullptr, s),
                             "gs_bin_and_sort_batched(scan)");
   if (st != GS_OK) return st;
   const uint64_t M = *num_instances;
@@ -746,9 +749,8 @@ gs_status gs_bin_and_sort_batched(int32_t num_cams, int64_t ld, const float* mea
              (unsigned long long)M, (unsigned long long)capacity);
     return GS_ERR_CAPACITY;
   }
-  return hip_status(gs_launch_dup_sort_ranges(rows, ld, means2d, radii, depths, tiles_touched,
-                                              offsets, width, height, num_cams, M, dbits, false,
-                                              keys, ids, tile_ranges, workspace, capacity, s),
+  return hip_status(gs_launch_bin_back(rows, width, height, num_cams, M, dbits, false, keys, ids,
+                                       tile_ranges, workspace, capacity, s),
                     "gs_bin_and_sort_batched");
 }
 

@@ -94,13 +94,36 @@ __device__ inline uint64_t block_excl_scan_u64(uint64_t x, uint64_t& excl) {
 // order to vis_ids; its per-block sums follow the first set at sums + nb.
 // ---------------------------------------------------------------------------
 constexpr int kScanItems = 8;
-// sort shapes the duplication's zeroing needs (see the sort below)
-constexpr int kDigits = 1024;          // radix of a sort pass
+// sort shapes the duplication needs (see the sort below)
+constexpr int kDigitBits = 10;         // bits of a sort pass's digit
+constexpr int kDigits = 1 << kDigitBits;  // radix of a sort pass
 constexpr int kPartKeys = 8192;        // keys per sort partition
 constexpr int kGroupPartitions = 16;   // partitions per look-back group
 constexpr int kDbitsShift = 58;
 constexpr uint64_t kCountBits = (1ull << kDbitsShift) - 1ull;
 constexpr int kScanBlock = 256 * kScanItems;
+
+// Passes of a sort over `bits` key bits (at least one).
+__host__ __device__ inline int sort_pass_count(int bits) {
+  return bits > 0 ? (bits + kDigitBits - 1) / kDigitBits : 1;
+}
+
+// How the sort runs, decided from the key map on the device (the duplication
+// and the first digit's histogram run before the host has read the count
+// back) and again on the host from the read-back depth bits, with the same
+// result: the pass count for the key's bits, and whether the keys travel as
+// key-id words (see pass_digit).  pass_dbits >= 0 plans for that many depth
+// bits instead of the map's; idbits < 0 never uses words.
+struct SortMode {
+  int passes;
+  bool words;
+};
+__host__ __device__ inline SortMode sort_mode(int dbits, int tbits, int idbits) {
+  SortMode m;
+  m.passes = sort_pass_count(dbits + tbits);
+  m.words = idbits >= 0 && idbits + kDigitBits * m.passes <= 64;
+  return m;
+}
 
 // Smallest and largest u32 over a 256-lane workgroup (valid in every lane).
 __device__ inline void block_minmax_u32(uint32_t& lo, uint32_t& hi) {
@@ -345,7 +368,9 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     const float* __restrict__ depths, const uint32_t* __restrict__ tiles_touched,
     const uint32_t* __restrict__ offsets, int gx, int gy, bool batched,
     const uint32_t* __restrict__ meff, SortZero z, const uint32_t* __restrict__ keymap,
-    int idbits, uint64_t* __restrict__ keys, uint32_t* __restrict__ ids) {
+    int tbits, int idbits, int pass_dbits, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ ids, uint64_t* __restrict__ keys_alt,
+    uint32_t* __restrict__ ids_alt) {
   const uint32_t Meff = *meff;
   {
     const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -385,8 +410,13 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
   }
   __syncthreads();
   const uint32_t begin = s_off[0], end = s_off[nloc];
-  const uint32_t dmin = idbits >= 0 ? keymap[0] : 0u;
-  const int dbits = idbits >= 0 ? (int)keymap[1] : 32;
+  const SortMode mode = sort_mode(pass_dbits >= 0 ? pass_dbits : (int)keymap[1], tbits, idbits);
+  // the buffers the first pass reads: an odd pass count starts from the
+  // alternate ones, so that the last pass writes (keys, ids)
+  uint64_t* __restrict__ kdst = (mode.passes & 1) ? keys_alt : keys;
+  uint32_t* __restrict__ idst = (mode.passes & 1) ? ids_alt : ids;
+  const uint32_t dmin = keymap[0];
+  const int dbits = (int)keymap[1];
   for (uint32_t slot = begin + t; slot < end; slot += 256) {
     // last j with s_off[j] <= slot (zero-count Gaussians share offsets)
     int lo = 0, hi = (int)nloc;  // invariant: s_off[lo] <= slot < s_off[hi]
@@ -399,14 +429,14 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
     const uint32_t ty = (uint32_t)s_y0[lo] + k / w;
     const uint32_t tx = (uint32_t)s_x0[lo] + k % w;
     const uint32_t tile = s_tb[lo] + ty * (uint32_t)gx + tx;
-    if (idbits >= 0) {
+    if (mode.words) {
       // the sort's own key (tile above the depth bits less the frame's
       // smallest) with the row index below it, in one word
       const uint64_t mk = ((uint64_t)tile << dbits) | (uint64_t)(s_db[lo] - dmin);
-      keys[slot] = (mk << idbits) | (uint64_t)(g0 + lo);
+      kdst[slot] = (mk << idbits) | (uint64_t)(g0 + lo);
     } else {
-      keys[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
-      ids[slot] = (uint32_t)(g0 + lo);
+      kdst[slot] = ((uint64_t)tile << 32) | (uint64_t)s_db[lo];
+      idst[slot] = (uint32_t)(g0 + lo);
     }
   }
 }
@@ -416,7 +446,7 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 // ---------------------------------------------------------------------------
 // 10-bit digits: a frame's keys need only the bits that vary (see KeyMap),
 // about 39 at 1080p, so four passes.
-constexpr int kRadixBits = 10;
+constexpr int kRadixBits = kDigitBits;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortItems = 8;
 // 1024-lane workgroups of 8192 keys, one digit per lane in the per-digit
@@ -443,8 +473,10 @@ constexpr int kGroupParts = 16;
 constexpr int kGroupLookback = 8;
 static_assert(kDigits == kRadix && kPartKeys == kPart && kGroupPartitions == kGroupParts,
               "the duplication zeroes what the sort uses");
-// Most blocks of the first digit's histogram.
-constexpr int kHistBlocks = 256;
+// Most blocks of the first digit's histogram (its grid is sized before the
+// count is known; 128 blocks of 8192-key strides took 0.145 ms of binning
+// at 1080p one frame at a time, 256 blocks 0.147).
+constexpr int kHistBlocks = 128;
 
 // The key a pass takes its digit from: the tile id above the depth bits
 // minus the frame's smallest depth bits, in dbits bits.  Within a frame this
@@ -510,14 +542,19 @@ __device__ inline void finish_digit_offsets(uint32_t* sum, uint32_t* hist) {
   }
 }
 
-template <bool kIdInKey>
+// The keys are in `keys`, or in `keys_alt` for an odd pass count, as key-id
+// words or not (sort_mode, from the key map unless pass_dbits >= 0; a NULL
+// key map sorts the keys' own bits).
 __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
-    const uint64_t* __restrict__ keys, const uint32_t* __restrict__ meff,
-    const uint32_t* __restrict__ keymap, int shift0, uint32_t* __restrict__ sum,
-    uint32_t* __restrict__ ctr, uint32_t* __restrict__ hist) {
+    const uint64_t* __restrict__ keys, const uint64_t* __restrict__ keys_alt,
+    const uint32_t* __restrict__ meff, const uint32_t* __restrict__ keymap, int tbits,
+    int idbits, int pass_dbits, uint32_t* __restrict__ sum, uint32_t* __restrict__ ctr,
+    uint32_t* __restrict__ hist) {
   static_assert(kHistThreads == kRadix, "a lane per digit");
   const uint32_t M = *meff;
   const KeyMap km = load_keymap(keymap);
+  const SortMode mode = sort_mode(pass_dbits >= 0 ? pass_dbits : km.dbits, tbits, idbits);
+  const uint64_t* __restrict__ kin = (mode.passes & 1) ? keys_alt : keys;
   __shared__ uint32_t s_h[kRadix];
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -531,12 +568,14 @@ __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
 #pragma unroll
     for (int it = 0; it < kHistItems; ++it) {
       const uint32_t i = b + (uint32_t)(it * kHistThreads + tid);
-      k[it] = i < hi ? keys[i] : ~0ull;
+      k[it] = i < hi ? kin[i] : ~0ull;
     }
 #pragma unroll
     for (int it = 0; it < kHistItems; ++it)
       if (b + (uint32_t)(it * kHistThreads + tid) < hi)
-        atomicAdd(&s_h[pass_digit<kIdInKey>(k[it], km, shift0)], 1u);
+        atomicAdd(&s_h[mode.words ? pass_digit<true>(k[it], km, idbits)
+                                  : pass_digit<false>(k[it], km, 0)],
+                  1u);
   }
   __syncthreads();
   if (s_h[tid]) atomicAdd(&sum[tid], s_h[tid]);
@@ -897,9 +936,8 @@ static inline int ceil_log2_u64(uint64_t x) {
 // dbits: the depth bits the frame's key map keeps (32 when unknown on the
 // host).
 static inline SortPlan sort_plan(uint64_t M, int32_t T, int dbits = 32) {
-  const int bits = dbits + ceil_log2((uint32_t)T);
   SortPlan p;
-  p.passes = bits > 0 ? (bits + kRadixBits - 1) / kRadixBits : 1;
+  p.passes = sort_pass_count(dbits + ceil_log2((uint32_t)T));
   p.parts = (uint32_t)((M + kPart - 1) / kPart);
   p.groups = (p.parts + kGroupParts - 1) / kGroupParts;
   const uint64_t hb = (M + kHistThreads * kHistItems - 1) / (kHistThreads * kHistItems);
@@ -953,28 +991,21 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
   return w;
 }
 
-// Digit offsets and the passes, ping-ponging between (ka, ia) and
-// (kb, ib); an even pass count ends in (ka, ia).  dsum and ticket must be
-// zero.  idbits >= 0: ka holds key-id words (pass_digit); the passes move
+// The passes, ping-ponging between (ka, ia) and (kb, ib); an even pass
+// count ends in (ka, ia).  The first digit's offsets are in hist (from
+// sort_first_hist_kernel); ticket and the later digits' totals must be zero.
+// Statuses are laid out for lay.parts partitions and lay.groups groups per
+// pass.  idbits >= 0: ka holds key-id words (pass_digit); the passes move
 // only the words, and the last writes the stored keys and the ids.
-static hipError_t launch_sort_passes(const SortPlan& sp, const uint32_t* meff,
-                                     const uint32_t* keymap, uint32_t* hist, uint32_t* dsum,
-                                     uint32_t* ticket, uint32_t* pstat, uint32_t* gstat,
-                                     uint64_t* ka, uint32_t* ia, uint64_t* kb, uint32_t* ib,
-                                     int idbits, hipStream_t s) {
+static hipError_t launch_sort_passes(const SortPlan& sp, const SortPlan& lay,
+                                     const uint32_t* meff, const uint32_t* keymap, uint32_t* hist,
+                                     uint32_t* dsum, uint32_t* ticket, uint32_t* pstat,
+                                     uint32_t* gstat, uint64_t* ka, uint32_t* ia, uint64_t* kb,
+                                     uint32_t* ib, int idbits, hipStream_t s) {
   hipError_t e;
   uint32_t* ctr = ticket + kMaxPasses;
   const bool words = idbits >= 0;
   const int s0 = words ? idbits : 0;
-  if (words)
-    hipLaunchKernelGGL(sort_first_hist_kernel<true>, dim3((unsigned)sp.hblocks),
-                       dim3(kHistThreads), 0, s, (const uint64_t*)ka, meff, keymap, s0, dsum, ctr,
-                       hist);
-  else
-    hipLaunchKernelGGL(sort_first_hist_kernel<false>, dim3((unsigned)sp.hblocks),
-                       dim3(kHistThreads), 0, s, (const uint64_t*)ka, meff, keymap, s0, dsum, ctr,
-                       hist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int p = 0; p < sp.passes; ++p) {
     const bool next = p + 1 < sp.passes;
     if (words)
@@ -982,16 +1013,16 @@ static hipError_t launch_sort_passes(const SortPlan& sp, const uint32_t* meff,
                          (const uint64_t*)ka, (const uint32_t*)nullptr, kb,
                          next ? (uint32_t*)nullptr : ib, meff, s0 + p * kRadixBits, idbits,
                          keymap, (const uint32_t*)(hist + p * kRadix),
-                         pstat + (size_t)p * sp.parts * kRadix,
-                         gstat + (size_t)p * sp.groups * kRadix, ticket + p,
+                         pstat + (size_t)p * lay.parts * kRadix,
+                         gstat + (size_t)p * lay.groups * kRadix, ticket + p,
                          next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
                          next ? hist + (p + 1) * kRadix : nullptr);
     else
       hipLaunchKernelGGL(sort_pass_kernel<false>, dim3(sp.parts), dim3(kSortThreads), 0, s,
                          (const uint64_t*)ka, (const uint32_t*)ia, kb, ib, meff, p * kRadixBits,
                          0, keymap, (const uint32_t*)(hist + p * kRadix),
-                         pstat + (size_t)p * sp.parts * kRadix,
-                         gstat + (size_t)p * sp.groups * kRadix, ticket + p,
+                         pstat + (size_t)p * lay.parts * kRadix,
+                         gstat + (size_t)p * lay.groups * kRadix, ticket + p,
                          next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
                          next ? hist + (p + 1) * kRadix : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1007,17 +1038,44 @@ extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32
   return gs::carve(nullptr, N, capacity, T).bytes;
 }
 
-// Scan; writes offsets and M to totals_host[0] (one synchronising read),
-// and the depth bits the sort's key map keeps to *dbits.  With vis_ids
-// non-NULL also the ascending indices of the Gaussians with tiles, and their
-// count V to totals_host[1], in the same read.  totals_host NULL: the counts
-// and the key map stay on the device (dbits is not written), and
-// dev_counts (device, optional) receives M and the overflow flag.
-extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const float* depths,
-                                     uint32_t* offsets, uint32_t* vis_ids, void* workspace,
-                                     uint64_t capacity, int32_t T, uint64_t* totals_host,
-                                     int* dbits, uint64_t* dev_counts, hipStream_t s) {
+namespace gs {
+// One event per device and host thread marks the count's copy to the host
+// (a thread's calls wait on their own copies only).
+static hipError_t count_copy_event(hipEvent_t* ev) {
+  static thread_local hipEvent_t evs[64] = {};
+  int dev = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!evs[dev] && (e = hipEventCreateWithFlags(&evs[dev], hipEventDisableTiming)) != hipSuccess)
+    return e;
+  *ev = evs[dev];
+  return hipSuccess;
+}
+}  // namespace gs
+
+// First half of binning: scan, duplication and the first digit's histogram.
+// Writes offsets and, with totals_host, M to totals_host[0] (read back) and
+// the depth bits the sort's key map keeps to *dbits; with vis_ids non-NULL
+// also the ascending indices of the Gaussians with tiles and their count V
+// (totals_host[1], same read).  The host waits only for that read, which is
+// queued before the duplication, so the duplication and the histogram run
+// while the count travels.  totals_host NULL: the count and the key map stay
+// on the device (dbits is not written), dev_counts (device, optional)
+// receives M and the overflow flag, and the passes are planned for 32 depth
+// bits.  The kernels take M from the device, 0 when it exceeds `capacity`.
+// ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
+extern "C" hipError_t gs_launch_bin_front(int64_t N, int64_t ld, const float* means2d,
+                                          const int32_t* radii, const float* depths,
+                                          const uint32_t* tiles, uint32_t* offsets,
+                                          uint32_t* vis_ids, int32_t W, int32_t H, int ncams,
+                                          uint64_t* keys, uint32_t* ids, uint32_t* ranges,
+                                          void* workspace, uint64_t capacity,
+                                          uint64_t* totals_host, int* dbits,
+                                          uint64_t* dev_counts, hipStream_t s) {
   using namespace gs;
+  const int gx = grid_dim(W), gy = grid_dim(H);
+  const int32_t T = gx * gy * ncams;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
   const bool vis = vis_ids != nullptr;
@@ -1051,67 +1109,83 @@ extern "C" hipError_t gs_launch_scan(int64_t N, const uint32_t* tiles, const flo
                        N, (const uint64_t*)w.scan_sums, (const uint32_t*)w.minmax, offsets,
                        (uint32_t*)nullptr, w.total, w.keymap, capacity, w.meff, dcounts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipEvent_t ev = nullptr;
+  if (totals_host) {
+    // straight into the caller's host words: page-locked memory there makes
+    // this a direct transfer instead of a staged one
+    if ((e = count_copy_event(&ev)) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
+                            hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return e;
+    if ((e = hipEventRecord(ev, s)) != hipSuccess) return e;
+  }
+  if (capacity > 0) {
+    // statuses laid out for the capacity and 32 depth bits (the most passes)
+    const SortPlan lay = sort_plan(capacity, T);
+    // dsum follows hist, ticket follows dsum: one span from dsum to the counters
+    const SortZero z = {ranges, 2 * (int64_t)T, w.dsum,
+                        (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum), w.pstat, w.gstat,
+                        lay.parts, lay.groups, lay.passes};
+    const int tbits = ceil_log2((uint32_t)T);
+    // key-id words only when the host knows the pass count (see sort_mode)
+    const int idbits = totals_host ? ceil_log2_u64((uint64_t)N) : -1;
+    const int pass_dbits = totals_host ? -1 : 32;
+    // enough blocks for the rows and for a few zeroing strides
+    int64_t nblk = (N + 255) / 256;
+    const int64_t zblk = (2 * (int64_t)T + (int64_t)lay.parts * kRadix + 4095) / 4096;
+    if (nblk < zblk) nblk = zblk;
+    hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld,
+                       radii, depths, tiles, (const uint32_t*)offsets, gx, gy, ncams > 1,
+                       (const uint32_t*)w.meff, z, (const uint32_t*)w.keymap, tbits, idbits,
+                       pass_dbits, keys, ids, w.keys_alt, w.ids_alt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the first digit's offsets, over a grid for the capacity (each block
+    // takes its share of the device count)
+    const uint64_t hb = (capacity + kHistThreads * kHistItems - 1) / (kHistThreads * kHistItems);
+    const unsigned hblocks = hb > (uint64_t)kHistBlocks ? (unsigned)kHistBlocks : (unsigned)hb;
+    hipLaunchKernelGGL(sort_first_hist_kernel, dim3(hblocks), dim3(kHistThreads), 0, s,
+                       (const uint64_t*)keys, (const uint64_t*)w.keys_alt,
+                       (const uint32_t*)w.meff, (const uint32_t*)w.keymap, tbits, idbits,
+                       pass_dbits, w.dsum, w.ticket + kMaxPasses, w.hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (!totals_host) return hipSuccess;  // the count stays on the device
-  // straight into the caller's host words: page-locked memory there makes
-  // this a direct transfer instead of a staged one
-  if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
-                          hipMemcpyDeviceToHost, s)) != hipSuccess)
-    return e;
-  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  if ((e = hipEventSynchronize(ev)) != hipSuccess) return e;
   *dbits = (int)(totals_host[0] >> kDbitsShift);
   totals_host[0] &= kCountBits;
   return hipSuccess;
 }
 
-// Duplicate, sort and extract ranges for M instances (M <= capacity).
-// ncams > 1: a batch; N = ncams * ld rows, T = ncams tiles per camera.
-// M, dbits: the instance count and the key map's depth bits read back by the
-// caller, or, with device_count, unknown on the host: the kernels then take
-// M from the scan on the device (0 when it exceeded `capacity`), grids are
-// sized for `capacity` and the passes cover 32 depth bits.
-extern "C" hipError_t gs_launch_dup_sort_ranges(int64_t N, int64_t ld, const float* means2d,
-                                                const int32_t* radii, const float* depths,
-                                                const uint32_t* tiles, const uint32_t* offsets,
-                                                int32_t W, int32_t H, int ncams, uint64_t M,
-                                                int dbits, bool device_count, uint64_t* keys,
-                                                uint32_t* ids, uint32_t* ranges, void* workspace,
-                                                uint64_t capacity, hipStream_t s) {
+// Second half: the sort passes and the per-tile ranges for M instances
+// (M <= capacity), after gs_launch_bin_front with the same arguments.  M,
+// dbits: as read back by the first half, or, with device_count, unknown on
+// the host: the kernels then take M from the device, grids are sized for
+// `capacity` and the passes cover 32 depth bits.
+extern "C" hipError_t gs_launch_bin_back(int64_t N, int32_t W, int32_t H, int ncams, uint64_t M,
+                                         int dbits, bool device_count, uint64_t* keys,
+                                         uint32_t* ids, uint32_t* ranges, void* workspace,
+                                         uint64_t capacity, hipStream_t s) {
   using namespace gs;
   const int gx = grid_dim(W), gy = grid_dim(H);
   const int32_t T = gx * gy * ncams;
   Workspace w = carve(workspace, N, capacity, T);
   hipError_t e;
-  if (!device_count && M == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   // grids for M, or for the largest count the buffers hold
   const uint64_t Mg = device_count ? capacity : M;
   if (Mg == 0) return fill_u32(ranges, 2 * (int64_t)T, 0u, s);
   const SortPlan sp = sort_plan(Mg, T, device_count ? 32 : dbits);
-  // dsum follows hist, ticket follows dsum: one span from dsum to the counters
-  const SortZero z = {ranges, 2 * (int64_t)T, w.dsum, (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
-                      w.pstat, w.gstat, sp.parts, sp.groups, sp.passes};
-  // land the final pass in (keys, ids): start from the alternate buffer when
-  // the pass count is odd
+  const SortPlan lay = sort_plan(capacity, T);
+  // the same choice the first half made on the device
+  const SortMode mode = sort_mode(device_count ? 32 : dbits, ceil_log2((uint32_t)T),
+                                  device_count ? -1 : ceil_log2_u64((uint64_t)N));
+  if (mode.passes != sp.passes) return hipErrorInvalidValue;
   uint64_t* ka = (sp.passes & 1) ? w.keys_alt : keys;
   uint32_t* ia = (sp.passes & 1) ? w.ids_alt : ids;
   uint64_t* kb = (sp.passes & 1) ? keys : w.keys_alt;
   uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
-  // enough blocks for the rows and for a few zeroing strides
-  int64_t nblk = (N + 255) / 256;
-  const int64_t zblk = (2 * (int64_t)T + (int64_t)sp.parts * kRadix + 4095) / 4096;
-  if (nblk < zblk) nblk = zblk;
-  if (nblk < 1) nblk = 1;
-  // key-id words when the sort key, the row index and every pass's digit
-  // fit one word (1080p, 1M rows: 39 + 20 bits, four passes)
-  const int idbits = ceil_log2_u64((uint64_t)N);
-  const bool words = !device_count && idbits + kRadixBits * sp.passes <= 64;
-  hipLaunchKernelGGL(duplicate_kernel, dim3((unsigned)nblk), dim3(256), 0, s, N, means2d, ld, radii,
-                     depths, tiles, offsets, gx, gy, ncams > 1, (const uint32_t*)w.meff, z,
-                     (const uint32_t*)w.keymap, words ? idbits : -1, ka, ia);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
-  if ((e = launch_sort_passes(sp, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum, w.ticket,
-                               w.pstat, w.gstat, ka, ia, kb, ib, words ? idbits : -1, s)) !=
-      hipSuccess)
+  if ((e = launch_sort_passes(sp, lay, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum,
+                               w.ticket, w.pstat, w.gstat, ka, ia, kb, ib,
+                               mode.words ? ceil_log2_u64((uint64_t)N) : -1, s)) != hipSuccess)
     return e;
   const unsigned rblocks = (unsigned)((Mg + 255) / 256);
   hipLaunchKernelGGL(ranges_kernel, dim3(rblocks), dim3(256), 0, s, keys, w.meff, (uint32_t)T,
@@ -1202,8 +1276,13 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
     ka = w.keys_alt; ia = w.vals_alt; kb = keys; ib = vals;
   }
   if ((e = fill_u32(w.meff, 1, (uint32_t)n, s)) != hipSuccess) return e;
-  return launch_sort_passes(w.sp, w.meff, nullptr, w.hist, w.dsum, w.ticket, w.pstat, w.gstat,
-                            ka, ia, kb, ib, -1, s);
+  hipLaunchKernelGGL(sort_first_hist_kernel, dim3((unsigned)w.sp.hblocks), dim3(kHistThreads), 0,
+                     s, (const uint64_t*)ka, (const uint64_t*)ka, (const uint32_t*)w.meff,
+                     (const uint32_t*)nullptr, 0, -1, bits, w.dsum, w.ticket + kMaxPasses,
+                     w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_sort_passes(w.sp, w.sp, w.meff, nullptr, w.hist, w.dsum, w.ticket, w.pstat,
+                            w.gstat, ka, ia, kb, ib, -1, s);
 }
 
 extern "C" size_t gs_scan_workspace_bytes(int64_t n) {
