@@ -102,3 +102,31 @@ def test_binning_without_the_read_back():
                ids=fr.ids[:m].cpu().numpy().view(np.uint32),
                ranges=fr.ranges.cpu().numpy().view(np.uint32))
     _check(out, o, "device count")
+
+
+def test_key_id_words_filling_64_bits():
+    """2^23 + 1 rows (24 row bits) at 1920x1080 (13 tile bits) with depths
+    spanning 18 to 27 bits: four passes, and 24 + 4 x 10 = 64, so the
+    instances travel as key-id words that use all 64 bits (the all-ones
+    padding word's last digit is its top ten bits).  Visible rows sit at the
+    start, just below and at row 2^23 and at the end, so the top row bits
+    vary; every other row is behind the camera."""
+    n = (1 << 23) + 1
+    base, _ = scenes.tiny_scene(n=n, seed=25)
+    cam = scenes.identity_camera(1920, 1080, 1100.0)
+    rng = np.random.default_rng(25)
+    vis = np.unique(np.concatenate([np.arange(0, 3000), np.arange((1 << 23) - 1500, n),
+                                    np.arange(n - 3000, n)]))
+    means = base.means.astype(np.float64)
+    means[:, 2] = -1.0
+    z = 10.0 ** rng.uniform(0.0, 2.0, len(vis))
+    xy = rng.uniform(-0.8, 0.8, (len(vis), 2)) * np.array([960.0, 540.0]) / 1100.0 * z[:, None]
+    means[vis] = np.concatenate([xy, z[:, None]], 1)
+    shift = np.zeros(n)
+    shift[vis] = np.log(z / 20.0)
+    scene = _scene_with(base, means, shift)
+    out = gpu_frame(scene, cam, backward=False)
+    o = oracle.render(scene, cam)
+    assert 18 <= _depth_bits_span(o) <= 27  # 31..40 key bits: four passes
+    assert int(o["bins"]["ids"].max()) == n - 1
+    _check(out, o, "64-bit words")
