@@ -8,12 +8,12 @@
 //   - duplication is balanced by output slot: a workgroup owns 256 Gaussians
 //     and writes all of their instances with consecutive, coalesced stores,
 //     so one Gaussian touching thousands of tiles does not serialise a lane;
-//   - the sort is a onesweep LSD radix sort with 10-bit digits: one pass
-//     computes every digit's global histogram (partial histograms per block,
-//     summed by the digit scan), then each digit pass reads and writes the
-//     keys once.  A workgroup takes its partition from an atomic ticket (so
-//     it only ever waits on partitions already running), ranks its 8192
-//     keys stably with wave64 ballots into LDS histograms, publishes
+//   - the sort is a onesweep LSD radix sort with 10-bit digits: one kernel
+//     histograms the first digit, and each digit pass, which reads and
+//     writes the keys once, also totals the next digit.  A workgroup takes
+//     its partition from an atomic ticket (so it only ever waits on
+//     partitions already running), ranks its 7168 keys stably with wave64
+//     ballots into LDS histograms, publishes
 //     per-digit counts and resolves its global offsets by a two-level
 //     look-back (within a group of 16 partitions, then over groups), then
 //     scatters through LDS so that global writes come out in digit runs.
@@ -21,7 +21,9 @@
 //     finds the smallest and largest depth bits of the rows with tiles, and
 //     the passes sort (tile, depth bits - smallest) in ceil(log2 T) +
 //     bits(largest - smallest) bits; with the depths of a typical frame
-//     spanning ~2^26 fp32 codes that is four passes at 1080p.
+//     spanning ~2^26 fp32 codes that is four passes at 1080p.  Where that
+//     key, the row index and every pass's digit fit one 64-bit word, the
+//     keys travel as such words and the last pass writes keys and ids.
 #include "gs_common.h"
 
 namespace gs {
@@ -97,7 +99,7 @@ constexpr int kScanItems = 8;
 // sort shapes the duplication needs (see the sort below)
 constexpr int kDigitBits = 10;         // bits of a sort pass's digit
 constexpr int kDigits = 1 << kDigitBits;  // radix of a sort pass
-constexpr int kPartKeys = 8192;        // keys per sort partition
+constexpr int kPartKeys = 7168;        // keys per sort partition
 constexpr int kGroupPartitions = 16;   // partitions per look-back group
 constexpr int kDbitsShift = 58;
 constexpr uint64_t kCountBits = (1ull << kDbitsShift) - 1ull;
@@ -448,13 +450,16 @@ __global__ __launch_bounds__(256) void duplicate_kernel(
 // about 39 at 1080p, so four passes.
 constexpr int kRadixBits = kDigitBits;
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kSortItems = 8;
-// 1024-lane workgroups of 8192 keys, one digit per lane in the per-digit
-// phase; ~76 KB of LDS (see sort_pass_kernel).  Large partitions keep the
-// number of partitions, and with it the look-back, short.  (512-lane
-// partitions of 4096 keys, two digits per lane and 43 KB of LDS, sort a
-// 1080p frame in 0.141 instead of 0.098 ms and gain nothing with frames in
-// flight.)
+constexpr int kSortItems = 7;
+// 1024-lane workgroups of 7168 keys, one digit per lane in the per-digit
+// phase; ~66 KB of LDS (see sort_pass_kernel).  Large partitions keep the
+// number of partitions, and with it the look-back, short; at 1080p 7168
+// keys give about 200 partitions, one per CU, and the four passes of a
+// frame's 1.47M keys take 100 us against 104.5 us with 8192 (180
+// partitions, 76 CUs idle) and 100 us with 6144 (longer look-back).
+// (512-lane partitions of 4096 keys, two digits per lane and 43 KB of LDS,
+// sort a 1080p frame in 0.141 instead of 0.098 ms and gain nothing with
+// frames in flight.)
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = 64 * kSortWaves;
 constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
