@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void scan_down_bin_kernel(
 // i seen by camera c, whose means2d are [c][2][ld] and whose tiles are
 // numbered from c * T (batched = true).
 // What the sort and the ranges need zeroed before they run: the ranges, the
-// digit totals and counters, and for each of `passes` passes (laid out for
+// digit totals and the partition tickets, and for each of `passes` passes (laid out for
 // `parts` partitions and `groups` groups) the statuses of the partitions and
 // groups the instance count actually uses.
 struct SortZero {
@@ -522,30 +522,12 @@ __device__ inline uint64_t unpack_key(uint64_t w, KeyMap m, int idbits) {
   return ((mk >> m.dbits) << 32) | (uint64_t)((uint32_t)(mk & dmask) + m.dmin);
 }
 
-// Digit offsets of the first pass: each block histograms a contiguous share
+// Digit totals of the first pass: each block histograms a contiguous share
 // of the keys in LDS and adds it to sum[] (agent-scope atomics, at most
-// kRadix per block); the last block to finish turns the totals into
-// exclusive offsets hist[].  The later passes' offsets come from the pass
-// before (sort_pass_kernel).
+// kRadix per block).  Each pass turns its digit's totals into offsets itself
+// (sort_pass_kernel) and totals the next pass's digit.
 constexpr int kHistThreads = 1024;
 constexpr int kHistItems = 8;
-template <int NT>
-__device__ inline void finish_digit_offsets(uint32_t* sum, uint32_t* hist) {
-  constexpr int DL = kRadix / NT;  // digits per lane: tid, tid + NT, ...
-  uint32_t x[DL];
-#pragma unroll
-  for (int h = 0; h < DL; ++h)
-    x[h] = __hip_atomic_load(&sum[threadIdx.x + h * NT], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t carry = 0;
-#pragma unroll
-  for (int h = 0; h < DL; ++h) {
-    uint64_t excl;
-    const uint64_t t = block_excl_scan_u64<NT / 64>(x[h], excl);
-    hist[threadIdx.x + h * NT] = (uint32_t)(carry + excl);
-    carry += t;
-  }
-}
 
 // The keys are in `keys`, or in `keys_alt` for an odd pass count, as key-id
 // words or not (sort_mode, from the key map unless pass_dbits >= 0; a NULL
@@ -553,15 +535,13 @@ __device__ inline void finish_digit_offsets(uint32_t* sum, uint32_t* hist) {
 __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
     const uint64_t* __restrict__ keys, const uint64_t* __restrict__ keys_alt,
     const uint32_t* __restrict__ meff, const uint32_t* __restrict__ keymap, int tbits,
-    int idbits, int pass_dbits, uint32_t* __restrict__ sum, uint32_t* __restrict__ ctr,
-    uint32_t* __restrict__ hist) {
+    int idbits, int pass_dbits, uint32_t* __restrict__ sum) {
   static_assert(kHistThreads == kRadix, "a lane per digit");
   const uint32_t M = *meff;
   const KeyMap km = load_keymap(keymap);
   const SortMode mode = sort_mode(pass_dbits >= 0 ? pass_dbits : km.dbits, tbits, idbits);
   const uint64_t* __restrict__ kin = (mode.passes & 1) ? keys_alt : keys;
   __shared__ uint32_t s_h[kRadix];
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   s_h[tid] = 0u;
   __syncthreads();
@@ -584,13 +564,6 @@ __global__ __launch_bounds__(kHistThreads) void sort_first_hist_kernel(
   }
   __syncthreads();
   if (s_h[tid]) atomicAdd(&sum[tid], s_h[tid]);
-  // every lane's add has completed before the block counts itself done (a
-  // barrier alone does not wait for outstanding global atomics)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ctr, 1u) == gridDim.x - 1u;
-  __syncthreads();
-  if (s_last) finish_digit_offsets<kHistThreads>(sum, hist);
 }
 
 __device__ inline uint64_t lanemask_lt() {
@@ -612,13 +585,12 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     const uint64_t* __restrict__ kin, const uint32_t* __restrict__ vin,
     uint64_t* __restrict__ kout, uint32_t* __restrict__ vout, const uint32_t* __restrict__ meff,
     int shift, int idbits, const uint32_t* __restrict__ keymap,
-    const uint32_t* __restrict__ digit_offsets,
+    const uint32_t* __restrict__ digit_totals,
     uint32_t* __restrict__ pstat, uint32_t* __restrict__ gstat, uint32_t* __restrict__ ticket,
-    uint32_t* __restrict__ next_sum, uint32_t* __restrict__ next_ctr,
-    uint32_t* __restrict__ next_hist) {
+    uint32_t* __restrict__ next_sum) {
   const uint32_t M = *meff;
   const KeyMap km = load_keymap(keymap);
-  const bool has_next = next_sum != nullptr;  // the next pass's offsets are built here
+  const bool has_next = next_sum != nullptr;  // the next pass's digit is totalled here
   // One buffer in three roles, one after another: the per-wave digit counts
   // (then offsets) while ranking, the keys in local sorted order, then the
   // values.
@@ -631,10 +603,14 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   __shared__ uint32_t s_gbase[kRadix];  // global base minus local start
   __shared__ uint32_t s_next[kRadix];   // histogram of the next pass's digit
   __shared__ uint32_t s_part;
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_part = atomicAdd(ticket, 1u);
+  // this pass's digit totals (complete: the kernel before added them), turned
+  // into offsets beside the partition's own counts below
+  uint32_t dtot[kDL];
+#pragma unroll
+  for (int h = 0; h < kDL; ++h) dtot[h] = digit_totals[tid + h * kSortThreads];
   for (int k = tid; k < kSortWaves * kRadix / 2; k += kSortThreads)
     reinterpret_cast<uint32_t*>(&s_wh[0][0])[k] = 0u;
 #pragma unroll
@@ -710,6 +686,17 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
       uint64_t ex;
       const uint64_t t = block_excl_scan_u64<kSortWaves>(cnt[h], ex);
       start[h] = (uint32_t)(carry + ex);
+      carry += t;
+    }
+  }
+  uint32_t doff[kDL];  // where each of the lane's digits starts in the output
+  {
+    uint64_t carry = 0;
+#pragma unroll
+    for (int h = 0; h < kDL; ++h) {
+      uint64_t ex;
+      const uint64_t t = block_excl_scan_u64<kSortWaves>(dtot[h], ex);
+      doff[h] = (uint32_t)(carry + ex);
       carry += t;
     }
   }
@@ -840,7 +827,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
 #pragma unroll
   for (int h = 0; h < kDL; ++h) {
     const int d = tid + h * kSortThreads;
-    s_gbase[d] = digit_offsets[d] + gp[h] + sin[h] - start[h];
+    s_gbase[d] = doff[h] + gp[h] + sin[h] - start[h];
   }
   __syncthreads();
 
@@ -889,15 +876,6 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
       if (j < nvalid) vout[outj[i]] = s_vals[j];
     }
   }
-  if (!has_next) return;
-  // the last partition to finish turns the next digit's totals into offsets
-  // (each lane's adds to next_sum have completed before the block counts
-  // itself done)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(next_ctr, 1u) == parts - 1u;
-  __syncthreads();
-  if (s_last) finish_digit_offsets<kSortThreads>(next_sum, next_hist);
 }
 #undef GS_LD
 #undef GS_ST
@@ -960,10 +938,8 @@ struct Workspace {
   uint32_t* meff;    // [1] instance count used by the binning kernels
   uint32_t* minmax;  // [nb][2] per scan block: smallest, largest depth bits
   uint32_t* keymap;  // [2] the sort's key map: smallest depth bits, bits kept
-  uint32_t* hist;     // [kMaxPasses][kRadix] digit offsets
   uint32_t* dsum;     // [kMaxPasses][kRadix] digit totals (zeroed per call)
-  uint32_t* ticket;   // [kMaxPasses] partition tickets, then [kMaxPasses]
-                      // completion counters (zeroed per call)
+  uint32_t* ticket;   // [kMaxPasses] partition tickets (zeroed per call)
   uint32_t* pstat;    // [passes][parts][kRadix] partition statuses
   uint32_t* gstat;    // [passes][groups][kRadix] group statuses
   size_t bytes;       // (passes, parts, groups as planned for 32 depth bits)
@@ -987,9 +963,8 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
   w.meff = (uint32_t*)take(sizeof(uint32_t));
   w.minmax = (uint32_t*)take(sizeof(uint32_t) * 2 * (nb ? nb : 1));
   w.keymap = (uint32_t*)take(sizeof(uint32_t) * 2);
-  w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
   w.dsum = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
-  w.ticket = (uint32_t*)take(sizeof(uint32_t) * 2 * kMaxPasses);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
   w.pstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.parts ? sp.parts : 1) * kRadix);
   w.gstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)sp.passes * (sp.groups ? sp.groups : 1) * kRadix);
   w.bytes = off;
@@ -997,18 +972,17 @@ static Workspace carve(void* base, int64_t N, uint64_t capacity, int32_t T) {
 }
 
 // The passes, ping-ponging between (ka, ia) and (kb, ib); an even pass
-// count ends in (ka, ia).  The first digit's offsets are in hist (from
+// count ends in (ka, ia).  The first digit's totals are in dsum (from
 // sort_first_hist_kernel); ticket and the later digits' totals must be zero.
 // Statuses are laid out for lay.parts partitions and lay.groups groups per
 // pass.  idbits >= 0: ka holds key-id words (pass_digit); the passes move
 // only the words, and the last writes the stored keys and the ids.
 static hipError_t launch_sort_passes(const SortPlan& sp, const SortPlan& lay,
-                                     const uint32_t* meff, const uint32_t* keymap, uint32_t* hist,
+                                     const uint32_t* meff, const uint32_t* keymap,
                                      uint32_t* dsum, uint32_t* ticket, uint32_t* pstat,
                                      uint32_t* gstat, uint64_t* ka, uint32_t* ia, uint64_t* kb,
                                      uint32_t* ib, int idbits, hipStream_t s) {
   hipError_t e;
-  uint32_t* ctr = ticket + kMaxPasses;
   const bool words = idbits >= 0;
   const int s0 = words ? idbits : 0;
   for (int p = 0; p < sp.passes; ++p) {
@@ -1017,19 +991,17 @@ static hipError_t launch_sort_passes(const SortPlan& sp, const SortPlan& lay,
       hipLaunchKernelGGL(sort_pass_kernel<true>, dim3(sp.parts), dim3(kSortThreads), 0, s,
                          (const uint64_t*)ka, (const uint32_t*)nullptr, kb,
                          next ? (uint32_t*)nullptr : ib, meff, s0 + p * kRadixBits, idbits,
-                         keymap, (const uint32_t*)(hist + p * kRadix),
+                         keymap, (const uint32_t*)(dsum + p * kRadix),
                          pstat + (size_t)p * lay.parts * kRadix,
                          gstat + (size_t)p * lay.groups * kRadix, ticket + p,
-                         next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
-                         next ? hist + (p + 1) * kRadix : nullptr);
+                         next ? dsum + (p + 1) * kRadix : nullptr);
     else
       hipLaunchKernelGGL(sort_pass_kernel<false>, dim3(sp.parts), dim3(kSortThreads), 0, s,
                          (const uint64_t*)ka, (const uint32_t*)ia, kb, ib, meff, p * kRadixBits,
-                         0, keymap, (const uint32_t*)(hist + p * kRadix),
+                         0, keymap, (const uint32_t*)(dsum + p * kRadix),
                          pstat + (size_t)p * lay.parts * kRadix,
                          gstat + (size_t)p * lay.groups * kRadix, ticket + p,
-                         next ? dsum + (p + 1) * kRadix : nullptr, next ? ctr + p + 1 : nullptr,
-                         next ? hist + (p + 1) * kRadix : nullptr);
+                         next ? dsum + (p + 1) * kRadix : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint64_t* tk = ka; ka = kb; kb = tk;
     uint32_t* ti = ia; ia = ib; ib = ti;
@@ -1127,9 +1099,9 @@ extern "C" hipError_t gs_launch_bin_front(int64_t N, int64_t ld, const float* me
   if (capacity > 0) {
     // statuses laid out for the capacity and 32 depth bits (the most passes)
     const SortPlan lay = sort_plan(capacity, T);
-    // dsum follows hist, ticket follows dsum: one span from dsum to the counters
+    // ticket follows dsum: one span from the digit totals to the tickets
     const SortZero z = {ranges, 2 * (int64_t)T, w.dsum,
-                        (int64_t)(w.ticket + 2 * kMaxPasses - w.dsum), w.pstat, w.gstat,
+                        (int64_t)(w.ticket + kMaxPasses - w.dsum), w.pstat, w.gstat,
                         lay.parts, lay.groups, lay.passes};
     const int tbits = ceil_log2((uint32_t)T);
     // key-id words only when the host knows the pass count (see sort_mode)
@@ -1151,7 +1123,7 @@ extern "C" hipError_t gs_launch_bin_front(int64_t N, int64_t ld, const float* me
     hipLaunchKernelGGL(sort_first_hist_kernel, dim3(hblocks), dim3(kHistThreads), 0, s,
                        (const uint64_t*)keys, (const uint64_t*)w.keys_alt,
                        (const uint32_t*)w.meff, (const uint32_t*)w.keymap, tbits, idbits,
-                       pass_dbits, w.dsum, w.ticket + kMaxPasses, w.hist);
+                       pass_dbits, w.dsum);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (!totals_host) return hipSuccess;  // the count stays on the device
@@ -1188,7 +1160,7 @@ extern "C" hipError_t gs_launch_bin_back(int64_t N, int32_t W, int32_t H, int nc
   uint32_t* ia = (sp.passes & 1) ? w.ids_alt : ids;
   uint64_t* kb = (sp.passes & 1) ? keys : w.keys_alt;
   uint32_t* ib = (sp.passes & 1) ? ids : w.ids_alt;
-  if ((e = launch_sort_passes(sp, lay, w.meff, (const uint32_t*)w.keymap, w.hist, w.dsum,
+  if ((e = launch_sort_passes(sp, lay, w.meff, (const uint32_t*)w.keymap, w.dsum,
                                w.ticket, w.pstat, w.gstat, ka, ia, kb, ib,
                                mode.words ? ceil_log2_u64((uint64_t)N) : -1, s)) != hipSuccess)
     return e;
@@ -1208,7 +1180,6 @@ struct PairSortWs {
   uint64_t* keys_alt;
   uint32_t* vals_alt;
   uint32_t* meff;
-  uint32_t* hist;
   uint32_t* dsum;
   uint32_t* ticket;
   uint32_t* pstat;
@@ -1230,9 +1201,8 @@ static PairSortWs carve_pairsort(void* base, uint64_t n, int bits) {
   w.keys_alt = (uint64_t*)take(sizeof(uint64_t) * (n ? n : 1));
   w.vals_alt = (uint32_t*)take(sizeof(uint32_t) * (n ? n : 1));
   w.meff = (uint32_t*)take(sizeof(uint32_t));
-  w.hist = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
   w.dsum = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses * kRadix);
-  w.ticket = (uint32_t*)take(sizeof(uint32_t) * 2 * kMaxPasses);
+  w.ticket = (uint32_t*)take(sizeof(uint32_t) * kMaxPasses);
   w.pstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.sp.passes * (w.sp.parts ? w.sp.parts : 1) *
                             kRadix);
   w.gstat = (uint32_t*)take(sizeof(uint32_t) * (size_t)w.sp.passes * (w.sp.groups ? w.sp.groups : 1) *
@@ -1256,7 +1226,7 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   hipError_t e;
   {
     Segs sg = {{w.dsum, w.pstat, w.gstat, w.gstat},
-               {(int64_t)(w.ticket + 2 * kMaxPasses - w.dsum),
+               {(int64_t)(w.ticket + kMaxPasses - w.dsum),
                 (int64_t)w.sp.passes * w.sp.parts * kRadix,
                 (int64_t)w.sp.passes * w.sp.groups * kRadix, 0}};
     int64_t blocks = (sg.n[1] + 255) / 256;
@@ -1283,10 +1253,9 @@ extern "C" hipError_t gs_pairsort(uint64_t* keys, uint32_t* vals, uint64_t n, in
   if ((e = fill_u32(w.meff, 1, (uint32_t)n, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(sort_first_hist_kernel, dim3((unsigned)w.sp.hblocks), dim3(kHistThreads), 0,
                      s, (const uint64_t*)ka, (const uint64_t*)ka, (const uint32_t*)w.meff,
-                     (const uint32_t*)nullptr, 0, -1, bits, w.dsum, w.ticket + kMaxPasses,
-                     w.hist);
+                     (const uint32_t*)nullptr, 0, -1, bits, w.dsum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_sort_passes(w.sp, w.sp, w.meff, nullptr, w.hist, w.dsum, w.ticket, w.pstat,
+  return launch_sort_passes(w.sp, w.sp, w.meff, nullptr, w.dsum, w.ticket, w.pstat,
                             w.gstat, ka, ia, kb, ib, -1, s);
 }
 
