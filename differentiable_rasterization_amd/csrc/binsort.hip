@@ -640,12 +640,19 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
 #pragma unroll
   for (int it = 0; it < kSortItems; ++it) {
     const uint32_t d = pass_digit<kIdInKey>(k[it], km, shift);
-    uint64_t match = ~0ull;
+    // the lanes whose digit equals this lane's: per bit, the ballot where
+    // the lane's bit is set, its complement where it is clear, i.e. the
+    // complement of (ballot xor m) with m the bit spread over a word, on the
+    // two halves of the mask
+    uint32_t mlo = ~0u, mhi = ~0u;
 #pragma unroll
     for (int b = 0; b < kRadixBits; ++b) {
-      const uint64_t bal = __ballot((d >> b) & 1u);
-      match &= ((d >> b) & 1u) ? bal : ~bal;
+      const uint32_t m = (uint32_t)((int32_t)(d << (31 - b)) >> 31);
+      const uint64_t bal = __ballot(m != 0u);
+      mlo &= ~((uint32_t)bal ^ m);
+      mhi &= ~((uint32_t)(bal >> 32) ^ m);
     }
+    const uint64_t match = ((uint64_t)mhi << 32) | mlo;
     const uint32_t before = s_wh[wave][d];
     rank[it] = before + (uint32_t)__popcll(match & lt);
     const int leader = __ffsll((long long)match) - 1;
