@@ -730,6 +730,13 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
 #pragma unroll
   for (int h = 0; h < kDL; ++h)
     GS_ST(&pstat[(size_t)part * kRadix + tid + h * kSortThreads], kFlagAgg | mine[h]);
+  // while the other partitions' counts travel: the keys into LDS in local
+  // sorted order (the buffer held the per-wave counts, which every wave has
+  // read once all have passed the barrier)
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kSortItems; ++it)
+    if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_buf[rank[it]] = k[it];
   uint32_t sin[kDL];
 #pragma unroll
   for (int h = 0; h < kDL; ++h) sin[h] = 0;
@@ -838,12 +845,9 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   }
   __syncthreads();
 
-  // keys (then values) through LDS in local sorted order; written out in
-  // that order, consecutive lanes hit consecutive slots of a digit run
-#pragma unroll
-  for (int it = 0; it < kSortItems; ++it)
-    if (wbase + (uint32_t)it * 64u + (uint32_t)lane < M) s_buf[rank[it]] = k[it];
-  __syncthreads();
+  // keys (then values) out of LDS in local sorted order; written out in
+  // that order, consecutive lanes hit consecutive slots of a digit run (the
+  // barrier after the offsets also covers the keys' LDS writes above)
   if constexpr (kIdInKey) {
     const uint64_t idmask = (1ull << idbits) - 1ull;  // idbits < 64
 #pragma unroll
