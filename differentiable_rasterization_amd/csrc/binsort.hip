@@ -686,6 +686,15 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
     }
     cnt[h] = c;
   }
+  // publish this partition's digit counts (padding keys, all in the last
+  // digit, left out) as soon as they are known
+  const uint32_t pad = (uint32_t)kPart - nvalid;
+#pragma unroll
+  for (int h = 0; h < kDL; ++h) {
+    const int d = tid + h * kSortThreads;
+    mine[h] = (d == kRadix - 1) ? cnt[h] - pad : cnt[h];
+    GS_ST(&pstat[(size_t)part * kRadix + d], kFlagAgg | mine[h]);
+  }
   {
     uint64_t carry = 0;
 #pragma unroll
@@ -707,13 +716,8 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
       carry += t;
     }
   }
-  const uint32_t pad = (uint32_t)kPart - nvalid;  // padding keys sit in the last digit
 #pragma unroll
-  for (int h = 0; h < kDL; ++h) {
-    const int d = tid + h * kSortThreads;
-    s_start[d] = (uint16_t)start[h];
-    mine[h] = (d == kRadix - 1) ? cnt[h] - pad : cnt[h];
-  }
+  for (int h = 0; h < kDL; ++h) s_start[tid + h * kSortThreads] = (uint16_t)start[h];
   __syncthreads();
   // each key's position in local sorted order (the counts' buffer is free
   // after this)
@@ -724,12 +728,9 @@ __global__ __launch_bounds__(kSortThreads) void sort_pass_kernel(
   }
 
   // look-back, level 1: the earlier partitions of this group (each
-  // publishes its counts without waiting)
+  // published its counts above without waiting)
   const uint32_t g = part / kGroupParts, r = part % kGroupParts;
   const bool glast = r == kGroupParts - 1 || part == parts - 1;
-#pragma unroll
-  for (int h = 0; h < kDL; ++h)
-    GS_ST(&pstat[(size_t)part * kRadix + tid + h * kSortThreads], kFlagAgg | mine[h]);
   // while the other partitions' counts travel: the keys into LDS in local
   // sorted order (the buffer held the per-wave counts, which every wave has
   // read once all have passed the barrier)
