@@ -422,14 +422,16 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
       const float alpha = fminf(oG, amax);
       const bool ok = act & !done & !(alpha < amin);
       const float Tn = T * (1.0f - alpha);
-      const bool low = Tn < Tmin;
-      const bool blend = ok & !low;
+      // stop (ok and T would fall below T_min) or blend (ok otherwise): one
+      // compare, the other mask by exclusive or
+      const bool stop = ok & (Tn < Tmin);
+      const bool blend = ok ^ stop;
       if (kStats) {
         n_eval += act ? 1u : 0u;
         n_blend += blend ? 1u : 0u;
-        stop_at = (ok & low) ? base + (uint32_t)k : stop_at;
+        stop_at = stop ? base + (uint32_t)k : stop_at;
       }
-      done = done | (ok & low);
+      done = done | stop;
       const float w = blend ? alpha * T : 0.0f;
       C0 = fmaf(s.r, w, C0);
       C1 = fmaf(s.g, w, C1);
