@@ -38,11 +38,11 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # VALU slots of the compositing inner loops, counted in the gfx950 assembly
 # of raster.hip (a quarter-rate v_exp_f32 / v_rcp_f32 counts four slots):
-#   forward: 50 VALU and two v_exp_f32 per two unrolled pairs -> 29 / pair;
+#   forward: 49 VALU and two v_exp_f32 per two unrolled pairs -> 28.5 / pair;
 #   backward: 20 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (28
 #   slots); a wavefront with a hit on the splat adds 13 VALU of gradient
 #   terms and 35 of the nine-field reduction (lane swaps + DPP row scan).
-FWD_SLOTS_PER_PAIR = 29.0
+FWD_SLOTS_PER_PAIR = 28.5
 BWD_EVAL_SLOTS = 28.0
 BWD_GRAD_SLOTS = 13.0
 BWD_REDUCE_SLOTS = 35.0
