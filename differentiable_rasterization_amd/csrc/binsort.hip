@@ -13,10 +13,10 @@
 //     writes the keys once, also totals the next digit.  A workgroup takes
 //     its partition from an atomic ticket (so it only ever waits on
 //     partitions already running), ranks its 7168 keys stably with wave64
-//     ballots into LDS histograms, publishes
-//     per-digit counts and resolves its global offsets by a two-level
-//     look-back (within a group of 16 partitions, then over groups), then
-//     scatters through LDS so that global writes come out in digit runs.
+//     ballots into LDS histograms, publishes per-digit counts and resolves
+//     its global offsets by a two-level look-back (within a group of 16
+//     partitions, then over groups), then scatters through LDS so that
+//     global writes come out in digit runs.
 //     Only the bits that vary within the frame are sorted: the scan also
 //     finds the smallest and largest depth bits of the rows with tiles, and
 //     the passes sort (tile, depth bits - smallest) in ceil(log2 T) +
@@ -346,9 +346,9 @@ __global__ __launch_bounds__(256) void scan_down_bin_kernel(
 // i seen by camera c, whose means2d are [c][2][ld] and whose tiles are
 // numbered from c * T (batched = true).
 // What the sort and the ranges need zeroed before they run: the ranges, the
-// digit totals and the partition tickets, and for each of `passes` passes (laid out for
-// `parts` partitions and `groups` groups) the statuses of the partitions and
-// groups the instance count actually uses.
+// digit totals and the partition tickets, and for each of `passes` passes
+// (laid out for `parts` partitions and `groups` groups) the statuses of the
+// partitions and groups the instance count actually uses.
 struct SortZero {
   uint32_t* ranges;
   int64_t nranges;
@@ -457,9 +457,9 @@ constexpr int kSortItems = 7;
 // keys give about 200 partitions, one per CU, and the four passes of a
 // frame's 1.47M keys take 100 us against 104.5 us with 8192 (180
 // partitions, 76 CUs idle) and 100 us with 6144 (longer look-back).
-// (512-lane partitions of 4096 keys, two digits per lane and 43 KB of LDS,
-// sort a 1080p frame in 0.141 instead of 0.098 ms and gain nothing with
-// frames in flight.)
+// (512-lane partitions of 3584 or 4096 keys, two digits per lane and 38-43
+// KB of LDS: binning a 1080p frame takes 0.155 or 0.172 instead of 0.138 ms
+// one frame at a time, with no gain with frames in flight.)
 constexpr int kSortWaves = 16;
 constexpr int kSortThreads = 64 * kSortWaves;
 constexpr int kPart = kSortThreads * kSortItems;  // keys per partition
