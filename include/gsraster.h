@@ -187,7 +187,7 @@ GS_API gs_status gs_bin_and_sort_device(int64_t N, int64_t ld, const float* mean
  * a 64 MiB array inside the library instead of a workspace argument.  The
  * caller still passes every input and output.  Limit: the
  * gs_bin_and_sort_workspace_size() of (N, capacity, width, height) must be
- * at most 64 MiB (capacity up to about 4.8 million instances for a million
+ * at most 64 MiB (capacity up to about 4.4 million instances for a million
  * Gaussians at 1920x1080); larger requests return GS_ERR_INVALID_ARGUMENT
  * before anything runs.  The call allocates nothing: each device holds its
  * own copy of the array from the library's first use on it until the
