@@ -1029,15 +1029,26 @@ extern "C" size_t gs_binsort_workspace_bytes(int64_t N, uint64_t capacity, int32
 
 namespace gs {
 // One event per device and host thread marks the count's copy to the host
-// (a thread's calls wait on their own copies only).
-static hipError_t count_copy_event(hipEvent_t* ev) {
+// (a thread's calls wait on their own copies only); it is created on the
+// device of stream s, which need not be the current one.
+static hipError_t count_copy_event(hipStream_t s, hipEvent_t* ev) {
   static thread_local hipEvent_t evs[64] = {};
-  int dev = 0;
+  int cur = 0;
+  hipDevice_t dev = 0;
   hipError_t e;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (!s) dev = cur;  // the null stream: the current device's
+  else if ((e = hipStreamGetDevice(s, &dev)) != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!evs[dev] && (e = hipEventCreateWithFlags(&evs[dev], hipEventDisableTiming)) != hipSuccess)
-    return e;
+  if (!evs[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = hipEventCreateWithFlags(&evs[dev], hipEventDisableTiming);
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+  }
   *ev = evs[dev];
   return hipSuccess;
 }
@@ -1102,7 +1113,7 @@ extern "C" hipError_t gs_launch_bin_front(int64_t N, int64_t ld, const float* me
   if (totals_host) {
     // straight into the caller's host words: page-locked memory there makes
     // this a direct transfer instead of a staged one
-    if ((e = count_copy_event(&ev)) != hipSuccess) return e;
+    if ((e = count_copy_event(s, &ev)) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(totals_host, w.total, sizeof(uint64_t) * (vis ? 2 : 1),
                             hipMemcpyDeviceToHost, s)) != hipSuccess)
       return e;
