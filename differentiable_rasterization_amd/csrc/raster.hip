@@ -24,7 +24,8 @@
 // (skipped with a ballot when no lane of the wave touched the splat); the
 // wave partials meet in LDS and the tile stores its sums for the splat, with
 // a plain 48-byte store, into the instance's own slot (the Gaussian's offset
-// plus the tile's index in its rect).  A second kernel adds each Gaussian's
+// plus the tile's index in its rect; slots are packed 48 bytes apart, so no
+// line carries unused bytes).  A second kernel adds each Gaussian's
 // slots in a fixed order.  No global atomics: device-scope float atomics go
 // to memory on this part, and a fixed order makes gradients reproducible.
 //
@@ -629,9 +630,9 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
         instance_slot(a.x, a.y, __float_as_int(c.y), offsets[id], tx, ty, gx, gy);
     if (slot < capacity) {
       const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      partials[4 * slot + 0] = z;
-      partials[4 * slot + 1] = z;
-      partials[4 * slot + 2] = z;
+      partials[3 * slot + 0] = z;
+      partials[3 * slot + 1] = z;
+      partials[3 * slot + 2] = z;
     }
   }
 
@@ -770,10 +771,10 @@ __global__ __launch_bounds__(256) void raster_bwd_kernel(
       const uint64_t slot =
           instance_slot(s_sp[tid].u, s_sp[tid].v, my_rad, my_off, tx, ty, gx, gy);
       if (slot < capacity) {
-        partials[4 * slot + 0] = make_float4(gu, gv, -0.5f * acc[2], -acc[3]);
-        partials[4 * slot + 1] =
+        partials[3 * slot + 0] = make_float4(gu, gv, -0.5f * acc[2], -acc[3]);
+        partials[3 * slot + 1] =
             make_float4(-0.5f * acc[4], acc[5] * s_sp[tid].z, acc[6], acc[7]);
-        partials[4 * slot + 2] =
+        partials[3 * slot + 2] =
             make_float4(acc[8], kAbs ? acc[kF - 2] : 0.0f, kAbs ? acc[kF - 1] : 0.0f, 0.0f);
       }
     }
@@ -860,13 +861,13 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
         // four slots' loads in flight before their (in-order) additions
         uint32_t k = 0;
         for (; k + 4 <= cnt; k += 4) {
-          const float4* p = partials + 4 * (base + k);
+          const float4* p = partials + 3 * (base + k);
           float4 x[4][3];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            x[j][0] = p[4 * j];
-            x[j][1] = p[4 * j + 1];
-            x[j][2] = p[4 * j + 2];
+            x[j][0] = p[3 * j];
+            x[j][1] = p[3 * j + 1];
+            x[j][2] = p[3 * j + 2];
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -875,7 +876,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
             a[8] += x[j][2].x; a[9] += x[j][2].y; a[10] += x[j][2].z;
           }
         }
-        for (; k < cnt; ++k) add_rec(a, partials + 4 * (base + k));
+        for (; k < cnt; ++k) add_rec(a, partials + 3 * (base + k));
       }
       store_grads(g, r, a, mode, cnt > 0);
     }
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     const uint32_t cnt = tiles[gi];
     const uint64_t base = offsets[gi];
     float a[kFieldsAbs] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    for (uint32_t k = (uint32_t)t; k < cnt; k += 256u) add_rec(a, partials + 4 * (base + k));
+    for (uint32_t k = (uint32_t)t; k < cnt; k += 256u) add_rec(a, partials + 3 * (base + k));
 #pragma unroll
     for (int q = 0; q < kFieldsAbs; ++q) s_red[q][t] = a[q];
     __syncthreads();

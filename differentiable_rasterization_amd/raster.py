@@ -713,8 +713,8 @@ class Frame:
         self.capacity = int(capacity)
         self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
         self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
-        # per-instance 64-byte gradient slots of the compositing backward
-        self.partials = torch.empty((self.capacity, 16), dtype=torch.float32, device=self.device)
+        # per-instance 48-byte gradient slots of the compositing backward
+        self.partials = torch.empty((self.capacity, 12), dtype=torch.float32, device=self.device)
         self.ws_bytes = gs_bin_and_sort_workspace_size(self.ld, self.capacity, self.W, self.H)
         self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8, device=self.device)
         # 256-byte alignment of the workspace start
@@ -902,7 +902,7 @@ class BatchFrame:
         self.capacity = int(capacity)
         self.keys = torch.zeros((self.capacity,), dtype=torch.int64, device=self.device)
         self.ids = torch.zeros((self.capacity,), dtype=torch.int32, device=self.device)
-        self.partials = torch.empty((self.capacity, 16), dtype=torch.float32, device=self.device)
+        self.partials = torch.empty((self.capacity, 12), dtype=torch.float32, device=self.device)
         self.ws_bytes = gs_bin_and_sort_batched_workspace_size(self.C, self.ld, self.capacity,
                                                                self.W, self.H)
         self.workspace = torch.zeros((self.ws_bytes + 256,), dtype=torch.uint8,

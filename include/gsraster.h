@@ -287,7 +287,7 @@ GS_API gs_status gs_rasterize_fwd_loss(int64_t N, int64_t ld, int32_t width, int
  * q = A dx^2 + 2B dx dy + C dy^2), opacity and colour, given dL_dimage
  * [H][W][3].  Each tile writes its sums for each of its Gaussians with a
  * plain store into that instance's slot of partials (offsets[i] + k for the
- * k-th tile, row-major, of Gaussian i's rect; partials [capacity][16] floats,
+ * k-th tile, row-major, of Gaussian i's rect; partials [capacity][12] floats,
  * 64-byte aligned, capacity >= num_instances); a segmented reduction then
  * adds each Gaussian's slots, in slot order, into dL_dmeans2d [2][ld],
  * dL_dconics [3][ld], dL_dopacities [ld], dL_dcolors [3][ld].  There are no

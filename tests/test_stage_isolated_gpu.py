@@ -80,7 +80,7 @@ def run_case(name):
     dl = oracle.loss_grad_image(orc["raster"]["image"], scenes.target_image(cam, 7), kind)
     bw = oracle.backward(scene, cam, orc, dl, None, bg, with_abs=True)
     cap = max(M, 1)
-    partials = torch.empty((cap, 16), dtype=torch.float32, device="cuda")
+    partials = torch.empty((cap, 12), dtype=torch.float32, device="cuda")
     g2 = raster.Grad2D(f32(2, ld), f32(3, ld), f32(ld), f32(3, ld), f32(2, ld))
     raster.gs_rasterize_bwd(N, ld, W, H, ranges, ids, sp, offsets, tiles, M, bg, st, final_T,
                             last, _dev(torch, dl), ws, wsb, 1, partials, cap, g2)
