@@ -12,8 +12,13 @@ own HIP stream with its own buffers and gradients, step i on stream
 i mod --in-flight; the per-stage times, the roofline and the "serial" figure
 come from passes with one frame at a time.
 
+The default line also carries short legs for the other workloads: the
+100k-Gaussian box at 1080p, the 3M-Gaussian 4K inference batch of four poses
+(forward with depth and alpha), and the 6M-Gaussian heavy-tailed shard's
+step (eight cameras fwd+bwd, then densify/prune).
+
   python bench.py [--steps K] [--warmup W] [--config cluster_1m_1080p]
-                  [--in-flight F] [--no-cpu-baseline] [--gpus 1]
+                  [--in-flight F] [--no-cpu-baseline] [--no-config-legs] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -303,9 +308,10 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
     # forward + backward of a group: the L1 loss gradient over the group's
     # images, the batched compositing backward, and the projection backward
     # summed over the group's cameras
-    tg = [torch.from_numpy(np.stack([scenes_target(c, k) for k, c in
-                                     enumerate(cams[i:i + batch])])).cuda()
-          for i in range(0, len(cams) - batch + 1, batch)]
+    tg = [] if depth_alpha else [
+        torch.from_numpy(np.stack([scenes_target(c, k) for k, c in
+                                   enumerate(cams[i:i + batch])])).cuda()
+        for i in range(0, len(cams) - batch + 1, batch)]
 
     def group_fb(b, grp, t):
         # the L1 loss gradient fused into the batch's compositing forward
@@ -319,7 +325,8 @@ def fwd_batch_bench(args, scene, cams, batch, depth_alpha):
     # the groups are independent too: --in-flight of them at once, each on
     # its own stream with its own buffers, group k on stream k mod in-flight
     nf = max(1, args.in_flight)
-    bfs = [bf] + [raster.BatchFrame(g.ld, scene.sh_degree, W, H, batch) for _ in range(nf - 1)]
+    bfs = [bf] + ([] if depth_alpha else
+                  [raster.BatchFrame(g.ld, scene.sh_degree, W, H, batch) for _ in range(nf - 1)])
     streams = [torch.cuda.Stream() for _ in range(nf)]
 
     issued = [0]
@@ -548,6 +555,118 @@ def box_100k_bench(args):
                                 "not a target"}}
 
 
+def cluster_3m_4k_bench(args):
+    """The inference batch: 3M clustered Gaussians (SH3) rendered at
+    3840x2160 for four seeded poses, forward only, with the depth and alpha
+    buffers written beside the fp32 image.  Frames/s through the
+    single-camera calls (one pose at a time) and through the batched calls
+    (the four poses in one launch per stage)."""
+    import torch
+    from differentiable_rasterization_amd import scenes
+    scene, cams, _ = scenes.make_config("cluster_3m_4k")
+    r = fwd_batch_bench(args, scene, cams, len(cams), depth_alpha=True)
+    out = {"workload": "cluster_3m_4k", "gaussians": scene.n, "width": cams[0].width,
+           "height": cams[0].height, "sh_degree": scene.sh_degree, "poses": len(cams)}
+    out.update(r)
+    del scene
+    torch.cuda.empty_cache()
+    return out
+
+
+def heavy_6m_step_bench(args, steps=3, warmup=1):
+    """The 6M-Gaussian heavy-tailed shard (SH3, Student-t log-scales), one
+    step at a time: each of its eight seeded 1024x1024 cameras goes forward
+    and backward (L1) through the single-camera calls, the 3D gradients
+    summed over the cameras in the buffers (accumulate), then
+    gs_densify_prune clones the 2% of rows with the largest mean-gradient
+    norm and drops those with opacity below 0.005 into the second parameter
+    set, which the next step renders, so the count changes from step to
+    step.  One frame buffer on one stream, since the cameras add into the
+    same gradient sums; the densify call ends with its count read-back."""
+    import torch
+    from differentiable_rasterization_amd import raster, scenes
+    scene, cams, _ = scenes.make_config("heavy_6m_1024")
+    deg = scene.sh_degree
+    K = (deg + 1) ** 2
+    frac, min_op = 0.02, 0.005
+    # room for every step's clones: N grows by at most round(frac N) a step
+    ld = scene.n
+    for _ in range(warmup + steps):
+        ld += int(np.floor(float(np.float32(frac)) * ld + 0.5))
+    z = lambda P: torch.zeros((P, ld), dtype=torch.float32, device="cuda")
+    start = raster.Gaussians.from_scene(scene, ld=ld)
+    sets = [raster.Gaussians(z(3), z(3), z(4), z(1), z(3 * K), deg, 0) for _ in range(2)]
+    n0 = scene.n
+    del scene
+    W, H = cams[0].width, cams[0].height
+    gc = [raster.make_camera(c) for c in cams]
+    tg = [torch.from_numpy(scenes.target_image(c, k)).cuda() for k, c in enumerate(cams)]
+    fr = raster.Frame(ld, deg, W, H, capacity=8 * ld)
+    ws_bytes = raster.gs_densify_prune_workspace_size(ld, frac)
+    ws_buf = torch.empty((ws_bytes + 256,), dtype=torch.uint8, device="cuda")
+    off = (-ws_buf.data_ptr()) % 256
+    ws = ws_buf[off:off + ws_bytes]
+
+    def step(k):
+        """Returns (N in, N out, instances over the cameras, fwd+bwd ms,
+        densify ms)."""
+        g, h = sets[k % 2], sets[(k + 1) % 2]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m = 0
+        for c, (cam, t) in enumerate(zip(gc, tg)):
+            fr.project(g, cam)
+            m += fr.bin_and_sort(g)
+            fr.rasterize_loss(g, t, 1)
+            fr.backward(g, accumulate=1 if c else 0)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        assert raster.gs_densify_prune_workspace_size(g.N, frac) <= ws_bytes
+        h.N = raster.gs_densify_prune(g.N, g.ld, deg, g.means, g.scales, g.quats,
+                                      g.opacities, g.sh, fr.g_means, frac, min_op, ld,
+                                      h.means, h.scales, h.quats, h.opacities, h.sh, ws,
+                                      ws_bytes)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        return g.N, h.N, m, 1e3 * (t1 - t0), 1e3 * (t2 - t1)
+
+    def restart():
+        for name in ("means", "scales", "quats", "opacities", "sh"):
+            getattr(sets[0], name).copy_(getattr(start, name))
+        sets[0].N = start.N
+
+    # the instance count grows from step to step (the clones of large
+    # splats add tiles): an untimed pass over the same steps sizes the sort
+    # buffers for the largest, then the timed pass repeats the steps from
+    # the starting parameters (the same counts, bit for bit)
+    restart()
+    for k in range(warmup + steps):
+        step(k)
+    cap0 = fr.capacity
+    restart()
+    rows = []
+    for k in range(warmup + steps):
+        r = step(k)
+        if k >= warmup:
+            rows.append(r)
+    total = sum(r[3] + r[4] for r in rows) * 1e-3
+    out = {"workload": "heavy_6m_1024", "gaussians": n0, "width": W, "height": H,
+           "sh_degree": deg, "cameras_per_step": len(gc), "steps": steps, "warmup": warmup,
+           "steps_per_s": round(steps / total, 3),
+           "frames_per_s": round(steps * len(gc) / total, 2),
+           "per_step": [{"gaussians_in": r[0], "gaussians_out": r[1], "instances": r[2],
+                         "fwdbwd_ms": round(r[3], 3), "densify_ms": round(r[4], 3)}
+                        for r in rows],
+           "sort_buffers_regrown": fr.capacity != cap0,
+           "clone_fraction": frac, "min_opacity": min_op,
+           "form": "per step: fwd+bwd of the 8 cameras (gradients summed), then densify/prune "
+                   "into the next step's parameters; the clones of the largest-gradient "
+                   "rows add instances, so each step renders more than the last"}
+    del sets, start, fr, ws_buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,6 +694,8 @@ def main():
                     help="only the forward of the poses in batches of --batch (single-camera "
                          "calls against batched calls), e.g. with --config cluster_3m_4k")
     ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--no-config-legs", action="store_true",
+                    help="leave out the 3M/4K inference batch and the 6M densify step legs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -858,6 +979,9 @@ def main():
         out["graph"] = graph_line
     if not args.no_train_step and args.config == "cluster_1m_1080p":
         out["box_100k_1080p"] = box_100k_bench(args)
+        if not args.no_config_legs:
+            out["cluster_3m_4k"] = cluster_3m_4k_bench(args)
+            out["heavy_6m_1024"] = heavy_6m_step_bench(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, cams, targets_np, loss_kind, args.cpu_frames,
                                            args.cpu_frames_one_thread)
