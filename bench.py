@@ -748,14 +748,6 @@ def main():
     Px = W * H
     tile_bits = int(np.ceil(np.log2(max(T, 2))))
 
-    def sort_passes_of(fr):
-        """The radix passes the sort runs on this frame: 10-bit digits over
-        the tile bits and the bits that the depths of the rows with tiles
-        span."""
-        has = (fr.tiles[:N] > 0).cpu().numpy()
-        db = fr.depths[:N].cpu().numpy().view(np.uint32)[has].astype(np.int64)
-        span = int(db.max() - db.min()) if db.size else 0
-        return max(1, -(-(tile_bits + span.bit_length()) // 10))
     names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "rasterize_bwd", "project_bwd"]
 
     def step(i, ev=None, fr=fr):
@@ -780,30 +772,50 @@ def main():
             ev[5].record()
         return fr.M
 
-    # workload statistics per pose (one untimed pass with the counting variants)
-    cnt = torch.zeros(8, dtype=torch.int64, device="cuda")
-    stats = []
+    # workload statistics per pose: one untimed pass with the counting
+    # variants, each pose on the frame and stream the timed steps give it.
+    # What the statistics need is copied on the device and analysed on the
+    # host after the timed passes, so the warm-up steps follow this pass
+    # with no idle gap and every frame's buffers have been used before.
+    raw = []
     for i in range(P):
-        step(i)
-        cnt.zero_()
-        fr.rasterize(g, counters=cnt[0:4])
-        fr.rasterize_backward(g, counters=cnt[4:8])
-        torch.cuda.synchronize()
-        c = cnt.cpu().numpy()
-        V = int((fr.radii[:N] > 0).sum().item())
-        rng = fr.ranges.cpu().numpy().view(np.uint32).astype(np.int64)
+        k = i % nf
+        f = frames[k]
+        # the timed steps' stream for this frame (one frame: the current one)
+        with torch.cuda.stream(streams[k] if nf > 1 else torch.cuda.current_stream()):
+            step(i, fr=f)
+            c = torch.zeros(8, dtype=torch.int64, device="cuda")
+            f.rasterize(g, counters=c[0:4])
+            f.rasterize_backward(g, counters=c[4:8])
+            d = f.depths[:N].view(torch.int32).to(torch.int64)
+            has = f.tiles[:N] != 0
+            raw.append(dict(M=f.M, cnt=c, V=(f.radii[:N] > 0).sum(),
+                            ranges=f.ranges.clone(), last=f.last_idx.clone(),
+                            dmax=torch.where(has, d, torch.full_like(d, -1)).max(),
+                            dmin=torch.where(has, d, torch.full_like(d, 1 << 40)).min()))
+
+    def analyse(r):
+        """Per-pose counts from the statistics pass: V, M, the instances the
+        backward stages, the pairs of each loop and the sort's passes (10-bit
+        digits over the tile bits and the bits that the depths of the rows
+        with tiles span)."""
+        c = r["cnt"].cpu().numpy()
+        rng = r["ranges"].cpu().numpy().view(np.uint32).astype(np.int64)
         lens = rng[:, 1] - rng[:, 0]
-        last = fr.last_idx.cpu().numpy().view(np.uint32).astype(np.int64)
+        last = r["last"].cpu().numpy().view(np.uint32).astype(np.int64)
         gx = (W + 15) // 16
         tile_of = (np.arange(H)[:, None] // 16) * gx + (np.arange(W)[None, :] // 16)
         maxlast = np.zeros(T, np.int64)
         np.maximum.at(maxlast, tile_of.ravel(), last.ravel())
         inside = np.bincount(tile_of.ravel(), minlength=T)
-        stats.append(dict(V=V, M=fr.M, M_bwd=int(maxlast.sum()),
-                          pairs_tile=int((inside * lens).sum()), fwd_eval=int(c[0]),
-                          blended=int(c[1]), plain_pairs=int(c[2]), fwd_plain_tile=int(c[3]),
-                          bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
-                          bwd_reductions=int(c[7]), sort_passes=sort_passes_of(fr)))
+        dmax, dmin = int(r["dmax"].item()), int(r["dmin"].item())
+        span = dmax - dmin if dmax >= 0 else 0
+        return dict(V=int(r["V"].item()), M=r["M"], M_bwd=int(maxlast.sum()),
+                    pairs_tile=int((inside * lens).sum()), fwd_eval=int(c[0]),
+                    blended=int(c[1]), plain_pairs=int(c[2]), fwd_plain_tile=int(c[3]),
+                    bwd_eval=int(c[4]), bwd_hit=int(c[5]), bwd_plain_tile=int(c[6]),
+                    bwd_reductions=int(c[7]),
+                    sort_passes=max(1, -(-(tile_bits + span.bit_length()) // 10)))
 
     def run_steps(frs, first, count):
         """Steps first .. first+count-1, step i on frame/stream i mod len(frs)
@@ -846,6 +858,8 @@ def main():
         return dt, dt_serial, {n: v / args.steps for n, v in ms.items()}
 
     dt, dt_serial, stage_ms = timed(frames)
+    stats = [analyse(r) for r in raw]
+    del raw
     packed_line = None
     train_line = None if args.no_train_step else train_step_bench(args, scene, gcams, targets,
                                                                    fr.capacity)
