@@ -750,11 +750,14 @@ def main():
 
     names = ["project_fwd", "bin_and_sort", "rasterize_fwd", "rasterize_bwd", "project_bwd"]
 
-    def step(i, ev=None, fr=fr):
+    def step(i, ev=None, fr=fr, project=True):
+        """The five stages of step i on frame fr (project=False: its
+        projection was issued already)."""
         c = gcams[i % P]
         if ev is not None:
             ev[0].record()
-        fr.project(g, c)
+        if project:
+            fr.project(g, c)
         if ev is not None:
             ev[1].record()
         fr.bin_and_sort(g)
@@ -819,14 +822,26 @@ def main():
 
     def run_steps(frs, first, count):
         """Steps first .. first+count-1, step i on frame/stream i mod len(frs)
-        (one frame: the current stream)."""
-        for i in range(first, first + count):
-            k = i % len(frs)
-            if len(frs) == 1:
+        (one frame: the current stream).  With several frames in flight, the
+        next step's projection is issued before this step's binning waits
+        for its instance count, so the host's wait overlaps it; each step
+        still runs the five stages of its own frame, and no projection past
+        the last step is issued."""
+        n = len(frs)
+        if n == 1:
+            for i in range(first, first + count):
                 step(i, fr=frs[0])
-            else:
-                with torch.cuda.stream(streams[k]):
-                    step(i, fr=frs[k])
+            return
+        on = lambda i: torch.cuda.stream(streams[i % n])
+        if count > 0:
+            with on(first):
+                frs[first % n].project(g, gcams[first % P])
+        for i in range(first, first + count):
+            if i + 1 < first + count:
+                with on(i + 1):
+                    frs[(i + 1) % n].project(g, gcams[(i + 1) % P])
+            with on(i):
+                step(i, fr=frs[i % n], project=False)
 
     def timed(frs):
         """Warm-up, then the timed steps with len(frs) frames in flight;
