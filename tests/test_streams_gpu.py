@@ -4,7 +4,9 @@ memory from the caller's buffers, so frames issued concurrently, each with
 its own buffers, must give the same bits as the same frames one at a time.
 Six poses of a 200k-Gaussian clustered scene at 640x416, dense and packed,
 on three streams, step i on stream i mod 3 with the frame buffers reused
-(each frame's outputs copied out on its stream before the next use).  Rows
+(each frame's outputs copied out on its stream before the next use), in
+the plain order and in the benchmark's order, where the next pose's
+projection is issued before this pose's binning waits on its count.  Rows
 a call leaves unwritten (the 2D records of culled Gaussians; packed rows past
 the visible count) keep an earlier pose's values and are not compared."""
 import numpy as np
@@ -21,7 +23,7 @@ ROWS = ("g_means2d", "g_conics", "g_colors", "g_means", "g_scales", "g_quats", "
         "g_sh")  # [..., rows]
 
 
-def _run(packed, streams):
+def _run(packed, streams, ahead=False):
     import torch
     from differentiable_rasterization_amd import raster
     s = scenes.cluster_scene(200_000)
@@ -32,13 +34,22 @@ def _run(packed, streams):
     frs = [raster.Frame(g.ld, s.sh_degree, 640, 416, capacity=4 * s.n, packed=packed)
            for _ in range(nf)]
     outs = [None] * len(cams)
+
+    def on(i):
+        return torch.cuda.stream(streams[i % nf]) if streams else torch.cuda.stream(
+            torch.cuda.current_stream())
+    if ahead:
+        with on(0):
+            frs[0].project(g, cams[0])
     for i, c in enumerate(cams):
         k = i % nf
-        ctx = torch.cuda.stream(streams[k]) if streams else torch.cuda.stream(
-            torch.cuda.current_stream())
-        with ctx:
+        if ahead and i + 1 < len(cams):
+            with on(i + 1):
+                frs[(i + 1) % nf].project(g, cams[i + 1])
+        with on(i):
             fr = frs[k]
-            fr.project(g, c)
+            if not ahead:
+                fr.project(g, c)
             fr.bin_and_sort(g)
             fr.rasterize_loss(g, tg[i], 1)
             fr.rasterize_backward(g)
@@ -50,11 +61,12 @@ def _run(packed, streams):
             for o in outs], s.n
 
 
+@pytest.mark.parametrize("ahead", [False, True])
 @pytest.mark.parametrize("packed", [False, True])
-def test_frames_in_flight_match_serial(packed):
+def test_frames_in_flight_match_serial(packed, ahead):
     import torch
     ref, N = _run(packed, [])
-    got, _ = _run(packed, [torch.cuda.Stream() for _ in range(3)])
+    got, _ = _run(packed, [torch.cuda.Stream() for _ in range(3)], ahead)
     for i, (a, b) in enumerate(zip(ref, got)):
         for n in ("image", "final_T", "last_idx", "radii"):
             assert_bits_equal(b[n], a[n], "pose %d %s" % (i, n))
@@ -66,5 +78,5 @@ def test_frames_in_flight_match_serial(packed):
         else:
             for n in ROWS:
                 assert_bits_equal(b[n][..., :N], a[n][..., :N], "pose %d %s" % (i, n))
-    print("[streams] packed=%s: 6 poses on 3 streams bit-identical to serial" % packed,
-          flush=True)
+    print("[streams] packed=%s ahead=%s: 6 poses on 3 streams bit-identical to serial"
+          % (packed, ahead), flush=True)
