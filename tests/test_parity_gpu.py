@@ -37,6 +37,11 @@ def _case(name):
     if name == "box_100k_1080p":
         s, c = scenes.box_scene()
         return s, c, "l2", (0.0, 0.0, 0.0)
+    if name == "cluster_200k_5k":
+        # 320 x 180 = 57,600 tiles: more than the schedule keeps in LDS
+        s = scenes.cluster_scene(n=200_000, seed=13)
+        c = scenes.sphere_poses(1, 6.0, 31, 5120, 2880, scenes.focal_for(5120))[0]
+        return s, c, "l1", (0.0, 0.0, 0.0)
     if name in ("cluster_1m_1080p", "cluster_1m_1280x832"):
         s, cams, loss = scenes.make_config(name)
         return s, cams[0], loss, (0.0, 0.0, 0.0)
@@ -44,7 +49,7 @@ def _case(name):
 
 
 CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "box_100k_1080p",
-         "cluster_1m_1280x832", "cluster_1m_1080p"]
+         "cluster_200k_5k", "cluster_1m_1280x832", "cluster_1m_1080p"]
 
 
 @functools.lru_cache(maxsize=None)

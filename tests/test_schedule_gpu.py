@@ -14,7 +14,10 @@ from test_parity_gpu import _case
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "cluster_1m_1080p"]
+# cluster_200k_5k: 57,600 tiles, past the 32,768 whose buckets the schedule
+# keeps in LDS (its second pass recomputes them from the ranges)
+CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "cluster_200k_5k",
+         "cluster_1m_1080p"]
 OUTPUTS = ("image", "final_T", "last", "g_means2d", "g_conics", "g_opac2d", "g_colors",
            "g_means", "g_scales", "g_quats", "g_opacities", "g_sh")
 
@@ -66,15 +69,16 @@ def test_schedule_leaves_outputs_unchanged(name, packed):
         assert_bits_equal(a[k], b[k], k)
 
 
-def test_batched_schedule():
+@pytest.mark.parametrize("W,H,ncam", [(640, 416, 3), (5120, 2880, 2)])
+def test_batched_schedule(W, H, ncam):
     import torch
     from differentiable_rasterization_amd import raster
     scene = scenes.cluster_scene(n=200_000, seed=13)
-    cams = scenes.sphere_poses(3, 6.0, 31, 640, 416, scenes.focal_for(640))
+    cams = scenes.sphere_poses(ncam, 6.0, 31, W, H, scenes.focal_for(W))
     g = raster.Gaussians.from_scene(scene)
     out = []
     for schedule in (True, False):
-        bf = raster.BatchFrame(g.ld, scene.sh_degree, 640, 416, len(cams), schedule=schedule)
+        bf = raster.BatchFrame(g.ld, scene.sh_degree, W, H, len(cams), schedule=schedule)
         bf.forward(g, cams)
         bf.dL_dimage.copy_(torch.sign(bf.image - 0.5))
         bf.backward(g)
