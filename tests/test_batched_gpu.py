@@ -238,3 +238,42 @@ def test_batch_backward_ragged_padded():
 def test_batch_backward_cluster_1m_1080p_four_poses():
     scene, cams, _ = scenes.make_config("cluster_1m_1080p")
     _check_backward("cluster_1m_1080p", scene, cams[:4])
+
+
+def test_batch_eight_cameras_forward_and_backward():
+    """The largest batch the calls take (eight cameras): the forward and the
+    backward against single-camera calls, bit for bit."""
+    scene = scenes.cluster_scene(n=200_000, seed=13)
+    cams = scenes.sphere_poses(8, 6.0, 33, 640, 416, scenes.focal_for(640))
+    _check_batch("cluster_200k_640x416 x8", scene, cams)
+    _check_backward("cluster_200k_640x416 x8", scene, cams)
+
+
+def test_batch_all_culled():
+    """A batch in which no camera sees any Gaussian (all behind every
+    camera): no instances, every image the background with T = 1 and no
+    last index, and zero gradients from the backward."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    scene, _ = scenes.tiny_scene(n=50)
+    scene.means[:, 2] = -scene.means[:, 2]
+    cams = [scenes.identity_camera(40, 24, 30.0), scenes.identity_camera(40, 24, 45.0)]
+    bg = (0.25, 0.5, 0.75)
+    g = raster.Gaussians.from_scene(scene)
+    bf = raster.BatchFrame(g.ld, scene.sh_degree, 40, 24, len(cams), background=bg)
+    bf.forward(g, cams)
+    bf.dL_dimage.fill_(1.0)
+    bf.backward(g)
+    torch.cuda.synchronize()
+    assert bf.M == 0
+    assert np.all(bf.ranges.cpu().numpy() == 0)
+    for c in range(len(cams)):
+        np.testing.assert_array_equal(bf.image[c].cpu().numpy(),
+                                      np.broadcast_to(np.float32(bg), (24, 40, 3)))
+        assert np.all(bf.final_T[c].cpu().numpy() == 1.0)
+        assert np.all(bf.last_idx[c].cpu().numpy() == 0)
+    n = scene.n
+    for k in ("g_means2d", "g_conics", "g_colors", "g_opacities_cams"):
+        assert np.all(getattr(bf, k)[..., :n].cpu().numpy() == 0), k
+    for k in ("g_means", "g_scales", "g_quats", "g_opacities", "g_sh"):
+        assert np.all(getattr(bf, k)[..., :n].cpu().numpy() == 0), k

@@ -45,7 +45,8 @@ def test_counting_variant_matches_and_counts_consistently():
     assert c[4] <= c[6] <= c[3]
 
 
-def test_zero_gaussians_and_all_culled():
+@pytest.mark.parametrize("packed", [False, True])
+def test_zero_gaussians_and_all_culled(packed):
     torch = _torch()
     cam = scenes.identity_camera(40, 24, 30.0)
     bg = (0.25, 0.5, 0.75)
@@ -56,8 +57,10 @@ def test_zero_gaussians_and_all_culled():
     behind.means[:, 2] = -behind.means[:, 2]
     for sc in (empty, behind):
         out = gpu_frame(sc, cam, background=bg, loss_kind="l2",
-                        target=scenes.target_image(cam, 1))
+                        target=scenes.target_image(cam, 1), packed=packed)
         assert out["M"] == 0
+        if packed:
+            assert out["V"] == 0
         np.testing.assert_array_equal(out["image"], np.broadcast_to(np.float32(bg), (24, 40, 3)))
         assert np.all(out["final_T"] == 1.0) and np.all(out["last"] == 0)
         assert np.all(out["ranges"] == 0)
