@@ -37,6 +37,11 @@ def _case(name):
     if name == "box_100k_1080p":
         s, c = scenes.box_scene()
         return s, c, "l2", (0.0, 0.0, 0.0)
+    if name in ("box_20k_sh1", "box_20k_sh2"):
+        # the projection kernels' SH degree 1 and 2 instances
+        s, c = scenes.box_scene(n=20000, seed=15, sh_degree=int(name[-1]), width=320,
+                                height=200, fx=190.0)
+        return s, c, "l2", (0.0, 0.0, 0.0)
     if name == "cluster_200k_5k":
         # 320 x 180 = 57,600 tiles: more than the schedule keeps in LDS
         s = scenes.cluster_scene(n=200_000, seed=13)
@@ -48,7 +53,8 @@ def _case(name):
     raise KeyError(name)
 
 
-CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "box_100k_1080p",
+CASES = ["tiny_1k_64", "box_20k_ragged", "box_20k_sh1", "box_20k_sh2", "cluster_200k_640x416",
+         "box_100k_1080p",
          "cluster_200k_5k", "cluster_1m_1280x832", "cluster_1m_1080p"]
 
 
