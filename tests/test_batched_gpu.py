@@ -279,10 +279,10 @@ def test_batch_all_culled():
         assert np.all(getattr(bf, k)[..., :n].cpu().numpy() == 0), k
 
 
-@pytest.mark.parametrize("deg", [1, 2])
+@pytest.mark.parametrize("deg", [0, 1, 2])
 def test_batch_low_sh_degrees(deg):
-    """The batched projection and projection backward at SH degrees 1 and 2
-    against single-camera calls, bit for bit."""
+    """The batched projection and projection backward at SH degrees 0, 1 and
+    2 against single-camera calls, bit for bit."""
     s, cam = scenes.box_scene(n=20000, seed=15, sh_degree=deg, width=320, height=200,
                               fx=190.0)
     cam2 = scenes.look_at_camera(np.array([3.0, 2.0, -7.0]), 320, 200, 190.0)

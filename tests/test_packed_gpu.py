@@ -23,7 +23,8 @@ from test_parity_gpu import _case
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["tiny_1k_64", "box_20k_ragged", "cluster_200k_640x416", "cluster_1m_1280x832"]
+CASES = ["tiny_1k_64", "box_20k_ragged", "box_20k_sh1", "box_20k_sh2", "cluster_200k_640x416",
+         "cluster_1m_1280x832"]
 
 
 @functools.lru_cache(maxsize=None)
