@@ -252,3 +252,34 @@ def test_absgrad_variant_keeps_the_gradients():
     assert np.all(b[:, 9:11] >= 0) and np.count_nonzero(b[:, 9:11]) > 0
     # |sum| <= sum |.|
     assert np.all(np.abs(b[:, 0:2]) <= b[:, 9:11] * (1 + 1e-5) + 1e-30)
+
+
+@pytest.mark.parametrize("absgrad", [False, True])
+def test_backward_stages_its_own_records(absgrad):
+    """gs_rasterize_bwd with staged = 0 stages the records from the planes
+    itself, into a workspace and partial slots that hold NaN, and gives the
+    same bits as reusing what the forward staged (staged = 1)."""
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    from test_parity_gpu import _case
+    scene, cam, loss, bg = _case("cluster_200k_640x416")
+    out = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=scenes.target_image(cam, 7),
+                    absgrad=absgrad)
+    fr = out["frame"]
+    g = raster.Gaussians.from_scene(scene)
+    nan = lambda t: torch.full_like(t, float("nan"))
+    ws, parts = nan(fr.records), nan(fr.partials)
+    g2 = raster.Grad2D(nan(fr.g_means2d), nan(fr.g_conics), nan(fr.g_opacities),
+                       nan(fr.g_colors), nan(fr.g_abs) if absgrad else None)
+    raster.gs_rasterize_bwd(g.N, g.ld, fr.W, fr.H, fr.ranges, fr.ids, fr.planes(g), fr.offsets,
+                            fr.tiles, fr.M, fr.background, fr.settings, fr.final_T, fr.last_idx,
+                            fr.dL_dimage, ws, fr.rec_bytes, 0, parts, fr.capacity, g2, 0,
+                            tile_order=fr.order)
+    torch.cuda.synchronize()
+    N = scene.n
+    pairs = [(g2.means2d, fr.g_means2d), (g2.conics, fr.g_conics),
+             (g2.opacities, fr.g_opacities), (g2.colors, fr.g_colors)]
+    if absgrad:
+        pairs.append((g2.abs, fr.g_abs))
+    for a, b in pairs:
+        assert_bits_equal(a[..., :N].cpu().numpy(), b[..., :N].cpu().numpy(), "staged=0")
