@@ -283,3 +283,32 @@ def test_backward_stages_its_own_records(absgrad):
         pairs.append((g2.abs, fr.g_abs))
     for a, b in pairs:
         assert_bits_equal(a[..., :N].cpu().numpy(), b[..., :N].cpu().numpy(), "staged=0")
+
+
+def test_rasterize_bwd_accumulate_modes():
+    """gs_rasterize_bwd's accumulate modes on top of a first pass (x + x == 2x
+    exactly in fp32): 1 adds to every 2D plane; 2 adds to the opacity and
+    absolute-gradient planes and overwrites the per-camera mean, conic and
+    colour planes.  Rows without tiles keep their (zero) values."""
+    torch = _torch()
+    from differentiable_rasterization_amd import raster
+    from test_parity_gpu import _case
+    scene, cam, loss, bg = _case("cluster_200k_640x416")
+    out = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=scenes.target_image(cam, 7),
+                    absgrad=True)
+    fr, g = out["frame"], raster.Gaussians.from_scene(scene)
+    N = scene.n
+    get = lambda t: t[..., :N].cpu().numpy().copy()
+    names = ("g_means2d", "g_conics", "g_colors", "g_opacities", "g_abs")
+    first = {k: get(getattr(fr, k)) for k in names}
+    assert np.count_nonzero(first["g_means2d"]) > 0
+    fr.rasterize_backward(g, absgrad=True, accumulate=1)
+    torch.cuda.synchronize()
+    for k in names:
+        assert_bits_equal(get(getattr(fr, k)), 2 * first[k], "accumulate=1 %s" % k)
+    fr.rasterize_backward(g, absgrad=True, accumulate=2)
+    torch.cuda.synchronize()
+    for k in ("g_means2d", "g_conics", "g_colors"):
+        assert_bits_equal(get(getattr(fr, k)), first[k], "accumulate=2 %s" % k)
+    for k in ("g_opacities", "g_abs"):
+        assert_bits_equal(get(getattr(fr, k)), 3 * first[k], "accumulate=2 %s" % k)
