@@ -86,20 +86,26 @@ def test_capacity_retry_and_leading_dimension():
         assert_bits_equal(small[k], ref[k], k)
 
 
-def test_accumulate_adds_into_outputs():
+@pytest.mark.parametrize("packed", [False, True])
+def test_accumulate_adds_into_outputs(packed):
+    """A second backward with accumulate on top of the first doubles the
+    gradients with respect to the Gaussians (x + x == 2x in fp32); packed:
+    the rows of the visible list."""
     torch = _torch()
     from differentiable_rasterization_amd import raster
     scene, cam = scenes.tiny_scene()
-    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 3))
+    out = gpu_frame(scene, cam, loss_kind="l2", target=scenes.target_image(cam, 3),
+                    packed=packed)
     fr, g = out["frame"], raster.Gaussians.from_scene(scene)
+    R = fr.V if packed else scene.n
+    assert R > 0
+    rows = lambda t: t[..., :R].cpu().numpy().copy()
+    names = ("g_opacities", "g_means", "g_scales", "g_quats", "g_sh")
+    first = {k: rows(getattr(fr, k)) for k in names}
     fr.backward(g, accumulate=1)  # second pass on top of the first
     torch.cuda.synchronize()
-    N = scene.n
-    twice = lambda t: t[:, :N].T.cpu().numpy() if t.dim() == 2 else t[:N].cpu().numpy()
-    # the second pass reproduces the first exactly, and x + x == 2x in fp32
-    assert_bits_equal(twice(fr.g_opacities), 2 * out["g_opacities"], "g_opacities")
-    assert_bits_equal(twice(fr.g_means), 2 * out["g_means"], "g_means")
-    assert_bits_equal(twice(fr.g_sh).reshape(N, 1, 3), 2 * out["g_sh"], "g_sh")
+    for k in names:
+        assert_bits_equal(rows(getattr(fr, k)), 2 * first[k], k)
 
 
 def test_non_finite_and_degenerate_gaussians_are_culled():
@@ -285,7 +291,8 @@ def test_backward_stages_its_own_records(absgrad):
         assert_bits_equal(a[..., :N].cpu().numpy(), b[..., :N].cpu().numpy(), "staged=0")
 
 
-def test_rasterize_bwd_accumulate_modes():
+@pytest.mark.parametrize("packed", [False, True])
+def test_rasterize_bwd_accumulate_modes(packed):
     """gs_rasterize_bwd's accumulate modes on top of a first pass (x + x == 2x
     exactly in fp32): 1 adds to every 2D plane; 2 adds to the opacity and
     absolute-gradient planes and overwrites the per-camera mean, conic and
@@ -295,9 +302,9 @@ def test_rasterize_bwd_accumulate_modes():
     from test_parity_gpu import _case
     scene, cam, loss, bg = _case("cluster_200k_640x416")
     out = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=scenes.target_image(cam, 7),
-                    absgrad=True)
+                    absgrad=True, packed=packed)
     fr, g = out["frame"], raster.Gaussians.from_scene(scene)
-    N = scene.n
+    N = fr.V if packed else scene.n  # packed: the rows of the visible list
     get = lambda t: t[..., :N].cpu().numpy().copy()
     names = ("g_means2d", "g_conics", "g_colors", "g_opacities", "g_abs")
     first = {k: get(getattr(fr, k)) for k in names}
