@@ -120,7 +120,7 @@ def grad2d_rows(fr, n, absgrad=False):
     return torch.cat([p[:, :n] for p in planes], 0).T.contiguous()
 
 
-def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None):
+def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None, settings=None):
     """GPU projection backward fed the given 2D gradients (dict with means2d
     [N,2], conics [N,3], colors [N,3]), rounded to fp32 into its 2D gradient
     planes; returns the 3D gradients in [N, ...] layout.  With ``vis_ids``
@@ -131,7 +131,8 @@ def gpu_project_bwd(scene, cam, g2, ld=None, vis_ids=None):
     N = scene.n
     g = raster.Gaussians.from_scene(scene, ld=ld)
     fr = raster.Frame(g.ld, scene.sh_degree, cam.width, cam.height, capacity=1024,
-                      packed=vis_ids is not None)
+                      packed=vis_ids is not None,
+                      settings=raster.default_settings(**(settings or {})))
     fr.project(g, cam)
     rows = np.arange(N) if vis_ids is None else np.asarray(vis_ids, np.int64)
     V = len(rows)
@@ -236,28 +237,33 @@ def compare_grad(g_gpu, g_or, abs_sum=None, exempt_rows=None, name="grad"):
 # stages in isolation (data flows from the oracle to the GPU only).
 # ---------------------------------------------------------------------------
 def run_parity_case(name, scene, cam, loss, bg, target, backward=True, depth_alpha=False,
-                    ld=None, packed=False):
+                    ld=None, packed=False, settings=None):
+    """Both whole paths on one case; ``settings`` (a dict of gs_settings
+    fields, default values elsewhere) goes to both sides."""
     import time
     t0 = time.time()
     print("\n[parity] case %s" % name, flush=True)
     gpu = gpu_frame(scene, cam, background=bg, loss_kind=loss, target=target,
-                    backward=backward, depth_alpha=depth_alpha, ld=ld, packed=packed)
+                    backward=backward, depth_alpha=depth_alpha, ld=ld, packed=packed,
+                    settings=settings)
     t1 = time.time()
-    orc = oracle.render(scene, cam, None, bg, with_margin=True)
-    r = dict(name=name, scene=scene, cam=cam, loss=loss, bg=bg, target=target, gpu=gpu, orc=orc)
+    orc = oracle.render(scene, cam, settings, bg, with_margin=True)
+    r = dict(name=name, scene=scene, cam=cam, loss=loss, bg=bg, target=target, gpu=gpu, orc=orc,
+             settings=settings)
     if backward:
         kind = oracle.LOSS_L2 if loss == "l2" else oracle.LOSS_L1
         dl = oracle.loss_grad_image(orc["raster"]["image"], target, kind).astype(np.float32)
-        bw = oracle.backward(scene, cam, orc, dl.astype(np.float64), None, bg, with_abs=True)
+        bw = oracle.backward(scene, cam, orc, dl.astype(np.float64), settings, bg, with_abs=True)
         r.update(dl=dl, bw=bw)
     t2 = time.time()
     if backward:
         # the isolated run also exercises the absolute-gradient variant
         r["gpu_iso"] = gpu_frame(scene, cam, background=bg, dL_dimage=r["dl"], ld=ld,
-                                 absgrad=True, packed=packed)
+                                 absgrad=True, packed=packed, settings=settings)
         # packed: the projection backward runs over the oracle's visible list
         vis_ids = np.flatnonzero(orc["proj"]["tiles"] > 0) if packed else None
-        r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld, vis_ids=vis_ids)
+        r["gpu_pbwd"] = gpu_project_bwd(scene, cam, r["bw"]["g2"], ld=ld, vis_ids=vis_ids,
+                                        settings=settings)
     print("[parity] %s: N=%d M=%d gpu %.1fs oracle %.1fs" % (
         name, scene.n, gpu["M"], t1 - t0 + time.time() - t2, t2 - t1), flush=True)
     return r
@@ -343,7 +349,7 @@ def _inherited(r, s_m2, s_con, s_col):
     scene, cam = r["scene"], r["cam"]
     return oracle.project_bwd_bound(scene.means, scene.scales, scene.quats, scene.sh,
                                     scene.sh_degree, cam, r["orc"]["proj"]["radii"], s_m2, s_con,
-                                    s_col)
+                                    s_col, r.get("settings"))
 
 
 def _classify_3d(r, g, o, e, rows, what):

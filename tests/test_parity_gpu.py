@@ -42,6 +42,11 @@ def _case(name):
         s, c = scenes.box_scene(n=20000, seed=15, sh_degree=int(name[-1]), width=320,
                                 height=200, fx=190.0)
         return s, c, "l2", (0.0, 0.0, 0.0)
+    if name == "cluster_200k_settings":
+        # every gs_settings field away from its default (SETTINGS below)
+        s = scenes.cluster_scene(n=200_000, seed=13)
+        c = scenes.sphere_poses(1, 6.0, 37, 640, 416, scenes.focal_for(640))[0]
+        return s, c, "l1", (0.2, 0.1, 0.3)
     if name == "cluster_200k_5k":
         # 320 x 180 = 57,600 tiles: more than the schedule keeps in LDS
         s = scenes.cluster_scene(n=200_000, seed=13)
@@ -54,14 +59,21 @@ def _case(name):
 
 
 CASES = ["tiny_1k_64", "box_20k_ragged", "box_20k_sh1", "box_20k_sh2", "cluster_200k_640x416",
-         "box_100k_1080p",
+         "cluster_200k_settings", "box_100k_1080p",
          "cluster_200k_5k", "cluster_1m_1280x832", "cluster_1m_1080p"]
+
+
+# settings of the cases that do not run with the defaults (eps2d 0.3,
+# alpha_min 1/255, alpha_max 0.99, T_min 1e-4, fov_clamp 1.3, sh_offset 0.5)
+SETTINGS = {"cluster_200k_settings": dict(eps2d=0.1, alpha_min=0.02, alpha_max=0.95,
+                                          T_min=0.05, fov_clamp=1.15, sh_offset=0.25)}
 
 
 @functools.lru_cache(maxsize=None)
 def run_case(name):
     scene, cam, loss, bg = _case(name)
-    return run_parity_case(name, scene, cam, loss, bg, scenes.target_image(cam, 7))
+    return run_parity_case(name, scene, cam, loss, bg, scenes.target_image(cam, 7),
+                           settings=SETTINGS.get(name))
 
 
 @pytest.mark.parametrize("name", CASES)
