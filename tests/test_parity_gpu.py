@@ -11,8 +11,10 @@ isolation by feeding the GPU the oracle's own upstream gradient: the
 oracle's dL/dimage (rounded to fp32) into the compositing backward, and the
 oracle's 2D gradients into the projection backward.
 """
+import dataclasses
 import functools
 
+import numpy as np
 import pytest
 
 from differentiable_rasterization_amd import scenes
@@ -47,6 +49,14 @@ def _case(name):
         s = scenes.cluster_scene(n=200_000, seed=13)
         c = scenes.sphere_poses(1, 6.0, 37, 640, 416, scenes.focal_for(640))[0]
         return s, c, "l1", (0.2, 0.1, 0.3)
+    if name == "cluster_200k_offaxis":
+        # fx != fy and a principal point off the image centre (and not on a
+        # pixel centre), near plane 0.5
+        s = scenes.cluster_scene(n=200_000, seed=13)
+        c = scenes.sphere_poses(1, 6.0, 39, 640, 416, 520.0, 470.0)[0]
+        c = dataclasses.replace(c, cx=float(np.float32(300.3)), cy=float(np.float32(231.7)),
+                                near=0.5)
+        return s, c, "l2", (0.0, 0.0, 0.0)
     if name == "cluster_200k_5k":
         # 320 x 180 = 57,600 tiles: more than the schedule keeps in LDS
         s = scenes.cluster_scene(n=200_000, seed=13)
@@ -59,7 +69,7 @@ def _case(name):
 
 
 CASES = ["tiny_1k_64", "box_20k_ragged", "box_20k_sh1", "box_20k_sh2", "cluster_200k_640x416",
-         "cluster_200k_settings", "box_100k_1080p",
+         "cluster_200k_settings", "cluster_200k_offaxis", "box_100k_1080p",
          "cluster_200k_5k", "cluster_1m_1280x832", "cluster_1m_1080p"]
 
 
