@@ -44,6 +44,13 @@ def _case(name):
         s, c = scenes.box_scene(n=20000, seed=15, sh_degree=int(name[-1]), width=320,
                                 height=200, fx=190.0)
         return s, c, "l2", (0.0, 0.0, 0.0)
+    if name == "box_20k_quatnorm":
+        # quaternions of any norm (U[0.3, 3] times a unit one): the backward
+        # differentiates through the normalisation
+        s, c = scenes.box_scene(n=20000, seed=16, width=320, height=200, fx=190.0)
+        rng = np.random.default_rng(16)
+        s.quats = (s.quats * rng.uniform(0.3, 3.0, size=(s.n, 1))).astype(np.float32)
+        return s, c, "l1", (0.0, 0.0, 0.0)
     if name == "cluster_200k_settings":
         # every gs_settings field away from its default (SETTINGS below)
         s = scenes.cluster_scene(n=200_000, seed=13)
@@ -70,7 +77,7 @@ def _case(name):
 
 
 CASES = ["tiny_1k_64", "box_20k_ragged", "box_20k_sh1", "box_20k_sh2", "cluster_200k_640x416",
-         "cluster_200k_settings", "cluster_200k_offaxis", "box_100k_1080p",
+         "box_20k_quatnorm", "cluster_200k_settings", "cluster_200k_offaxis", "box_100k_1080p",
          "cluster_200k_5k", "cluster_1m_1280x832", "cluster_1m_1080p"]
 
 
