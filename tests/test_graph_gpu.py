@@ -130,3 +130,48 @@ def test_graph_replays_equal_eager_frames():
             torch.cuda.synchronize()
             assert frames[c].check_counts()[1] is False
     _same(_snap(other, N), eager[2], "eager camera 2")
+
+
+def test_full_size_device_count_and_graph_replays():
+    """The benchmark's graph frames at full size (1M Gaussians, 1920x1080,
+    buffers for 1.25 x the largest M of the poses + 8192, as the benchmark
+    sizes them): device-count binning equals the read-back frame, and a
+    captured frame replayed twice (outputs poisoned before each replay,
+    eager work and synchronisations in between) equals the eager frame, bit
+    for bit."""
+    import torch
+    from differentiable_rasterization_amd import raster
+    scene, cams, _ = scenes.make_config("cluster_1m_1080p")
+    cams = cams[:2]
+    g = raster.Gaussians.from_scene(scene)
+    tg = [torch.from_numpy(scenes.target_image(c, k)).cuda() for k, c in enumerate(cams)]
+    N = scene.n
+    hosts = [_frame(g, scene, c, tg[k]) for k, c in enumerate(cams)]
+    Ms = [h.M for h in hosts]
+    eager = [_snap(h, N) for h in hosts]
+    del hosts
+    cap = int(1.25 * max(Ms)) + 8192
+    dev = _frame(g, scene, cams[0], tg[0], device_count=True, capacity=cap)
+    M, over = dev.check_counts()
+    assert M == Ms[0] and not over
+    _same(_snap(dev, N), eager[0], "device count camera 0")
+    fr = raster.Frame(g.ld, scene.sh_degree, cams[1].width, cams[1].height, device_count=True,
+                      capacity=cap)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(fr, g, cams[1], tg[1])  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        _step(fr, g, cams[1], tg[1])
+    for rep in range(2):
+        for k in OUTS:
+            getattr(fr, k).fill_(-7)
+        gr.replay()
+        _same(_snap(fr, N), eager[1], "full-size replay %d" % rep)
+        assert fr.check_counts() == (Ms[1], False)
+        _step(dev, g, cams[0], tg[0])
+        torch.cuda.synchronize()
+    _same(_snap(dev, N), eager[0], "device count camera 0 after the replays")
