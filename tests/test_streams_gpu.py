@@ -23,15 +23,21 @@ ROWS = ("g_means2d", "g_conics", "g_colors", "g_means", "g_scales", "g_quats", "
         "g_sh")  # [..., rows]
 
 
-def _run(packed, streams, ahead=False):
+def _run(packed, streams, ahead=False, full=False):
     import torch
     from differentiable_rasterization_amd import raster
-    s = scenes.cluster_scene(200_000)
-    cams = scenes.sphere_poses(6, 6.0, 31, 640, 416, scenes.focal_for(640))
+    if full:
+        # the benchmark's workload: 1M Gaussians, 1920x1080, its first poses
+        s, cams, _ = scenes.make_config("cluster_1m_1080p")
+        cams = cams[:4]
+    else:
+        s = scenes.cluster_scene(200_000)
+        cams = scenes.sphere_poses(6, 6.0, 31, 640, 416, scenes.focal_for(640))
+    W, H = cams[0].width, cams[0].height
     g = raster.Gaussians.from_scene(s)
     tg = [torch.from_numpy(scenes.target_image(c, i)).cuda() for i, c in enumerate(cams)]
     nf = max(1, len(streams))
-    frs = [raster.Frame(g.ld, s.sh_degree, 640, 416, capacity=4 * s.n, packed=packed)
+    frs = [raster.Frame(g.ld, s.sh_degree, W, H, capacity=4 * s.n, packed=packed)
            for _ in range(nf)]
     outs = [None] * len(cams)
 
@@ -80,3 +86,17 @@ def test_frames_in_flight_match_serial(packed, ahead):
                 assert_bits_equal(b[n][..., :N], a[n][..., :N], "pose %d %s" % (i, n))
     print("[streams] packed=%s ahead=%s: 6 poses on 3 streams bit-identical to serial"
           % (packed, ahead), flush=True)
+
+
+def test_full_size_frames_in_flight_match_serial():
+    """The benchmark's launch configuration at full size: four poses of the
+    1M-Gaussian 1080p workload, three frames in flight in its issue order,
+    bit-identical to the same frames one at a time."""
+    import torch
+    ref, N = _run(False, [], full=True)
+    got, _ = _run(False, [torch.cuda.Stream() for _ in range(3)], True, full=True)
+    for i, (a, b) in enumerate(zip(ref, got)):
+        for n in ("image", "final_T", "last_idx", "radii"):
+            assert_bits_equal(b[n], a[n], "full pose %d %s" % (i, n))
+        for n in ROWS:
+            assert_bits_equal(b[n][..., :N], a[n][..., :N], "full pose %d %s" % (i, n))
