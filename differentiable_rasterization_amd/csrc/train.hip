@@ -97,22 +97,42 @@ __global__ __launch_bounds__(256) void ssim_stats_kernel(int W, int H, int tiles
   const int64_t plane = (int64_t)W * H;
   double acc_s = 0.0, acc_l1 = 0.0;
   const int ox = t & 31, oy0 = (t >> 5) * 2;  // column pass: two rows per thread
+  // halo element k of this thread (rows of 42 as 64 lanes): its pixel's
+  // offset, -1 outside the image (zero there); the next channel's values are
+  // loaded into registers while the current channel is computed
+  constexpr int kLd = (kSsimHy * 64 + 255) / 256;
+  int64_t hpix[kLd];
+#pragma unroll
+  for (int k = 0; k < kLd; ++k) {
+    const int idx = t + 256 * k, r = idx >> 6, px = idx & 63;
+    const int gx = x0 - kSsimR + px, gy = y0 - kSsimR + r;
+    hpix[k] = (idx < kSsimHy * 64 && px < kSsimHx && gx >= 0 && gx < W && gy >= 0 && gy < H)
+                  ? ((int64_t)gy * W + gx) * 3 : -1;
+  }
+  float px_[kLd], py_[kLd];
+#pragma unroll
+  for (int k = 0; k < kLd; ++k) {
+    px_[k] = hpix[k] >= 0 ? x[hpix[k]] : 0.0f;
+    py_[k] = hpix[k] >= 0 ? y[hpix[k]] : 0.0f;
+  }
   for (int c = 0; c < 3; ++c) {
-    // channel c of the halo, zero outside the image (rows of 42 as 64 lanes)
-    for (int idx = t; idx < kSsimHy * 64; idx += 256) {
-      const int r = idx >> 6, px = idx & 63;
-      if (px >= kSsimHx) continue;
-      const int gx = x0 - kSsimR + px, gy = y0 - kSsimR + r;
-      float vx = 0.0f, vy = 0.0f;
-      if (gx >= 0 && gx < W && gy >= 0 && gy < H) {
-        const int64_t o = ((int64_t)gy * W + gx) * 3 + c;
-        vx = x[o];
-        vy = y[o];
+    // channel c of the halo into LDS
+#pragma unroll
+    for (int k = 0; k < kLd; ++k) {
+      const int idx = t + 256 * k, px = idx & 63;
+      if (idx < kSsimHy * 64 && px < kSsimHx) {
+        sx[idx >> 6][px] = px_[k];
+        sy[idx >> 6][px] = py_[k];
       }
-      sx[r][px] = vx;
-      sy[r][px] = vy;
     }
     __syncthreads();
+    if (c < 2) {
+#pragma unroll
+      for (int k = 0; k < kLd; ++k) {
+        px_[k] = hpix[k] >= 0 ? x[hpix[k] + c + 1] : 0.0f;
+        py_[k] = hpix[k] >= 0 ? y[hpix[k] + c + 1] : 0.0f;
+      }
+    }
     // row pass: 26 rows x 8 groups of four outputs
     if (t < kSsimHy * 8) {
       const int r = t >> 3, j0 = (t & 7) * 4;
