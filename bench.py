@@ -46,11 +46,12 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 #   forward: 49 VALU and two v_exp_f32 per two unrolled pairs -> 28.5 / pair;
 #   backward: 20 VALU plus v_exp_f32 and v_rcp_f32 per evaluated pair (28
 #   slots); a wavefront with a hit on the splat adds 13 VALU of gradient
-#   terms and 35 of the nine-field reduction (lane swaps + DPP row scan).
+#   terms and 32 of the nine-field reduction (lane swaps, an 8-lane merge
+#   and DPP half-row totals, with the LDS addresses).
 FWD_SLOTS_PER_PAIR = 28.5
 BWD_EVAL_SLOTS = 28.0
 BWD_GRAD_SLOTS = 13.0
-BWD_REDUCE_SLOTS = 35.0
+BWD_REDUCE_SLOTS = 32.0
 BWD_SLOTS_PER_PAIR = BWD_EVAL_SLOTS + BWD_GRAD_SLOTS
 
 

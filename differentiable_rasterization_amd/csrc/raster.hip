@@ -488,10 +488,32 @@ __global__ __launch_bounds__(256) void raster_fwd_kernel(
 // lane swaps (v_permlane32_swap exchanges the upper half of one register
 // with the lower half of another, v_permlane16_swap the odd 16-lane rows of
 // one with the even rows of another), so that after them every 16-lane row
-// of a register carries one field; then an inclusive DPP row scan leaves each
-// row's total in its lane 15.  About 30 instructions instead of six DPP
-// steps per field.
+// of a register carries one field; a third step at 8-lane granularity (two
+// selects and an add from the lanes 8 apart in the row) puts fields 0-3 and
+// 4-7 in the two halves of each row of one register; then three DPP adds
+// (half-row mirror, two quad permutations) leave each 8-lane half's total in
+// all of its lanes.  About 27 instructions instead of six DPP steps per
+// field.
 // ---------------------------------------------------------------------------
+// DPP lane permutations within 16-lane rows (no lane reads outside its row).
+constexpr int kRowRor8 = 0x128;       // row_ror:8: lane i reads lane (i + 8) mod 16
+constexpr int kRowHalfMirror = 0x141;  // row_half_mirror: lane i reads 7 - i in its half
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+template <int kCtrl>
+__device__ inline float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+// The total of each 8-lane half-row, in all eight of its lanes: lane i plus
+// lane 7 - i, then the pairs and the halves of each quad.
+__device__ inline float half_row_total(float v) {
+  v += dpp_f32<kRowHalfMirror>(v);
+  v += dpp_f32<kQuadSwap2>(v);
+  v += dpp_f32<kQuadSwap1>(v);
+  return v;
+}
+
 __device__ inline float swap_add32(float a, float b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
                                                   false, false);
@@ -519,21 +541,26 @@ __device__ inline void reduce_add(const float* f, float* dst, int stride) {
   const float s89 = swap_add32(f[8], kAbs ? f[9] : f[8]);
   const float sA = kAbs ? swap_add32(f[10], f[10]) : s89;
   // rows of t0: fields 0, 2, 1, 3; of t1: 4, 6, 5, 7; of t2: 8, 10, 9, -
-  float t0 = swap_add16(s01, s23);
-  float t1 = swap_add16(s45, s67);
+  const float t0 = swap_add16(s01, s23);
+  const float t1 = swap_add16(s45, s67);
   float t2 = swap_add16(s89, sA);
-  t0 = row_total_lane15(t0);
-  t1 = row_total_lane15(t1);
-  t2 = row_total_lane15(t2);
+  // the low half of each row keeps t0's partial sums (lane i plus lane i + 8),
+  // the high half t1's (lane i plus lane i - 8)
+  const bool hi = (threadIdx.x & 8) != 0;
+  float m = (hi ? t1 : t0) + dpp_f32<kRowRor8>(hi ? t0 : t1);
+  m = half_row_total(m);
+  t2 += dpp_f32<kRowRor8>(t2);
+  t2 = half_row_total(t2);  // the row's total, in every lane of the row
   const int lane = threadIdx.x & 63;
-  if ((lane & 15) == 15) {
+  if ((lane & 7) == 7) {
     const int row = lane >> 4;
-    const int q = (row == 1) ? 2 : (row == 2 ? 1 : row);
-    atomicAdd(&dst[q * stride], t0);
-    atomicAdd(&dst[(4 + q) * stride], t1);
-    if (row == 0) atomicAdd(&dst[8 * stride], t2);
-    if (kAbs && row == 1) atomicAdd(&dst[10 * stride], t2);
-    if (kAbs && row == 2) atomicAdd(&dst[9 * stride], t2);
+    const int q = ((row == 1) ? 2 : (row == 2 ? 1 : row)) + (hi ? 4 : 0);
+    atomicAdd(&dst[q * stride], m);
+    if (hi) {
+      if (row == 0) atomicAdd(&dst[8 * stride], t2);
+      if (kAbs && row == 1) atomicAdd(&dst[10 * stride], t2);
+      if (kAbs && row == 2) atomicAdd(&dst[9 * stride], t2);
+    }
   }
 }
 
