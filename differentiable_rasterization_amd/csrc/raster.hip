@@ -20,14 +20,15 @@
 //
 // The backward walks the same lists back to front from each pixel's last
 // blended entry.  Per splat each wave reduces its 64 pixels' nine gradient
-// terms with two gfx950 lane-swap transpose steps and a DPP row scan
-// (skipped with a ballot when no lane of the wave touched the splat); the
-// wave partials meet in LDS and the tile stores its sums for the splat, with
-// a plain 48-byte store, into the instance's own slot (the Gaussian's offset
-// plus the tile's index in its rect; slots are packed 48 bytes apart, so no
-// line carries unused bytes).  A second kernel adds each Gaussian's
-// slots in a fixed order.  No global atomics: device-scope float atomics go
-// to memory on this part, and a fixed order makes gradients reproducible.
+// terms with two gfx950 lane-swap transpose steps, an 8-lane merge and DPP
+// half-row totals (skipped with a ballot when no lane of the wave touched
+// the splat); the wave partials meet in LDS and the tile stores its sums for
+// the splat, with a plain 48-byte store, into the instance's own slot (the
+// Gaussian's offset plus the tile's index in its rect; slots are packed 48
+// bytes apart, so no line carries unused bytes).  A second kernel adds each
+// Gaussian's slots in a fixed order.  No global atomics: device-scope float
+// atomics go to memory on this part, and a fixed order makes gradients
+// reproducible.
 //
 // The calls take the projection's planes; pack_splats_kernel first stages
 // each visible row into a 64-byte record in the caller's workspace, so that
